@@ -1,0 +1,22 @@
+"""CPU oracle for kernelized linear attention (test infrastructure only).
+
+Only tests, the smoke check and the bench's CPU-baseline leg may import this
+package. It shares no code with the HIP library or its binding.
+"""
+
+from .linattn_oracle import (  # noqa: F401
+    EPS,
+    FMAPS,
+    attention,
+    attention_via_state,
+    chunked,
+    cumsum_form,
+    decode_step,
+    feature_dim,
+    feature_map,
+    final_state,
+    phi_elu1,
+    phi_identity,
+    phi_performer,
+    recurrent,
+)

@@ -1,0 +1,278 @@
+"""CPU oracle for kernelized linear attention (NumPy, float64).
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check and the bench's
+CPU-baseline leg may import or run this module. The product (the HIP library
+and its Python binding) never does; the two share no code.
+
+Sources (the three pages on linear attention):
+  [LA]  "Linear Attention" article (marovi.ai), sections "Reformulación con
+        núcleos", "Mapas de características", "Forma recurrente e inferencia
+        autorregresiva", "Entrenamiento: forma paralela".
+  [LT]  "Linear Transformer (Transformers are RNNs)" glossary entry
+        (visibilidadia.com), sections "La función ELU + 1", "Formulación
+        matemática de la atención lineal", "La formulación recurrente paso a
+        paso", "Comprobar la equivalencia entre cálculo recurrente y cálculo
+        causal vectorizado".
+  [UL]  "Linear Attention" glossary entry (ultralytics.com), "Ejemplo de
+        código" (the output without a denominator).
+
+Every input is upcast to float64 exactly; everything is computed in float64.
+
+Readings taken where the pages are silent or disagree (each one is also
+listed with its reasons in the design notes of the repository):
+  * causal sums include the current token (j <= i): [LA] recurrent form and
+    [LT] step-by-step form update the state before reading it out;
+  * the denominator is clamped, y = num / max(den, EPS) with EPS = 1e-6, as
+    the code examples of [LT] do; with positive feature maps the clamp only
+    matters when den < 1e-6;
+  * ``normalize=False`` returns the numerator alone ([LA] notes some
+    implementations drop the denominator; [UL]'s example does);
+  * elu+1 uses alpha = 1 and takes the exponential branch at x = 0 ([LT]
+    "La función ELU + 1");
+  * random features: phi(x) = exp(W x~ - |x~|^2/2) / sqrt(m) with
+    x~ = d^(-1/4) x, so that E[phi(q).phi(k)] = exp(q.k / sqrt(d)), the
+    kernel that [LA] "Reformulación con núcleos" writes for softmax;
+  * an optional initial state (S0, z0) stands for tokens before the first
+    one given: it adds phi(q_i).S0 to the numerator and phi(q_i).z0 to the
+    denominator of every output.
+
+Parity pins: every function here is checked by tests that do not reuse its
+code (hand-derived worked examples, closed forms, library routines,
+invariants); see tests/test_oracle_pins.py.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+EPS = 1e-6
+
+FMAPS = ("elu1", "performer", "identity")
+
+
+# ---------------------------------------------------------------------------
+# Feature maps  ([LA] "Mapas de características"; [LT] "La función ELU + 1")
+# ---------------------------------------------------------------------------
+
+def phi_elu1(x):
+    """elu(x) + 1 elementwise: x + 1 for x > 0, exp(x) for x <= 0 ([LT] "La función ELU + 1")."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0.0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def phi_performer(x, W):
+    """Positive random features ([LA] "Mapas de características", Performer bullet).
+
+    phi(x) = exp(W x~ - |x~|^2 / 2) / sqrt(m), x~ = d^(-1/4) x, W of shape (m, d).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    d = x.shape[-1]
+    m = W.shape[0]
+    xt = x * d ** -0.25
+    u = xt @ W.T
+    sq = np.sum(xt * xt, axis=-1, keepdims=True)
+    return np.exp(u - 0.5 * sq) / np.sqrt(m)
+
+
+def phi_identity(x):
+    """phi(x) = x ([LA] "Mapas de características", identity bullet); used as a test device."""
+    return np.asarray(x, dtype=np.float64)
+
+
+def feature_map(x, fmap="elu1", W=None):
+    if fmap == "elu1":
+        return phi_elu1(x)
+    if fmap == "performer":
+        if W is None:
+            raise ValueError("performer map needs W")
+        return phi_performer(x, W)
+    if fmap == "identity":
+        return phi_identity(x)
+    raise ValueError(f"unknown feature map {fmap!r}")
+
+
+def feature_dim(d, fmap="elu1", W=None):
+    return int(np.asarray(W).shape[0]) if fmap == "performer" else d
+
+
+def _finish(num, den, normalize):
+    if not normalize:
+        return num
+    return num / np.maximum(den, EPS)[..., None]
+
+
+def _bh(x):
+    """View [B, H, N, d] (or [N, d]) input as float64 [G, N, d]."""
+    x = np.asarray(x, dtype=np.float64)
+    if x.ndim == 2:
+        return x[None]
+    return x.reshape(-1, x.shape[-2], x.shape[-1])
+
+
+def _state(S0, z0, G, dfeat, dv):
+    S = np.zeros((G, dfeat, dv)) if S0 is None else np.asarray(S0, np.float64).reshape(G, dfeat, dv).copy()
+    z = np.zeros((G, dfeat)) if z0 is None else np.asarray(z0, np.float64).reshape(G, dfeat).copy()
+    return S, z
+
+
+# ---------------------------------------------------------------------------
+# The definition  ([LA] "Reformulación con núcleos", first form of y_i)
+# ---------------------------------------------------------------------------
+
+def attention(q, k, v, fmap="elu1", W=None, causal=True, normalize=True,
+              S0=None, z0=None, rows=None):
+    """y_i = sum_j (phi(q_i).phi(k_j)) v_j / sum_j phi(q_i).phi(k_j).
+
+    The sums run over j <= i when ``causal`` (inclusive), else over all j.
+    The N x N similarity matrix is formed explicitly (brute force). ``rows``
+    restricts the computation to a subset of query positions, so long
+    sequences can be checked at sampled outputs.
+    Returns float64 of shape [..., len(rows) or N, d_v].
+    """
+    shape = np.asarray(q).shape
+    Q, K, V = _bh(q), _bh(k), _bh(v)
+    G, N, _ = Q.shape
+    dv = V.shape[-1]
+    idx = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    Kf = feature_map(K, fmap, W)
+    Qf = feature_map(Q[:, idx], fmap, W)
+    dfeat = Kf.shape[-1]
+    S, z = _state(S0, z0, G, dfeat, dv)
+    out = np.empty((G, idx.size, dv))
+    for g in range(G):
+        A = Qf[g] @ Kf[g].T                           # [R, N] similarities
+        if causal:
+            A = np.where(np.arange(N)[None, :] <= idx[:, None], A, 0.0)
+        num = A @ V[g] + Qf[g] @ S[g]
+        den = A.sum(axis=1) + Qf[g] @ z[g]
+        out[g] = _finish(num, den, normalize)
+    return out.reshape(shape[:-2] + (idx.size, dv))
+
+
+def final_state(k, v, fmap="elu1", W=None, S0=None, z0=None):
+    """S = S0 + sum_j phi(k_j) v_j^T, z = z0 + sum_j phi(k_j) ([LA] "Reformulación con núcleos")."""
+    shape = np.asarray(k).shape
+    K, V = _bh(k), _bh(v)
+    G = K.shape[0]
+    Kf = feature_map(K, fmap, W)
+    S, z = _state(S0, z0, G, Kf.shape[-1], V.shape[-1])
+    S = S + np.einsum("gnc,gne->gce", Kf, V)
+    z = z + Kf.sum(axis=1)
+    lead = shape[:-2]
+    return S.reshape(lead + S.shape[1:]), z.reshape(lead + z.shape[1:])
+
+
+# ---------------------------------------------------------------------------
+# Non-causal form through the two sums ([LA] "Reformulación con núcleos",
+# second form; [LT] "Formulación matemática": Q'(K'^T V) / Q'(K'^T 1))
+# ---------------------------------------------------------------------------
+
+def attention_via_state(q, k, v, fmap="elu1", W=None, normalize=True, S0=None, z0=None):
+    shape = np.asarray(q).shape
+    Q = _bh(q)
+    S, z = final_state(k, v, fmap, W, S0, z0)
+    G = Q.shape[0]
+    S = np.asarray(S).reshape(G, S.shape[-2], S.shape[-1])
+    z = np.asarray(z).reshape(G, z.shape[-1])
+    Qf = feature_map(Q, fmap, W)
+    num = np.einsum("gnc,gce->gne", Qf, S)
+    den = np.einsum("gnc,gc->gn", Qf, z)
+    return _finish(num, den, normalize).reshape(shape[:-1] + (S.shape[-1],))
+
+
+# ---------------------------------------------------------------------------
+# Recurrent form ([LA] "Forma recurrente e inferencia autorregresiva";
+# [LT] "La formulación recurrente paso a paso")
+# ---------------------------------------------------------------------------
+
+def decode_step(S, z, q, k, v, fmap="elu1", W=None, normalize=True):
+    """One token per head: S += phi(k) v^T, z += phi(k), then y = phi(q)^T S / phi(q).z.
+
+    S: [..., d', d], z: [..., d'], q/k/v: [..., d]. Returns (y, S_new, z_new);
+    the inputs are not modified.
+    """
+    S = np.asarray(S, np.float64)
+    z = np.asarray(z, np.float64)
+    qf = feature_map(np.asarray(q, np.float64), fmap, W)
+    kf = feature_map(np.asarray(k, np.float64), fmap, W)
+    v = np.asarray(v, np.float64)
+    S_new = S + kf[..., :, None] * v[..., None, :]
+    z_new = z + kf
+    num = np.einsum("...c,...ce->...e", qf, S_new)
+    den = np.einsum("...c,...c->...", qf, z_new)
+    return _finish(num, den, normalize), S_new, z_new
+
+
+def recurrent(q, k, v, fmap="elu1", W=None, normalize=True, S0=None, z0=None):
+    """Token-by-token loop over the sequence (every head at once).
+
+    Returns (y, S_N, z_N).
+    """
+    shape = np.asarray(q).shape
+    Q, K, V = _bh(q), _bh(k), _bh(v)
+    G, N, _ = Q.shape
+    dv = V.shape[-1]
+    dfeat = feature_dim(Q.shape[-1], fmap, W)
+    S, z = _state(S0, z0, G, dfeat, dv)
+    y = np.empty((G, N, dv))
+    for t in range(N):
+        y[:, t], S, z = decode_step(S, z, Q[:, t], K[:, t], V[:, t], fmap, W, normalize)
+    lead = shape[:-2]
+    return (y.reshape(shape[:-1] + (dv,)), S.reshape(lead + S.shape[1:]),
+            z.reshape(lead + z.shape[1:]))
+
+
+# ---------------------------------------------------------------------------
+# Cumulative-sum form ([LT] "Comprobar la equivalencia ..."): per-token outer
+# products, prefix sums along the sequence, contraction with phi(q). Tiny
+# inputs only (materializes N x d' x d per head).
+# ---------------------------------------------------------------------------
+
+def cumsum_form(q, k, v, fmap="elu1", W=None, normalize=True):
+    shape = np.asarray(q).shape
+    Q, K, V = _bh(q), _bh(k), _bh(v)
+    Qf = feature_map(Q, fmap, W)
+    Kf = feature_map(K, fmap, W)
+    kv = Kf[..., :, None] * V[..., None, :]          # [G, N, d', d]
+    S = np.cumsum(kv, axis=1)
+    z = np.cumsum(Kf, axis=1)
+    num = np.einsum("gnc,gnce->gne", Qf, S)
+    den = np.einsum("gnc,gnc->gn", Qf, z)
+    return _finish(num, den, normalize).reshape(shape[:-1] + (V.shape[-1],))
+
+
+# ---------------------------------------------------------------------------
+# Blockwise form ([LA] "Entrenamiento: forma paralela"): the sequence is cut
+# into blocks of C tokens; inside a block the masked quadratic similarity
+# form, across blocks the running sums S, z.
+# ---------------------------------------------------------------------------
+
+def chunked(q, k, v, fmap="elu1", W=None, causal=True, normalize=True, chunk=64,
+            S0=None, z0=None):
+    """Returns (y, S_N, z_N). For ``causal=False`` the full sums are formed first."""
+    if not causal:
+        y = attention_via_state(q, k, v, fmap, W, normalize, S0, z0)
+        S, z = final_state(k, v, fmap, W, S0, z0)
+        return y, S, z
+    shape = np.asarray(q).shape
+    Q, K, V = _bh(q), _bh(k), _bh(v)
+    G, N, _ = Q.shape
+    dv = V.shape[-1]
+    Qf = feature_map(Q, fmap, W)
+    Kf = feature_map(K, fmap, W)
+    S, z = _state(S0, z0, G, Qf.shape[-1], dv)
+    y = np.empty((G, N, dv))
+    for s in range(0, N, chunk):
+        e = min(N, s + chunk)
+        qc, kc, vc = Qf[:, s:e], Kf[:, s:e], V[:, s:e]
+        A = np.einsum("gic,gjc->gij", qc, kc)
+        A = A * np.tril(np.ones((e - s, e - s)))[None]
+        num = np.einsum("gij,gje->gie", A, vc) + np.einsum("gic,gce->gie", qc, S)
+        den = A.sum(axis=2) + np.einsum("gic,gc->gi", qc, z)
+        y[:, s:e] = _finish(num, den, normalize)
+        S = S + np.einsum("gjc,gje->gce", kc, vc)
+        z = z + kc.sum(axis=1)
+    lead = shape[:-2]
+    return (y.reshape(shape[:-1] + (dv,)), S.reshape(lead + S.shape[1:]),
+            z.reshape(lead + z.shape[1:]))
