@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of kernelized linear attention on one MI355X.
+
+One step = one causal prefill of the long-context workload (B=1, H=16,
+N=65536, d=128, bf16, elu+1, normalized), inputs resident in HBM. The decode
+workload (256 sequences x 32 heads, d=64, fp32 state, 1000 single-token steps
+after a 4096-token prefill) is timed in the same run and reported under
+"decode". Prints one JSON line.
+
+Roofline: per dominant kernel, algorithmic bytes per launch / average launch
+duration (HIP events recorded on the launch stream) against 8 TB/s.
+cpu_baseline: the CPU oracle on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--decode-steps", type=int, default=1000)
+    p.add_argument("--decode-warmup", type=int, default=20)
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-heads", type=int, default=1, help="heads of the prefill the oracle times")
+    p.add_argument("--cpu-decode-steps", type=int, default=2)
+    return p.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(every sequence/head shards with no communication; see the design notes)", file=sys.stderr)
+        return 2
+
+    import torch
+    import la_inputs
+    import causal_linear_attention_02_amd as la
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    W = la_inputs.WORKLOADS["prefill_b1h16n65536d128"]
+    B, H, N, d = W["B"], W["H"], W["N"], W["d"]
+
+    # ---------------- prefill ----------------
+    log(f"prefill: generating inputs B{B} H{H} N{N} d{d}")
+    q, k, v = la_inputs.gaussian_qkv(B, H, N, d, seed=W["seed"], scale=W["scale"], bf16=True)
+    tq = torch.from_numpy(q).to(torch.bfloat16).to(dev)
+    tk = torch.from_numpy(k).to(torch.bfloat16).to(dev)
+    tv = torch.from_numpy(v).to(torch.bfloat16).to(dev)
+    out = torch.empty_like(tq)
+    ws_bytes = la.la_forward_workspace_size(B, H, N, d, causal=True)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    del q, k, v
+
+    def fwd(events=None):
+        la.la_forward_ex(tq, tk, tv, causal=True, normalize=True, out=out, workspace=ws, events=events)
+
+    log(f"prefill: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"prefill: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fwd(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])  # ms
+    ms_step = wall * 1e3 / args.steps
+    ms_state, ms_scan, ms_out = stage.mean(axis=0)
+    tokens = B * N
+    value = tokens / (ms_step * 1e-3)
+    head_tokens = B * H * N
+    alg_bytes = head_tokens * 4 * d * 2                     # q, k, v read + out written, bf16
+    out_gbs = alg_bytes / (ms_out * 1e-3) / 1e9
+    whole_gbs = alg_bytes / (ms_step * 1e-3) / 1e9
+    C = 64
+    flops_useful = head_tokens * (4 * d * d + (C + 1) * 2 * d)  # chunked form, masked triangle
+    log(f"prefill: {ms_step*1e3:.1f} us/step (state {ms_state*1e3:.1f}, scan {ms_scan*1e3:.1f}, "
+        f"output {ms_out*1e3:.1f} us); output pass {out_gbs:.0f} GB/s")
+
+    del tq, tk, tv, out, ws
+    torch.cuda.empty_cache()
+
+    # ---------------- decode ----------------
+    decode = None
+    if not args.no_decode:
+        Wd = la_inputs.WORKLOADS["decode_s256h32d64"]
+        Bd, Hd, dd, N0 = Wd["B"], Wd["H"], Wd["d"], Wd["prefill"]
+        T = args.decode_steps
+        log(f"decode: prefill state from {N0} tokens x {Bd*Hd} heads")
+        S = torch.empty((Bd, Hd, dd, dd), dtype=torch.float32, device=dev)
+        z = torch.empty((Bd, Hd, dd), dtype=torch.float32, device=dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(Wd["prefill_seed"])
+        step_b = 32
+        for b0 in range(0, Bd, step_b):
+            shp = (step_b, Hd, N0, dd)
+            pq = torch.randn(shp, generator=gen, device=dev).to(torch.bfloat16)
+            pk = torch.randn(shp, generator=gen, device=dev).to(torch.bfloat16)
+            pv = torch.randn(shp, generator=gen, device=dev).to(torch.bfloat16)
+            _, s_, z_ = la.la_forward(pq, pk, pv, causal=True, return_state=True)
+            S[b0:b0 + step_b].copy_(s_)
+            z[b0:b0 + step_b].copy_(z_)
+            del pq, pk, pv
+        gen.manual_seed(Wd["step_seed"])
+        nsteps = T + args.decode_warmup
+        shp = (nsteps, Bd, Hd, dd)
+        sq = torch.randn(shp, generator=gen, device=dev).to(torch.bfloat16)
+        sk = torch.randn(shp, generator=gen, device=dev).to(torch.bfloat16)
+        sv = torch.randn(shp, generator=gen, device=dev).to(torch.bfloat16)
+        y = torch.empty((Bd, Hd, dd), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        for t in range(args.decode_warmup):
+            la.la_decode_step(S, z, sq[t], sk[t], sv[t], out=y)
+        torch.cuda.synchronize()
+        dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * T)]
+        log(f"decode: timing {T} steps")
+        t0 = time.perf_counter()
+        for t in range(T):
+            dev_ev[2 * t].record()
+            la.la_decode_step(S, z, sq[args.decode_warmup + t], sk[args.decode_warmup + t],
+                              sv[args.decode_warmup + t], out=y)
+            dev_ev[2 * t + 1].record()
+        torch.cuda.synchronize()
+        dwall = time.perf_counter() - t0
+        kern_ms = np.array([dev_ev[2 * t].elapsed_time(dev_ev[2 * t + 1]) for t in range(T)])
+        heads = Bd * Hd
+        step_bytes = heads * (2 * 4 * (dd * dd + dd) + 3 * 2 * dd + 2 * dd)
+        k_ms = float(kern_ms.mean())
+        d_gbs = step_bytes / (k_ms * 1e-3) / 1e9
+        decode = {
+            "metric": "decode steps/s",
+            "value": T / dwall,
+            "unit": "steps/s",
+            "steps": T,
+            "ms_per_step": dwall * 1e3 / T,
+            "config": {"workload": "decode_s256h32d64", "sequences": Bd, "heads": Hd, "d": dd,
+                       "prefill_tokens": N0, "state": "fp32", "inputs": "bf16"},
+            "roofline": {"bound": "hbm", "kernel": "decode_step_kernel", "achieved": round(d_gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(d_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": None, "bytes_per_launch": step_bytes, "avg_launch_us": round(k_ms * 1e3, 2)},
+        }
+        log(f"decode: {dwall*1e6/T:.1f} us/step wall, kernel {k_ms*1e3:.1f} us, {d_gbs:.0f} GB/s")
+        del sq, sk, sv, S, z, y
+
+    # ---------------- CPU oracle baseline ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        nh = max(1, min(args.cpu_heads, H))
+        qc, kc, vc = la_inputs.gaussian_qkv(1, nh, N, d, seed=W["seed"] + 1, scale=W["scale"], bf16=True)
+        log(f"cpu baseline: oracle blockwise form on {nh} head(s) x {N} tokens")
+        t0 = time.perf_counter()
+        O.chunked(qc, kc, vc, "elu1", causal=True, normalize=True, chunk=64)
+        tc = time.perf_counter() - t0
+        cpu = {"value": (nh * N / H) / tc, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+               "sample": f"oracle.chunked (fp64) on {nh} of {H} heads x {N} tokens, d={d}; "
+                         f"tokens/s = B*N*(heads timed/H)/time", "seconds": round(tc, 2)}
+        if decode is not None:
+            Wd = la_inputs.WORKLOADS["decode_s256h32d64"]
+            heads = Wd["B"] * Wd["H"]
+            rng = np.random.default_rng(0)
+            Sd = rng.standard_normal((heads, Wd["d"], Wd["d"]))
+            zd = np.abs(rng.standard_normal((heads, Wd["d"]))) * 100
+            toks = [la_inputs.decode_tokens(Wd["step_seed"], t, (heads, Wd["d"]))
+                    for t in range(args.cpu_decode_steps)]
+            t0 = time.perf_counter()
+            for (tq_, tk_, tv_) in toks:
+                _, Sd, zd = O.decode_step(Sd, zd, tq_, tk_, tv_, "elu1")
+            td = time.perf_counter() - t0
+            cpu["decode"] = {"value": args.cpu_decode_steps / td, "unit": "steps/s",
+                             "sample": f"oracle.decode_step (fp64) over all {heads} heads, "
+                                       f"{args.cpu_decode_steps} steps"}
+
+    result = {
+        "metric": "causal linear-attn prefill tokens/s (N=64K,d=128) + decode steps/s, % roofline",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_b1h16n65536d128", "batch": B, "heads": H, "seq_len": N, "d": d,
+                   "feature_map": "elu1", "causal": True, "normalize": True, "chunk": C, "accumulate": "fp32"},
+        "roofline": {"bound": "hbm", "kernel": "output_pass_kernel", "achieved": round(out_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(out_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": alg_bytes, "avg_launch_us": round(ms_out * 1e3, 2)},
+        "prefill_breakdown_us": {"state_pass": round(ms_state * 1e3, 2), "carry_scan": round(ms_scan * 1e3, 2),
+                                 "output_pass": round(ms_out * 1e3, 2)},
+        "prefill_whole_op": {"achieved_gbs": round(whole_gbs, 1), "frac_hbm": round(whole_gbs / HBM_PEAK_GBS, 4),
+                             "useful_tflops": round(flops_useful / (ms_step * 1e-3) / 1e12, 2),
+                             "frac_bf16_mfma": round(flops_useful / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                                                     4),
+                             "head_tokens_per_s": head_tokens / (ms_step * 1e-3)},
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,276 @@
+// Host side of the C ABI declared in include/linattn.h: argument validation,
+// work planning (sequence segments, workspace carving) and kernel dispatch.
+// Nothing here allocates device memory or keeps state between calls.
+#include "linattn.h"
+
+#include <stdint.h>
+
+#include "la_kernels.h"
+
+namespace {
+
+constexpr int kChunk = 64;
+// Output/state passes aim for this many workgroups so that every compute unit
+// has work even when batch * heads is small (long single sequences).
+constexpr long long kTargetBlocks = 512;
+// A segment never gets fewer chunks than this (its carried state costs about
+// as much traffic as 64 tokens of q, k, v and out at d' = d).
+constexpr int kMinChunksPerSegment = 4;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, long long abytes, const void* b, long long bbytes) {
+  if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+bool d_supported(int d) { return d == 32 || d == 64 || d == 128; }
+
+// Feature dimension d' for a map, or a negative status.
+int feature_dim(const la_feature_map* fm, int d) {
+  if (!fm) return LA_ERR_INVALID_ARG;
+  if (fm->kind == LA_ELU1) return d;
+  if (fm->kind == LA_PERFORMER) {
+    if (fm->m <= 0 || !fm->W || !aligned16(fm->W)) return LA_ERR_INVALID_ARG;
+    return LA_ERR_UNSUPPORTED;
+  }
+  return LA_ERR_INVALID_ARG;
+}
+
+struct Plan {
+  int nchunks = 0;
+  int P = 1, cps = 0;        // output pass
+  int Ps = 0, cpss = 0;      // state pass
+  int ws_slots = 0;
+  bool state_pass = false, scan = false;
+  size_t ws_bytes = 0;
+};
+
+void split(int nchunks, long long BH, int& P, int& cps) {
+  long long want = (kTargetBlocks + BH - 1) / BH;
+  long long cap = nchunks / kMinChunksPerSegment;
+  if (cap < 1) cap = 1;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  cps = (int)((nchunks + want - 1) / want);
+  P = (nchunks + cps - 1) / cps;
+}
+
+Plan make_plan(long long BH, int N, int d, int dfeat, bool causal) {
+  Plan p;
+  p.nchunks = (N + kChunk - 1) / kChunk;
+  const size_t state_bytes = (size_t)(dfeat * d + dfeat) * sizeof(float);
+  if (N == 0 || BH == 0) return p;
+  split(p.nchunks, BH, p.P, p.cps);
+  if (causal) {
+    if (p.P > 1) {
+      p.Ps = p.P - 1;  // the last segment's local sums are never carried
+      p.cpss = p.cps;
+      p.ws_slots = p.P;
+      p.state_pass = true;
+      p.scan = true;
+    }
+  } else {
+    split(p.nchunks, BH, p.Ps, p.cpss);
+    p.ws_slots = p.Ps + 1;
+    p.state_pass = true;
+    p.scan = true;
+  }
+  p.ws_bytes = (size_t)BH * p.ws_slots * state_bytes;
+  return p;
+}
+
+int status_from_hip(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int la_version(void) { return (0 << 16) | 1; }
+
+const char* la_status_string(int status) {
+  switch (status) {
+    case LA_OK: return "ok";
+    case LA_ERR_INVALID_ARG: return "invalid argument";
+    case LA_ERR_UNSUPPORTED: return "unsupported shape or feature map";
+    case LA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t la_forward_workspace_size(int B, int H, int N, int d, const la_feature_map* feature_map, int causal) {
+  if (B < 0 || H < 0 || N < 0 || !d_supported(d)) return 0;
+  const int dfeat = feature_dim(feature_map, d);
+  if (dfeat <= 0) return 0;
+  return make_plan((long long)B * H, N, d, dfeat, causal != 0).ws_bytes;
+}
+
+int la_forward_ex(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+                  const la_feature_map* feature_map, int causal, int normalize, int dtype, const float* S_in,
+                  const float* z_in, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream, hipEvent_t* events) {
+  if (B < 0 || H < 0 || N < 0) return LA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return LA_ERR_INVALID_ARG;
+  if (normalize != 0 && normalize != 1) return LA_ERR_INVALID_ARG;
+  if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
+  if ((S_in == nullptr) != (z_in == nullptr)) return LA_ERR_INVALID_ARG;
+  if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_INVALID_ARG;
+  if (!d_supported(d)) return LA_ERR_UNSUPPORTED;
+  const int dfeat = feature_dim(feature_map, d);
+  if (dfeat < 0) return dfeat;
+  const long long BH = (long long)B * H;
+  if (BH > (1LL << 31) - 1) return LA_ERR_UNSUPPORTED;
+  const long long esz = dtype == LA_BF16 ? 2 : 4;
+  const long long tok_bytes = BH * N * d * esz;
+  const long long s_bytes = BH * dfeat * d * 4, z_bytes = BH * dfeat * 4;
+  if (S_in && (!aligned16(S_in) || !aligned16(z_in))) return LA_ERR_INVALID_ARG;
+  if (S_out && (!aligned16(S_out) || !aligned16(z_out))) return LA_ERR_INVALID_ARG;
+  if (S_out && (overlaps(S_out, s_bytes, z_out, z_bytes) || overlaps(S_out, s_bytes, S_in, s_bytes) ||
+                overlaps(S_out, s_bytes, z_in, z_bytes) || overlaps(z_out, z_bytes, S_in, s_bytes) ||
+                overlaps(z_out, z_bytes, z_in, z_bytes)))
+    return LA_ERR_INVALID_ARG;
+
+  if (BH == 0) return LA_OK;
+  if (N == 0) {
+    if (!S_out) return LA_OK;
+    return status_from_hip(la::copy_state_dispatch(S_in, z_in, S_out, z_out, s_bytes / 4, z_bytes / 4, stream));
+  }
+  if (!q || !k || !v || !out) return LA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_INVALID_ARG;
+  if (overlaps(out, tok_bytes, q, tok_bytes) || overlaps(out, tok_bytes, k, tok_bytes) ||
+      overlaps(out, tok_bytes, v, tok_bytes))
+    return LA_ERR_INVALID_ARG;
+  if (S_out && (overlaps(S_out, s_bytes, q, tok_bytes) || overlaps(S_out, s_bytes, k, tok_bytes) ||
+                overlaps(S_out, s_bytes, v, tok_bytes) || overlaps(S_out, s_bytes, out, tok_bytes) ||
+                overlaps(z_out, z_bytes, q, tok_bytes) || overlaps(z_out, z_bytes, k, tok_bytes) ||
+                overlaps(z_out, z_bytes, v, tok_bytes) || overlaps(z_out, z_bytes, out, tok_bytes)))
+    return LA_ERR_INVALID_ARG;
+
+  const Plan p = make_plan(BH, N, d, dfeat, causal != 0);
+  if (p.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < p.ws_bytes) return LA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LA_ERR_INVALID_ARG;
+    if (overlaps(workspace, (long long)p.ws_bytes, out, tok_bytes) ||
+        overlaps(workspace, (long long)p.ws_bytes, q, tok_bytes) ||
+        overlaps(workspace, (long long)p.ws_bytes, k, tok_bytes) ||
+        overlaps(workspace, (long long)p.ws_bytes, v, tok_bytes) ||
+        overlaps(workspace, (long long)p.ws_bytes, S_out, s_bytes) ||
+        overlaps(workspace, (long long)p.ws_bytes, S_in, s_bytes))
+      return LA_ERR_INVALID_ARG;
+  }
+
+  la::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.BH = (int)BH;
+  a.N = N;
+  a.nchunks = p.nchunks;
+  a.nseg = p.P;
+  a.chunks_per_seg = p.cps;
+  a.nseg_state = p.Ps;
+  a.chunks_per_seg_state = p.cpss;
+  a.run_state_pass = p.state_pass;
+  a.run_scan = p.scan;
+  a.ws = static_cast<float*>(workspace);
+  a.ws_slots = p.ws_slots;
+  a.ws_total_slot = causal ? 0 : p.Ps;
+  a.state_elems = dfeat * d + dfeat;
+  a.init_from_ws = p.ws_slots > 0;
+  a.S_in = S_in;
+  a.z_in = z_in;
+  a.S_out = causal ? S_out : nullptr;
+  a.z_out = causal ? z_out : nullptr;
+  a.normalize = normalize;
+  a.W = feature_map->W;
+
+  la::ScanArgs s{};
+  s.ws = a.ws;
+  s.ws_slots = p.ws_slots;
+  s.state_elems = a.state_elems;
+  s.BH = (int)BH;
+  s.DF = dfeat;
+  s.D = d;
+  s.S_in = S_in;
+  s.z_in = z_in;
+  if (causal) {
+    s.P = p.P - 1;
+    s.exclusive = 1;
+    s.write_total = 1;  // prefix of the last segment
+  } else {
+    s.P = p.Ps;
+    s.exclusive = 0;
+    s.write_total = 1;
+    s.S_out = S_out;
+    s.z_out = z_out;
+  }
+  return status_from_hip(la::prefill_dispatch(a, s, d, dfeat, feature_map->kind, dtype, causal != 0, stream,
+                                              events));
+}
+
+int la_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+               const la_feature_map* feature_map, int causal, int normalize, int dtype, const float* S_in,
+               const float* z_in, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
+               hipStream_t stream) {
+  return la_forward_ex(q, k, v, out, B, H, N, d, feature_map, causal, normalize, dtype, S_in, z_in, S_out, z_out,
+                       workspace, workspace_bytes, stream, nullptr);
+}
+
+int la_decode_step(float* S, float* z, const void* q, const void* k, const void* v, void* out, int B, int H,
+                   int d, const la_feature_map* feature_map, int normalize, int dtype, hipStream_t stream) {
+  if (B < 0 || H < 0) return LA_ERR_INVALID_ARG;
+  if (normalize != 0 && normalize != 1) return LA_ERR_INVALID_ARG;
+  if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
+  if (!d_supported(d)) return LA_ERR_UNSUPPORTED;
+  const int dfeat = feature_dim(feature_map, d);
+  if (dfeat < 0) return dfeat;
+  const long long BH = (long long)B * H;
+  if (BH == 0) return LA_OK;
+  if (BH > (1LL << 31) - 1) return LA_ERR_UNSUPPORTED;
+  if (!S || !z || !q || !k || !v || !out) return LA_ERR_INVALID_ARG;
+  if (!aligned16(S) || !aligned16(z) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return LA_ERR_INVALID_ARG;
+  const long long esz = dtype == LA_BF16 ? 2 : 4;
+  const long long tb = BH * d * esz, sb = BH * dfeat * d * 4, zb = BH * dfeat * 4;
+  if (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb) || overlaps(out, tb, S, sb) ||
+      overlaps(out, tb, z, zb) || overlaps(S, sb, z, zb) || overlaps(S, sb, q, tb) || overlaps(S, sb, k, tb) ||
+      overlaps(S, sb, v, tb) || overlaps(z, zb, q, tb) || overlaps(z, zb, k, tb) || overlaps(z, zb, v, tb))
+    return LA_ERR_INVALID_ARG;
+  la::DecodeArgs a{};
+  a.S = S;
+  a.z = z;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.BH = (int)BH;
+  a.normalize = normalize;
+  a.W = feature_map->W;
+  return status_from_hip(la::decode_dispatch(a, d, dfeat, feature_map->kind, dtype, stream));
+}
+
+int la_feature_map_apply(const void* x, void* phi, long long rows, int d, const la_feature_map* feature_map,
+                         int in_dtype, int out_dtype, hipStream_t stream) {
+  if (rows < 0) return LA_ERR_INVALID_ARG;
+  if ((in_dtype != LA_F32 && in_dtype != LA_BF16) || (out_dtype != LA_F32 && out_dtype != LA_BF16))
+    return LA_ERR_INVALID_ARG;
+  if (!d_supported(d)) return LA_ERR_UNSUPPORTED;
+  const int dfeat = feature_dim(feature_map, d);
+  if (dfeat < 0) return dfeat;
+  if (rows == 0) return LA_OK;
+  if (!x || !phi || !aligned16(x) || !aligned16(phi)) return LA_ERR_INVALID_ARG;
+  const long long xb = rows * d * (in_dtype == LA_BF16 ? 2 : 4);
+  const long long pb = rows * dfeat * (out_dtype == LA_BF16 ? 2 : 4);
+  if (overlaps(x, xb, phi, pb)) return LA_ERR_INVALID_ARG;
+  la::FmapArgs a{};
+  a.x = x;
+  a.phi = phi;
+  a.rows = rows;
+  a.W = feature_map->W;
+  return status_from_hip(la::fmap_dispatch(a, d, dfeat, feature_map->kind, in_dtype, out_dtype, stream));
+}
+
+}  // extern "C"

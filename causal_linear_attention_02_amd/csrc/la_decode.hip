@@ -1,0 +1,188 @@
+// Recurrent decode step of kernelized linear attention on gfx950.
+//
+// One new token per (batch, head) ("Linear Attention", marovi.ai, "Forma
+// recurrente e inferencia autorregresiva"; "Linear Transformer (Transformers
+// are RNNs)", "La formulación recurrente paso a paso"):
+//   S <- S + phi(k) v^T,  z <- z + phi(k),  y = phi(q)^T S / phi(q).z
+// (the state is updated first, so the new token attends to itself).
+//
+// The step is a pure stream over the fp32 state: every state element is read
+// once and written once. Each head's DF x D state is covered by TPH threads,
+// each owning a 4-column group (one 16-byte vector) of DF/R rows, so one load
+// instruction of a head covers R consecutive rows = TPH * 16 contiguous
+// bytes. All state loads are issued before any arithmetic.
+#include "la_device.h"
+#include "la_kernels.h"
+
+namespace la {
+
+template <int D, int DF>
+struct DecodeShape {
+  static constexpr int TPH = (DF * D / 64 > 64) ? DF * D / 64 : 64;  // threads per head
+  static constexpr int HPB = 256 / TPH;                               // heads per block
+  static constexpr int CG = D / 4;                                    // 16-byte column groups
+  static constexpr int R = TPH / CG;                                  // row groups
+  static constexpr int RPT = DF / R;                                  // rows per thread
+  static constexpr int WPH = TPH / 64;                                // waves per head
+  static_assert(TPH % CG == 0 && DF % R == 0, "decode tiling");
+};
+
+template <typename IN> __device__ __forceinline__ float load_elem(const void* p, long long i);
+template <> __device__ __forceinline__ float load_elem<__bf16>(const void* p, long long i) {
+  return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+template <> __device__ __forceinline__ float load_elem<float>(const void* p, long long i) {
+  return static_cast<const float*>(p)[i];
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+template <int D, int DF, typename IN>
+__global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
+  using SH = DecodeShape<D, DF>;
+  __shared__ float s_phiq[SH::HPB][DF];
+  __shared__ float s_phik[SH::HPB][DF];
+  __shared__ float s_v[SH::HPB][D];
+  __shared__ f32x4 s_num[SH::HPB][SH::R][SH::CG];
+  __shared__ float s_den[SH::HPB][SH::WPH];
+
+  const int hb = threadIdx.x / SH::TPH;      // head within block
+  const int t = threadIdx.x % SH::TPH;       // thread within head
+  const long long head = (long long)blockIdx.x * SH::HPB + hb;
+  const bool valid = head < a.BH;
+  const int cg = t % SH::CG, rg = t / SH::CG;
+
+  // state loads first (the bulk of the traffic)
+  float* Sh = a.S + head * (DF * D);
+  f32x4 Sv[SH::RPT];
+  if (valid) {
+#pragma unroll
+    for (int i = 0; i < SH::RPT; ++i)
+      Sv[i] = *reinterpret_cast<const f32x4*>(Sh + (long long)(rg + SH::R * i) * D + 4 * cg);
+  }
+  // token features
+  if (valid) {
+    for (int e = t; e < D; e += SH::TPH) {
+      const long long off = head * D + e;
+      s_phiq[hb][e] = phi_elu1(load_elem<IN>(a.q, off));
+      s_phik[hb][e] = phi_elu1(load_elem<IN>(a.k, off));
+      s_v[hb][e] = load_elem<IN>(a.v, off);
+    }
+  }
+  __syncthreads();
+
+  // z <- z + phi(k); partial phi(q).z
+  float dpart = 0.f;
+  if (valid) {
+    for (int c = t; c < DF; c += SH::TPH) {
+      const float zn = a.z[head * DF + c] + s_phik[hb][c];
+      a.z[head * DF + c] = zn;
+      dpart += s_phiq[hb][c] * zn;
+    }
+  }
+  dpart = wave_sum(dpart);
+  if ((t & 63) == 0) s_den[hb][t >> 6] = dpart;
+
+  // S <- S + phi(k) v^T; numerator phi(q)^T S over this thread's rows
+  const f32x4 v4 = valid ? *reinterpret_cast<const f32x4*>(&s_v[hb][4 * cg]) : f32x4{0, 0, 0, 0};
+  f32x4 num = {0, 0, 0, 0};
+  if (valid) {
+#pragma unroll
+    for (int i = 0; i < SH::RPT; ++i) {
+      const int r = rg + SH::R * i;
+      const float pk = s_phik[hb][r], pq = s_phiq[hb][r];
+      f32x4 s = Sv[i];
+      s[0] += pk * v4[0];
+      s[1] += pk * v4[1];
+      s[2] += pk * v4[2];
+      s[3] += pk * v4[3];
+      *reinterpret_cast<f32x4*>(Sh + (long long)r * D + 4 * cg) = s;
+      num[0] += pq * s[0];
+      num[1] += pq * s[1];
+      num[2] += pq * s[2];
+      num[3] += pq * s[3];
+    }
+  }
+  s_num[hb][rg][cg] = num;
+  __syncthreads();
+
+  if (valid && rg == 0) {
+    f32x4 acc = s_num[hb][0][cg];
+#pragma unroll
+    for (int g = 1; g < SH::R; ++g) {
+      const f32x4 o = s_num[hb][g][cg];
+      acc[0] += o[0];
+      acc[1] += o[1];
+      acc[2] += o[2];
+      acc[3] += o[3];
+    }
+    float inv = 1.f;
+    if (a.normalize) {
+      float den = 0.f;
+#pragma unroll
+      for (int wv = 0; wv < SH::WPH; ++wv) den += s_den[hb][wv];
+      inv = 1.f / fmaxf(den, kEps);
+    }
+    const long long off = head * D + 4 * cg;
+    if constexpr (sizeof(IN) == 2) {
+      uint32_t* o = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + off);
+      o[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+      o[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + off) =
+          f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    }
+  }
+}
+
+template <int D, int DF, typename IN>
+static hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+  using SH = DecodeShape<D, DF>;
+  const int blocks = (a.BH + SH::HPB - 1) / SH::HPB;
+  hipLaunchKernelGGL((decode_step_kernel<D, DF, IN>), dim3(blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t decode_dispatch(const DecodeArgs& a, int D, int DF, int fmap, int dtype, hipStream_t st) {
+  if (fmap != kElu1) return hipErrorInvalidValue;
+  (void)DF;
+  if (dtype == 1) {
+    switch (D) {
+      case 32: return launch_decode<32, 32, __bf16>(a, st);
+      case 64: return launch_decode<64, 64, __bf16>(a, st);
+      case 128: return launch_decode<128, 128, __bf16>(a, st);
+    }
+  } else {
+    switch (D) {
+      case 32: return launch_decode<32, 32, float>(a, st);
+      case 64: return launch_decode<64, 64, float>(a, st);
+      case 128: return launch_decode<128, 128, float>(a, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Plain state copy (N = 0 forward with a state hand-off): S_out <- S_in or 0.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void copy_state_kernel(const float* S_in, const float* z_in, float* S_out,
+                                                         float* z_out, long long nS, long long nz) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < nS && S_out) S_out[i] = S_in ? S_in[i] : 0.f;
+  if (i < nz && z_out) z_out[i] = z_in ? z_in[i] : 0.f;
+}
+
+hipError_t copy_state_dispatch(const float* S_in, const float* z_in, float* S_out, float* z_out, long long nS,
+                               long long nz, hipStream_t st) {
+  const long long n = nS > nz ? nS : nz;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, S_in, z_in, S_out,
+                     z_out, nS, nz);
+  return hipGetLastError();
+}
+
+}  // namespace la

@@ -1,0 +1,78 @@
+// Kernel argument blocks and launch entry points shared by the host API
+// (la_api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace la {
+
+// Chunked forward (prefill / non-causal). All pointers are device pointers.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  int BH;                  // batch * heads
+  int N;                   // tokens per sequence
+  int nchunks;             // ceil(N / 64)
+  int nseg;                // output-pass segments per sequence
+  int chunks_per_seg;      // output-pass chunks per segment
+  int nseg_state;          // state-pass segments per sequence
+  int chunks_per_seg_state;
+  int run_state_pass;
+  int run_scan;
+  float* ws;               // workspace: [BH][ws_slots][state_elems] fp32
+  int ws_slots;
+  int ws_total_slot;       // non-causal: slot holding the full-sequence state
+  int state_elems;         // DF * D + DF
+  int init_from_ws;        // output pass starts from the workspace slot (else S_in/z_in or zero)
+  const float* S_in;       // [BH][DF][D] or null
+  const float* z_in;       // [BH][DF] or null
+  float* S_out;            // [BH][DF][D] or null (causal: written by the last segment)
+  float* z_out;
+  int normalize;
+  const float* W;          // random-feature projection [DF][D] (fp32) or null
+};
+
+struct ScanArgs {
+  float* ws;
+  int ws_slots;
+  int state_elems;
+  int BH;
+  int P;            // number of local states to combine (slots 0..P-1)
+  int DF, D;
+  int exclusive;    // rewrite slots 0..P-1 with exclusive prefixes
+  int write_total;  // write the sum into slot P
+  const float* S_in;
+  const float* z_in;
+  float* S_out;     // total state (non-causal only)
+  float* z_out;
+};
+
+struct DecodeArgs {
+  float* S;         // [BH][DF][D], updated in place
+  float* z;         // [BH][DF], updated in place
+  const void* q;    // [BH][D]
+  const void* k;
+  const void* v;
+  void* out;        // [BH][D]
+  int BH;
+  int normalize;
+  const float* W;   // [DF][D] or null
+};
+
+struct FmapArgs {
+  const void* x;    // [rows][D]
+  void* phi;        // [rows][DF]
+  long long rows;
+  const float* W;   // [DF][D] or null
+};
+
+hipError_t prefill_dispatch(const FwdArgs& a, const ScanArgs& s, int D, int DF, int fmap, int dtype, bool causal,
+                            hipStream_t st, hipEvent_t* ev);
+hipError_t decode_dispatch(const DecodeArgs& a, int D, int DF, int fmap, int dtype, hipStream_t st);
+hipError_t fmap_dispatch(const FmapArgs& a, int D, int DF, int fmap, int in_dtype, int out_dtype, hipStream_t st);
+hipError_t copy_state_dispatch(const float* S_in, const float* z_in, float* S_out, float* z_out, long long nS,
+                               long long nz, hipStream_t st);
+
+}  // namespace la

@@ -1,0 +1,139 @@
+/*
+ * linattn.h - C ABI of the kernelized (linear) attention library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed (pages on linear attention):
+ *   "Linear Attention" (marovi.ai), "Reformulación con núcleos":
+ *       y_i = phi(q_i)^T S / phi(q_i)^T z,
+ *       S = sum_j phi(k_j) v_j^T  (d' x d),  z = sum_j phi(k_j)  (d')
+ *   causal form ("Forma recurrente e inferencia autorregresiva"): the sums run
+ *       over j <= i, the current token included;
+ *   blockwise evaluation ("Entrenamiento: forma paralela");
+ *   the denominator may be omitted (same section as the definition; the
+ *       "Linear Attention" glossary of ultralytics.com, "Ejemplo de código");
+ *   phi = elu(x) + 1 ("Linear Transformer (Transformers are RNNs)",
+ *       "La función ELU + 1"), d' = d;
+ *   phi = positive random features ("Linear Attention", "Mapas de
+ *       características"): phi(x) = exp(W x~ - |x~|^2/2) / sqrt(m),
+ *       x~ = d^(-1/4) x, W of shape m x d, d' = m.
+ * With normalization on, y = num / max(den, 1e-6).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, contiguous, row-major, 16-byte
+ *     aligned. q, k, v, out: [B][H][N][d]. State S: [B][H][d'][d] fp32 (row =
+ *     feature index, column = value index). Normalizer z: [B][H][d'] fp32.
+ *   - Element type of q, k, v and out: LA_BF16 or LA_F32 (same for all four).
+ *     bf16 inputs are multiplied on bf16 matrix cores with fp32 accumulation;
+ *     fp32 inputs use fp32 matrix cores. State is always fp32.
+ *   - Supported: d in {32, 64, 128}.
+ *   - Ownership: the caller allocates and frees every buffer. The library
+ *     keeps no pointer after returning and allocates no device memory.
+ *   - Errors: validation happens before anything is enqueued, so a failed
+ *     call has no side effect. Return value LA_OK (0) or a negative LA_ERR_*.
+ *     On LA_OK the work is enqueued on `stream` (asynchronous); faults of the
+ *     device work surface at the caller's next synchronization.
+ *   - Thread safety: calls on different streams may run concurrently.
+ */
+#ifndef LINATTN_H_
+#define LINATTN_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes */
+#define LA_OK 0
+#define LA_ERR_INVALID_ARG (-1)  /* null/misaligned pointer, bad size, overlapping output, bad flag */
+#define LA_ERR_UNSUPPORTED (-2)  /* valid request outside the supported shapes/maps */
+#define LA_ERR_WORKSPACE (-3)    /* workspace null or smaller than la_forward_workspace_size() */
+#define LA_ERR_HIP (-4)          /* the HIP runtime rejected a launch */
+
+/* Element types */
+#define LA_F32 0
+#define LA_BF16 1
+
+/* Feature maps */
+#define LA_ELU1 0      /* elu(x) + 1, d' = d */
+#define LA_PERFORMER 1 /* positive random features, d' = m */
+
+typedef struct la_feature_map {
+  int kind;        /* LA_ELU1 or LA_PERFORMER */
+  int m;           /* LA_PERFORMER: number of features (d'); ignored for LA_ELU1 */
+  const float* W;  /* LA_PERFORMER: device pointer, m x d fp32 row-major, shared by all
+                      batches and heads; bf16 inputs use W rounded to bf16. NULL for LA_ELU1 */
+} la_feature_map;
+
+/* Library version, (major << 16) | minor. */
+int la_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* la_status_string(int status);
+
+/*
+ * Bytes of fp32 device workspace that la_forward needs for these sizes
+ * (0 when none is needed). Returns 0 also for invalid arguments.
+ */
+size_t la_forward_workspace_size(int B, int H, int N, int d, const la_feature_map* feature_map, int causal);
+
+/*
+ * Linear attention over whole sequences ("Reformulación con núcleos"; causal:
+ * "Forma recurrente ..." evaluated blockwise as in "Entrenamiento: forma
+ * paralela").
+ *   q, k, v   in:  [B][H][N][d], element type `dtype`.
+ *   out       out: [B][H][N][d], element type `dtype`; must not overlap any input.
+ *   causal    1: sums over j <= i;  0: sums over all j.
+ *   normalize 1: divide by the denominator;  0: numerator only.
+ *   S_in,z_in optional (both or neither): state of earlier tokens, added to
+ *             the sums of every position (split/resume of a sequence).
+ *   S_out,z_out optional (both or neither): state after the last token,
+ *             S_in + sum_j phi(k_j) v_j^T and z_in + sum_j phi(k_j) (the
+ *             hand-off to la_decode_step).
+ *   workspace device scratch of at least la_forward_workspace_size() bytes,
+ *             256-byte aligned (may be NULL when that size is 0). Its contents
+ *             are overwritten.
+ * N = 0 writes only S_out/z_out (= S_in/z_in, or zeros).
+ */
+int la_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+               const la_feature_map* feature_map, int causal, int normalize, int dtype, const float* S_in,
+               const float* z_in, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
+               hipStream_t stream);
+
+/*
+ * la_forward, plus timing markers: when `events` is not NULL it points to 4
+ * caller-created HIP events that are recorded on `stream` before the state
+ * pass, before the carry scan, before the output pass and after the output
+ * pass (a skipped pass has zero length).
+ */
+int la_forward_ex(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+                  const la_feature_map* feature_map, int causal, int normalize, int dtype, const float* S_in,
+                  const float* z_in, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream, hipEvent_t* events);
+
+/*
+ * One recurrent decode step for every (batch, head) ("Forma recurrente e
+ * inferencia autorregresiva"; "La formulación recurrente paso a paso"):
+ *   S <- S + phi(k) v^T,  z <- z + phi(k),  out = phi(q)^T S / max(phi(q).z, 1e-6)
+ * (state updated first; normalize = 0 drops the division).
+ *   S, z      in/out: [B][H][d'][d], [B][H][d'] fp32, updated in place.
+ *   q, k, v   in:  [B][H][d] (one token per head), element type `dtype`.
+ *   out       out: [B][H][d]; must not overlap q, k, v, S or z.
+ */
+int la_decode_step(float* S, float* z, const void* q, const void* k, const void* v, void* out, int B, int H,
+                   int d, const la_feature_map* feature_map, int normalize, int dtype, hipStream_t stream);
+
+/*
+ * The feature map alone ("Mapas de características"): phi applied to each row.
+ *   x    in:  [rows][d], element type in_dtype.
+ *   phi  out: [rows][d'], element type out_dtype; must not overlap x.
+ */
+int la_feature_map_apply(const void* x, void* phi, long long rows, int d, const la_feature_map* feature_map,
+                         int in_dtype, int out_dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H_ */

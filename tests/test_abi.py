@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+function, and rejects bad arguments before enqueuing anything."""
+
+import ctypes
+
+import pytest
+
+import causal_linear_attention_02_amd as la
+from causal_linear_attention_02_amd import lib, la_feature_map
+
+FAKE = 0x10000          # 16-byte aligned address that is never dereferenced
+FAKE2 = 0x40000000
+ELU = la_feature_map(la.LA_ELU1, 0, None)
+
+
+def test_library_exports_every_declared_function():
+    names = la.declared_functions()
+    assert {"la_forward", "la_forward_ex", "la_decode_step", "la_feature_map_apply",
+            "la_forward_workspace_size", "la_status_string", "la_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    for code in (la.LA_OK, la.LA_ERR_INVALID_ARG, la.LA_ERR_UNSUPPORTED, la.LA_ERR_WORKSPACE, la.LA_ERR_HIP, 7):
+        s = la.la_status_string(code)
+        assert isinstance(s, str) and s
+    assert la.la_version() > 0
+
+
+def _fwd(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, out=FAKE2, B=1, H=1, N=128, d=64, fm=ELU, causal=1,
+         normalize=1, dtype=la.LA_BF16, S_in=None, z_in=None, S_out=None, z_out=None, ws=None, ws_bytes=0):
+    return lib.la_forward(q, k, v, out, B, H, N, d, ctypes.byref(fm) if fm is not None else None, causal,
+                          normalize, dtype, S_in, z_in, S_out, z_out, ws, ws_bytes, None)
+
+
+def test_forward_rejects_bad_arguments():
+    assert _fwd(B=-1) == la.LA_ERR_INVALID_ARG
+    assert _fwd(N=-5) == la.LA_ERR_INVALID_ARG
+    assert _fwd(causal=2) == la.LA_ERR_INVALID_ARG
+    assert _fwd(normalize=-1) == la.LA_ERR_INVALID_ARG
+    assert _fwd(dtype=5) == la.LA_ERR_INVALID_ARG
+    assert _fwd(fm=None) == la.LA_ERR_INVALID_ARG
+    assert _fwd(fm=la_feature_map(9, 0, None)) == la.LA_ERR_INVALID_ARG
+    assert _fwd(d=48) == la.LA_ERR_UNSUPPORTED
+    assert _fwd(d=256) == la.LA_ERR_UNSUPPORTED
+    assert _fwd(q=None) == la.LA_ERR_INVALID_ARG
+    assert _fwd(out=None) == la.LA_ERR_INVALID_ARG
+    assert _fwd(q=FAKE + 2) == la.LA_ERR_INVALID_ARG               # misaligned
+    assert _fwd(out=FAKE + 64) == la.LA_ERR_INVALID_ARG            # out overlaps q
+    assert _fwd(S_in=FAKE2 + 0x100000) == la.LA_ERR_INVALID_ARG    # S_in without z_in
+    assert _fwd(S_out=FAKE2 + 0x100000) == la.LA_ERR_INVALID_ARG   # S_out without z_out
+    # S_out overlapping the output
+    assert _fwd(S_out=FAKE2 + 256, z_out=FAKE2 + 0x200000) == la.LA_ERR_INVALID_ARG
+    # performer map without W
+    assert _fwd(fm=la_feature_map(la.LA_PERFORMER, 64, None)) == la.LA_ERR_INVALID_ARG
+
+
+def test_forward_workspace_checks():
+    # a long single sequence is split into segments and needs workspace
+    need = lib.la_forward_workspace_size(1, 1, 65536, 128, ctypes.byref(ELU), 1)
+    assert need > 0
+    assert _fwd(N=65536, d=128) == la.LA_ERR_WORKSPACE
+    assert _fwd(N=65536, d=128, ws=FAKE2 * 2, ws_bytes=need - 4) == la.LA_ERR_WORKSPACE
+    assert _fwd(N=65536, d=128, ws=FAKE2 * 2 + 16, ws_bytes=need) == la.LA_ERR_INVALID_ARG  # not 256-aligned
+    # workspace overlapping the output buffer
+    assert _fwd(N=65536, d=128, ws=FAKE2, ws_bytes=need) == la.LA_ERR_INVALID_ARG
+
+
+def test_empty_problems_are_noops():
+    assert _fwd(B=0) == la.LA_OK
+    assert _fwd(H=0, q=None, k=None, v=None, out=None) == la.LA_OK
+    assert lib.la_decode_step(None, None, None, None, None, None, 0, 4, 64, ctypes.byref(ELU), 1, 1, None) == la.LA_OK
+    assert lib.la_feature_map_apply(None, None, 0, 64, ctypes.byref(ELU), 1, 1, None) == la.LA_OK
+
+
+def test_workspace_size_plan():
+    ws = lambda B, H, N, d, c: lib.la_forward_workspace_size(B, H, N, d, ctypes.byref(ELU), c)
+    st = lambda d: (d * d + d) * 4
+    # one chunk per sequence: nothing to carry (causal), one total slot (non-causal)
+    assert ws(4, 8, 64, 64, 1) == 0
+    assert ws(4, 8, 64, 64, 0) == 32 * 2 * st(64)
+    # many sequences: one segment each, no causal workspace
+    assert ws(256, 32, 4096, 64, 1) == 0
+    # invalid requests report 0
+    assert ws(1, 1, 100, 48, 1) == 0
+    assert ws(-1, 1, 100, 64, 1) == 0
+    # long sequence: several segments, workspace grows with the state size
+    a, b = ws(1, 16, 65536, 64, 1), ws(1, 16, 65536, 128, 1)
+    assert a > 0 and b > 0 and b % st(128) == 0 and a % st(64) == 0
+    assert b // st(128) == a // st(64)
+
+
+def test_decode_rejects_bad_arguments():
+    dec = lambda **kw: lib.la_decode_step(kw.get("S", FAKE), kw.get("z", FAKE + 0x1000000),
+                                          kw.get("q", FAKE + 0x2000000), kw.get("k", FAKE + 0x3000000),
+                                          kw.get("v", FAKE + 0x4000000), kw.get("out", FAKE + 0x5000000),
+                                          kw.get("B", 2), kw.get("H", 2), kw.get("d", 64),
+                                          ctypes.byref(kw.get("fm", ELU)), kw.get("normalize", 1),
+                                          kw.get("dtype", 1), None)
+    assert dec(B=-1) == la.LA_ERR_INVALID_ARG
+    assert dec(d=96) == la.LA_ERR_UNSUPPORTED
+    assert dec(S=None) == la.LA_ERR_INVALID_ARG
+    assert dec(out=FAKE + 0x2000000) == la.LA_ERR_INVALID_ARG   # out == q
+    assert dec(z=FAKE + 64) == la.LA_ERR_INVALID_ARG             # z inside S
+    assert dec(q=FAKE + 0x2000008) == la.LA_ERR_INVALID_ARG      # misaligned
+    assert dec(normalize=3) == la.LA_ERR_INVALID_ARG
+    assert dec(dtype=2) == la.LA_ERR_INVALID_ARG
+
+
+def test_feature_map_apply_rejects_bad_arguments():
+    fa = lambda **kw: lib.la_feature_map_apply(kw.get("x", FAKE), kw.get("phi", FAKE2), kw.get("rows", 10),
+                                               kw.get("d", 64), ctypes.byref(kw.get("fm", ELU)),
+                                               kw.get("i", 1), kw.get("o", 1), None)
+    assert fa(rows=-1) == la.LA_ERR_INVALID_ARG
+    assert fa(d=40) == la.LA_ERR_UNSUPPORTED
+    assert fa(x=None) == la.LA_ERR_INVALID_ARG
+    assert fa(phi=FAKE + 32) == la.LA_ERR_INVALID_ARG            # overlap
+    assert fa(i=3) == la.LA_ERR_INVALID_ARG
+
+
+def test_binding_maps_errors_to_exceptions():
+    import torch
+    q = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):          # host tensors are refused, nothing is called
+        la.la_forward(q, q.clone(), q.clone())
+    with pytest.raises(NotImplementedError):
+        la._check(la.LA_ERR_UNSUPPORTED, "x")
+    with pytest.raises(ValueError):
+        la._check(la.LA_ERR_WORKSPACE, "x")
+    with pytest.raises(la.LinAttnError):
+        la._check(la.LA_ERR_HIP, "x")
+    la._check(la.LA_OK, "x")
