@@ -49,6 +49,21 @@ __device__ __forceinline__ float round_bf16(float a) {
   return bf16_bits_to_f32(pack_bf16x2(a, 0.f) & 0xffffu);
 }
 
+// ---------------------------------------------------------------------------
+// Raw buffer access: a wave-uniform descriptor (base, size in bytes) and a
+// per-lane 32-bit byte offset. Loads past `bytes` return zero and stores past
+// it are dropped by the hardware range check.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, int voff, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 0);
+}
+
 // 8 consecutive input elements -> fp32
 template <typename IN> struct In8;
 template <> struct In8<__bf16> {
@@ -61,7 +76,9 @@ template <> struct In8<__bf16> {
     }
   }
   __device__ static raw load(const void* p) { return *reinterpret_cast<const raw*>(p); }
+  __device__ static raw bload(__amdgpu_buffer_rsrc_t r, int voff) { return buf_load16(r, voff); }
   __device__ static raw zero() { return raw{0, 0, 0, 0}; }
+  __device__ static raw neg_inf() { return raw{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u}; }
 };
 template <> struct In8<float> {
   struct raw { f32x4 a, b; };  // 32 bytes
@@ -73,14 +90,27 @@ template <> struct In8<float> {
     const f32x4* q = reinterpret_cast<const f32x4*>(p);
     return raw{q[0], q[1]};
   }
+  __device__ static raw bload(__amdgpu_buffer_rsrc_t r, int voff) {
+    return raw{__builtin_bit_cast(f32x4, buf_load16(r, voff)), __builtin_bit_cast(f32x4, buf_load16(r, voff + 16))};
+  }
   __device__ static raw zero() { return raw{f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}}; }
+  __device__ static raw neg_inf() {
+    const float n = -__builtin_inff();
+    return raw{f32x4{n, n, n, n}, f32x4{n, n, n, n}};
+  }
 };
 
 // ---------------------------------------------------------------------------
 // Feature maps (fp32 math)
 // ---------------------------------------------------------------------------
 // elu(x) + 1 with alpha = 1: x + 1 for x > 0, exp(x) for x <= 0.
-__device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+// Written as max(x, 0) + min(exp(x), 1): for x > 0 that is x + 1, for x <= 0
+// it is exp(x). The min is the clamp output modifier of the hardware exp2 and
+// the max is the NaN-propagating maximum, so NaN stays NaN and exp(-inf) = 0.
+__device__ __forceinline__ float phi_elu1(float x) {
+  const float e = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(x * 1.4426950408889634f), 0.f, 1.f);
+  return __builtin_elementwise_maximum(x, 0.f) + e;
+}
 
 // ---------------------------------------------------------------------------
 // Swizzled LDS tiles. Rows of RB bytes; 16-byte units are permuted per row so
@@ -207,6 +237,9 @@ template <> struct Ops<float> {
     *reinterpret_cast<f32x4*>(tile + tile_off<RB>(row, k0 * 4 + 16)) = f32x4{x[4], x[5], x[6], x[7]};
   }
 };
+
+// s_waitcnt vmcnt(0): wait for every outstanding vector memory operation.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Exchange with the lane 32 positions away (l ^ 32).
 __device__ __forceinline__ float xor32(float x) {

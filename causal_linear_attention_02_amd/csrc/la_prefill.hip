@@ -15,188 +15,288 @@
 // The non-causal form reuses the state pass, a total-sum scan and the output
 // pass without the intra-chunk term.
 //
-// Wave w of a workgroup owns value columns [32w, 32w+32): it keeps the fp32
-// state S[:, 32w:32w+32] in MFMA accumulators and produces those output
-// columns. Layouts: q, k, v, out are [BH][N][D]; S is [BH][DF][D] (row c =
-// feature, column e = value dim); z is [BH][DF].
+// Output pass workgroup = D/32 consumer waves + D/32 producer waves (two per
+// SIMD at d = 128, so vector work and matrix work overlap):
+//   producers: global loads one chunk ahead (two register sets), the feature
+//     map, LDS staging, the running z (column sums of phi(K)) and the
+//     cross-chunk denominator phi(q_i).z of every row;
+//   consumers: consumer wave w owns value columns [32w, 32w+32) and keeps
+//     S[:, 32w:32w+32] in fp32 MFMA accumulators; it forms the masked scores,
+//     both numerator terms, normalizes, stores y and updates S.
+// Layouts: q, k, v, out are [BH][N][D]; S is [BH][DF][D] (row = feature,
+// column = value dim); z is [BH][DF].
 #include "la_device.h"
 #include "la_kernels.h"
 
 namespace la {
 
-// One chunk's worth of raw rows held in registers between issue and staging.
-template <int D, typename IN>
-struct Prefetch {
-  static constexpr int kPer = 4;  // 8-element pieces per thread per tensor (64*D/8 / (64*D/32))
-  typename In8<IN>::raw q[kPer], k[kPer], v[kPer];
+// ---------------------------------------------------------------------------
+// Staging geometry. NP = 2*D staging threads; thread p holds 8-element
+// pieces i = 0..3 of each tensor at row p/RL + 16 i, columns 8*(p % RL).
+// RL = D/8 threads cover one row; threads with equal p % RL share columns.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Stage {
+  static constexpr int NP = 2 * D;
+  static constexpr int RL = D / 8;
+  static constexpr int kPer = 4;
 };
 
-template <int D, int NT>
-__device__ __forceinline__ void piece_of(int p, int& row, int& col8) {
-  row = p / (D / 8);
-  col8 = (p % (D / 8)) * 8;
+template <int D, typename IN>
+struct Pref {
+  typename In8<IN>::raw q[4], k[4], v[4];
+};
+
+// Byte offset of piece i of staging thread p inside a chunk.
+template <int D, typename IN>
+__device__ __forceinline__ int piece_voff(int p, int i) {
+  constexpr int RL = Stage<D>::RL;
+  return ((p / RL + 16 * i) * D + 8 * (p % RL)) * (int)sizeof(IN);
 }
 
-// Issue global loads of rows [t0, t0 + valid) of one chunk (zeros beyond).
-template <int D, typename IN, bool LOADQ, bool LOADKV>
-__device__ __forceinline__ void issue_loads(Prefetch<D, IN>& pf, const IN* q, const IN* k, const IN* v,
-                                            long long row_base, int valid) {
-  constexpr int NT = D * 2;  // threads: 64 * (D/32)
+// Loads of one chunk (rows [row_base, row_base + valid)); rows past the end
+// read as zero through the descriptor's range check.
+template <int D, typename IN, bool LQ, bool LKV>
+__device__ __forceinline__ void prod_load(Pref<D, IN>& pf, const int (&voff)[4], const IN* q, const IN* k,
+                                          const IN* v, long long row_base, int valid) {
+  const long long eo = row_base * D;
+  const unsigned bytes = (unsigned)(valid * D * (int)sizeof(IN));
 #pragma unroll
-  for (int i = 0; i < Prefetch<D, IN>::kPer; ++i) {
-    const int p = threadIdx.x + i * NT;
-    int row, col;
-    piece_of<D, NT>(p, row, col);
-    if (row < valid) {
-      const long long off = (row_base + row) * D + col;
-      if constexpr (LOADQ) pf.q[i] = In8<IN>::load(q + off);
-      if constexpr (LOADKV) {
-        pf.k[i] = In8<IN>::load(k + off);
-        pf.v[i] = In8<IN>::load(v + off);
-      }
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (LQ) pf.q[i] = In8<IN>::bload(make_rsrc(q + eo, bytes), voff[i]);
+    if constexpr (LKV) {
+      pf.k[i] = In8<IN>::bload(make_rsrc(k + eo, bytes), voff[i]);
+      pf.v[i] = In8<IN>::bload(make_rsrc(v + eo, bytes), voff[i]);
+    }
+  }
+}
+
+// Key rows past the end of the sequence become -inf, so phi(k) = 0 there.
+// Branch-free, so every step has the same instruction stream.
+template <int D, typename IN>
+__device__ __forceinline__ void mask_tail_keys(Pref<D, IN>& pf, int p, int valid) {
+  constexpr int RL = Stage<D>::RL;
+  const auto ninf = In8<IN>::neg_inf();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool past = p / RL + 16 * i >= valid;
+    if constexpr (sizeof(IN) == 2) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pf.k[i][j] = past ? ninf[j] : pf.k[i][j];
     } else {
-      if constexpr (LOADQ) pf.q[i] = In8<IN>::zero();
-      if constexpr (LOADKV) {
-        pf.k[i] = In8<IN>::zero();
-        pf.v[i] = In8<IN>::zero();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pf.k[i].a[j] = past ? ninf.a[j] : pf.k[i].a[j];
+        pf.k[i].b[j] = past ? ninf.b[j] : pf.k[i].b[j];
       }
     }
   }
 }
 
-// Apply the feature map and write one chunk into LDS (phi(Q), phi(K), V).
-// Rows beyond `valid` get phi = 0 and v = 0, so they add nothing to any sum.
-template <int D, typename IN, typename OP, bool LOADQ, bool LOADKV>
-__device__ __forceinline__ void stage_chunk(const Prefetch<D, IN>& pf, uint8_t* sQ, uint8_t* sK,
-                                            uint8_t* sV, int valid) {
-  constexpr int NT = D * 2;
+template <typename IN, typename OP, int RB>
+__device__ __forceinline__ void store_raw(uint8_t* tile, int row, int col, const typename In8<IN>::raw& r) {
+  static_assert(sizeof(IN) == sizeof(OP), "raw staging needs matching element types");
+  if constexpr (sizeof(IN) == 2) {
+    *reinterpret_cast<u32x4*>(tile + tile_off<RB>(row, col * 2)) = r;
+  } else {
+    *reinterpret_cast<f32x4*>(tile + tile_off<RB>(row, col * 4)) = r.a;
+    *reinterpret_cast<f32x4*>(tile + tile_off<RB>(row, col * 4 + 16)) = r.b;
+  }
+}
+
+// Feature map + LDS writes for one chunk. Key rows past the end of the
+// sequence hold -inf, so phi(k) = exp(-inf) = 0 there and they add nothing to
+// the scores, S or z; their values read as zero.
+// Accumulates, per piece i, dp[i] = sum_e phi(q)[i][e] * z[e] (if LQ) and the
+// column sums of phi(k) over the thread's four rows in cs (if LKV).
+template <int D, typename IN, typename OP, bool LQ, bool LKV>
+__device__ __forceinline__ void prod_stage(const Pref<D, IN>& pf, int p, uint8_t* sQ, uint8_t* sK, uint8_t* sV,
+                                           const float (&z)[8], float (&dp)[4], float (&cs)[8]) {
   constexpr int RB = D * Ops<OP>::kBytes;
+  constexpr int RL = Stage<D>::RL;
+  const int rg = p / RL, col = 8 * (p % RL);
 #pragma unroll
-  for (int i = 0; i < Prefetch<D, IN>::kPer; ++i) {
-    const int p = threadIdx.x + i * NT;
-    int row, col;
-    piece_of<D, NT>(p, row, col);
-    const bool ok = row < valid;
+  for (int e = 0; e < 8; ++e) cs[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = rg + 16 * i;
     float x[8];
-    if constexpr (LOADQ) {
+    if constexpr (LQ) {
       In8<IN>::to_f32(pf.q[i], x);
+      float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = ok ? phi_elu1(x[e]) : 0.f;
+      for (int e = 0; e < 8; ++e) {
+        x[e] = phi_elu1(x[e]);
+        d += x[e] * z[e];
+      }
+      dp[i] = d;
       Ops<OP>::template store8<RB>(sQ, row, col, x);
     }
-    if constexpr (LOADKV) {
+    if constexpr (LKV) {
       In8<IN>::to_f32(pf.k[i], x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = ok ? phi_elu1(x[e]) : 0.f;
+      for (int e = 0; e < 8; ++e) {
+        x[e] = phi_elu1(x[e]);
+        cs[e] += x[e];
+      }
       Ops<OP>::template store8<RB>(sK, row, col, x);
-      In8<IN>::to_f32(pf.v[i], x);
-      Ops<OP>::template store8<RB>(sV, row, col, x);
+      store_raw<IN, OP, RB>(sV, row, col, pf.v[i]);
     }
   }
 }
 
-// Load this wave's state tiles (accumulator layout) and its copy of z.
+// DPP lane moves within rows of 16 lanes (quad_perm, mirrors, rotations).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+constexpr int kDppRor4 = 0x124;
+constexpr int kDppRor8 = 0x128;
+
+// Sum over the RL lanes that share one row (aligned groups of RL lanes).
+template <int RL>
+__device__ __forceinline__ float row_reduce(float x) {
+  if constexpr (RL >= 2) x += dpp_mov<kDppQuadXor1>(x);
+  if constexpr (RL >= 4) x += dpp_mov<kDppQuadXor2>(x);
+  if constexpr (RL >= 8) x += dpp_mov<kDppHalfMirror>(x);
+  if constexpr (RL >= 16) x += dpp_mov<kDppMirror>(x);
+  return x;
+}
+// Sum over the lanes of a wave that share p % RL.
+template <int RL>
+__device__ __forceinline__ float col_reduce(float x) {
+  if constexpr (RL <= 4) x += dpp_mov<kDppRor4>(x);
+  if constexpr (RL <= 8) x += dpp_mov<kDppRor8>(x);
+  x += xor32(x);
+  x += __shfl_xor(x, 16, 64);
+  return x;
+}
+
+// Load this wave's state tiles (accumulator layout): rows = features
+// 32cb + ..., columns = value dims 32w + lane%32.
 template <int D, int DF>
-__device__ __forceinline__ void load_state(f32x16 (&S)[DF / 32], float (&zc)[DF / 32], const float* Sp,
-                                           const float* zp) {
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6, h = l >> 5, li = l & 31;
+__device__ __forceinline__ void load_state_tiles(f32x16 (&S)[DF / 32], const float* Sp, int w) {
+  const int l = threadIdx.x & 63, h = l >> 5, li = l & 31;
 #pragma unroll
-  for (int cb = 0; cb < DF / 32; ++cb) {
+  for (int cb = 0; cb < DF / 32; ++cb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int c = 32 * cb + 8 * (r >> 2) + 4 * h + (r & 3);
       S[cb][r] = Sp ? Sp[(long long)c * D + 32 * w + li] : 0.f;
     }
-    zc[cb] = zp ? zp[32 * cb + li] : 0.f;
-  }
 }
 
 template <int D, int DF>
-__device__ __forceinline__ void store_state(const f32x16 (&S)[DF / 32], const float (&zc)[DF / 32], float* Sp,
-                                            float* zp) {
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6, h = l >> 5, li = l & 31;
+__device__ __forceinline__ void store_state_tiles(const f32x16 (&S)[DF / 32], float* Sp, int w) {
+  const int l = threadIdx.x & 63, h = l >> 5, li = l & 31;
 #pragma unroll
-  for (int cb = 0; cb < DF / 32; ++cb) {
+  for (int cb = 0; cb < DF / 32; ++cb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int c = 32 * cb + 8 * (r >> 2) + 4 * h + (r & 3);
       Sp[(long long)c * D + 32 * w + li] = S[cb][r];
     }
-    if (w == 0 && h == 0) zp[32 * cb + li] = zc[cb];
-  }
-}
-
-// S[:, e-block] += phi(K)^T V over one staged chunk; zc (per lane: feature
-// 32cb + lane%32, this half's tokens) += column sums of phi(K).
-template <int D, int DF, typename OP>
-__device__ __forceinline__ void state_update(f32x16 (&S)[DF / 32], float (&zpart)[DF / 32], const uint8_t* sK,
-                                             const uint8_t* sV, const typename Ops<OP>::frag (&Vf)[4]) {
-  constexpr int RBF = DF * Ops<OP>::kBytes;
-#pragma unroll
-  for (int cb = 0; cb < DF / 32; ++cb) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {  // 64 tokens = 4 blocks of 16
-      typename Ops<OP>::frag Kt = Ops<OP>::template load_cols<RBF>(sK, 16 * kb, 32 * cb);
-      Ops<OP>::mma(S[cb], Kt, Vf[kb]);
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) zpart[cb] += Ops<OP>::elem(Kt, jj);
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
-// State pass: local (S, z) of every segment.
-// grid = (BH, P), block = 64 * D/32 threads.
+// State pass: local (S, z) of every segment. All 2*D threads stage; wave w
+// owns value columns [32w, 32w+32) of S.
+// grid = (BH, P), block = 2*D threads.
 // ---------------------------------------------------------------------------
 template <int D, int DF, typename OP, typename IN>
 __global__ __launch_bounds__(D * 2) void state_pass_kernel(FwdArgs a) {
+  using Frag = typename Ops<OP>::frag;
   constexpr int RBF = DF * Ops<OP>::kBytes;
   constexpr int RBV = D * Ops<OP>::kBytes;
-  constexpr int KBYTES = 64 * RBF, VBYTES = 64 * RBV;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (KBYTES + VBYTES)];
+  constexpr int KB = 64 * RBF, VB = 64 * RBV, BUF = KB + VB;
+  constexpr int RL = Stage<D>::RL;
+  constexpr int NW = D / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
+  __shared__ float zsum[NW][DF];
+
   const int bh = blockIdx.x, seg = blockIdx.y;
   const int c0 = seg * a.chunks_per_seg_state;
   const int c1 = min(c0 + a.chunks_per_seg_state, a.nchunks);
   const long long base = (long long)bh * a.N;
   const IN* k = static_cast<const IN*>(a.k);
   const IN* v = static_cast<const IN*>(a.v);
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int p = threadIdx.x, w = p >> 6, l = p & 63;
 
   f32x16 S[DF / 32];
-  float zc[DF / 32];
 #pragma unroll
-  for (int cb = 0; cb < DF / 32; ++cb) {
-    S[cb] = f32x16{};
-    zc[cb] = 0.f;
-  }
-  Prefetch<D, IN> pf;
-  if (c0 < c1) {
-    issue_loads<D, IN, false, true>(pf, nullptr, k, v, base + 64LL * c0, min(64, a.N - 64 * c0));
-    stage_chunk<D, IN, OP, false, true>(pf, nullptr, smem, smem + KBYTES, min(64, a.N - 64 * c0));
-  }
+  for (int cb = 0; cb < DF / 32; ++cb) S[cb] = f32x16{};
+  float zr[8], cs[8], dp[4];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) zr[e] = 0.f;
+  int voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = piece_voff<D, IN>(p, i);
+
+  // chunk m of the segment is held in register set m % 3; it is loaded two
+  // iterations before it is staged into LDS
+  Pref<D, IN> pA, pB, pC;
+  const int nch = c1 - c0;
+  // every load is issued (with zero size past the segment) so that all
+  // iterations have the same memory instruction stream
+  auto load = [&](Pref<D, IN>& pf, int m) {
+    const int c = c0 + m;
+    const int valid = m < nch ? min(64, a.N - 64 * c) : 0;
+    prod_load<D, IN, false, true>(pf, voff, nullptr, k, v, base + 64LL * min(c, a.nchunks - 1), valid);
+  };
+  auto stage = [&](Pref<D, IN>& pf, int m) {
+    const int c = c0 + m;
+    const int valid = min(64, a.N - 64 * c);
+    mask_tail_keys<D, IN>(pf, p, valid);
+    uint8_t* sK = smem + (m & 1) * BUF;
+    prod_stage<D, IN, OP, false, true>(pf, p, nullptr, sK, sK + KB, zr, dp, cs);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zr[e] += cs[e];
+  };
+  load(pA, 0);
+  load(pB, 1);
+  if (nch > 0) stage(pA, 0);
   __syncthreads();
-  for (int c = c0; c < c1; ++c) {
-    const int buf = (c - c0) & 1;
-    uint8_t* sK = smem + buf * (KBYTES + VBYTES);
-    uint8_t* sV = sK + KBYTES;
-    const bool more = c + 1 < c1;
-    const int nvalid = more ? min(64, a.N - 64 * (c + 1)) : 0;
-    if (more) issue_loads<D, IN, false, true>(pf, nullptr, k, v, base + 64LL * (c + 1), nvalid);
-    typename Ops<OP>::frag Vf[4];
+  // iteration m: load chunk m+2, multiply chunk m, stage chunk m+1
+  auto iter = [&](int m, Pref<D, IN>& ld, Pref<D, IN>& st) {
+    load(ld, m + 2);
+    const uint8_t* sK = smem + (m & 1) * BUF;
+    const uint8_t* sV = sK + KB;
+    Frag Vf[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) Vf[kb] = Ops<OP>::template load_cols<RBV>(sV, 16 * kb, 32 * w);
-    state_update<D, DF, OP>(S, zc, sK, sV, Vf);
-    if (more) {
-      uint8_t* nK = smem + (buf ^ 1) * (KBYTES + VBYTES);
-      stage_chunk<D, IN, OP, false, true>(pf, nullptr, nK, nK + KBYTES, nvalid);
-    }
-    __syncthreads();
-  }
 #pragma unroll
-  for (int cb = 0; cb < DF / 32; ++cb) zc[cb] += xor32(zc[cb]);
-  (void)l;
+    for (int cb = 0; cb < DF / 32; ++cb)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        Ops<OP>::mma(S[cb], Ops<OP>::template load_cols<RBF>(sK, 16 * kb, 32 * cb), Vf[kb]);
+    if (m + 1 < nch) stage(st, m + 1);
+    __syncthreads();
+  };
+  for (int m = 0; m < nch; m += 3) {
+    iter(m, pC, pB);
+    if (m + 1 < nch) iter(m + 1, pA, pC);
+    if (m + 2 < nch) iter(m + 2, pB, pA);
+  }
+  // z: reduce the per-thread column sums over rows (lanes, then waves)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) zr[e] = col_reduce<RL>(zr[e]);
+  if (l < RL) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zsum[w][8 * l + e] = zr[e];
+  }
+  __syncthreads();
   float* st = a.ws + ((long long)bh * a.ws_slots + seg) * a.state_elems;
-  store_state<D, DF>(S, zc, st, st + DF * D);
+  store_state_tiles<D, DF>(S, st, w);
+  for (int c = p; c < DF; c += 2 * D) {
+    float s = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) s += zsum[ww][c];
+    st[DF * D + c] = s;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -233,197 +333,300 @@ __global__ __launch_bounds__(256) void carry_scan_kernel(ScanArgs a) {
 // Output pass.
 // CAUSAL: y_i = [sum_{j<=i in chunk} w_ij v_j + phi(q_i)^T S_prev] / [..]
 // otherwise: y_i = phi(q_i)^T S / phi(q_i)^T z with the total (S, z).
-// grid = (BH, P), block = 64 * D/32 threads.
+// grid = (BH, P), block = 2 * 64 * D/32 threads (consumers, then producers).
 // ---------------------------------------------------------------------------
 template <int D, int DF, typename OP, typename IN, bool CAUSAL>
-__global__ __launch_bounds__(D * 2) void output_pass_kernel(FwdArgs a) {
+struct OutLayout {
+  static constexpr int NWC = D / 32, NWP = D / 32;
+  static constexpr int RBF = DF * Ops<OP>::kBytes;
+  static constexpr int RBV = D * Ops<OP>::kBytes;
+  static constexpr int QB = 64 * RBF, KB = CAUSAL ? 64 * RBF : 0, VB = CAUSAL ? 64 * RBV : 0;
+  static constexpr int BUF = QB + KB + VB;
+  static constexpr int DEN = 2 * 64 * 4;                         // den_inter, double-buffered
+  static constexpr int ZP = CAUSAL ? 2 * NWP * DF * 4 : 0;       // colsum partials, double-buffered
+  // two staged chunks when they fit in LDS; otherwise one, with an extra
+  // barrier per step so the producers wait for the consumers
+  static constexpr int NB = (2 * BUF + DEN + ZP <= 160 * 1024) ? 2 : 1;
+  static constexpr int NBAR = NB == 2 ? 1 : 2;
+  // output tiles go through LDS (double-buffered) and the producers store
+  // them as whole rows one step later, when that fits
+  static constexpr int RBY = D * (int)sizeof(IN);
+  static constexpr int YB1 = 64 * RBY;
+  static constexpr bool YS = NB * BUF + DEN + ZP + 2 * YB1 <= 160 * 1024;
+  static constexpr int YB = YS ? 2 * YB1 : 0;
+  static constexpr int BYTES = NB * BUF + DEN + ZP + YB;
+};
+
+template <int D, int DF, typename OP, typename IN, bool CAUSAL>
+__global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
   using Frag = typename Ops<OP>::frag;
-  constexpr int NW = D / 32;
-  constexpr int RBF = DF * Ops<OP>::kBytes;
-  constexpr int RBV = D * Ops<OP>::kBytes;
-  constexpr int QBYTES = 64 * RBF, KBYTES = CAUSAL ? 64 * RBF : 0, VBYTES = CAUSAL ? 64 * RBV : 0;
-  constexpr int BUF = QBYTES + KBYTES + VBYTES;
-  // double-buffer the staged chunk when two copies fit in LDS
-  constexpr int NBUF = (2 * BUF + NW * DF * 4 <= 160 * 1024) ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * BUF + NW * DF * 4];
-  float* zbuf = reinterpret_cast<float*>(smem + NBUF * BUF) + (threadIdx.x >> 6) * DF;
+  using L = OutLayout<D, DF, OP, IN, CAUSAL>;
+  constexpr int RL = Stage<D>::RL;
+  static_assert(DF == D, "elu+1 keeps d' = d");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
+  float* dbuf = reinterpret_cast<float*>(smem + L::NB * L::BUF);
+  float* zpart = reinterpret_cast<float*>(smem + L::NB * L::BUF + L::DEN);
+  uint8_t* ybuf = smem + L::NB * L::BUF + L::DEN + L::ZP;
+  constexpr int LAST = L::YS ? 1 : 0;  // extra step in which the last output tile is stored
 
   const int bh = blockIdx.x, seg = blockIdx.y;
   const int c0 = seg * a.chunks_per_seg;
-  const int c1 = min(c0 + a.chunks_per_seg, a.nchunks);
+  const int n = max(0, min(c0 + a.chunks_per_seg, a.nchunks) - c0);
   const long long base = (long long)bh * a.N;
   const IN* q = static_cast<const IN*>(a.q);
   const IN* k = static_cast<const IN*>(a.k);
   const IN* v = static_cast<const IN*>(a.v);
   IN* out = static_cast<IN*>(a.out);
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6, h = l >> 5, li = l & 31;
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, li = l & 31;
+  const bool producer = wave >= L::NWC;
+  const int p = threadIdx.x - 64 * L::NWC;     // producer thread index
+  const int pw = wave - L::NWC;                // producer wave index
+  const int cw = wave;                         // consumer wave = value-column block
 
-  // ---- starting state ----
-  f32x16 S[DF / 32];
-  float zc[DF / 32];
-  {
-    const float* Sp;
-    const float* zp;
-    if (a.init_from_ws) {
-      const float* st = a.ws + ((long long)bh * a.ws_slots + (CAUSAL ? seg : a.ws_total_slot)) * a.state_elems;
-      Sp = st;
-      zp = st + DF * D;
-    } else {
-      Sp = a.S_in ? a.S_in + (long long)bh * DF * D : nullptr;
-      zp = a.z_in ? a.z_in + (long long)bh * DF : nullptr;
-    }
-    load_state<D, DF>(S, zc, Sp, zp);
-  }
-  // every wave keeps its own copy of z in LDS (read back by feature index)
-#pragma unroll
-  for (int cb = 0; cb < DF / 32; ++cb)
-    if (h == 0) zbuf[32 * cb + li] = zc[cb];
-  // non-causal: the state never changes; convert it once
-  Frag Sf_const[CAUSAL ? 1 : DF / 16];
-  if constexpr (!CAUSAL) {
-#pragma unroll
-    for (int kb = 0; kb < DF / 16; ++kb) Sf_const[kb] = Ops<OP>::from_acc(S[kb >> 1], kb & 1);
+  const float* Sinit;
+  const float* zinit;
+  if (a.init_from_ws) {
+    const float* st = a.ws + ((long long)bh * a.ws_slots + (CAUSAL ? seg : a.ws_total_slot)) * a.state_elems;
+    Sinit = st;
+    zinit = st + DF * D;
+  } else {
+    Sinit = a.S_in ? a.S_in + (long long)bh * DF * D : nullptr;
+    zinit = a.z_in ? a.z_in + (long long)bh * DF : nullptr;
   }
 
-  Prefetch<D, IN> pf;
-  if (c0 < c1) {
-    const int nv = min(64, a.N - 64 * c0);
-    issue_loads<D, IN, true, CAUSAL>(pf, q, k, v, base + 64LL * c0, nv);
-    stage_chunk<D, IN, OP, true, CAUSAL>(pf, smem, smem + QBYTES, smem + QBYTES + KBYTES, nv);
-  }
-  __syncthreads();
+  if (producer) {
+    // ------------------------------------------------------------------
+    // producers: chunk `it` is loaded during step it-1 and staged in step it
+    // ------------------------------------------------------------------
+    Pref<D, IN> pA, pB, pC;
+    float zrun[8], dp[4], cs[8];
+    const int cr = 8 * (p % RL);
+    int voff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) voff[i] = piece_voff<D, IN>(p, i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zrun[e] = zinit ? zinit[cr + e] : 0.f;
+    // Drain that load now: otherwise the wait-count analysis carries it
+    // around the loop and waits for every outstanding prefetch each step.
+    wait_vmem_all();
+    // every load and store below is issued in every step (zero size when out
+    // of range), so the wait counts are the same on every path
+    auto load = [&](Pref<D, IN>& pf, int it) {
+      const int c = c0 + it;
+      const int valid = it < n ? min(64, a.N - 64 * c) : 0;
+      prod_load<D, IN, true, CAUSAL>(pf, voff, q, k, v, base + 64LL * min(c, a.nchunks - 1), valid);
+    };
+    load(pA, 0);
+    load(pB, 1);
 
-  for (int c = c0; c < c1; ++c) {
-    const int buf = NBUF == 2 ? ((c - c0) & 1) : 0;
-    uint8_t* sQ = smem + buf * BUF;
-    uint8_t* sK = sQ + QBYTES;
-    uint8_t* sV = sK + KBYTES;
-    const int valid = min(64, a.N - 64 * c);
-    const bool more = c + 1 < c1;
-    const int nvalid = more ? min(64, a.N - 64 * (c + 1)) : 0;
-    if (more) issue_loads<D, IN, true, CAUSAL>(pf, q, k, v, base + 64LL * (c + 1), nvalid);
-
-    // phi(Q) fragments (B operand: contraction = feature, columns = query rows)
-    Frag Bq[2][DF / 16];
+    // step `it` stores the output tile of chunk it-2, stages chunk it (held in
+    // `cur`) and issues the loads of chunk it+2 into `nxt`
+    auto pstep = [&](int it, Pref<D, IN>& cur, Pref<D, IN>& nxt) {
+      if constexpr (L::YS) {
+        {
+          const int c = c0 + max(it - 2, 0);
+          const int valid = it >= 2 ? min(64, a.N - 64 * c) : 0;
+          const uint8_t* yb = ybuf + (it & 1) * L::YB1;
+          const auto ro = make_rsrc(out + (base + 64LL * c) * D, (unsigned)(valid * D * (int)sizeof(IN)));
+          const int rg = p / RL, col = 8 * (p % RL);
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-      for (int kb = 0; kb < DF / 16; ++kb) Bq[ib][kb] = Ops<OP>::template load_rows<RBF>(sQ, 32 * ib, 16 * kb);
-
-    f32x16 num[2] = {f32x16{}, f32x16{}};
-    float dpart[2] = {0.f, 0.f};
-    Frag Vf[4];
-    if constexpr (CAUSAL) {
-      // scores A^T[j][i] = phi(k_j).phi(q_i) for tile pairs (jb, ib) with jb <= ib
-      f32x16 A00 = {}, A01 = {}, A11 = {};
-#pragma unroll
-      for (int kb = 0; kb < DF / 16; ++kb) {
-        Frag k0 = Ops<OP>::template load_rows<RBF>(sK, 0, 16 * kb);
-        Frag k1 = Ops<OP>::template load_rows<RBF>(sK, 32, 16 * kb);
-        Ops<OP>::mma(A00, k0, Bq[0][kb]);
-        Ops<OP>::mma(A01, k0, Bq[1][kb]);
-        Ops<OP>::mma(A11, k1, Bq[1][kb]);
-      }
-      // causal mask on the diagonal tiles (keep j <= i), rounding to the
-      // operand precision, and the within-chunk part of the denominator
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int jt = 8 * (r >> 2) + 4 * h + (r & 3);
-        const bool keep = jt <= li;
-        float x00 = keep ? A00[r] : 0.f, x11 = keep ? A11[r] : 0.f, x01 = A01[r];
-        if constexpr (sizeof(OP) == 2) {
-          x00 = round_bf16(x00);
-          x11 = round_bf16(x11);
-          x01 = round_bf16(x01);
-        }
-        A00[r] = x00;
-        A11[r] = x11;
-        A01[r] = x01;
-        dpart[0] += x00;
-        dpart[1] += x01 + x11;
-      }
-      // V^T fragments (rows = value columns of this wave, contraction = token)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) Vf[kb] = Ops<OP>::template load_cols<RBV>(sV, 16 * kb, 32 * w);
-      // intra-chunk numerator: num^T[e][i] += sum_j V^T[e][j] A^T[j][i]
-#pragma unroll
-      for (int kbj = 0; kbj < 2; ++kbj) {
-        Ops<OP>::mma(num[0], Vf[kbj], Ops<OP>::from_acc(A00, kbj));
-        Ops<OP>::mma(num[1], Vf[kbj], Ops<OP>::from_acc(A01, kbj));
-        Ops<OP>::mma(num[1], Vf[2 + kbj], Ops<OP>::from_acc(A11, kbj));
-      }
-    }
-    // inter-chunk numerator: num^T[e][i] += sum_c S^T[e][c] phi(Q)^T[c][i]
-#pragma unroll
-    for (int kb = 0; kb < DF / 16; ++kb) {
-      Frag Sf;
-      if constexpr (CAUSAL) Sf = Ops<OP>::from_acc(S[kb >> 1], kb & 1);
-      else Sf = Sf_const[kb];
-      Ops<OP>::mma(num[0], Sf, Bq[0][kb]);
-      Ops<OP>::mma(num[1], Sf, Bq[1][kb]);
-    }
-    // denominator: phi(q_i).z over this lane's half of the features
-    if (a.normalize) {
-#pragma unroll
-      for (int kb = 0; kb < DF / 16; ++kb) {
-        const f32x4 z0 = *reinterpret_cast<const f32x4*>(zbuf + 16 * kb + 8 * h);
-        const f32x4 z1 = *reinterpret_cast<const f32x4*>(zbuf + 16 * kb + 8 * h + 4);
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-          float s = 0.f;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) s += Ops<OP>::elem(Bq[ib][kb], jj) * z0[jj];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) s += Ops<OP>::elem(Bq[ib][kb], 4 + jj) * z1[jj];
-          dpart[ib] += s;
-        }
-      }
-    }
-    // normalize and store: lane holds y[i = 32ib + li][e = 32w + 8(r/4) + 4h + r%4]
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      float inv = 1.f;
-      if (a.normalize) {
-        const float den = dpart[ib] + xor32(dpart[ib]);
-        inv = 1.f / fmaxf(den, kEps);
-      }
-      const int i = 32 * ib + li;
-      if (i < valid) {
-        const long long rowoff = (base + 64LL * c + i) * D + 32 * w + 4 * h;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float y0 = num[ib][4 * g + 0] * inv, y1 = num[ib][4 * g + 1] * inv;
-          const float y2 = num[ib][4 * g + 2] * inv, y3 = num[ib][4 * g + 3] * inv;
-          if constexpr (sizeof(IN) == 2) {
-            *reinterpret_cast<u32x2*>(out + rowoff + 8 * g) = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
-          } else {
-            *reinterpret_cast<f32x4*>(out + rowoff + 8 * g) = f32x4{y0, y1, y2, y3};
+          for (int i = 0; i < 4; ++i) {
+            const int row = rg + 16 * i;
+            if constexpr (sizeof(IN) == 2) {
+              buf_store16(ro, voff[i], *reinterpret_cast<const u32x4*>(yb + tile_off<L::RBY>(row, col * 2)));
+            } else {
+              buf_store16(ro, voff[i], *reinterpret_cast<const u32x4*>(yb + tile_off<L::RBY>(row, col * 4)));
+              buf_store16(ro, voff[i] + 16, *reinterpret_cast<const u32x4*>(yb + tile_off<L::RBY>(row, col * 4 + 16)));
+            }
           }
         }
       }
+      load(nxt, it + 2);
+      if (it < n) {
+        const int c = c0 + it;
+        const int valid = min(64, a.N - 64 * c);
+        if constexpr (CAUSAL) {
+          mask_tail_keys<D, IN>(cur, p, valid);
+          // z_{it-1} = z_{it-2} + column sums of chunk it-1 (all producer waves)
+          if (it >= 1) {
+            const float* zp = zpart + ((it - 1) & 1) * L::NWP * DF;
+#pragma unroll
+            for (int ww = 0; ww < L::NWP; ++ww) {
+              const f32x4 z0 = *reinterpret_cast<const f32x4*>(zp + ww * DF + cr);
+              const f32x4 z1 = *reinterpret_cast<const f32x4*>(zp + ww * DF + cr + 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                zrun[e] += z0[e];
+                zrun[4 + e] += z1[e];
+              }
+            }
+          }
+        }
+        uint8_t* sQ = smem + (L::NB == 2 ? (it & 1) : 0) * L::BUF;
+        if constexpr (L::NB == 1) __syncthreads();  // consumers are done with the buffer
+        prod_stage<D, IN, OP, true, CAUSAL>(cur, p, sQ, sQ + L::QB, sQ + L::QB + L::KB, zrun, dp, cs);
+        if constexpr (CAUSAL) {
+          // publish this chunk's column sums of phi(K)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) cs[e] = col_reduce<RL>(cs[e]);
+          if (l < RL) {
+            float* zw = zpart + (it & 1) * L::NWP * DF + pw * DF + cr;
+            *reinterpret_cast<f32x4*>(zw) = f32x4{cs[0], cs[1], cs[2], cs[3]};
+            *reinterpret_cast<f32x4*>(zw + 4) = f32x4{cs[4], cs[5], cs[6], cs[7]};
+          }
+        }
+        // cross-chunk denominator phi(q_i).z_{it-1} for the thread's rows
+        if (a.normalize) {
+          float* db = dbuf + (it & 1) * 64;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float s = row_reduce<RL>(dp[i]);
+            if ((p % RL) == 0) db[p / RL + 16 * i] = s;
+          }
+        }
+      } else {
+        if constexpr (L::NB == 1) __syncthreads();
+        if constexpr (CAUSAL) if (it == n) {
+          // final z = z_{n-2} + column sums of the last chunk
+          const float* zp = zpart + ((it - 1) & 1) * L::NWP * DF;
+#pragma unroll
+          for (int ww = 0; ww < L::NWP; ++ww)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) zrun[e] += zp[ww * DF + cr + e];
+        }
+      }
+      __syncthreads();
+    };
+    for (int it = 0; it <= n + LAST; it += 3) {
+      pstep(it, pA, pC);
+      if (it + 1 <= n + LAST) pstep(it + 1, pB, pA);
+      if (it + 2 <= n + LAST) pstep(it + 2, pC, pB);
     }
     if constexpr (CAUSAL) {
-      // state update and z for the next chunk
-      float zp[DF / 32];
+      if (a.S_out && seg == a.nseg - 1 && p < RL) {
+        float* zo = a.z_out + (long long)bh * DF + cr;
 #pragma unroll
-      for (int cb = 0; cb < DF / 32; ++cb) zp[cb] = 0.f;
-      state_update<D, DF, OP>(S, zp, sK, sV, Vf);
-#pragma unroll
-      for (int cb = 0; cb < DF / 32; ++cb) {
-        zc[cb] += zp[cb] + xor32(zp[cb]);
-        if (h == 0) zbuf[32 * cb + li] = zc[cb];
+        for (int e = 0; e < 8; ++e) zo[e] = zrun[e];
       }
     }
-    if (more) {
-      if constexpr (NBUF == 1) __syncthreads();
-      uint8_t* nQ = smem + (NBUF == 2 ? (buf ^ 1) : 0) * BUF;
-      stage_chunk<D, IN, OP, true, CAUSAL>(pf, nQ, nQ + QBYTES, nQ + QBYTES + KBYTES, nvalid);
+  } else {
+    // ------------------------------------------------------------------
+    // consumers: chunk it-1 in step it
+    // ------------------------------------------------------------------
+    f32x16 S[DF / 32];
+    load_state_tiles<D, DF>(S, Sinit, cw);
+    Frag Sf_const[CAUSAL ? 1 : DF / 16];
+    if constexpr (!CAUSAL) {
+#pragma unroll
+      for (int kb = 0; kb < DF / 16; ++kb) Sf_const[kb] = Ops<OP>::from_acc(S[kb >> 1], kb & 1);
     }
-    __syncthreads();
-  }
-  if constexpr (CAUSAL) {
-    if (a.S_out && seg == a.nseg - 1) {
-      store_state<D, DF>(S, zc, a.S_out + (long long)bh * DF * D, a.z_out + (long long)bh * DF);
+    for (int bar = 0; bar < L::NBAR; ++bar) __syncthreads();  // the producers' first step
+    for (int it = 1; it <= n + LAST; ++it) {
+      if (it > n) {  // the producers store the last tile
+        for (int bar = 0; bar < L::NBAR; ++bar) __syncthreads();
+        continue;
+      }
+      const int c = c0 + it - 1;
+      const int b = L::NB == 2 ? ((it - 1) & 1) : 0;
+      const uint8_t* sQ = smem + b * L::BUF;
+      const uint8_t* sK = sQ + L::QB;
+      const uint8_t* sV = sK + L::KB;
+      const int valid = min(64, a.N - 64 * c);
+      f32x16 num0 = {}, num1 = {};
+      float dpart0 = 0.f, dpart1 = 0.f;
+      Frag Vf[4];
+      if constexpr (CAUSAL) {
+        f32x16 A00 = {}, A01 = {}, A11 = {};
+#pragma unroll
+        for (int kb = 0; kb < DF / 16; ++kb) {
+          const Frag bq0 = Ops<OP>::template load_rows<L::RBF>(sQ, 0, 16 * kb);
+          const Frag bq1 = Ops<OP>::template load_rows<L::RBF>(sQ, 32, 16 * kb);
+          const Frag k0 = Ops<OP>::template load_rows<L::RBF>(sK, 0, 16 * kb);
+          const Frag k1 = Ops<OP>::template load_rows<L::RBF>(sK, 32, 16 * kb);
+          Ops<OP>::mma(A00, k0, bq0);
+          Ops<OP>::mma(A01, k0, bq1);
+          Ops<OP>::mma(A11, k1, bq1);
+          const Frag sf = Ops<OP>::from_acc(S[kb >> 1], kb & 1);
+          Ops<OP>::mma(num0, sf, bq0);
+          Ops<OP>::mma(num1, sf, bq1);
+        }
+        // causal mask on the diagonal tiles (keep j <= i) and the in-chunk
+        // part of the denominator
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jt = 8 * (r >> 2) + 4 * h + (r & 3);
+          const bool keep = jt <= li;
+          A00[r] = keep ? A00[r] : 0.f;
+          A11[r] = keep ? A11[r] : 0.f;
+          dpart0 += A00[r];
+          dpart1 += A01[r] + A11[r];
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) Vf[kb] = Ops<OP>::template load_cols<L::RBV>(sV, 16 * kb, 32 * cw);
+#pragma unroll
+        for (int kbj = 0; kbj < 2; ++kbj) {
+          Ops<OP>::mma(num0, Vf[kbj], Ops<OP>::from_acc(A00, kbj));
+          Ops<OP>::mma(num1, Vf[kbj], Ops<OP>::from_acc(A01, kbj));
+          Ops<OP>::mma(num1, Vf[2 + kbj], Ops<OP>::from_acc(A11, kbj));
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < DF / 16; ++kb) {
+          Ops<OP>::mma(num0, Sf_const[kb], Ops<OP>::template load_rows<L::RBF>(sQ, 0, 16 * kb));
+          Ops<OP>::mma(num1, Sf_const[kb], Ops<OP>::template load_rows<L::RBF>(sQ, 32, 16 * kb));
+        }
+      }
+      // normalize and store: lane holds y[i = 32ib + li][e = 32cw + 8(r/4) + 4h + r%4]
+      const float* db = dbuf + ((it - 1) & 1) * 64;
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+        const f32x16& nm = ib ? num1 : num0;
+        float inv = 1.f;
+        if (a.normalize) {
+          const float dp = ib ? dpart1 : dpart0;
+          const float den = dp + xor32(dp) + db[32 * ib + li];
+          inv = 1.f / fmaxf(den, kEps);
+        }
+        const int i = 32 * ib + li;
+        if constexpr (L::YS) {
+          uint8_t* yb = ybuf + ((it - 1) & 1) * L::YB1;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float y0 = nm[4 * g + 0] * inv, y1 = nm[4 * g + 1] * inv;
+            const float y2 = nm[4 * g + 2] * inv, y3 = nm[4 * g + 3] * inv;
+            const int e = 32 * cw + 8 * g + 4 * h;
+            if constexpr (sizeof(IN) == 2) {
+              *reinterpret_cast<u32x2*>(yb + tile_off<L::RBY>(i, e * 2)) =
+                  u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+            } else {
+              *reinterpret_cast<f32x4*>(yb + tile_off<L::RBY>(i, e * 4)) = f32x4{y0, y1, y2, y3};
+            }
+          }
+        } else if (i < valid) {
+          const long long rowoff = (base + 64LL * c + i) * D + 32 * cw + 4 * h;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float y0 = nm[4 * g + 0] * inv, y1 = nm[4 * g + 1] * inv;
+            const float y2 = nm[4 * g + 2] * inv, y3 = nm[4 * g + 3] * inv;
+            if constexpr (sizeof(IN) == 2) {
+              *reinterpret_cast<u32x2*>(out + rowoff + 8 * g) = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+            } else {
+              *reinterpret_cast<f32x4*>(out + rowoff + 8 * g) = f32x4{y0, y1, y2, y3};
+            }
+          }
+        }
+      }
+      if constexpr (CAUSAL) {
+#pragma unroll
+        for (int cb = 0; cb < DF / 32; ++cb)
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+            Ops<OP>::mma(S[cb], Ops<OP>::template load_cols<L::RBF>(sK, 16 * kb, 32 * cb), Vf[kb]);
+      }
+      for (int bar = 0; bar < L::NBAR; ++bar) __syncthreads();
+    }
+    if constexpr (CAUSAL) {
+      if (a.S_out && seg == a.nseg - 1) store_state_tiles<D, DF>(S, a.S_out + (long long)bh * DF * D, cw);
     }
   }
 }
@@ -434,10 +637,9 @@ __global__ __launch_bounds__(D * 2) void output_pass_kernel(FwdArgs a) {
 template <int D, int DF, typename OP, typename IN>
 static hipError_t launch_prefill(const FwdArgs& a, const ScanArgs& s, bool causal, hipStream_t st,
                                  hipEvent_t* ev) {
-  const dim3 block(D * 2);
   if (ev) (void)hipEventRecord(ev[0], st);
   if (a.run_state_pass) {
-    hipLaunchKernelGGL((state_pass_kernel<D, DF, OP, IN>), dim3(a.BH, a.nseg_state), block, 0, st, a);
+    hipLaunchKernelGGL((state_pass_kernel<D, DF, OP, IN>), dim3(a.BH, a.nseg_state), dim3(D * 2), 0, st, a);
   }
   if (ev) (void)hipEventRecord(ev[1], st);
   if (a.run_scan) {
@@ -445,9 +647,9 @@ static hipError_t launch_prefill(const FwdArgs& a, const ScanArgs& s, bool causa
   }
   if (ev) (void)hipEventRecord(ev[2], st);
   if (causal) {
-    hipLaunchKernelGGL((output_pass_kernel<D, DF, OP, IN, true>), dim3(a.BH, a.nseg), block, 0, st, a);
+    hipLaunchKernelGGL((output_pass_kernel<D, DF, OP, IN, true>), dim3(a.BH, a.nseg), dim3(D * 4), 0, st, a);
   } else {
-    hipLaunchKernelGGL((output_pass_kernel<D, DF, OP, IN, false>), dim3(a.BH, a.nseg), block, 0, st, a);
+    hipLaunchKernelGGL((output_pass_kernel<D, DF, OP, IN, false>), dim3(a.BH, a.nseg), dim3(D * 4), 0, st, a);
   }
   if (ev) (void)hipEventRecord(ev[3], st);
   return hipGetLastError();
@@ -456,6 +658,7 @@ static hipError_t launch_prefill(const FwdArgs& a, const ScanArgs& s, bool causa
 hipError_t prefill_dispatch(const FwdArgs& a, const ScanArgs& s, int D, int DF, int fmap, int dtype, bool causal,
                             hipStream_t st, hipEvent_t* ev) {
   if (fmap != kElu1) return hipErrorInvalidValue;
+  (void)DF;
   if (dtype == 1) {  // bf16
     switch (D) {
       case 32: return launch_prefill<32, 32, __bf16, __bf16>(a, s, causal, st, ev);
@@ -469,7 +672,6 @@ hipError_t prefill_dispatch(const FwdArgs& a, const ScanArgs& s, int D, int DF, 
       case 128: return launch_prefill<128, 128, float, float>(a, s, causal, st, ev);
     }
   }
-  (void)DF;
   return hipErrorInvalidValue;
 }
 
