@@ -27,16 +27,29 @@ bool overlaps(const void* a, long long abytes, const void* b, long long bbytes) 
 
 bool d_supported(int d) { return d == 32 || d == 64 || d == 128; }
 
+// (d, m) pairs with random-feature kernels.
+bool perf_supported(int d, int m) {
+  switch (d) {
+    case 32: return m == 64 || m == 128;
+    case 64: return m == 64 || m == 128 || m == 256;
+    case 128: return m == 64 || m == 128;
+  }
+  return false;
+}
+
 // Feature dimension d' for a map, or a negative status.
 int feature_dim(const la_feature_map* fm, int d) {
   if (!fm) return LA_ERR_INVALID_ARG;
   if (fm->kind == LA_ELU1) return d;
   if (fm->kind == LA_PERFORMER) {
     if (fm->m <= 0 || !fm->W || !aligned16(fm->W)) return LA_ERR_INVALID_ARG;
-    return LA_ERR_UNSUPPORTED;
+    if (!perf_supported(d, fm->m)) return LA_ERR_UNSUPPORTED;
+    return fm->m;
   }
   return LA_ERR_INVALID_ARG;
 }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
   int nchunks = 0;
@@ -44,7 +57,8 @@ struct Plan {
   int Ps = 0, cpss = 0;      // state pass
   int ws_slots = 0;
   bool state_pass = false, scan = false;
-  size_t ws_bytes = 0;
+  size_t phi_bytes = 0;      // one mapped-feature buffer (random features), fp32-sized
+  size_t ws_bytes = 0;       // total: two feature buffers, then the segment states
 };
 
 void split(int nchunks, long long BH, int& P, int& cps) {
@@ -57,8 +71,9 @@ void split(int nchunks, long long BH, int& P, int& cps) {
   P = (nchunks + cps - 1) / cps;
 }
 
-Plan make_plan(long long BH, int N, int d, int dfeat, bool causal) {
+Plan make_plan(long long BH, int N, int d, int dfeat, bool causal, bool mapped_inputs) {
   Plan p;
+  if (mapped_inputs && N > 0) p.phi_bytes = align256((size_t)BH * N * dfeat * sizeof(float));
   p.nchunks = (N + kChunk - 1) / kChunk;
   const size_t state_bytes = (size_t)(dfeat * d + dfeat) * sizeof(float);
   if (N == 0 || BH == 0) return p;
@@ -77,7 +92,7 @@ Plan make_plan(long long BH, int N, int d, int dfeat, bool causal) {
     p.state_pass = true;
     p.scan = true;
   }
-  p.ws_bytes = (size_t)BH * p.ws_slots * state_bytes;
+  p.ws_bytes = 2 * p.phi_bytes + (size_t)BH * p.ws_slots * state_bytes;
   return p;
 }
 
@@ -104,7 +119,7 @@ size_t la_forward_workspace_size(int B, int H, int N, int d, const la_feature_ma
   if (B < 0 || H < 0 || N < 0 || !d_supported(d)) return 0;
   const int dfeat = feature_dim(feature_map, d);
   if (dfeat <= 0) return 0;
-  return make_plan((long long)B * H, N, d, dfeat, causal != 0).ws_bytes;
+  return make_plan((long long)B * H, N, d, dfeat, causal != 0, feature_map->kind == LA_PERFORMER).ws_bytes;
 }
 
 int la_forward_ex(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
@@ -132,10 +147,15 @@ int la_forward_ex(const void* q, const void* k, const void* v, void* out, int B,
                 overlaps(z_out, z_bytes, z_in, z_bytes)))
     return LA_ERR_INVALID_ARG;
 
-  if (BH == 0) return LA_OK;
-  if (N == 0) {
-    if (!S_out) return LA_OK;
-    return status_from_hip(la::copy_state_dispatch(S_in, z_in, S_out, z_out, s_bytes / 4, z_bytes / 4, stream));
+  if (BH == 0 || N == 0) {
+    int st = LA_OK;
+    if (BH > 0 && S_out)
+      st = status_from_hip(la::copy_state_dispatch(S_in, z_in, S_out, z_out, s_bytes / 4, z_bytes / 4, stream));
+    if (st == LA_OK && events) {  // every pass is empty: all four markers at once
+      for (int i = 0; i < 4; ++i)
+        if (hipEventRecord(events[i], stream) != hipSuccess) return LA_ERR_HIP;
+    }
+    return st;
   }
   if (!q || !k || !v || !out) return LA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_INVALID_ARG;
@@ -148,7 +168,14 @@ int la_forward_ex(const void* q, const void* k, const void* v, void* out, int B,
                 overlaps(z_out, z_bytes, v, tok_bytes) || overlaps(z_out, z_bytes, out, tok_bytes)))
     return LA_ERR_INVALID_ARG;
 
-  const Plan p = make_plan(BH, N, d, dfeat, causal != 0);
+  const bool mapped = feature_map->kind == LA_PERFORMER;
+  if (mapped) {
+    const long long wb = (long long)dfeat * d * 4;
+    if (overlaps(out, tok_bytes, feature_map->W, wb) || overlaps(S_out, s_bytes, feature_map->W, wb) ||
+        overlaps(z_out, z_bytes, feature_map->W, wb))
+      return LA_ERR_INVALID_ARG;
+  }
+  const Plan p = make_plan(BH, N, d, dfeat, causal != 0, mapped);
   if (p.ws_bytes > 0) {
     if (!workspace || workspace_bytes < p.ws_bytes) return LA_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LA_ERR_INVALID_ARG;
@@ -157,13 +184,40 @@ int la_forward_ex(const void* q, const void* k, const void* v, void* out, int B,
         overlaps(workspace, (long long)p.ws_bytes, k, tok_bytes) ||
         overlaps(workspace, (long long)p.ws_bytes, v, tok_bytes) ||
         overlaps(workspace, (long long)p.ws_bytes, S_out, s_bytes) ||
-        overlaps(workspace, (long long)p.ws_bytes, S_in, s_bytes))
+        overlaps(workspace, (long long)p.ws_bytes, S_in, s_bytes) ||
+        (mapped && overlaps(workspace, (long long)p.ws_bytes, feature_map->W, (long long)dfeat * d * 4)))
       return LA_ERR_INVALID_ARG;
   }
 
+  if (events) {
+    if (hipEventRecord(events[0], stream) != hipSuccess) return LA_ERR_HIP;
+  }
+  char* wsb = static_cast<char*>(workspace);
+  const void* qm = q;
+  const void* km = k;
+  if (mapped) {
+    // random features: phi(q), phi(k) into the workspace, in the operand
+    // precision of the chunked passes; those passes then use them as given
+    void* fq = wsb;
+    void* fk = wsb + p.phi_bytes;
+    la::FmapArgs fa{};
+    fa.x = q;
+    fa.phi = fq;
+    fa.rows = BH * N;
+    fa.W = feature_map->W;
+    hipError_t e = la::fmap_dispatch(fa, d, dfeat, la::kPerformer, dtype, dtype, stream);
+    if (e != hipSuccess) return LA_ERR_HIP;
+    fa.x = k;
+    fa.phi = fk;
+    e = la::fmap_dispatch(fa, d, dfeat, la::kPerformer, dtype, dtype, stream);
+    if (e != hipSuccess) return LA_ERR_HIP;
+    qm = fq;
+    km = fk;
+  }
+
   la::FwdArgs a{};
-  a.q = q;
-  a.k = k;
+  a.q = qm;
+  a.k = km;
   a.v = v;
   a.out = out;
   a.BH = (int)BH;
@@ -175,7 +229,7 @@ int la_forward_ex(const void* q, const void* k, const void* v, void* out, int B,
   a.chunks_per_seg_state = p.cpss;
   a.run_state_pass = p.state_pass;
   a.run_scan = p.scan;
-  a.ws = static_cast<float*>(workspace);
+  a.ws = reinterpret_cast<float*>(wsb + 2 * p.phi_bytes);
   a.ws_slots = p.ws_slots;
   a.ws_total_slot = causal ? 0 : p.Ps;
   a.state_elems = dfeat * d + dfeat;
@@ -207,8 +261,8 @@ int la_forward_ex(const void* q, const void* k, const void* v, void* out, int B,
     s.S_out = S_out;
     s.z_out = z_out;
   }
-  return status_from_hip(la::prefill_dispatch(a, s, d, dfeat, feature_map->kind, dtype, causal != 0, stream,
-                                              events));
+  return status_from_hip(la::prefill_dispatch(a, s, d, dfeat, mapped ? la::kPremapped : la::kElu1, dtype,
+                                              causal != 0, stream, events));
 }
 
 int la_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
@@ -239,6 +293,12 @@ int la_decode_step(float* S, float* z, const void* q, const void* k, const void*
       overlaps(out, tb, z, zb) || overlaps(S, sb, z, zb) || overlaps(S, sb, q, tb) || overlaps(S, sb, k, tb) ||
       overlaps(S, sb, v, tb) || overlaps(z, zb, q, tb) || overlaps(z, zb, k, tb) || overlaps(z, zb, v, tb))
     return LA_ERR_INVALID_ARG;
+  if (feature_map->kind == LA_PERFORMER) {
+    const long long wb = (long long)dfeat * d * 4;
+    if (overlaps(out, tb, feature_map->W, wb) || overlaps(S, sb, feature_map->W, wb) ||
+        overlaps(z, zb, feature_map->W, wb))
+      return LA_ERR_INVALID_ARG;
+  }
   la::DecodeArgs a{};
   a.S = S;
   a.z = z;
@@ -265,6 +325,8 @@ int la_feature_map_apply(const void* x, void* phi, long long rows, int d, const 
   const long long xb = rows * d * (in_dtype == LA_BF16 ? 2 : 4);
   const long long pb = rows * dfeat * (out_dtype == LA_BF16 ? 2 : 4);
   if (overlaps(x, xb, phi, pb)) return LA_ERR_INVALID_ARG;
+  if (feature_map->kind == LA_PERFORMER && overlaps(phi, pb, feature_map->W, (long long)dfeat * d * 4))
+    return LA_ERR_INVALID_ARG;
   la::FmapArgs a{};
   a.x = x;
   a.phi = phi;

@@ -6,6 +6,11 @@
 //   S <- S + phi(k) v^T,  z <- z + phi(k),  y = phi(q)^T S / phi(q).z
 // (the state is updated first, so the new token attends to itself).
 //
+// Random features: phi(x) = exp(W x~ - |x~|^2/2) / sqrt(m), x~ = d^(-1/4) x
+// ("Linear Attention", "Mapas de características"), computed per head in fp32
+// from W (m x d, fp32; rounded to bf16 for bf16 inputs) before the state
+// update.
+//
 // The step is a pure stream over the fp32 state: every state element is read
 // once and written once. Each head's DF x D state is covered by TPH threads,
 // each owning a 4-column group (one 16-byte vector) of DF/R rows, so one load
@@ -41,7 +46,7 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <int D, int DF, typename IN>
+template <int D, int DF, typename IN, int FM>
 __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   using SH = DecodeShape<D, DF>;
   __shared__ float s_phiq[SH::HPB][DF];
@@ -49,6 +54,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   __shared__ float s_v[SH::HPB][D];
   __shared__ f32x4 s_num[SH::HPB][SH::R][SH::CG];
   __shared__ float s_den[SH::HPB][SH::WPH];
+  __shared__ float s_x[FM == kPerformer ? SH::HPB : 1][FM == kPerformer ? 2 * D : 1];
 
   const int hb = threadIdx.x / SH::TPH;      // head within block
   const int t = threadIdx.x % SH::TPH;       // thread within head
@@ -65,12 +71,51 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
       Sv[i] = *reinterpret_cast<const f32x4*>(Sh + (long long)(rg + SH::R * i) * D + 4 * cg);
   }
   // token features
-  if (valid) {
-    for (int e = t; e < D; e += SH::TPH) {
-      const long long off = head * D + e;
-      s_phiq[hb][e] = phi_elu1(load_elem<IN>(a.q, off));
-      s_phik[hb][e] = phi_elu1(load_elem<IN>(a.k, off));
-      s_v[hb][e] = load_elem<IN>(a.v, off);
+  if constexpr (FM == kElu1) {
+    if (valid) {
+      for (int e = t; e < D; e += SH::TPH) {
+        const long long off = head * D + e;
+        s_phiq[hb][e] = phi_elu1(load_elem<IN>(a.q, off));
+        s_phik[hb][e] = phi_elu1(load_elem<IN>(a.k, off));
+        s_v[hb][e] = load_elem<IN>(a.v, off);
+      }
+    }
+  } else {
+    if (valid) {
+      for (int e = t; e < D; e += SH::TPH) {
+        const long long off = head * D + e;
+        s_x[hb][e] = load_elem<IN>(a.q, off);
+        s_x[hb][D + e] = load_elem<IN>(a.k, off);
+        s_v[hb][e] = load_elem<IN>(a.v, off);
+      }
+    }
+    __syncthreads();
+    if (valid) {
+      float nq = 0.f, nk = 0.f;
+      for (int e = 0; e < D; ++e) {
+        nq += s_x[hb][e] * s_x[hb][e];
+        nk += s_x[hb][D + e] * s_x[hb][D + e];
+      }
+      const float A = sqrtf(sqrtf(1.0f / (float)D)) * 1.4426950408889634f;
+      const float c = 1.4426950408889634f * 0.5f / sqrtf((float)D);
+      const float Bm = 0.5f * __log2f((float)DF);
+      for (int f = t; f < DF; f += SH::TPH) {
+        const float* wr = a.W + (long long)f * D;
+        float uq = 0.f, uk = 0.f;
+#pragma unroll 4
+        for (int e = 0; e < D; e += 4) {
+          const f32x4 w4 = *reinterpret_cast<const f32x4*>(wr + e);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            // bf16 inputs project with W in bf16, as the chunked forward does
+            const float wj = sizeof(IN) == 2 ? round_bf16(w4[j]) : w4[j];
+            uq += wj * s_x[hb][e + j];
+            uk += wj * s_x[hb][D + e + j];
+          }
+        }
+        s_phiq[hb][f] = __builtin_amdgcn_exp2f(A * uq - c * nq - Bm);
+        s_phik[hb][f] = __builtin_amdgcn_exp2f(A * uk - c * nk - Bm);
+      }
     }
   }
   __syncthreads();
@@ -139,31 +184,36 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   }
 }
 
-template <int D, int DF, typename IN>
+template <int D, int DF, typename IN, int FM>
 static hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   using SH = DecodeShape<D, DF>;
   const int blocks = (a.BH + SH::HPB - 1) / SH::HPB;
-  hipLaunchKernelGGL((decode_step_kernel<D, DF, IN>), dim3(blocks), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_step_kernel<D, DF, IN, FM>), dim3(blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t decode_dispatch(const DecodeArgs& a, int D, int DF, int fmap, int dtype, hipStream_t st) {
-  if (fmap != kElu1) return hipErrorInvalidValue;
-  (void)DF;
-  if (dtype == 1) {
+template <typename IN>
+static hipError_t decode_typed(const DecodeArgs& a, int D, int DF, int fmap, hipStream_t st) {
+  if (fmap == kElu1) {
     switch (D) {
-      case 32: return launch_decode<32, 32, __bf16>(a, st);
-      case 64: return launch_decode<64, 64, __bf16>(a, st);
-      case 128: return launch_decode<128, 128, __bf16>(a, st);
+      case 32: return launch_decode<32, 32, IN, kElu1>(a, st);
+      case 64: return launch_decode<64, 64, IN, kElu1>(a, st);
+      case 128: return launch_decode<128, 128, IN, kElu1>(a, st);
     }
-  } else {
-    switch (D) {
-      case 32: return launch_decode<32, 32, float>(a, st);
-      case 64: return launch_decode<64, 64, float>(a, st);
-      case 128: return launch_decode<128, 128, float>(a, st);
-    }
+    return hipErrorInvalidValue;
   }
+#define LA_PERF_CASE(d, m) \
+  if (D == d && DF == m) return launch_decode<d, m, IN, kPerformer>(a, st);
+  LA_PERF_CASE(32, 64) LA_PERF_CASE(32, 128)
+  LA_PERF_CASE(64, 64) LA_PERF_CASE(64, 128) LA_PERF_CASE(64, 256)
+  LA_PERF_CASE(128, 64) LA_PERF_CASE(128, 128)
+#undef LA_PERF_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t decode_dispatch(const DecodeArgs& a, int D, int DF, int fmap, int dtype, hipStream_t st) {
+  if (dtype == 1) return decode_typed<__bf16>(a, D, DF, fmap, st);
+  return decode_typed<float>(a, D, DF, fmap, st);
 }
 
 // ---------------------------------------------------------------------------

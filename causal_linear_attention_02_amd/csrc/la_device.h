@@ -33,7 +33,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 constexpr int kChunk = 64;      // tokens per chunk (two 32-row MFMA tiles)
 constexpr float kEps = 1e-6f;   // denominator clamp: y = num / max(den, eps)
 
-enum FeatureMap { kElu1 = 0, kPerformer = 1 };
 
 // ---------------------------------------------------------------------------
 // Scalar conversions

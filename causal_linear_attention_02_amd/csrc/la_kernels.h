@@ -6,6 +6,12 @@
 
 namespace la {
 
+enum FeatureMap {
+  kElu1 = 0,       // elu(x) + 1 applied in the kernels
+  kPerformer = 1,  // positive random features
+  kPremapped = 2,  // inputs already hold phi(q), phi(k) (identity inside the kernels)
+};
+
 // Chunked forward (prefill / non-causal). All pointers are device pointers.
 struct FwdArgs {
   const void* q;

@@ -31,63 +31,86 @@
 namespace la {
 
 // ---------------------------------------------------------------------------
-// Staging geometry. NP = 2*D staging threads; thread p holds 8-element
-// pieces i = 0..3 of each tensor at row p/RL + 16 i, columns 8*(p % RL).
-// RL = D/8 threads cover one row; threads with equal p % RL share columns.
+// Staging geometry. NP = 2*D staging threads. Feature-side rows (phi(Q),
+// phi(K); DF values) are covered by RLF = DF/8 threads each, so thread p
+// holds pieces i = 0..NQ-1 at row p/RLF + RSF*i, columns 8*(p % RLF); value
+// rows (D values) by RLV = D/8 threads, pieces i = 0..3 at row p/RLV + 16 i.
+// Threads with equal p % RLF share feature columns.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int DF>
 struct Stage {
   static constexpr int NP = 2 * D;
-  static constexpr int RL = D / 8;
-  static constexpr int kPer = 4;
+  static constexpr int RLF = DF / 8, RSF = NP / RLF, NQ = 64 / RSF;
+  static constexpr int RLV = D / 8;
+  static_assert(NP % RLF == 0 && 64 % RSF == 0 && NQ <= 16, "staging geometry");
+  // register sets for the loads in flight (prefetch distance NSET - 1)
+  static constexpr int NSET = NQ <= 4 ? 3 : 2;
 };
 
-template <int D, typename IN>
+template <int D, int DF, typename IN>
 struct Pref {
-  typename In8<IN>::raw q[4], k[4], v[4];
+  typename In8<IN>::raw q[Stage<D, DF>::NQ], k[Stage<D, DF>::NQ], v[4];
 };
 
-// Byte offset of piece i of staging thread p inside a chunk.
-template <int D, typename IN>
-__device__ __forceinline__ int piece_voff(int p, int i) {
-  constexpr int RL = Stage<D>::RL;
-  return ((p / RL + 16 * i) * D + 8 * (p % RL)) * (int)sizeof(IN);
-}
+template <int D, int DF, typename IN>
+struct Voff {
+  static constexpr bool kSame = DF == D;  // then feature and value pieces coincide
+  int f[Stage<D, DF>::NQ];  // byte offsets of the feature-side pieces
+  int v_[kSame ? 1 : 4];    // byte offsets of the value pieces
+  __device__ __forceinline__ explicit Voff(int p) {
+    using G = Stage<D, DF>;
+#pragma unroll
+    for (int i = 0; i < G::NQ; ++i)
+      f[i] = ((p / G::RLF + G::RSF * i) * DF + 8 * (p % G::RLF)) * (int)sizeof(IN);
+    if constexpr (!kSame) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v_[i] = ((p / G::RLV + 16 * i) * D + 8 * (p % G::RLV)) * (int)sizeof(IN);
+    }
+  }
+  __device__ __forceinline__ int v(int i) const {
+    if constexpr (kSame) return f[i];
+    else return v_[i];
+  }
+};
 
 // Loads of one chunk (rows [row_base, row_base + valid)); rows past the end
-// read as zero through the descriptor's range check.
-template <int D, typename IN, bool LQ, bool LKV>
-__device__ __forceinline__ void prod_load(Pref<D, IN>& pf, const int (&voff)[4], const IN* q, const IN* k,
+// read as zero through the descriptor's range check. q and k rows have DF
+// elements, v rows D.
+template <int D, int DF, typename IN, bool LQ, bool LKV>
+__device__ __forceinline__ void prod_load(Pref<D, DF, IN>& pf, const Voff<D, DF, IN>& vo, const IN* q, const IN* k,
                                           const IN* v, long long row_base, int valid) {
-  const long long eo = row_base * D;
-  const unsigned bytes = (unsigned)(valid * D * (int)sizeof(IN));
+  using G = Stage<D, DF>;
+  const unsigned fbytes = (unsigned)(valid * DF * (int)sizeof(IN));
+  const unsigned vbytes = (unsigned)(valid * D * (int)sizeof(IN));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if constexpr (LQ) pf.q[i] = In8<IN>::bload(make_rsrc(q + eo, bytes), voff[i]);
-    if constexpr (LKV) {
-      pf.k[i] = In8<IN>::bload(make_rsrc(k + eo, bytes), voff[i]);
-      pf.v[i] = In8<IN>::bload(make_rsrc(v + eo, bytes), voff[i]);
-    }
+  for (int i = 0; i < G::NQ; ++i) {
+    if constexpr (LQ) pf.q[i] = In8<IN>::bload(make_rsrc(q + row_base * DF, fbytes), vo.f[i]);
+    if constexpr (LKV) pf.k[i] = In8<IN>::bload(make_rsrc(k + row_base * DF, fbytes), vo.f[i]);
+  }
+  if constexpr (LKV) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pf.v[i] = In8<IN>::bload(make_rsrc(v + row_base * D, vbytes), vo.v(i));
   }
 }
 
-// Key rows past the end of the sequence become -inf, so phi(k) = 0 there.
+// Key rows past the end of the sequence become -inf (elu+1: phi = 0 there)
+// or 0 (pre-mapped features), so they add nothing to the scores, S or z.
 // Branch-free, so every step has the same instruction stream.
-template <int D, typename IN>
-__device__ __forceinline__ void mask_tail_keys(Pref<D, IN>& pf, int p, int valid) {
-  constexpr int RL = Stage<D>::RL;
-  const auto ninf = In8<IN>::neg_inf();
+template <int D, int DF, typename IN, int FM>
+__device__ __forceinline__ void mask_tail_keys(Pref<D, DF, IN>& pf, int p, int valid) {
+  using G = Stage<D, DF>;
+  const auto fill = FM == kElu1 ? In8<IN>::neg_inf() : In8<IN>::zero();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bool past = p / RL + 16 * i >= valid;
+  for (int i = 0; i < G::NQ; ++i) {
+    const bool past = p / G::RLF + G::RSF * i >= valid;
     if constexpr (sizeof(IN) == 2) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pf.k[i][j] = past ? ninf[j] : pf.k[i][j];
+      for (int j = 0; j < 4; ++j) pf.k[i][j] = past ? fill[j] : pf.k[i][j];
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        pf.k[i].a[j] = past ? ninf.a[j] : pf.k[i].a[j];
-        pf.k[i].b[j] = past ? ninf.b[j] : pf.k[i].b[j];
+        pf.k[i].a[j] = past ? fill.a[j] : pf.k[i].a[j];
+        pf.k[i].b[j] = past ? fill.b[j] : pf.k[i].b[j];
       }
     }
   }
@@ -104,44 +127,54 @@ __device__ __forceinline__ void store_raw(uint8_t* tile, int row, int col, const
   }
 }
 
-// Feature map + LDS writes for one chunk. Key rows past the end of the
-// sequence hold -inf, so phi(k) = exp(-inf) = 0 there and they add nothing to
-// the scores, S or z; their values read as zero.
+template <int FM>
+__device__ __forceinline__ float fmap_in_stage(float x) {
+  if constexpr (FM == kElu1) return phi_elu1(x);
+  else return x;  // features already mapped by the random-feature kernel
+}
+
+// Feature map + LDS writes for one chunk.
 // Accumulates, per piece i, dp[i] = sum_e phi(q)[i][e] * z[e] (if LQ) and the
-// column sums of phi(k) over the thread's four rows in cs (if LKV).
-template <int D, typename IN, typename OP, bool LQ, bool LKV>
-__device__ __forceinline__ void prod_stage(const Pref<D, IN>& pf, int p, uint8_t* sQ, uint8_t* sK, uint8_t* sV,
-                                           const float (&z)[8], float (&dp)[4], float (&cs)[8]) {
-  constexpr int RB = D * Ops<OP>::kBytes;
-  constexpr int RL = Stage<D>::RL;
-  const int rg = p / RL, col = 8 * (p % RL);
+// column sums of phi(k) over the thread's rows in cs (if LKV).
+template <int D, int DF, typename IN, typename OP, int FM, bool LQ, bool LKV>
+__device__ __forceinline__ void prod_stage(const Pref<D, DF, IN>& pf, int p, uint8_t* sQ, uint8_t* sK, uint8_t* sV,
+                                           const float (&z)[8], float (&dp)[Stage<D, DF>::NQ], float (&cs)[8]) {
+  using G = Stage<D, DF>;
+  constexpr int RBF = DF * Ops<OP>::kBytes, RBV = D * Ops<OP>::kBytes;
+  const int fcol = 8 * (p % G::RLF);
 #pragma unroll
   for (int e = 0; e < 8; ++e) cs[e] = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = rg + 16 * i;
+  for (int i = 0; i < G::NQ; ++i) {
+    const int row = p / G::RLF + G::RSF * i;
     float x[8];
     if constexpr (LQ) {
       In8<IN>::to_f32(pf.q[i], x);
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        x[e] = phi_elu1(x[e]);
+        x[e] = fmap_in_stage<FM>(x[e]);
         d += x[e] * z[e];
       }
       dp[i] = d;
-      Ops<OP>::template store8<RB>(sQ, row, col, x);
+      Ops<OP>::template store8<RBF>(sQ, row, fcol, x);
     }
     if constexpr (LKV) {
       In8<IN>::to_f32(pf.k[i], x);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        x[e] = phi_elu1(x[e]);
+        x[e] = fmap_in_stage<FM>(x[e]);
         cs[e] += x[e];
       }
-      Ops<OP>::template store8<RB>(sK, row, col, x);
-      store_raw<IN, OP, RB>(sV, row, col, pf.v[i]);
+      Ops<OP>::template store8<RBF>(sK, row, fcol, x);
+      // equal widths: value piece i sits at the same row and column, and
+      // storing it here frees its registers early
+      if constexpr (DF == D) store_raw<IN, OP, RBV>(sV, row, fcol, pf.v[i]);
     }
+  }
+  if constexpr (LKV && DF != D) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) store_raw<IN, OP, RBV>(sV, p / G::RLV + 16 * i, 8 * (p % G::RLV), pf.v[i]);
   }
 }
 
@@ -164,15 +197,16 @@ __device__ __forceinline__ float row_reduce(float x) {
   if constexpr (RL >= 4) x += dpp_mov<kDppQuadXor2>(x);
   if constexpr (RL >= 8) x += dpp_mov<kDppHalfMirror>(x);
   if constexpr (RL >= 16) x += dpp_mov<kDppMirror>(x);
+  if constexpr (RL >= 32) x += __shfl_xor(x, 16, 64);
   return x;
 }
-// Sum over the lanes of a wave that share p % RL.
+// Sum over the lanes of a wave that share lane % RL.
 template <int RL>
 __device__ __forceinline__ float col_reduce(float x) {
   if constexpr (RL <= 4) x += dpp_mov<kDppRor4>(x);
   if constexpr (RL <= 8) x += dpp_mov<kDppRor8>(x);
-  x += xor32(x);
-  x += __shfl_xor(x, 16, 64);
+  if constexpr (RL <= 32) x += xor32(x);
+  if constexpr (RL <= 16) x += __shfl_xor(x, 16, 64);
   return x;
 }
 
@@ -207,15 +241,17 @@ __device__ __forceinline__ void store_state_tiles(const f32x16 (&S)[DF / 32], fl
 // owns value columns [32w, 32w+32) of S.
 // grid = (BH, P), block = 2*D threads.
 // ---------------------------------------------------------------------------
-template <int D, int DF, typename OP, typename IN>
+template <int D, int DF, typename OP, typename IN, int FM>
 __global__ __launch_bounds__(D * 2) void state_pass_kernel(FwdArgs a) {
   using Frag = typename Ops<OP>::frag;
+  using G = Stage<D, DF>;
   constexpr int RBF = DF * Ops<OP>::kBytes;
   constexpr int RBV = D * Ops<OP>::kBytes;
   constexpr int KB = 64 * RBF, VB = 64 * RBV, BUF = KB + VB;
-  constexpr int RL = Stage<D>::RL;
   constexpr int NW = D / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
+  // two staged chunks when they fit; otherwise one, with an extra barrier
+  constexpr int NB = 2 * BUF + NW * DF * 4 <= 160 * 1024 ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NB * BUF];
   __shared__ float zsum[NW][DF];
 
   const int bh = blockIdx.x, seg = blockIdx.y;
@@ -229,41 +265,31 @@ __global__ __launch_bounds__(D * 2) void state_pass_kernel(FwdArgs a) {
   f32x16 S[DF / 32];
 #pragma unroll
   for (int cb = 0; cb < DF / 32; ++cb) S[cb] = f32x16{};
-  float zr[8], cs[8], dp[4];
+  float zr[8], cs[8], dp[G::NQ];
 #pragma unroll
   for (int e = 0; e < 8; ++e) zr[e] = 0.f;
-  int voff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) voff[i] = piece_voff<D, IN>(p, i);
+  const Voff<D, DF, IN> vo(p);
 
-  // chunk m of the segment is held in register set m % 3; it is loaded two
-  // iterations before it is staged into LDS
-  Pref<D, IN> pA, pB, pC;
-  const int nch = c1 - c0;
   // every load is issued (with zero size past the segment) so that all
   // iterations have the same memory instruction stream
-  auto load = [&](Pref<D, IN>& pf, int m) {
+  const int nch = c1 - c0;
+  auto load = [&](Pref<D, DF, IN>& pf, int m) {
     const int c = c0 + m;
     const int valid = m < nch ? min(64, a.N - 64 * c) : 0;
-    prod_load<D, IN, false, true>(pf, voff, nullptr, k, v, base + 64LL * min(c, a.nchunks - 1), valid);
+    prod_load<D, DF, IN, false, true>(pf, vo, nullptr, k, v, base + 64LL * min(c, a.nchunks - 1), valid);
   };
-  auto stage = [&](Pref<D, IN>& pf, int m) {
+  auto stage = [&](Pref<D, DF, IN>& pf, int m) {
     const int c = c0 + m;
-    const int valid = min(64, a.N - 64 * c);
-    mask_tail_keys<D, IN>(pf, p, valid);
-    uint8_t* sK = smem + (m & 1) * BUF;
-    prod_stage<D, IN, OP, false, true>(pf, p, nullptr, sK, sK + KB, zr, dp, cs);
+    mask_tail_keys<D, DF, IN, FM>(pf, p, min(64, a.N - 64 * c));
+    uint8_t* sK = smem + (NB == 2 ? (m & 1) : 0) * BUF;
+    prod_stage<D, DF, IN, OP, FM, false, true>(pf, p, nullptr, sK, sK + KB, zr, dp, cs);
 #pragma unroll
     for (int e = 0; e < 8; ++e) zr[e] += cs[e];
   };
-  load(pA, 0);
-  load(pB, 1);
-  if (nch > 0) stage(pA, 0);
-  __syncthreads();
-  // iteration m: load chunk m+2, multiply chunk m, stage chunk m+1
-  auto iter = [&](int m, Pref<D, IN>& ld, Pref<D, IN>& st) {
-    load(ld, m + 2);
-    const uint8_t* sK = smem + (m & 1) * BUF;
+  // iteration m: multiply chunk m (in LDS), stage chunk m+1, and keep the
+  // loads of the following chunk(s) in flight
+  auto mult = [&](int m) {
+    const uint8_t* sK = smem + (NB == 2 ? (m & 1) : 0) * BUF;
     const uint8_t* sV = sK + KB;
     Frag Vf[4];
 #pragma unroll
@@ -273,18 +299,43 @@ __global__ __launch_bounds__(D * 2) void state_pass_kernel(FwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
         Ops<OP>::mma(S[cb], Ops<OP>::template load_cols<RBF>(sK, 16 * kb, 32 * cb), Vf[kb]);
+  };
+  // iteration m multiplies chunk m (LDS), stages chunk m+1 (registers) and
+  // issues the loads of chunk m+NSET into the set chunk m occupied
+  auto iter = [&](int m, Pref<D, DF, IN>& ld, Pref<D, DF, IN>& st) {
+    load(ld, m + G::NSET);
+    mult(m);
+    if constexpr (NB == 1) __syncthreads();
     if (m + 1 < nch) stage(st, m + 1);
     __syncthreads();
   };
-  for (int m = 0; m < nch; m += 3) {
-    iter(m, pC, pB);
-    if (m + 1 < nch) iter(m + 1, pA, pC);
-    if (m + 2 < nch) iter(m + 2, pB, pA);
+  if constexpr (G::NSET == 3) {
+    Pref<D, DF, IN> pA, pB, pC;
+    load(pA, 0);
+    load(pB, 1);
+    load(pC, 2);
+    if (nch > 0) stage(pA, 0);
+    __syncthreads();
+    for (int m = 0; m < nch; m += 3) {
+      iter(m, pA, pB);
+      if (m + 1 < nch) iter(m + 1, pB, pC);
+      if (m + 2 < nch) iter(m + 2, pC, pA);
+    }
+  } else {
+    Pref<D, DF, IN> pA, pB;
+    load(pA, 0);
+    load(pB, 1);
+    if (nch > 0) stage(pA, 0);
+    __syncthreads();
+    for (int m = 0; m < nch; m += 2) {
+      iter(m, pA, pB);
+      if (m + 1 < nch) iter(m + 1, pB, pA);
+    }
   }
   // z: reduce the per-thread column sums over rows (lanes, then waves)
 #pragma unroll
-  for (int e = 0; e < 8; ++e) zr[e] = col_reduce<RL>(zr[e]);
-  if (l < RL) {
+  for (int e = 0; e < 8; ++e) zr[e] = col_reduce<G::RLF>(zr[e]);
+  if (l < G::RLF) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) zsum[w][8 * l + e] = zr[e];
   }
@@ -357,12 +408,11 @@ struct OutLayout {
   static constexpr int BYTES = NB * BUF + DEN + ZP + YB;
 };
 
-template <int D, int DF, typename OP, typename IN, bool CAUSAL>
+template <int D, int DF, typename OP, typename IN, int FM, bool CAUSAL>
 __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
   using Frag = typename Ops<OP>::frag;
   using L = OutLayout<D, DF, OP, IN, CAUSAL>;
-  constexpr int RL = Stage<D>::RL;
-  static_assert(DF == D, "elu+1 keeps d' = d");
+  using G = Stage<D, DF>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
   float* dbuf = reinterpret_cast<float*>(smem + L::NB * L::BUF);
   float* zpart = reinterpret_cast<float*>(smem + L::NB * L::BUF + L::DEN);
@@ -396,14 +446,11 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
 
   if (producer) {
     // ------------------------------------------------------------------
-    // producers: chunk `it` is loaded during step it-1 and staged in step it
+    // producers: chunk `it` is loaded NSET-1 steps before step it stages it
     // ------------------------------------------------------------------
-    Pref<D, IN> pA, pB, pC;
-    float zrun[8], dp[4], cs[8];
-    const int cr = 8 * (p % RL);
-    int voff[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) voff[i] = piece_voff<D, IN>(p, i);
+    float zrun[8], dp[G::NQ], cs[8];
+    const int cr = 8 * (p % G::RLF);
+    const Voff<D, DF, IN> vo(p);
 #pragma unroll
     for (int e = 0; e < 8; ++e) zrun[e] = zinit ? zinit[cr + e] : 0.f;
     // Drain that load now: otherwise the wait-count analysis carries it
@@ -411,42 +458,37 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
     wait_vmem_all();
     // every load and store below is issued in every step (zero size when out
     // of range), so the wait counts are the same on every path
-    auto load = [&](Pref<D, IN>& pf, int it) {
+    auto load = [&](Pref<D, DF, IN>& pf, int it) {
       const int c = c0 + it;
       const int valid = it < n ? min(64, a.N - 64 * c) : 0;
-      prod_load<D, IN, true, CAUSAL>(pf, voff, q, k, v, base + 64LL * min(c, a.nchunks - 1), valid);
+      prod_load<D, DF, IN, true, CAUSAL>(pf, vo, q, k, v, base + 64LL * min(c, a.nchunks - 1), valid);
     };
-    load(pA, 0);
-    load(pB, 1);
 
-    // step `it` stores the output tile of chunk it-2, stages chunk it (held in
-    // `cur`) and issues the loads of chunk it+2 into `nxt`
-    auto pstep = [&](int it, Pref<D, IN>& cur, Pref<D, IN>& nxt) {
+    // step `it` stores the output tile of chunk it-2, stages chunk it (held
+    // in `cur`) and issues the loads of chunk it+NSET-1 into `nxt`
+    auto pstep = [&](int it, Pref<D, DF, IN>& cur, Pref<D, DF, IN>& nxt) {
       if constexpr (L::YS) {
-        {
-          const int c = c0 + max(it - 2, 0);
-          const int valid = it >= 2 ? min(64, a.N - 64 * c) : 0;
-          const uint8_t* yb = ybuf + (it & 1) * L::YB1;
-          const auto ro = make_rsrc(out + (base + 64LL * c) * D, (unsigned)(valid * D * (int)sizeof(IN)));
-          const int rg = p / RL, col = 8 * (p % RL);
+        const int c = c0 + max(it - 2, 0);
+        const int valid = it >= 2 ? min(64, a.N - 64 * c) : 0;
+        const uint8_t* yb = ybuf + (it & 1) * L::YB1;
+        const auto ro = make_rsrc(out + (base + 64LL * c) * D, (unsigned)(valid * D * (int)sizeof(IN)));
+        const int rg = p / G::RLV, col = 8 * (p % G::RLV);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = rg + 16 * i;
-            if constexpr (sizeof(IN) == 2) {
-              buf_store16(ro, voff[i], *reinterpret_cast<const u32x4*>(yb + tile_off<L::RBY>(row, col * 2)));
-            } else {
-              buf_store16(ro, voff[i], *reinterpret_cast<const u32x4*>(yb + tile_off<L::RBY>(row, col * 4)));
-              buf_store16(ro, voff[i] + 16, *reinterpret_cast<const u32x4*>(yb + tile_off<L::RBY>(row, col * 4 + 16)));
-            }
+        for (int i = 0; i < 4; ++i) {
+          const int row = rg + 16 * i;
+          if constexpr (sizeof(IN) == 2) {
+            buf_store16(ro, vo.v(i), *reinterpret_cast<const u32x4*>(yb + tile_off<L::RBY>(row, col * 2)));
+          } else {
+            buf_store16(ro, vo.v(i), *reinterpret_cast<const u32x4*>(yb + tile_off<L::RBY>(row, col * 4)));
+            buf_store16(ro, vo.v(i) + 16, *reinterpret_cast<const u32x4*>(yb + tile_off<L::RBY>(row, col * 4 + 16)));
           }
         }
       }
-      load(nxt, it + 2);
+      load(nxt, it + G::NSET - 1);
       if (it < n) {
         const int c = c0 + it;
-        const int valid = min(64, a.N - 64 * c);
         if constexpr (CAUSAL) {
-          mask_tail_keys<D, IN>(cur, p, valid);
+          mask_tail_keys<D, DF, IN, FM>(cur, p, min(64, a.N - 64 * c));
           // z_{it-1} = z_{it-2} + column sums of chunk it-1 (all producer waves)
           if (it >= 1) {
             const float* zp = zpart + ((it - 1) & 1) * L::NWP * DF;
@@ -464,12 +506,12 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
         }
         uint8_t* sQ = smem + (L::NB == 2 ? (it & 1) : 0) * L::BUF;
         if constexpr (L::NB == 1) __syncthreads();  // consumers are done with the buffer
-        prod_stage<D, IN, OP, true, CAUSAL>(cur, p, sQ, sQ + L::QB, sQ + L::QB + L::KB, zrun, dp, cs);
+        prod_stage<D, DF, IN, OP, FM, true, CAUSAL>(cur, p, sQ, sQ + L::QB, sQ + L::QB + L::KB, zrun, dp, cs);
         if constexpr (CAUSAL) {
           // publish this chunk's column sums of phi(K)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) cs[e] = col_reduce<RL>(cs[e]);
-          if (l < RL) {
+          for (int e = 0; e < 8; ++e) cs[e] = col_reduce<G::RLF>(cs[e]);
+          if (l < G::RLF) {
             float* zw = zpart + (it & 1) * L::NWP * DF + pw * DF + cr;
             *reinterpret_cast<f32x4*>(zw) = f32x4{cs[0], cs[1], cs[2], cs[3]};
             *reinterpret_cast<f32x4*>(zw + 4) = f32x4{cs[4], cs[5], cs[6], cs[7]};
@@ -479,9 +521,9 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
         if (a.normalize) {
           float* db = dbuf + (it & 1) * 64;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float s = row_reduce<RL>(dp[i]);
-            if ((p % RL) == 0) db[p / RL + 16 * i] = s;
+          for (int i = 0; i < G::NQ; ++i) {
+            const float s = row_reduce<G::RLF>(dp[i]);
+            if ((p % G::RLF) == 0) db[p / G::RLF + G::RSF * i] = s;
           }
         }
       } else {
@@ -497,13 +539,25 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
       }
       __syncthreads();
     };
-    for (int it = 0; it <= n + LAST; it += 3) {
-      pstep(it, pA, pC);
-      if (it + 1 <= n + LAST) pstep(it + 1, pB, pA);
-      if (it + 2 <= n + LAST) pstep(it + 2, pC, pB);
+    if constexpr (G::NSET == 3) {
+      Pref<D, DF, IN> pA, pB, pC;
+      load(pA, 0);
+      load(pB, 1);
+      for (int it = 0; it <= n + LAST; it += 3) {
+        pstep(it, pA, pC);
+        if (it + 1 <= n + LAST) pstep(it + 1, pB, pA);
+        if (it + 2 <= n + LAST) pstep(it + 2, pC, pB);
+      }
+    } else {
+      Pref<D, DF, IN> pA, pB;
+      load(pA, 0);
+      for (int it = 0; it <= n + LAST; it += 2) {
+        pstep(it, pA, pB);
+        if (it + 1 <= n + LAST) pstep(it + 1, pB, pA);
+      }
     }
     if constexpr (CAUSAL) {
-      if (a.S_out && seg == a.nseg - 1 && p < RL) {
+      if (a.S_out && seg == a.nseg - 1 && p < G::RLF) {
         float* zo = a.z_out + (long long)bh * DF + cr;
 #pragma unroll
         for (int e = 0; e < 8; ++e) zo[e] = zrun[e];
@@ -634,12 +688,12 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // Host-side launchers (one instantiation per supported shape)
 // ---------------------------------------------------------------------------
-template <int D, int DF, typename OP, typename IN>
+template <int D, int DF, typename OP, typename IN, int FM>
 static hipError_t launch_prefill(const FwdArgs& a, const ScanArgs& s, bool causal, hipStream_t st,
                                  hipEvent_t* ev) {
-  if (ev) (void)hipEventRecord(ev[0], st);
+  // ev[0] is recorded by the caller (before any feature-map kernels)
   if (a.run_state_pass) {
-    hipLaunchKernelGGL((state_pass_kernel<D, DF, OP, IN>), dim3(a.BH, a.nseg_state), dim3(D * 2), 0, st, a);
+    hipLaunchKernelGGL((state_pass_kernel<D, DF, OP, IN, FM>), dim3(a.BH, a.nseg_state), dim3(D * 2), 0, st, a);
   }
   if (ev) (void)hipEventRecord(ev[1], st);
   if (a.run_scan) {
@@ -647,32 +701,39 @@ static hipError_t launch_prefill(const FwdArgs& a, const ScanArgs& s, bool causa
   }
   if (ev) (void)hipEventRecord(ev[2], st);
   if (causal) {
-    hipLaunchKernelGGL((output_pass_kernel<D, DF, OP, IN, true>), dim3(a.BH, a.nseg), dim3(D * 4), 0, st, a);
+    hipLaunchKernelGGL((output_pass_kernel<D, DF, OP, IN, FM, true>), dim3(a.BH, a.nseg), dim3(D * 4), 0, st, a);
   } else {
-    hipLaunchKernelGGL((output_pass_kernel<D, DF, OP, IN, false>), dim3(a.BH, a.nseg), dim3(D * 4), 0, st, a);
+    hipLaunchKernelGGL((output_pass_kernel<D, DF, OP, IN, FM, false>), dim3(a.BH, a.nseg), dim3(D * 4), 0, st, a);
   }
   if (ev) (void)hipEventRecord(ev[3], st);
   return hipGetLastError();
 }
 
+template <typename T>
+static hipError_t prefill_typed(const FwdArgs& a, const ScanArgs& s, int D, int DF, int fmap, bool causal,
+                                hipStream_t st, hipEvent_t* ev) {
+  if (fmap == kElu1) {
+    switch (D) {
+      case 32: return launch_prefill<32, 32, T, T, kElu1>(a, s, causal, st, ev);
+      case 64: return launch_prefill<64, 64, T, T, kElu1>(a, s, causal, st, ev);
+      case 128: return launch_prefill<128, 128, T, T, kElu1>(a, s, causal, st, ev);
+    }
+    return hipErrorInvalidValue;
+  }
+#define LA_PRE_CASE(d, m) \
+  if (D == d && DF == m) return launch_prefill<d, m, T, T, kPremapped>(a, s, causal, st, ev);
+  LA_PRE_CASE(32, 64) LA_PRE_CASE(32, 128)
+  LA_PRE_CASE(64, 64) LA_PRE_CASE(64, 128) LA_PRE_CASE(64, 256)
+  LA_PRE_CASE(128, 64) LA_PRE_CASE(128, 128)
+#undef LA_PRE_CASE
+  return hipErrorInvalidValue;
+}
+
 hipError_t prefill_dispatch(const FwdArgs& a, const ScanArgs& s, int D, int DF, int fmap, int dtype, bool causal,
                             hipStream_t st, hipEvent_t* ev) {
-  if (fmap != kElu1) return hipErrorInvalidValue;
-  (void)DF;
-  if (dtype == 1) {  // bf16
-    switch (D) {
-      case 32: return launch_prefill<32, 32, __bf16, __bf16>(a, s, causal, st, ev);
-      case 64: return launch_prefill<64, 64, __bf16, __bf16>(a, s, causal, st, ev);
-      case 128: return launch_prefill<128, 128, __bf16, __bf16>(a, s, causal, st, ev);
-    }
-  } else {
-    switch (D) {
-      case 32: return launch_prefill<32, 32, float, float>(a, s, causal, st, ev);
-      case 64: return launch_prefill<64, 64, float, float>(a, s, causal, st, ev);
-      case 128: return launch_prefill<128, 128, float, float>(a, s, causal, st, ev);
-    }
-  }
-  return hipErrorInvalidValue;
+  if (fmap != kElu1 && fmap != kPremapped) return hipErrorInvalidValue;
+  if (dtype == 1) return prefill_typed<__bf16>(a, s, D, DF, fmap, causal, st, ev);
+  return prefill_typed<float>(a, s, D, DF, fmap, causal, st, ev);
 }
 
 }  // namespace la

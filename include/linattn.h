@@ -25,7 +25,9 @@
  *   - Element type of q, k, v and out: LA_BF16 or LA_F32 (same for all four).
  *     bf16 inputs are multiplied on bf16 matrix cores with fp32 accumulation;
  *     fp32 inputs use fp32 matrix cores. State is always fp32.
- *   - Supported: d in {32, 64, 128}.
+ *   - Supported: d in {32, 64, 128} with elu+1; random features with
+ *     (d, m) in {(32, 64), (32, 128), (64, 64), (64, 128), (64, 256),
+ *     (128, 64), (128, 128)}. Other valid requests return LA_ERR_UNSUPPORTED.
  *   - Ownership: the caller allocates and frees every buffer. The library
  *     keeps no pointer after returning and allocates no device memory.
  *   - Errors: validation happens before anything is enqueued, so a failed
@@ -73,8 +75,10 @@ int la_version(void);
 const char* la_status_string(int status);
 
 /*
- * Bytes of fp32 device workspace that la_forward needs for these sizes
- * (0 when none is needed). Returns 0 also for invalid arguments.
+ * Bytes of device workspace that la_forward needs for these sizes (0 when
+ * none is needed; any element type). Returns 0 also for invalid arguments.
+ * It holds the fp32 states of the sequence segments and, for random features,
+ * phi(q) and phi(k) ([B][H][N][m] each, sized for fp32).
  */
 size_t la_forward_workspace_size(int B, int H, int N, int d, const la_feature_map* feature_map, int causal);
 
@@ -103,9 +107,10 @@ int la_forward(const void* q, const void* k, const void* v, void* out, int B, in
 
 /*
  * la_forward, plus timing markers: when `events` is not NULL it points to 4
- * caller-created HIP events that are recorded on `stream` before the state
- * pass, before the carry scan, before the output pass and after the output
- * pass (a skipped pass has zero length).
+ * caller-created HIP events that are recorded on `stream` before the first
+ * kernel (the random-feature map, when used, else the state pass), before the
+ * carry scan, before the output pass and after the output pass (a skipped
+ * pass has zero length).
  */
 int la_forward_ex(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
                   const la_feature_map* feature_map, int causal, int normalize, int dtype, const float* S_in,
@@ -127,7 +132,9 @@ int la_decode_step(float* S, float* z, const void* q, const void* k, const void*
 /*
  * The feature map alone ("Mapas de características"): phi applied to each row.
  *   x    in:  [rows][d], element type in_dtype.
- *   phi  out: [rows][d'], element type out_dtype; must not overlap x.
+ *   phi  out: [rows][d'], element type out_dtype; must not overlap x or W.
+ * Random features with bf16 input multiply in bf16 (W rounded to bf16) with
+ * fp32 accumulation; the exponential and the output are computed in fp32.
  */
 int la_feature_map_apply(const void* x, void* phi, long long rows, int d, const la_feature_map* feature_map,
                          int in_dtype, int out_dtype, hipStream_t stream);

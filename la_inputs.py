@@ -98,7 +98,7 @@ def performer_W(m: int, d: int, seed: int, bf16: bool = True) -> np.ndarray:
         blocks.append(qm.T)
     w = np.concatenate(blocks, axis=0)[:m]
     lengths = np.linalg.norm(rng.standard_normal((m, d)), axis=1)
-    w = (w * lengths[:, None]).astype(np.float32)
+    w = np.ascontiguousarray((w * lengths[:, None]).astype(np.float32))
     return bf16_round(w) if bf16 else w
 
 
