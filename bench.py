@@ -36,13 +36,48 @@ def parse():
     p.add_argument("--decode-warmup", type=int, default=20)
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-heads", type=int, default=1, help="heads of the prefill the oracle times")
-    p.add_argument("--cpu-decode-steps", type=int, default=2)
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="time budget of the oracle's prefill sample (whole heads; the decode sample gets half)")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="first run a plain device-to-device copy of this size three times (counter calibration)")
     return p.parse_args()
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest(names):
+    """sha256 over the kernel sources a counter summary was taken with."""
+    import hashlib
+    h = hashlib.sha256()
+    base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "causal_linear_attention_02_amd", "csrc")
+    for n in names:
+        with open(os.path.join(base, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(summary, sources, bytes_per_launch):
+    """HBM bytes per launch from a committed counter summary (key = value lines).
+
+    Returns (traffic_bytes, note). traffic is None when the summary is missing
+    or was taken with kernel sources other than the current ones."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", summary)
+    try:
+        with open(path) as f:
+            kv = dict(line.split("=", 1) for line in f.read().splitlines() if "=" in line and not line.startswith("#"))
+    except OSError:
+        return None, "no counter summary"
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_digest") != kernel_source_digest(sources):
+        return None, "kernel changed since the counters were taken"
+    try:
+        t = float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None, "summary without traffic"
+    return t, f"{summary}: read {kv.get('read_bytes_per_launch')} + write {kv.get('write_bytes_per_launch')} B " \
+              f"(calibrated FETCH_SIZE/WRITE_SIZE), {t / bytes_per_launch:.3f} x algorithmic"
 
 
 def blas_threads():
@@ -67,6 +102,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe_mib > 0:
+        nb = args.copy_probe_mib << 20
+        log(f"copy probe: 3 x {nb} bytes device-to-device")
+        src = torch.ones(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     W = la_inputs.WORKLOADS["prefill_b1h16n65536d128"]
     B, H, N, d = W["B"], W["H"], W["N"], W["d"]
 
@@ -112,6 +156,9 @@ def main():
 
     del tq, tk, tv, out, ws
     torch.cuda.empty_cache()
+    prefill_sources = ["la_prefill.hip", "la_device.h", "la_kernels.h"]
+    out_traffic, out_note = read_traffic("traffic_output_pass_prefill_b1h16n65536d128.txt", prefill_sources,
+                                         alg_bytes)
 
     # ---------------- decode ----------------
     decode = None
@@ -160,6 +207,8 @@ def main():
         step_bytes = heads * (2 * 4 * (dd * dd + dd) + 3 * 2 * dd + 2 * dd)
         k_ms = float(kern_ms.mean())
         d_gbs = step_bytes / (k_ms * 1e-3) / 1e9
+        dec_traffic, dec_note = read_traffic("traffic_decode_step_decode_s256h32d64.txt",
+                                             ["la_decode.hip", "la_device.h", "la_kernels.h"], step_bytes)
         decode = {
             "metric": "decode steps/s",
             "value": T / dwall,
@@ -170,7 +219,8 @@ def main():
                        "prefill_tokens": N0, "state": "fp32", "inputs": "bf16"},
             "roofline": {"bound": "hbm", "kernel": "decode_step_kernel", "achieved": round(d_gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(d_gbs / HBM_PEAK_GBS, 4),
-                         "traffic": None, "bytes_per_launch": step_bytes, "avg_launch_us": round(k_ms * 1e3, 2)},
+                         "traffic": dec_traffic, "traffic_note": dec_note, "bytes_per_launch": step_bytes,
+                         "avg_launch_us": round(k_ms * 1e3, 2)},
         }
         log(f"decode: {dwall*1e6/T:.1f} us/step wall, kernel {k_ms*1e3:.1f} us, {d_gbs:.0f} GB/s")
         del sq, sk, sv, S, z, y
@@ -179,14 +229,16 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle as O
-        nh = max(1, min(args.cpu_heads, H))
-        qc, kc, vc = la_inputs.gaussian_qkv(1, nh, N, d, seed=W["seed"] + 1, scale=W["scale"], bf16=True)
-        log(f"cpu baseline: oracle blockwise form on {nh} head(s) x {N} tokens")
-        t0 = time.perf_counter()
-        O.chunked(qc, kc, vc, "elu1", causal=True, normalize=True, chunk=64)
-        tc = time.perf_counter() - t0
+        log(f"cpu baseline: oracle blockwise form, whole heads of {N} tokens, budget {args.cpu_seconds:.0f} s")
+        nh, tc = 0, 0.0
+        while nh < H and tc < args.cpu_seconds:
+            qc, kc, vc = la_inputs.gaussian_qkv(1, 1, N, d, seed=W["seed"] + 1 + nh, scale=W["scale"], bf16=True)
+            t0 = time.perf_counter()
+            O.chunked(qc, kc, vc, "elu1", causal=True, normalize=True, chunk=64)
+            tc += time.perf_counter() - t0
+            nh += 1
         cpu = {"value": (nh * N / H) / tc, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
-               "sample": f"oracle.chunked (fp64) on {nh} of {H} heads x {N} tokens, d={d}; "
+               "sample": f"oracle.chunked (fp64, numpy) on {nh} of {H} heads x {N} tokens, d={d}; "
                          f"tokens/s = B*N*(heads timed/H)/time", "seconds": round(tc, 2)}
         if decode is not None:
             Wd = la_inputs.WORKLOADS["decode_s256h32d64"]
@@ -194,15 +246,15 @@ def main():
             rng = np.random.default_rng(0)
             Sd = rng.standard_normal((heads, Wd["d"], Wd["d"]))
             zd = np.abs(rng.standard_normal((heads, Wd["d"]))) * 100
-            toks = [la_inputs.decode_tokens(Wd["step_seed"], t, (heads, Wd["d"]))
-                    for t in range(args.cpu_decode_steps)]
-            t0 = time.perf_counter()
-            for (tq_, tk_, tv_) in toks:
+            nt, td = 0, 0.0
+            while nt < 1000 and td < args.cpu_seconds / 2:
+                tq_, tk_, tv_ = la_inputs.decode_tokens(Wd["step_seed"], nt, (heads, Wd["d"]))
+                t0 = time.perf_counter()
                 _, Sd, zd = O.decode_step(Sd, zd, tq_, tk_, tv_, "elu1")
-            td = time.perf_counter() - t0
-            cpu["decode"] = {"value": args.cpu_decode_steps / td, "unit": "steps/s",
-                             "sample": f"oracle.decode_step (fp64) over all {heads} heads, "
-                                       f"{args.cpu_decode_steps} steps"}
+                td += time.perf_counter() - t0
+                nt += 1
+            cpu["decode"] = {"value": nt / td, "unit": "steps/s", "seconds": round(td, 2),
+                             "sample": f"oracle.decode_step (fp64, numpy) over all {heads} heads, {nt} steps"}
 
     result = {
         "metric": "causal linear-attn prefill tokens/s (N=64K,d=128) + decode steps/s, % roofline",
@@ -221,7 +273,8 @@ def main():
                    "feature_map": "elu1", "causal": True, "normalize": True, "chunk": C, "accumulate": "fp32"},
         "roofline": {"bound": "hbm", "kernel": "output_pass_kernel", "achieved": round(out_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(out_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": alg_bytes, "avg_launch_us": round(ms_out * 1e3, 2)},
+                     "traffic": out_traffic, "traffic_note": out_note, "bytes_per_launch": alg_bytes,
+                     "avg_launch_us": round(ms_out * 1e3, 2)},
         "prefill_breakdown_us": {"state_pass": round(ms_state * 1e3, 2), "carry_scan": round(ms_scan * 1e3, 2),
                                  "output_pass": round(ms_out * 1e3, 2)},
         "prefill_whole_op": {"achieved_gbs": round(whole_gbs, 1), "frac_hbm": round(whole_gbs / HBM_PEAK_GBS, 4),
