@@ -1,0 +1,95 @@
+"""The oracle pins catch plausible mistakes in the oracle.
+
+Each case plants one mistake (a dropped term, a wrong sign, an off-by-one
+index, a transposed operand, an exclusive instead of inclusive mask, ...) in
+a copy of the oracle package, runs tests/test_oracle_pins.py against that
+copy in a fresh interpreter, and requires the pins to fail. Two controls
+check the harness itself: an unaltered copy passes, and a copy that cannot
+be imported fails.
+"""
+
+import os
+import pathlib
+import subprocess
+import sys
+
+import pytest
+
+ROOT = pathlib.Path(__file__).resolve().parent.parent
+SRC = (ROOT / "oracle" / "linattn_oracle.py").read_text()
+INIT = (ROOT / "oracle" / "__init__.py").read_text()
+
+# (text in the oracle, replacement, the mistake it stands for)
+MUTANTS = [
+    ("np.arange(N)[None, :] <= idx[:, None]", "np.arange(N)[None, :] < idx[:, None]",
+     "definition: causal mask excludes the diagonal"),
+    ("A = Qf[g] @ Kf[g].T", "A = Kf[g][:idx.size] @ Qf[g].T",
+     "definition: similarity matrix transposed"),
+    ("num = A @ V[g] + Qf[g] @ S[g]", "num = A @ V[g]", "definition: initial state dropped from the numerator"),
+    ("den = A.sum(axis=1) + Qf[g] @ z[g]", "den = A.sum(axis=1)",
+     "definition: initial state dropped from the denominator"),
+    ("return num / np.maximum(den, EPS)[..., None]", "return num / (den + EPS)[..., None]",
+     "eps added to the denominator instead of a clamp"),
+    ("np.where(x > 0.0, x + 1.0, np.exp(np.minimum(x, 0.0)))", "np.where(x > 0.0, x, np.exp(np.minimum(x, 0.0)))",
+     "elu+1 without the +1"),
+    ("np.where(x > 0.0, x + 1.0, np.exp(np.minimum(x, 0.0)))",
+     "np.where(x > 0.0, x + 1.0, np.exp(np.minimum(x, 0.0)) - 1.0)", "plain elu on the negative branch"),
+    ("xt = x * d ** -0.25", "xt = x", "random features: input not scaled by d^(-1/4)"),
+    ("xt = x * d ** -0.25", "xt = x * d ** -0.5", "random features: input scaled by d^(-1/2)"),
+    ("return np.exp(u - 0.5 * sq) / np.sqrt(m)", "return np.exp(u - 0.5 * sq)",
+     "random features: 1/sqrt(m) dropped"),
+    ("return np.exp(u - 0.5 * sq) / np.sqrt(m)", "return np.exp(u + 0.5 * sq) / np.sqrt(m)",
+     "random features: wrong sign of the norm term"),
+    ("u = xt @ W.T", "u = xt @ W[:, ::-1].T", "random features: W columns reversed"),
+    ("S = S + np.einsum(\"gnc,gne->gce\", Kf, V)", "S = S + np.einsum(\"gnc,gne->gce\", Kf[:, 1:], V[:, :-1])",
+     "final state: keys and values misaligned by one"),
+    ("z = z + Kf.sum(axis=1)", "z = z + Kf[:, 1:].sum(axis=1)", "final state: first key dropped from z"),
+    ("den = np.einsum(\"gnc,gc->gn\", Qf, z)", "den = np.einsum(\"gnc,gc->gn\", Qf, z[:, ::-1])",
+     "non-causal form: normalizer read with reversed feature index"),
+    ("S_new = S + kf[..., :, None] * v[..., None, :]", "S_new = S + qf[..., :, None] * v[..., None, :]",
+     "decode: state updated with phi(q)"),
+    ("num = np.einsum(\"...c,...ce->...e\", qf, S_new)", "num = np.einsum(\"...c,...ce->...e\", qf, S)",
+     "decode: numerator read before the update"),
+    ("den = np.einsum(\"...c,...c->...\", qf, z_new)", "den = np.einsum(\"...c,...c->...\", qf, z)",
+     "decode: denominator read before the update"),
+    ("y[:, t], S, z = decode_step(S, z, Q[:, t], K[:, t], V[:, t], fmap, W, normalize)",
+     "y[:, t], S, z = decode_step(S, z, Q[:, t], K[:, t], V[:, max(t - 1, 0)], fmap, W, normalize)",
+     "recurrent loop: value of the previous token"),
+    ("S = np.cumsum(kv, axis=1)", "S = np.cumsum(kv, axis=1) - kv", "cumulative form: exclusive prefix for S"),
+    ("A = A * np.tril(np.ones((e - s, e - s)))[None]", "A = A * np.tril(np.ones((e - s, e - s)), -1)[None]",
+     "blockwise form: strict mask inside the block"),
+    ("+ np.einsum(\"gic,gce->gie\", qc, S)", "+ 0.0", "blockwise form: inter-block numerator dropped"),
+    ("den = A.sum(axis=2) + np.einsum(\"gic,gc->gi\", qc, z)", "den = A.sum(axis=2)",
+     "blockwise form: inter-block denominator dropped"),
+    ("        z = z + kc.sum(axis=1)\n", "        z = z + kc[:, :-1].sum(axis=1)\n",
+     "blockwise form: last key of each block dropped from z"),
+]
+
+
+def _run_pins(tmp_path, src, init=INIT):
+    pkg = tmp_path / "oracle"
+    pkg.mkdir()
+    (pkg / "linattn_oracle.py").write_text(src)
+    (pkg / "__init__.py").write_text(init)
+    env = dict(os.environ, LA_ORACLE_UNDER_TEST=str(tmp_path), PYTHONDONTWRITEBYTECODE="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", str(ROOT / "tests" / "test_oracle_pins.py"), "-x", "-q",
+                        "-p", "no:cacheprovider"], env=env, cwd=str(ROOT), capture_output=True, text=True,
+                       timeout=600)
+    return r.returncode, r.stdout[-2000:]
+
+
+def test_control_unaltered_copy_passes(tmp_path):
+    rc, out = _run_pins(tmp_path, SRC)
+    assert rc == 0, out
+
+
+def test_control_copy_is_the_one_imported(tmp_path):
+    rc, _ = _run_pins(tmp_path, "raise ImportError('altered copy')\n")
+    assert rc != 0
+
+
+@pytest.mark.parametrize("old,new,what", MUTANTS, ids=[m[2] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, old, new, what):
+    assert SRC.count(old) >= 1, f"mutation site not found: {old!r}"
+    rc, out = _run_pins(tmp_path, SRC.replace(old, new, 1))
+    assert rc != 0, f"the pins did not catch: {what}\n{out}"
