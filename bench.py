@@ -223,7 +223,27 @@ def main():
                          "avg_launch_us": round(k_ms * 1e3, 2)},
         }
         log(f"decode: {dwall*1e6/T:.1f} us/step wall, kernel {k_ms*1e3:.1f} us, {d_gbs:.0f} GB/s")
-        del sq, sk, sv, S, z, y
+        # the same T steps (next tokens, same state) captured once as a HIP graph and replayed
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            graph.capture_begin()
+            for t in range(T):
+                la.la_decode_step(S, z, sq[args.decode_warmup + t], sk[args.decode_warmup + t],
+                                  sv[args.decode_warmup + t], out=y)
+            graph.capture_end()
+        torch.cuda.current_stream().wait_stream(cap)
+        graph.replay()  # warm replay
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        gwall = time.perf_counter() - t0
+        decode["graph"] = {"value": T / gwall, "unit": "steps/s", "ms_per_step": gwall * 1e3 / T,
+                           "how": f"{T} steps captured as one HIP graph, one replay timed"}
+        log(f"decode: graph replay {gwall*1e6/T:.1f} us/step")
+        del graph, sq, sk, sv, S, z, y
 
     # ---------------- CPU oracle baseline ----------------
     cpu = None
