@@ -84,12 +84,37 @@ __device__ __forceinline__ void prod_load(Pref<D, DF, IN>& pf, const Voff<D, DF,
   const unsigned vbytes = (unsigned)(valid * D * (int)sizeof(IN));
 #pragma unroll
   for (int i = 0; i < G::NQ; ++i) {
-    if constexpr (LQ) pf.q[i] = In8<IN>::bload(make_rsrc(q + row_base * DF, fbytes), vo.f[i]);
-    if constexpr (LKV) pf.k[i] = In8<IN>::bload(make_rsrc(k + row_base * DF, fbytes), vo.f[i]);
+    if constexpr (LQ) pf.q[i] = In8<IN>::bload_nt(make_rsrc(q + row_base * DF, fbytes), vo.f[i]);
+    if constexpr (LKV) pf.k[i] = In8<IN>::bload_nt(make_rsrc(k + row_base * DF, fbytes), vo.f[i]);
   }
   if constexpr (LKV) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pf.v[i] = In8<IN>::bload(make_rsrc(v + row_base * D, vbytes), vo.v(i));
+    for (int i = 0; i < 4; ++i) pf.v[i] = In8<IN>::bload_nt(make_rsrc(v + row_base * D, vbytes), vo.v(i));
+  }
+}
+
+// Marks the registers of a prefetched chunk as read without touching them.
+// A step that does not stage its chunk calls this, so that every load is
+// retired on every path through a step: the wait-count analysis then needs no
+// conservative drain of the loads still in flight at the loop's back edge.
+template <typename R> __device__ __forceinline__ void touch(const R& r) {
+  if constexpr (sizeof(R) == 16) {
+    asm volatile("" ::"v"(r));
+  } else {
+    asm volatile("" ::"v"(r.a));
+    asm volatile("" ::"v"(r.b));
+  }
+}
+template <int D, int DF, typename IN, bool LQ, bool LKV>
+__device__ __forceinline__ void retire(const Pref<D, DF, IN>& pf) {
+#pragma unroll
+  for (int i = 0; i < Stage<D, DF>::NQ; ++i) {
+    if constexpr (LQ) touch(pf.q[i]);
+    if constexpr (LKV) touch(pf.k[i]);
+  }
+  if constexpr (LKV) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) touch(pf.v[i]);
   }
 }
 
@@ -176,6 +201,67 @@ __device__ __forceinline__ void prod_stage(const Pref<D, DF, IN>& pf, int p, uin
 #pragma unroll
     for (int i = 0; i < 4; ++i) store_raw<IN, OP, RBV>(sV, p / G::RLV + 16 * i, 8 * (p % G::RLV), pf.v[i]);
   }
+}
+
+// Piecewise forms of prod_load / mask_tail_keys / prod_stage for the output
+// pass, which interleaves the loads of the next chunk with the staging of the
+// current one piece by piece, so that each wave's memory requests spread over
+// the whole step instead of leaving in one burst after the barrier.
+struct ChunkRsrc {
+  __amdgpu_buffer_rsrc_t q, k, v;
+};
+template <int D, int DF, typename IN>
+__device__ __forceinline__ ChunkRsrc chunk_rsrc(const IN* q, const IN* k, const IN* v, long long row_base,
+                                                int valid) {
+  const unsigned fbytes = (unsigned)(valid * DF * (int)sizeof(IN));
+  const unsigned vbytes = (unsigned)(valid * D * (int)sizeof(IN));
+  return ChunkRsrc{make_rsrc(q + row_base * DF, fbytes), make_rsrc(k + row_base * DF, fbytes),
+                   make_rsrc(v + row_base * D, vbytes)};
+}
+
+// phi(q) piece i: LDS tile row, and dp = phi(q) . z over the piece's columns
+template <int D, int DF, typename IN, typename OP, int FM>
+__device__ __forceinline__ float stage_q_piece(const typename In8<IN>::raw& r, int p, int i, uint8_t* sQ,
+                                               const float (&z)[8]) {
+  using G = Stage<D, DF>;
+  float x[8];
+  In8<IN>::to_f32(r, x);
+  float d = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x[e] = fmap_in_stage<FM>(x[e]);
+    d += x[e] * z[e];
+  }
+  Ops<OP>::template store8<DF * Ops<OP>::kBytes>(sQ, p / G::RLF + G::RSF * i, 8 * (p % G::RLF), x);
+  return d;
+}
+
+// phi(k) piece i (rows past `valid` masked to phi = 0): LDS tile row, column sums into cs
+template <int D, int DF, typename IN, typename OP, int FM>
+__device__ __forceinline__ void stage_k_piece(typename In8<IN>::raw r, int p, int i, int valid, uint8_t* sK,
+                                              float (&cs)[8]) {
+  using G = Stage<D, DF>;
+  const int row = p / G::RLF + G::RSF * i;
+  const auto fill = FM == kElu1 ? In8<IN>::neg_inf() : In8<IN>::zero();
+  const bool past = row >= valid;
+  if constexpr (sizeof(IN) == 2) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = past ? fill[j] : r[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r.a[j] = past ? fill.a[j] : r.a[j];
+      r.b[j] = past ? fill.b[j] : r.b[j];
+    }
+  }
+  float x[8];
+  In8<IN>::to_f32(r, x);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x[e] = fmap_in_stage<FM>(x[e]);
+    cs[e] += x[e];
+  }
+  Ops<OP>::template store8<DF * Ops<OP>::kBytes>(sK, row, 8 * (p % G::RLF), x);
 }
 
 // DPP lane moves within rows of 16 lanes (quad_perm, mirrors, rotations).
@@ -302,34 +388,41 @@ __global__ __launch_bounds__(D * 2) void state_pass_kernel(FwdArgs a) {
   };
   // iteration m multiplies chunk m (LDS), stages chunk m+1 (registers) and
   // issues the loads of chunk m+NSET into the set chunk m occupied
+  // The rotation of register sets runs whole (iteration count rounded up to
+  // a multiple of NSET); iterations past the segment multiply nothing and
+  // only retire their (empty) loads.
   auto iter = [&](int m, Pref<D, DF, IN>& ld, Pref<D, DF, IN>& st) {
     load(ld, m + G::NSET);
-    mult(m);
+    if (m < nch) mult(m);
     if constexpr (NB == 1) __syncthreads();
     if (m + 1 < nch) stage(st, m + 1);
+    else retire<D, DF, IN, false, true>(st);
     __syncthreads();
   };
+  const int nround = (nch + G::NSET - 1) / G::NSET * G::NSET;
   if constexpr (G::NSET == 3) {
     Pref<D, DF, IN> pA, pB, pC;
     load(pA, 0);
     load(pB, 1);
     load(pC, 2);
     if (nch > 0) stage(pA, 0);
+    else retire<D, DF, IN, false, true>(pA);
     __syncthreads();
-    for (int m = 0; m < nch; m += 3) {
+    for (int m = 0; m < nround; m += 3) {
       iter(m, pA, pB);
-      if (m + 1 < nch) iter(m + 1, pB, pC);
-      if (m + 2 < nch) iter(m + 2, pC, pA);
+      iter(m + 1, pB, pC);
+      iter(m + 2, pC, pA);
     }
   } else {
     Pref<D, DF, IN> pA, pB;
     load(pA, 0);
     load(pB, 1);
     if (nch > 0) stage(pA, 0);
+    else retire<D, DF, IN, false, true>(pA);
     __syncthreads();
-    for (int m = 0; m < nch; m += 2) {
+    for (int m = 0; m < nround; m += 2) {
       iter(m, pA, pB);
-      if (m + 1 < nch) iter(m + 1, pB, pA);
+      iter(m + 1, pB, pA);
     }
   }
   // z: reduce the per-thread column sums over rows (lanes, then waves)
@@ -422,6 +515,12 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
   const int bh = blockIdx.x, seg = blockIdx.y;
   const int c0 = seg * a.chunks_per_seg;
   const int n = max(0, min(c0 + a.chunks_per_seg, a.nchunks) - c0);
+  // Producer steps IT0 .. itend-1, whole rotations of the register sets. The
+  // first NSET-1 steps (negative) only issue the loads of chunks 0..NSET-2, so
+  // the loop is entered with no loads in flight and the wait counts inside it
+  // follow the steady state alone. Steps past n + LAST only retire empty loads.
+  constexpr int IT0 = -(Stage<D, DF>::NSET - 1);
+  const int itend = IT0 + (n + LAST + 1 - IT0 + Stage<D, DF>::NSET - 1) / Stage<D, DF>::NSET * Stage<D, DF>::NSET;
   const long long base = (long long)bh * a.N;
   const IN* q = static_cast<const IN*>(a.q);
   const IN* k = static_cast<const IN*>(a.k);
@@ -458,55 +557,79 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
     wait_vmem_all();
     // every load and store below is issued in every step (zero size when out
     // of range), so the wait counts are the same on every path
-    auto load = [&](Pref<D, DF, IN>& pf, int it) {
-      const int c = c0 + it;
-      const int valid = it < n ? min(64, a.N - 64 * c) : 0;
-      prod_load<D, DF, IN, true, CAUSAL>(pf, vo, q, k, v, base + 64LL * min(c, a.nchunks - 1), valid);
-    };
+
 
     // step `it` stores the output tile of chunk it-2, stages chunk it (held
     // in `cur`) and issues the loads of chunk it+NSET-1 into `nxt`
+    // Step `it` stores the output tile of chunk it-2, stages chunk it (held
+    // in `cur`) and loads chunk it+NSET-1 into `nxt`, piece by piece.
+    constexpr int NSLOT = G::NQ > 4 ? G::NQ : 4;
     auto pstep = [&](int it, Pref<D, DF, IN>& cur, Pref<D, DF, IN>& nxt) {
-      if constexpr (L::YS) {
-        const int c = c0 + max(it - 2, 0);
-        const int valid = it >= 2 ? min(64, a.N - 64 * c) : 0;
-        const uint8_t* yb = ybuf + (it & 1) * L::YB1;
-        const auto ro = make_rsrc(out + (base + 64LL * c) * D, (unsigned)(valid * D * (int)sizeof(IN)));
-        const int rg = p / G::RLV, col = 8 * (p % G::RLV);
+      const bool stg = it >= 0 && it < n;
+      const int cs_ = c0 + it;                       // chunk staged in this step
+      const int vs = stg ? min(64, a.N - 64 * cs_) : 0;
+      const int ln = it + G::NSET - 1;               // chunk loaded in this step
+      const int cl = c0 + ln;
+      const ChunkRsrc rl = chunk_rsrc<D, DF, IN>(q, k, v, base + 64LL * min(cl, a.nchunks - 1),
+                                                 ln < n ? min(64, a.N - 64 * cl) : 0);
+      const int cy = c0 + max(0, min(it - 2, n - 1));  // chunk whose output tile is stored
+      const int vy = (it >= 2 && it - 2 < n) ? min(64, a.N - 64 * cy) : 0;
+      const auto ro = make_rsrc(out + (base + 64LL * cy) * D, (unsigned)(vy * D * (int)sizeof(IN)));
+      const uint8_t* yb = ybuf + (it & 1) * L::YB1;
+      uint8_t* sQ = smem + (L::NB == 2 ? (it & 1) : 0) * L::BUF;
+      uint8_t* sK = sQ + L::QB;
+      uint8_t* sV = sK + L::KB;
+      if constexpr (CAUSAL) {
+        // z_{it-1} = z_{it-2} + column sums of chunk it-1 (all producer waves)
+        if (stg && it >= 1) {
+          const float* zp = zpart + ((it - 1) & 1) * L::NWP * DF;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = rg + 16 * i;
-          if constexpr (sizeof(IN) == 2) {
-            buf_store16(ro, vo.v(i), *reinterpret_cast<const u32x4*>(yb + tile_off<L::RBY>(row, col * 2)));
-          } else {
-            buf_store16(ro, vo.v(i), *reinterpret_cast<const u32x4*>(yb + tile_off<L::RBY>(row, col * 4)));
-            buf_store16(ro, vo.v(i) + 16, *reinterpret_cast<const u32x4*>(yb + tile_off<L::RBY>(row, col * 4 + 16)));
-          }
-        }
-      }
-      load(nxt, it + G::NSET - 1);
-      if (it < n) {
-        const int c = c0 + it;
-        if constexpr (CAUSAL) {
-          mask_tail_keys<D, DF, IN, FM>(cur, p, min(64, a.N - 64 * c));
-          // z_{it-1} = z_{it-2} + column sums of chunk it-1 (all producer waves)
-          if (it >= 1) {
-            const float* zp = zpart + ((it - 1) & 1) * L::NWP * DF;
+          for (int ww = 0; ww < L::NWP; ++ww) {
+            const f32x4 z0 = *reinterpret_cast<const f32x4*>(zp + ww * DF + cr);
+            const f32x4 z1 = *reinterpret_cast<const f32x4*>(zp + ww * DF + cr + 4);
 #pragma unroll
-            for (int ww = 0; ww < L::NWP; ++ww) {
-              const f32x4 z0 = *reinterpret_cast<const f32x4*>(zp + ww * DF + cr);
-              const f32x4 z1 = *reinterpret_cast<const f32x4*>(zp + ww * DF + cr + 4);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                zrun[e] += z0[e];
-                zrun[4 + e] += z1[e];
-              }
+            for (int e = 0; e < 4; ++e) {
+              zrun[e] += z0[e];
+              zrun[4 + e] += z1[e];
             }
           }
         }
-        uint8_t* sQ = smem + (L::NB == 2 ? (it & 1) : 0) * L::BUF;
-        if constexpr (L::NB == 1) __syncthreads();  // consumers are done with the buffer
-        prod_stage<D, DF, IN, OP, FM, true, CAUSAL>(cur, p, sQ, sQ + L::QB, sQ + L::QB + L::KB, zrun, dp, cs);
+      }
+      if constexpr (L::NB == 1) __syncthreads();  // consumers are done with the buffer
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cs[e] = 0.f;
+#pragma unroll
+      for (int i = 0; i < NSLOT; ++i) {
+        if (i < 4) {
+          if constexpr (L::YS) {
+            const int row = p / G::RLV + 16 * i, col = 8 * (p % G::RLV);
+            if constexpr (sizeof(IN) == 2) {
+              buf_store16_nt(ro, vo.v(i), *reinterpret_cast<const u32x4*>(yb + tile_off<L::RBY>(row, col * 2)));
+            } else {
+              buf_store16_nt(ro, vo.v(i), *reinterpret_cast<const u32x4*>(yb + tile_off<L::RBY>(row, col * 4)));
+              buf_store16_nt(ro, vo.v(i) + 16,
+                             *reinterpret_cast<const u32x4*>(yb + tile_off<L::RBY>(row, col * 4 + 16)));
+            }
+          }
+        }
+        if (i < G::NQ) {
+          nxt.q[i] = In8<IN>::bload_nt(rl.q, vo.f[i]);
+          if constexpr (CAUSAL) nxt.k[i] = In8<IN>::bload(rl.k, vo.f[i]);
+        }
+        if constexpr (CAUSAL) {
+          if (i < 4) nxt.v[i] = In8<IN>::bload(rl.v, vo.v(i));
+        }
+        if (stg) {
+          if (i < G::NQ) {
+            dp[i] = stage_q_piece<D, DF, IN, OP, FM>(cur.q[i], p, i, sQ, zrun);
+            if constexpr (CAUSAL) stage_k_piece<D, DF, IN, OP, FM>(cur.k[i], p, i, vs, sK, cs);
+          }
+          if constexpr (CAUSAL) {
+            if (i < 4) store_raw<IN, OP, L::RBV>(sV, p / G::RLV + 16 * i, 8 * (p % G::RLV), cur.v[i]);
+          }
+        }
+      }
+      if (stg) {
         if constexpr (CAUSAL) {
           // publish this chunk's column sums of phi(K)
 #pragma unroll
@@ -527,7 +650,7 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
           }
         }
       } else {
-        if constexpr (L::NB == 1) __syncthreads();
+        retire<D, DF, IN, true, CAUSAL>(cur);
         if constexpr (CAUSAL) if (it == n) {
           // final z = z_{n-2} + column sums of the last chunk
           const float* zp = zpart + ((it - 1) & 1) * L::NWP * DF;
@@ -539,21 +662,21 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
       }
       __syncthreads();
     };
+    // whole rotations of the register sets; the steps past n + LAST only
+    // retire their empty loads (the consumers run as many barriers)
+    // chunk c is held in the set that step c - NSET + 1 loads and step c stages
     if constexpr (G::NSET == 3) {
       Pref<D, DF, IN> pA, pB, pC;
-      load(pA, 0);
-      load(pB, 1);
-      for (int it = 0; it <= n + LAST; it += 3) {
+      for (int it = IT0; it < itend; it += 3) {
         pstep(it, pA, pC);
-        if (it + 1 <= n + LAST) pstep(it + 1, pB, pA);
-        if (it + 2 <= n + LAST) pstep(it + 2, pC, pB);
+        pstep(it + 1, pB, pA);
+        pstep(it + 2, pC, pB);
       }
     } else {
       Pref<D, DF, IN> pA, pB;
-      load(pA, 0);
-      for (int it = 0; it <= n + LAST; it += 2) {
+      for (int it = IT0; it < itend; it += 2) {
         pstep(it, pA, pB);
-        if (it + 1 <= n + LAST) pstep(it + 1, pB, pA);
+        pstep(it + 1, pB, pA);
       }
     }
     if constexpr (CAUSAL) {
@@ -574,9 +697,9 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < DF / 16; ++kb) Sf_const[kb] = Ops<OP>::from_acc(S[kb >> 1], kb & 1);
     }
-    for (int bar = 0; bar < L::NBAR; ++bar) __syncthreads();  // the producers' first step
-    for (int it = 1; it <= n + LAST; ++it) {
-      if (it > n) {  // the producers store the last tile
+    for (int bar = 0; bar < L::NBAR * (1 - IT0); ++bar) __syncthreads();  // producer steps IT0 .. 0
+    for (int it = 1; it < itend; ++it) {
+      if (it > n) {  // the producers store the last tile, or idle
         for (int bar = 0; bar < L::NBAR; ++bar) __syncthreads();
         continue;
       }
