@@ -132,16 +132,22 @@ def main():
     for _ in range(args.warmup):
         fwd()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     log(f"prefill: timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        fwd(evs[i])
+        fwd()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])  # ms
     ms_step = wall * 1e3 / args.steps
+    # per-pass durations from HIP events recorded on the launch stream, in a
+    # second run of the same length (events add a little launch overhead, so
+    # they stay out of the timed steps above)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        fwd(evs[i])
+    torch.cuda.synchronize()
+    stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])  # ms
     ms_state, ms_scan, ms_out = stage.mean(axis=0)
     tokens = B * N
     value = tokens / (ms_step * 1e-3)
@@ -192,17 +198,18 @@ def main():
         for t in range(args.decode_warmup):
             la.la_decode_step(S, z, sq[t], sk[t], sv[t], out=y)
         torch.cuda.synchronize()
-        dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * T)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         log(f"decode: timing {T} steps")
         t0 = time.perf_counter()
+        e0.record()
         for t in range(T):
-            dev_ev[2 * t].record()
             la.la_decode_step(S, z, sq[args.decode_warmup + t], sk[args.decode_warmup + t],
                               sv[args.decode_warmup + t], out=y)
-            dev_ev[2 * t + 1].record()
+        e1.record()
         torch.cuda.synchronize()
         dwall = time.perf_counter() - t0
-        kern_ms = np.array([dev_ev[2 * t].elapsed_time(dev_ev[2 * t + 1]) for t in range(T)])
+        # average launch duration: device time of the T back-to-back launches / T
+        kern_ms = np.array([e0.elapsed_time(e1) / T])
         heads = Bd * Hd
         step_bytes = heads * (2 * 4 * (dd * dd + dd) + 3 * 2 * dd + 2 * dd)
         k_ms = float(kern_ms.mean())

@@ -446,30 +446,46 @@ __global__ __launch_bounds__(D * 2) void state_pass_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // Carry scan: ws[bh][p] <- init + sum_{p' < p} ws[bh][p']  (exclusive), and
 // the total into ws[bh][P] (and S_out/z_out) when requested.
-// grid = (BH, ceil(state_elems/256)), block = 256.
+// grid = (BH, ceil(state_elems/1024)), block = 256.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void carry_scan_kernel(ScanArgs a) {
-  const int e = blockIdx.y * 256 + threadIdx.x;
+  // four consecutive state elements per thread (the state size d'(d+1) is a
+  // multiple of 4 and every slot starts 16-byte aligned); the loads of eight
+  // segments are issued before their dependent adds and stores
+  const int e = 4 * (blockIdx.y * 256 + threadIdx.x);
   const int bh = blockIdx.x;
   if (e >= a.state_elems) return;
   const int sdd = a.DF * a.D;
-  float run = 0.f;
+  f32x4 run = {0.f, 0.f, 0.f, 0.f};
   if (e < sdd) {
-    if (a.S_in) run = a.S_in[(long long)bh * sdd + e];
+    if (a.S_in) run = *reinterpret_cast<const f32x4*>(a.S_in + (long long)bh * sdd + e);
   } else {
-    if (a.z_in) run = a.z_in[(long long)bh * a.DF + (e - sdd)];
+    if (a.z_in) run = *reinterpret_cast<const f32x4*>(a.z_in + (long long)bh * a.DF + (e - sdd));
   }
   float* col = a.ws + (long long)bh * a.ws_slots * a.state_elems + e;
-  for (int p = 0; p < a.P; ++p) {
-    const float t = col[(long long)p * a.state_elems];
-    if (a.exclusive) col[(long long)p * a.state_elems] = run;
-    run += t;
+  const long long st = a.state_elems;
+  for (int p0 = 0; p0 < a.P; p0 += 8) {
+    const int cnt = min(8, a.P - p0);
+    f32x4 t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < cnt) t[j] = *reinterpret_cast<const f32x4*>(col + (p0 + j) * st);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < cnt) {
+        if (a.exclusive) *reinterpret_cast<f32x4*>(col + (p0 + j) * st) = run;
+        run[0] += t[j][0];
+        run[1] += t[j][1];
+        run[2] += t[j][2];
+        run[3] += t[j][3];
+      }
+    }
   }
-  if (a.write_total) col[(long long)a.P * a.state_elems] = run;
+  if (a.write_total) *reinterpret_cast<f32x4*>(col + a.P * st) = run;
   if (e < sdd) {
-    if (a.S_out) a.S_out[(long long)bh * sdd + e] = run;
+    if (a.S_out) *reinterpret_cast<f32x4*>(a.S_out + (long long)bh * sdd + e) = run;
   } else {
-    if (a.z_out) a.z_out[(long long)bh * a.DF + (e - sdd)] = run;
+    if (a.z_out) *reinterpret_cast<f32x4*>(a.z_out + (long long)bh * a.DF + (e - sdd)) = run;
   }
 }
 
@@ -820,7 +836,7 @@ static hipError_t launch_prefill(const FwdArgs& a, const ScanArgs& s, bool causa
   }
   if (ev) (void)hipEventRecord(ev[1], st);
   if (a.run_scan) {
-    hipLaunchKernelGGL(carry_scan_kernel, dim3(s.BH, (s.state_elems + 255) / 256), dim3(256), 0, st, s);
+    hipLaunchKernelGGL(carry_scan_kernel, dim3(s.BH, (s.state_elems / 4 + 255) / 256), dim3(256), 0, st, s);
   }
   if (ev) (void)hipEventRecord(ev[2], st);
   if (causal) {
