@@ -40,7 +40,7 @@ bool perf_supported(int d, int m) {
 // Feature dimension d' for a map, or a negative status.
 int feature_dim(const la_feature_map* fm, int d) {
   if (!fm) return LA_ERR_INVALID_ARG;
-  if (fm->kind == LA_ELU1) return d;
+  if (fm->kind == LA_ELU1 || fm->kind == LA_IDENTITY) return d;
   if (fm->kind == LA_PERFORMER) {
     if (fm->m <= 0 || !fm->W || !aligned16(fm->W)) return LA_ERR_INVALID_ARG;
     if (!perf_supported(d, fm->m)) return LA_ERR_UNSUPPORTED;
@@ -261,7 +261,8 @@ int la_forward_ex(const void* q, const void* k, const void* v, void* out, int B,
     s.S_out = S_out;
     s.z_out = z_out;
   }
-  return status_from_hip(la::prefill_dispatch(a, s, d, dfeat, mapped ? la::kPremapped : la::kElu1, dtype,
+  const int kfm = feature_map->kind == LA_ELU1 ? la::kElu1 : la::kIdentity;  // mapped features: identity inside
+  return status_from_hip(la::prefill_dispatch(a, s, d, dfeat, kfm, dtype,
                                               causal != 0, stream, events));
 }
 

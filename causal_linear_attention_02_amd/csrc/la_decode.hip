@@ -6,6 +6,7 @@
 //   S <- S + phi(k) v^T,  z <- z + phi(k),  y = phi(q)^T S / phi(q).z
 // (the state is updated first, so the new token attends to itself).
 //
+// The identity map uses q and k as they are.
 // Random features: phi(x) = exp(W x~ - |x~|^2/2) / sqrt(m), x~ = d^(-1/4) x
 // ("Linear Attention", "Mapas de características"), computed per head in fp32
 // from W (m x d, fp32; rounded to bf16 for bf16 inputs) before the state
@@ -77,6 +78,15 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
         const long long off = head * D + e;
         s_phiq[hb][e] = phi_elu1(load_elem<IN>(a.q, off));
         s_phik[hb][e] = phi_elu1(load_elem<IN>(a.k, off));
+        s_v[hb][e] = load_elem<IN>(a.v, off);
+      }
+    }
+  } else if constexpr (FM == kIdentity) {
+    if (valid) {
+      for (int e = t; e < D; e += SH::TPH) {
+        const long long off = head * D + e;
+        s_phiq[hb][e] = load_elem<IN>(a.q, off);
+        s_phik[hb][e] = load_elem<IN>(a.k, off);
         s_v[hb][e] = load_elem<IN>(a.v, off);
       }
     }
@@ -199,6 +209,15 @@ static hipError_t decode_typed(const DecodeArgs& a, int D, int DF, int fmap, hip
       case 32: return launch_decode<32, 32, IN, kElu1>(a, st);
       case 64: return launch_decode<64, 64, IN, kElu1>(a, st);
       case 128: return launch_decode<128, 128, IN, kElu1>(a, st);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (fmap == kIdentity) {
+    if (DF != D) return hipErrorInvalidValue;
+    switch (D) {
+      case 32: return launch_decode<32, 32, IN, kIdentity>(a, st);
+      case 64: return launch_decode<64, 64, IN, kIdentity>(a, st);
+      case 128: return launch_decode<128, 128, IN, kIdentity>(a, st);
     }
     return hipErrorInvalidValue;
   }

@@ -2,6 +2,8 @@
 //
 // elu+1 ("Linear Transformer (Transformers are RNNs)", "La función ELU + 1"):
 // elementwise, the same device function the prefill and decode kernels use.
+// The identity map ("Linear Attention", "Mapas de características") is the
+// same kernel without the map: a copy in the requested precision.
 //
 // Positive random features ("Linear Attention", marovi.ai, "Mapas de
 // características"): phi(x) = exp(W x~ - |x~|^2 / 2) / sqrt(m), x~ = d^(-1/4) x,
@@ -28,13 +30,16 @@ template <> __device__ __forceinline__ void store8_out<float>(void* p, long long
   q[1] = f32x4{x[4], x[5], x[6], x[7]};
 }
 
-template <typename IN, typename OUT>
-__global__ __launch_bounds__(256) void fmap_elu1_kernel(FmapArgs a, long long pieces) {
+// elementwise maps: elu+1 or the identity (a precision-converting copy)
+template <typename IN, typename OUT, int FM>
+__global__ __launch_bounds__(256) void fmap_elementwise_kernel(FmapArgs a, long long pieces) {
   for (long long p = (long long)blockIdx.x * 256 + threadIdx.x; p < pieces; p += (long long)gridDim.x * 256) {
     float x[8];
     In8<IN>::to_f32(In8<IN>::load(static_cast<const IN*>(a.x) + 8 * p), x);
+    if constexpr (FM == kElu1) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = phi_elu1(x[i]);
+      for (int i = 0; i < 8; ++i) x[i] = phi_elu1(x[i]);
+    }
     store8_out<OUT>(a.phi, 8 * p, x);
   }
 }
@@ -142,14 +147,22 @@ __global__ __launch_bounds__(256) void fmap_perf_kernel(FmapArgs a) {
   }
 }
 
-template <typename IN, typename OUT>
-static hipError_t launch_fmap_elu(const FmapArgs& a, int D, hipStream_t st) {
+template <typename IN, typename OUT, int FM>
+static hipError_t launch_fmap_elementwise(const FmapArgs& a, int D, hipStream_t st) {
   const long long pieces = a.rows * D / 8;
   if (pieces == 0) return hipSuccess;
   long long blocks = (pieces + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL((fmap_elu1_kernel<IN, OUT>), dim3((unsigned)blocks), dim3(256), 0, st, a, pieces);
+  hipLaunchKernelGGL((fmap_elementwise_kernel<IN, OUT, FM>), dim3((unsigned)blocks), dim3(256), 0, st, a, pieces);
   return hipGetLastError();
+}
+
+template <int FM>
+static hipError_t fmap_elementwise_dispatch(const FmapArgs& a, int D, int in_dtype, int out_dtype, hipStream_t st) {
+  if (in_dtype == 1 && out_dtype == 1) return launch_fmap_elementwise<__bf16, __bf16, FM>(a, D, st);
+  if (in_dtype == 1 && out_dtype == 0) return launch_fmap_elementwise<__bf16, float, FM>(a, D, st);
+  if (in_dtype == 0 && out_dtype == 1) return launch_fmap_elementwise<float, __bf16, FM>(a, D, st);
+  return launch_fmap_elementwise<float, float, FM>(a, D, st);
 }
 
 template <int D, int DF, typename IN, typename OUT>
@@ -174,12 +187,8 @@ static hipError_t fmap_perf_dispatch(const FmapArgs& a, int D, int DF, hipStream
 }
 
 hipError_t fmap_dispatch(const FmapArgs& a, int D, int DF, int fmap, int in_dtype, int out_dtype, hipStream_t st) {
-  if (fmap == kElu1) {
-    if (in_dtype == 1 && out_dtype == 1) return launch_fmap_elu<__bf16, __bf16>(a, D, st);
-    if (in_dtype == 1 && out_dtype == 0) return launch_fmap_elu<__bf16, float>(a, D, st);
-    if (in_dtype == 0 && out_dtype == 1) return launch_fmap_elu<float, __bf16>(a, D, st);
-    return launch_fmap_elu<float, float>(a, D, st);
-  }
+  if (fmap == kElu1) return fmap_elementwise_dispatch<kElu1>(a, D, in_dtype, out_dtype, st);
+  if (fmap == kIdentity) return fmap_elementwise_dispatch<kIdentity>(a, D, in_dtype, out_dtype, st);
   if (in_dtype == 1 && out_dtype == 1) return fmap_perf_dispatch<__bf16, __bf16>(a, D, DF, st);
   if (in_dtype == 1 && out_dtype == 0) return fmap_perf_dispatch<__bf16, float>(a, D, DF, st);
   if (in_dtype == 0 && out_dtype == 1) return fmap_perf_dispatch<float, __bf16>(a, D, DF, st);

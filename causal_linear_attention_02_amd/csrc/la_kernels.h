@@ -9,7 +9,7 @@ namespace la {
 enum FeatureMap {
   kElu1 = 0,       // elu(x) + 1 applied in the kernels
   kPerformer = 1,  // positive random features
-  kPremapped = 2,  // inputs already hold phi(q), phi(k) (identity inside the kernels)
+  kIdentity = 2,   // phi(x) = x: the identity map, or features already mapped by the random-feature kernel
 };
 
 // Chunked forward (prefill / non-causal). All pointers are device pointers.

@@ -860,8 +860,8 @@ static hipError_t prefill_typed(const FwdArgs& a, const ScanArgs& s, int D, int 
     return hipErrorInvalidValue;
   }
 #define LA_PRE_CASE(d, m) \
-  if (D == d && DF == m) return launch_prefill<d, m, T, T, kPremapped>(a, s, causal, st, ev);
-  LA_PRE_CASE(32, 64) LA_PRE_CASE(32, 128)
+  if (D == d && DF == m) return launch_prefill<d, m, T, T, kIdentity>(a, s, causal, st, ev);
+  LA_PRE_CASE(32, 32) LA_PRE_CASE(32, 64) LA_PRE_CASE(32, 128)
   LA_PRE_CASE(64, 64) LA_PRE_CASE(64, 128) LA_PRE_CASE(64, 256)
   LA_PRE_CASE(128, 64) LA_PRE_CASE(128, 128)
 #undef LA_PRE_CASE
@@ -870,7 +870,7 @@ static hipError_t prefill_typed(const FwdArgs& a, const ScanArgs& s, int D, int 
 
 hipError_t prefill_dispatch(const FwdArgs& a, const ScanArgs& s, int D, int DF, int fmap, int dtype, bool causal,
                             hipStream_t st, hipEvent_t* ev) {
-  if (fmap != kElu1 && fmap != kPremapped) return hipErrorInvalidValue;
+  if (fmap != kElu1 && fmap != kIdentity) return hipErrorInvalidValue;
   if (dtype == 1) return prefill_typed<__bf16>(a, s, D, DF, fmap, causal, st, ev);
   return prefill_typed<float>(a, s, D, DF, fmap, causal, st, ev);
 }

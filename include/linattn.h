@@ -15,7 +15,8 @@
  *       "La función ELU + 1"), d' = d;
  *   phi = positive random features ("Linear Attention", "Mapas de
  *       características"): phi(x) = exp(W x~ - |x~|^2/2) / sqrt(m),
- *       x~ = d^(-1/4) x, W of shape m x d, d' = m.
+ *       x~ = d^(-1/4) x, W of shape m x d, d' = m;
+ *   phi = identity (same section), d' = d.
  * With normalization on, y = num / max(den, 1e-6).
  *
  * Conventions for every entry point:
@@ -25,7 +26,7 @@
  *   - Element type of q, k, v and out: LA_BF16 or LA_F32 (same for all four).
  *     bf16 inputs are multiplied on bf16 matrix cores with fp32 accumulation;
  *     fp32 inputs use fp32 matrix cores. State is always fp32.
- *   - Supported: d in {32, 64, 128} with elu+1; random features with
+ *   - Supported: d in {32, 64, 128} with elu+1 or the identity; random features with
  *     (d, m) in {(32, 64), (32, 128), (64, 64), (64, 128), (64, 256),
  *     (128, 64), (128, 128)}. Other valid requests return LA_ERR_UNSUPPORTED.
  *   - Ownership: the caller allocates and frees every buffer. The library
@@ -60,12 +61,14 @@ extern "C" {
 /* Feature maps */
 #define LA_ELU1 0      /* elu(x) + 1, d' = d */
 #define LA_PERFORMER 1 /* positive random features, d' = m */
+#define LA_IDENTITY 2  /* phi(x) = x, d' = d; the denominator may be <= 0 (then clamped to 1e-6),
+                          so normalize = 0 is its usual use */
 
 typedef struct la_feature_map {
-  int kind;        /* LA_ELU1 or LA_PERFORMER */
+  int kind;        /* LA_ELU1, LA_PERFORMER or LA_IDENTITY */
   int m;           /* LA_PERFORMER: number of features (d'); ignored for LA_ELU1 */
   const float* W;  /* LA_PERFORMER: device pointer, m x d fp32 row-major, shared by all
-                      batches and heads; bf16 inputs use W rounded to bf16. NULL for LA_ELU1 */
+                      batches and heads; bf16 inputs use W rounded to bf16. Ignored otherwise */
 } la_feature_map;
 
 /* Library version, (major << 16) | minor. */

@@ -34,7 +34,13 @@ listed with its reasons in the design notes of the repository):
     kernel that [LA] "Reformulación con núcleos" writes for softmax;
   * an optional initial state (S0, z0) stands for tokens before the first
     one given: it adds phi(q_i).S0 to the numerator and phi(q_i).z0 to the
-    denominator of every output.
+    denominator of every output;
+  * decay ([LA] "Variantes y extensiones", RetNet item): the state recurs as
+    S_t = gamma S_{t-1} + phi(k_t) v_t^T and the normalizer the same way,
+    z_t = gamma z_{t-1} + phi(k_t); unrolled, token j enters output i with
+    weight gamma^(i-j) and an initial state with weight gamma^(i+1). It is
+    defined for the causal and recurrent forms only; gamma may differ per
+    head (one value per leading index, or per head of a [B, H, ...] input).
 
 Parity pins: every function here is checked by tests that do not reuse its
 code (hand-derived worked examples, closed forms, library routines,
@@ -110,6 +116,20 @@ def _bh(x):
     return x.reshape(-1, x.shape[-2], x.shape[-1])
 
 
+def _gammas(decay, shape, G):
+    """Per-(batch, head) decay factors as float64 [G], or None for no decay.
+
+    ``decay`` is a number, or an array broadcastable to the leading dims of
+    ``shape`` (e.g. one value per head of a [B, H, N, d] input)."""
+    if decay is None:
+        return None
+    lead = tuple(shape[:-2]) if len(shape) > 2 else (1,)
+    g = np.broadcast_to(np.asarray(decay, dtype=np.float64), lead).reshape(-1)
+    if g.size != G:
+        raise ValueError("decay does not match the leading dimensions")
+    return g
+
+
 def _state(S0, z0, G, dfeat, dv):
     S = np.zeros((G, dfeat, dv)) if S0 is None else np.asarray(S0, np.float64).reshape(G, dfeat, dv).copy()
     z = np.zeros((G, dfeat)) if z0 is None else np.asarray(z0, np.float64).reshape(G, dfeat).copy()
@@ -121,10 +141,12 @@ def _state(S0, z0, G, dfeat, dv):
 # ---------------------------------------------------------------------------
 
 def attention(q, k, v, fmap="elu1", W=None, causal=True, normalize=True,
-              S0=None, z0=None, rows=None):
+              S0=None, z0=None, rows=None, decay=None):
     """y_i = sum_j (phi(q_i).phi(k_j)) v_j / sum_j phi(q_i).phi(k_j).
 
     The sums run over j <= i when ``causal`` (inclusive), else over all j.
+    With ``decay`` (causal only) term j of output i is weighted gamma^(i-j)
+    and the initial state gamma^(i+1).
     The N x N similarity matrix is formed explicitly (brute force). ``rows``
     restricts the computation to a subset of query positions, so long
     sequences can be checked at sampled outputs.
@@ -139,26 +161,42 @@ def attention(q, k, v, fmap="elu1", W=None, causal=True, normalize=True,
     Qf = feature_map(Q[:, idx], fmap, W)
     dfeat = Kf.shape[-1]
     S, z = _state(S0, z0, G, dfeat, dv)
+    gam = _gammas(decay, shape, G)
+    if gam is not None and not causal:
+        raise ValueError("decay is defined for the causal form only")
     out = np.empty((G, idx.size, dv))
+    lag = idx[:, None] - np.arange(N)[None, :]        # i - j
     for g in range(G):
         A = Qf[g] @ Kf[g].T                           # [R, N] similarities
+        s0 = np.ones((idx.size, 1))
         if causal:
-            A = np.where(np.arange(N)[None, :] <= idx[:, None], A, 0.0)
-        num = A @ V[g] + Qf[g] @ S[g]
-        den = A.sum(axis=1) + Qf[g] @ z[g]
+            A = np.where(lag >= 0, A, 0.0)
+            if gam is not None:
+                A = A * np.where(lag >= 0, gam[g] ** np.maximum(lag, 0), 0.0)
+                s0 = (gam[g] ** (idx + 1.0))[:, None]
+        num = A @ V[g] + s0 * (Qf[g] @ S[g])
+        den = A.sum(axis=1) + s0[:, 0] * (Qf[g] @ z[g])
         out[g] = _finish(num, den, normalize)
     return out.reshape(shape[:-2] + (idx.size, dv))
 
 
-def final_state(k, v, fmap="elu1", W=None, S0=None, z0=None):
-    """S = S0 + sum_j phi(k_j) v_j^T, z = z0 + sum_j phi(k_j) ([LA] "Reformulación con núcleos")."""
+def final_state(k, v, fmap="elu1", W=None, S0=None, z0=None, decay=None):
+    """S = S0 + sum_j phi(k_j) v_j^T, z = z0 + sum_j phi(k_j) ([LA] "Reformulación con núcleos").
+
+    With decay: S = gamma^N S0 + sum_j gamma^(N-1-j) phi(k_j) v_j^T (and z alike)."""
     shape = np.asarray(k).shape
     K, V = _bh(k), _bh(v)
-    G = K.shape[0]
+    G, N = K.shape[0], K.shape[1]
     Kf = feature_map(K, fmap, W)
     S, z = _state(S0, z0, G, Kf.shape[-1], V.shape[-1])
-    S = S + np.einsum("gnc,gne->gce", Kf, V)
-    z = z + Kf.sum(axis=1)
+    gam = _gammas(decay, shape, G)
+    if gam is not None:
+        wgt = gam[:, None] ** (N - 1.0 - np.arange(N))[None, :]     # [G, N]
+        S = gam[:, None, None] ** N * S + np.einsum("gn,gnc,gne->gce", wgt, Kf, V)
+        z = gam[:, None] ** N * z + np.einsum("gn,gnc->gc", wgt, Kf)
+    else:
+        S = S + np.einsum("gnc,gne->gce", Kf, V)
+        z = z + Kf.sum(axis=1)
     lead = shape[:-2]
     return S.reshape(lead + S.shape[1:]), z.reshape(lead + z.shape[1:])
 
@@ -186,17 +224,23 @@ def attention_via_state(q, k, v, fmap="elu1", W=None, normalize=True, S0=None, z
 # [LT] "La formulación recurrente paso a paso")
 # ---------------------------------------------------------------------------
 
-def decode_step(S, z, q, k, v, fmap="elu1", W=None, normalize=True):
+def decode_step(S, z, q, k, v, fmap="elu1", W=None, normalize=True, decay=None):
     """One token per head: S += phi(k) v^T, z += phi(k), then y = phi(q)^T S / phi(q).z.
 
-    S: [..., d', d], z: [..., d'], q/k/v: [..., d]. Returns (y, S_new, z_new);
-    the inputs are not modified.
+    With decay: S = gamma S + phi(k) v^T, z = gamma z + phi(k) ([LA]
+    "Variantes y extensiones"); gamma a number or an array over the leading
+    dims of q. S: [..., d', d], z: [..., d'], q/k/v: [..., d]. Returns
+    (y, S_new, z_new); the inputs are not modified.
     """
     S = np.asarray(S, np.float64)
     z = np.asarray(z, np.float64)
     qf = feature_map(np.asarray(q, np.float64), fmap, W)
     kf = feature_map(np.asarray(k, np.float64), fmap, W)
     v = np.asarray(v, np.float64)
+    if decay is not None:
+        gam = np.broadcast_to(np.asarray(decay, np.float64), z.shape[:-1])
+        S = gam[..., None, None] * S
+        z = gam[..., None] * z
     S_new = S + kf[..., :, None] * v[..., None, :]
     z_new = z + kf
     num = np.einsum("...c,...ce->...e", qf, S_new)
@@ -204,7 +248,7 @@ def decode_step(S, z, q, k, v, fmap="elu1", W=None, normalize=True):
     return _finish(num, den, normalize), S_new, z_new
 
 
-def recurrent(q, k, v, fmap="elu1", W=None, normalize=True, S0=None, z0=None):
+def recurrent(q, k, v, fmap="elu1", W=None, normalize=True, S0=None, z0=None, decay=None):
     """Token-by-token loop over the sequence (every head at once).
 
     Returns (y, S_N, z_N).
@@ -215,9 +259,10 @@ def recurrent(q, k, v, fmap="elu1", W=None, normalize=True, S0=None, z0=None):
     dv = V.shape[-1]
     dfeat = feature_dim(Q.shape[-1], fmap, W)
     S, z = _state(S0, z0, G, dfeat, dv)
+    gam = _gammas(decay, shape, G)
     y = np.empty((G, N, dv))
     for t in range(N):
-        y[:, t], S, z = decode_step(S, z, Q[:, t], K[:, t], V[:, t], fmap, W, normalize)
+        y[:, t], S, z = decode_step(S, z, Q[:, t], K[:, t], V[:, t], fmap, W, normalize, gam)
     lead = shape[:-2]
     return (y.reshape(shape[:-1] + (dv,)), S.reshape(lead + S.shape[1:]),
             z.reshape(lead + z.shape[1:]))
@@ -249,8 +294,16 @@ def cumsum_form(q, k, v, fmap="elu1", W=None, normalize=True):
 # ---------------------------------------------------------------------------
 
 def chunked(q, k, v, fmap="elu1", W=None, causal=True, normalize=True, chunk=64,
-            S0=None, z0=None):
-    """Returns (y, S_N, z_N). For ``causal=False`` the full sums are formed first."""
+            S0=None, z0=None, decay=None):
+    """Returns (y, S_N, z_N). For ``causal=False`` the full sums are formed first.
+
+    With decay (causal only): inside a block of L tokens the similarity of
+    rows i, j (block positions r_i, r_j) is weighted gamma^(r_i-r_j), the
+    carried state enters row i with weight gamma^(r_i+1), and the state moves
+    on as S <- gamma^L S + sum_j gamma^(L-1-r_j) phi(k_j) v_j^T.
+    """
+    if decay is not None and not causal:
+        raise ValueError("decay is defined for the causal form only")
     if not causal:
         y = attention_via_state(q, k, v, fmap, W, normalize, S0, z0)
         S, z = final_state(k, v, fmap, W, S0, z0)
@@ -262,17 +315,29 @@ def chunked(q, k, v, fmap="elu1", W=None, causal=True, normalize=True, chunk=64,
     Qf = feature_map(Q, fmap, W)
     Kf = feature_map(K, fmap, W)
     S, z = _state(S0, z0, G, Qf.shape[-1], dv)
+    gam = _gammas(decay, shape, G)
     y = np.empty((G, N, dv))
     for s in range(0, N, chunk):
         e = min(N, s + chunk)
+        L = e - s
         qc, kc, vc = Qf[:, s:e], Kf[:, s:e], V[:, s:e]
         A = np.einsum("gic,gjc->gij", qc, kc)
-        A = A * np.tril(np.ones((e - s, e - s)))[None]
-        num = np.einsum("gij,gje->gie", A, vc) + np.einsum("gic,gce->gie", qc, S)
-        den = A.sum(axis=2) + np.einsum("gic,gc->gi", qc, z)
+        A = A * np.tril(np.ones((L, L)))[None]
+        if gam is None:
+            sin = np.ones((G, L))                                   # weight of the carried state
+            kw = np.ones((G, L))                                    # weight of key j in the update
+            carry = np.ones(G)
+        else:
+            r = np.arange(L, dtype=np.float64)
+            A = A * gam[:, None, None] ** np.maximum(r[:, None] - r[None, :], 0.0)[None]
+            sin = gam[:, None] ** (r[None, :] + 1.0)
+            kw = gam[:, None] ** (L - 1.0 - r[None, :])
+            carry = gam ** L
+        num = np.einsum("gij,gje->gie", A, vc) + sin[:, :, None] * np.einsum("gic,gce->gie", qc, S)
+        den = A.sum(axis=2) + sin * np.einsum("gic,gc->gi", qc, z)
         y[:, s:e] = _finish(num, den, normalize)
-        S = S + np.einsum("gjc,gje->gce", kc, vc)
-        z = z + kc.sum(axis=1)
+        S = carry[:, None, None] * S + np.einsum("gj,gjc,gje->gce", kw, kc, vc)
+        z = carry[:, None] * z + np.einsum("gj,gjc->gc", kw, kc)
     lead = shape[:-2]
     return (y.reshape(shape[:-1] + (dv,)), S.reshape(lead + S.shape[1:]),
             z.reshape(lead + z.shape[1:]))

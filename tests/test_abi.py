@@ -56,6 +56,15 @@ def test_forward_rejects_bad_arguments():
     assert _fwd(fm=la_feature_map(la.LA_PERFORMER, 64, None)) == la.LA_ERR_INVALID_ARG
 
 
+def test_identity_map_accepted_by_planning():
+    ident = la_feature_map(la.LA_IDENTITY, 0, None)
+    for d in (32, 64, 128):
+        got = la.lib.la_forward_workspace_size(1, 2, 4096, d, ctypes.byref(ident), 1)
+        want = la.lib.la_forward_workspace_size(1, 2, 4096, d, ctypes.byref(ELU), 1)
+        assert got == want > 0   # same plan as elu+1 (d' = d, no mapped-feature buffers)
+    assert _fwd(fm=ident, d=48) == la.LA_ERR_UNSUPPORTED
+
+
 def test_forward_workspace_checks():
     # a long single sequence is split into segments and needs workspace
     need = lib.la_forward_workspace_size(1, 1, 65536, 128, ctypes.byref(ELU), 1)

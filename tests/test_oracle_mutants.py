@@ -21,12 +21,13 @@ INIT = (ROOT / "oracle" / "__init__.py").read_text()
 
 # (text in the oracle, replacement, the mistake it stands for)
 MUTANTS = [
-    ("np.arange(N)[None, :] <= idx[:, None]", "np.arange(N)[None, :] < idx[:, None]",
+    ("A = np.where(lag >= 0, A, 0.0)", "A = np.where(lag > 0, A, 0.0)",
      "definition: causal mask excludes the diagonal"),
     ("A = Qf[g] @ Kf[g].T", "A = Kf[g][:idx.size] @ Qf[g].T",
      "definition: similarity matrix transposed"),
-    ("num = A @ V[g] + Qf[g] @ S[g]", "num = A @ V[g]", "definition: initial state dropped from the numerator"),
-    ("den = A.sum(axis=1) + Qf[g] @ z[g]", "den = A.sum(axis=1)",
+    ("num = A @ V[g] + s0 * (Qf[g] @ S[g])", "num = A @ V[g]",
+     "definition: initial state dropped from the numerator"),
+    ("den = A.sum(axis=1) + s0[:, 0] * (Qf[g] @ z[g])", "den = A.sum(axis=1)",
      "definition: initial state dropped from the denominator"),
     ("return num / np.maximum(den, EPS)[..., None]", "return num / (den + EPS)[..., None]",
      "eps added to the denominator instead of a clamp"),
@@ -52,17 +53,30 @@ MUTANTS = [
      "decode: numerator read before the update"),
     ("den = np.einsum(\"...c,...c->...\", qf, z_new)", "den = np.einsum(\"...c,...c->...\", qf, z)",
      "decode: denominator read before the update"),
-    ("y[:, t], S, z = decode_step(S, z, Q[:, t], K[:, t], V[:, t], fmap, W, normalize)",
-     "y[:, t], S, z = decode_step(S, z, Q[:, t], K[:, t], V[:, max(t - 1, 0)], fmap, W, normalize)",
+    ("y[:, t], S, z = decode_step(S, z, Q[:, t], K[:, t], V[:, t], fmap, W, normalize, gam)",
+     "y[:, t], S, z = decode_step(S, z, Q[:, t], K[:, t], V[:, max(t - 1, 0)], fmap, W, normalize, gam)",
      "recurrent loop: value of the previous token"),
     ("S = np.cumsum(kv, axis=1)", "S = np.cumsum(kv, axis=1) - kv", "cumulative form: exclusive prefix for S"),
-    ("A = A * np.tril(np.ones((e - s, e - s)))[None]", "A = A * np.tril(np.ones((e - s, e - s)), -1)[None]",
+    ("A = A * np.tril(np.ones((L, L)))[None]", "A = A * np.tril(np.ones((L, L)), -1)[None]",
      "blockwise form: strict mask inside the block"),
-    ("+ np.einsum(\"gic,gce->gie\", qc, S)", "+ 0.0", "blockwise form: inter-block numerator dropped"),
-    ("den = A.sum(axis=2) + np.einsum(\"gic,gc->gi\", qc, z)", "den = A.sum(axis=2)",
+    ("+ sin[:, :, None] * np.einsum(\"gic,gce->gie\", qc, S)", "+ 0.0",
+     "blockwise form: inter-block numerator dropped"),
+    ("den = A.sum(axis=2) + sin * np.einsum(\"gic,gc->gi\", qc, z)", "den = A.sum(axis=2)",
      "blockwise form: inter-block denominator dropped"),
-    ("        z = z + kc.sum(axis=1)\n", "        z = z + kc[:, :-1].sum(axis=1)\n",
+    ("z = carry[:, None] * z + np.einsum(\"gj,gjc->gc\", kw, kc)",
+     "z = carry[:, None] * z + np.einsum(\"gj,gjc->gc\", kw[:, :-1], kc[:, :-1])",
      "blockwise form: last key of each block dropped from z"),
+    ("A = A * np.where(lag >= 0, gam[g] ** np.maximum(lag, 0), 0.0)",
+     "A = A * np.where(lag >= 0, gam[g] ** np.maximum(lag + 1, 0), 0.0)", "decay: exponent i-j+1"),
+    ("s0 = (gam[g] ** (idx + 1.0))[:, None]", "s0 = (gam[g] ** idx)[:, None]",
+     "decay: initial state weighted gamma^i instead of gamma^(i+1)"),
+    ("        z = gam[:, None] ** N * z + np.einsum(\"gn,gnc->gc\", wgt, Kf)",
+     "        z = z + np.einsum(\"gn,gnc->gc\", wgt, Kf)", "decay: initial normalizer not decayed"),
+    ("        S = gam[..., None, None] * S\n", "        S = S\n", "decay: decode step without decay of S"),
+    ("            sin = gam[:, None] ** (r[None, :] + 1.0)", "            sin = gam[:, None] ** r[None, :]",
+     "decay: blockwise carried state weighted gamma^r"),
+    ("            kw = gam[:, None] ** (L - 1.0 - r[None, :])", "            kw = gam[:, None] ** (L - r[None, :])",
+     "decay: blockwise update weights off by one"),
 ]
 
 

@@ -348,3 +348,95 @@ def test_performer_W_structure():
         assert np.max(np.abs(off)) < 1e-4 * np.max(np.diag(G))
     Wb = la_inputs.performer_W(m, d, seed=2)
     np.testing.assert_array_equal(la_inputs.bf16_round(Wb), Wb)
+
+
+# ---------------------------------------------------------------------------
+# Decay (RetNet item of "Variantes y extensiones"): S_t = gamma S_{t-1} + phi(k_t) v_t^T
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def decay_example():
+    g = _load("worked_example_decay.json")
+    e = _load("worked_example_elu1.json")
+    return g, _mat(e["q"]), _mat(e["k"]), _mat(e["v"]), _mat(e["S0"]), np.array(e["z0"], dtype=np.float64)
+
+
+def test_decay_worked_example(decay_example):
+    """Hand-derived values with gamma = 1/2: catches a wrong exponent (i-j+1,
+    j-i), an undecayed normalizer, or the decay applied after the update."""
+    g, q, k, v, S0, z0 = decay_example
+    gam = g["gamma"]
+    for norm, key in [(True, "causal_normalized"), (False, "causal_unnormalized")]:
+        want = _frac(g[key])
+        np.testing.assert_allclose(O.attention(q, k, v, "elu1", normalize=norm, decay=gam), want, rtol=1e-12)
+        np.testing.assert_allclose(O.recurrent(q, k, v, "elu1", normalize=norm, decay=gam)[0], want, rtol=1e-12)
+        for c in (1, 2, 3):
+            np.testing.assert_allclose(O.chunked(q, k, v, "elu1", normalize=norm, chunk=c, decay=gam)[0], want,
+                                       rtol=1e-12, err_msg=f"chunk {c}")
+    S, z = O.final_state(k, v, "elu1", decay=gam)
+    np.testing.assert_allclose(S, _frac(g["final_S"]), rtol=1e-12)
+    np.testing.assert_allclose(z, np.array([float(Fraction(x)) for x in g["final_z"]]), rtol=1e-12)
+    for c in (1, 2):
+        _, Sc, zc = O.chunked(q, k, v, "elu1", chunk=c, decay=gam)
+        np.testing.assert_allclose(Sc, S, rtol=1e-12)
+        np.testing.assert_allclose(zc, z, rtol=1e-12)
+    Sw, zw = _frac(g["final_S_with_state"]), np.array([float(Fraction(x)) for x in g["final_z_with_state"]])
+    for Sx, zx in (O.final_state(k, v, "elu1", S0=S0, z0=z0, decay=gam),
+                   O.recurrent(q, k, v, "elu1", S0=S0, z0=z0, decay=gam)[1:],
+                   O.chunked(q, k, v, "elu1", chunk=2, S0=S0, z0=z0, decay=gam)[1:]):
+        np.testing.assert_allclose(Sx, Sw, rtol=1e-12)
+        np.testing.assert_allclose(zx, zw, rtol=1e-12)
+    want0 = np.array([float(Fraction(x)) for x in g["causal_normalized_with_state_row0"]])
+    for y in (O.attention(q, k, v, "elu1", S0=S0, z0=z0, decay=gam)[0],
+              O.recurrent(q, k, v, "elu1", S0=S0, z0=z0, decay=gam)[0][0],
+              O.chunked(q, k, v, "elu1", chunk=2, S0=S0, z0=z0, decay=gam)[0][0]):
+        np.testing.assert_allclose(y, want0, rtol=1e-12)
+
+
+def test_decay_zero_and_one():
+    """gamma = 0 keeps only the current token (normalized y_i = v_i); gamma = 1 is no decay."""
+    q, k, v = la_inputs.gaussian_qkv(1, 2, 70, 8, seed=3, scale=1.0, bf16=False)
+    for f in (lambda **kw: O.attention(q, k, v, "elu1", **kw),
+              lambda **kw: O.recurrent(q, k, v, "elu1", **kw)[0],
+              lambda **kw: O.chunked(q, k, v, "elu1", chunk=16, **kw)[0]):
+        np.testing.assert_allclose(f(decay=0.0), v, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(f(decay=1.0), f(), rtol=1e-12, atol=1e-12)
+    qf, kf = O.phi_elu1(q), O.phi_elu1(k)
+    np.testing.assert_allclose(O.attention(q, k, v, "elu1", normalize=False, decay=0.0),
+                               np.sum(qf * kf, axis=-1, keepdims=True) * v, rtol=1e-12)
+
+
+def test_decay_equal_keys_is_a_first_order_filter():
+    """All keys equal: y_i = sum_j gamma^(i-j) v_j / sum_j gamma^(i-j), the
+    ratio of two first-order recursive filters (scipy.signal.lfilter)."""
+    from scipy.signal import lfilter
+    rng = np.random.default_rng(8)
+    N, d, gam = 90, 6, 0.83
+    # positive q, k keep the identity map's denominator positive (away from the clamp)
+    q = rng.uniform(0.1, 1.0, (N, d))
+    k = np.broadcast_to(rng.uniform(0.1, 1.0, (1, d)), (N, d))
+    v = rng.standard_normal((N, d))
+    want = lfilter([1.0], [1.0, -gam], v, axis=0) / lfilter([1.0], [1.0, -gam], np.ones((N, 1)), axis=0)
+    for fmap in ("elu1", "identity"):
+        np.testing.assert_allclose(O.attention(q, k, v, fmap, decay=gam), want, rtol=1e-10)
+        np.testing.assert_allclose(O.chunked(q, k, v, fmap, chunk=32, decay=gam)[0], want, rtol=1e-10)
+
+
+def test_decay_split_resume_per_head_and_decode():
+    """The state after a prefix (decayed to its end) continues the sequence;
+    each head keeps its own gamma; decode steps continue a decayed prefill."""
+    q, k, v = la_inputs.gaussian_qkv(2, 3, 150, 16, seed=12, scale=0.7, bf16=False)
+    gam = np.array([0.95, 0.6, 0.999])
+    full = O.attention(q, k, v, "elu1", decay=gam)
+    S, z = O.final_state(k[:, :, :100], v[:, :, :100], "elu1", decay=gam)
+    tail = O.attention(q[:, :, 100:], k[:, :, 100:], v[:, :, 100:], "elu1", S0=S, z0=z, decay=gam)
+    np.testing.assert_allclose(tail, full[:, :, 100:], rtol=1e-10, atol=1e-12)
+    for h in range(3):
+        one = O.attention(q[:, h], k[:, h], v[:, h], "elu1", decay=gam[h])
+        np.testing.assert_allclose(one, full[:, h], rtol=1e-12)
+    Sd, zd = S, z
+    for t in range(100, 104):
+        y, Sd, zd = O.decode_step(Sd, zd, q[:, :, t], k[:, :, t], v[:, :, t], "elu1", decay=gam[None, :])
+        np.testing.assert_allclose(y, full[:, :, t], rtol=1e-10, atol=1e-12)
+    with pytest.raises(ValueError):
+        O.attention(q, k, v, "elu1", causal=False, decay=0.9)
