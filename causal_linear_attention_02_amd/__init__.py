@@ -22,7 +22,7 @@ __all__ = [
     "LA_F32", "LA_BF16", "LA_ELU1", "LA_PERFORMER", "LA_IDENTITY",
     "la_feature_map", "lib", "library_path", "LinAttnError",
     "la_version", "la_status_string", "la_forward_workspace_size", "la_forward", "la_forward_ex",
-    "la_decode_step", "la_feature_map_apply", "feature_dim",
+    "la_decode_step", "la_feature_map_apply", "feature_dim", "la_forward_decay", "la_decode_step_decay",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,6 +62,10 @@ def _load():
     L.la_forward_ex.argtypes, L.la_forward_ex.restype = fwd + [vp], i
     L.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, fmp, i, i, vp]
     L.la_decode_step.restype = i
+    L.la_forward_decay.argtypes = [vp, vp, vp, vp, i, i, i, i, fmp, vp, i, i, vp, vp, vp, vp, vp, sz, vp]
+    L.la_forward_decay.restype = i
+    L.la_decode_step_decay.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, fmp, vp, i, i, vp]
+    L.la_decode_step_decay.restype = i
     L.la_feature_map_apply.argtypes = [vp, vp, ctypes.c_longlong, i, fmp, i, i, vp]
     L.la_feature_map_apply.restype = i
     return L
@@ -206,6 +210,61 @@ def la_decode_step(S, z, q, k, v, *, feature_map="elu1", W=None, normalize=True,
     st = lib.la_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, d, ctypes.byref(fm),
                             int(normalize), _dtype_code(q), _stream(stream))
     _check(st, "la_decode_step")
+    return out
+
+
+def _gamma(gamma, H, device):
+    if not torch.is_tensor(gamma) or gamma.dtype != torch.float32 or gamma.numel() != H:
+        raise ValueError("gamma: a float32 tensor with one value per head")
+    if gamma.device != device:
+        raise ValueError("gamma must live on the same device as the inputs")
+    return gamma.contiguous()
+
+
+def la_forward_decay(q, k, v, gamma, *, feature_map="elu1", W=None, normalize=True, S_in=None, z_in=None,
+                     return_state=False, out=None, workspace=None, stream=None):
+    """Causal linear attention with a per-head decay gamma [H] on [B, H, N, d] tensors."""
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    g = _gamma(gamma, H, q.device)
+    fm = _fmap(feature_map, W)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    S_out = z_out = None
+    if return_state:
+        df = feature_dim(d, feature_map, W)
+        S_out = torch.empty((B, H, df, d), device=q.device, dtype=torch.float32)
+        z_out = torch.empty((B, H, df), device=q.device, dtype=torch.float32)
+    need = int(lib.la_forward_workspace_size(B, H, N, d, ctypes.byref(fm), 1))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.la_forward_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d, ctypes.byref(fm), _ptr(g),
+                              int(normalize), _dtype_code(q), _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out),
+                              _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "la_forward_decay")
+    return (out, S_out, z_out) if return_state else out
+
+
+def la_decode_step_decay(S, z, q, k, v, gamma, *, feature_map="elu1", W=None, normalize=True, out=None,
+                         stream=None):
+    """Decode step with a per-head decay gamma [H]; S, z updated in place."""
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, d] shape")
+    B, H, d = q.shape
+    g = _gamma(gamma, H, q.device)
+    fm = _fmap(feature_map, W)
+    df = feature_dim(d, feature_map, W)
+    if tuple(S.shape) != (B, H, df, d) or tuple(z.shape) != (B, H, df):
+        raise ValueError("state shapes must be S [B, H, d', d] and z [B, H, d']")
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib.la_decode_step_decay(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, d, ctypes.byref(fm),
+                                  _ptr(g), int(normalize), _dtype_code(q), _stream(stream))
+    _check(st, "la_decode_step_decay")
     return out
 
 

@@ -122,11 +122,17 @@ size_t la_forward_workspace_size(int B, int H, int N, int d, const la_feature_ma
   return make_plan((long long)B * H, N, d, dfeat, causal != 0, feature_map->kind == LA_PERFORMER).ws_bytes;
 }
 
-int la_forward_ex(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
-                  const la_feature_map* feature_map, int causal, int normalize, int dtype, const float* S_in,
-                  const float* z_in, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
-                  hipStream_t stream, hipEvent_t* events) {
+}  // extern "C"
+
+namespace {
+
+// The whole forward; gamma (device, [H]) is the per-head decay or null.
+int forward_impl(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+                 const la_feature_map* feature_map, int causal, int normalize, int dtype, const float* S_in,
+                 const float* z_in, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream, hipEvent_t* events, const float* gamma) {
   if (B < 0 || H < 0 || N < 0) return LA_ERR_INVALID_ARG;
+  if (gamma && (causal != 1 || (reinterpret_cast<uintptr_t>(gamma) & 3u) != 0)) return LA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return LA_ERR_INVALID_ARG;
   if (normalize != 0 && normalize != 1) return LA_ERR_INVALID_ARG;
   if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
@@ -240,6 +246,8 @@ int la_forward_ex(const void* q, const void* k, const void* v, void* out, int B,
   a.z_out = causal ? z_out : nullptr;
   a.normalize = normalize;
   a.W = feature_map->W;
+  a.gamma = gamma;
+  a.H = H;
 
   la::ScanArgs s{};
   s.ws = a.ws;
@@ -250,6 +258,9 @@ int la_forward_ex(const void* q, const void* k, const void* v, void* out, int B,
   s.D = d;
   s.S_in = S_in;
   s.z_in = z_in;
+  s.gamma = gamma;
+  s.H = H;
+  s.seg_len = 64 * p.cps;  // every combined (non-last) segment is whole
   if (causal) {
     s.P = p.P - 1;
     s.exclusive = 1;
@@ -262,8 +273,29 @@ int la_forward_ex(const void* q, const void* k, const void* v, void* out, int B,
     s.z_out = z_out;
   }
   const int kfm = feature_map->kind == LA_ELU1 ? la::kElu1 : la::kIdentity;  // mapped features: identity inside
-  return status_from_hip(la::prefill_dispatch(a, s, d, dfeat, kfm, dtype,
-                                              causal != 0, stream, events));
+  return status_from_hip(la::prefill_dispatch(a, s, d, dfeat, kfm, dtype, causal != 0, gamma != nullptr, stream,
+                                              events));
+}
+
+}  // namespace
+
+extern "C" {
+
+int la_forward_ex(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+                  const la_feature_map* feature_map, int causal, int normalize, int dtype, const float* S_in,
+                  const float* z_in, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream, hipEvent_t* events) {
+  return forward_impl(q, k, v, out, B, H, N, d, feature_map, causal, normalize, dtype, S_in, z_in, S_out, z_out,
+                      workspace, workspace_bytes, stream, events, nullptr);
+}
+
+int la_forward_decay(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+                     const la_feature_map* feature_map, const float* gamma, int normalize, int dtype,
+                     const float* S_in, const float* z_in, float* S_out, float* z_out, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  if (!gamma) return LA_ERR_INVALID_ARG;
+  return forward_impl(q, k, v, out, B, H, N, d, feature_map, 1, normalize, dtype, S_in, z_in, S_out, z_out,
+                      workspace, workspace_bytes, stream, nullptr, gamma);
 }
 
 int la_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
@@ -274,9 +306,15 @@ int la_forward(const void* q, const void* k, const void* v, void* out, int B, in
                        workspace, workspace_bytes, stream, nullptr);
 }
 
-int la_decode_step(float* S, float* z, const void* q, const void* k, const void* v, void* out, int B, int H,
-                   int d, const la_feature_map* feature_map, int normalize, int dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_impl(float* S, float* z, const void* q, const void* k, const void* v, void* out, int B, int H, int d,
+                const la_feature_map* feature_map, int normalize, int dtype, hipStream_t stream,
+                const float* gamma) {
   if (B < 0 || H < 0) return LA_ERR_INVALID_ARG;
+  if (gamma && (reinterpret_cast<uintptr_t>(gamma) & 3u) != 0) return LA_ERR_INVALID_ARG;
   if (normalize != 0 && normalize != 1) return LA_ERR_INVALID_ARG;
   if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
   if (!d_supported(d)) return LA_ERR_UNSUPPORTED;
@@ -310,7 +348,25 @@ int la_decode_step(float* S, float* z, const void* q, const void* k, const void*
   a.BH = (int)BH;
   a.normalize = normalize;
   a.W = feature_map->W;
+  a.gamma = gamma;
+  a.H = H;
   return status_from_hip(la::decode_dispatch(a, d, dfeat, feature_map->kind, dtype, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int la_decode_step(float* S, float* z, const void* q, const void* k, const void* v, void* out, int B, int H,
+                   int d, const la_feature_map* feature_map, int normalize, int dtype, hipStream_t stream) {
+  return decode_impl(S, z, q, k, v, out, B, H, d, feature_map, normalize, dtype, stream, nullptr);
+}
+
+int la_decode_step_decay(float* S, float* z, const void* q, const void* k, const void* v, void* out, int B, int H,
+                         int d, const la_feature_map* feature_map, const float* gamma, int normalize, int dtype,
+                         hipStream_t stream) {
+  if (!gamma) return LA_ERR_INVALID_ARG;
+  return decode_impl(S, z, q, k, v, out, B, H, d, feature_map, normalize, dtype, stream, gamma);
 }
 
 int la_feature_map_apply(const void* x, void* phi, long long rows, int d, const la_feature_map* feature_map,

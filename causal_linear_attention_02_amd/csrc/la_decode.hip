@@ -130,11 +130,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // z <- z + phi(k); partial phi(q).z
+  // decay ("Linear Attention", "Variantes y extensiones"): S <- gamma S + phi(k) v^T, z alike
+  const float gm = (a.gamma && valid) ? a.gamma[head % a.H] : 1.f;
+  // z <- gamma z + phi(k); partial phi(q).z
   float dpart = 0.f;
   if (valid) {
     for (int c = t; c < DF; c += SH::TPH) {
-      const float zn = a.z[head * DF + c] + s_phik[hb][c];
+      const float zn = gm * a.z[head * DF + c] + s_phik[hb][c];
       a.z[head * DF + c] = zn;
       dpart += s_phiq[hb][c] * zn;
     }
@@ -151,10 +153,10 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
       const int r = rg + SH::R * i;
       const float pk = s_phik[hb][r], pq = s_phiq[hb][r];
       f32x4 s = Sv[i];
-      s[0] += pk * v4[0];
-      s[1] += pk * v4[1];
-      s[2] += pk * v4[2];
-      s[3] += pk * v4[3];
+      s[0] = gm * s[0] + pk * v4[0];
+      s[1] = gm * s[1] + pk * v4[1];
+      s[2] = gm * s[2] + pk * v4[2];
+      s[3] = gm * s[3] + pk * v4[3];
       *reinterpret_cast<f32x4*>(Sh + (long long)r * D + 4 * cg) = s;
       num[0] += pq * s[0];
       num[1] += pq * s[1];

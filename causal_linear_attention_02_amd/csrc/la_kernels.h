@@ -38,6 +38,8 @@ struct FwdArgs {
   float* z_out;
   int normalize;
   const float* W;          // random-feature projection [DF][D] (fp32) or null
+  const float* gamma;      // decay per head [H] (causal only) or null
+  int H;                   // heads (gamma index = bh % H)
 };
 
 struct ScanArgs {
@@ -53,6 +55,9 @@ struct ScanArgs {
   const float* z_in;
   float* S_out;     // total state (non-causal only)
   float* z_out;
+  const float* gamma;  // decay per head [H] or null: P_{s+1} = gamma^seg_len P_s + L_s
+  int H;
+  int seg_len;         // tokens per combined segment (all full)
 };
 
 struct DecodeArgs {
@@ -65,6 +70,8 @@ struct DecodeArgs {
   int BH;
   int normalize;
   const float* W;   // [DF][D] or null
+  const float* gamma;  // decay per head [H] or null: S <- gamma S + phi(k) v^T
+  int H;
 };
 
 struct FmapArgs {
@@ -75,7 +82,7 @@ struct FmapArgs {
 };
 
 hipError_t prefill_dispatch(const FwdArgs& a, const ScanArgs& s, int D, int DF, int fmap, int dtype, bool causal,
-                            hipStream_t st, hipEvent_t* ev);
+                            bool decay, hipStream_t st, hipEvent_t* ev);
 hipError_t decode_dispatch(const DecodeArgs& a, int D, int DF, int fmap, int dtype, hipStream_t st);
 hipError_t fmap_dispatch(const FmapArgs& a, int D, int DF, int fmap, int in_dtype, int out_dtype, hipStream_t st);
 hipError_t copy_state_dispatch(const float* S_in, const float* z_in, float* S_out, float* z_out, long long nS,

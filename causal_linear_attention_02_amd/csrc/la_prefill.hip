@@ -219,10 +219,11 @@ __device__ __forceinline__ ChunkRsrc chunk_rsrc(const IN* q, const IN* k, const 
                    make_rsrc(v + row_base * D, vbytes)};
 }
 
-// phi(q) piece i: LDS tile row, and dp = phi(q) . z over the piece's columns
-template <int D, int DF, typename IN, typename OP, int FM>
+// phi(q) piece i (times the row scale sc when SC): LDS tile row, and
+// dp = phi(q) . z over the piece's columns
+template <int D, int DF, typename IN, typename OP, int FM, bool SC>
 __device__ __forceinline__ float stage_q_piece(const typename In8<IN>::raw& r, int p, int i, uint8_t* sQ,
-                                               const float (&z)[8]) {
+                                               const float (&z)[8], float sc) {
   using G = Stage<D, DF>;
   float x[8];
   In8<IN>::to_f32(r, x);
@@ -230,16 +231,18 @@ __device__ __forceinline__ float stage_q_piece(const typename In8<IN>::raw& r, i
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     x[e] = fmap_in_stage<FM>(x[e]);
+    if constexpr (SC) x[e] *= sc;
     d += x[e] * z[e];
   }
   Ops<OP>::template store8<DF * Ops<OP>::kBytes>(sQ, p / G::RLF + G::RSF * i, 8 * (p % G::RLF), x);
   return d;
 }
 
-// phi(k) piece i (rows past `valid` masked to phi = 0): LDS tile row, column sums into cs
-template <int D, int DF, typename IN, typename OP, int FM>
+// phi(k) piece i (rows past `valid` masked to phi = 0; times the row scale sc
+// when SC): LDS tile row, column sums into cs
+template <int D, int DF, typename IN, typename OP, int FM, bool SC>
 __device__ __forceinline__ void stage_k_piece(typename In8<IN>::raw r, int p, int i, int valid, uint8_t* sK,
-                                              float (&cs)[8]) {
+                                              float (&cs)[8], float sc) {
   using G = Stage<D, DF>;
   const int row = p / G::RLF + G::RSF * i;
   const auto fill = FM == kElu1 ? In8<IN>::neg_inf() : In8<IN>::zero();
@@ -259,10 +262,26 @@ __device__ __forceinline__ void stage_k_piece(typename In8<IN>::raw r, int p, in
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     x[e] = fmap_in_stage<FM>(x[e]);
+    if constexpr (SC) x[e] *= sc;
     cs[e] += x[e];
   }
   Ops<OP>::template store8<DF * Ops<OP>::kBytes>(sK, row, 8 * (p % G::RLF), x);
 }
+
+// ---------------------------------------------------------------------------
+// Decay ("Linear Attention", "Variantes y extensiones", RetNet item):
+// S_t = gamma S_{t-1} + phi(k_t) v_t^T, z alike. Inside a chunk, row r of
+// phi(Q) is staged times gamma^(r-32) and row r of phi(K) times gamma^(32-r),
+// so the chunk's score matrix carries gamma^(r_i - r_j). Running states are
+// kept as gamma^-31 times the true ones; then one chunk moves them on as
+// S' <- gamma^64 S' + K^T V with the scaled keys, and the carried term of row
+// r_i, gamma^(r_i+1) phi(q_i) S, is (scaled q_i) . (gamma^64 S'). With
+// gamma >= 1/4 no scale exceeds 2^64; gamma^64 itself can fall below the
+// normal fp32 range, so it is applied as gamma^32 twice.
+// ---------------------------------------------------------------------------
+constexpr int kDecayCenter = 32;
+constexpr int kDecayFrame = kChunk - 1 - kDecayCenter;  // 31
+__device__ __forceinline__ float gpow(float lg, float n) { return __builtin_amdgcn_exp2f(lg * n); }
 
 // DPP lane moves within rows of 16 lanes (quad_perm, mirrors, rotations).
 template <int CTRL>
@@ -327,7 +346,7 @@ __device__ __forceinline__ void store_state_tiles(const f32x16 (&S)[DF / 32], fl
 // owns value columns [32w, 32w+32) of S.
 // grid = (BH, P), block = 2*D threads.
 // ---------------------------------------------------------------------------
-template <int D, int DF, typename OP, typename IN, int FM>
+template <int D, int DF, typename OP, typename IN, int FM, bool DECAY>
 __global__ __launch_bounds__(D * 2) void state_pass_kernel(FwdArgs a) {
   using Frag = typename Ops<OP>::frag;
   using G = Stage<D, DF>;
@@ -355,6 +374,8 @@ __global__ __launch_bounds__(D * 2) void state_pass_kernel(FwdArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) zr[e] = 0.f;
   const Voff<D, DF, IN> vo(p);
+  const float lg = DECAY ? __log2f(a.gamma[bh % a.H]) : 0.f;
+  const float gH = DECAY ? gpow(lg, kChunk / 2) : 1.f;  // gamma^32; a chunk moves states on by gH twice
 
   // every load is issued (with zero size past the segment) so that all
   // iterations have the same memory instruction stream
@@ -368,15 +389,33 @@ __global__ __launch_bounds__(D * 2) void state_pass_kernel(FwdArgs a) {
     const int c = c0 + m;
     mask_tail_keys<D, DF, IN, FM>(pf, p, min(64, a.N - 64 * c));
     uint8_t* sK = smem + (NB == 2 ? (m & 1) : 0) * BUF;
-    prod_stage<D, DF, IN, OP, FM, false, true>(pf, p, nullptr, sK, sK + KB, zr, dp, cs);
+    if constexpr (DECAY) {
+      // scaled keys (see the decay note above); v pieces raw
 #pragma unroll
-    for (int e = 0; e < 8; ++e) zr[e] += cs[e];
+      for (int e = 0; e < 8; ++e) cs[e] = 0.f;
+#pragma unroll
+      for (int i = 0; i < G::NQ; ++i)
+        stage_k_piece<D, DF, IN, OP, FM, true>(pf.k[i], p, i, 64, sK, cs,
+                                               gpow(lg, kDecayCenter - (p / G::RLF + G::RSF * i)));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store_raw<IN, OP, RBV>(sK + KB, p / G::RLV + 16 * i, 8 * (p % G::RLV), pf.v[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zr[e] = gH * (gH * zr[e]) + cs[e];
+    } else {
+      prod_stage<D, DF, IN, OP, FM, false, true>(pf, p, nullptr, sK, sK + KB, zr, dp, cs);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zr[e] += cs[e];
+    }
   };
   // iteration m: multiply chunk m (in LDS), stage chunk m+1, and keep the
   // loads of the following chunk(s) in flight
   auto mult = [&](int m) {
     const uint8_t* sK = smem + (NB == 2 ? (m & 1) : 0) * BUF;
     const uint8_t* sV = sK + KB;
+    if constexpr (DECAY) {
+#pragma unroll
+      for (int cb = 0; cb < DF / 32; ++cb) S[cb] = (S[cb] * gH) * gH;
+    }
     Frag Vf[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) Vf[kb] = Ops<OP>::template load_cols<RBV>(sV, 16 * kb, 32 * w);
@@ -434,12 +473,17 @@ __global__ __launch_bounds__(D * 2) void state_pass_kernel(FwdArgs a) {
   }
   __syncthreads();
   float* st = a.ws + ((long long)bh * a.ws_slots + seg) * a.state_elems;
+  const float fr = DECAY ? gpow(lg, kDecayFrame) : 1.f;  // back from the scaled frame
+  if constexpr (DECAY) {
+#pragma unroll
+    for (int cb = 0; cb < DF / 32; ++cb) S[cb] *= fr;
+  }
   store_state_tiles<D, DF>(S, st, w);
   for (int c = p; c < DF; c += 2 * D) {
     float s = 0.f;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) s += zsum[ww][c];
-    st[DF * D + c] = s;
+    st[DF * D + c] = fr * s;
   }
 }
 
@@ -464,6 +508,8 @@ __global__ __launch_bounds__(256) void carry_scan_kernel(ScanArgs a) {
   }
   float* col = a.ws + (long long)bh * a.ws_slots * a.state_elems + e;
   const long long st = a.state_elems;
+  // decay: each combined segment of seg_len tokens multiplies what precedes it by gamma^seg_len
+  const float g = a.gamma ? gpow(__log2f(a.gamma[bh % a.H]), (float)a.seg_len) : 1.f;
   for (int p0 = 0; p0 < a.P; p0 += 8) {
     const int cnt = min(8, a.P - p0);
     f32x4 t[8];
@@ -474,10 +520,10 @@ __global__ __launch_bounds__(256) void carry_scan_kernel(ScanArgs a) {
     for (int j = 0; j < 8; ++j) {
       if (j < cnt) {
         if (a.exclusive) *reinterpret_cast<f32x4*>(col + (p0 + j) * st) = run;
-        run[0] += t[j][0];
-        run[1] += t[j][1];
-        run[2] += t[j][2];
-        run[3] += t[j][3];
+        run[0] = g * run[0] + t[j][0];
+        run[1] = g * run[1] + t[j][1];
+        run[2] = g * run[2] + t[j][2];
+        run[3] = g * run[3] + t[j][3];
       }
     }
   }
@@ -517,8 +563,9 @@ struct OutLayout {
   static constexpr int BYTES = NB * BUF + DEN + ZP + YB;
 };
 
-template <int D, int DF, typename OP, typename IN, int FM, bool CAUSAL>
+template <int D, int DF, typename OP, typename IN, int FM, bool CAUSAL, bool DECAY>
 __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
+  static_assert(!DECAY || CAUSAL, "decay is defined for the causal form only");
   using Frag = typename Ops<OP>::frag;
   using L = OutLayout<D, DF, OP, IN, CAUSAL>;
   using G = Stage<D, DF>;
@@ -548,6 +595,15 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
   const int pw = wave - L::NWC;                // producer wave index
   const int cw = wave;                         // consumer wave = value-column block
 
+  // decay: per-head gamma, the per-chunk factor and the factor of the final
+  // state (scaled frame back to the true one, and a partial last chunk of
+  // vl rows moved on by gamma^vl instead of gamma^64)
+  const float lg = DECAY ? __log2f(a.gamma[bh % a.H]) : 0.f;
+  const float gH = DECAY ? gpow(lg, kChunk / 2) : 1.f;  // gamma^32; a chunk moves states on by gH twice
+  const int vl = a.N - kChunk * (a.nchunks - 1);
+  const float fout = DECAY ? gpow(lg, kDecayFrame + vl - kChunk) : 1.f;
+  const float fin = DECAY ? gpow(lg, -kDecayFrame) : 1.f;
+
   const float* Sinit;
   const float* zinit;
   if (a.init_from_ws) {
@@ -567,7 +623,7 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
     const int cr = 8 * (p % G::RLF);
     const Voff<D, DF, IN> vo(p);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) zrun[e] = zinit ? zinit[cr + e] : 0.f;
+    for (int e = 0; e < 8; ++e) zrun[e] = zinit ? fin * zinit[cr + e] : 0.f;
     // Drain that load now: otherwise the wait-count analysis carries it
     // around the loop and waits for every outstanding prefetch each step.
     wait_vmem_all();
@@ -605,15 +661,21 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
             const f32x4 z1 = *reinterpret_cast<const f32x4*>(zp + ww * DF + cr + 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              zrun[e] += z0[e];
-              zrun[4 + e] += z1[e];
+              zrun[e] = (ww == 0 ? gH * (gH * zrun[e]) : zrun[e]) + z0[e];
+              zrun[4 + e] = (ww == 0 ? gH * (gH * zrun[4 + e]) : zrun[4 + e]) + z1[e];
             }
           }
         }
       }
       if constexpr (L::NB == 1) __syncthreads();  // consumers are done with the buffer
+      // decay: the carried normalizer moved on by gamma^64 before the dot
+      // product with the scaled q rows (the two scales would overflow apart)
+      float zs[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) cs[e] = 0.f;
+      for (int e = 0; e < 8; ++e) {
+        zs[e] = gH * (gH * zrun[e]);
+        cs[e] = 0.f;
+      }
 #pragma unroll
       for (int i = 0; i < NSLOT; ++i) {
         if (i < 4) {
@@ -637,8 +699,12 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
         }
         if (stg) {
           if (i < G::NQ) {
-            dp[i] = stage_q_piece<D, DF, IN, OP, FM>(cur.q[i], p, i, sQ, zrun);
-            if constexpr (CAUSAL) stage_k_piece<D, DF, IN, OP, FM>(cur.k[i], p, i, vs, sK, cs);
+            const int row = p / G::RLF + G::RSF * i;
+            dp[i] = stage_q_piece<D, DF, IN, OP, FM, DECAY>(cur.q[i], p, i, sQ, zs,
+                                                            DECAY ? gpow(lg, row - kDecayCenter) : 1.f);
+            if constexpr (CAUSAL)
+              stage_k_piece<D, DF, IN, OP, FM, DECAY>(cur.k[i], p, i, vs, sK, cs,
+                                                      DECAY ? gpow(lg, kDecayCenter - row) : 1.f);
           }
           if constexpr (CAUSAL) {
             if (i < 4) store_raw<IN, OP, L::RBV>(sV, p / G::RLV + 16 * i, 8 * (p % G::RLV), cur.v[i]);
@@ -671,6 +737,8 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
           // final z = z_{n-2} + column sums of the last chunk
           const float* zp = zpart + ((it - 1) & 1) * L::NWP * DF;
 #pragma unroll
+          for (int e = 0; e < 8; ++e) zrun[e] = gH * (gH * zrun[e]);
+#pragma unroll
           for (int ww = 0; ww < L::NWP; ++ww)
 #pragma unroll
             for (int e = 0; e < 8; ++e) zrun[e] += zp[ww * DF + cr + e];
@@ -699,7 +767,7 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
       if (a.S_out && seg == a.nseg - 1 && p < G::RLF) {
         float* zo = a.z_out + (long long)bh * DF + cr;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) zo[e] = zrun[e];
+        for (int e = 0; e < 8; ++e) zo[e] = fout * zrun[e];
       }
     }
   } else {
@@ -708,6 +776,10 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
     // ------------------------------------------------------------------
     f32x16 S[DF / 32];
     load_state_tiles<D, DF>(S, Sinit, cw);
+    if constexpr (DECAY) {
+#pragma unroll
+      for (int cb = 0; cb < DF / 32; ++cb) S[cb] *= fin;
+    }
     Frag Sf_const[CAUSAL ? 1 : DF / 16];
     if constexpr (!CAUSAL) {
 #pragma unroll
@@ -729,6 +801,10 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
       float dpart0 = 0.f, dpart1 = 0.f;
       Frag Vf[4];
       if constexpr (CAUSAL) {
+        if constexpr (DECAY) {
+#pragma unroll
+          for (int cb = 0; cb < DF / 32; ++cb) S[cb] = (S[cb] * gH) * gH;
+        }
         f32x16 A00 = {}, A01 = {}, A11 = {};
 #pragma unroll
         for (int kb = 0; kb < DF / 16; ++kb) {
@@ -819,7 +895,13 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
       for (int bar = 0; bar < L::NBAR; ++bar) __syncthreads();
     }
     if constexpr (CAUSAL) {
-      if (a.S_out && seg == a.nseg - 1) store_state_tiles<D, DF>(S, a.S_out + (long long)bh * DF * D, cw);
+      if (a.S_out && seg == a.nseg - 1) {
+        if constexpr (DECAY) {
+#pragma unroll
+          for (int cb = 0; cb < DF / 32; ++cb) S[cb] *= fout;
+        }
+        store_state_tiles<D, DF>(S, a.S_out + (long long)bh * DF * D, cw);
+      }
     }
   }
 }
@@ -827,12 +909,13 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // Host-side launchers (one instantiation per supported shape)
 // ---------------------------------------------------------------------------
-template <int D, int DF, typename OP, typename IN, int FM>
-static hipError_t launch_prefill(const FwdArgs& a, const ScanArgs& s, bool causal, hipStream_t st,
-                                 hipEvent_t* ev) {
+template <int D, int DF, typename OP, typename IN, int FM, bool DECAY>
+static hipError_t launch_prefill_t(const FwdArgs& a, const ScanArgs& s, bool causal, hipStream_t st,
+                                   hipEvent_t* ev) {
   // ev[0] is recorded by the caller (before any feature-map kernels)
   if (a.run_state_pass) {
-    hipLaunchKernelGGL((state_pass_kernel<D, DF, OP, IN, FM>), dim3(a.BH, a.nseg_state), dim3(D * 2), 0, st, a);
+    hipLaunchKernelGGL((state_pass_kernel<D, DF, OP, IN, FM, DECAY>), dim3(a.BH, a.nseg_state), dim3(D * 2), 0, st,
+                       a);
   }
   if (ev) (void)hipEventRecord(ev[1], st);
   if (a.run_scan) {
@@ -840,27 +923,38 @@ static hipError_t launch_prefill(const FwdArgs& a, const ScanArgs& s, bool causa
   }
   if (ev) (void)hipEventRecord(ev[2], st);
   if (causal) {
-    hipLaunchKernelGGL((output_pass_kernel<D, DF, OP, IN, FM, true>), dim3(a.BH, a.nseg), dim3(D * 4), 0, st, a);
+    hipLaunchKernelGGL((output_pass_kernel<D, DF, OP, IN, FM, true, DECAY>), dim3(a.BH, a.nseg), dim3(D * 4), 0, st,
+                       a);
   } else {
-    hipLaunchKernelGGL((output_pass_kernel<D, DF, OP, IN, FM, false>), dim3(a.BH, a.nseg), dim3(D * 4), 0, st, a);
+    if constexpr (DECAY) return hipErrorInvalidValue;
+    else
+      hipLaunchKernelGGL((output_pass_kernel<D, DF, OP, IN, FM, false, false>), dim3(a.BH, a.nseg), dim3(D * 4), 0,
+                         st, a);
   }
   if (ev) (void)hipEventRecord(ev[3], st);
   return hipGetLastError();
 }
 
+template <int D, int DF, typename OP, typename IN, int FM>
+static hipError_t launch_prefill(const FwdArgs& a, const ScanArgs& s, bool causal, bool decay, hipStream_t st,
+                                 hipEvent_t* ev) {
+  if (decay) return launch_prefill_t<D, DF, OP, IN, FM, true>(a, s, causal, st, ev);
+  return launch_prefill_t<D, DF, OP, IN, FM, false>(a, s, causal, st, ev);
+}
+
 template <typename T>
-static hipError_t prefill_typed(const FwdArgs& a, const ScanArgs& s, int D, int DF, int fmap, bool causal,
+static hipError_t prefill_typed(const FwdArgs& a, const ScanArgs& s, int D, int DF, int fmap, bool causal, bool decay,
                                 hipStream_t st, hipEvent_t* ev) {
   if (fmap == kElu1) {
     switch (D) {
-      case 32: return launch_prefill<32, 32, T, T, kElu1>(a, s, causal, st, ev);
-      case 64: return launch_prefill<64, 64, T, T, kElu1>(a, s, causal, st, ev);
-      case 128: return launch_prefill<128, 128, T, T, kElu1>(a, s, causal, st, ev);
+      case 32: return launch_prefill<32, 32, T, T, kElu1>(a, s, causal, decay, st, ev);
+      case 64: return launch_prefill<64, 64, T, T, kElu1>(a, s, causal, decay, st, ev);
+      case 128: return launch_prefill<128, 128, T, T, kElu1>(a, s, causal, decay, st, ev);
     }
     return hipErrorInvalidValue;
   }
 #define LA_PRE_CASE(d, m) \
-  if (D == d && DF == m) return launch_prefill<d, m, T, T, kIdentity>(a, s, causal, st, ev);
+  if (D == d && DF == m) return launch_prefill<d, m, T, T, kIdentity>(a, s, causal, decay, st, ev);
   LA_PRE_CASE(32, 32) LA_PRE_CASE(32, 64) LA_PRE_CASE(32, 128)
   LA_PRE_CASE(64, 64) LA_PRE_CASE(64, 128) LA_PRE_CASE(64, 256)
   LA_PRE_CASE(128, 64) LA_PRE_CASE(128, 128)
@@ -869,10 +963,11 @@ static hipError_t prefill_typed(const FwdArgs& a, const ScanArgs& s, int D, int 
 }
 
 hipError_t prefill_dispatch(const FwdArgs& a, const ScanArgs& s, int D, int DF, int fmap, int dtype, bool causal,
-                            hipStream_t st, hipEvent_t* ev) {
+                            bool decay, hipStream_t st, hipEvent_t* ev) {
   if (fmap != kElu1 && fmap != kIdentity) return hipErrorInvalidValue;
-  if (dtype == 1) return prefill_typed<__bf16>(a, s, D, DF, fmap, causal, st, ev);
-  return prefill_typed<float>(a, s, D, DF, fmap, causal, st, ev);
+  if (decay && !causal) return hipErrorInvalidValue;
+  if (dtype == 1) return prefill_typed<__bf16>(a, s, D, DF, fmap, causal, decay, st, ev);
+  return prefill_typed<float>(a, s, D, DF, fmap, causal, decay, st, ev);
 }
 
 }  // namespace la

@@ -133,6 +133,34 @@ int la_decode_step(float* S, float* z, const void* q, const void* k, const void*
                    int d, const la_feature_map* feature_map, int normalize, int dtype, hipStream_t stream);
 
 /*
+ * Causal linear attention with decay ("Linear Attention", "Variantes y
+ * extensiones", RetNet item): S_t = gamma S_{t-1} + phi(k_t) v_t^T, with the
+ * normalizer decayed alike, z_t = gamma z_{t-1} + phi(k_t) (reading: the
+ * pages give the recurrence for S only), y_t = phi(q_t)^T S_t / phi(q_t).z_t.
+ * Unrolled, token j enters output i with weight gamma^(i-j); S_in/z_in enter
+ * output i with weight gamma^(i+1); S_out/z_out are the decayed state after
+ * the last token.
+ *   gamma  in: DEVICE pointer to H fp32 values, one per head (head h of every
+ *          batch uses gamma[h]); each must lie in [1/4, 1] (1 = no decay;
+ *          the kernels scale rows of a 64-token chunk by up to gamma^(-32)).
+ *          Values are not checked on the host.
+ * Everything else as la_forward with causal = 1 (same workspace size).
+ */
+int la_forward_decay(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+                     const la_feature_map* feature_map, const float* gamma, int normalize, int dtype,
+                     const float* S_in, const float* z_in, float* S_out, float* z_out, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * la_decode_step with decay: S <- gamma S + phi(k) v^T, z <- gamma z + phi(k),
+ * then the readout. gamma: DEVICE pointer to H fp32 values (any value in
+ * [0, 1] is valid here).
+ */
+int la_decode_step_decay(float* S, float* z, const void* q, const void* k, const void* v, void* out, int B, int H,
+                         int d, const la_feature_map* feature_map, const float* gamma, int normalize, int dtype,
+                         hipStream_t stream);
+
+/*
  * The feature map alone ("Mapas de características"): phi applied to each row.
  *   x    in:  [rows][d], element type in_dtype.
  *   phi  out: [rows][d'], element type out_dtype; must not overlap x or W.

@@ -140,3 +140,18 @@ def test_binding_maps_errors_to_exceptions():
     with pytest.raises(la.LinAttnError):
         la._check(la.LA_ERR_HIP, "x")
     la._check(la.LA_OK, "x")
+
+
+def test_decay_entry_points_validate_before_launch():
+    ident = ELU
+    args = dict()
+    # null gamma, non-causal is not reachable through la_forward_decay (always causal)
+    st = lib.la_forward_decay(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, 1, 2, 64, 64,
+                              ctypes.byref(ident), None, 1, la.LA_BF16, None, None, None, None, None, 0, None)
+    assert st == la.LA_ERR_INVALID_ARG
+    st = lib.la_forward_decay(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, 1, 2, 64, 64,
+                              ctypes.byref(ident), FAKE2 + 2, 1, la.LA_BF16, None, None, None, None, None, 0, None)
+    assert st == la.LA_ERR_INVALID_ARG          # misaligned gamma
+    st = lib.la_decode_step_decay(FAKE, FAKE2, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000,
+                                  1, 2, 64, ctypes.byref(ident), None, 1, la.LA_BF16, None)
+    assert st == la.LA_ERR_INVALID_ARG

@@ -1,0 +1,114 @@
+"""GPU parity of linear attention with decay: S_t = gamma S_{t-1} + phi(k_t) v_t^T
+and z alike ("Linear Attention", marovi.ai, "Variantes y extensiones", RetNet
+item), per-head gamma, against the CPU oracle. Tolerance as elsewhere.
+"""
+
+import numpy as np
+import pytest
+
+import la_inputs
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("no GPU", allow_module_level=True)
+
+import causal_linear_attention_02_amd as la  # noqa: E402
+from gpu_helpers import TOL, log, qkv, rel_err, to_dev, to_host  # noqa: E402
+
+
+def _gammas(H, kind):
+    if kind == "retnet":   # one scale per head, 1 - 2^-(5+h)
+        return np.array([1.0 - 2.0 ** (-5 - h) for h in range(H)], dtype=np.float32)
+    if kind == "mixed":
+        return np.array([0.25, 0.6, 0.9, 0.999, 1.0][:H], dtype=np.float32)
+    return np.full(H, float(kind), dtype=np.float32)
+
+
+def _check(B, H, N, d, dt, kind, seed, fmap="elu1", m=None, normalize=True, state_in=False):
+    log(f"case decay forward B{B} H{H} N{N} d{d} {dt} gamma={kind} fmap={fmap} norm={normalize} state_in={state_in}")
+    q, k, v = qkv(B, H, N, d, seed, dt, 1.0 / np.sqrt(d))
+    g = _gammas(H, kind)
+    kw, Wref, S0, z0 = {}, None, None, None
+    if fmap == "performer":
+        w = la_inputs.performer_W(m, d, seed + 1)
+        kw = dict(W=torch.from_numpy(w).cuda())
+        Wref = w.astype(np.float64)
+    dfeat = m if fmap == "performer" else d
+    if state_in:
+        rng = np.random.default_rng(seed + 2)
+        kk = la_inputs.gaussian(rng, (B, H, 90, d), bf16=False)
+        vv = la_inputs.gaussian(rng, (B, H, 90, d), bf16=False)
+        S0, z0 = O.final_state(kk, vv, fmap, W=Wref)
+        kw.update(S_in=torch.from_numpy(S0.astype(np.float32)).cuda(), z_in=torch.from_numpy(z0.astype(np.float32)).cuda())
+    y, S, z = la.la_forward_decay(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), torch.from_numpy(g).cuda(),
+                                  feature_map=fmap, normalize=normalize, return_state=True, **kw)
+    torch.cuda.synchronize()
+    gd = g.astype(np.float64)
+    ref = O.attention(q, k, v, fmap, W=Wref, normalize=normalize, S0=S0, z0=z0, decay=gd)
+    Sr, zr = O.final_state(k, v, fmap, W=Wref, S0=S0, z0=z0, decay=gd)
+    e, eS = rel_err(to_host(y), ref), rel_err(to_host(S), Sr)
+    ez = rel_err(to_host(z)[..., None], zr[..., None])
+    log(f"  rel err y {e:.3e} S {eS:.3e} z {ez:.3e}")
+    assert e <= TOL[dt] and eS <= TOL[dt] and ez <= TOL[dt], (e, eS, ez)
+    assert S.shape[-2] == dfeat
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_decay_small(d, dt):
+    for N in (1, 63, 65, 200):
+        _check(2, 4, N, d, dt, "retnet", 40 + N + d)
+
+
+@pytest.mark.parametrize("kind", ["mixed", "retnet", 0.5])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_decay_multisegment(kind, dt):
+    """Long enough to be split into segments (the carry scan applies gamma^segment), ragged tail."""
+    _check(1, 4 if kind != "mixed" else 5, 64 * 40 - 17, 64, dt, kind, 11)
+
+
+def test_decay_state_in_unnormalized_and_maps():
+    _check(1, 3, 64 * 12 + 5, 64, "bf16", "retnet", 21, state_in=True)
+    _check(1, 3, 64 * 12 + 5, 64, "bf16", "retnet", 22, normalize=False)
+    _check(1, 2, 64 * 40 - 3, 64, "bf16", "retnet", 23, fmap="performer", m=256)
+    rng = np.random.default_rng(5)
+    # identity map, unnormalized
+    _check(1, 2, 64 * 7 + 1, 32, "f32", 0.9, 24, fmap="identity", normalize=False)
+
+
+def test_decay_one_equals_no_decay():
+    q, k, v = qkv(1, 2, 64 * 20 + 9, 64, 3, "bf16")
+    tq, tk, tv = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    a = la.la_forward_decay(tq, tk, tv, torch.ones(2, device="cuda"))
+    b = la.la_forward(tq, tk, tv)
+    torch.cuda.synchronize()
+    assert rel_err(to_host(a), to_host(b)) <= 1e-2
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_decay_decode_and_handoff(dt):
+    log(f"case decay decode {dt}")
+    B, H, d, N0, T = 2, 4, 64, 64 * 5 + 3, 5
+    q, k, v = qkv(B, H, N0 + T, d, 77, dt)
+    g = _gammas(H, "retnet")
+    tg = torch.from_numpy(g).cuda()
+    tq, tk, tv = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    _, S, z = la.la_forward_decay(tq[:, :, :N0].contiguous(), tk[:, :, :N0].contiguous(), tv[:, :, :N0].contiguous(),
+                                  tg, return_state=True)
+    ref = O.attention(q, k, v, "elu1", decay=g.astype(np.float64))
+    for t in range(N0, N0 + T):
+        y = la.la_decode_step_decay(S, z, tq[:, :, t].contiguous(), tk[:, :, t].contiguous(), tv[:, :, t].contiguous(),
+                                    tg)
+        torch.cuda.synchronize()
+        assert rel_err(to_host(y)[..., None, :], ref[:, :, t][..., None, :]) <= TOL[dt]
+    Sr, zr = O.final_state(k, v, "elu1", decay=g.astype(np.float64))
+    assert rel_err(to_host(S), Sr) <= TOL[dt]
+
+
+def test_decay_rejected_for_bad_gamma_argument():
+    x = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        la.la_forward_decay(x, x.clone(), x.clone(), torch.ones(3, device="cuda"))
