@@ -31,7 +31,10 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    # untimed calls before the timed ones: the clocks take some tens of
+    # milliseconds of sustained work to settle (5 calls: ~396 us/call,
+    # 200 calls: ~338 us/call on the long-context prefill)
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--decode-steps", type=int, default=1000)
     p.add_argument("--decode-warmup", type=int, default=20)
     p.add_argument("--no-decode", action="store_true")

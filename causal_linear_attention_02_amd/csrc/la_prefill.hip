@@ -494,8 +494,8 @@ __global__ __launch_bounds__(D * 2) void state_pass_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void carry_scan_kernel(ScanArgs a) {
   // four consecutive state elements per thread (the state size d'(d+1) is a
-  // multiple of 4 and every slot starts 16-byte aligned); the loads of eight
-  // segments are issued before their dependent adds and stores
+  // multiple of 4 and every slot starts 16-byte aligned); the loads of up to
+  // kScanBatch segments are issued before their dependent adds and stores
   const int e = 4 * (blockIdx.y * 256 + threadIdx.x);
   const int bh = blockIdx.x;
   if (e >= a.state_elems) return;
@@ -510,14 +510,15 @@ __global__ __launch_bounds__(256) void carry_scan_kernel(ScanArgs a) {
   const long long st = a.state_elems;
   // decay: each combined segment of seg_len tokens multiplies what precedes it by gamma^seg_len
   const float g = a.gamma ? gpow(__log2f(a.gamma[bh % a.H]), (float)a.seg_len) : 1.f;
-  for (int p0 = 0; p0 < a.P; p0 += 8) {
-    const int cnt = min(8, a.P - p0);
-    f32x4 t[8];
+  constexpr int kScanBatch = 32;
+  for (int p0 = 0; p0 < a.P; p0 += kScanBatch) {
+    const int cnt = min(kScanBatch, a.P - p0);
+    f32x4 t[kScanBatch];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < kScanBatch; ++j)
       if (j < cnt) t[j] = *reinterpret_cast<const f32x4*>(col + (p0 + j) * st);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kScanBatch; ++j) {
       if (j < cnt) {
         if (a.exclusive) *reinterpret_cast<f32x4*>(col + (p0 + j) * st) = run;
         run[0] = g * run[0] + t[j][0];
