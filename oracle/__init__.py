@@ -8,15 +8,18 @@ from .linattn_oracle import (  # noqa: F401
     EPS,
     FMAPS,
     attention,
+    attention_backward,
     attention_via_state,
     chunked,
     cumsum_form,
     decode_step,
     feature_dim,
     feature_map,
+    feature_map_vjp,
     final_state,
     phi_elu1,
     phi_identity,
     phi_performer,
     recurrent,
+    recurrent_backward,
 )

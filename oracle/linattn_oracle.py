@@ -341,3 +341,177 @@ def chunked(q, k, v, fmap="elu1", W=None, causal=True, normalize=True, chunk=64,
     lead = shape[:-2]
     return (y.reshape(shape[:-1] + (dv,)), S.reshape(lead + S.shape[1:]),
             z.reshape(lead + z.shape[1:]))
+
+
+# ---------------------------------------------------------------------------
+# Gradients. [LA] "Entrenamiento: forma paralela" says the parallel form
+# exists so that training (back-propagation) is fast; the pages print no
+# gradient formulas. The functions below are the vector-Jacobian products of
+# the definitions above, derived by hand: with the outputs' cotangents dY
+# (and optionally the final state's, dS_N and dz_N) they return the
+# gradients of L = <dY, Y> + <dS_N, S_N> + <dz_N, z_N> with respect to q, k,
+# v (and the initial state). They are pinned by central finite differences
+# of `attention` / `final_state` in tests/test_oracle_backward_pins.py.
+#
+# Derivative of the clamp: d max(den, EPS) / d den = 1 when den >= EPS,
+# else 0 (at the configurations tested den is far above EPS).
+# ---------------------------------------------------------------------------
+
+def feature_map_vjp(x, dphi, fmap="elu1", W=None):
+    """Gradient with respect to x of <dphi, phi(x)> (row-wise maps).
+
+    elu+1: phi'(x) = 1 for x > 0, exp(x) for x <= 0. identity: 1.
+    random features: phi_c = exp(u_c - |x~|^2/2)/sqrt(m), u = W x~, x~ = d^(-1/4) x,
+    so d phi_c / d x = d^(-1/4) phi_c (W_c - x~).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dphi = np.asarray(dphi, dtype=np.float64)
+    if fmap == "elu1":
+        return dphi * np.where(x > 0.0, 1.0, np.exp(np.minimum(x, 0.0)))
+    if fmap == "identity":
+        return dphi.copy()
+    if fmap == "performer":
+        W = np.asarray(W, dtype=np.float64)
+        d = x.shape[-1]
+        s = d ** -0.25
+        f = phi_performer(x, W)
+        t = dphi * f                                   # [..., m]
+        return s * (t @ W - (x * s) * t.sum(axis=-1, keepdims=True))
+    raise ValueError(f"unknown feature map {fmap!r}")
+
+
+def _cot_state(dS, dz, G, dfeat, dv):
+    dS = np.zeros((G, dfeat, dv)) if dS is None else np.asarray(dS, np.float64).reshape(G, dfeat, dv)
+    dz = np.zeros((G, dfeat)) if dz is None else np.asarray(dz, np.float64).reshape(G, dfeat)
+    return dS, dz
+
+
+def attention_backward(q, k, v, dy, fmap="elu1", W=None, causal=True, normalize=True,
+                       S0=None, z0=None, dS_N=None, dz_N=None, decay=None):
+    """Vector-Jacobian product of `attention` (and of `final_state` for the
+    seeds dS_N, dz_N), with the N x N similarity matrix formed explicitly.
+
+    Per head, with Qf = phi(Q), Kf = phi(K), the weights Gm (the causal mask,
+    times gamma^(i-j) with decay), s0_i the weight of the initial state
+    (gamma^(i+1) with decay, else 1) and w_j the weight of key j in the final
+    state (gamma^(N-1-j), else 1):
+      A = (Qf Kf^T) * Gm,  num = A V + s0 (Qf S0),  den = A 1 + s0 (Qf z0)
+      dnum = dY / max(den, EPS),  dden = -<dY, num> / max(den, EPS)^2  (normalized)
+      dnum = dY,                  dden = 0                             (not normalized)
+      dM   = (dnum V^T + dden 1^T) * Gm
+      dQf  = dM Kf + s0 (dnum S0^T + dden z0^T)
+      dKf  = dM^T Qf + w (V dS_N^T + 1 dz_N^T)
+      dV   = A^T dnum + w (Kf dS_N)
+      dS0  = Qf^T (s0 dnum) + gamma^N dS_N,   dz0 = Qf^T (s0 dden) + gamma^N dz_N
+    and dq, dk from dQf, dKf through the feature map.
+    Returns (dq, dk, dv, dS0, dz0) in float64, shaped like the inputs
+    (dS0 [..., d', d], dz0 [..., d']).
+    """
+    shape = np.asarray(q).shape
+    Q, K, V, dY = _bh(q), _bh(k), _bh(v), _bh(dy)
+    G, N, _ = Q.shape
+    dv = V.shape[-1]
+    Qf = feature_map(Q, fmap, W)
+    Kf = feature_map(K, fmap, W)
+    dfeat = Qf.shape[-1]
+    S, z = _state(S0, z0, G, dfeat, dv)
+    dSN, dzN = _cot_state(dS_N, dz_N, G, dfeat, dv)
+    gam = _gammas(decay, shape, G)
+    if gam is not None and not causal:
+        raise ValueError("decay is defined for the causal form only")
+    lag = np.arange(N)[:, None] - np.arange(N)[None, :]
+    dQf = np.empty_like(Qf)
+    dKf = np.empty_like(Kf)
+    dV = np.empty_like(V)
+    dS0 = np.empty_like(S)
+    dz0 = np.empty_like(z)
+    for g in range(G):
+        Gm = np.ones((N, N))
+        s0 = np.ones(N)
+        w = np.ones(N)
+        carry = 1.0
+        if causal:
+            Gm = np.where(lag >= 0, 1.0, 0.0)
+            if gam is not None:
+                Gm = Gm * gam[g] ** np.maximum(lag, 0)
+                s0 = gam[g] ** (np.arange(N) + 1.0)
+                w = gam[g] ** (N - 1.0 - np.arange(N))
+                carry = gam[g] ** N
+        A = (Qf[g] @ Kf[g].T) * Gm
+        num = A @ V[g] + s0[:, None] * (Qf[g] @ S[g])
+        den = A.sum(axis=1) + s0 * (Qf[g] @ z[g])
+        if normalize:
+            Dn = np.maximum(den, EPS)
+            dnum = dY[g] / Dn[:, None]
+            dden = np.where(den >= EPS, -np.sum(dY[g] * num, axis=1) / Dn ** 2, 0.0)
+        else:
+            dnum = dY[g]
+            dden = np.zeros(N)
+        dM = (dnum @ V[g].T + dden[:, None]) * Gm
+        dQf[g] = dM @ Kf[g] + s0[:, None] * (dnum @ S[g].T + dden[:, None] * z[g][None, :])
+        dKf[g] = dM.T @ Qf[g] + w[:, None] * (V[g] @ dSN[g].T + dzN[g][None, :])
+        dV[g] = A.T @ dnum + w[:, None] * (Kf[g] @ dSN[g])
+        dS0[g] = Qf[g].T @ (s0[:, None] * dnum) + carry * dSN[g]
+        dz0[g] = Qf[g].T @ (s0 * dden) + carry * dzN[g]
+    dq = feature_map_vjp(Q, dQf, fmap, W)
+    dk = feature_map_vjp(K, dKf, fmap, W)
+    lead = shape[:-2]
+    return (dq.reshape(shape), dk.reshape(shape), dV.reshape(lead + (N, dv)),
+            dS0.reshape(lead + (dfeat, dv)), dz0.reshape(lead + (dfeat,)))
+
+
+def recurrent_backward(q, k, v, dy, fmap="elu1", W=None, normalize=True,
+                       S0=None, z0=None, dS_N=None, dz_N=None, decay=None):
+    """Back-propagation through the recurrent form (causal), O(N d' d) per head.
+
+    Forward sweep: S_t = gamma S_{t-1} + phi(k_t) v_t^T (z alike), the output
+    cotangents dnum_t, dden_t as in `attention_backward`, and
+    d phi(q_t) = S_t dnum_t + z_t dden_t. Reverse sweep with the adjoint
+    states R = dL/dS_t, r = dL/dz_t, starting from (dS_N, dz_N):
+      R += phi(q_t) dnum_t^T, r += phi(q_t) dden_t,
+      d phi(k_t) = R v_t + r,  dv_t = R^T phi(k_t),
+      then R, r <- gamma R, gamma r (on to S_{t-1}); finally dS0 = R, dz0 = r.
+    Same return values as `attention_backward`.
+    """
+    shape = np.asarray(q).shape
+    Q, K, V, dY = _bh(q), _bh(k), _bh(v), _bh(dy)
+    G, N, _ = Q.shape
+    dv = V.shape[-1]
+    Qf = feature_map(Q, fmap, W)
+    Kf = feature_map(K, fmap, W)
+    dfeat = Qf.shape[-1]
+    S, z = _state(S0, z0, G, dfeat, dv)
+    R, r = _cot_state(dS_N, dz_N, G, dfeat, dv)
+    R, r = R.copy(), r.copy()
+    gam = _gammas(decay, shape, G)
+    gm = np.ones(G) if gam is None else gam
+    dQf = np.empty_like(Qf)
+    dnum = np.empty_like(dY)
+    dden = np.empty((G, N))
+    for t in range(N):
+        S = gm[:, None, None] * S + Kf[:, t, :, None] * V[:, t, None, :]
+        z = gm[:, None] * z + Kf[:, t]
+        num = np.einsum("gc,gce->ge", Qf[:, t], S)
+        den = np.einsum("gc,gc->g", Qf[:, t], z)
+        if normalize:
+            Dn = np.maximum(den, EPS)
+            dnum[:, t] = dY[:, t] / Dn[:, None]
+            dden[:, t] = np.where(den >= EPS, -np.sum(dY[:, t] * num, axis=1) / Dn ** 2, 0.0)
+        else:
+            dnum[:, t] = dY[:, t]
+            dden[:, t] = 0.0
+        dQf[:, t] = np.einsum("gce,ge->gc", S, dnum[:, t]) + z * dden[:, t][:, None]
+    dKf = np.empty_like(Kf)
+    dV = np.empty_like(V)
+    for t in range(N - 1, -1, -1):
+        R = R + Qf[:, t, :, None] * dnum[:, t, None, :]
+        r = r + Qf[:, t] * dden[:, t][:, None]
+        dKf[:, t] = np.einsum("gce,ge->gc", R, V[:, t]) + r
+        dV[:, t] = np.einsum("gce,gc->ge", R, Kf[:, t])
+        R = gm[:, None, None] * R
+        r = gm[:, None] * r
+    dq = feature_map_vjp(Q, dQf, fmap, W)
+    dk = feature_map_vjp(K, dKf, fmap, W)
+    lead = shape[:-2]
+    return (dq.reshape(shape), dk.reshape(shape), dV.reshape(lead + (N, dv)),
+            R.reshape(lead + (dfeat, dv)), r.reshape(lead + (dfeat,)))

@@ -2,8 +2,9 @@
 
 Each case plants one mistake (a dropped term, a wrong sign, an off-by-one
 index, a transposed operand, an exclusive instead of inclusive mask, ...) in
-a copy of the oracle package, runs tests/test_oracle_pins.py against that
-copy in a fresh interpreter, and requires the pins to fail. Two controls
+a copy of the oracle package, runs the pins (tests/test_oracle_pins.py, or
+tests/test_oracle_backward_pins.py for the gradients) against that copy in a
+fresh interpreter, and requires them to fail. Two controls
 check the harness itself: an unaltered copy passes, and a copy that cannot
 be imported fails.
 """
@@ -79,21 +80,63 @@ MUTANTS = [
      "decay: blockwise update weights off by one"),
 ]
 
+# mistakes in the gradients, caught by tests/test_oracle_backward_pins.py
+BACKWARD_MUTANTS = [
+    ("dden = np.where(den >= EPS, -np.sum(dY[g] * num, axis=1) / Dn ** 2, 0.0)",
+     "dden = np.where(den >= EPS, np.sum(dY[g] * num, axis=1) / Dn ** 2, 0.0)",
+     "backward: wrong sign of the denominator cotangent"),
+    ("dden = np.where(den >= EPS, -np.sum(dY[g] * num, axis=1) / Dn ** 2, 0.0)",
+     "dden = np.where(den >= EPS, -np.sum(dY[g] * num, axis=1) / Dn, 0.0)",
+     "backward: denominator cotangent divided by den once"),
+    ("dM = (dnum @ V[g].T + dden[:, None]) * Gm", "dM = (dnum @ V[g].T) * Gm",
+     "backward: denominator term dropped from the similarity cotangent"),
+    ("dM = (dnum @ V[g].T + dden[:, None]) * Gm", "dM = dnum @ V[g].T + dden[:, None]",
+     "backward: causal mask not applied to the similarity cotangent"),
+    ("dKf[g] = dM.T @ Qf[g]", "dKf[g] = dM @ Qf[g]", "backward: key gradient with untransposed cotangent"),
+    ("dV[g] = A.T @ dnum", "dV[g] = A @ dnum", "backward: value gradient with untransposed similarities"),
+    ("dQf[g] = dM @ Kf[g] + s0[:, None] * (dnum @ S[g].T + dden[:, None] * z[g][None, :])",
+     "dQf[g] = dM @ Kf[g] + s0[:, None] * (dnum @ S[g].T)",
+     "backward: initial normalizer dropped from the query gradient"),
+    ("dS0[g] = Qf[g].T @ (s0[:, None] * dnum) + carry * dSN[g]", "dS0[g] = Qf[g].T @ (s0[:, None] * dnum)",
+     "backward: final-state cotangent not passed to the initial state"),
+    ("dKf[g] = dM.T @ Qf[g] + w[:, None] * (V[g] @ dSN[g].T + dzN[g][None, :])",
+     "dKf[g] = dM.T @ Qf[g] + w[:, None] * (V[g] @ dSN[g] + dzN[g][None, :])",
+     "backward: final-state cotangent transposed in the key gradient"),
+    ("                w = gam[g] ** (N - 1.0 - np.arange(N))", "                w = gam[g] ** (N - np.arange(N))",
+     "backward: decay weights of the final state off by one"),
+    ("return dphi * np.where(x > 0.0, 1.0, np.exp(np.minimum(x, 0.0)))", "return dphi",
+     "backward: elu+1 derivative missing"),
+    ("return dphi * np.where(x > 0.0, 1.0, np.exp(np.minimum(x, 0.0)))",
+     "return dphi * np.where(x >= 0.0, 0.0, np.exp(np.minimum(x, 0.0))) + dphi * (x > 0.0)",
+     "backward: elu+1 derivative, branch point moved"),
+    ("return s * (t @ W - (x * s) * t.sum(axis=-1, keepdims=True))", "return s * (t @ W)",
+     "backward: random-feature norm term dropped"),
+    ("""        R = R + Qf[:, t, :, None] * dnum[:, t, None, :]
+        r = r + Qf[:, t] * dden[:, t][:, None]
+        dKf[:, t] = np.einsum("gce,ge->gc", R, V[:, t]) + r""",
+     """        dKf[:, t] = np.einsum("gce,ge->gc", R, V[:, t]) + r
+        R = R + Qf[:, t, :, None] * dnum[:, t, None, :]
+        r = r + Qf[:, t] * dden[:, t][:, None]""",
+     "recurrent backward: adjoint state exclusive of the current token"),
+    ("        R = gm[:, None, None] * R\n", "        R = R\n", "recurrent backward: adjoint state not decayed"),
+]
 
-def _run_pins(tmp_path, src, init=INIT):
+
+def _run_pins(tmp_path, src, init=INIT, pins="test_oracle_pins.py"):
     pkg = tmp_path / "oracle"
     pkg.mkdir()
     (pkg / "linattn_oracle.py").write_text(src)
     (pkg / "__init__.py").write_text(init)
     env = dict(os.environ, LA_ORACLE_UNDER_TEST=str(tmp_path), PYTHONDONTWRITEBYTECODE="1")
-    r = subprocess.run([sys.executable, "-m", "pytest", str(ROOT / "tests" / "test_oracle_pins.py"), "-x", "-q",
+    r = subprocess.run([sys.executable, "-m", "pytest", str(ROOT / "tests" / pins), "-x", "-q",
                         "-p", "no:cacheprovider"], env=env, cwd=str(ROOT), capture_output=True, text=True,
                        timeout=600)
     return r.returncode, r.stdout[-2000:]
 
 
-def test_control_unaltered_copy_passes(tmp_path):
-    rc, out = _run_pins(tmp_path, SRC)
+@pytest.mark.parametrize("pins", ["test_oracle_pins.py", "test_oracle_backward_pins.py"])
+def test_control_unaltered_copy_passes(tmp_path, pins):
+    rc, out = _run_pins(tmp_path, SRC, pins=pins)
     assert rc == 0, out
 
 
@@ -106,4 +149,11 @@ def test_control_copy_is_the_one_imported(tmp_path):
 def test_pins_catch_planted_mistake(tmp_path, old, new, what):
     assert SRC.count(old) >= 1, f"mutation site not found: {old!r}"
     rc, out = _run_pins(tmp_path, SRC.replace(old, new, 1))
+    assert rc != 0, f"the pins did not catch: {what}\n{out}"
+
+
+@pytest.mark.parametrize("old,new,what", BACKWARD_MUTANTS, ids=[m[2] for m in BACKWARD_MUTANTS])
+def test_backward_pins_catch_planted_mistake(tmp_path, old, new, what):
+    assert SRC.count(old) >= 1, f"mutation site not found: {old!r}"
+    rc, out = _run_pins(tmp_path, SRC.replace(old, new, 1), pins="test_oracle_backward_pins.py")
     assert rc != 0, f"the pins did not catch: {what}\n{out}"
