@@ -23,6 +23,7 @@ __all__ = [
     "la_feature_map", "lib", "library_path", "LinAttnError",
     "la_version", "la_status_string", "la_forward_workspace_size", "la_forward", "la_forward_ex",
     "la_decode_step", "la_feature_map_apply", "feature_dim", "la_forward_decay", "la_decode_step_decay",
+    "la_backward_workspace_size", "la_backward",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +69,10 @@ def _load():
     L.la_decode_step_decay.restype = i
     L.la_feature_map_apply.argtypes = [vp, vp, ctypes.c_longlong, i, fmp, i, i, vp]
     L.la_feature_map_apply.restype = i
+    L.la_backward_workspace_size.argtypes = [i, i, i, i, fmp]
+    L.la_backward_workspace_size.restype = sz
+    L.la_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, fmp, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.la_backward.restype = i
     return L
 
 
@@ -281,3 +286,36 @@ def la_feature_map_apply(x, *, feature_map="elu1", W=None, out_dtype=None, out=N
                                   _stream(stream))
     _check(st, "la_feature_map_apply")
     return out
+
+
+def la_backward_workspace_size(B, H, N, d, feature_map="elu1") -> int:
+    fm = _fmap(feature_map, None)
+    return int(lib.la_backward_workspace_size(B, H, N, d, ctypes.byref(fm)))
+
+
+def la_backward(q, k, v, dout, *, feature_map="elu1", normalize=True, S_in=None, z_in=None, dS_out=None,
+                dz_out=None, return_state_grad=False, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of causal la_forward: returns (dq, dk, dv), or (dq, dk, dv, dS_in, dz_in)."""
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, k, v, dout must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    fm = _fmap(feature_map, None)
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype or dout.dtype != q.dtype:
+        raise TypeError("q, k, v, dout must share one dtype")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    dS_in = dz_in = None
+    if return_state_grad:
+        dS_in = torch.empty((B, H, d, d), device=q.device, dtype=torch.float32)
+        dz_in = torch.empty((B, H, d), device=q.device, dtype=torch.float32)
+    need = int(lib.la_backward_workspace_size(B, H, N, d, ctypes.byref(fm)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d,
+                         ctypes.byref(fm), int(normalize), dt, _ptr(S_in), _ptr(z_in), _ptr(dS_out), _ptr(dz_out),
+                         _ptr(dS_in), _ptr(dz_in), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "la_backward")
+    return (dq, dk, dv, dS_in, dz_in) if return_state_grad else (dq, dk, dv)

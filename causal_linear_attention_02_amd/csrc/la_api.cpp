@@ -393,3 +393,178 @@ int la_feature_map_apply(const void* x, void* phi, long long rows, int d, const 
 }
 
 }  // extern "C"
+
+namespace {
+
+struct BwdPlan {
+  int nchunks = 0, P = 1, cps = 0;
+  size_t fwd_bytes = 0, rev_bytes = 0, row_bytes = 0, ws_bytes = 0;
+};
+
+BwdPlan make_bwd_plan(long long BH, int N, int d) {
+  BwdPlan p;
+  if (N == 0 || BH == 0) return p;
+  p.nchunks = (N + kChunk - 1) / kChunk;
+  split(p.nchunks, BH, p.P, p.cps);
+  const size_t state_bytes = (size_t)(d * d + d) * sizeof(float);
+  p.fwd_bytes = p.P > 1 ? align256((size_t)BH * p.P * state_bytes) : 0;
+  p.rev_bytes = align256((size_t)BH * (p.P + 1) * state_bytes);
+  p.row_bytes = align256((size_t)BH * N * 2 * sizeof(float));
+  p.ws_bytes = p.fwd_bytes + p.rev_bytes + p.row_bytes;
+  return p;
+}
+
+// Gradient requests support the maps applied inside the kernels (d' = d).
+int bwd_map(const la_feature_map* fm, int d) {
+  const int dfeat = feature_dim(fm, d);
+  if (dfeat < 0) return dfeat;
+  return fm->kind == LA_PERFORMER ? LA_ERR_UNSUPPORTED : LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t la_backward_workspace_size(int B, int H, int N, int d, const la_feature_map* feature_map) {
+  if (B < 0 || H < 0 || N < 0 || !d_supported(d) || bwd_map(feature_map, d) != LA_OK) return 0;
+  return make_bwd_plan((long long)B * H, N, d).ws_bytes;
+}
+
+int la_backward(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv, int B,
+                int H, int N, int d, const la_feature_map* feature_map, int normalize, int dtype, const float* S_in,
+                const float* z_in, const float* dS_out, const float* dz_out, float* dS_in, float* dz_in,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || H < 0 || N < 0) return LA_ERR_INVALID_ARG;
+  if (normalize != 0 && normalize != 1) return LA_ERR_INVALID_ARG;
+  if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
+  if ((S_in == nullptr) != (z_in == nullptr) || (dS_out == nullptr) != (dz_out == nullptr) ||
+      (dS_in == nullptr) != (dz_in == nullptr))
+    return LA_ERR_INVALID_ARG;
+  if (!d_supported(d)) return LA_ERR_UNSUPPORTED;
+  const int fs = bwd_map(feature_map, d);
+  if (fs != LA_OK) return fs;
+  const long long BH = (long long)B * H;
+  if (BH > (1LL << 31) - 1) return LA_ERR_UNSUPPORTED;
+  const long long esz = dtype == LA_BF16 ? 2 : 4;
+  const long long tb = BH * N * d * esz, sb = BH * d * d * 4, zb = BH * d * 4;
+  for (const void* p : {(const void*)S_in, (const void*)z_in, (const void*)dS_out, (const void*)dz_out,
+                        (const void*)dS_in, (const void*)dz_in})
+    if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
+  // written state gradients overlap nothing else
+  if (dS_in) {
+    const void* ro[] = {S_in, z_in, dS_out, dz_out};
+    const long long rb[] = {sb, zb, sb, zb};
+    if (overlaps(dS_in, sb, dz_in, zb)) return LA_ERR_INVALID_ARG;
+    for (int i = 0; i < 4; ++i)
+      if (overlaps(dS_in, sb, ro[i], rb[i]) || overlaps(dz_in, zb, ro[i], rb[i])) return LA_ERR_INVALID_ARG;
+  }
+  const BwdPlan p = make_bwd_plan(BH, N, d);
+  if (BH == 0 || N == 0) {
+    if (BH > 0 && dS_in)
+      return status_from_hip(la::copy_state_dispatch(dS_out, dz_out, dS_in, dz_in, sb / 4, zb / 4, stream));
+    return LA_OK;
+  }
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return LA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv))
+    return LA_ERR_INVALID_ARG;
+  {
+    const void* wr[] = {dq, dk, dv, dS_in, dz_in};
+    const long long wrb[] = {tb, tb, tb, sb, zb};
+    const void* all[] = {q, k, v, dout, S_in, z_in, dS_out, dz_out, dq, dk, dv, dS_in, dz_in};
+    const long long allb[] = {tb, tb, tb, tb, sb, zb, sb, zb, tb, tb, tb, sb, zb};
+    for (int i = 0; i < 5; ++i)
+      for (int j = 0; j < 13; ++j)
+        if (all[j] != wr[i] && overlaps(wr[i], wrb[i], all[j], allb[j])) return LA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < p.ws_bytes) return LA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LA_ERR_INVALID_ARG;
+    for (int j = 0; j < 13; ++j)
+      if (overlaps(workspace, (long long)p.ws_bytes, all[j], allb[j])) return LA_ERR_INVALID_ARG;
+  }
+  char* wsb = static_cast<char*>(workspace);
+  float* ws_fwd = reinterpret_cast<float*>(wsb);
+  float* ws_rev = reinterpret_cast<float*>(wsb + p.fwd_bytes);
+  float* rowstats = reinterpret_cast<float*>(wsb + p.fwd_bytes + p.rev_bytes);
+  const int state_elems = d * d + d;
+
+  // forward states entering each segment (as la_forward, causal)
+  la::FwdArgs fa{};
+  fa.q = q;
+  fa.k = k;
+  fa.v = v;
+  fa.BH = (int)BH;
+  fa.N = N;
+  fa.nchunks = p.nchunks;
+  fa.nseg = p.P;
+  fa.chunks_per_seg = p.cps;
+  fa.nseg_state = p.P - 1;
+  fa.chunks_per_seg_state = p.cps;
+  fa.run_state_pass = p.P > 1;
+  fa.run_scan = p.P > 1;
+  fa.ws = ws_fwd;
+  fa.ws_slots = p.P;
+  fa.state_elems = state_elems;
+  fa.S_in = S_in;
+  fa.z_in = z_in;
+  fa.normalize = normalize;
+  fa.H = H;
+  la::ScanArgs fsa{};
+  fsa.ws = ws_fwd;
+  fsa.ws_slots = p.P;
+  fsa.state_elems = state_elems;
+  fsa.BH = (int)BH;
+  fsa.P = p.P - 1;
+  fsa.DF = d;
+  fsa.D = d;
+  fsa.exclusive = 1;
+  fsa.write_total = 1;
+  fsa.S_in = S_in;
+  fsa.z_in = z_in;
+  fsa.H = H;
+  fsa.seg_len = 64 * p.cps;
+
+  la::BwdArgs b{};
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.dy = dout;
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.BH = (int)BH;
+  b.N = N;
+  b.nchunks = p.nchunks;
+  b.nseg = p.P;
+  b.chunks_per_seg = p.cps;
+  b.normalize = normalize;
+  b.ws_fwd = ws_fwd;
+  b.fwd_slots = p.P;
+  b.init_from_ws = p.P > 1;
+  b.S_in = S_in;
+  b.z_in = z_in;
+  b.ws_rev = ws_rev;
+  b.state_elems = state_elems;
+  b.rowstats = rowstats;
+
+  // suffix sums of the segments' gradient states, seeded with dS_out / dz_out
+  la::ScanArgs rs{};
+  rs.ws = ws_rev;
+  rs.ws_slots = p.P + 1;
+  rs.state_elems = state_elems;
+  rs.BH = (int)BH;
+  rs.P = p.P;
+  rs.DF = d;
+  rs.D = d;
+  rs.exclusive = 1;
+  rs.write_total = 1;
+  rs.S_in = dS_out;
+  rs.z_in = dz_out;
+  rs.S_out = dS_in;
+  rs.z_out = dz_in;
+  rs.H = H;
+  rs.seg_len = 64 * p.cps;
+  const int kfm = feature_map->kind == LA_ELU1 ? la::kElu1 : la::kIdentity;
+  return status_from_hip(la::backward_dispatch(fa, fsa, b, rs, d, kfm, dtype, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,671 @@
+// Gradients of causal chunked linear attention on gfx950.
+//
+// "Linear Attention" (marovi.ai), "Entrenamiento: forma paralela", motivates
+// the blockwise form by training; the pages print no gradient formulas.
+// Differentiating y_i = num_i / max(den_i, eps), num_i = sum_{j<=i}
+// (phi(q_i).phi(k_j)) v_j, den_i = sum_{j<=i} phi(q_i).phi(k_j) (plus an
+// initial state), with the output cotangents dY, gives per token
+//   D_i = max(den_i, eps),  g_i = dY_i / D_i,  h_i = -(dY_i . num_i) / D_i^2
+//   (h_i = 0 when den_i < eps; without normalization g = dY, h = 0)
+//   d phi(q_i) = sum_{j<=i} phi(k_j) (g_i.v_j + h_i)        [= S_i g_i + z_i h_i]
+//   d phi(k_j) = sum_{i>=j} phi(q_i) (g_i.v_j + h_i)        [= R_j v_j + r_j]
+//   dv_j       = sum_{i>=j} (phi(q_i).phi(k_j)) g_i        [= R_j^T phi(k_j)]
+// with the suffix states R_j = dS_N + sum_{i>=j} phi(q_i) g_i^T and
+// r_j = dz_N + sum_{i>=j} phi(q_i) h_i, and dq, dk through phi'
+// (elu+1: phi' = 1 for x > 0, exp(x) otherwise, i.e. min(phi(x), 1)).
+//
+// Passes (each (batch, head) sequence split into P segments of whole chunks,
+// as in the forward):
+//   forward state pass + carry scan : state (S, z) entering every segment
+//   dq pass      : per chunk, in order: scores, value products, numerator and
+//                  denominator terms -> D_i, h_i (kept per token), dq
+//   r-state pass : per segment, local sums of phi(q_i) g_i^T and phi(q_i) h_i
+//   carry scan   : suffix sums (slots in reverse segment order), seeded with
+//                  the final-state cotangents; the total is dS_in, dz_in
+//   dk/dv pass   : per chunk, in reverse order, from the segment's suffix state
+// Matrix products on the 32x32 MFMA shape (la_device.h): acc[m][n] +=
+// sum_k a[m][k] b[n][k], the a-fragment's lanes give the rows m and the
+// b-fragment's lanes the columns n of the accumulator.
+#include "la_device.h"
+#include "la_kernels.h"
+
+namespace la {
+namespace {
+
+template <int FM>
+__device__ __forceinline__ float bphi(float x) {
+  if constexpr (FM == kElu1) return phi_elu1(x);
+  else return x;
+}
+// phi'(x) from phi(x): elu+1 -> min(phi, 1); identity -> 1
+template <int FM>
+__device__ __forceinline__ float bdphi(float f) {
+  if constexpr (FM == kElu1) return fminf(f, 1.f);
+  else return 1.f;
+}
+
+template <typename IN, typename OP, int RB>
+__device__ __forceinline__ void put_raw(uint8_t* tile, int row, int col, const typename In8<IN>::raw& r) {
+  static_assert(sizeof(IN) == sizeof(OP), "raw staging needs matching element types");
+  if constexpr (sizeof(IN) == 2) {
+    *reinterpret_cast<u32x4*>(tile + tile_off<RB>(row, col * 2)) = r;
+  } else {
+    *reinterpret_cast<f32x4*>(tile + tile_off<RB>(row, col * 4)) = r.a;
+    *reinterpret_cast<f32x4*>(tile + tile_off<RB>(row, col * 4 + 16)) = r.b;
+  }
+}
+
+// four consecutive operand values of one tile row, as fp32
+template <typename OP, int RB>
+__device__ __forceinline__ void lds_read4(const uint8_t* tile, int row, int col, float* x) {
+  if constexpr (sizeof(OP) == 2) {
+    const u32x2 u = *reinterpret_cast<const u32x2*>(tile + tile_off<RB>(row, col * 2));
+    x[0] = __uint_as_float(u[0] << 16);
+    x[1] = __uint_as_float(u[0] & 0xffff0000u);
+    x[2] = __uint_as_float(u[1] << 16);
+    x[3] = __uint_as_float(u[1] & 0xffff0000u);
+  } else {
+    const f32x4 f = *reinterpret_cast<const f32x4*>(tile + tile_off<RB>(row, col * 4));
+    x[0] = f[0];
+    x[1] = f[1];
+    x[2] = f[2];
+    x[3] = f[3];
+  }
+}
+
+template <typename IN>
+__device__ __forceinline__ void store4(IN* p, float a, float b, float c, float d) {
+  if constexpr (sizeof(IN) == 2) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+  } else {
+    *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+  }
+}
+
+// operand fragment holding x[0..7] as its 8 contraction values (every lane)
+template <typename OP>
+__device__ __forceinline__ typename Ops<OP>::frag frag8(const float (&x)[8]) {
+  if constexpr (sizeof(OP) == 2) {
+    const u32x4 u = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                     pack_bf16x2(x[6], x[7])};
+    return __builtin_bit_cast(typename Ops<OP>::frag, u);
+  } else {
+    return typename Ops<OP>::frag{x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  }
+}
+
+// sum over the lanes of a wave that share lane % RL
+template <int RL>
+__device__ __forceinline__ float lane_colsum(float x) {
+#pragma unroll
+  for (int s = RL; s < 64; s <<= 1) x += __shfl_xor(x, s, 64);
+  return x;
+}
+
+// One chunk of q, k, v, dy as raw 16-byte pieces: 4*D threads, two pieces
+// per tile each, rows t/(D/8) and t/(D/8) + 32, columns 8 (t % (D/8)).
+// bf16 chunks are prefetched into registers during the previous chunk's
+// products; fp32 chunks (twice the registers) are loaded just before staging.
+template <typename IN>
+constexpr bool kPrefetch = sizeof(IN) == 2;
+
+template <int D, typename IN>
+struct Chunk4 {
+  typename In8<IN>::raw q[2], k[2], v[2], y[2];
+  f32x2 rs[2];  // per-token (1 / D_i, h_i) of the two rows (dk/dv pass)
+};
+
+template <int D, typename IN, bool RS>
+__device__ __forceinline__ void load_chunk4(Chunk4<D, IN>& ck, const BwdArgs& a, long long row0, int valid) {
+  constexpr int RL = D / 8;
+  const int t = threadIdx.x;
+  const unsigned bytes = (unsigned)(valid * D * (int)sizeof(IN));
+  const long long off = row0 * D;
+  const auto Rq = make_rsrc(static_cast<const IN*>(a.q) + off, bytes);
+  const auto Rk = make_rsrc(static_cast<const IN*>(a.k) + off, bytes);
+  const auto Rv = make_rsrc(static_cast<const IN*>(a.v) + off, bytes);
+  const auto Ry = make_rsrc(static_cast<const IN*>(a.dy) + off, bytes);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = t / RL + 32 * i;
+    const int o = (row * D + 8 * (t % RL)) * (int)sizeof(IN);
+    ck.q[i] = In8<IN>::bload(Rq, o);
+    ck.k[i] = In8<IN>::bload(Rk, o);
+    ck.v[i] = In8<IN>::bload(Rv, o);
+    ck.y[i] = In8<IN>::bload(Ry, o);
+    if constexpr (RS) {
+      ck.rs[i] = row < valid ? *reinterpret_cast<const f32x2*>(a.rowstats + 2 * (row0 + row)) : f32x2{0.f, 0.f};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dq pass. grid = (BH, P), block = 4*D threads: wave (ib, w) handles query
+// rows [32 ib, 32 ib + 32) of the chunk and features [32 w, 32 w + 32). Each
+// wave keeps S^T (rows = value dims, columns = its features) and z over its
+// features in fp32 accumulators; the two waves of one feature block hold
+// the same state.
+// ---------------------------------------------------------------------------
+template <int D, typename OP, typename IN, int FM>
+__global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
+  using Frag = typename Ops<OP>::frag;
+  constexpr int NW = D / 32;
+  constexpr int RB = D * Ops<OP>::kBytes;
+  constexpr int TB = 64 * RB;
+  constexpr int RL = D / 8;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TB];
+  __shared__ float red[2][NW][32][2];  // per row block and feature block: (phi(q).z, phi(q).(S dy)) partials
+  uint8_t* sQ = smem;
+  uint8_t* sK = smem + TB;
+  uint8_t* sV = smem + 2 * TB;
+  uint8_t* sY = smem + 3 * TB;
+
+  const int bh = blockIdx.x, seg = blockIdx.y;
+  const int c0 = seg * a.chunks_per_seg;
+  const int n = max(0, min(c0 + a.chunks_per_seg, a.nchunks) - c0);
+  const int t = threadIdx.x, wave = t >> 6, l = t & 63, h = l >> 5, li = l & 31;
+  const int ib = wave / NW, w = wave % NW;
+  const long long base = (long long)bh * a.N;
+  IN* dq = static_cast<IN*>(a.dq);
+
+  const float* Sp;
+  const float* zp;
+  if (a.init_from_ws) {
+    Sp = a.ws_fwd + ((long long)bh * a.fwd_slots + seg) * a.state_elems;
+    zp = Sp + D * D;
+  } else {
+    Sp = a.S_in ? a.S_in + (long long)bh * D * D : nullptr;
+    zp = a.z_in ? a.z_in + (long long)bh * D : nullptr;
+  }
+  f32x16 ST[NW], Z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int rr = 8 * (r >> 2) + 4 * h + (r & 3);
+#pragma unroll
+    for (int eb = 0; eb < NW; ++eb) ST[eb][r] = Sp ? Sp[(long long)(32 * w + li) * D + 32 * eb + rr] : 0.f;
+    Z[r] = zp ? zp[32 * w + rr] : 0.f;
+  }
+  Frag ones;
+  {
+    float o[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+    ones = frag8<OP>(o);
+  }
+
+  Chunk4<D, IN> ck;
+  if (kPrefetch<IN> && n > 0) load_chunk4<D, IN, false>(ck, a, base + 64LL * c0, min(64, a.N - 64 * c0));
+  for (int m = 0; m < n; ++m) {
+    const int c = c0 + m;
+    const int valid = min(64, a.N - 64 * c);
+    if (!kPrefetch<IN>) load_chunk4<D, IN, false>(ck, a, base + 64LL * c, valid);
+    // stage phi(Q), phi(K) (rows past the end: 0), V, dY
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = t / RL + 32 * i, col = 8 * (t % RL);
+      float x[8];
+      In8<IN>::to_f32(ck.q[i], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = bphi<FM>(x[e]);
+      Ops<OP>::template store8<RB>(sQ, row, col, x);
+      In8<IN>::to_f32(ck.k[i], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = row < valid ? bphi<FM>(x[e]) : 0.f;
+      Ops<OP>::template store8<RB>(sK, row, col, x);
+      put_raw<IN, OP, RB>(sV, row, col, ck.v[i]);
+      put_raw<IN, OP, RB>(sY, row, col, ck.y[i]);
+    }
+    __syncthreads();
+    if (kPrefetch<IN> && m + 1 < n) load_chunk4<D, IN, false>(ck, a, base + 64LL * (c + 1), min(64, a.N - 64 * (c + 1)));
+
+    // scores A[j][i] = phi(k_j).phi(q_i) and value products P[j][i] = v_j.dy_i
+    // for the wave's query rows i: the diagonal key block (d) and, for the
+    // second row block, the first key block (o)
+    // (each score tile is reduced into the row sums as soon as it is formed)
+    f32x16 Pd = {}, Po = {};
+    float den = 0.f, dyn = 0.f;
+    {
+      f32x16 Ad = {};
+#pragma unroll
+      for (int kb = 0; kb < D / 16; ++kb) {
+        Ops<OP>::mma(Ad, Ops<OP>::template load_rows<RB>(sK, 32 * ib, 16 * kb),
+                     Ops<OP>::template load_rows<RB>(sQ, 32 * ib, 16 * kb));
+        Ops<OP>::mma(Pd, Ops<OP>::template load_rows<RB>(sV, 32 * ib, 16 * kb),
+                     Ops<OP>::template load_rows<RB>(sY, 32 * ib, 16 * kb));
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool keep = 8 * (r >> 2) + 4 * h + (r & 3) <= li;
+        const float x = keep ? Ad[r] : 0.f;
+        den += x;
+        dyn += x * Pd[r];
+      }
+    }
+    if (ib) {
+      f32x16 Ao = {};
+#pragma unroll
+      for (int kb = 0; kb < D / 16; ++kb) {
+        Ops<OP>::mma(Ao, Ops<OP>::template load_rows<RB>(sK, 0, 16 * kb),
+                     Ops<OP>::template load_rows<RB>(sQ, 32 * ib, 16 * kb));
+        Ops<OP>::mma(Po, Ops<OP>::template load_rows<RB>(sV, 0, 16 * kb),
+                     Ops<OP>::template load_rows<RB>(sY, 32 * ib, 16 * kb));
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        den += Ao[r];
+        dyn += Ao[r] * Po[r];
+      }
+    }
+    // T[f][i] = sum_e S[f][e] dy_i[e] over the wave's features
+    f32x16 T = {};
+#pragma unroll
+    for (int eb = 0; eb < NW; ++eb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        Ops<OP>::mma(T, Ops<OP>::from_acc(ST[eb], kk),
+                     Ops<OP>::template load_rows<RB>(sY, 32 * ib, 32 * eb + 16 * kk));
+    // in-chunk parts (keys j <= i) of den_i and dy_i.num_i: both lane halves
+    den += xor32(den);
+    dyn += xor32(dyn);
+    // carried parts over the wave's features: phi(q_i).z and phi(q_i).T_i
+    const int irow = 32 * ib + li;
+    float fq[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) lds_read4<OP, RB>(sQ, irow, 32 * w + 8 * g + 4 * h, &fq[4 * g]);
+    float pden = 0.f, pdyn = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pden += fq[r] * Z[r];
+      pdyn += fq[r] * T[r];
+    }
+    pden += xor32(pden);
+    pdyn += xor32(pdyn);
+    if (h == 0) {
+      red[ib][w][li][0] = pden;
+      red[ib][w][li][1] = pdyn;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      den += red[ib][ww][li][0];
+      dyn += red[ib][ww][li][1];
+    }
+    float inv = 1.f, hh = 0.f;
+    if (a.normalize) {
+      const float Dn = fmaxf(den, kEps);
+      inv = 1.f / Dn;
+      hh = den >= kEps ? -dyn * inv * inv : 0.f;
+    }
+    // B[j][i] = g_i.v_j + h_i (keys j <= i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool keep = 8 * (r >> 2) + 4 * h + (r & 3) <= li;
+      Pd[r] = keep ? Pd[r] * inv + hh : 0.f;
+      Po[r] = Po[r] * inv + hh;
+    }
+    // d phi(q_i)[f] = T[f][i] / D_i + h_i z_f + sum_j phi(k_j)[f] B[j][i]
+#pragma unroll
+    for (int r = 0; r < 16; ++r) T[r] = T[r] * inv + hh * Z[r];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      Ops<OP>::mma(T, Ops<OP>::template load_cols<RB>(sK, 32 * ib + 16 * kk, 32 * w), Ops<OP>::from_acc(Pd, kk));
+    if (ib) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        Ops<OP>::mma(T, Ops<OP>::template load_cols<RB>(sK, 16 * kk, 32 * w), Ops<OP>::from_acc(Po, kk));
+    }
+    if (irow < valid) {
+      IN* o = dq + (base + 64LL * c + irow) * D + 32 * w + 4 * h;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4<IN>(o + 8 * g, T[4 * g] * bdphi<FM>(fq[4 * g]), T[4 * g + 1] * bdphi<FM>(fq[4 * g + 1]),
+                   T[4 * g + 2] * bdphi<FM>(fq[4 * g + 2]), T[4 * g + 3] * bdphi<FM>(fq[4 * g + 3]));
+      if (w == 0 && h == 0)
+        *reinterpret_cast<f32x2*>(a.rowstats + 2 * (base + 64LL * c + irow)) = f32x2{inv, hh};
+    }
+    // S^T += V^T phi(K), z += column sums of phi(K)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const Frag kf = Ops<OP>::template load_cols<RB>(sK, 16 * kb, 32 * w);
+#pragma unroll
+      for (int eb = 0; eb < NW; ++eb) Ops<OP>::mma(ST[eb], Ops<OP>::template load_cols<RB>(sV, 16 * kb, 32 * eb), kf);
+      Ops<OP>::mma(Z, kf, ones);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// r-state pass: per segment R_loc = sum_i phi(q_i) g_i^T, r_loc = sum_i
+// phi(q_i) h_i into ws_rev slot P-1-seg. grid = (BH, P), block = 2*D
+// threads; wave w keeps R[:, 32w:32w+32] (rows = features). Staging threads
+// hold pieces at rows t/(D/8) + 16 i, i = 0..3.
+// ---------------------------------------------------------------------------
+template <int D, typename OP, typename IN, int FM>
+__global__ __launch_bounds__(D * 2) void bwd_rstate_kernel(BwdArgs a) {
+  constexpr int NW = D / 32;
+  constexpr int RB = D * Ops<OP>::kBytes;
+  constexpr int TB = 64 * RB;
+  constexpr int RL = D / 8;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TB];
+  __shared__ float rsum[NW][D];
+  uint8_t* sQ = smem;
+  uint8_t* sG = smem + TB;
+
+  const int bh = blockIdx.x, seg = blockIdx.y;
+  const int c0 = seg * a.chunks_per_seg;
+  const int n = max(0, min(c0 + a.chunks_per_seg, a.nchunks) - c0);
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, h = l >> 5, li = l & 31;
+  const long long base = (long long)bh * a.N;
+  const IN* q = static_cast<const IN*>(a.q);
+  const IN* dy = static_cast<const IN*>(a.dy);
+
+  f32x16 R[NW];
+#pragma unroll
+  for (int fb = 0; fb < NW; ++fb) R[fb] = f32x16{};
+  float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int col = 8 * (t % RL);
+  for (int m = 0; m < n; ++m) {
+    const int c = c0 + m;
+    const int valid = min(64, a.N - 64 * c);
+    const unsigned bytes = (unsigned)(valid * D * (int)sizeof(IN));
+    const long long row0 = base + 64LL * c;
+    const auto Rq = make_rsrc(q + row0 * D, bytes);
+    const auto Ry = make_rsrc(dy + row0 * D, bytes);
+    typename In8<IN>::raw rq[4], ry[4];
+    f32x2 rs[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = t / RL + 16 * i;
+      const int o = (row * D + col) * (int)sizeof(IN);
+      rq[i] = In8<IN>::bload(Rq, o);
+      ry[i] = In8<IN>::bload(Ry, o);
+      rs[i] = row < valid ? *reinterpret_cast<const f32x2*>(a.rowstats + 2 * (row0 + row)) : f32x2{0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = t / RL + 16 * i;
+      float x[8];
+      In8<IN>::to_f32(rq[i], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = row < valid ? bphi<FM>(x[e]) : 0.f;
+        cs[e] += x[e] * rs[i][1];
+      }
+      Ops<OP>::template store8<RB>(sQ, row, col, x);
+      In8<IN>::to_f32(ry[i], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= rs[i][0];
+      Ops<OP>::template store8<RB>(sG, row, col, x);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const auto gf = Ops<OP>::template load_cols<RB>(sG, 16 * kb, 32 * w);
+#pragma unroll
+      for (int fb = 0; fb < NW; ++fb) Ops<OP>::mma(R[fb], Ops<OP>::template load_cols<RB>(sQ, 16 * kb, 32 * fb), gf);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) cs[e] = lane_colsum<RL>(cs[e]);
+  if (l < RL) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rsum[w][col + e] = cs[e];
+  }
+  __syncthreads();
+  float* st = a.ws_rev + ((long long)bh * (a.nseg + 1) + (a.nseg - 1 - seg)) * a.state_elems;
+#pragma unroll
+  for (int fb = 0; fb < NW; ++fb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[(long long)(32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)) * D + 32 * w + li] = R[fb][r];
+  for (int f = t; f < D; f += 2 * D) {
+    float s = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) s += rsum[ww][f];
+    st[D * D + f] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dk/dv pass. grid = (BH, P), block = 4*D threads, chunks of the segment in
+// reverse order, starting from the cotangent of the state leaving the
+// segment (ws_rev slot P-1-seg).
+//   waves 0..NW-1 (value block w): R[:, 32w:32w+32] (rows = features), the
+//     scores A[i][j] = phi(q_i).phi(k_j) of the chunk, dv for value dims
+//     [32w, 32w+32);
+//   waves NW..2NW-1 (feature block w): R^T[:, 32w:32w+32] (rows = value
+//     dims), r over the block's features, B[i][j] = g_i.v_j + h_i, dk for
+//     features [32w, 32w+32).
+// With bf16 operands B is formed as (dy_i.v_j) / D_i + h_i from the raw dY
+// tile: g_i.v_j and -h_i cancel where v_j is close to the output y_i, and a
+// product with g rounded to bf16 would leave that rounding in dk.
+// ---------------------------------------------------------------------------
+template <int D, typename OP, typename IN, int FM>
+__global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
+  using Frag = typename Ops<OP>::frag;
+  constexpr int NW = D / 32;
+  constexpr int RB = D * Ops<OP>::kBytes;
+  constexpr int TB = 64 * RB;
+  constexpr int RL = D / 8;
+  constexpr bool RAWY = sizeof(OP) == 2;  // separate raw dY tile for B
+  __shared__ __attribute__((aligned(16))) uint8_t smem[(RAWY ? 5 : 4) * TB];
+  __shared__ __attribute__((aligned(16))) float sH[64];
+  __shared__ __attribute__((aligned(16))) float sI[64];
+  uint8_t* sQ = smem;
+  uint8_t* sK = smem + TB;
+  uint8_t* sV = smem + 2 * TB;
+  uint8_t* sG = smem + 3 * TB;
+  uint8_t* sY = RAWY ? smem + 4 * TB : sG;
+
+  const int bh = blockIdx.x, seg = blockIdx.y;
+  const int c0 = seg * a.chunks_per_seg;
+  const int n = max(0, min(c0 + a.chunks_per_seg, a.nchunks) - c0);
+  const int t = threadIdx.x, wave = t >> 6, l = t & 63, h = l >> 5, li = l & 31;
+  const bool vgroup = wave < NW;
+  const int w = vgroup ? wave : wave - NW;
+  const long long base = (long long)bh * a.N;
+  IN* dk = static_cast<IN*>(a.dk);
+  IN* dv = static_cast<IN*>(a.dv);
+
+  const float* Rp = a.ws_rev + ((long long)bh * (a.nseg + 1) + (a.nseg - 1 - seg)) * a.state_elems;
+  f32x16 RS[NW], rK;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int rr = 8 * (r >> 2) + 4 * h + (r & 3);
+#pragma unroll
+    for (int b = 0; b < NW; ++b)
+      RS[b][r] = vgroup ? Rp[(long long)(32 * b + rr) * D + 32 * w + li] : Rp[(long long)(32 * w + li) * D + 32 * b + rr];
+    rK[r] = vgroup ? 0.f : Rp[D * D + 32 * w + rr];
+  }
+
+  Chunk4<D, IN> ck;
+  if (kPrefetch<IN> && n > 0)
+    load_chunk4<D, IN, true>(ck, a, base + 64LL * (c0 + n - 1), min(64, a.N - 64 * (c0 + n - 1)));
+  for (int m = n - 1; m >= 0; --m) {
+    const int c = c0 + m;
+    const int valid = min(64, a.N - 64 * c);
+    if (!kPrefetch<IN>) load_chunk4<D, IN, true>(ck, a, base + 64LL * c, valid);
+    // stage phi(Q), phi(K) (rows past the end: 0), V, G = dY / D_i, h
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = t / RL + 32 * i, col = 8 * (t % RL);
+      const bool live = row < valid;
+      float x[8];
+      In8<IN>::to_f32(ck.q[i], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = live ? bphi<FM>(x[e]) : 0.f;
+      Ops<OP>::template store8<RB>(sQ, row, col, x);
+      In8<IN>::to_f32(ck.k[i], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = live ? bphi<FM>(x[e]) : 0.f;
+      Ops<OP>::template store8<RB>(sK, row, col, x);
+      put_raw<IN, OP, RB>(sV, row, col, ck.v[i]);
+      In8<IN>::to_f32(ck.y[i], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= ck.rs[i][0];
+      Ops<OP>::template store8<RB>(sG, row, col, x);
+      if constexpr (RAWY) put_raw<IN, OP, RB>(sY, row, col, ck.y[i]);
+      if (col == 0) {
+        sH[row] = ck.rs[i][1];
+        sI[row] = RAWY ? ck.rs[i][0] : 1.f;
+      }
+    }
+    __syncthreads();
+    if (kPrefetch<IN> && m > 0) load_chunk4<D, IN, true>(ck, a, base + 64LL * (c - 1), min(64, a.N - 64 * (c - 1)));
+
+    if (vgroup) {
+      // dv_j[e] = sum_{i>=j} G[i][e] A[i][j] + sum_f R[f][e] phi(k_j)[f], with the
+      // scores A[i][j] of (query block, key block) (0,0), (1,0), (1,1), j <= i,
+      // formed one tile at a time
+      f32x16 V0 = {}, V1 = {};
+#pragma unroll
+      for (int tI = 0; tI < 3; ++tI) {
+        const int qb = tI == 0 ? 0 : 1, kbk = tI == 2 ? 1 : 0;
+        f32x16 A = {};
+#pragma unroll
+        for (int kb = 0; kb < D / 16; ++kb)
+          Ops<OP>::mma(A, Ops<OP>::template load_rows<RB>(sQ, 32 * qb, 16 * kb),
+                       Ops<OP>::template load_rows<RB>(sK, 32 * kbk, 16 * kb));
+        if (qb == kbk) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) A[r] = li <= 8 * (r >> 2) + 4 * h + (r & 3) ? A[r] : 0.f;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          Ops<OP>::mma(kbk ? V1 : V0, Ops<OP>::template load_cols<RB>(sG, 32 * qb + 16 * kk, 32 * w),
+                       Ops<OP>::from_acc(A, kk));
+      }
+#pragma unroll
+      for (int fb = 0; fb < NW; ++fb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const Frag rf = Ops<OP>::from_acc(RS[fb], kk);
+          Ops<OP>::mma(V0, rf, Ops<OP>::template load_rows<RB>(sK, 0, 32 * fb + 16 * kk));
+          Ops<OP>::mma(V1, rf, Ops<OP>::template load_rows<RB>(sK, 32, 32 * fb + 16 * kk));
+        }
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const f32x16& Vt = jb ? V1 : V0;
+        const int j = 32 * jb + li;
+        if (j < valid) {
+          IN* o = dv + (base + 64LL * c + j) * D + 32 * w + 4 * h;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) store4<IN>(o + 8 * g, Vt[4 * g], Vt[4 * g + 1], Vt[4 * g + 2], Vt[4 * g + 3]);
+        }
+      }
+      // R += phi(Q)^T G over the chunk
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const Frag gf = Ops<OP>::template load_cols<RB>(sG, 16 * kb, 32 * w);
+#pragma unroll
+        for (int fb = 0; fb < NW; ++fb) Ops<OP>::mma(RS[fb], Ops<OP>::template load_cols<RB>(sQ, 16 * kb, 32 * fb), gf);
+      }
+    } else {
+      // d phi(k_j)[f] = sum_{i>=j} phi(q_i)[f] B[i][j] + sum_e R[f][e] v_j[e] + r_f,
+      // with B[i][j] = g_i.v_j + h_i of (query block, key block) (0,0), (1,0),
+      // (1,1), j <= i, formed one tile at a time
+      f32x16 K0 = rK, K1 = rK;
+#pragma unroll
+      for (int tI = 0; tI < 3; ++tI) {
+        const int qb = tI == 0 ? 0 : 1, kbk = tI == 2 ? 1 : 0;
+        f32x16 Bt = {};
+#pragma unroll
+        for (int kb = 0; kb < D / 16; ++kb)
+          Ops<OP>::mma(Bt, Ops<OP>::template load_rows<RB>(sY, 32 * qb, 16 * kb),
+                       Ops<OP>::template load_rows<RB>(sV, 32 * kbk, 16 * kb));
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 hq = *reinterpret_cast<const f32x4*>(sH + 32 * qb + 8 * g + 4 * h);
+          const f32x4 iq = *reinterpret_cast<const f32x4*>(sI + 32 * qb + 8 * g + 4 * h);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool keep = qb != kbk || li <= 8 * g + 4 * h + e;
+            Bt[4 * g + e] = keep ? Bt[4 * g + e] * iq[e] + hq[e] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          Ops<OP>::mma(kbk ? K1 : K0, Ops<OP>::template load_cols<RB>(sQ, 32 * qb + 16 * kk, 32 * w),
+                       Ops<OP>::from_acc(Bt, kk));
+      }
+#pragma unroll
+      for (int eb = 0; eb < NW; ++eb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const Frag rf = Ops<OP>::from_acc(RS[eb], kk);
+          Ops<OP>::mma(K0, rf, Ops<OP>::template load_rows<RB>(sV, 0, 32 * eb + 16 * kk));
+          Ops<OP>::mma(K1, rf, Ops<OP>::template load_rows<RB>(sV, 32, 32 * eb + 16 * kk));
+        }
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const f32x16& Kt = jb ? K1 : K0;
+        const int j = 32 * jb + li;
+        if (j < valid) {
+          IN* o = dk + (base + 64LL * c + j) * D + 32 * w + 4 * h;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float fk[4];
+            lds_read4<OP, RB>(sK, j, 32 * w + 8 * g + 4 * h, fk);
+            store4<IN>(o + 8 * g, Kt[4 * g] * bdphi<FM>(fk[0]), Kt[4 * g + 1] * bdphi<FM>(fk[1]),
+                       Kt[4 * g + 2] * bdphi<FM>(fk[2]), Kt[4 * g + 3] * bdphi<FM>(fk[3]));
+          }
+        }
+      }
+      // R^T += G^T phi(Q), r += phi(Q)^T h over the chunk
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const Frag qf = Ops<OP>::template load_cols<RB>(sQ, 16 * kb, 32 * w);
+#pragma unroll
+        for (int eb = 0; eb < NW; ++eb) Ops<OP>::mma(RS[eb], Ops<OP>::template load_cols<RB>(sG, 16 * kb, 32 * eb), qf);
+        const f32x4 ha = *reinterpret_cast<const f32x4*>(sH + 16 * kb + 8 * h);
+        const f32x4 hb = *reinterpret_cast<const f32x4*>(sH + 16 * kb + 8 * h + 4);
+        const float hv[8] = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
+        Ops<OP>::mma(rK, qf, frag8<OP>(hv));
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int D, typename T, int FM>
+hipError_t launch_backward(const FwdArgs& fa, const ScanArgs& fs, const BwdArgs& b, const ScanArgs& rs, int dtype,
+                           hipStream_t st) {
+  if (fa.run_state_pass || fa.run_scan) {
+    FwdArgs f = fa;
+    f.skip_output = 1;
+    const hipError_t e = prefill_dispatch(f, fs, D, D, FM, dtype, true, false, st, nullptr);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((bwd_dq_kernel<D, T, T, FM>), dim3(b.BH, b.nseg), dim3(4 * D), 0, st, b);
+  hipLaunchKernelGGL((bwd_rstate_kernel<D, T, T, FM>), dim3(b.BH, b.nseg), dim3(2 * D), 0, st, b);
+  const hipError_t e = scan_dispatch(rs, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, T, T, FM>), dim3(b.BH, b.nseg), dim3(4 * D), 0, st, b);
+  return hipGetLastError();
+}
+
+template <typename T, int FM>
+hipError_t backward_d(const FwdArgs& fa, const ScanArgs& fs, const BwdArgs& b, const ScanArgs& rs, int D, int dtype,
+                      hipStream_t st) {
+  switch (D) {
+    case 32: return launch_backward<32, T, FM>(fa, fs, b, rs, dtype, st);
+    case 64: return launch_backward<64, T, FM>(fa, fs, b, rs, dtype, st);
+    case 128: return launch_backward<128, T, FM>(fa, fs, b, rs, dtype, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t backward_dispatch(const FwdArgs& fa, const ScanArgs& fs, const BwdArgs& b, const ScanArgs& rs, int D,
+                             int fmap, int dtype, hipStream_t st) {
+  if (dtype == 1) {
+    if (fmap == kElu1) return backward_d<__bf16, kElu1>(fa, fs, b, rs, D, dtype, st);
+    if (fmap == kIdentity) return backward_d<__bf16, kIdentity>(fa, fs, b, rs, D, dtype, st);
+  } else {
+    if (fmap == kElu1) return backward_d<float, kElu1>(fa, fs, b, rs, D, dtype, st);
+    if (fmap == kIdentity) return backward_d<float, kIdentity>(fa, fs, b, rs, D, dtype, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace la

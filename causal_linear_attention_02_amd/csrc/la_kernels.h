@@ -40,6 +40,7 @@ struct FwdArgs {
   const float* W;          // random-feature projection [DF][D] (fp32) or null
   const float* gamma;      // decay per head [H] (causal only) or null
   int H;                   // heads (gamma index = bh % H)
+  int skip_output;         // run the state pass and scan only (segment prefixes for the gradient passes)
 };
 
 struct ScanArgs {
@@ -74,6 +75,31 @@ struct DecodeArgs {
   int H;
 };
 
+// Gradient passes (causal; d' = d). Workspace regions: the forward segment
+// prefixes (as FwdArgs::ws), the reverse ("suffix") states and two floats per
+// token (1 / max(den, eps) and the denominator cotangent).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dy;          // output cotangent [BH][N][D]
+  void* dq;
+  void* dk;
+  void* dv;
+  int BH, N, nchunks;
+  int nseg, chunks_per_seg;
+  int normalize;
+  const float* ws_fwd;     // [BH][fwd_slots][state_elems]: state entering segment s (slot s)
+  int fwd_slots;
+  int init_from_ws;        // else S_in / z_in (or zero) enter the single segment
+  const float* S_in;
+  const float* z_in;
+  float* ws_rev;           // [BH][nseg + 1][state_elems]: slot nseg-1-s holds segment s's sums, then
+                           // (after the scan) the cotangent of the state leaving segment s
+  int state_elems;         // D * D + D
+  float* rowstats;         // [BH][N][2]: 1 / max(den, eps), d loss / d den
+};
+
 struct FmapArgs {
   const void* x;    // [rows][D]
   void* phi;        // [rows][DF]
@@ -83,6 +109,9 @@ struct FmapArgs {
 
 hipError_t prefill_dispatch(const FwdArgs& a, const ScanArgs& s, int D, int DF, int fmap, int dtype, bool causal,
                             bool decay, hipStream_t st, hipEvent_t* ev);
+hipError_t scan_dispatch(const ScanArgs& s, hipStream_t st);
+hipError_t backward_dispatch(const FwdArgs& fa, const ScanArgs& fs, const BwdArgs& b, const ScanArgs& rs, int D,
+                             int fmap, int dtype, hipStream_t st);
 hipError_t decode_dispatch(const DecodeArgs& a, int D, int DF, int fmap, int dtype, hipStream_t st);
 hipError_t fmap_dispatch(const FmapArgs& a, int D, int DF, int fmap, int in_dtype, int out_dtype, hipStream_t st);
 hipError_t copy_state_dispatch(const float* S_in, const float* z_in, float* S_out, float* z_out, long long nS,

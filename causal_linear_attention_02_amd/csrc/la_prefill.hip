@@ -923,6 +923,7 @@ static hipError_t launch_prefill_t(const FwdArgs& a, const ScanArgs& s, bool cau
     hipLaunchKernelGGL(carry_scan_kernel, dim3(s.BH, (s.state_elems / 4 + 255) / 256), dim3(256), 0, st, s);
   }
   if (ev) (void)hipEventRecord(ev[2], st);
+  if (a.skip_output) return hipGetLastError();
   if (causal) {
     hipLaunchKernelGGL((output_pass_kernel<D, DF, OP, IN, FM, true, DECAY>), dim3(a.BH, a.nseg), dim3(D * 4), 0, st,
                        a);
@@ -961,6 +962,11 @@ static hipError_t prefill_typed(const FwdArgs& a, const ScanArgs& s, int D, int 
   LA_PRE_CASE(128, 64) LA_PRE_CASE(128, 128)
 #undef LA_PRE_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t scan_dispatch(const ScanArgs& s, hipStream_t st) {
+  hipLaunchKernelGGL(carry_scan_kernel, dim3(s.BH, (s.state_elems / 4 + 255) / 256), dim3(256), 0, st, s);
+  return hipGetLastError();
 }
 
 hipError_t prefill_dispatch(const FwdArgs& a, const ScanArgs& s, int D, int DF, int fmap, int dtype, bool causal,

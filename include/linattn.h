@@ -170,6 +170,39 @@ int la_decode_step_decay(float* S, float* z, const void* q, const void* k, const
 int la_feature_map_apply(const void* x, void* phi, long long rows, int d, const la_feature_map* feature_map,
                          int in_dtype, int out_dtype, hipStream_t stream);
 
+/*
+ * Bytes of device workspace that la_backward needs (0 for invalid
+ * arguments): the forward states entering each sequence segment, the
+ * gradient states leaving each segment and two fp32 values per token.
+ */
+size_t la_backward_workspace_size(int B, int H, int N, int d, const la_feature_map* feature_map);
+
+/*
+ * Gradients of causal la_forward ("Entrenamiento: forma paralela" trains
+ * through the blockwise form; the pages give no gradient formulas, so these
+ * are the exact derivatives of the causal definition, up to rounding).
+ * With L = <dout, out> + <dS_out, S_out> + <dz_out, z_out> for the outputs
+ * of la_forward(q, k, v, causal = 1, normalize, S_in, z_in):
+ *   dq, dk, dv out: dL/dq, dL/dk, dL/dv, [B][H][N][d], element type `dtype`;
+ *             each must overlap no other buffer of the call.
+ *   dout      in:  [B][H][N][d], element type `dtype`.
+ *   S_in,z_in optional in (both or neither): the forward's initial state.
+ *   dS_out,dz_out optional in (both or neither): cotangents of the final
+ *             state (zero when absent).
+ *   dS_in,dz_in optional out (both or neither): dL/dS_in, dL/dz_in
+ *             ([B][H][d][d], [B][H][d] fp32; defined also without S_in).
+ *   workspace at least la_backward_workspace_size() bytes, 256-byte aligned.
+ * The forward is recomputed (no saved activations). Where max(den, 1e-6)
+ * clamps, its derivative is taken as 0 (den < 1e-6) or 1 (den >= 1e-6).
+ * Supported: elu+1 and the identity map, d in {32, 64, 128}; random
+ * features and decay return LA_ERR_UNSUPPORTED. N = 0 writes only
+ * dS_in/dz_in (= dS_out/dz_out, or zeros).
+ */
+int la_backward(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv, int B,
+                int H, int N, int d, const la_feature_map* feature_map, int normalize, int dtype, const float* S_in,
+                const float* z_in, const float* dS_out, const float* dz_out, float* dS_in, float* dz_in,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

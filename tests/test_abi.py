@@ -155,3 +155,50 @@ def test_decay_entry_points_validate_before_launch():
     st = lib.la_decode_step_decay(FAKE, FAKE2, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000,
                                   1, 2, 64, ctypes.byref(ident), None, 1, la.LA_BF16, None)
     assert st == la.LA_ERR_INVALID_ARG
+
+
+def _bwd(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, dout=FAKE + 0x3000000, dq=FAKE2, dk=FAKE2 + 0x1000000,
+         dv=FAKE2 + 0x2000000, B=1, H=1, N=128, d=64, fm=ELU, normalize=1, dtype=la.LA_BF16, S_in=None, z_in=None,
+         dS_out=None, dz_out=None, dS_in=None, dz_in=None, ws=FAKE2 * 4, ws_bytes=1 << 30):
+    return lib.la_backward(q, k, v, dout, dq, dk, dv, B, H, N, d, ctypes.byref(fm) if fm is not None else None,
+                           normalize, dtype, S_in, z_in, dS_out, dz_out, dS_in, dz_in, ws, ws_bytes, None)
+
+
+def test_backward_rejects_bad_arguments():
+    assert _bwd(B=-1) == la.LA_ERR_INVALID_ARG
+    assert _bwd(normalize=2) == la.LA_ERR_INVALID_ARG
+    assert _bwd(dtype=3) == la.LA_ERR_INVALID_ARG
+    assert _bwd(fm=None) == la.LA_ERR_INVALID_ARG
+    assert _bwd(d=48) == la.LA_ERR_UNSUPPORTED
+    W = FAKE2 * 8
+    assert _bwd(fm=la_feature_map(la.LA_PERFORMER, 64, W)) == la.LA_ERR_UNSUPPORTED  # no random-feature gradients
+    assert _bwd(dq=None) == la.LA_ERR_INVALID_ARG
+    assert _bwd(dout=FAKE + 0x3000000 + 8) == la.LA_ERR_INVALID_ARG           # misaligned
+    assert _bwd(dq=FAKE + 0x100) == la.LA_ERR_INVALID_ARG                      # dq overlaps q
+    assert _bwd(dk=FAKE2 + 0x100) == la.LA_ERR_INVALID_ARG                     # dk overlaps dq
+    assert _bwd(S_in=FAKE2 * 6) == la.LA_ERR_INVALID_ARG                       # S_in without z_in
+    assert _bwd(dS_out=FAKE2 * 6) == la.LA_ERR_INVALID_ARG                     # dS_out without dz_out
+    assert _bwd(dS_in=FAKE2 * 6) == la.LA_ERR_INVALID_ARG                      # dS_in without dz_in
+    # dS_in overlapping dS_out
+    assert _bwd(dS_out=FAKE2 * 6, dz_out=FAKE2 * 7, dS_in=FAKE2 * 6 + 256, dz_in=FAKE2 * 7 + 0x100000) \
+        == la.LA_ERR_INVALID_ARG
+    need = lib.la_backward_workspace_size(1, 1, 128, 64, ctypes.byref(ELU))
+    assert need > 0
+    assert _bwd(ws=None) == la.LA_ERR_WORKSPACE
+    assert _bwd(ws_bytes=need - 1) == la.LA_ERR_WORKSPACE
+    assert _bwd(ws=FAKE2 * 4 + 16) == la.LA_ERR_INVALID_ARG                    # not 256-aligned
+    assert _bwd(ws=FAKE2, ws_bytes=need) == la.LA_ERR_INVALID_ARG              # workspace overlaps dq
+    assert _bwd(B=0) == la.LA_OK and _bwd(N=0) == la.LA_OK                     # nothing to do
+
+
+def test_backward_workspace_plan():
+    ident = la_feature_map(la.LA_IDENTITY, 0, None)
+    for d in (32, 64, 128):
+        for N in (1, 64, 1000, 65536):
+            a = lib.la_backward_workspace_size(2, 3, N, d, ctypes.byref(ELU))
+            b = lib.la_backward_workspace_size(2, 3, N, d, ctypes.byref(ident))
+            # at least the per-token statistics and one gradient state per sequence
+            assert a == b >= 2 * 3 * (N * 8 + 2 * (d * d + d) * 4)
+    assert lib.la_backward_workspace_size(1, 1, 0, 64, ctypes.byref(ELU)) == 0
+    assert lib.la_backward_workspace_size(1, 1, 64, 48, ctypes.byref(ELU)) == 0
+    assert lib.la_backward_workspace_size(1, 1, 64, 64, ctypes.byref(la_feature_map(la.LA_PERFORMER, 64, FAKE))) == 0
