@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=1000)
     p.add_argument("--decode-warmup", type=int, default=20)
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--backward-steps", type=int, default=20)
+    p.add_argument("--no-backward", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="time budget of the oracle's prefill sample (whole heads; the decode sample gets half)")
@@ -162,6 +164,42 @@ def main():
     flops_useful = head_tokens * (4 * d * d + (C + 1) * 2 * d)  # chunked form, masked triangle
     log(f"prefill: {ms_step*1e3:.1f} us/step (state {ms_state*1e3:.1f}, scan {ms_scan*1e3:.1f}, "
         f"output {ms_out*1e3:.1f} us); output pass {out_gbs:.0f} GB/s")
+
+    # ---------------- gradients (la_backward) on the same workload ----------------
+    backward = None
+    if not args.no_backward:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(W["seed"] + 7919)
+        tdy = torch.randn((B, H, N, d), generator=gen, device=dev).to(torch.bfloat16)
+        gq, gk, gv = torch.empty_like(tq), torch.empty_like(tq), torch.empty_like(tq)
+        bws = torch.empty(la.la_backward_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
+
+        def bwd():
+            la.la_backward(tq, tk, tv, tdy, normalize=True, dq=gq, dk=gk, dv=gv, workspace=bws)
+
+        for _ in range(10):
+            bwd()
+        torch.cuda.synchronize()
+        log(f"backward: timing {args.backward_steps} calls")
+        t0 = time.perf_counter()
+        for _ in range(args.backward_steps):
+            bwd()
+        torch.cuda.synchronize()
+        bwall = (time.perf_counter() - t0) / args.backward_steps
+        # least traffic any gradient pass needs: q, k, v, dout read and dq, dk, dv written once
+        min_bytes = head_tokens * 7 * d * 2
+        backward = {
+            "metric": "causal linear-attn gradients (dq, dk, dv) head-tokens/s",
+            "value": head_tokens / bwall, "unit": "head-tokens/s", "us_per_call": round(bwall * 1e6, 1),
+            "steps": args.backward_steps, "forward_us_per_call": round(ms_step * 1e3, 1),
+            "config": {"workload": "prefill_b1h16n65536d128", "batch": B, "heads": H, "seq_len": N, "d": d,
+                       "feature_map": "elu1", "normalize": True, "dout": "N(0,1) bf16, seeded"},
+            "min_traffic": {"bytes": min_bytes, "achieved_gbs": round(min_bytes / bwall / 1e9, 1),
+                            "frac_hbm": round(min_bytes / bwall / 1e9 / HBM_PEAK_GBS, 4),
+                            "note": "q, k, v, dout read once and dq, dk, dv written once, bf16"},
+        }
+        log(f"backward: {bwall*1e6:.1f} us/call ({bwall*1e3/ms_step:.2f}x the forward)")
+        del tdy, gq, gk, gv, bws
 
     del tq, tk, tv, out, ws
     torch.cuda.empty_cache()
@@ -313,6 +351,7 @@ def main():
                                                      4),
                              "head_tokens_per_s": head_tokens / (ms_step * 1e-3)},
         "decode": decode,
+        "backward": backward,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result))

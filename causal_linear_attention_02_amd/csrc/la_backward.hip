@@ -94,6 +94,27 @@ __device__ __forceinline__ typename Ops<OP>::frag frag8(const float (&x)[8]) {
   }
 }
 
+// An accumulator block as two bf16 fragments hi + lo (x = hi + lo to within
+// 2^-16 |x|): for products whose result is a small difference of large
+// terms. Same lane layout as Ops<__bf16>::from_acc.
+__device__ __forceinline__ void frag_hilo(const f32x16& c, int kb, bf16x8& hi, bf16x8& lo) {
+  uint32_t ph[4], pl[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x0 = c[8 * kb + 2 * i], x1 = c[8 * kb + 2 * i + 1];
+    ph[i] = pack_bf16x2(x0, x1);
+    pl[i] = pack_bf16x2(x0 - __uint_as_float(ph[i] << 16), x1 - __uint_as_float(ph[i] & 0xffff0000u));
+  }
+  // elements 0-3 of the block are rows 0-3 (this half) and 4-7 rows 8-11 of
+  // the group of 16; the swap completes 8 contiguous rows per lane half
+  auto h0 = __builtin_amdgcn_permlane32_swap(ph[0], ph[2], false, false);
+  auto h1 = __builtin_amdgcn_permlane32_swap(ph[1], ph[3], false, false);
+  auto l0 = __builtin_amdgcn_permlane32_swap(pl[0], pl[2], false, false);
+  auto l1 = __builtin_amdgcn_permlane32_swap(pl[1], pl[3], false, false);
+  hi = __builtin_bit_cast(bf16x8, u32x4{h0[0], h1[0], h0[1], h1[1]});
+  lo = __builtin_bit_cast(bf16x8, u32x4{l0[0], l1[0], l0[1], l1[1]});
+}
+
 // sum over the lanes of a wave that share lane % RL
 template <int RL>
 __device__ __forceinline__ float lane_colsum(float x) {
@@ -104,10 +125,11 @@ __device__ __forceinline__ float lane_colsum(float x) {
 
 // One chunk of q, k, v, dy as raw 16-byte pieces: 4*D threads, two pieces
 // per tile each, rows t/(D/8) and t/(D/8) + 32, columns 8 (t % (D/8)).
-// bf16 chunks are prefetched into registers during the previous chunk's
-// products; fp32 chunks (twice the registers) are loaded just before staging.
+// bf16 chunks go straight from HBM into LDS while the previous chunk's
+// products run (below); fp32 chunks are loaded into registers just before
+// staging (two sets of fp32 tiles do not fit in LDS at d = 128).
 template <typename IN>
-constexpr bool kPrefetch = sizeof(IN) == 2;
+constexpr bool kDma = sizeof(IN) == 2;
 
 template <int D, typename IN>
 struct Chunk4 {
@@ -139,12 +161,77 @@ __device__ __forceinline__ void load_chunk4(Chunk4<D, IN>& ck, const BwdArgs& a,
   }
 }
 
+// A bf16 tile of a 64-token chunk loaded straight into LDS, no registers
+// involved: 4*D threads = D/16 waves, two 1 KB blocks of the swizzled tile
+// per wave. The hardware puts lane l's 16 bytes of block b at LDS bytes
+// 1024 b + 16 l, so that lane fetches the 16-byte unit of the global row that
+// the swizzle maps to that place. Rows past the descriptor's range (the end
+// of the sequence) arrive as zeros.
+template <int D>
+__device__ __forceinline__ int dma_off(int i) {
+  return (2 * (threadIdx.x >> 6) + i) * 1024 + 16 * (threadIdx.x & 63);
+}
+//
+// The transfer is written as inline assembly: the compiler cannot tell which
+// LDS bytes a transfer writes, and for the builtin form it waits for every
+// outstanding transfer before the next LDS read, which would serialize the
+// load of chunk m+1 with the products of chunk m. Here the kernels order the
+// transfers themselves: a full vector-memory wait and a barrier before any
+// wave reads the set they filled.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds_wave_base, int voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)lds_wave_base));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" : : "s"(m0), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+template <int D>
+__device__ __forceinline__ void dma_tile(uint8_t* tile, __amdgpu_buffer_rsrc_t r) {
+  constexpr int RB = 2 * D;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int o = dma_off<D>(i);
+    const int row = o / RB;
+    const int u = ((o % RB) >> 4) ^ swz<RB>(row);
+    dma16(r, tile + (o & ~1023), row * RB + 16 * u);
+  }
+}
+
+// elementwise phi (rows at or past `valid`: 0 when MASK) on 8 bf16 values in place
+template <int FM, bool MASK>
+__device__ __forceinline__ u32x4 phi_bf16x8(u32x4 r, bool live) {
+  float x[8];
+  In8<__bf16>::to_f32(r, x);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (!MASK || live) ? bphi<FM>(x[e]) : 0.f;
+  return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+}
+
+// phi of 8 bf16 values as hi + lo bf16 (rows at or past `valid`: 0)
+template <int FM>
+__device__ __forceinline__ void phi_bf16x8_hilo(u32x4 r, bool live, u32x4& hi, u32x4& lo) {
+  float x[8];
+  In8<__bf16>::to_f32(r, x);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = live ? bphi<FM>(x[e]) : 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    lo[i] = pack_bf16x2(x[2 * i] - __uint_as_float(hi[i] << 16), x[2 * i + 1] - __uint_as_float(hi[i] & 0xffff0000u));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dq pass. grid = (BH, P), block = 4*D threads: wave (ib, w) handles query
 // rows [32 ib, 32 ib + 32) of the chunk and features [32 w, 32 w + 32). Each
 // wave keeps S^T (rows = value dims, columns = its features) and z over its
 // features in fp32 accumulators; the two waves of one feature block hold
 // the same state.
+// Precision: d phi(q_i) = sum_j phi(k_j) (v_j - y_i).g_i is a small
+// difference of large sums when phi(k) varies little over the keys (q, k of
+// small norm: phi(k) = 1 + a small part), and one bf16 rounding of phi(k)
+// loses a large share of that small part. With bf16 operands phi(K) enters
+// the S and z updates and the in-chunk product as hi + lo tiles, and S the
+// product with dY as hi + lo fragments.
 // ---------------------------------------------------------------------------
 template <int D, typename OP, typename IN, int FM>
 __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
@@ -153,12 +240,14 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
   constexpr int RB = D * Ops<OP>::kBytes;
   constexpr int TB = 64 * RB;
   constexpr int RL = D / 8;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TB];
+  constexpr bool DMA = kDma<IN>;
+  // one set of tiles phi(Q), phi(K), V, dY per chunk; with DMA two sets, the
+  // next chunk landing in one while the other is multiplied, and the low
+  // part of phi(K)
+  constexpr bool HILO = sizeof(OP) == 2;
+  static_assert(!HILO || DMA, "bf16 operands take the transfer path, which also writes the low part of phi(K)");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[(DMA ? 2 : 1) * 4 * TB + (HILO ? TB : 0)];
   __shared__ float red[2][NW][32][2];  // per row block and feature block: (phi(q).z, phi(q).(S dy)) partials
-  uint8_t* sQ = smem;
-  uint8_t* sK = smem + TB;
-  uint8_t* sV = smem + 2 * TB;
-  uint8_t* sY = smem + 3 * TB;
 
   const int bh = blockIdx.x, seg = blockIdx.y;
   const int c0 = seg * a.chunks_per_seg;
@@ -191,30 +280,66 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
     ones = frag8<OP>(o);
   }
 
-  Chunk4<D, IN> ck;
-  if (kPrefetch<IN> && n > 0) load_chunk4<D, IN, false>(ck, a, base + 64LL * c0, min(64, a.N - 64 * c0));
+  auto issue = [&](int m) {  // DMA of chunk c0 + m into set m & 1
+    const int c = c0 + m;
+    const unsigned bytes = (unsigned)(min(64, a.N - 64 * c) * D * 2);
+    const long long off = (base + 64LL * c) * D;
+    uint8_t* t0 = smem + (m & 1) * 4 * TB;
+    dma_tile<D>(t0, make_rsrc(static_cast<const IN*>(a.q) + off, bytes));
+    dma_tile<D>(t0 + TB, make_rsrc(static_cast<const IN*>(a.k) + off, bytes));
+    dma_tile<D>(t0 + 2 * TB, make_rsrc(static_cast<const IN*>(a.v) + off, bytes));
+    dma_tile<D>(t0 + 3 * TB, make_rsrc(static_cast<const IN*>(a.dy) + off, bytes));
+  };
+  if constexpr (DMA) {
+    if (n > 0) issue(0);
+  }
   for (int m = 0; m < n; ++m) {
     const int c = c0 + m;
     const int valid = min(64, a.N - 64 * c);
-    if (!kPrefetch<IN>) load_chunk4<D, IN, false>(ck, a, base + 64LL * c, valid);
-    // stage phi(Q), phi(K) (rows past the end: 0), V, dY
+    uint8_t* sQ = smem + (DMA ? (m & 1) : 0) * 4 * TB;
+    uint8_t* sK = sQ + TB;
+    uint8_t* sV = sQ + 2 * TB;
+    uint8_t* sY = sQ + 3 * TB;
+    uint8_t* sKl = smem + (DMA ? 2 : 1) * 4 * TB;  // low part of phi(K) (HILO)
+    if constexpr (DMA) {
+      // chunk m has landed (every wave's transfers, then the barrier); phi in place
+      wait_vmem_all();
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = t / RL + 32 * i, col = 8 * (t % RL);
-      float x[8];
-      In8<IN>::to_f32(ck.q[i], x);
+      for (int i = 0; i < 2; ++i) {
+        const int o = dma_off<D>(i);
+        const bool live = o / RB < valid;
+        u32x4* pq = reinterpret_cast<u32x4*>(sQ + o);
+        u32x4* pk = reinterpret_cast<u32x4*>(sK + o);
+        *pq = phi_bf16x8<FM, false>(*pq, live);
+        u32x4 khi, klo;
+        phi_bf16x8_hilo<FM>(*pk, live, khi, klo);
+        *pk = khi;
+        *reinterpret_cast<u32x4*>(sKl + o) = klo;
+      }
+      __syncthreads();
+      if (m + 1 < n) issue(m + 1);
+    } else {
+      Chunk4<D, IN> ck;
+      load_chunk4<D, IN, false>(ck, a, base + 64LL * c, valid);
+      // stage phi(Q), phi(K) (rows past the end: 0), V, dY
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = bphi<FM>(x[e]);
-      Ops<OP>::template store8<RB>(sQ, row, col, x);
-      In8<IN>::to_f32(ck.k[i], x);
+      for (int i = 0; i < 2; ++i) {
+        const int row = t / RL + 32 * i, col = 8 * (t % RL);
+        float x[8];
+        In8<IN>::to_f32(ck.q[i], x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = row < valid ? bphi<FM>(x[e]) : 0.f;
-      Ops<OP>::template store8<RB>(sK, row, col, x);
-      put_raw<IN, OP, RB>(sV, row, col, ck.v[i]);
-      put_raw<IN, OP, RB>(sY, row, col, ck.y[i]);
+        for (int e = 0; e < 8; ++e) x[e] = bphi<FM>(x[e]);
+        Ops<OP>::template store8<RB>(sQ, row, col, x);
+        In8<IN>::to_f32(ck.k[i], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = row < valid ? bphi<FM>(x[e]) : 0.f;
+        Ops<OP>::template store8<RB>(sK, row, col, x);
+        put_raw<IN, OP, RB>(sV, row, col, ck.v[i]);
+        put_raw<IN, OP, RB>(sY, row, col, ck.y[i]);
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (kPrefetch<IN> && m + 1 < n) load_chunk4<D, IN, false>(ck, a, base + 64LL * (c + 1), min(64, a.N - 64 * (c + 1)));
 
     // scores A[j][i] = phi(k_j).phi(q_i) and value products P[j][i] = v_j.dy_i
     // for the wave's query rows i: the diagonal key block (d) and, for the
@@ -254,14 +379,26 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
         dyn += Ao[r] * Po[r];
       }
     }
-    // T[f][i] = sum_e S[f][e] dy_i[e] over the wave's features
+    // T[f][i] = sum_e S[f][e] dy_i[e] over the wave's features. With bf16
+    // operands S enters as hi + lo: T / D_i and h_i z cancel down to
+    // sum_j phi(k_j) (v_j - y_i).g_i, which is much smaller than either term
+    // when phi(k) varies little over the keys, and a single bf16 rounding of
+    // S would be magnified by that ratio.
     f32x16 T = {};
 #pragma unroll
     for (int eb = 0; eb < NW; ++eb)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        Ops<OP>::mma(T, Ops<OP>::from_acc(ST[eb], kk),
-                     Ops<OP>::template load_rows<RB>(sY, 32 * ib, 32 * eb + 16 * kk));
+      for (int kk = 0; kk < 2; ++kk) {
+        const Frag yf = Ops<OP>::template load_rows<RB>(sY, 32 * ib, 32 * eb + 16 * kk);
+        if constexpr (sizeof(OP) == 2) {
+          bf16x8 hi, lo;
+          frag_hilo(ST[eb], kk, hi, lo);
+          Ops<OP>::mma(T, hi, yf);
+          Ops<OP>::mma(T, lo, yf);
+        } else {
+          Ops<OP>::mma(T, Ops<OP>::from_acc(ST[eb], kk), yf);
+        }
+      }
     // in-chunk parts (keys j <= i) of den_i and dy_i.num_i: both lane halves
     den += xor32(den);
     dyn += xor32(dyn);
@@ -304,14 +441,24 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
     // d phi(q_i)[f] = T[f][i] / D_i + h_i z_f + sum_j phi(k_j)[f] B[j][i]
 #pragma unroll
     for (int r = 0; r < 16; ++r) T[r] = T[r] * inv + hh * Z[r];
+    // (bf16: phi(K) and B both as hi + lo; the lo x lo term is below 2^-16)
+    auto intra = [&](const f32x16& Bt, int j0) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-      Ops<OP>::mma(T, Ops<OP>::template load_cols<RB>(sK, 32 * ib + 16 * kk, 32 * w), Ops<OP>::from_acc(Pd, kk));
-    if (ib) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        Ops<OP>::mma(T, Ops<OP>::template load_cols<RB>(sK, 16 * kk, 32 * w), Ops<OP>::from_acc(Po, kk));
-    }
+      for (int kk = 0; kk < 2; ++kk) {
+        const Frag kf = Ops<OP>::template load_cols<RB>(sK, j0 + 16 * kk, 32 * w);
+        if constexpr (HILO) {
+          bf16x8 bh, bl;
+          frag_hilo(Bt, kk, bh, bl);
+          Ops<OP>::mma(T, kf, bh);
+          Ops<OP>::mma(T, kf, bl);
+          Ops<OP>::mma(T, Ops<OP>::template load_cols<RB>(sKl, j0 + 16 * kk, 32 * w), bh);
+        } else {
+          Ops<OP>::mma(T, kf, Ops<OP>::from_acc(Bt, kk));
+        }
+      }
+    };
+    intra(Pd, 32 * ib);
+    if (ib) intra(Po, 0);
     if (irow < valid) {
       IN* o = dq + (base + 64LL * c + irow) * D + 32 * w + 4 * h;
 #pragma unroll
@@ -325,11 +472,19 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const Frag kf = Ops<OP>::template load_cols<RB>(sK, 16 * kb, 32 * w);
+      const Frag kl = HILO ? Ops<OP>::template load_cols<RB>(sKl, 16 * kb, 32 * w) : kf;
 #pragma unroll
-      for (int eb = 0; eb < NW; ++eb) Ops<OP>::mma(ST[eb], Ops<OP>::template load_cols<RB>(sV, 16 * kb, 32 * eb), kf);
+      for (int eb = 0; eb < NW; ++eb) {
+        const Frag vf = Ops<OP>::template load_cols<RB>(sV, 16 * kb, 32 * eb);
+        Ops<OP>::mma(ST[eb], vf, kf);
+        if constexpr (HILO) Ops<OP>::mma(ST[eb], vf, kl);
+      }
       Ops<OP>::mma(Z, kf, ones);
+      if constexpr (HILO) Ops<OP>::mma(Z, kl, ones);
     }
-    __syncthreads();
+    // the single set is restaged next; with two sets the next chunk's
+    // barriers already order these reads before that set is refilled
+    if constexpr (!DMA) __syncthreads();
   }
 }
 
@@ -435,9 +590,12 @@ __global__ __launch_bounds__(D * 2) void bwd_rstate_kernel(BwdArgs a) {
 //   waves NW..2NW-1 (feature block w): R^T[:, 32w:32w+32] (rows = value
 //     dims), r over the block's features, B[i][j] = g_i.v_j + h_i, dk for
 //     features [32w, 32w+32).
-// With bf16 operands B is formed as (dy_i.v_j) / D_i + h_i from the raw dY
-// tile: g_i.v_j and -h_i cancel where v_j is close to the output y_i, and a
-// product with g rounded to bf16 would leave that rounding in dk.
+// Tiles: phi(Q), phi(K), V, a "Y" tile and a "Qs" tile, with a per-row
+// scale sI: bf16 keeps Y = raw dY, Qs = phi(Q) / D_i and sI = 1 / D_i, so
+// the 1/D_i scaling happens in fp32 (B = (dy_i.v_j) sI_i + h_i, and the
+// scores times sI_i for dv): g_i.v_j and -h_i cancel where v_j is close to
+// the output y_i, and a product with g rounded to bf16 would leave that
+// rounding in dk. fp32 keeps Y = G = dY / D_i, Qs = phi(Q) and sI = 1.
 // ---------------------------------------------------------------------------
 template <int D, typename OP, typename IN, int FM>
 __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
@@ -446,15 +604,12 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int RB = D * Ops<OP>::kBytes;
   constexpr int TB = 64 * RB;
   constexpr int RL = D / 8;
-  constexpr bool RAWY = sizeof(OP) == 2;  // separate raw dY tile for B
-  __shared__ __attribute__((aligned(16))) uint8_t smem[(RAWY ? 5 : 4) * TB];
+  constexpr bool DMA = kDma<IN>;
+  // DMA: two sets of q, k, v, dY tiles (the next chunk lands in one while the
+  // other is multiplied) and the Qs tile; otherwise one set (Y = G, Qs = phi(Q))
+  __shared__ __attribute__((aligned(16))) uint8_t smem[(DMA ? 9 : 4) * TB];
   __shared__ __attribute__((aligned(16))) float sH[64];
   __shared__ __attribute__((aligned(16))) float sI[64];
-  uint8_t* sQ = smem;
-  uint8_t* sK = smem + TB;
-  uint8_t* sV = smem + 2 * TB;
-  uint8_t* sG = smem + 3 * TB;
-  uint8_t* sY = RAWY ? smem + 4 * TB : sG;
 
   const int bh = blockIdx.x, seg = blockIdx.y;
   const int c0 = seg * a.chunks_per_seg;
@@ -477,40 +632,92 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
     rK[r] = vgroup ? 0.f : Rp[D * D + 32 * w + rr];
   }
 
-  Chunk4<D, IN> ck;
-  if (kPrefetch<IN> && n > 0)
-    load_chunk4<D, IN, true>(ck, a, base + 64LL * (c0 + n - 1), min(64, a.N - 64 * (c0 + n - 1)));
+  uint8_t* sQs = smem + 8 * TB;  // DMA only
+  f32x2 rs[2];                    // DMA: (1 / D_i, h_i) of the rows of the thread's two units
+  auto issue = [&](int m) {       // DMA of chunk c0 + m into set m & 1, and its row statistics
+    const int c = c0 + m;
+    const int valid = min(64, a.N - 64 * c);
+    const unsigned bytes = (unsigned)(valid * D * 2);
+    const long long row0 = base + 64LL * c;
+    const long long off = row0 * D;
+    uint8_t* t0 = smem + (m & 1) * 4 * TB;
+    dma_tile<D>(t0, make_rsrc(static_cast<const IN*>(a.q) + off, bytes));
+    dma_tile<D>(t0 + TB, make_rsrc(static_cast<const IN*>(a.k) + off, bytes));
+    dma_tile<D>(t0 + 2 * TB, make_rsrc(static_cast<const IN*>(a.v) + off, bytes));
+    dma_tile<D>(t0 + 3 * TB, make_rsrc(static_cast<const IN*>(a.dy) + off, bytes));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = dma_off<D>(i) / RB;
+      rs[i] = row < valid ? *reinterpret_cast<const f32x2*>(a.rowstats + 2 * (row0 + row)) : f32x2{0.f, 0.f};
+    }
+  };
+  if constexpr (DMA) {
+    if (n > 0) issue(n - 1);
+  }
   for (int m = n - 1; m >= 0; --m) {
     const int c = c0 + m;
     const int valid = min(64, a.N - 64 * c);
-    if (!kPrefetch<IN>) load_chunk4<D, IN, true>(ck, a, base + 64LL * c, valid);
-    // stage phi(Q), phi(K) (rows past the end: 0), V, G = dY / D_i, h
+    uint8_t* sQ = smem + (DMA ? (m & 1) : 0) * 4 * TB;
+    uint8_t* sK = sQ + TB;
+    uint8_t* sV = sQ + 2 * TB;
+    uint8_t* sY = sQ + 3 * TB;
+    uint8_t* sQq = DMA ? sQs : sQ;
+    if constexpr (DMA) {
+      // chunk m has landed: phi in place (rows past the end: 0), Qs = phi(Q) / D_i
+      wait_vmem_all();
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = t / RL + 32 * i, col = 8 * (t % RL);
-      const bool live = row < valid;
-      float x[8];
-      In8<IN>::to_f32(ck.q[i], x);
+      for (int i = 0; i < 2; ++i) {
+        const int o = dma_off<D>(i);
+        const int row = o / RB;
+        const bool live = row < valid;
+        u32x4* pq = reinterpret_cast<u32x4*>(sQ + o);
+        u32x4* pk = reinterpret_cast<u32x4*>(sK + o);
+        const u32x4 fq = phi_bf16x8<FM, true>(*pq, live);
+        *pq = fq;
+        *pk = phi_bf16x8<FM, true>(*pk, live);
+        float x[8];
+        In8<__bf16>::to_f32(fq, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = live ? bphi<FM>(x[e]) : 0.f;
-      Ops<OP>::template store8<RB>(sQ, row, col, x);
-      In8<IN>::to_f32(ck.k[i], x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = live ? bphi<FM>(x[e]) : 0.f;
-      Ops<OP>::template store8<RB>(sK, row, col, x);
-      put_raw<IN, OP, RB>(sV, row, col, ck.v[i]);
-      In8<IN>::to_f32(ck.y[i], x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] *= ck.rs[i][0];
-      Ops<OP>::template store8<RB>(sG, row, col, x);
-      if constexpr (RAWY) put_raw<IN, OP, RB>(sY, row, col, ck.y[i]);
-      if (col == 0) {
-        sH[row] = ck.rs[i][1];
-        sI[row] = RAWY ? ck.rs[i][0] : 1.f;
+        for (int e = 0; e < 8; ++e) x[e] *= rs[i][0];
+        *reinterpret_cast<u32x4*>(sQs + o) = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                                   pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+        if ((o % RB) == 0) {
+          sH[row] = rs[i][1];
+          sI[row] = rs[i][0];
+        }
       }
+      __syncthreads();
+      if (m > 0) issue(m - 1);
+    } else {
+      Chunk4<D, IN> ck;
+      load_chunk4<D, IN, true>(ck, a, base + 64LL * c, valid);
+      // stage phi(Q), phi(K) (rows past the end: 0), V, G = dY / D_i, h
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = t / RL + 32 * i, col = 8 * (t % RL);
+        const bool live = row < valid;
+        float x[8];
+        In8<IN>::to_f32(ck.q[i], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = live ? bphi<FM>(x[e]) : 0.f;
+        Ops<OP>::template store8<RB>(sQ, row, col, x);
+        In8<IN>::to_f32(ck.k[i], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = live ? bphi<FM>(x[e]) : 0.f;
+        Ops<OP>::template store8<RB>(sK, row, col, x);
+        put_raw<IN, OP, RB>(sV, row, col, ck.v[i]);
+        In8<IN>::to_f32(ck.y[i], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= ck.rs[i][0];
+        Ops<OP>::template store8<RB>(sY, row, col, x);
+        if (col == 0) {
+          sH[row] = ck.rs[i][1];
+          sI[row] = 1.f;
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (kPrefetch<IN> && m > 0) load_chunk4<D, IN, true>(ck, a, base + 64LL * (c - 1), min(64, a.N - 64 * (c - 1)));
 
     if (vgroup) {
       // dv_j[e] = sum_{i>=j} G[i][e] A[i][j] + sum_f R[f][e] phi(k_j)[f], with the
@@ -521,17 +728,23 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
       for (int tI = 0; tI < 3; ++tI) {
         const int qb = tI == 0 ? 0 : 1, kbk = tI == 2 ? 1 : 0;
         f32x16 A = {};
-#pragma unroll
+// partial unroll: full unrolling hoists every fragment load and spills
+#pragma unroll 2
         for (int kb = 0; kb < D / 16; ++kb)
           Ops<OP>::mma(A, Ops<OP>::template load_rows<RB>(sQ, 32 * qb, 16 * kb),
                        Ops<OP>::template load_rows<RB>(sK, 32 * kbk, 16 * kb));
-        if (qb == kbk) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) A[r] = li <= 8 * (r >> 2) + 4 * h + (r & 3) ? A[r] : 0.f;
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 iq = *reinterpret_cast<const f32x4*>(sI + 32 * qb + 8 * g + 4 * h);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool keep = qb != kbk || li <= 8 * g + 4 * h + e;
+            A[4 * g + e] = keep ? A[4 * g + e] * iq[e] : 0.f;
+          }
         }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
-          Ops<OP>::mma(kbk ? V1 : V0, Ops<OP>::template load_cols<RB>(sG, 32 * qb + 16 * kk, 32 * w),
+          Ops<OP>::mma(kbk ? V1 : V0, Ops<OP>::template load_cols<RB>(sY, 32 * qb + 16 * kk, 32 * w),
                        Ops<OP>::from_acc(A, kk));
       }
 #pragma unroll
@@ -552,12 +765,12 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
           for (int g = 0; g < 4; ++g) store4<IN>(o + 8 * g, Vt[4 * g], Vt[4 * g + 1], Vt[4 * g + 2], Vt[4 * g + 3]);
         }
       }
-      // R += phi(Q)^T G over the chunk
+      // R += phi(Q)^T G = Qs^T Y over the chunk
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const Frag gf = Ops<OP>::template load_cols<RB>(sG, 16 * kb, 32 * w);
+        const Frag gf = Ops<OP>::template load_cols<RB>(sY, 16 * kb, 32 * w);
 #pragma unroll
-        for (int fb = 0; fb < NW; ++fb) Ops<OP>::mma(RS[fb], Ops<OP>::template load_cols<RB>(sQ, 16 * kb, 32 * fb), gf);
+        for (int fb = 0; fb < NW; ++fb) Ops<OP>::mma(RS[fb], Ops<OP>::template load_cols<RB>(sQq, 16 * kb, 32 * fb), gf);
       }
     } else {
       // d phi(k_j)[f] = sum_{i>=j} phi(q_i)[f] B[i][j] + sum_e R[f][e] v_j[e] + r_f,
@@ -568,7 +781,8 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
       for (int tI = 0; tI < 3; ++tI) {
         const int qb = tI == 0 ? 0 : 1, kbk = tI == 2 ? 1 : 0;
         f32x16 Bt = {};
-#pragma unroll
+// partial unroll: full unrolling hoists every fragment load and spills
+#pragma unroll 2
         for (int kb = 0; kb < D / 16; ++kb)
           Ops<OP>::mma(Bt, Ops<OP>::template load_rows<RB>(sY, 32 * qb, 16 * kb),
                        Ops<OP>::template load_rows<RB>(sV, 32 * kbk, 16 * kb));
@@ -614,15 +828,18 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const Frag qf = Ops<OP>::template load_cols<RB>(sQ, 16 * kb, 32 * w);
+        const Frag qsf = DMA ? Ops<OP>::template load_cols<RB>(sQq, 16 * kb, 32 * w) : qf;
 #pragma unroll
-        for (int eb = 0; eb < NW; ++eb) Ops<OP>::mma(RS[eb], Ops<OP>::template load_cols<RB>(sG, 16 * kb, 32 * eb), qf);
+        for (int eb = 0; eb < NW; ++eb) Ops<OP>::mma(RS[eb], Ops<OP>::template load_cols<RB>(sY, 16 * kb, 32 * eb), qsf);
         const f32x4 ha = *reinterpret_cast<const f32x4*>(sH + 16 * kb + 8 * h);
         const f32x4 hb = *reinterpret_cast<const f32x4*>(sH + 16 * kb + 8 * h + 4);
         const float hv[8] = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
         Ops<OP>::mma(rK, qf, frag8<OP>(hv));
       }
     }
-    __syncthreads();
+    // the single set is restaged next; with two sets the next chunk's
+    // barriers already order these reads before that set is refilled
+    if constexpr (!DMA) __syncthreads();
   }
 }
 
@@ -632,6 +849,7 @@ hipError_t launch_backward(const FwdArgs& fa, const ScanArgs& fs, const BwdArgs&
   if (fa.run_state_pass || fa.run_scan) {
     FwdArgs f = fa;
     f.skip_output = 1;
+    f.hilo_keys = 1;  // S carries phi(k) to ~2^-16 (the dq pass needs it; see there)
     const hipError_t e = prefill_dispatch(f, fs, D, D, FM, dtype, true, false, st, nullptr);
     if (e != hipSuccess) return e;
   }

@@ -41,6 +41,7 @@ struct FwdArgs {
   const float* gamma;      // decay per head [H] (causal only) or null
   int H;                   // heads (gamma index = bh % H)
   int skip_output;         // run the state pass and scan only (segment prefixes for the gradient passes)
+  int hilo_keys;           // state pass with phi(K) as hi + lo bf16 (bf16, no decay, d' = d; gradient passes)
 };
 
 struct ScanArgs {

@@ -344,15 +344,20 @@ __device__ __forceinline__ void store_state_tiles(const f32x16 (&S)[DF / 32], fl
 // ---------------------------------------------------------------------------
 // State pass: local (S, z) of every segment. All 2*D threads stage; wave w
 // owns value columns [32w, 32w+32) of S.
+// HILO (bf16 operands, for the gradient passes): phi(K) enters S as hi + lo
+// bf16 tiles, so S carries phi(k) to about 2^-16 instead of 2^-9 (the
+// gradient with respect to q magnifies that rounding where phi(k) varies
+// little over the keys).
 // grid = (BH, P), block = 2*D threads.
 // ---------------------------------------------------------------------------
-template <int D, int DF, typename OP, typename IN, int FM, bool DECAY>
+template <int D, int DF, typename OP, typename IN, int FM, bool DECAY, bool HILO = false>
 __global__ __launch_bounds__(D * 2) void state_pass_kernel(FwdArgs a) {
   using Frag = typename Ops<OP>::frag;
   using G = Stage<D, DF>;
+  static_assert(!HILO || (sizeof(OP) == 2 && !DECAY && DF == D), "hi + lo keys: bf16 operands, no decay, d' = d");
   constexpr int RBF = DF * Ops<OP>::kBytes;
   constexpr int RBV = D * Ops<OP>::kBytes;
-  constexpr int KB = 64 * RBF, VB = 64 * RBV, BUF = KB + VB;
+  constexpr int KB = 64 * RBF, VB = 64 * RBV, BUF = KB + VB + (HILO ? KB : 0);
   constexpr int NW = D / 32;
   // two staged chunks when they fit; otherwise one, with an extra barrier
   constexpr int NB = 2 * BUF + NW * DF * 4 <= 160 * 1024 ? 2 : 1;
@@ -401,6 +406,23 @@ __global__ __launch_bounds__(D * 2) void state_pass_kernel(FwdArgs a) {
       for (int i = 0; i < 4; ++i) store_raw<IN, OP, RBV>(sK + KB, p / G::RLV + 16 * i, 8 * (p % G::RLV), pf.v[i]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) zr[e] = gH * (gH * zr[e]) + cs[e];
+    } else if constexpr (HILO) {
+      uint8_t* sKl = sK + KB + VB;
+#pragma unroll
+      for (int i = 0; i < G::NQ; ++i) {
+        const int row = p / G::RLF + G::RSF * i, col = 8 * (p % G::RLF);
+        float x[8], lo[8];
+        In8<IN>::to_f32(pf.k[i], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[e] = fmap_in_stage<FM>(x[e]);
+          zr[e] += x[e];
+          lo[e] = x[e] - round_bf16(x[e]);
+        }
+        Ops<OP>::template store8<RBF>(sK, row, col, x);
+        Ops<OP>::template store8<RBF>(sKl, row, col, lo);
+        store_raw<IN, OP, RBV>(sK + KB, row, col, pf.v[i]);
+      }
     } else {
       prod_stage<D, DF, IN, OP, FM, false, true>(pf, p, nullptr, sK, sK + KB, zr, dp, cs);
 #pragma unroll
@@ -422,8 +444,10 @@ __global__ __launch_bounds__(D * 2) void state_pass_kernel(FwdArgs a) {
 #pragma unroll
     for (int cb = 0; cb < DF / 32; ++cb)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb) {
         Ops<OP>::mma(S[cb], Ops<OP>::template load_cols<RBF>(sK, 16 * kb, 32 * cb), Vf[kb]);
+        if constexpr (HILO) Ops<OP>::mma(S[cb], Ops<OP>::template load_cols<RBF>(sV + VB, 16 * kb, 32 * cb), Vf[kb]);
+      }
   };
   // iteration m multiplies chunk m (LDS), stages chunk m+1 (registers) and
   // issues the loads of chunk m+NSET into the set chunk m occupied
@@ -620,6 +644,10 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
     // ------------------------------------------------------------------
     // producers: chunk `it` is loaded NSET-1 steps before step it stages it
     // ------------------------------------------------------------------
+    // The producers are the critical path; a producer and a consumer wave
+    // share each SIMD, and the raised priority lets the producer's VALU and
+    // memory instructions issue first (about 3% on the long-context shape).
+    __builtin_amdgcn_s_setprio(1);
     float zrun[8], dp[G::NQ], cs[8];
     const int cr = 8 * (p % G::RLF);
     const Voff<D, DF, IN> vo(p);
@@ -915,8 +943,13 @@ static hipError_t launch_prefill_t(const FwdArgs& a, const ScanArgs& s, bool cau
                                    hipEvent_t* ev) {
   // ev[0] is recorded by the caller (before any feature-map kernels)
   if (a.run_state_pass) {
-    hipLaunchKernelGGL((state_pass_kernel<D, DF, OP, IN, FM, DECAY>), dim3(a.BH, a.nseg_state), dim3(D * 2), 0, st,
-                       a);
+    constexpr bool kHiloOk = sizeof(OP) == 2 && !DECAY && DF == D;
+    if (kHiloOk && a.hilo_keys)
+      hipLaunchKernelGGL((state_pass_kernel<D, DF, OP, IN, FM, DECAY, kHiloOk>), dim3(a.BH, a.nseg_state),
+                         dim3(D * 2), 0, st, a);
+    else
+      hipLaunchKernelGGL((state_pass_kernel<D, DF, OP, IN, FM, DECAY>), dim3(a.BH, a.nseg_state), dim3(D * 2), 0,
+                         st, a);
   }
   if (ev) (void)hipEventRecord(ev[1], st);
   if (a.run_scan) {
