@@ -17,6 +17,11 @@ from .linattn_oracle import (  # noqa: F401
     feature_map,
     feature_map_vjp,
     final_state,
+    gated_attention,
+    gated_chunked,
+    gated_decode_step,
+    gated_final_state,
+    gated_recurrent,
     phi_elu1,
     phi_identity,
     phi_performer,

@@ -35,6 +35,10 @@ listed with its reasons in the design notes of the repository):
   * an optional initial state (S0, z0) stands for tokens before the first
     one given: it adds phi(q_i).S0 to the numerator and phi(q_i).z0 to the
     denominator of every output;
+  * gates ([LA] "Variantes y extensiones", GLA item): a data-dependent
+    per-token, per-channel gate alpha_t on the feature dimension,
+    S_t = diag(alpha_t) S_{t-1} + phi(k_t) v_t^T, z gated alike (given as
+    log-gates); a constant gate equal over channels is the decay below;
   * decay ([LA] "Variantes y extensiones", RetNet item): the state recurs as
     S_t = gamma S_{t-1} + phi(k_t) v_t^T and the normalizer the same way,
     z_t = gamma z_{t-1} + phi(k_t); unrolled, token j enters output i with
@@ -515,3 +519,139 @@ def recurrent_backward(q, k, v, dy, fmap="elu1", W=None, normalize=True,
     lead = shape[:-2]
     return (dq.reshape(shape), dk.reshape(shape), dV.reshape(lead + (N, dv)),
             R.reshape(lead + (dfeat, dv)), r.reshape(lead + (dfeat,)))
+
+
+# ---------------------------------------------------------------------------
+# Gated linear attention ([LA] "Variantes y extensiones", GLA item: the
+# scalar decay replaced by a gate that depends on the data). Reading: a
+# per-token, per-channel gate alpha_t in (0, 1]^d' on the feature dimension,
+# S_t = diag(alpha_t) S_{t-1} + phi(k_t) v_t^T, the normalizer gated alike,
+# z_t = alpha_t * z_{t-1} + phi(k_t), y_t = phi(q_t)^T S_t / phi(q_t).z_t.
+# Gates are given as log-gates lg = log(alpha), an array [..., N, d'].
+# Unrolled, token j enters output i through channel f with weight
+# exp(L_if - L_jf), L_t = sum_{s<=t} lg_s; an initial state enters with
+# exp(L_if). A constant gate equal over channels is the decay above.
+# ---------------------------------------------------------------------------
+
+def _lg(log_gates, G, N, dfeat):
+    lg = np.asarray(log_gates, dtype=np.float64)
+    return lg.reshape(G, N, dfeat)
+
+
+def gated_attention(q, k, v, log_gates, fmap="elu1", W=None, normalize=True, S0=None, z0=None, rows=None):
+    """Definition, causal: y_i = sum_{j<=i} sum_f phi(q_i)_f phi(k_j)_f exp(L_if - L_jf) v_j / (same without v_j).
+
+    Each output row forms its weights over every earlier key explicitly
+    (brute force); ``rows`` restricts the computation to sampled outputs.
+    """
+    shape = np.asarray(q).shape
+    Q, K, V = _bh(q), _bh(k), _bh(v)
+    G, N, _ = Q.shape
+    dv = V.shape[-1]
+    Qf = feature_map(Q, fmap, W)
+    Kf = feature_map(K, fmap, W)
+    dfeat = Qf.shape[-1]
+    L = np.cumsum(_lg(log_gates, G, N, dfeat), axis=1)       # [G, N, d']
+    S, z = _state(S0, z0, G, dfeat, dv)
+    idx = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty((G, idx.size, dv))
+    for g in range(G):
+        for n, i in enumerate(idx):
+            wgt = np.exp(L[g, i][None, :] - L[g, :i + 1])       # [i+1, d'] per key and channel
+            a = (Qf[g, i][None, :] * Kf[g, :i + 1] * wgt).sum(axis=1)
+            s0 = np.exp(L[g, i])                                 # initial state, per channel
+            num = a @ V[g, :i + 1] + (Qf[g, i] * s0) @ S[g]
+            den = a.sum() + (Qf[g, i] * s0) @ z[g]
+            out[g, n] = num / max(den, EPS) if normalize else num
+    return out.reshape(shape[:-2] + (idx.size, dv))
+
+
+def gated_final_state(k, v, log_gates, fmap="elu1", W=None, S0=None, z0=None):
+    """S_N = diag(exp(L_N-1)) S0 + sum_j diag(exp(L_N-1 - L_j)) phi(k_j) v_j^T, z alike."""
+    shape = np.asarray(k).shape
+    K, V = _bh(k), _bh(v)
+    G, N = K.shape[0], K.shape[1]
+    Kf = feature_map(K, fmap, W)
+    dfeat = Kf.shape[-1]
+    L = np.cumsum(_lg(log_gates, G, N, dfeat), axis=1)
+    S, z = _state(S0, z0, G, dfeat, V.shape[-1])
+    if N > 0:
+        last = L[:, -1]                                          # [G, d']
+        wgt = np.exp(last[:, None, :] - L)                       # [G, N, d']
+        S = np.exp(last)[:, :, None] * S + np.einsum("gnc,gnc,gne->gce", wgt, Kf, V)
+        z = np.exp(last) * z + np.einsum("gnc,gnc->gc", wgt, Kf)
+    lead = shape[:-2]
+    return S.reshape(lead + S.shape[1:]), z.reshape(lead + z.shape[1:])
+
+
+def gated_decode_step(S, z, q, k, v, log_gate, fmap="elu1", W=None, normalize=True):
+    """One token per head: S = diag(alpha) S + phi(k) v^T, z = alpha z + phi(k), then the readout.
+
+    log_gate: [..., d'] (log alpha of this token). Returns (y, S_new, z_new).
+    """
+    S = np.asarray(S, np.float64)
+    z = np.asarray(z, np.float64)
+    a = np.exp(np.asarray(log_gate, np.float64))
+    qf = feature_map(np.asarray(q, np.float64), fmap, W)
+    kf = feature_map(np.asarray(k, np.float64), fmap, W)
+    v = np.asarray(v, np.float64)
+    S_new = a[..., :, None] * S + kf[..., :, None] * v[..., None, :]
+    z_new = a * z + kf
+    num = np.einsum("...c,...ce->...e", qf, S_new)
+    den = np.einsum("...c,...c->...", qf, z_new)
+    return _finish(num, den, normalize), S_new, z_new
+
+
+def gated_recurrent(q, k, v, log_gates, fmap="elu1", W=None, normalize=True, S0=None, z0=None):
+    """Token-by-token loop of gated_decode_step. Returns (y, S_N, z_N)."""
+    shape = np.asarray(q).shape
+    Q, K, V = _bh(q), _bh(k), _bh(v)
+    G, N, _ = Q.shape
+    dv = V.shape[-1]
+    dfeat = feature_dim(Q.shape[-1], fmap, W)
+    lg = _lg(log_gates, G, N, dfeat)
+    S, z = _state(S0, z0, G, dfeat, dv)
+    y = np.empty((G, N, dv))
+    for t in range(N):
+        y[:, t], S, z = gated_decode_step(S, z, Q[:, t], K[:, t], V[:, t], lg[:, t], fmap, W, normalize)
+    lead = shape[:-2]
+    return (y.reshape(shape[:-1] + (dv,)), S.reshape(lead + S.shape[1:]),
+            z.reshape(lead + z.shape[1:]))
+
+
+def gated_chunked(q, k, v, log_gates, fmap="elu1", W=None, normalize=True, chunk=64, S0=None, z0=None):
+    """Blockwise gated form ([LA] "Entrenamiento: forma paralela" applied to the
+    gated recurrence): inside a block of L tokens with in-block cumulative
+    log-gates lam (lam_r = sum of the block's log-gates up to row r), key j
+    enters row i through channel f with weight exp(lam_if - lam_jf) (j <= i),
+    the carried state with exp(lam_if), and the state moves on as
+    S <- diag(exp(lam_last)) S + sum_j diag(exp(lam_last - lam_j)) phi(k_j) v_j^T.
+    Returns (y, S_N, z_N)."""
+    shape = np.asarray(q).shape
+    Q, K, V = _bh(q), _bh(k), _bh(v)
+    G, N, _ = Q.shape
+    dv = V.shape[-1]
+    Qf = feature_map(Q, fmap, W)
+    Kf = feature_map(K, fmap, W)
+    dfeat = Qf.shape[-1]
+    lg = _lg(log_gates, G, N, dfeat)
+    S, z = _state(S0, z0, G, dfeat, dv)
+    y = np.empty((G, N, dv))
+    for s in range(0, N, chunk):
+        e = min(N, s + chunk)
+        Lb = e - s
+        qc, kc, vc = Qf[:, s:e], Kf[:, s:e], V[:, s:e]
+        lam = np.cumsum(lg[:, s:e], axis=1)                      # [G, L, d']
+        wgt = np.exp(lam[:, :, None, :] - lam[:, None, :, :])    # [G, L(i), L(j), d']
+        A = np.einsum("gic,gjc,gijc->gij", qc, kc, wgt) * np.tril(np.ones((Lb, Lb)))[None]
+        qs = qc * np.exp(lam)                                    # carried-state weight per channel
+        num = np.einsum("gij,gje->gie", A, vc) + np.einsum("gic,gce->gie", qs, S)
+        den = A.sum(axis=2) + np.einsum("gic,gc->gi", qs, z)
+        y[:, s:e] = _finish(num, den, normalize)
+        last = lam[:, -1]
+        kw = kc * np.exp(last[:, None, :] - lam)
+        S = np.exp(last)[:, :, None] * S + np.einsum("gjc,gje->gce", kw, vc)
+        z = np.exp(last) * z + kw.sum(axis=1)
+    lead = shape[:-2]
+    return (y.reshape(shape[:-1] + (dv,)), S.reshape(lead + S.shape[1:]),
+            z.reshape(lead + z.shape[1:]))

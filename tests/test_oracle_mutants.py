@@ -121,6 +121,32 @@ BACKWARD_MUTANTS = [
     ("        R = gm[:, None, None] * R\n", "        R = R\n", "recurrent backward: adjoint state not decayed"),
 ]
 
+# mistakes in the gated forms, caught by tests/test_oracle_gated_pins.py
+GATED_MUTANTS = [
+    ("wgt = np.exp(L[g, i][None, :] - L[g, :i + 1])       # [i+1, d'] per key and channel",
+     "wgt = np.exp(L[g, i][None, :] - L[g, :i + 1] + _lg(log_gates, G, N, dfeat)[g, :i + 1])",
+     "gated definition: key weight includes its own gate"),
+    ("s0 = np.exp(L[g, i])                                 # initial state, per channel",
+     "s0 = np.exp(L[g, i] - _lg(log_gates, G, N, dfeat)[g, 0])",
+     "gated definition: initial state skips the first gate"),
+    ("num = a @ V[g, :i + 1] + (Qf[g, i] * s0) @ S[g]", "num = a @ V[g, :i + 1] + Qf[g, i] @ S[g]",
+     "gated definition: initial state not gated"),
+    ("wgt = np.exp(L[g, i][None, :] - L[g, :i + 1])       # [i+1, d'] per key and channel",
+     "wgt = np.exp(L[g, i][None, :] - L[g, :i + 1])[:, ::-1]",
+     "gated definition: channels of the gate reversed"),
+    ("S_new = a[..., :, None] * S + kf[..., :, None] * v[..., None, :]",
+     "S_new = a[..., None, :] * S + kf[..., :, None] * v[..., None, :]",
+     "gated decode: gate applied to the value dimension"),
+    ("z_new = a * z + kf", "z_new = z + kf", "gated decode: normalizer not gated"),
+    ("wgt = np.exp(last[:, None, :] - L)                       # [G, N, d']",
+     "wgt = np.exp(last[:, None, :] - L + _lg(log_gates, G, N, dfeat))",
+     "gated final state: key weight off by one gate"),
+    ("qs = qc * np.exp(lam)                                    # carried-state weight per channel",
+     "qs = qc * np.exp(lam - lg[:, s:e])", "gated blockwise: carried state misses the row's own gate"),
+    ("kw = kc * np.exp(last[:, None, :] - lam)", "kw = kc * np.exp(last[:, None, :] - lam + lg[:, s:e])",
+     "gated blockwise: update weights off by one gate"),
+]
+
 
 def _run_pins(tmp_path, src, init=INIT, pins="test_oracle_pins.py"):
     pkg = tmp_path / "oracle"
@@ -134,7 +160,7 @@ def _run_pins(tmp_path, src, init=INIT, pins="test_oracle_pins.py"):
     return r.returncode, r.stdout[-2000:]
 
 
-@pytest.mark.parametrize("pins", ["test_oracle_pins.py", "test_oracle_backward_pins.py"])
+@pytest.mark.parametrize("pins", ["test_oracle_pins.py", "test_oracle_backward_pins.py", "test_oracle_gated_pins.py"])
 def test_control_unaltered_copy_passes(tmp_path, pins):
     rc, out = _run_pins(tmp_path, SRC, pins=pins)
     assert rc == 0, out
@@ -156,4 +182,11 @@ def test_pins_catch_planted_mistake(tmp_path, old, new, what):
 def test_backward_pins_catch_planted_mistake(tmp_path, old, new, what):
     assert SRC.count(old) >= 1, f"mutation site not found: {old!r}"
     rc, out = _run_pins(tmp_path, SRC.replace(old, new, 1), pins="test_oracle_backward_pins.py")
+    assert rc != 0, f"the pins did not catch: {what}\n{out}"
+
+
+@pytest.mark.parametrize("old,new,what", GATED_MUTANTS, ids=[m[2] for m in GATED_MUTANTS])
+def test_gated_pins_catch_planted_mistake(tmp_path, old, new, what):
+    assert SRC.count(old) >= 1, f"mutation site not found: {old!r}"
+    rc, out = _run_pins(tmp_path, SRC.replace(old, new, 1), pins="test_oracle_gated_pins.py")
     assert rc != 0, f"the pins did not catch: {what}\n{out}"
