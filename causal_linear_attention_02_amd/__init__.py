@@ -23,7 +23,8 @@ __all__ = [
     "la_feature_map", "lib", "library_path", "LinAttnError",
     "la_version", "la_status_string", "la_forward_workspace_size", "la_forward", "la_forward_ex",
     "la_decode_step", "la_feature_map_apply", "feature_dim", "la_forward_decay", "la_decode_step_decay",
-    "la_backward_workspace_size", "la_backward",
+    "la_backward_workspace_size", "la_backward", "la_forward_gated_workspace_size", "la_forward_gated",
+    "la_decode_step_gated",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +74,12 @@ def _load():
     L.la_backward_workspace_size.restype = sz
     L.la_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, fmp, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.la_backward.restype = i
+    L.la_forward_gated_workspace_size.argtypes = [i, i, i, i, fmp]
+    L.la_forward_gated_workspace_size.restype = sz
+    L.la_forward_gated.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, fmp, i, i, vp, vp, vp, vp, vp, sz, vp]
+    L.la_forward_gated.restype = i
+    L.la_decode_step_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, fmp, i, i, vp]
+    L.la_decode_step_gated.restype = i
     return L
 
 
@@ -319,3 +326,62 @@ def la_backward(q, k, v, dout, *, feature_map="elu1", normalize=True, S_in=None,
                          _ptr(dS_in), _ptr(dz_in), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "la_backward")
     return (dq, dk, dv, dS_in, dz_in) if return_state_grad else (dq, dk, dv)
+
+
+def la_forward_gated_workspace_size(B, H, N, d, feature_map="elu1") -> int:
+    fm = _fmap(feature_map, None)
+    return int(lib.la_forward_gated_workspace_size(B, H, N, d, ctypes.byref(fm)))
+
+
+def _gates(g, shape, device):
+    if not torch.is_tensor(g) or g.dtype != torch.float32 or tuple(g.shape) != tuple(shape):
+        raise ValueError(f"log-gates: a float32 tensor of shape {tuple(shape)}")
+    if g.device != device:
+        raise ValueError("log-gates must live on the same device as the inputs")
+    return g
+
+
+def la_forward_gated(q, k, v, log_gates, *, feature_map="elu1", normalize=True, S_in=None, z_in=None,
+                     return_state=False, out=None, workspace=None, stream=None):
+    """Causal gated linear attention on [B, H, N, d] tensors; log_gates [B, H, N, d] float32."""
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    g = _gates(log_gates, q.shape, q.device)
+    fm = _fmap(feature_map, None)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    S_out = z_out = None
+    if return_state:
+        S_out = torch.empty((B, H, d, d), device=q.device, dtype=torch.float32)
+        z_out = torch.empty((B, H, d), device=q.device, dtype=torch.float32)
+    need = int(lib.la_forward_gated_workspace_size(B, H, N, d, ctypes.byref(fm)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.la_forward_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out), B, H, N, d, ctypes.byref(fm),
+                              int(normalize), _dtype_code(q), _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out),
+                              _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "la_forward_gated")
+    return (out, S_out, z_out) if return_state else out
+
+
+def la_decode_step_gated(S, z, q, k, v, log_gate, *, feature_map="elu1", W=None, normalize=True, out=None,
+                         stream=None):
+    """Decode step with a per-feature gate: S, z updated in place; log_gate [B, H, d'] float32."""
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, d] shape")
+    B, H, d = q.shape
+    fm = _fmap(feature_map, W)
+    df = feature_dim(d, feature_map, W)
+    g = _gates(log_gate, (B, H, df), q.device)
+    if tuple(S.shape) != (B, H, df, d) or tuple(z.shape) != (B, H, df):
+        raise ValueError("state shapes must be S [B, H, d', d] and z [B, H, d']")
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib.la_decode_step_gated(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out), B, H, d,
+                                  ctypes.byref(fm), int(normalize), _dtype_code(q), _stream(stream))
+    _check(st, "la_decode_step_gated")
+    return out

@@ -568,3 +568,178 @@ int la_backward(const void* q, const void* k, const void* v, const void* dout, v
 }
 
 }  // extern "C"
+
+namespace {
+
+struct GatedPlan {
+  Plan p;
+  size_t state_bytes = 0, lfac_bytes = 0, ws_bytes = 0;
+};
+
+GatedPlan make_gated_plan(long long BH, int N, int d) {
+  GatedPlan g;
+  g.p = make_plan(BH, N, d, d, true, false);  // the causal split; its workspace holds the segment states
+  if (N == 0 || BH == 0) return g;
+  g.state_bytes = align256(g.p.ws_bytes);
+  g.lfac_bytes = g.p.P > 1 ? align256((size_t)BH * g.p.P * d * sizeof(float)) : 0;
+  g.ws_bytes = g.state_bytes + g.lfac_bytes;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t la_forward_gated_workspace_size(int B, int H, int N, int d, const la_feature_map* feature_map) {
+  if (B < 0 || H < 0 || N < 0 || !d_supported(d) || bwd_map(feature_map, d) != LA_OK) return 0;
+  return make_gated_plan((long long)B * H, N, d).ws_bytes;
+}
+
+int la_forward_gated(const void* q, const void* k, const void* v, const float* log_gates, void* out, int B, int H,
+                     int N, int d, const la_feature_map* feature_map, int normalize, int dtype, const float* S_in,
+                     const float* z_in, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  if (B < 0 || H < 0 || N < 0) return LA_ERR_INVALID_ARG;
+  if (normalize != 0 && normalize != 1) return LA_ERR_INVALID_ARG;
+  if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
+  if ((S_in == nullptr) != (z_in == nullptr) || (S_out == nullptr) != (z_out == nullptr)) return LA_ERR_INVALID_ARG;
+  if (!d_supported(d)) return LA_ERR_UNSUPPORTED;
+  const int fs = bwd_map(feature_map, d);  // maps applied in the kernels (d' = d)
+  if (fs != LA_OK) return fs;
+  const long long BH = (long long)B * H;
+  if (BH > (1LL << 31) - 1) return LA_ERR_UNSUPPORTED;
+  const long long esz = dtype == LA_BF16 ? 2 : 4;
+  const long long tb = BH * N * d * esz, gb = BH * N * d * 4, sb = BH * d * d * 4, zb = BH * d * 4;
+  for (const void* p : {(const void*)S_in, (const void*)z_in, (const void*)S_out, (const void*)z_out})
+    if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
+  if (S_out) {
+    const void* ro[] = {S_in, z_in};
+    const long long rb[] = {sb, zb};
+    if (overlaps(S_out, sb, z_out, zb)) return LA_ERR_INVALID_ARG;
+    for (int i = 0; i < 2; ++i)
+      if (overlaps(S_out, sb, ro[i], rb[i]) || overlaps(z_out, zb, ro[i], rb[i])) return LA_ERR_INVALID_ARG;
+  }
+  if (BH == 0 || N == 0) {
+    if (BH > 0 && S_out)
+      return status_from_hip(la::copy_state_dispatch(S_in, z_in, S_out, z_out, sb / 4, zb / 4, stream));
+    return LA_OK;
+  }
+  if (!q || !k || !v || !out || !log_gates) return LA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(log_gates))
+    return LA_ERR_INVALID_ARG;
+  const GatedPlan g = make_gated_plan(BH, N, d);
+  {
+    const void* all[] = {q, k, v, log_gates, S_in, z_in};
+    const long long allb[] = {tb, tb, tb, gb, sb, zb};
+    for (int j = 0; j < 6; ++j) {
+      if (overlaps(out, tb, all[j], allb[j])) return LA_ERR_INVALID_ARG;
+      if (S_out && (overlaps(S_out, sb, all[j], allb[j]) || overlaps(z_out, zb, all[j], allb[j])))
+        return LA_ERR_INVALID_ARG;
+    }
+    if (S_out && (overlaps(S_out, sb, out, tb) || overlaps(z_out, zb, out, tb))) return LA_ERR_INVALID_ARG;
+    if (g.ws_bytes > 0) {
+      if (!workspace || workspace_bytes < g.ws_bytes) return LA_ERR_WORKSPACE;
+      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LA_ERR_INVALID_ARG;
+      const void* any[] = {q, k, v, log_gates, S_in, z_in, out, S_out, z_out};
+      const long long anyb[] = {tb, tb, tb, gb, sb, zb, tb, sb, zb};
+      for (int j = 0; j < 9; ++j)
+        if (overlaps(workspace, (long long)g.ws_bytes, any[j], anyb[j])) return LA_ERR_INVALID_ARG;
+    }
+  }
+  const Plan& p = g.p;
+  char* wsb = static_cast<char*>(workspace);
+  la::GatedArgs ga{};
+  la::FwdArgs& a = ga.f;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.BH = (int)BH;
+  a.N = N;
+  a.nchunks = p.nchunks;
+  a.nseg = p.P;
+  a.chunks_per_seg = p.cps;
+  a.nseg_state = p.Ps;
+  a.chunks_per_seg_state = p.cpss;
+  a.run_state_pass = p.state_pass;
+  a.run_scan = p.scan;
+  a.ws = reinterpret_cast<float*>(wsb);
+  a.ws_slots = p.ws_slots;
+  a.state_elems = d * d + d;
+  a.init_from_ws = p.ws_slots > 0;
+  a.S_in = S_in;
+  a.z_in = z_in;
+  a.S_out = S_out;
+  a.z_out = z_out;
+  a.normalize = normalize;
+  a.H = H;
+  ga.log_gates = log_gates;
+  ga.lfac = g.lfac_bytes ? reinterpret_cast<float*>(wsb + g.state_bytes) : nullptr;
+
+  la::ScanArgs s{};
+  s.ws = a.ws;
+  s.ws_slots = p.ws_slots;
+  s.state_elems = a.state_elems;
+  s.BH = (int)BH;
+  s.P = p.P - 1;
+  s.DF = d;
+  s.D = d;
+  s.exclusive = 1;
+  s.write_total = 1;
+  s.S_in = S_in;
+  s.z_in = z_in;
+  s.H = H;
+  s.seg_len = 64 * p.cps;
+  s.lfac = ga.lfac;
+  s.lfac_stride = p.P;
+  const int kfm = feature_map->kind == LA_ELU1 ? la::kElu1 : la::kIdentity;
+  return status_from_hip(la::gated_dispatch(ga, s, d, kfm, dtype, stream));
+}
+
+int la_decode_step_gated(float* S, float* z, const void* q, const void* k, const void* v, const float* log_gate,
+                         void* out, int B, int H, int d, const la_feature_map* feature_map, int normalize, int dtype,
+                         hipStream_t stream) {
+  if (B < 0 || H < 0) return LA_ERR_INVALID_ARG;
+  if (normalize != 0 && normalize != 1) return LA_ERR_INVALID_ARG;
+  if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
+  if (!d_supported(d)) return LA_ERR_UNSUPPORTED;
+  const int dfeat = feature_dim(feature_map, d);
+  if (dfeat < 0) return dfeat;
+  const long long BH = (long long)B * H;
+  if (BH == 0) return LA_OK;
+  if (!log_gate || !aligned16(log_gate)) return LA_ERR_INVALID_ARG;
+  const long long tb = BH * d * (dtype == LA_BF16 ? 2 : 4), sb = BH * dfeat * d * 4, zb = BH * dfeat * 4;
+  if (overlaps(log_gate, zb, out, tb) || overlaps(log_gate, zb, S, sb) || overlaps(log_gate, zb, z, zb))
+    return LA_ERR_INVALID_ARG;
+  // the shared decode path with the per-feature gate
+  if (B < 0 || H < 0) return LA_ERR_INVALID_ARG;
+  if (!S || !z || !q || !k || !v || !out) return LA_ERR_INVALID_ARG;
+  if (!aligned16(S) || !aligned16(z) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return LA_ERR_INVALID_ARG;
+  if (BH > (1LL << 31) - 1) return LA_ERR_UNSUPPORTED;
+  if (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb) || overlaps(out, tb, S, sb) ||
+      overlaps(out, tb, z, zb) || overlaps(S, sb, z, zb) || overlaps(S, sb, q, tb) || overlaps(S, sb, k, tb) ||
+      overlaps(S, sb, v, tb) || overlaps(z, zb, q, tb) || overlaps(z, zb, k, tb) || overlaps(z, zb, v, tb))
+    return LA_ERR_INVALID_ARG;
+  if (feature_map->kind == LA_PERFORMER) {
+    const long long wb = (long long)dfeat * d * 4;
+    if (overlaps(out, tb, feature_map->W, wb) || overlaps(S, sb, feature_map->W, wb) ||
+        overlaps(z, zb, feature_map->W, wb))
+      return LA_ERR_INVALID_ARG;
+  }
+  la::DecodeArgs a{};
+  a.S = S;
+  a.z = z;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.BH = (int)BH;
+  a.normalize = normalize;
+  a.W = feature_map->W;
+  a.H = H;
+  a.lgate = log_gate;
+  return status_from_hip(la::decode_dispatch(a, d, dfeat, feature_map->kind, dtype, stream));
+}
+
+}  // extern "C"

@@ -136,7 +136,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   float dpart = 0.f;
   if (valid) {
     for (int c = t; c < DF; c += SH::TPH) {
-      const float zn = gm * a.z[head * DF + c] + s_phik[hb][c];
+      const float gz = a.lgate ? gm * __builtin_amdgcn_exp2f(a.lgate[head * DF + c] * 1.4426950408889634f) : gm;
+      const float zn = gz * a.z[head * DF + c] + s_phik[hb][c];
       a.z[head * DF + c] = zn;
       dpart += s_phiq[hb][c] * zn;
     }
@@ -152,11 +153,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
     for (int i = 0; i < SH::RPT; ++i) {
       const int r = rg + SH::R * i;
       const float pk = s_phik[hb][r], pq = s_phiq[hb][r];
+      // gated: per-feature gate exp(lgate) of this row of S
+      const float gr = a.lgate ? gm * __builtin_amdgcn_exp2f(a.lgate[head * DF + r] * 1.4426950408889634f) : gm;
       f32x4 s = Sv[i];
-      s[0] = gm * s[0] + pk * v4[0];
-      s[1] = gm * s[1] + pk * v4[1];
-      s[2] = gm * s[2] + pk * v4[2];
-      s[3] = gm * s[3] + pk * v4[3];
+      s[0] = gr * s[0] + pk * v4[0];
+      s[1] = gr * s[1] + pk * v4[1];
+      s[2] = gr * s[2] + pk * v4[2];
+      s[3] = gr * s[3] + pk * v4[3];
       *reinterpret_cast<f32x4*>(Sh + (long long)r * D + 4 * cg) = s;
       num[0] += pq * s[0];
       num[1] += pq * s[1];

@@ -60,6 +60,8 @@ struct ScanArgs {
   const float* gamma;  // decay per head [H] or null: P_{s+1} = gamma^seg_len P_s + L_s
   int H;
   int seg_len;         // tokens per combined segment (all full)
+  const float* lfac;   // gated: per-segment, per-channel log factors [BH][lfac_stride][DF] or null:
+  int lfac_stride;     //   P_{s+1} = diag(exp(lfac_s)) P_s + L_s
 };
 
 struct DecodeArgs {
@@ -74,6 +76,7 @@ struct DecodeArgs {
   const float* W;   // [DF][D] or null
   const float* gamma;  // decay per head [H] or null: S <- gamma S + phi(k) v^T
   int H;
+  const float* lgate;  // gated: log-gate per head and feature [BH][DF] or null: S <- diag(exp(lgate)) S + ...
 };
 
 // Gradient passes (causal; d' = d). Workspace regions: the forward segment
@@ -101,6 +104,15 @@ struct BwdArgs {
   float* rowstats;         // [BH][N][2]: 1 / max(den, eps), d loss / d den
 };
 
+// Gated linear attention (per-token, per-channel log-gates on the feature
+// dimension): the forward's argument block plus the gates and the
+// per-segment total log-gates the state pass writes for the scan.
+struct GatedArgs {
+  FwdArgs f;
+  const float* log_gates;  // [BH][N][D] fp32, natural log of the gates, in [-log 4, 0]
+  float* lfac;             // [BH][f.nseg][D] fp32 (workspace)
+};
+
 struct FmapArgs {
   const void* x;    // [rows][D]
   void* phi;        // [rows][DF]
@@ -113,6 +125,7 @@ hipError_t prefill_dispatch(const FwdArgs& a, const ScanArgs& s, int D, int DF, 
 hipError_t scan_dispatch(const ScanArgs& s, hipStream_t st);
 hipError_t backward_dispatch(const FwdArgs& fa, const ScanArgs& fs, const BwdArgs& b, const ScanArgs& rs, int D,
                              int fmap, int dtype, hipStream_t st);
+hipError_t gated_dispatch(const GatedArgs& g, const ScanArgs& s, int D, int fmap, int dtype, hipStream_t st);
 hipError_t decode_dispatch(const DecodeArgs& a, int D, int DF, int fmap, int dtype, hipStream_t st);
 hipError_t fmap_dispatch(const FmapArgs& a, int D, int DF, int fmap, int in_dtype, int out_dtype, hipStream_t st);
 hipError_t copy_state_dispatch(const float* S_in, const float* z_in, float* S_out, float* z_out, long long nS,

@@ -545,10 +545,21 @@ __global__ __launch_bounds__(256) void carry_scan_kernel(ScanArgs a) {
     for (int j = 0; j < kScanBatch; ++j) {
       if (j < cnt) {
         if (a.exclusive) *reinterpret_cast<f32x4*>(col + (p0 + j) * st) = run;
-        run[0] = g * run[0] + t[j][0];
-        run[1] = g * run[1] + t[j][1];
-        run[2] = g * run[2] + t[j][2];
-        run[3] = g * run[3] + t[j][3];
+        f32x4 gf = {g, g, g, g};
+        if (a.lfac) {  // gated: per-channel factor of the combined segment (row of S, or entry of z)
+          const float* lf = a.lfac + ((long long)bh * a.lfac_stride + p0 + j) * a.DF;
+          if (e < sdd) {
+            const float x = gpow(lf[e / a.D] * 1.4426950408889634f, 1.f);
+            gf = f32x4{x, x, x, x};
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) gf[u] = gpow(lf[e - sdd + u] * 1.4426950408889634f, 1.f);
+          }
+        }
+        run[0] = gf[0] * run[0] + t[j][0];
+        run[1] = gf[1] * run[1] + t[j][1];
+        run[2] = gf[2] * run[2] + t[j][2];
+        run[3] = gf[3] * run[3] + t[j][3];
       }
     }
   }

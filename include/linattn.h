@@ -203,6 +203,43 @@ int la_backward(const void* q, const void* k, const void* v, const void* dout, v
                 const float* z_in, const float* dS_out, const float* dz_out, float* dS_in, float* dz_in,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Bytes of device workspace that la_forward_gated needs (0 for invalid
+ * arguments or when none is needed).
+ */
+size_t la_forward_gated_workspace_size(int B, int H, int N, int d, const la_feature_map* feature_map);
+
+/*
+ * Gated linear attention, causal ("Linear Attention", "Variantes y
+ * extensiones", GLA item: the scalar decay replaced by a data-dependent
+ * gate). Reading: a per-token, per-feature gate alpha_t on the feature
+ * dimension,
+ *   S_t = diag(alpha_t) S_{t-1} + phi(k_t) v_t^T,  z_t = alpha_t * z_{t-1} + phi(k_t),
+ *   out_t = phi(q_t)^T S_t / max(phi(q_t).z_t, 1e-6)  (normalize = 0: numerator only),
+ * evaluated blockwise ("Entrenamiento: forma paralela").
+ *   log_gates in: DEVICE pointer, [B][H][N][d] fp32, log(alpha) in [-log 4, 0]
+ *             (alpha in [1/4, 1]; the kernels scale rows of a 64-token chunk by
+ *             up to alpha^-32 per feature). Values are not checked on the host.
+ *   S_in, z_in enter output t through feature f with the product of the gates
+ *             of tokens 0..t; S_out, z_out are the gated state after the last token.
+ * elu+1 and the identity map; random features return LA_ERR_UNSUPPORTED.
+ * Everything else as la_forward with causal = 1; the workspace is
+ * la_forward_gated_workspace_size() bytes.
+ */
+int la_forward_gated(const void* q, const void* k, const void* v, const float* log_gates, void* out, int B, int H,
+                     int N, int d, const la_feature_map* feature_map, int normalize, int dtype, const float* S_in,
+                     const float* z_in, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/*
+ * la_decode_step with a per-feature gate: S <- diag(exp(log_gate)) S + phi(k) v^T,
+ * z <- exp(log_gate) * z + phi(k), then the readout. log_gate: DEVICE pointer,
+ * [B][H][d'] fp32 (any value <= 0 is valid here). All maps.
+ */
+int la_decode_step_gated(float* S, float* z, const void* q, const void* k, const void* v, const float* log_gate,
+                         void* out, int B, int H, int d, const la_feature_map* feature_map, int normalize, int dtype,
+                         hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,6 +18,8 @@ dimension d per head, queries/keys/values drawn i.i.d. Gaussian):
   length of an independent N(0, I_d) vector, then rounded to bf16 values.
 * ``decode_tokens``: per-sequence / per-step token blocks seeded by
   ``default_rng([base, index])`` so that any subset can be regenerated alone.
+* ``log_gates``: natural logs of gates alpha ~ U(lo, 1), float32, for the
+  gated (GLA) variant; lo = 1/4 is the smallest gate the kernels accept.
 """
 
 from __future__ import annotations
@@ -34,6 +36,7 @@ __all__ = [
     "gaussian_qkv",
     "performer_W",
     "decode_tokens",
+    "log_gates",
     "WORKLOADS",
 ]
 
@@ -109,6 +112,11 @@ def decode_tokens(base_seed: int, index: int, shape, scale: float = 1.0, bf16: b
     k = gaussian(rng, shape, scale, bf16)
     v = gaussian(rng, shape, scale, bf16)
     return q, k, v
+
+
+def log_gates(rng: np.random.Generator, shape, lo: float = 0.25) -> np.ndarray:
+    """float32 log(alpha), alpha ~ U(lo, 1)."""
+    return np.log(rng.uniform(lo, 1.0, shape)).astype(np.float32)
 
 
 # Named synthetic workloads.  Every entry is plain data: shapes, seeds and the

@@ -202,3 +202,26 @@ def test_backward_workspace_plan():
     assert lib.la_backward_workspace_size(1, 1, 0, 64, ctypes.byref(ELU)) == 0
     assert lib.la_backward_workspace_size(1, 1, 64, 48, ctypes.byref(ELU)) == 0
     assert lib.la_backward_workspace_size(1, 1, 64, 64, ctypes.byref(la_feature_map(la.LA_PERFORMER, 64, FAKE))) == 0
+
+
+def test_gated_entry_points_validate_before_launch():
+    ident = la_feature_map(la.LA_IDENTITY, 0, None)
+    G = FAKE2 * 8
+
+    def fg(lg=G, fm=ELU, d=64, N=128, ws=FAKE2 * 4, wsb=1 << 30, out=FAKE2):
+        return lib.la_forward_gated(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, lg, out, 1, 1, N, d,
+                                    ctypes.byref(fm), 1, la.LA_BF16, None, None, None, None, ws, wsb, None)
+    assert fg(lg=None) == la.LA_ERR_INVALID_ARG
+    assert fg(lg=G + 4) == la.LA_ERR_INVALID_ARG                          # misaligned gates
+    assert fg(d=48) == la.LA_ERR_UNSUPPORTED
+    assert fg(fm=la_feature_map(la.LA_PERFORMER, 64, FAKE2 * 9)) == la.LA_ERR_UNSUPPORTED
+    assert fg(out=G) == la.LA_ERR_INVALID_ARG                             # out overlaps the gates
+    assert fg(N=65536, ws=None) == la.LA_ERR_WORKSPACE
+    assert fg(N=0) == la.LA_OK
+    assert lib.la_forward_gated_workspace_size(1, 1, 65536, 128, ctypes.byref(ELU)) > 0
+    assert lib.la_forward_gated_workspace_size(1, 1, 64, 48, ctypes.byref(ELU)) == 0
+    assert lib.la_forward_gated_workspace_size(1, 2, 4096, 64, ctypes.byref(ident)) == \
+        lib.la_forward_gated_workspace_size(1, 2, 4096, 64, ctypes.byref(ELU))
+    st = lib.la_decode_step_gated(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000, None,
+                                  FAKE + 0x500000, 1, 1, 64, ctypes.byref(ELU), 1, la.LA_BF16, None)
+    assert st == la.LA_ERR_INVALID_ARG                                    # gate missing
