@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--backward-steps", type=int, default=20)
     p.add_argument("--no-backward", action="store_true")
+    p.add_argument("--gated-steps", type=int, default=20)
+    p.add_argument("--no-gated", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="time budget of the oracle's prefill sample (whole heads; the decode sample gets half)")
@@ -201,6 +203,39 @@ def main():
         log(f"backward: {bwall*1e6:.1f} us/call ({bwall*1e3/ms_step:.2f}x the forward)")
         del tdy, gq, gk, gv, bws
 
+    # ---------------- gated linear attention on the same workload ----------------
+    gated = None
+    if not args.no_gated:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(W["seed"] + 313)
+        tlg = torch.log(torch.rand((B, H, N, d), generator=gen, device=dev) * 0.75 + 0.25)  # alpha ~ U(1/4, 1)
+        gws = torch.empty(max(la.la_forward_gated_workspace_size(B, H, N, d), 256), dtype=torch.uint8, device=dev)
+
+        def gfwd():
+            la.la_forward_gated(tq, tk, tv, tlg, normalize=True, out=out, workspace=gws)
+
+        for _ in range(10):
+            gfwd()
+        torch.cuda.synchronize()
+        log(f"gated: timing {args.gated_steps} calls")
+        t0 = time.perf_counter()
+        for _ in range(args.gated_steps):
+            gfwd()
+        torch.cuda.synchronize()
+        gwall = (time.perf_counter() - t0) / args.gated_steps
+        g_bytes = head_tokens * (4 * d * 2 + d * 4)  # q, k, v read + out written (bf16), log-gates read (fp32)
+        gated = {
+            "metric": "causal gated linear-attn prefill tokens/s (per-channel gates)",
+            "value": tokens / gwall, "unit": "tokens/s", "us_per_call": round(gwall * 1e6, 1),
+            "steps": args.gated_steps,
+            "config": {"workload": "prefill_b1h16n65536d128", "batch": B, "heads": H, "seq_len": N, "d": d,
+                       "feature_map": "elu1", "normalize": True, "gates": "log U(1/4, 1), fp32, per token and channel"},
+            "whole_op": {"bytes": g_bytes, "achieved_gbs": round(g_bytes / gwall / 1e9, 1),
+                         "frac_hbm": round(g_bytes / gwall / 1e9 / HBM_PEAK_GBS, 4)},
+        }
+        log(f"gated: {gwall*1e6:.1f} us/call")
+        del tlg, gws
+
     del tq, tk, tv, out, ws
     torch.cuda.empty_cache()
     prefill_sources = ["la_prefill.hip", "la_device.h", "la_kernels.h"]
@@ -352,6 +387,7 @@ def main():
                              "head_tokens_per_s": head_tokens / (ms_step * 1e-3)},
         "decode": decode,
         "backward": backward,
+        "gated": gated,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result))

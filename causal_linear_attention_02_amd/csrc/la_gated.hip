@@ -60,28 +60,36 @@ __device__ __forceinline__ float colsum_lanes(float x) {
   return x;
 }
 
-// In-chunk prefix of the log-gates: NT threads, D channels, NT/D threads per
-// channel each owning 64*D/NT consecutive rows. Writes lam[r][f] (fp32) for
-// the 64 rows of the chunk; rows past the end of the sequence carry gate 0
-// (the buffer range check returns 0), so lam stays at its last value.
-// tot: NT/D x D scratch. Two barriers inside.
+// In-chunk prefix of the log-gates: lam[r][f] = lg_0f + ... + lg_rf for the
+// 64 rows of the chunk (fp32). The gate tile is loaded in 16-byte row pieces
+// into lam; then NT/D threads per channel scan it in place, each over
+// 64*D/NT consecutive rows, and add the totals of the rows before theirs.
+// Rows past the end of the sequence load as 0 (buffer range check), so lam
+// stays at its last value there. tot: NT/D x D scratch. Three barriers.
 template <int D, int NT>
 __device__ __forceinline__ void gate_prefix(const float* lg, long long row0, int valid, float* lam, float* tot) {
-  constexpr int NQ = NT / D, RPQ = 64 / NQ;
+  constexpr int NQ = NT / D, RPQ = 64 / NQ, NPC = 16 * D / NT;  // pieces of 4 per thread
   const int t = threadIdx.x, col = t % D, qt = t / D;
   const auto R = make_rsrc(lg + row0 * D, (unsigned)(valid * D * 4));
-  float x[RPQ];
+  f32x4 p[NPC];
 #pragma unroll
-  for (int r = 0; r < RPQ; ++r)
-    x[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(R, ((qt * RPQ + r) * D + col) * 4, 0, 0));
+  for (int i = 0; i < NPC; ++i) p[i] = __builtin_bit_cast(f32x4, buf_load16(R, (t + NT * i) * 16));
 #pragma unroll
-  for (int r = 1; r < RPQ; ++r) x[r] += x[r - 1];
-  tot[qt * D + col] = x[RPQ - 1];
+  for (int i = 0; i < NPC; ++i) *reinterpret_cast<f32x4*>(lam + 4 * (t + NT * i)) = p[i];
+  __syncthreads();
+  float run = 0.f;
+  for (int r = 0; r < RPQ; ++r) {
+    float* x = lam + (qt * RPQ + r) * D + col;
+    run += *x;
+    *x = run;
+  }
+  tot[qt * D + col] = run;
   __syncthreads();
   float off = 0.f;
   for (int q2 = 0; q2 < qt; ++q2) off += tot[q2 * D + col];
-#pragma unroll
-  for (int r = 0; r < RPQ; ++r) lam[(qt * RPQ + r) * D + col] = x[r] + off;
+  if (qt > 0) {
+    for (int r = 0; r < RPQ; ++r) lam[(qt * RPQ + r) * D + col] += off;
+  }
   __syncthreads();
 }
 
@@ -101,6 +109,7 @@ __global__ __launch_bounds__(D * 2) void gla_state_kernel(GatedArgs g) {
   __shared__ __attribute__((aligned(16))) float lam[64 * D];
   __shared__ float tot[(NT / D) * D];
   __shared__ float zsum[NW][D];
+  __shared__ float f63[D];  // per channel exp(lam_63)
   uint8_t* sK = smem;
   uint8_t* sV = smem + TB;
   const FwdArgs& a = g.f;
@@ -139,7 +148,10 @@ __global__ __launch_bounds__(D * 2) void gla_state_kernel(GatedArgs g) {
       l63[e] = lam[63 * D + col + e];
       zr[e] *= exp_nat(l63[e]);
     }
-    if (t < D) ltot += lam[63 * D + t];
+    if (t < D) {
+      ltot += lam[63 * D + t];
+      f63[t] = exp_nat(lam[63 * D + t]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = t / RL + 16 * i;
@@ -158,7 +170,7 @@ __global__ __launch_bounds__(D * 2) void gla_state_kernel(GatedArgs g) {
 #pragma unroll
     for (int fb = 0; fb < NW; ++fb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S[fb][r] *= exp_nat(lam[63 * D + 32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)]);
+      for (int r = 0; r < 16; ++r) S[fb][r] *= f63[32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const Frag vf = Ops<OP>::template load_cols<RB>(sV, 16 * kb, 32 * w);
@@ -204,6 +216,7 @@ __global__ __launch_bounds__(D * 4) void gla_output_kernel(GatedArgs g) {
   __shared__ float tot[(NT / D) * D];
   __shared__ float zpart[NWAVE][D];
   __shared__ __attribute__((aligned(16))) float zc[D];  // exp(lam_c) z of the state entering the chunk
+  __shared__ float fc[D], fe[D];                         // per channel: exp(lam_c), exp(lam_63 - lam_c)
   uint8_t* sQ = smem;
   uint8_t* sK = smem + TB;
   uint8_t* sV = smem + 2 * TB;
@@ -269,9 +282,9 @@ __global__ __launch_bounds__(D * 4) void gla_output_kernel(GatedArgs g) {
       In8<IN>::to_f32(rk[i], xk);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float d = lam[row * D + col + e] - lc[e];
-        xq[e] = gphi<FM>(xq[e]) * exp_nat(d);
-        xk[e] = row < valid ? gphi<FM>(xk[e]) * exp_nat(-d) : 0.f;
+        const float f = exp_nat(lam[row * D + col + e] - lc[e]);
+        xq[e] = gphi<FM>(xq[e]) * f;
+        xk[e] = row < valid ? gphi<FM>(xk[e]) * __builtin_amdgcn_rcpf(f) : 0.f;
         cs[e] += xk[e];
       }
       Ops<OP>::template store8<RB>(sQ, row, col, xq);
@@ -292,16 +305,19 @@ __global__ __launch_bounds__(D * 4) void gla_output_kernel(GatedArgs g) {
 #pragma unroll
       for (int ww = 0; ww < NWAVE; ++ww) s += zpart[ww][t];
       const float lct = lam[kCenter * D + t];
-      const float zcar = exp_nat(lct) * zreg;
+      const float ec = exp_nat(lct), ee = exp_nat(lam[63 * D + t] - lct);
+      fc[t] = ec;
+      fe[t] = ee;
+      const float zcar = ec * zreg;
       zc[t] = zcar;
-      zreg = exp_nat(lam[63 * D + t] - lct) * (zcar + s);
+      zreg = ee * (zcar + s);
     }
+    __syncthreads();
     // S' = diag(exp(lam_c)) S
 #pragma unroll
     for (int fb = 0; fb < NW; ++fb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S[fb][r] *= exp_nat(lam[kCenter * D + 32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)]);
-    __syncthreads();
+      for (int r = 0; r < 16; ++r) S[fb][r] *= fc[32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)];
 
     // scores A[j][i] for the wave's query rows (key blocks 0..ib), numerator
     f32x16 num = {};
@@ -310,7 +326,8 @@ __global__ __launch_bounds__(D * 4) void gla_output_kernel(GatedArgs g) {
     for (int jb = 0; jb < 2; ++jb) {
       if (jb > ib) break;
       f32x16 A = {};
-#pragma unroll
+      // partial unroll: full unrolling hoists every fragment load and spills
+#pragma unroll 2
       for (int kb = 0; kb < D / 16; ++kb)
         Ops<OP>::mma(A, Ops<OP>::template load_rows<RB>(sK, 32 * jb, 16 * kb),
                      Ops<OP>::template load_rows<RB>(sQ, 32 * ib, 16 * kb));
@@ -376,10 +393,7 @@ __global__ __launch_bounds__(D * 4) void gla_output_kernel(GatedArgs g) {
 #pragma unroll
     for (int fb = 0; fb < NW; ++fb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int f = 32 * fb + 8 * (r >> 2) + 4 * h + (r & 3);
-        S[fb][r] *= exp_nat(lam[63 * D + f] - lam[kCenter * D + f]);
-      }
+      for (int r = 0; r < 16; ++r) S[fb][r] *= fe[32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)];
     __syncthreads();
   }
   if (a.S_out && seg == a.nseg - 1) {
