@@ -42,6 +42,7 @@ def parse():
     p.add_argument("--no-backward", action="store_true")
     p.add_argument("--gated-steps", type=int, default=20)
     p.add_argument("--no-gated", action="store_true")
+    p.add_argument("--no-variants", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="time budget of the oracle's prefill sample (whole heads; the decode sample gets half)")
@@ -236,6 +237,31 @@ def main():
         log(f"gated: {gwall*1e6:.1f} us/call")
         del tlg, gws
 
+    # ---------------- decay and identity-map forwards on the same workload ----------------
+    variants = None
+    if not args.no_variants:
+        variants = {}
+        gam = torch.linspace(0.9, 0.999, H, device=dev, dtype=torch.float32)  # one decay per head
+        runs = {
+            "decay": lambda: la.la_forward_decay(tq, tk, tv, gam, normalize=True, out=out, workspace=ws),
+            "identity_map": lambda: la.la_forward(tq, tk, tv, feature_map="identity", normalize=False, out=out,
+                                                  workspace=ws),
+        }
+        for name, fn in runs.items():
+            for _ in range(20):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(20):
+                fn()
+            torch.cuda.synchronize()
+            vw = (time.perf_counter() - t0) / 20
+            variants[name] = {"us_per_call": round(vw * 1e6, 1), "tokens_per_s": tokens / vw,
+                              "whole_op_frac_hbm": round(alg_bytes / vw / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"{name}: {vw*1e6:.1f} us/call")
+        variants["note"] = ("same workload and bytes as the headline prefill; decay: gamma per head "
+                            "0.9..0.999; identity map: numerator only")
+
     del tq, tk, tv, out, ws
     torch.cuda.empty_cache()
     prefill_sources = ["la_prefill.hip", "la_device.h", "la_kernels.h"]
@@ -388,6 +414,7 @@ def main():
         "decode": decode,
         "backward": backward,
         "gated": gated,
+        "variants": variants,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result))

@@ -712,7 +712,6 @@ int la_decode_step_gated(float* S, float* z, const void* q, const void* k, const
   if (overlaps(log_gate, zb, out, tb) || overlaps(log_gate, zb, S, sb) || overlaps(log_gate, zb, z, zb))
     return LA_ERR_INVALID_ARG;
   // the shared decode path with the per-feature gate
-  if (B < 0 || H < 0) return LA_ERR_INVALID_ARG;
   if (!S || !z || !q || !k || !v || !out) return LA_ERR_INVALID_ARG;
   if (!aligned16(S) || !aligned16(z) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return LA_ERR_INVALID_ARG;

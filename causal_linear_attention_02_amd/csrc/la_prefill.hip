@@ -45,6 +45,11 @@ struct Stage {
   static_assert(NP % RLF == 0 && 64 % RSF == 0 && NQ <= 16, "staging geometry");
   // register sets for the loads in flight (prefetch distance NSET - 1)
   static constexpr int NSET = NQ <= 4 ? 3 : 2;
+  // the decay variants keep one set fewer: their scaling needs registers
+  // (with a third set the decay state pass ran at half the occupancy and
+  // the decay output pass spilled more)
+  template <bool DECAY>
+  static constexpr int nset() { return DECAY ? 2 : NSET; }
 };
 
 template <int D, int DF, typename IN>
@@ -351,7 +356,7 @@ __device__ __forceinline__ void store_state_tiles(const f32x16 (&S)[DF / 32], fl
 // grid = (BH, P), block = 2*D threads.
 // ---------------------------------------------------------------------------
 template <int D, int DF, typename OP, typename IN, int FM, bool DECAY, bool HILO = false>
-__global__ __launch_bounds__(D * 2) void state_pass_kernel(FwdArgs a) {
+__global__ __launch_bounds__(D * 2, DECAY ? 2 : 1) void state_pass_kernel(FwdArgs a) {
   using Frag = typename Ops<OP>::frag;
   using G = Stage<D, DF>;
   static_assert(!HILO || (sizeof(OP) == 2 && !DECAY && DF == D), "hi + lo keys: bf16 operands, no decay, d' = d");
@@ -359,6 +364,7 @@ __global__ __launch_bounds__(D * 2) void state_pass_kernel(FwdArgs a) {
   constexpr int RBV = D * Ops<OP>::kBytes;
   constexpr int KB = 64 * RBF, VB = 64 * RBV, BUF = KB + VB + (HILO ? KB : 0);
   constexpr int NW = D / 32;
+  constexpr int NS = G::template nset<DECAY>();  // register sets in the load rotation
   // two staged chunks when they fit; otherwise one, with an extra barrier
   constexpr int NB = 2 * BUF + NW * DF * 4 <= 160 * 1024 ? 2 : 1;
   __shared__ __attribute__((aligned(16))) uint8_t smem[NB * BUF];
@@ -455,15 +461,15 @@ __global__ __launch_bounds__(D * 2) void state_pass_kernel(FwdArgs a) {
   // a multiple of NSET); iterations past the segment multiply nothing and
   // only retire their (empty) loads.
   auto iter = [&](int m, Pref<D, DF, IN>& ld, Pref<D, DF, IN>& st) {
-    load(ld, m + G::NSET);
+    load(ld, m + NS);
     if (m < nch) mult(m);
     if constexpr (NB == 1) __syncthreads();
     if (m + 1 < nch) stage(st, m + 1);
     else retire<D, DF, IN, false, true>(st);
     __syncthreads();
   };
-  const int nround = (nch + G::NSET - 1) / G::NSET * G::NSET;
-  if constexpr (G::NSET == 3) {
+  const int nround = (nch + NS - 1) / NS * NS;
+  if constexpr (NS == 3) {
     Pref<D, DF, IN> pA, pB, pC;
     load(pA, 0);
     load(pB, 1);
@@ -618,8 +624,9 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
   // first NSET-1 steps (negative) only issue the loads of chunks 0..NSET-2, so
   // the loop is entered with no loads in flight and the wait counts inside it
   // follow the steady state alone. Steps past n + LAST only retire empty loads.
-  constexpr int IT0 = -(Stage<D, DF>::NSET - 1);
-  const int itend = IT0 + (n + LAST + 1 - IT0 + Stage<D, DF>::NSET - 1) / Stage<D, DF>::NSET * Stage<D, DF>::NSET;
+  constexpr int NS = Stage<D, DF>::template nset<DECAY>();
+  constexpr int IT0 = -(NS - 1);
+  const int itend = IT0 + (n + LAST + 1 - IT0 + NS - 1) / NS * NS;
   const long long base = (long long)bh * a.N;
   const IN* q = static_cast<const IN*>(a.q);
   const IN* k = static_cast<const IN*>(a.k);
@@ -680,7 +687,7 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
       const bool stg = it >= 0 && it < n;
       const int cs_ = c0 + it;                       // chunk staged in this step
       const int vs = stg ? min(64, a.N - 64 * cs_) : 0;
-      const int ln = it + G::NSET - 1;               // chunk loaded in this step
+      const int ln = it + NS - 1;                    // chunk loaded in this step
       const int cl = c0 + ln;
       const ChunkRsrc rl = chunk_rsrc<D, DF, IN>(q, k, v, base + 64LL * min(cl, a.nchunks - 1),
                                                  ln < n ? min(64, a.N - 64 * cl) : 0);
@@ -789,7 +796,7 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
     // whole rotations of the register sets; the steps past n + LAST only
     // retire their empty loads (the consumers run as many barriers)
     // chunk c is held in the set that step c - NSET + 1 loads and step c stages
-    if constexpr (G::NSET == 3) {
+    if constexpr (NS == 3) {
       Pref<D, DF, IN> pA, pB, pC;
       for (int it = IT0; it < itend; it += 3) {
         pstep(it, pA, pC);
@@ -859,6 +866,7 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
           Ops<OP>::mma(num0, sf, bq0);
           Ops<OP>::mma(num1, sf, bq1);
         }
+
         // causal mask on the diagonal tiles (keep j <= i) and the in-chunk
         // part of the denominator
 #pragma unroll
