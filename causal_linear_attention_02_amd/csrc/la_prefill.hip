@@ -365,8 +365,10 @@ __global__ __launch_bounds__(D * 2, DECAY ? 2 : 1) void state_pass_kernel(FwdArg
   constexpr int KB = 64 * RBF, VB = 64 * RBV, BUF = KB + VB + (HILO ? KB : 0);
   constexpr int NW = D / 32;
   constexpr int NS = G::template nset<DECAY>();  // register sets in the load rotation
-  // two staged chunks when they fit; otherwise one, with an extra barrier
-  constexpr int NB = 2 * BUF + NW * DF * 4 <= 160 * 1024 ? 2 : 1;
+  // two staged chunks when they fit; otherwise one, with an extra barrier.
+  // The hi + lo-keys variant stages one: two of its larger buffers would
+  // leave room for one workgroup per CU, one buffer for two.
+  constexpr int NB = (!HILO && 2 * BUF + NW * DF * 4 <= 160 * 1024) ? 2 : 1;
   __shared__ __attribute__((aligned(16))) uint8_t smem[NB * BUF];
   __shared__ float zsum[NW][DF];
 
