@@ -23,7 +23,7 @@ __all__ = [
     "la_feature_map", "lib", "library_path", "LinAttnError",
     "la_version", "la_status_string", "la_forward_workspace_size", "la_forward", "la_forward_ex",
     "la_decode_step", "la_feature_map_apply", "feature_dim", "la_forward_decay", "la_decode_step_decay",
-    "la_backward_workspace_size", "la_backward", "la_forward_gated_workspace_size", "la_forward_gated",
+    "la_backward_workspace_size", "la_backward", "la_backward_decay", "la_forward_gated_workspace_size", "la_forward_gated",
     "la_decode_step_gated",
 ]
 
@@ -51,7 +51,7 @@ def _load():
     if not os.path.exists(library_path):
         raise ImportError(
             f"{library_path} is missing: build the HIP library first "
-            "(python -m causal_linear_attention_02_amd.build)")
+            "(python causal_linear_attention_02_amd/build.py)")
     L = ctypes.CDLL(library_path)
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     fmp = ctypes.POINTER(la_feature_map)
@@ -74,6 +74,9 @@ def _load():
     L.la_backward_workspace_size.restype = sz
     L.la_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, fmp, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.la_backward.restype = i
+    L.la_backward_decay.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, fmp, vp, i, i, vp, vp, vp, vp, vp, vp, vp,
+                                    sz, vp]
+    L.la_backward_decay.restype = i
     L.la_forward_gated_workspace_size.argtypes = [i, i, i, i, fmp]
     L.la_forward_gated_workspace_size.restype = sz
     L.la_forward_gated.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, fmp, i, i, vp, vp, vp, vp, vp, sz, vp]
@@ -303,6 +306,23 @@ def la_backward_workspace_size(B, H, N, d, feature_map="elu1") -> int:
 def la_backward(q, k, v, dout, *, feature_map="elu1", normalize=True, S_in=None, z_in=None, dS_out=None,
                 dz_out=None, return_state_grad=False, dq=None, dk=None, dv=None, workspace=None, stream=None):
     """Gradients of causal la_forward: returns (dq, dk, dv), or (dq, dk, dv, dS_in, dz_in)."""
+    return _backward(q, k, v, dout, None, feature_map, normalize, S_in, z_in, dS_out, dz_out, return_state_grad,
+                     dq, dk, dv, workspace, stream)
+
+
+def la_backward_decay(q, k, v, dout, gamma, *, feature_map="elu1", normalize=True, S_in=None, z_in=None,
+                      dS_out=None, dz_out=None, return_state_grad=False, dq=None, dk=None, dv=None, workspace=None,
+                      stream=None):
+    """Gradients of la_forward_decay (per-head decay gamma [H]): (dq, dk, dv[, dS_in, dz_in])."""
+    if q.dim() != 4:
+        raise ValueError("q, k, v, dout must share one [B, H, N, d] shape")
+    g = _gamma(gamma, q.shape[1], q.device)
+    return _backward(q, k, v, dout, g, feature_map, normalize, S_in, z_in, dS_out, dz_out, return_state_grad,
+                     dq, dk, dv, workspace, stream)
+
+
+def _backward(q, k, v, dout, gamma, feature_map, normalize, S_in, z_in, dS_out, dz_out, return_state_grad, dq, dk,
+              dv, workspace, stream):
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or dout.shape != q.shape:
         raise ValueError("q, k, v, dout must share one [B, H, N, d] shape")
     B, H, N, d = q.shape
@@ -321,10 +341,17 @@ def la_backward(q, k, v, dout, *, feature_map="elu1", normalize=True, S_in=None,
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d,
-                         ctypes.byref(fm), int(normalize), dt, _ptr(S_in), _ptr(z_in), _ptr(dS_out), _ptr(dz_out),
-                         _ptr(dS_in), _ptr(dz_in), _ptr(workspace), ws_bytes, _stream(stream))
-    _check(st, "la_backward")
+    if gamma is None:
+        st = lib.la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d,
+                             ctypes.byref(fm), int(normalize), dt, _ptr(S_in), _ptr(z_in), _ptr(dS_out),
+                             _ptr(dz_out), _ptr(dS_in), _ptr(dz_in), _ptr(workspace), ws_bytes, _stream(stream))
+        _check(st, "la_backward")
+    else:
+        st = lib.la_backward_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d,
+                                   ctypes.byref(fm), _ptr(gamma), int(normalize), dt, _ptr(S_in), _ptr(z_in),
+                                   _ptr(dS_out), _ptr(dz_out), _ptr(dS_in), _ptr(dz_in), _ptr(workspace), ws_bytes,
+                                   _stream(stream))
+        _check(st, "la_backward_decay")
     return (dq, dk, dv, dS_in, dz_in) if return_state_grad else (dq, dk, dv)
 
 

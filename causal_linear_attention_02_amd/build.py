@@ -4,7 +4,7 @@ Every source under csrc/ is compiled with hipcc for gfx950 only; packed fp32
 VALU instructions are disabled for all device code. The shared library lands
 next to this file, where the Python binding loads it.
 
-Usage: python -m causal_linear_attention_02_amd.build   (or build() from Python)
+Usage: python causal_linear_attention_02_amd/build.py   (or __graft_entry__.build())
 """
 
 from __future__ import annotations

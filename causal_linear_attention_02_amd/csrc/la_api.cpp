@@ -430,11 +430,17 @@ size_t la_backward_workspace_size(int B, int H, int N, int d, const la_feature_m
   return make_bwd_plan((long long)B * H, N, d).ws_bytes;
 }
 
-int la_backward(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv, int B,
-                int H, int N, int d, const la_feature_map* feature_map, int normalize, int dtype, const float* S_in,
-                const float* z_in, const float* dS_out, const float* dz_out, float* dS_in, float* dz_in,
-                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The gradient passes; gamma (device, [H]) is the per-head decay or null.
+int backward_impl(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv, int B,
+                  int H, int N, int d, const la_feature_map* feature_map, int normalize, int dtype, const float* S_in,
+                  const float* z_in, const float* dS_out, const float* dz_out, float* dS_in, float* dz_in,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream, const float* gamma) {
   if (B < 0 || H < 0 || N < 0) return LA_ERR_INVALID_ARG;
+  if (gamma && (reinterpret_cast<uintptr_t>(gamma) & 3u) != 0) return LA_ERR_INVALID_ARG;
   if (normalize != 0 && normalize != 1) return LA_ERR_INVALID_ARG;
   if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
   if ((S_in == nullptr) != (z_in == nullptr) || (dS_out == nullptr) != (dz_out == nullptr) ||
@@ -473,13 +479,16 @@ int la_backward(const void* q, const void* k, const void* v, const void* dout, v
     const long long wrb[] = {tb, tb, tb, sb, zb};
     const void* all[] = {q, k, v, dout, S_in, z_in, dS_out, dz_out, dq, dk, dv, dS_in, dz_in};
     const long long allb[] = {tb, tb, tb, tb, sb, zb, sb, zb, tb, tb, tb, sb, zb};
-    for (int i = 0; i < 5; ++i)
+    for (int i = 0; i < 5; ++i) {
       for (int j = 0; j < 13; ++j)
         if (all[j] != wr[i] && overlaps(wr[i], wrb[i], all[j], allb[j])) return LA_ERR_INVALID_ARG;
+      if (gamma && overlaps(wr[i], wrb[i], gamma, 4LL * H)) return LA_ERR_INVALID_ARG;
+    }
     if (!workspace || workspace_bytes < p.ws_bytes) return LA_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LA_ERR_INVALID_ARG;
     for (int j = 0; j < 13; ++j)
       if (overlaps(workspace, (long long)p.ws_bytes, all[j], allb[j])) return LA_ERR_INVALID_ARG;
+    if (gamma && overlaps(workspace, (long long)p.ws_bytes, gamma, 4LL * H)) return LA_ERR_INVALID_ARG;
   }
   char* wsb = static_cast<char*>(workspace);
   float* ws_fwd = reinterpret_cast<float*>(wsb);
@@ -508,6 +517,7 @@ int la_backward(const void* q, const void* k, const void* v, const void* dout, v
   fa.z_in = z_in;
   fa.normalize = normalize;
   fa.H = H;
+  fa.gamma = gamma;
   la::ScanArgs fsa{};
   fsa.ws = ws_fwd;
   fsa.ws_slots = p.P;
@@ -522,6 +532,7 @@ int la_backward(const void* q, const void* k, const void* v, const void* dout, v
   fsa.z_in = z_in;
   fsa.H = H;
   fsa.seg_len = 64 * p.cps;
+  fsa.gamma = gamma;
 
   la::BwdArgs b{};
   b.q = q;
@@ -545,6 +556,10 @@ int la_backward(const void* q, const void* k, const void* v, const void* dout, v
   b.ws_rev = ws_rev;
   b.state_elems = state_elems;
   b.rowstats = rowstats;
+  b.gamma = gamma;
+  b.H = H;
+  b.dS_out = dS_out;
+  b.dz_out = dz_out;
 
   // suffix sums of the segments' gradient states, seeded with dS_out / dz_out
   la::ScanArgs rs{};
@@ -557,14 +572,38 @@ int la_backward(const void* q, const void* k, const void* v, const void* dout, v
   rs.D = d;
   rs.exclusive = 1;
   rs.write_total = 1;
-  rs.S_in = dS_out;
-  rs.z_in = dz_out;
+  // with decay the final-state cotangents enter through the gradient passes
+  // (the last segment may be partial, so a whole-segment factor would not fit)
+  rs.S_in = gamma ? nullptr : dS_out;
+  rs.z_in = gamma ? nullptr : dz_out;
   rs.S_out = dS_in;
   rs.z_out = dz_in;
   rs.H = H;
   rs.seg_len = 64 * p.cps;
+  rs.gamma = gamma;
   const int kfm = feature_map->kind == LA_ELU1 ? la::kElu1 : la::kIdentity;
-  return status_from_hip(la::backward_dispatch(fa, fsa, b, rs, d, kfm, dtype, stream));
+  return status_from_hip(la::backward_dispatch(fa, fsa, b, rs, d, kfm, dtype, gamma != nullptr, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int la_backward(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv, int B,
+                int H, int N, int d, const la_feature_map* feature_map, int normalize, int dtype, const float* S_in,
+                const float* z_in, const float* dS_out, const float* dz_out, float* dS_in, float* dz_in,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return backward_impl(q, k, v, dout, dq, dk, dv, B, H, N, d, feature_map, normalize, dtype, S_in, z_in, dS_out,
+                       dz_out, dS_in, dz_in, workspace, workspace_bytes, stream, nullptr);
+}
+
+int la_backward_decay(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
+                      int B, int H, int N, int d, const la_feature_map* feature_map, const float* gamma, int normalize,
+                      int dtype, const float* S_in, const float* z_in, const float* dS_out, const float* dz_out,
+                      float* dS_in, float* dz_in, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!gamma) return LA_ERR_INVALID_ARG;
+  return backward_impl(q, k, v, dout, dq, dk, dv, B, H, N, d, feature_map, normalize, dtype, S_in, z_in, dS_out,
+                       dz_out, dS_in, dz_in, workspace, workspace_bytes, stream, gamma);
 }
 
 }  // extern "C"

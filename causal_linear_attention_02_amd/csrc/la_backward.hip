@@ -198,26 +198,38 @@ __device__ __forceinline__ void dma_tile(uint8_t* tile, __amdgpu_buffer_rsrc_t r
 
 // elementwise phi (rows at or past `valid`: 0 when MASK) on 8 bf16 values in place
 template <int FM, bool MASK>
-__device__ __forceinline__ u32x4 phi_bf16x8(u32x4 r, bool live) {
+__device__ __forceinline__ u32x4 phi_bf16x8(u32x4 r, bool live, float sc = 1.f) {
   float x[8];
   In8<__bf16>::to_f32(r, x);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = (!MASK || live) ? bphi<FM>(x[e]) : 0.f;
+  for (int e = 0; e < 8; ++e) x[e] = (!MASK || live) ? bphi<FM>(x[e]) * sc : 0.f;
   return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
 }
 
 // phi of 8 bf16 values as hi + lo bf16 (rows at or past `valid`: 0)
 template <int FM>
-__device__ __forceinline__ void phi_bf16x8_hilo(u32x4 r, bool live, u32x4& hi, u32x4& lo) {
+__device__ __forceinline__ void phi_bf16x8_hilo(u32x4 r, bool live, u32x4& hi, u32x4& lo, float sc = 1.f) {
   float x[8];
   In8<__bf16>::to_f32(r, x);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = live ? bphi<FM>(x[e]) : 0.f;
+  for (int e = 0; e < 8; ++e) x[e] = live ? bphi<FM>(x[e]) * sc : 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     hi[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
     lo[i] = pack_bf16x2(x[2 * i] - __uint_as_float(hi[i] << 16), x[2 * i + 1] - __uint_as_float(hi[i] & 0xffff0000u));
   }
+}
+
+// Decay (per-head gamma): gamma^n as exp2(n log2 gamma).
+struct Decay {
+  float lg = 0.f;
+  __device__ __forceinline__ float pw(float n) const { return __builtin_amdgcn_exp2f(lg * n); }
+};
+template <bool DECAY>
+__device__ __forceinline__ Decay decay_of(const BwdArgs& a, int bh) {
+  Decay d;
+  if constexpr (DECAY) d.lg = __log2f(a.gamma[bh % a.H]);
+  return d;
 }
 
 // ---------------------------------------------------------------------------
@@ -232,8 +244,13 @@ __device__ __forceinline__ void phi_bf16x8_hilo(u32x4 r, bool live, u32x4& hi, u
 // loses a large share of that small part. With bf16 operands phi(K) enters
 // the S and z updates and the in-chunk product as hi + lo tiles, and S the
 // product with dY as hi + lo fragments.
+// Decay (DECAY): rows r of the chunk stage phi(q) gamma^(r-32) and phi(k)
+// gamma^(32-r) (the scores then carry gamma^(r_i-r_j)); the carried state
+// enters as gamma^33 S (so that row i gets gamma^(r_i+1) S), the result of
+// row i is scaled by gamma^(r_i-32), and the state moves on as
+// gamma^31 (gamma^33 S + Kh^T V) = gamma^64 S + sum_j gamma^(63-r_j) phi(k_j) v_j^T.
 // ---------------------------------------------------------------------------
-template <int D, typename OP, typename IN, int FM>
+template <int D, typename OP, typename IN, int FM, bool DECAY>
 __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
   using Frag = typename Ops<OP>::frag;
   constexpr int NW = D / 32;
@@ -256,6 +273,7 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
   const int ib = wave / NW, w = wave % NW;
   const long long base = (long long)bh * a.N;
   IN* dq = static_cast<IN*>(a.dq);
+  const Decay dc = decay_of<DECAY>(a, bh);
 
   const float* Sp;
   const float* zp;
@@ -308,12 +326,13 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int o = dma_off<D>(i);
-        const bool live = o / RB < valid;
+        const int row = o / RB;
+        const bool live = row < valid;
         u32x4* pq = reinterpret_cast<u32x4*>(sQ + o);
         u32x4* pk = reinterpret_cast<u32x4*>(sK + o);
-        *pq = phi_bf16x8<FM, false>(*pq, live);
+        *pq = phi_bf16x8<FM, false>(*pq, live, DECAY ? dc.pw(row - 32) : 1.f);
         u32x4 khi, klo;
-        phi_bf16x8_hilo<FM>(*pk, live, khi, klo);
+        phi_bf16x8_hilo<FM>(*pk, live, khi, klo, DECAY ? dc.pw(32 - row) : 1.f);
         *pk = khi;
         *reinterpret_cast<u32x4*>(sKl + o) = klo;
       }
@@ -328,12 +347,13 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
         const int row = t / RL + 32 * i, col = 8 * (t % RL);
         float x[8];
         In8<IN>::to_f32(ck.q[i], x);
+        const float sq = DECAY ? dc.pw(row - 32) : 1.f, sk = DECAY ? dc.pw(32 - row) : 1.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = bphi<FM>(x[e]);
+        for (int e = 0; e < 8; ++e) x[e] = bphi<FM>(x[e]) * sq;
         Ops<OP>::template store8<RB>(sQ, row, col, x);
         In8<IN>::to_f32(ck.k[i], x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = row < valid ? bphi<FM>(x[e]) : 0.f;
+        for (int e = 0; e < 8; ++e) x[e] = row < valid ? bphi<FM>(x[e]) * sk : 0.f;
         Ops<OP>::template store8<RB>(sK, row, col, x);
         put_raw<IN, OP, RB>(sV, row, col, ck.v[i]);
         put_raw<IN, OP, RB>(sY, row, col, ck.y[i]);
@@ -341,6 +361,12 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
       __syncthreads();
     }
 
+    if constexpr (DECAY) {  // the carried state as it enters the chunk's rows: gamma^33 S
+      const float g33 = dc.pw(33);
+#pragma unroll
+      for (int eb = 0; eb < NW; ++eb) ST[eb] *= g33;
+      Z *= g33;
+    }
     // scores A[j][i] = phi(k_j).phi(q_i) and value products P[j][i] = v_j.dy_i
     // for the wave's query rows i: the diagonal key block (d) and, for the
     // second row block, the first key block (o)
@@ -461,10 +487,14 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
     if (ib) intra(Po, 0);
     if (irow < valid) {
       IN* o = dq + (base + 64LL * c + irow) * D + 32 * w + 4 * h;
+      // decay: the row's factor gamma^(r-32), and phi(q) back from the staged row
+      const float fr = DECAY ? dc.pw(irow - 32) : 1.f, fb = DECAY ? dc.pw(32 - irow) : 1.f;
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        store4<IN>(o + 8 * g, T[4 * g] * bdphi<FM>(fq[4 * g]), T[4 * g + 1] * bdphi<FM>(fq[4 * g + 1]),
-                   T[4 * g + 2] * bdphi<FM>(fq[4 * g + 2]), T[4 * g + 3] * bdphi<FM>(fq[4 * g + 3]));
+        store4<IN>(o + 8 * g, fr * T[4 * g] * bdphi<FM>(fb * fq[4 * g]),
+                   fr * T[4 * g + 1] * bdphi<FM>(fb * fq[4 * g + 1]),
+                   fr * T[4 * g + 2] * bdphi<FM>(fb * fq[4 * g + 2]),
+                   fr * T[4 * g + 3] * bdphi<FM>(fb * fq[4 * g + 3]));
       if (w == 0 && h == 0)
         *reinterpret_cast<f32x2*>(a.rowstats + 2 * (base + 64LL * c + irow)) = f32x2{inv, hh};
     }
@@ -482,6 +512,12 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
       Ops<OP>::mma(Z, kf, ones);
       if constexpr (HILO) Ops<OP>::mma(Z, kl, ones);
     }
+    if constexpr (DECAY) {  // gamma^31 (gamma^33 S + Kh^T V): the state after the chunk
+      const float g31 = dc.pw(31);
+#pragma unroll
+      for (int eb = 0; eb < NW; ++eb) ST[eb] *= g31;
+      Z *= g31;
+    }
     // the single set is restaged next; with two sets the next chunk's
     // barriers already order these reads before that set is refilled
     if constexpr (!DMA) __syncthreads();
@@ -490,11 +526,12 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // r-state pass: per segment R_loc = sum_i phi(q_i) g_i^T, r_loc = sum_i
-// phi(q_i) h_i into ws_rev slot P-1-seg. grid = (BH, P), block = 2*D
+// phi(q_i) h_i into ws_rev slot P-1-seg (decay: weighted gamma^(i - s0 + 1),
+// relative to the row before the segment, s0 its first token). grid = (BH, P), block = 2*D
 // threads; wave w keeps R[:, 32w:32w+32] (rows = features). Staging threads
 // hold pieces at rows t/(D/8) + 16 i, i = 0..3.
 // ---------------------------------------------------------------------------
-template <int D, typename OP, typename IN, int FM>
+template <int D, typename OP, typename IN, int FM, bool DECAY>
 __global__ __launch_bounds__(D * 2) void bwd_rstate_kernel(BwdArgs a) {
   constexpr int NW = D / 32;
   constexpr int RB = D * Ops<OP>::kBytes;
@@ -512,13 +549,15 @@ __global__ __launch_bounds__(D * 2) void bwd_rstate_kernel(BwdArgs a) {
   const long long base = (long long)bh * a.N;
   const IN* q = static_cast<const IN*>(a.q);
   const IN* dy = static_cast<const IN*>(a.dy);
+  const Decay dc = decay_of<DECAY>(a, bh);
 
   f32x16 R[NW];
 #pragma unroll
   for (int fb = 0; fb < NW; ++fb) R[fb] = f32x16{};
   float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const int col = 8 * (t % RL);
-  for (int m = 0; m < n; ++m) {
+  for (int mm = 0; mm < n; ++mm) {
+    const int m = DECAY ? n - 1 - mm : mm;  // decay: chunks from the last, the sums moved on by gamma^64
     const int c = c0 + m;
     const int valid = min(64, a.N - 64 * c);
     const unsigned bytes = (unsigned)(valid * D * (int)sizeof(IN));
@@ -535,14 +574,22 @@ __global__ __launch_bounds__(D * 2) void bwd_rstate_kernel(BwdArgs a) {
       ry[i] = In8<IN>::bload(Ry, o);
       rs[i] = row < valid ? *reinterpret_cast<const f32x2*>(a.rowstats + 2 * (row0 + row)) : f32x2{0.f, 0.f};
     }
+    if constexpr (DECAY) {
+      const float g32 = dc.pw(32);
+#pragma unroll
+      for (int fb = 0; fb < NW; ++fb) R[fb] = (R[fb] * g32) * g32;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cs[e] = (cs[e] * g32) * g32;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = t / RL + 16 * i;
+      const float sq = DECAY ? dc.pw(row + 1) : 1.f;  // decay: relative to the row before the chunk
       float x[8];
       In8<IN>::to_f32(rq[i], x);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        x[e] = row < valid ? bphi<FM>(x[e]) : 0.f;
+        x[e] = row < valid ? bphi<FM>(x[e]) * sq : 0.f;
         cs[e] += x[e] * rs[i][1];
       }
       Ops<OP>::template store8<RB>(sQ, row, col, x);
@@ -568,15 +615,24 @@ __global__ __launch_bounds__(D * 2) void bwd_rstate_kernel(BwdArgs a) {
   }
   __syncthreads();
   float* st = a.ws_rev + ((long long)bh * (a.nseg + 1) + (a.nseg - 1 - seg)) * a.state_elems;
+  // decay: the last segment also carries the final-state cotangents, which
+  // reach the row before the segment with gamma^(N - s0)
+  const bool seed = DECAY && a.dS_out && seg == a.nseg - 1;
+  const float fs = seed ? dc.pw((float)(a.N - 64 * c0)) : 0.f;
+  const float* sS = seed ? a.dS_out + (long long)bh * D * D : nullptr;
+  const float* sz = seed ? a.dz_out + (long long)bh * D : nullptr;
 #pragma unroll
   for (int fb = 0; fb < NW; ++fb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st[(long long)(32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)) * D + 32 * w + li] = R[fb][r];
+    for (int r = 0; r < 16; ++r) {
+      const long long ix = (long long)(32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)) * D + 32 * w + li;
+      st[ix] = R[fb][r] + (seed ? fs * sS[ix] : 0.f);
+    }
   for (int f = t; f < D; f += 2 * D) {
     float s = 0.f;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) s += rsum[ww][f];
-    st[D * D + f] = s;
+    st[D * D + f] = s + (seed ? fs * sz[f] : 0.f);
   }
 }
 
@@ -596,8 +652,13 @@ __global__ __launch_bounds__(D * 2) void bwd_rstate_kernel(BwdArgs a) {
 // scores times sI_i for dv): g_i.v_j and -h_i cancel where v_j is close to
 // the output y_i, and a product with g rounded to bf16 would leave that
 // rounding in dk. fp32 keeps Y = G = dY / D_i, Qs = phi(Q) and sI = 1.
+// Decay (DECAY): rows stage phi(q) gamma^(r-32) and phi(k) gamma^(32-r);
+// the suffix state of a chunk of v valid rows is kept relative to its last
+// valid row, enters as gamma^(v-33) R (row j then gets gamma^(v-1-r_j) R
+// through the staged keys), the dk of row j is scaled by gamma^(32-r_j), and
+// the state moves to the previous chunk as gamma^33 (gamma^(v-33) R + Qs^T Y).
 // ---------------------------------------------------------------------------
-template <int D, typename OP, typename IN, int FM>
+template <int D, typename OP, typename IN, int FM, bool DECAY>
 __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
   using Frag = typename Ops<OP>::frag;
   constexpr int NW = D / 32;
@@ -620,6 +681,12 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
   const long long base = (long long)bh * a.N;
   IN* dk = static_cast<IN*>(a.dk);
   IN* dv = static_cast<IN*>(a.dv);
+  const Decay dc = decay_of<DECAY>(a, bh);
+  // decay: the last segment starts from the final-state cotangents (the
+  // reverse scan carries no seed then)
+  const bool seed = DECAY && a.dS_out && seg == a.nseg - 1;
+  const float* sS = seed ? a.dS_out + (long long)bh * D * D : nullptr;
+  const float* sz = seed ? a.dz_out + (long long)bh * D : nullptr;
 
   const float* Rp = a.ws_rev + ((long long)bh * (a.nseg + 1) + (a.nseg - 1 - seg)) * a.state_elems;
   f32x16 RS[NW], rK;
@@ -627,9 +694,11 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
   for (int r = 0; r < 16; ++r) {
     const int rr = 8 * (r >> 2) + 4 * h + (r & 3);
 #pragma unroll
-    for (int b = 0; b < NW; ++b)
-      RS[b][r] = vgroup ? Rp[(long long)(32 * b + rr) * D + 32 * w + li] : Rp[(long long)(32 * w + li) * D + 32 * b + rr];
-    rK[r] = vgroup ? 0.f : Rp[D * D + 32 * w + rr];
+    for (int b = 0; b < NW; ++b) {
+      const long long ix = vgroup ? (long long)(32 * b + rr) * D + 32 * w + li : (long long)(32 * w + li) * D + 32 * b + rr;
+      RS[b][r] = Rp[ix] + (seed ? sS[ix] : 0.f);
+    }
+    rK[r] = vgroup ? 0.f : Rp[D * D + 32 * w + rr] + (seed ? sz[32 * w + rr] : 0.f);
   }
 
   uint8_t* sQs = smem + 8 * TB;  // DMA only
@@ -673,9 +742,9 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
         const bool live = row < valid;
         u32x4* pq = reinterpret_cast<u32x4*>(sQ + o);
         u32x4* pk = reinterpret_cast<u32x4*>(sK + o);
-        const u32x4 fq = phi_bf16x8<FM, true>(*pq, live);
+        const u32x4 fq = phi_bf16x8<FM, true>(*pq, live, DECAY ? dc.pw(row - 32) : 1.f);
         *pq = fq;
-        *pk = phi_bf16x8<FM, true>(*pk, live);
+        *pk = phi_bf16x8<FM, true>(*pk, live, DECAY ? dc.pw(32 - row) : 1.f);
         float x[8];
         In8<__bf16>::to_f32(fq, x);
 #pragma unroll
@@ -698,13 +767,14 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
         const int row = t / RL + 32 * i, col = 8 * (t % RL);
         const bool live = row < valid;
         float x[8];
+        const float sq = DECAY ? dc.pw(row - 32) : 1.f, sk = DECAY ? dc.pw(32 - row) : 1.f;
         In8<IN>::to_f32(ck.q[i], x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = live ? bphi<FM>(x[e]) : 0.f;
+        for (int e = 0; e < 8; ++e) x[e] = live ? bphi<FM>(x[e]) * sq : 0.f;
         Ops<OP>::template store8<RB>(sQ, row, col, x);
         In8<IN>::to_f32(ck.k[i], x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = live ? bphi<FM>(x[e]) : 0.f;
+        for (int e = 0; e < 8; ++e) x[e] = live ? bphi<FM>(x[e]) * sk : 0.f;
         Ops<OP>::template store8<RB>(sK, row, col, x);
         put_raw<IN, OP, RB>(sV, row, col, ck.v[i]);
         In8<IN>::to_f32(ck.y[i], x);
@@ -719,6 +789,12 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
       __syncthreads();
     }
 
+    if constexpr (DECAY) {  // the suffix state as this chunk's rows see it: gamma^(v-33) R
+      const float fa = dc.pw(valid - 33);
+#pragma unroll
+      for (int b = 0; b < NW; ++b) RS[b] *= fa;
+      rK *= fa;
+    }
     if (vgroup) {
       // dv_j[e] = sum_{i>=j} G[i][e] A[i][j] + sum_f R[f][e] phi(k_j)[f], with the
       // scores A[i][j] of (query block, key block) (0,0), (1,0), (1,1), j <= i,
@@ -815,12 +891,14 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
         const int j = 32 * jb + li;
         if (j < valid) {
           IN* o = dk + (base + 64LL * c + j) * D + 32 * w + 4 * h;
+          // decay: the row's factor gamma^(32-r), and phi(k) back from the staged row
+          const float fr = DECAY ? dc.pw(32 - j) : 1.f, fb = DECAY ? dc.pw(j - 32) : 1.f;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             float fk[4];
             lds_read4<OP, RB>(sK, j, 32 * w + 8 * g + 4 * h, fk);
-            store4<IN>(o + 8 * g, Kt[4 * g] * bdphi<FM>(fk[0]), Kt[4 * g + 1] * bdphi<FM>(fk[1]),
-                       Kt[4 * g + 2] * bdphi<FM>(fk[2]), Kt[4 * g + 3] * bdphi<FM>(fk[3]));
+            store4<IN>(o + 8 * g, fr * Kt[4 * g] * bdphi<FM>(fb * fk[0]), fr * Kt[4 * g + 1] * bdphi<FM>(fb * fk[1]),
+                       fr * Kt[4 * g + 2] * bdphi<FM>(fb * fk[2]), fr * Kt[4 * g + 3] * bdphi<FM>(fb * fk[3]));
           }
         }
       }
@@ -837,51 +915,63 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
         Ops<OP>::mma(rK, qf, frag8<OP>(hv));
       }
     }
+    if constexpr (DECAY) {  // on to the previous chunk: gamma^33 (gamma^(v-33) R + Qs^T Y)
+      const float g33 = dc.pw(33);
+#pragma unroll
+      for (int b = 0; b < NW; ++b) RS[b] *= g33;
+      rK *= g33;
+    }
     // the single set is restaged next; with two sets the next chunk's
     // barriers already order these reads before that set is refilled
     if constexpr (!DMA) __syncthreads();
   }
 }
 
-template <int D, typename T, int FM>
+template <int D, typename T, int FM, bool DECAY>
 hipError_t launch_backward(const FwdArgs& fa, const ScanArgs& fs, const BwdArgs& b, const ScanArgs& rs, int dtype,
                            hipStream_t st) {
   if (fa.run_state_pass || fa.run_scan) {
     FwdArgs f = fa;
     f.skip_output = 1;
     f.hilo_keys = 1;  // S carries phi(k) to ~2^-16 (the dq pass needs it; see there)
-    const hipError_t e = prefill_dispatch(f, fs, D, D, FM, dtype, true, false, st, nullptr);
+    const hipError_t e = prefill_dispatch(f, fs, D, D, FM, dtype, true, DECAY, st, nullptr);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((bwd_dq_kernel<D, T, T, FM>), dim3(b.BH, b.nseg), dim3(4 * D), 0, st, b);
-  hipLaunchKernelGGL((bwd_rstate_kernel<D, T, T, FM>), dim3(b.BH, b.nseg), dim3(2 * D), 0, st, b);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, T, T, FM, DECAY>), dim3(b.BH, b.nseg), dim3(4 * D), 0, st, b);
+  hipLaunchKernelGGL((bwd_rstate_kernel<D, T, T, FM, DECAY>), dim3(b.BH, b.nseg), dim3(2 * D), 0, st, b);
   const hipError_t e = scan_dispatch(rs, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, T, T, FM>), dim3(b.BH, b.nseg), dim3(4 * D), 0, st, b);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, T, T, FM, DECAY>), dim3(b.BH, b.nseg), dim3(4 * D), 0, st, b);
   return hipGetLastError();
 }
 
-template <typename T, int FM>
+template <typename T, int FM, bool DECAY>
 hipError_t backward_d(const FwdArgs& fa, const ScanArgs& fs, const BwdArgs& b, const ScanArgs& rs, int D, int dtype,
                       hipStream_t st) {
   switch (D) {
-    case 32: return launch_backward<32, T, FM>(fa, fs, b, rs, dtype, st);
-    case 64: return launch_backward<64, T, FM>(fa, fs, b, rs, dtype, st);
-    case 128: return launch_backward<128, T, FM>(fa, fs, b, rs, dtype, st);
+    case 32: return launch_backward<32, T, FM, DECAY>(fa, fs, b, rs, dtype, st);
+    case 64: return launch_backward<64, T, FM, DECAY>(fa, fs, b, rs, dtype, st);
+    case 128: return launch_backward<128, T, FM, DECAY>(fa, fs, b, rs, dtype, st);
   }
   return hipErrorInvalidValue;
+}
+
+template <typename T, int FM>
+hipError_t backward_dd(const FwdArgs& fa, const ScanArgs& fs, const BwdArgs& b, const ScanArgs& rs, int D, int dtype,
+                       bool decay, hipStream_t st) {
+  return decay ? backward_d<T, FM, true>(fa, fs, b, rs, D, dtype, st) : backward_d<T, FM, false>(fa, fs, b, rs, D, dtype, st);
 }
 
 }  // namespace
 
 hipError_t backward_dispatch(const FwdArgs& fa, const ScanArgs& fs, const BwdArgs& b, const ScanArgs& rs, int D,
-                             int fmap, int dtype, hipStream_t st) {
+                             int fmap, int dtype, bool decay, hipStream_t st) {
   if (dtype == 1) {
-    if (fmap == kElu1) return backward_d<__bf16, kElu1>(fa, fs, b, rs, D, dtype, st);
-    if (fmap == kIdentity) return backward_d<__bf16, kIdentity>(fa, fs, b, rs, D, dtype, st);
+    if (fmap == kElu1) return backward_dd<__bf16, kElu1>(fa, fs, b, rs, D, dtype, decay, st);
+    if (fmap == kIdentity) return backward_dd<__bf16, kIdentity>(fa, fs, b, rs, D, dtype, decay, st);
   } else {
-    if (fmap == kElu1) return backward_d<float, kElu1>(fa, fs, b, rs, D, dtype, st);
-    if (fmap == kIdentity) return backward_d<float, kIdentity>(fa, fs, b, rs, D, dtype, st);
+    if (fmap == kElu1) return backward_dd<float, kElu1>(fa, fs, b, rs, D, dtype, decay, st);
+    if (fmap == kIdentity) return backward_dd<float, kIdentity>(fa, fs, b, rs, D, dtype, decay, st);
   }
   return hipErrorInvalidValue;
 }

@@ -102,6 +102,10 @@ struct BwdArgs {
                            // (after the scan) the cotangent of the state leaving segment s
   int state_elems;         // D * D + D
   float* rowstats;         // [BH][N][2]: 1 / max(den, eps), d loss / d den
+  const float* gamma;      // decay per head [H] or null
+  int H;
+  const float* dS_out;     // decay: cotangents of the final state, added by the passes themselves
+  const float* dz_out;
 };
 
 // Gated linear attention (per-token, per-channel log-gates on the feature
@@ -124,7 +128,7 @@ hipError_t prefill_dispatch(const FwdArgs& a, const ScanArgs& s, int D, int DF, 
                             bool decay, hipStream_t st, hipEvent_t* ev);
 hipError_t scan_dispatch(const ScanArgs& s, hipStream_t st);
 hipError_t backward_dispatch(const FwdArgs& fa, const ScanArgs& fs, const BwdArgs& b, const ScanArgs& rs, int D,
-                             int fmap, int dtype, hipStream_t st);
+                             int fmap, int dtype, bool decay, hipStream_t st);
 hipError_t gated_dispatch(const GatedArgs& g, const ScanArgs& s, int D, int fmap, int dtype, hipStream_t st);
 hipError_t decode_dispatch(const DecodeArgs& a, int D, int DF, int fmap, int dtype, hipStream_t st);
 hipError_t fmap_dispatch(const FmapArgs& a, int D, int DF, int fmap, int in_dtype, int out_dtype, hipStream_t st);

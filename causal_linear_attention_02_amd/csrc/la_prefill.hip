@@ -359,7 +359,7 @@ template <int D, int DF, typename OP, typename IN, int FM, bool DECAY, bool HILO
 __global__ __launch_bounds__(D * 2, DECAY ? 2 : 1) void state_pass_kernel(FwdArgs a) {
   using Frag = typename Ops<OP>::frag;
   using G = Stage<D, DF>;
-  static_assert(!HILO || (sizeof(OP) == 2 && !DECAY && DF == D), "hi + lo keys: bf16 operands, no decay, d' = d");
+  static_assert(!HILO || (sizeof(OP) == 2 && DF == D), "hi + lo keys: bf16 operands, d' = d");
   constexpr int RBF = DF * Ops<OP>::kBytes;
   constexpr int RBV = D * Ops<OP>::kBytes;
   constexpr int KB = 64 * RBF, VB = 64 * RBV, BUF = KB + VB + (HILO ? KB : 0);
@@ -406,10 +406,29 @@ __global__ __launch_bounds__(D * 2, DECAY ? 2 : 1) void state_pass_kernel(FwdArg
       // scaled keys (see the decay note above); v pieces raw
 #pragma unroll
       for (int e = 0; e < 8; ++e) cs[e] = 0.f;
+      if constexpr (HILO) {
+        uint8_t* sKl = sK + KB + VB;
 #pragma unroll
-      for (int i = 0; i < G::NQ; ++i)
-        stage_k_piece<D, DF, IN, OP, FM, true>(pf.k[i], p, i, 64, sK, cs,
-                                               gpow(lg, kDecayCenter - (p / G::RLF + G::RSF * i)));
+        for (int i = 0; i < G::NQ; ++i) {
+          const int row = p / G::RLF + G::RSF * i, col = 8 * (p % G::RLF);
+          const float sc = gpow(lg, kDecayCenter - row);
+          float x[8], lo[8];
+          In8<IN>::to_f32(pf.k[i], x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            x[e] = fmap_in_stage<FM>(x[e]) * sc;
+            cs[e] += x[e];
+            lo[e] = x[e] - round_bf16(x[e]);
+          }
+          Ops<OP>::template store8<RBF>(sK, row, col, x);
+          Ops<OP>::template store8<RBF>(sKl, row, col, lo);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < G::NQ; ++i)
+          stage_k_piece<D, DF, IN, OP, FM, true>(pf.k[i], p, i, 64, sK, cs,
+                                                 gpow(lg, kDecayCenter - (p / G::RLF + G::RSF * i)));
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) store_raw<IN, OP, RBV>(sK + KB, p / G::RLV + 16 * i, 8 * (p % G::RLV), pf.v[i]);
 #pragma unroll
@@ -964,7 +983,7 @@ static hipError_t launch_prefill_t(const FwdArgs& a, const ScanArgs& s, bool cau
                                    hipEvent_t* ev) {
   // ev[0] is recorded by the caller (before any feature-map kernels)
   if (a.run_state_pass) {
-    constexpr bool kHiloOk = sizeof(OP) == 2 && !DECAY && DF == D;
+    constexpr bool kHiloOk = sizeof(OP) == 2 && DF == D;
     if (kHiloOk && a.hilo_keys)
       hipLaunchKernelGGL((state_pass_kernel<D, DF, OP, IN, FM, DECAY, kHiloOk>), dim3(a.BH, a.nseg_state),
                          dim3(D * 2), 0, st, a);

@@ -195,13 +195,28 @@ size_t la_backward_workspace_size(int B, int H, int N, int d, const la_feature_m
  * The forward is recomputed (no saved activations). Where max(den, 1e-6)
  * clamps, its derivative is taken as 0 (den < 1e-6) or 1 (den >= 1e-6).
  * Supported: elu+1 and the identity map, d in {32, 64, 128}; random
- * features and decay return LA_ERR_UNSUPPORTED. N = 0 writes only
- * dS_in/dz_in (= dS_out/dz_out, or zeros).
+ * features return LA_ERR_UNSUPPORTED (decay: la_backward_decay). N = 0
+ * writes only dS_in/dz_in (= dS_out/dz_out, or zeros).
  */
 int la_backward(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv, int B,
                 int H, int N, int d, const la_feature_map* feature_map, int normalize, int dtype, const float* S_in,
                 const float* z_in, const float* dS_out, const float* dz_out, float* dS_in, float* dz_in,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Gradients of la_forward_decay (causal, per-head decay, "Linear Attention",
+ * "Variantes y extensiones", RetNet item), as la_backward for
+ * L = <dout, out> + <dS_out, S_out> + <dz_out, z_out>:
+ * dS_in/dz_in then hold dL/dS_in, dL/dz_in, in which every token's term
+ * carries its decay factor. gamma: DEVICE pointer to H fp32 values in
+ * [1/4, 1], as for la_forward_decay (values are not checked on the host).
+ * Workspace: la_backward_workspace_size() bytes. Everything else as
+ * la_backward.
+ */
+int la_backward_decay(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk, void* dv,
+                      int B, int H, int N, int d, const la_feature_map* feature_map, const float* gamma, int normalize,
+                      int dtype, const float* S_in, const float* z_in, const float* dS_out, const float* dz_out,
+                      float* dS_in, float* dz_in, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Bytes of device workspace that la_forward_gated needs (0 for invalid

@@ -191,6 +191,30 @@ def test_backward_rejects_bad_arguments():
     assert _bwd(B=0) == la.LA_OK and _bwd(N=0) == la.LA_OK                     # nothing to do
 
 
+def _bwd_decay(gamma=FAKE2 * 9, **kw):
+    a = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, dout=FAKE + 0x3000000, dq=FAKE2, dk=FAKE2 + 0x1000000,
+             dv=FAKE2 + 0x2000000, B=1, H=1, N=128, d=64, fm=ELU, normalize=1, dtype=la.LA_BF16, S_in=None,
+             z_in=None, dS_out=None, dz_out=None, dS_in=None, dz_in=None, ws=FAKE2 * 4, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.la_backward_decay(a["q"], a["k"], a["v"], a["dout"], a["dq"], a["dk"], a["dv"], a["B"], a["H"],
+                                 a["N"], a["d"], ctypes.byref(a["fm"]) if a["fm"] is not None else None, gamma,
+                                 a["normalize"], a["dtype"], a["S_in"], a["z_in"], a["dS_out"], a["dz_out"],
+                                 a["dS_in"], a["dz_in"], a["ws"], a["ws_bytes"], None)
+
+
+def test_backward_decay_rejects_bad_arguments():
+    assert _bwd_decay(gamma=None) == la.LA_ERR_INVALID_ARG                   # gamma is required
+    assert _bwd_decay(gamma=FAKE2 * 9 + 2) == la.LA_ERR_INVALID_ARG          # misaligned gamma
+    assert _bwd_decay(gamma=FAKE2 + 0x40) == la.LA_ERR_INVALID_ARG           # gamma inside dq
+    assert _bwd_decay(gamma=FAKE2 * 4 + 0x40) == la.LA_ERR_INVALID_ARG       # gamma inside the workspace
+    assert _bwd_decay(B=-1) == la.LA_ERR_INVALID_ARG
+    assert _bwd_decay(d=48) == la.LA_ERR_UNSUPPORTED
+    assert _bwd_decay(fm=la_feature_map(la.LA_PERFORMER, 64, FAKE2 * 8)) == la.LA_ERR_UNSUPPORTED
+    assert _bwd_decay(dq=FAKE + 0x100) == la.LA_ERR_INVALID_ARG
+    assert _bwd_decay(ws=None) == la.LA_ERR_WORKSPACE
+    assert _bwd_decay(N=0) == la.LA_OK
+
+
 def test_backward_workspace_plan():
     ident = la_feature_map(la.LA_IDENTITY, 0, None)
     for d in (32, 64, 128):

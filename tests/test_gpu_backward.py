@@ -42,8 +42,13 @@ def _err(g, r, dy, vanishing=False):
     return float(np.max(num / den))
 
 
-def _check(B, H, N, d, dt, seed, fmap="elu1", normalize=True, state=False, positive=False):
-    log(f"case backward B{B} H{H} N{N} d{d} {dt} {fmap} norm={normalize} state={state}")
+def _gammas(H):
+    """Per-head decays spanning the supported range [1/4, 1]."""
+    return np.array([0.25, 0.7, 0.97, 1.0, 0.999, 0.5][:H], dtype=np.float32)
+
+
+def _check(B, H, N, d, dt, seed, fmap="elu1", normalize=True, state=False, positive=False, decay=False):
+    log(f"case backward B{B} H{H} N{N} d{d} {dt} {fmap} norm={normalize} state={state} decay={decay}")
     q, k, v = qkv(B, H, N, d, seed, dt, 1.0)
     if positive:  # identity map, normalized: positive q, k keep the denominators away from 0
         q, k = np.abs(q), np.abs(k)
@@ -58,8 +63,13 @@ def _check(B, H, N, d, dt, seed, fmap="elu1", normalize=True, state=False, posit
         dev = lambda x: torch.from_numpy(x).cuda()  # noqa: E731
         kw = dict(S_in=dev(S0), z_in=dev(z0), dS_out=dev(dS), dz_out=dev(dz), return_state_grad=True)
         okw = dict(S0=S0, z0=z0, dS_N=dS, dz_N=dz)
-    res = la.la_backward(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), to_dev(dy, dt), feature_map=fmap,
-                         normalize=normalize, **kw)
+    args = (to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), to_dev(dy, dt))
+    if decay:
+        g = _gammas(H)
+        res = la.la_backward_decay(*args, torch.from_numpy(g).cuda(), feature_map=fmap, normalize=normalize, **kw)
+        okw["decay"] = g.astype(np.float64)
+    else:
+        res = la.la_backward(*args, feature_map=fmap, normalize=normalize, **kw)
     torch.cuda.synchronize()
     ref = O.attention_backward(q, k, v, dy, fmap, causal=True, normalize=normalize, **okw)
     names = ("dq", "dk", "dv", "dS_in", "dz_in")
@@ -132,4 +142,82 @@ def test_backward_full_b1h16n65536d128_sampled_heads():
             log(f"  head {h} {name} rel err {err:.3e}")
             assert err <= TOL["bf16"], (h, name, err)
         ez = _err(to_host(dz[:, h])[..., None, :], ref[4][..., None, :], dy[:, h])
+        assert ez <= TOL["bf16"], (h, "dz_in", ez)
+
+
+# --- decay (per-head gamma): gradients of la_forward_decay ---------------------------------------------------
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_backward_decay_small(d, dt):
+    for N in (1, 63, 64, 65, 200):
+        _check(1, 4, N, d, dt, seed=1900 + N + d, decay=True)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("normalize", [True, False])
+def test_backward_decay_multisegment(d, dt, normalize):
+    # 40 chunks with a ragged tail: several segments, the last one partial
+    _check(1, 4, 64 * 40 - 17, d, dt, seed=131 + d, normalize=normalize, decay=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_backward_decay_state_in_and_out(d, dt):
+    _check(1, 4, 64 * 12 + 9, d, dt, seed=157 + d, state=True, decay=True)
+    _check(2, 2, 70, d, dt, seed=158 + d, state=True, decay=True)   # single segment
+    _check(1, 4, 64 * 12, d, dt, seed=159 + d, state=True, decay=True)   # whole chunks only
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_backward_decay_identity_map(d):
+    _check(1, 4, 64 * 9 + 30, d, "bf16", seed=177 + d, fmap="identity", normalize=False, decay=True)
+    _check(1, 4, 64 * 9 + 30, d, "f32", seed=178 + d, fmap="identity", normalize=True, positive=True, decay=True)
+
+
+def test_backward_decay_one_equals_no_decay():
+    q, k, v = qkv(1, 2, 700, 64, 5, "bf16", 1.0)
+    dy = _dout(1, 2, 700, 64, 5, "bf16")
+    args = [to_dev(x, "bf16") for x in (q, k, v, dy)]
+    a = la.la_backward(*args)
+    b = la.la_backward_decay(*args, torch.ones(2, device="cuda"))
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        err = _err(to_host(y), to_host(x), dy)
+        assert err <= 1e-5, err
+
+
+def test_backward_decay_empty_sequence_passes_state_gradient():
+    d = 64
+    dS = torch.randn(1, 2, d, d, device="cuda")
+    dz = torch.randn(1, 2, d, device="cuda")
+    x = torch.zeros(1, 2, 0, d, device="cuda", dtype=torch.bfloat16)
+    _, _, _, dS_in, dz_in = la.la_backward_decay(x, x.clone(), x.clone(), x.clone(), torch.full((2,), 0.5, device="cuda"),
+                                                 dS_out=dS, dz_out=dz, return_state_grad=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dS_in, dS) and torch.equal(dz_in, dz)
+
+
+def test_backward_decay_full_b1h16n65536d128_sampled_heads():
+    """The long-context workload with one decay per head, 1 - 2^-(5+h), in one
+    call; two heads checked against the recurrent form of the oracle's gradients."""
+    W = la_inputs.WORKLOADS["prefill_b1h16n65536d128"]
+    B, H, N, d = W["B"], W["H"], W["N"], W["d"]
+    log(f"case full decay backward B{B} H{H} N{N} d{d} bf16 (heads 0 and 15 checked)")
+    g = np.array([1.0 - 2.0 ** (-5 - h) for h in range(H)], dtype=np.float32)
+    q, k, v = la_inputs.gaussian_qkv(B, H, N, d, seed=W["seed"], scale=W["scale"], bf16=True)
+    dy = _dout(B, H, N, d, W["seed"], "bf16")
+    dq, dk, dv, dS, dz = la.la_backward_decay(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                                              to_dev(dy, "bf16"), torch.from_numpy(g).cuda(), return_state_grad=True)
+    torch.cuda.synchronize()
+    for h in (0, 15):
+        ref = O.recurrent_backward(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], dy[:, h:h + 1], "elu1",
+                                   decay=g[h:h + 1].astype(np.float64))
+        for name, got, r in zip(("dq", "dk", "dv", "dS_in"), (dq, dk, dv, dS), ref[:4]):
+            err = _err(to_host(got[:, h:h + 1]), r, dy[:, h:h + 1])
+            log(f"  head {h} {name} rel err {err:.3e}")
+            assert err <= TOL["bf16"], (h, name, err)
+        ez = _err(to_host(dz[:, h:h + 1])[..., None, :], ref[4][..., None, :], dy[:, h:h + 1])
         assert ez <= TOL["bf16"], (h, "dz_in", ez)
