@@ -245,9 +245,9 @@ __device__ __forceinline__ Decay decay_of(const BwdArgs& a, int bh) {
 // the S and z updates and the in-chunk product as hi + lo tiles, and S the
 // product with dY as hi + lo fragments.
 // Decay (DECAY): rows r of the chunk stage phi(q) gamma^(r-32) and phi(k)
-// gamma^(32-r) (the scores then carry gamma^(r_i-r_j)); the carried state
-// enters as gamma^33 S (so that row i gets gamma^(r_i+1) S), the result of
-// row i is scaled by gamma^(r_i-32), and the state moves on as
+// gamma^(32-r) (the scores then carry gamma^(r_i-r_j)); the carried terms
+// (S dy and z) enter scaled by gamma^33 (so that row i gets gamma^(r_i+1)),
+// the result of row i is scaled by gamma^(r_i-32), and the state moves on as
 // gamma^31 (gamma^33 S + Kh^T V) = gamma^64 S + sum_j gamma^(63-r_j) phi(k_j) v_j^T.
 // ---------------------------------------------------------------------------
 template <int D, typename OP, typename IN, int FM, bool DECAY>
@@ -361,12 +361,6 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
       __syncthreads();
     }
 
-    if constexpr (DECAY) {  // the carried state as it enters the chunk's rows: gamma^33 S
-      const float g33 = dc.pw(33);
-#pragma unroll
-      for (int eb = 0; eb < NW; ++eb) ST[eb] *= g33;
-      Z *= g33;
-    }
     // scores A[j][i] = phi(k_j).phi(q_i) and value products P[j][i] = v_j.dy_i
     // for the wave's query rows i: the diagonal key block (d) and, for the
     // second row block, the first key block (o)
@@ -375,7 +369,7 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
     float den = 0.f, dyn = 0.f;
     {
       f32x16 Ad = {};
-#pragma unroll
+#pragma unroll 4
       for (int kb = 0; kb < D / 16; ++kb) {
         Ops<OP>::mma(Ad, Ops<OP>::template load_rows<RB>(sK, 32 * ib, 16 * kb),
                      Ops<OP>::template load_rows<RB>(sQ, 32 * ib, 16 * kb));
@@ -392,7 +386,7 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
     }
     if (ib) {
       f32x16 Ao = {};
-#pragma unroll
+#pragma unroll 4
       for (int kb = 0; kb < D / 16; ++kb) {
         Ops<OP>::mma(Ao, Ops<OP>::template load_rows<RB>(sK, 0, 16 * kb),
                      Ops<OP>::template load_rows<RB>(sQ, 32 * ib, 16 * kb));
@@ -425,6 +419,8 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
           Ops<OP>::mma(T, Ops<OP>::from_acc(ST[eb], kk), yf);
         }
       }
+    const float g33 = DECAY ? dc.pw(33) : 1.f;
+    if constexpr (DECAY) T *= g33;
     // in-chunk parts (keys j <= i) of den_i and dy_i.num_i: both lane halves
     den += xor32(den);
     dyn += xor32(dyn);
@@ -439,6 +435,7 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
       pden += fq[r] * Z[r];
       pdyn += fq[r] * T[r];
     }
+    if constexpr (DECAY) pden *= g33;
     pden += xor32(pden);
     pdyn += xor32(pdyn);
     if (h == 0) {
@@ -466,7 +463,7 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
     }
     // d phi(q_i)[f] = T[f][i] / D_i + h_i z_f + sum_j phi(k_j)[f] B[j][i]
 #pragma unroll
-    for (int r = 0; r < 16; ++r) T[r] = T[r] * inv + hh * Z[r];
+    for (int r = 0; r < 16; ++r) T[r] = T[r] * inv + (DECAY ? hh * g33 : hh) * Z[r];
     // (bf16: phi(K) and B both as hi + lo; the lo x lo term is below 2^-16)
     auto intra = [&](const f32x16& Bt, int j0) {
 #pragma unroll
@@ -497,6 +494,11 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
                    fr * T[4 * g + 3] * bdphi<FM>(fb * fq[4 * g + 3]));
       if (w == 0 && h == 0)
         *reinterpret_cast<f32x2*>(a.rowstats + 2 * (base + 64LL * c + irow)) = f32x2{inv, hh};
+    }
+    if constexpr (DECAY) {
+#pragma unroll
+      for (int eb = 0; eb < NW; ++eb) ST[eb] *= g33;
+      Z *= g33;
     }
     // S^T += V^T phi(K), z += column sums of phi(K)
 #pragma unroll

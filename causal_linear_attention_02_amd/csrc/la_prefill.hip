@@ -844,9 +844,9 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
     // ------------------------------------------------------------------
     f32x16 S[DF / 32];
     load_state_tiles<D, DF>(S, Sinit, cw);
-    if constexpr (DECAY) {
+    if constexpr (DECAY) {  // entering the first chunk: moved on by gamma^64 in the scaled frame
 #pragma unroll
-      for (int cb = 0; cb < DF / 32; ++cb) S[cb] *= fin;
+      for (int cb = 0; cb < DF / 32; ++cb) S[cb] = ((S[cb] * fin) * gH) * gH;
     }
     Frag Sf_const[CAUSAL ? 1 : DF / 16];
     if constexpr (!CAUSAL) {
@@ -869,10 +869,6 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
       float dpart0 = 0.f, dpart1 = 0.f;
       Frag Vf[4];
       if constexpr (CAUSAL) {
-        if constexpr (DECAY) {
-#pragma unroll
-          for (int cb = 0; cb < DF / 32; ++cb) S[cb] = (S[cb] * gH) * gH;
-        }
         f32x16 A00 = {}, A01 = {}, A11 = {};
 #pragma unroll
         for (int kb = 0; kb < DF / 16; ++kb) {
@@ -960,6 +956,12 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
             Ops<OP>::mma(S[cb], Ops<OP>::template load_cols<L::RBF>(sK, 16 * kb, 32 * cb), Vf[kb]);
+        if constexpr (DECAY) {  // the state as the next chunk's rows see it: moved on by gamma^64
+          if (it < n) {
+#pragma unroll
+            for (int cb = 0; cb < DF / 32; ++cb) S[cb] = (S[cb] * gH) * gH;
+          }
+        }
       }
       for (int bar = 0; bar < L::NBAR; ++bar) __syncthreads();
     }
