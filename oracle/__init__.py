@@ -25,6 +25,7 @@ from .linattn_oracle import (  # noqa: F401
     phi_elu1,
     phi_identity,
     phi_performer,
+    phi_poly2,
     recurrent,
     recurrent_backward,
 )

@@ -29,6 +29,9 @@ listed with its reasons in the design notes of the repository):
     implementations drop the denominator; [UL]'s example does);
   * elu+1 uses alpha = 1 and takes the exponential branch at x = 0 ([LT]
     "La función ELU + 1");
+  * the polynomial map is truncated at degree 2 with unit coefficients,
+    phi(x) = (1, x, x (x) x) with x (x) x row-major, so the kernel is
+    1 + q.k + (q.k)^2 (always >= 3/4);
   * random features: phi(x) = exp(W x~ - |x~|^2/2) / sqrt(m) with
     x~ = d^(-1/4) x, so that E[phi(q).phi(k)] = exp(q.k / sqrt(d)), the
     kernel that [LA] "Reformulación con núcleos" writes for softmax;
@@ -57,7 +60,7 @@ import numpy as np
 
 EPS = 1e-6
 
-FMAPS = ("elu1", "performer", "identity")
+FMAPS = ("elu1", "performer", "identity", "poly2")
 
 
 # ---------------------------------------------------------------------------
@@ -90,6 +93,21 @@ def phi_identity(x):
     return np.asarray(x, dtype=np.float64)
 
 
+def phi_poly2(x):
+    """Degree-2 truncation of the polynomial map (1, x, x (x) x, ...)
+    ([LA] "Mapas de características", polynomial bullet).
+
+    Reading: no coefficients on the terms; the d x d block of x (x) x is laid
+    out row-major, entry 1 + d + a d + b = x_a x_b. Then
+    phi(q).phi(k) = 1 + q.k + (q.k)^2. d' = 1 + d + d^2.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    outer = x[..., :, None] * x[..., None, :]
+    one = np.ones(x.shape[:-1] + (1,))
+    return np.concatenate([one, x, outer.reshape(x.shape[:-1] + (d * d,))], axis=-1)
+
+
 def feature_map(x, fmap="elu1", W=None):
     if fmap == "elu1":
         return phi_elu1(x)
@@ -99,10 +117,14 @@ def feature_map(x, fmap="elu1", W=None):
         return phi_performer(x, W)
     if fmap == "identity":
         return phi_identity(x)
+    if fmap == "poly2":
+        return phi_poly2(x)
     raise ValueError(f"unknown feature map {fmap!r}")
 
 
 def feature_dim(d, fmap="elu1", W=None):
+    if fmap == "poly2":
+        return 1 + d + d * d
     return int(np.asarray(W).shape[0]) if fmap == "performer" else d
 
 

@@ -148,6 +148,19 @@ GATED_MUTANTS = [
 ]
 
 
+POLY_MUTANTS = [
+    ("one = np.ones(x.shape[:-1] + (1,))", "one = np.zeros(x.shape[:-1] + (1,))",
+     "polynomial map: constant term dropped"),
+    ("return np.concatenate([one, x, outer.reshape", "return np.concatenate([one, 0.5 * x, outer.reshape",
+     "polynomial map: linear term scaled"),
+    ("outer = x[..., :, None] * x[..., None, :]", "outer = x[..., :, None] * x[..., None, ::-1]",
+     "polynomial map: second factor of x (x) x reversed"),
+    ("outer = x[..., :, None] * x[..., None, :]", "outer = np.triu(x[..., :, None] * x[..., None, :])",
+     "polynomial map: upper triangle of x (x) x only"),
+    ("        return 1 + d + d * d", "        return d + d * d", "polynomial map: feature dimension without the 1"),
+]
+
+
 def _run_pins(tmp_path, src, init=INIT, pins="test_oracle_pins.py"):
     pkg = tmp_path / "oracle"
     pkg.mkdir()
@@ -160,7 +173,8 @@ def _run_pins(tmp_path, src, init=INIT, pins="test_oracle_pins.py"):
     return r.returncode, r.stdout[-2000:]
 
 
-@pytest.mark.parametrize("pins", ["test_oracle_pins.py", "test_oracle_backward_pins.py", "test_oracle_gated_pins.py"])
+@pytest.mark.parametrize("pins", ["test_oracle_pins.py", "test_oracle_backward_pins.py", "test_oracle_gated_pins.py",
+                                  "test_oracle_poly_pins.py"])
 def test_control_unaltered_copy_passes(tmp_path, pins):
     rc, out = _run_pins(tmp_path, SRC, pins=pins)
     assert rc == 0, out
@@ -189,4 +203,11 @@ def test_backward_pins_catch_planted_mistake(tmp_path, old, new, what):
 def test_gated_pins_catch_planted_mistake(tmp_path, old, new, what):
     assert SRC.count(old) >= 1, f"mutation site not found: {old!r}"
     rc, out = _run_pins(tmp_path, SRC.replace(old, new, 1), pins="test_oracle_gated_pins.py")
+    assert rc != 0, f"the pins did not catch: {what}\n{out}"
+
+
+@pytest.mark.parametrize("old,new,what", POLY_MUTANTS, ids=[m[2] for m in POLY_MUTANTS])
+def test_poly_pins_catch_planted_mistake(tmp_path, old, new, what):
+    assert SRC.count(old) >= 1, f"mutation site not found: {old!r}"
+    rc, out = _run_pins(tmp_path, SRC.replace(old, new, 1), pins="test_oracle_poly_pins.py")
     assert rc != 0, f"the pins did not catch: {what}\n{out}"
