@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "LA_OK", "LA_ERR_INVALID_ARG", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_HIP",
-    "LA_F32", "LA_BF16", "LA_ELU1", "LA_PERFORMER", "LA_IDENTITY",
+    "LA_F32", "LA_BF16", "LA_ELU1", "LA_PERFORMER", "LA_IDENTITY", "LA_POLY2",
     "la_feature_map", "lib", "library_path", "LinAttnError",
     "la_version", "la_status_string", "la_forward_workspace_size", "la_forward", "la_forward_ex",
     "la_decode_step", "la_feature_map_apply", "feature_dim", "la_forward_decay", "la_decode_step_decay",
@@ -41,6 +41,7 @@ LA_BF16 = 1
 LA_ELU1 = 0
 LA_PERFORMER = 1
 LA_IDENTITY = 2
+LA_POLY2 = 3
 
 
 class la_feature_map(ctypes.Structure):
@@ -135,6 +136,8 @@ def _fmap(feature_map: str, W):
         return la_feature_map(LA_ELU1, 0, None)
     if feature_map in ("identity", LA_IDENTITY):
         return la_feature_map(LA_IDENTITY, 0, None)
+    if feature_map in ("poly2", LA_POLY2):
+        return la_feature_map(LA_POLY2, 0, None)
     if feature_map in ("performer", LA_PERFORMER):
         if W is None:
             raise ValueError("the performer map needs W (m x d, float32, on the device)")
@@ -145,6 +148,8 @@ def _fmap(feature_map: str, W):
 
 
 def feature_dim(d: int, feature_map: str = "elu1", W=None) -> int:
+    if feature_map in ("poly2", LA_POLY2):
+        return 1 + d + d * d
     return int(W.shape[0]) if feature_map in ("performer", LA_PERFORMER) else d
 
 

@@ -41,6 +41,7 @@ bool perf_supported(int d, int m) {
 int feature_dim(const la_feature_map* fm, int d) {
   if (!fm) return LA_ERR_INVALID_ARG;
   if (fm->kind == LA_ELU1 || fm->kind == LA_IDENTITY) return d;
+  if (fm->kind == LA_POLY2) return (d == 32 || d == 64) ? 1 + d + d * d : LA_ERR_UNSUPPORTED;
   if (fm->kind == LA_PERFORMER) {
     if (fm->m <= 0 || !fm->W || !aligned16(fm->W)) return LA_ERR_INVALID_ARG;
     if (!perf_supported(d, fm->m)) return LA_ERR_UNSUPPORTED;
@@ -98,6 +99,15 @@ Plan make_plan(long long BH, int N, int d, int dfeat, bool causal, bool mapped_i
 
 int status_from_hip(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_HIP; }
 
+// Polynomial map: partial numerators, then the denominators.
+size_t poly_part_bytes(long long BH, int N, int d) {
+  return align256((size_t)la::poly_partials(d) * BH * N * d * sizeof(float));
+}
+size_t poly_ws_bytes(long long BH, int N, int d) {
+  if (BH == 0 || N == 0) return 0;
+  return poly_part_bytes(BH, N, d) + align256((size_t)BH * N * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,6 +129,7 @@ size_t la_forward_workspace_size(int B, int H, int N, int d, const la_feature_ma
   if (B < 0 || H < 0 || N < 0 || !d_supported(d)) return 0;
   const int dfeat = feature_dim(feature_map, d);
   if (dfeat <= 0) return 0;
+  if (feature_map->kind == LA_POLY2) return poly_ws_bytes((long long)B * H, N, d);
   return make_plan((long long)B * H, N, d, dfeat, causal != 0, feature_map->kind == LA_PERFORMER).ws_bytes;
 }
 
@@ -174,6 +185,40 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
                 overlaps(z_out, z_bytes, v, tok_bytes) || overlaps(z_out, z_bytes, out, tok_bytes)))
     return LA_ERR_INVALID_ARG;
 
+  if (feature_map->kind == LA_POLY2) {
+    if (gamma) return LA_ERR_UNSUPPORTED;
+    const size_t need = poly_ws_bytes(BH, N, d);
+    if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LA_ERR_INVALID_ARG;
+    const long long wsz = (long long)need;
+    if (overlaps(workspace, wsz, out, tok_bytes) || overlaps(workspace, wsz, q, tok_bytes) ||
+        overlaps(workspace, wsz, k, tok_bytes) || overlaps(workspace, wsz, v, tok_bytes) ||
+        overlaps(workspace, wsz, S_out, s_bytes) || overlaps(workspace, wsz, z_out, z_bytes) ||
+        overlaps(workspace, wsz, S_in, s_bytes) || overlaps(workspace, wsz, z_in, z_bytes))
+      return LA_ERR_INVALID_ARG;
+    if (events && hipEventRecord(events[0], stream) != hipSuccess) return LA_ERR_HIP;
+    la::PolyArgs pa{};
+    pa.q = q;
+    pa.k = k;
+    pa.v = v;
+    pa.out = out;
+    pa.BH = (int)BH;
+    pa.N = N;
+    pa.nchunks = (N + kChunk - 1) / kChunk;
+    pa.normalize = normalize;
+    pa.part = static_cast<float*>(workspace);
+    pa.den = reinterpret_cast<float*>(static_cast<char*>(workspace) + poly_part_bytes(BH, N, d));
+    pa.S_in = S_in;
+    pa.z_in = z_in;
+    pa.S_out = S_out;
+    pa.z_out = z_out;
+    const int st = status_from_hip(la::poly_forward_dispatch(pa, d, dtype, causal != 0, stream));
+    if (st == LA_OK && events) {  // one pass: the state, scan and output markers coincide at its end
+      for (int i = 1; i < 4; ++i)
+        if (hipEventRecord(events[i], stream) != hipSuccess) return LA_ERR_HIP;
+    }
+    return st;
+  }
   const bool mapped = feature_map->kind == LA_PERFORMER;
   if (mapped) {
     const long long wb = (long long)dfeat * d * 4;
@@ -350,6 +395,10 @@ int decode_impl(float* S, float* z, const void* q, const void* k, const void* v,
   a.W = feature_map->W;
   a.gamma = gamma;
   a.H = H;
+  if (feature_map->kind == LA_POLY2) {
+    if (gamma) return LA_ERR_UNSUPPORTED;
+    return status_from_hip(la::poly_decode_dispatch(a, d, dtype, stream));
+  }
   return status_from_hip(la::decode_dispatch(a, d, dfeat, feature_map->kind, dtype, stream));
 }
 
@@ -389,6 +438,7 @@ int la_feature_map_apply(const void* x, void* phi, long long rows, int d, const 
   a.phi = phi;
   a.rows = rows;
   a.W = feature_map->W;
+  if (feature_map->kind == LA_POLY2) return status_from_hip(la::poly_fmap_dispatch(a, d, in_dtype, out_dtype, stream));
   return status_from_hip(la::fmap_dispatch(a, d, dfeat, feature_map->kind, in_dtype, out_dtype, stream));
 }
 
@@ -418,7 +468,7 @@ BwdPlan make_bwd_plan(long long BH, int N, int d) {
 int bwd_map(const la_feature_map* fm, int d) {
   const int dfeat = feature_dim(fm, d);
   if (dfeat < 0) return dfeat;
-  return fm->kind == LA_PERFORMER ? LA_ERR_UNSUPPORTED : LA_OK;
+  return (fm->kind == LA_PERFORMER || fm->kind == LA_POLY2) ? LA_ERR_UNSUPPORTED : LA_OK;
 }
 
 }  // namespace
@@ -744,6 +794,7 @@ int la_decode_step_gated(float* S, float* z, const void* q, const void* k, const
   if (!d_supported(d)) return LA_ERR_UNSUPPORTED;
   const int dfeat = feature_dim(feature_map, d);
   if (dfeat < 0) return dfeat;
+  if (feature_map->kind == LA_POLY2) return LA_ERR_UNSUPPORTED;
   const long long BH = (long long)B * H;
   if (BH == 0) return LA_OK;
   if (!log_gate || !aligned16(log_gate)) return LA_ERR_INVALID_ARG;

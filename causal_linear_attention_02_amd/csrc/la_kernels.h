@@ -117,6 +117,24 @@ struct GatedArgs {
   float* lfac;             // [BH][f.nseg][D] fp32 (workspace)
 };
 
+// Degree-2 polynomial map (d' = 1 + d + d^2), chunked forward. Workspace:
+// partial numerators [poly_partials(D)][BH][N][D] fp32, then the
+// denominators [BH][N] fp32.
+struct PolyArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  int BH, N, nchunks;
+  int normalize;
+  float* part;
+  float* den;
+  const float* S_in;  // [BH][d'][D] or null
+  const float* z_in;  // [BH][d']
+  float* S_out;       // written at the end (causal: final state; non-causal: the total)
+  float* z_out;
+};
+
 struct FmapArgs {
   const void* x;    // [rows][D]
   void* phi;        // [rows][DF]
@@ -131,6 +149,10 @@ hipError_t backward_dispatch(const FwdArgs& fa, const ScanArgs& fs, const BwdArg
                              int fmap, int dtype, bool decay, hipStream_t st);
 hipError_t gated_dispatch(const GatedArgs& g, const ScanArgs& s, int D, int fmap, int dtype, hipStream_t st);
 hipError_t decode_dispatch(const DecodeArgs& a, int D, int DF, int fmap, int dtype, hipStream_t st);
+int poly_partials(int D);
+hipError_t poly_forward_dispatch(const PolyArgs& a, int D, int dtype, bool causal, hipStream_t st);
+hipError_t poly_decode_dispatch(const DecodeArgs& a, int D, int dtype, hipStream_t st);
+hipError_t poly_fmap_dispatch(const FmapArgs& a, int D, int in_dtype, int out_dtype, hipStream_t st);
 hipError_t fmap_dispatch(const FmapArgs& a, int D, int DF, int fmap, int in_dtype, int out_dtype, hipStream_t st);
 hipError_t copy_state_dispatch(const float* S_in, const float* z_in, float* S_out, float* z_out, long long nS,
                                long long nz, hipStream_t st);

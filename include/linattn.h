@@ -63,10 +63,15 @@ extern "C" {
 #define LA_PERFORMER 1 /* positive random features, d' = m */
 #define LA_IDENTITY 2  /* phi(x) = x, d' = d; the denominator may be <= 0 (then clamped to 1e-6),
                           so normalize = 0 is its usual use */
+#define LA_POLY2 3     /* degree-2 polynomial map ("Mapas de características", polynomial item):
+                          phi(x) = (1, x, x (x) x), unit coefficients, x (x) x row-major
+                          (feature 1 + d + a d + b = x_a x_b), so phi(q).phi(k) = 1 + q.k + (q.k)^2
+                          (>= 3/4); d' = 1 + d + d^2. d in {32, 64}; la_forward, la_decode_step and
+                          la_feature_map_apply only */
 
 typedef struct la_feature_map {
-  int kind;        /* LA_ELU1, LA_PERFORMER or LA_IDENTITY */
-  int m;           /* LA_PERFORMER: number of features (d'); ignored for LA_ELU1 */
+  int kind;        /* LA_ELU1, LA_PERFORMER, LA_IDENTITY or LA_POLY2 */
+  int m;           /* LA_PERFORMER: number of features (d'); ignored otherwise */
   const float* W;  /* LA_PERFORMER: device pointer, m x d fp32 row-major, shared by all
                       batches and heads; bf16 inputs use W rounded to bf16. Ignored otherwise */
 } la_feature_map;
@@ -81,7 +86,9 @@ const char* la_status_string(int status);
  * Bytes of device workspace that la_forward needs for these sizes (0 when
  * none is needed; any element type). Returns 0 also for invalid arguments.
  * It holds the fp32 states of the sequence segments and, for random features,
- * phi(q) and phi(k) ([B][H][N][m] each, sized for fp32).
+ * phi(q) and phi(k) ([B][H][N][m] each, sized for fp32). With LA_POLY2 it
+ * holds fp32 partial numerators (3 per token at d = 32, 5 at d = 64, [N][d]
+ * each per (batch, head)) and the denominators.
  */
 size_t la_forward_workspace_size(int B, int H, int N, int d, const la_feature_map* feature_map, int causal);
 
@@ -249,7 +256,7 @@ int la_forward_gated(const void* q, const void* k, const void* v, const float* l
 /*
  * la_decode_step with a per-feature gate: S <- diag(exp(log_gate)) S + phi(k) v^T,
  * z <- exp(log_gate) * z + phi(k), then the readout. log_gate: DEVICE pointer,
- * [B][H][d'] fp32 (any value <= 0 is valid here). All maps.
+ * [B][H][d'] fp32 (any value <= 0 is valid here). Every map but LA_POLY2.
  */
 int la_decode_step_gated(float* S, float* z, const void* q, const void* k, const void* v, const float* log_gate,
                          void* out, int B, int H, int d, const la_feature_map* feature_map, int normalize, int dtype,

@@ -249,3 +249,33 @@ def test_gated_entry_points_validate_before_launch():
     st = lib.la_decode_step_gated(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000, None,
                                   FAKE + 0x500000, 1, 1, 64, ctypes.byref(ELU), 1, la.LA_BF16, None)
     assert st == la.LA_ERR_INVALID_ARG                                    # gate missing
+
+
+def test_poly2_map_planning_and_limits():
+    poly = la_feature_map(la.LA_POLY2, 0, None)
+    B, H, N = 2, 3, 1000
+    for d, slots in ((32, 3), (64, 5)):
+        n = lib.la_forward_workspace_size(B, H, N, d, ctypes.byref(poly), 1)
+        # partial numerators (fp32, [slots][B*H][N][d]) and the denominators
+        assert n >= slots * B * H * N * d * 4 + B * H * N * 4
+        assert n == lib.la_forward_workspace_size(B, H, N, d, ctypes.byref(poly), 0)
+    assert lib.la_forward_workspace_size(1, 1, 64, 128, ctypes.byref(poly), 1) == 0   # d' = 16513: not built
+    assert lib.la_forward_workspace_size(1, 1, 0, 64, ctypes.byref(poly), 1) == 0
+    need = lib.la_forward_workspace_size(1, 1, 128, 64, ctypes.byref(poly), 1)
+    assert _fwd(fm=poly, d=128) == la.LA_ERR_UNSUPPORTED
+    assert _fwd(fm=poly) == la.LA_ERR_WORKSPACE
+    assert _fwd(fm=poly, ws=FAKE2 * 4, ws_bytes=need - 1) == la.LA_ERR_WORKSPACE
+    assert _fwd(fm=poly, ws=FAKE2 * 4 + 16, ws_bytes=need) == la.LA_ERR_INVALID_ARG   # not 256-aligned
+    assert _fwd(fm=poly, ws=FAKE2, ws_bytes=need) == la.LA_ERR_INVALID_ARG            # overlaps out
+    assert _fwd(fm=poly, N=0) == la.LA_OK
+    st = lib.la_forward_decay(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE2, 1, 1, 128, 64, ctypes.byref(poly),
+                              FAKE2 * 9, 1, la.LA_BF16, None, None, None, None, FAKE2 * 4, need, None)
+    assert st == la.LA_ERR_UNSUPPORTED                                    # no decay with this map
+    assert _bwd(fm=poly) == la.LA_ERR_UNSUPPORTED                          # no gradients with this map
+    st = lib.la_forward_gated(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE2 * 8, FAKE2, 1, 1, 128, 64,
+                              ctypes.byref(poly), 1, la.LA_BF16, None, None, None, None, FAKE2 * 4, 1 << 30, None)
+    assert st == la.LA_ERR_UNSUPPORTED
+    st = lib.la_decode_step_gated(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000,
+                                  FAKE2 * 8, FAKE + 0x500000, 1, 1, 64, ctypes.byref(poly), 1, la.LA_BF16, None)
+    assert st == la.LA_ERR_UNSUPPORTED
+    assert la.feature_dim(64, "poly2") == 4161
