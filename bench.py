@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--gated-steps", type=int, default=20)
     p.add_argument("--no-gated", action="store_true")
     p.add_argument("--no-variants", action="store_true")
+    p.add_argument("--poly-steps", type=int, default=50)
+    p.add_argument("--no-poly", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="time budget of the oracle's prefill sample (whole heads; the decode sample gets half)")
@@ -264,6 +266,50 @@ def main():
 
     del tq, tk, tv, out, ws
     torch.cuda.empty_cache()
+
+    # ---------------- degree-2 polynomial map (d' = 1 + d + d^2) ----------------
+    poly = None
+    if not args.no_poly:
+        Wp = la_inputs.WORKLOADS["prefill_b4h8n2048d64"]
+        Bp, Hp, Np, dp = Wp["B"], Wp["H"], Wp["N"], Wp["d"]
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(Wp["seed"])
+        shp = (Bp, Hp, Np, dp)
+        pq, pk, pv = ((torch.randn(shp, generator=gen, device=dev) * s_).to(torch.bfloat16)
+                      for s_ in (Wp["scale"], Wp["scale"], 1.0))
+        pout = torch.empty_like(pq)
+        pws = torch.empty(la.la_forward_workspace_size(Bp, Hp, Np, dp, feature_map="poly2"), dtype=torch.uint8,
+                          device=dev)
+
+        def pfwd():
+            la.la_forward(pq, pk, pv, feature_map="poly2", normalize=True, out=pout, workspace=pws)
+
+        for _ in range(20):
+            pfwd()
+        torch.cuda.synchronize()
+        log(f"poly2: timing {args.poly_steps} calls")
+        t0 = time.perf_counter()
+        for _ in range(args.poly_steps):
+            pfwd()
+        torch.cuda.synchronize()
+        pwall = (time.perf_counter() - t0) / args.poly_steps
+        p_ht = Bp * Hp * Np
+        # dense contractions per head-token: degree-2 read-out and update (2 d^3 each),
+        # degree-1 and normalizer states (8 d^2), in-chunk scores and products (2 (C+1) d)
+        p_flops = p_ht * (4 * dp ** 3 + 8 * dp * dp + 2 * (C + 1) * dp)
+        p_tf = p_flops / pwall / 1e12
+        poly = {
+            "metric": "causal prefill tokens/s, degree-2 polynomial map (d' = 1 + d + d^2)",
+            "value": Bp * Np / pwall, "unit": "tokens/s", "us_per_call": round(pwall * 1e6, 1),
+            "steps": args.poly_steps,
+            "config": {"workload": "prefill_b4h8n2048d64", "batch": Bp, "heads": Hp, "seq_len": Np, "d": dp,
+                       "feature_dim": 1 + dp + dp * dp, "feature_map": "poly2", "normalize": True},
+            "mfma": {"useful_tflops": round(p_tf, 2), "frac_bf16_mfma": round(p_tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "flops_per_head_token": 4 * dp ** 3 + 8 * dp * dp + 2 * (C + 1) * dp},
+        }
+        log(f"poly2: {pwall*1e6:.1f} us/call, {p_tf:.1f} TFLOP/s")
+        del pq, pk, pv, pout, pws
+        torch.cuda.empty_cache()
     prefill_sources = ["la_prefill.hip", "la_device.h", "la_kernels.h"]
     out_traffic, out_note = read_traffic("traffic_output_pass_prefill_b1h16n65536d128.txt", prefill_sources,
                                          alg_bytes)
@@ -415,6 +461,7 @@ def main():
         "backward": backward,
         "gated": gated,
         "variants": variants,
+        "poly2": poly,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result))

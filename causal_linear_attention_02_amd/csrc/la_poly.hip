@@ -67,15 +67,16 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
   constexpr int TS = 68;                   // row stride (floats) of the transposed fp32 tiles
   constexpr int TTB = D * TS * 4;
   constexpr int RL = D / 8;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * TB + 3 * TTB + C::NW * 1024 * 4];
+  constexpr int VB = TB > TTB ? TB : TTB;  // sV (low-degree workgroup) and sVt (the others) share it
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TB + 2 * TTB + VB + C::NW * 2048 * 4];
   __shared__ float dint[64], dpart[C::NE][64];
   uint8_t* sQ = smem;
   uint8_t* sK = smem + TB;
-  uint8_t* sV = smem + 2 * TB;
-  float* sQt = reinterpret_cast<float*>(smem + 3 * TB);  // [feature][row]
+  float* sQt = reinterpret_cast<float*>(smem + 2 * TB);  // [feature][row]
   float* sKt = sQt + D * TS;
-  float* sVt = sKt + D * TS;
-  float* red = sVt + D * TS;                              // [wave][16 registers][64 lanes]
+  uint8_t* sV = smem + 2 * TB + 2 * TTB;
+  float* sVt = reinterpret_cast<float*>(sV);
+  float* red = reinterpret_cast<float*>(smem + 2 * TB + 2 * TTB + VB);  // [wave][2][16 registers][64 lanes]
 
   const int bh = blockIdx.x, blk = blockIdx.y;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, hh = l >> 5, li = l & 31;
@@ -86,30 +87,47 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
   const IN* k = static_cast<const IN*>(a.k);
   const IN* v = static_cast<const IN*>(a.v);
 
-  // every thread stages one 8-element piece of q, k and v per chunk: into the
-  // swizzled operand tiles and, transposed and in fp32, into the feature-major tiles
-  auto stage = [&](int c) {
-    const int valid = min(64, a.N - 64 * c);
-    const int row = t / RL, c0 = 8 * (t % RL);
+  // Every thread moves one 8-element piece of q, k and v per chunk: loaded
+  // into registers one chunk ahead (fetch), then written (put) into the
+  // swizzled operand tiles and, transposed and in fp32, into the
+  // feature-major tiles (v: the operand tile in the low-degree workgroup,
+  // the transposed one in the others).
+  using Raw = typename In8<IN>::raw;
+  struct Piece {
+    Raw q, k, v;
+  };
+  const int prow = t / RL, pc0 = 8 * (t % RL);
+  auto fetch = [&](int c) -> Piece {
+    Piece pc;
+    const bool live = c < a.nchunks && prow < min(64, a.N - 64 * c);
+    const long long off = live ? (base + 64LL * c + prow) * D + pc0 : 0;
+    pc.q = live ? In8<IN>::load(q + off) : In8<IN>::zero();
+    pc.k = live ? In8<IN>::load(k + off) : In8<IN>::zero();
+    pc.v = live ? In8<IN>::load(v + off) : In8<IN>::zero();
+    return pc;
+  };
+  Piece cur = fetch(0);
+  auto put = [&]() {
     float xq[8], xk[8], xv[8];
-    if (row < valid) {
-      const long long off = (base + 64LL * c + row) * D + c0;
-      In8<IN>::to_f32(In8<IN>::load(q + off), xq);
-      In8<IN>::to_f32(In8<IN>::load(k + off), xk);
-      In8<IN>::to_f32(In8<IN>::load(v + off), xv);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xq[e] = xk[e] = xv[e] = 0.f;
-    }
-    Ops<OP>::template store8<RB>(sQ, row, c0, xq);
-    Ops<OP>::template store8<RB>(sK, row, c0, xk);
-    Ops<OP>::template store8<RB>(sV, row, c0, xv);
+    In8<IN>::to_f32(cur.q, xq);
+    In8<IN>::to_f32(cur.k, xk);
+    In8<IN>::to_f32(cur.v, xv);
+    Ops<OP>::template store8<RB>(sQ, prow, pc0, xq);
+    Ops<OP>::template store8<RB>(sK, prow, pc0, xk);
+    if (low) Ops<OP>::template store8<RB>(sV, prow, pc0, xv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      sQt[(c0 + e) * TS + row] = xq[e];
-      sKt[(c0 + e) * TS + row] = xk[e];
-      sVt[(c0 + e) * TS + row] = xv[e];
+      sQt[(pc0 + e) * TS + prow] = xq[e];
+      sKt[(pc0 + e) * TS + prow] = xk[e];
+      if (!low) sVt[(pc0 + e) * TS + prow] = xv[e];
     }
+  };
+  // chunk c into LDS, and the loads of chunk c + 1 issued
+  auto stage = [&](int c) {
+    if (c == 0) cur = fetch(0);
+    put();
+    __syncthreads();
+    cur = fetch(c + 1);
   };
 
   if (!low) {
@@ -157,44 +175,45 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
         for (int bb = 0; bb < C::NBB; ++bb)
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk) bf[bb][kk] = Ops<OP>::from_acc(ST[ia * C::NBB + bb], kk);
+        // both row blocks at once: two independent accumulation chains
+        f32x16 R[2] = {};
+#pragma unroll
+        for (int bb = 0; bb < C::NBB; ++bb)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+              Ops<OP>::mma(R[ib], Ops<OP>::template load_rows<RB>(sQ, 32 * ib, 32 * bb + 16 * kk), bf[bb][kk]);
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
-          f32x16 R = {};
-#pragma unroll
-          for (int bb = 0; bb < C::NBB; ++bb)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-              Ops<OP>::mma(R, Ops<OP>::template load_rows<RB>(sQ, 32 * ib, 32 * bb + 16 * kk), bf[bb][kk]);
           const float* qa = sQt + (a0 + ia) * TS + 32 * ib + 4 * hh;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const f32x4 qv = *reinterpret_cast<const f32x4*>(qa + 8 * g);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) Y[ib][4 * g + u] += qv[u] * R[4 * g + u];
+            for (int u = 0; u < 4; ++u) Y[ib][4 * g + u] += qv[u] * R[ib][4 * g + u];
           }
         }
       }
-      // sum the waves' tiles (one 32-row block at a time) and store the partial
+      // sum the waves' tiles and store the partial (the next writes to red
+      // come after the next chunk's staging barrier)
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
+      for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) red[(w * 16 + r) * 64 + l] = Y[ib][r];
-        __syncthreads();
-        for (int x = t; x < 1024; x += C::NT) {
-          float s = 0.f;
+        for (int r = 0; r < 16; ++r) red[((w * 2 + ib) * 16 + r) * 64 + l] = Y[ib][r];
+      __syncthreads();
+      for (int x = t; x < 2048; x += C::NT) {
+        float s = 0.f;
 #pragma unroll
-          for (int ww = 0; ww < C::NW; ++ww) s += red[ww * 1024 + x];
-          const int r = x >> 6, ll = x & 63;
-          const int row = 32 * ib + acc_row(r, ll >> 5);
-          if (row < valid) part[(64LL * c + row) * D + 32 * E + (ll & 31)] = s;
-        }
-        __syncthreads();
+        for (int ww = 0; ww < C::NW; ++ww) s += red[ww * 2048 + x];
+        const int ib = x >> 10, r = (x >> 6) & 15, ll = x & 63;
+        const int row = 32 * ib + acc_row(r, ll >> 5);
+        if (row < valid) part[(64LL * c + row) * D + 32 * E + (ll & 31)] = s;
       }
     };
     if constexpr (CAUSAL) {
       for (int c = 0; c < a.nchunks; ++c) {
         stage(c);
-        __syncthreads();
         readout(c);  // the state of the chunks before this one
         update();
         __syncthreads();
@@ -202,14 +221,13 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
     } else {
       for (int c = 0; c < a.nchunks; ++c) {
         stage(c);
-        __syncthreads();
         update();
         __syncthreads();
       }
       for (int c = 0; c < a.nchunks; ++c) {
         stage(c);
-        __syncthreads();
         readout(c);
+        __syncthreads();
       }
     }
     if (a.S_out) {
@@ -339,7 +357,6 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
   if constexpr (CAUSAL) {
     for (int c = 0; c < a.nchunks; ++c) {
       stage(c);
-      __syncthreads();
       readout(c, true);
       update(c);
       __syncthreads();
@@ -347,13 +364,11 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
   } else {
     for (int c = 0; c < a.nchunks; ++c) {
       stage(c);
-      __syncthreads();
       update(c);
       __syncthreads();
     }
     for (int c = 0; c < a.nchunks; ++c) {
       stage(c);
-      __syncthreads();
       readout(c, false);
       __syncthreads();
     }
