@@ -105,7 +105,7 @@ size_t poly_part_bytes(long long BH, int N, int d) {
 }
 size_t poly_ws_bytes(long long BH, int N, int d) {
   if (BH == 0 || N == 0) return 0;
-  return poly_part_bytes(BH, N, d) + align256((size_t)BH * N * sizeof(float));
+  return poly_part_bytes(BH, N, d) + align256((size_t)la::poly_den_slots(d) * BH * N * sizeof(float));
 }
 
 }  // namespace

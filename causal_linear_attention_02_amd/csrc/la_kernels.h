@@ -118,8 +118,8 @@ struct GatedArgs {
 };
 
 // Degree-2 polynomial map (d' = 1 + d + d^2), chunked forward. Workspace:
-// partial numerators [poly_partials(D)][BH][N][D] fp32, then the
-// denominators [BH][N] fp32.
+// partial numerators [poly_partials(D)][BH][N][D] fp32, then partial
+// denominators [poly_den_slots(D)][BH][N] fp32.
 struct PolyArgs {
   const void* q;
   const void* k;
@@ -150,6 +150,7 @@ hipError_t backward_dispatch(const FwdArgs& fa, const ScanArgs& fs, const BwdArg
 hipError_t gated_dispatch(const GatedArgs& g, const ScanArgs& s, int D, int fmap, int dtype, hipStream_t st);
 hipError_t decode_dispatch(const DecodeArgs& a, int D, int DF, int fmap, int dtype, hipStream_t st);
 int poly_partials(int D);
+int poly_den_slots(int D);
 hipError_t poly_forward_dispatch(const PolyArgs& a, int D, int dtype, bool causal, hipStream_t st);
 hipError_t poly_decode_dispatch(const DecodeArgs& a, int D, int dtype, hipStream_t st);
 hipError_t poly_fmap_dispatch(const FmapArgs& a, int D, int in_dtype, int out_dtype, hipStream_t st);

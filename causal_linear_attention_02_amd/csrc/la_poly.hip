@@ -14,12 +14,14 @@
 //   y_i[E] += sum_a q_ia (sum_b q_ib S2[a][b][E])     (MFMA over b, q_ia on the result)
 // and updates
 //   S2[a][b][E] += sum_j k_jb (k_ja v_j[E])            (MFMA over j, k_ja on the values).
-// One more workgroup per (batch, head) holds the low-degree state
-// (S0 = sum v, S1 = sum k v^T), the normalizer state (n, z1 = sum k,
-// Z2 = sum k k^T) and forms the in-chunk part with the kernel applied to the
-// scores, A_ij = 1 + s_ij + s_ij^2 (j <= i). Every workgroup walks the chunks
-// in order and writes its partial numerators (fp32) to the workspace; the
-// low-degree workgroup also writes the denominators. A last kernel sums the
+// The low-degree state (S0 = sum v, S1 = sum k v^T) and the normalizer state
+// (n, z1 = sum k, Z2 = sum k k^T) are small; they sit in LDS in the first
+// two workgroups of each value block, where a few waves read them out and
+// update them beside their own tiles, and form the in-chunk part with the
+// kernel applied to the scores, A_ij = 1 + s_ij + s_ij^2 (j <= i). So a head
+// takes exactly NE * NA workgroups, one per compute unit. Every workgroup
+// walks the chunks in order and writes its partial numerators (fp32) to the
+// workspace, and some write partial denominators; a last kernel sums the
 // partials and divides. Non-causal: every chunk updates first, then every
 // chunk reads out the total.
 #include "la_device.h"
@@ -67,31 +69,34 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
   constexpr int TS = 68;                   // row stride (floats) of the transposed fp32 tiles
   constexpr int TTB = D * TS * 4;
   constexpr int RL = D / 8;
-  constexpr int VB = TB > TTB ? TB : TTB;  // sV (low-degree workgroup) and sVt (the others) share it
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TB + 2 * TTB + VB + C::NW * 2048 * 4];
-  __shared__ float dint[64], dpart[C::NE][64];
+  constexpr int NB = C::NBB;
+  // operand tiles Q, K; fp32 feature-major tiles Q^T, K^T, V^T; the waves'
+  // partial outputs; the low-degree state tiles (fp32, accumulator layout)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TB + 3 * TTB + C::NW * 2048 * 4 + (NB + 1) * 4096];
   uint8_t* sQ = smem;
   uint8_t* sK = smem + TB;
   float* sQt = reinterpret_cast<float*>(smem + 2 * TB);  // [feature][row]
   float* sKt = sQt + D * TS;
-  uint8_t* sV = smem + 2 * TB + 2 * TTB;
-  float* sVt = reinterpret_cast<float*>(sV);
-  float* red = reinterpret_cast<float*>(smem + 2 * TB + 2 * TTB + VB);  // [wave][2][16 registers][64 lanes]
+  float* sVt = sKt + D * TS;
+  float* red = sVt + D * TS;                              // [wave][2][16 registers][64 lanes]
+  float* lowst = red + C::NW * 2048;                     // [tile][16 registers][64 lanes]
 
   const int bh = blockIdx.x, blk = blockIdx.y;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, hh = l >> 5, li = l & 31;
-  const bool low = blk == C::NE * C::NA;
+  const int E = blk % C::NE, hb = blk / C::NE;
+  const int a0 = hb * C::APB + w * C::APW;
   const long long base = (long long)bh * a.N;
   const long long SD = (long long)bh * C::DP;  // first state row of this (batch, head)
+  const long long BHN = (long long)a.BH * a.N;
   const IN* q = static_cast<const IN*>(a.q);
   const IN* k = static_cast<const IN*>(a.k);
   const IN* v = static_cast<const IN*>(a.v);
+  float* part = a.part + ((long long)hb * a.BH + bh) * a.N * D;
 
   // Every thread moves one 8-element piece of q, k and v per chunk: loaded
   // into registers one chunk ahead (fetch), then written (put) into the
   // swizzled operand tiles and, transposed and in fp32, into the
-  // feature-major tiles (v: the operand tile in the low-degree workgroup,
-  // the transposed one in the others).
+  // feature-major tiles.
   using Raw = typename In8<IN>::raw;
   struct Piece {
     Raw q, k, v;
@@ -114,12 +119,11 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
     In8<IN>::to_f32(cur.v, xv);
     Ops<OP>::template store8<RB>(sQ, prow, pc0, xq);
     Ops<OP>::template store8<RB>(sK, prow, pc0, xk);
-    if (low) Ops<OP>::template store8<RB>(sV, prow, pc0, xv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       sQt[(pc0 + e) * TS + prow] = xq[e];
       sKt[(pc0 + e) * TS + prow] = xk[e];
-      if (!low) sVt[(pc0 + e) * TS + prow] = xv[e];
+      sVt[(pc0 + e) * TS + prow] = xv[e];
     }
   };
   // chunk c into LDS, and the loads of chunk c + 1 issued
@@ -129,235 +133,236 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
     __syncthreads();
     cur = fetch(c + 1);
   };
-
-  if (!low) {
-    // ------------------------------------------------------------------
-    // quadratic part: value block E, a in [a0, a0 + APW) for this wave
-    // ------------------------------------------------------------------
-    const int E = blk % C::NE, hb = blk / C::NE;
-    const int a0 = hb * C::APB + w * C::APW;
-    float* part = a.part + ((long long)(1 + hb) * a.BH + bh) * a.N * D;
-    f32x16 ST[4];  // tile (ia, bb) at ia * NBB + bb: rows b = 32 bb + .., columns e = 32 E + ..
+  // value operand: V[j][e] for this lane's column e = 32 E + lane % 32 and
+  // rows j = j0 + 8 (lane / 32) + 0..7, optionally scaled per row
+  auto vfrag = [&](int j0, const float* scale) -> Frag {
+    const float* vt = sVt + (32 * E + li) * TS + j0 + 8 * hh;
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(vt), v1 = *reinterpret_cast<const f32x4*>(vt + 4);
+    float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    if (scale) {
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(scale + j0 + 8 * hh);
+      const f32x4 s1 = *reinterpret_cast<const f32x4*>(scale + j0 + 8 * hh + 4);
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int av = a0 + tt / C::NBB, bb = tt % C::NBB;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        ST[tt][r] = a.S_in ? a.S_in[(SD + 1 + D + av * D + 32 * bb + acc_row(r, hh)) * D + 32 * E + li] : 0.f;
-    }
-    auto update = [&]() {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        Frag kc[C::NBB];
-#pragma unroll
-        for (int bb = 0; bb < C::NBB; ++bb) kc[bb] = Ops<OP>::template load_cols<RB>(sK, 16 * kb, 32 * bb);
-        const float* vt = sVt + (32 * E + li) * TS + 16 * kb + 8 * hh;
-        const f32x4 v0 = *reinterpret_cast<const f32x4*>(vt), v1 = *reinterpret_cast<const f32x4*>(vt + 4);
-#pragma unroll
-        for (int ia = 0; ia < C::APW; ++ia) {
-          const float* kt = sKt + (a0 + ia) * TS + 16 * kb + 8 * hh;
-          const f32x4 k0 = *reinterpret_cast<const f32x4*>(kt), k1 = *reinterpret_cast<const f32x4*>(kt + 4);
-          const float x[8] = {v0[0] * k0[0], v0[1] * k0[1], v0[2] * k0[2], v0[3] * k0[3],
-                              v1[0] * k1[0], v1[1] * k1[1], v1[2] * k1[2], v1[3] * k1[3]};
-          const Frag vb = MkFrag<OP>::make(x);
-#pragma unroll
-          for (int bb = 0; bb < C::NBB; ++bb) Ops<OP>::mma(ST[ia * C::NBB + bb], kc[bb], vb);
-        }
-      }
-    };
-    auto readout = [&](int c) {
-      const int valid = min(64, a.N - 64 * c);
-      f32x16 Y[2] = {};
-#pragma unroll
-      for (int ia = 0; ia < C::APW; ++ia) {
-        Frag bf[C::NBB][2];
-#pragma unroll
-        for (int bb = 0; bb < C::NBB; ++bb)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) bf[bb][kk] = Ops<OP>::from_acc(ST[ia * C::NBB + bb], kk);
-        // both row blocks at once: two independent accumulation chains
-        f32x16 R[2] = {};
-#pragma unroll
-        for (int bb = 0; bb < C::NBB; ++bb)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib)
-              Ops<OP>::mma(R[ib], Ops<OP>::template load_rows<RB>(sQ, 32 * ib, 32 * bb + 16 * kk), bf[bb][kk]);
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-          const float* qa = sQt + (a0 + ia) * TS + 32 * ib + 4 * hh;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 qv = *reinterpret_cast<const f32x4*>(qa + 8 * g);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) Y[ib][4 * g + u] += qv[u] * R[ib][4 * g + u];
-          }
-        }
-      }
-      // sum the waves' tiles and store the partial (the next writes to red
-      // come after the next chunk's staging barrier)
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) red[((w * 2 + ib) * 16 + r) * 64 + l] = Y[ib][r];
-      __syncthreads();
-      for (int x = t; x < 2048; x += C::NT) {
-        float s = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < C::NW; ++ww) s += red[ww * 2048 + x];
-        const int ib = x >> 10, r = (x >> 6) & 15, ll = x & 63;
-        const int row = 32 * ib + acc_row(r, ll >> 5);
-        if (row < valid) part[(64LL * c + row) * D + 32 * E + (ll & 31)] = s;
-      }
-    };
-    if constexpr (CAUSAL) {
-      for (int c = 0; c < a.nchunks; ++c) {
-        stage(c);
-        readout(c);  // the state of the chunks before this one
-        update();
-        __syncthreads();
-      }
-    } else {
-      for (int c = 0; c < a.nchunks; ++c) {
-        stage(c);
-        update();
-        __syncthreads();
-      }
-      for (int c = 0; c < a.nchunks; ++c) {
-        stage(c);
-        readout(c);
-        __syncthreads();
+      for (int u = 0; u < 4; ++u) {
+        x[u] *= s0[u];
+        x[4 + u] *= s1[u];
       }
     }
-    if (a.S_out) {
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int av = a0 + tt / C::NBB, bb = tt % C::NBB;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          a.S_out[(SD + 1 + D + av * D + 32 * bb + acc_row(r, hh)) * D + 32 * E + li] = ST[tt][r];
-      }
-    }
-    return;
-  }
-
-  // --------------------------------------------------------------------
-  // low-degree workgroup. Waves 0 .. 2NE-1 ("num"): row block ib, value
-  // block E; they hold S1[:, E] (rows b) and S0[E] (every row of X equal).
-  // Waves 2NE .. 4NE-1 ("den"): row block ib, feature block Cb; they hold
-  // Z2[:, Cb] (rows b) and z1[Cb] (X: rows c, every column equal).
-  // --------------------------------------------------------------------
-  const bool numw = w < 2 * C::NE;
-  const int wr = numw ? w : w - 2 * C::NE;
-  const int ib = wr / C::NE, E = wr % C::NE;  // E: value block (num) or feature block (den)
-  float* part = a.part + (long long)bh * a.N * D;
+    return MkFrag<OP>::make(x);
+  };
   Frag ones;
   {
     const float o[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
     ones = MkFrag<OP>::make(o);
   }
-  f32x16 T[C::NBB], X;
+  auto ld_tile = [&](int ti) {
+    f32x16 x;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int rr = acc_row(r, hh);
+    for (int r = 0; r < 16; ++r) x[r] = lowst[(ti * 16 + r) * 64 + l];
+    return x;
+  };
+  auto st_tile = [&](int ti, const f32x16& x) {
 #pragma unroll
-    for (int bb = 0; bb < C::NBB; ++bb) {
-      if (numw)
-        T[bb][r] = a.S_in ? a.S_in[(SD + 1 + 32 * bb + rr) * D + 32 * E + li] : 0.f;
-      else
-        T[bb][r] = a.z_in ? a.z_in[SD + 1 + D + (32 * bb + rr) * D + 32 * E + li] : 0.f;
-    }
-    X[r] = numw ? (a.S_in ? a.S_in[SD * D + 32 * E + li] : 0.f) : (a.z_in ? a.z_in[SD + 1 + 32 * E + rr] : 0.f);
+    for (int r = 0; r < 16; ++r) lowst[(ti * 16 + r) * 64 + l] = x[r];
+  };
+
+  // quadratic state: tile (ia, bb) at ia * NB + bb, rows b = 32 bb + ..,
+  // columns e = 32 E + .. of S2[a0 + ia]
+  f32x16 ST[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int av = a0 + tt / NB, bb = tt % NB;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      ST[tt][r] = a.S_in ? a.S_in[(SD + 1 + D + av * D + 32 * bb + acc_row(r, hh)) * D + 32 * E + li] : 0.f;
   }
-  float n_prev = a.z_in ? a.z_in[SD] : 0.f;
+  // Low-degree state, in LDS. Workgroups hb = 0 hold S1[:, E] (tiles 0..NB-1,
+  // rows b) and S0[E] (tile NB, every row equal); workgroups hb = 1 hold
+  // Z2[:, E] (tiles 0..NB-1, rows b, columns c = 32 E + ..) and z1[E]
+  // (tile NB, rows c, every column equal). Wave w <= NB fills tile w.
+  const bool lnum = hb == 0, lden = hb == 1;
+  if ((lnum || lden) && w <= NB) {
+    f32x16 x;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rr = acc_row(r, hh);
+      float val = 0.f;
+      if (lnum && a.S_in) val = w < NB ? a.S_in[(SD + 1 + 32 * w + rr) * D + 32 * E + li] : a.S_in[SD * D + 32 * E + li];
+      if (lden && a.z_in) val = w < NB ? a.z_in[SD + 1 + D + (32 * w + rr) * D + 32 * E + li] : a.z_in[SD + 1 + 32 * E + rr];
+      x[r] = val;
+    }
+    st_tile(w, x);
+  }
+  float n_prev = a.z_in ? a.z_in[SD] : 0.f;  // tokens before the current chunk (and the carried count)
 
   auto update = [&](int c) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const Frag cf = numw ? Ops<OP>::template load_cols<RB>(sV, 16 * kb, 32 * E)
-                           : Ops<OP>::template load_cols<RB>(sK, 16 * kb, 32 * E);
+      Frag kc[NB];
 #pragma unroll
-      for (int bb = 0; bb < C::NBB; ++bb) Ops<OP>::mma(T[bb], Ops<OP>::template load_cols<RB>(sK, 16 * kb, 32 * bb), cf);
-      if (numw)
-        Ops<OP>::mma(X, ones, cf);  // S0[e] += sum_j v_je in every row
-      else
-        Ops<OP>::mma(X, cf, ones);  // z1[c] += sum_j k_jc in every column
+      for (int bb = 0; bb < NB; ++bb) kc[bb] = Ops<OP>::template load_cols<RB>(sK, 16 * kb, 32 * bb);
+#pragma unroll
+      for (int ia = 0; ia < C::APW; ++ia) {
+        const Frag vb = vfrag(16 * kb, sKt + (a0 + ia) * TS);  // k_ja v_je
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) Ops<OP>::mma(ST[ia * NB + bb], kc[bb], vb);
+      }
+    }
+    // low-degree updates, one tile per wave on the last waves
+    __builtin_amdgcn_sched_barrier(0);
+    const int u = C::NW - 1 - w;
+    if ((lnum || lden) && u <= NB) {
+      f32x16 x = ld_tile(u);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if (lnum) {
+          const Frag vb = vfrag(16 * kb, nullptr);
+          if (u < NB)
+            Ops<OP>::mma(x, Ops<OP>::template load_cols<RB>(sK, 16 * kb, 32 * u), vb);  // S1[b][e] += k_jb v_je
+          else
+            Ops<OP>::mma(x, ones, vb);  // S0[e] += v_je
+        } else {
+          const Frag kcb = Ops<OP>::template load_cols<RB>(sK, 16 * kb, 32 * E);
+          if (u < NB)
+            Ops<OP>::mma(x, Ops<OP>::template load_cols<RB>(sK, 16 * kb, 32 * u), kcb);  // Z2[b][c] += k_jb k_jc
+          else
+            Ops<OP>::mma(x, kcb, ones);  // z1[c] += k_jc
+        }
+      }
+      st_tile(u, x);
     }
     n_prev += (float)min(64, a.N - 64 * c);
   };
-  // numerator (num waves) or normalizer partials (den waves) of chunk c
+
   auto readout = [&](int c, bool intra) {
     const int valid = min(64, a.N - 64 * c);
-    f32x16 acc = X;
+    // Low-degree read-outs first (waves 0..3 of workgroup hb = 0, waves 0..1
+    // of hb = 1), while the output tiles are not yet live: the numerator part
+    // lands in lo (row block lo_ib) and seeds this wave's output tile.
+    f32x16 lo = {};
+    int lo_ib = -1;
+    if (lnum && w < 4) {
+      const int ib = w & 1;
+      if (w < 2) {
+        // S0[E] + q_i . S1[:, E]
+        f32x16 acc = ld_tile(NB);
 #pragma unroll
-    for (int bb = 0; bb < C::NBB; ++bb)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const Frag qf = Ops<OP>::template load_rows<RB>(sQ, 32 * ib, 32 * bb + 16 * kk);
-        if (numw)
-          Ops<OP>::mma(acc, qf, Ops<OP>::from_acc(T[bb], kk));  // [i][e] += sum_b q_ib S1[b][e]
-        else
-          Ops<OP>::mma(acc, Ops<OP>::from_acc(T[bb], kk), qf);  // [c][i] += sum_b Z2[b][c] q_ib
-      }
-    if (numw) {
-      float dsum = 0.f;
-      if (intra) {
-        for (int jb = 0; jb <= ib; ++jb) {
-          f32x16 Sc = {};
-#pragma unroll
-          for (int kb = 0; kb < D / 16; ++kb)
-            Ops<OP>::mma(Sc, Ops<OP>::template load_rows<RB>(sK, 32 * jb, 16 * kb),
-                         Ops<OP>::template load_rows<RB>(sQ, 32 * ib, 16 * kb));
-          // Sc[j][i] = k_j.q_i -> kernel 1 + s + s^2 on keys j <= i
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const bool keep = jb < ib || acc_row(r, hh) <= li;
-            const float s = Sc[r];
-            const float A = keep ? 1.f + s + s * s : 0.f;
-            Sc[r] = A;
-            dsum += A;
-          }
+        for (int bb = 0; bb < NB; ++bb) {
+          const f32x16 s1 = ld_tile(bb);
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk)
-            Ops<OP>::mma(acc, Ops<OP>::from_acc(Sc, kk),
-                         Ops<OP>::template load_cols<RB>(sV, 32 * jb + 16 * kk, 32 * E));
+            Ops<OP>::mma(acc, Ops<OP>::template load_rows<RB>(sQ, 32 * ib, 32 * bb + 16 * kk),
+                         Ops<OP>::from_acc(s1, kk));
         }
-      }
-      if (E == 0) {
-        dsum += xor32(dsum);
-        if (hh == 0) dint[32 * ib + li] = dsum;
-      }
+        lo = acc;
+        lo_ib = ib;
+      } else {
+        // in-chunk part A V[:, E] with A_ij = 1 + s + s^2 on keys j <= i; its
+        // row sums and the carried count form denominator slot 0
+        float dsum = 0.f;
+        f32x16 acc = {};
+        if (intra) {
+          for (int jb = 0; jb <= ib; ++jb) {
+            f32x16 Sc = {};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = 32 * ib + acc_row(r, hh);
-        if (i < valid) part[(64LL * c + i) * D + 32 * E + li] = acc[r];
+            for (int kb = 0; kb < D / 16; ++kb)
+              Ops<OP>::mma(Sc, Ops<OP>::template load_rows<RB>(sK, 32 * jb, 16 * kb),
+                           Ops<OP>::template load_rows<RB>(sQ, 32 * ib, 16 * kb));
+            // Sc[j][i] = k_j . q_i
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const bool keep = jb < ib || acc_row(r, hh) <= li;
+              const float s = Sc[r];
+              const float A = keep ? 1.f + s + s * s : 0.f;
+              Sc[r] = A;
+              dsum += A;
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+              Ops<OP>::mma(acc, Ops<OP>::from_acc(Sc, kk), vfrag(32 * jb + 16 * kk, nullptr));
+          }
+          lo = acc;
+          lo_ib = ib;
+        }
+        dsum += xor32(dsum);
+        const int i = 32 * ib + li;
+        if (E == 0 && a.normalize && hh == 0 && i < valid) a.den[base + 64LL * c + i] = n_prev + dsum;
       }
-    } else {
-      // phi(q_i) . (z1, Z2) over this feature block: sum_c q_ic (z1_c + sum_b Z2[b][c] q_ib)
+    }
+    if (lden && w < 2 && a.normalize) {
+      // phi(q_i) . (z1, Z2) over feature block E: sum_c q_ic (z1_c + sum_b Z2[b][c] q_ib)
+      const int ib = w;
+      f32x16 acc = ld_tile(NB);
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        const f32x16 z2 = ld_tile(bb);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          Ops<OP>::mma(acc, Ops<OP>::from_acc(z2, kk), Ops<OP>::template load_rows<RB>(sQ, 32 * ib, 32 * bb + 16 * kk));
+      }
       const int i = 32 * ib + li;
       float p = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) p += sQt[(32 * E + acc_row(r, hh)) * TS + i] * acc[r];
       p += xor32(p);
-      if (hh == 0) dpart[E][i] = p;
+      if (hh == 0 && i < valid) a.den[(1 + E) * BHN + base + 64LL * c + i] = p;
     }
-    __syncthreads();
-    if (!numw && E == 0 && hh == 0 && a.normalize) {
-      const int i = 32 * ib + li;
-      if (i < valid) {
-        float den = n_prev + (intra ? dint[i] : 0.f);
+    f32x16 Y[2];
 #pragma unroll
-        for (int cb = 0; cb < C::NE; ++cb) den += dpart[cb][i];
-        a.den[base + 64LL * c + i] = den;
+    for (int r = 0; r < 16; ++r) {
+      Y[0][r] = lo_ib == 0 ? lo[r] : 0.f;
+      Y[1][r] = lo_ib == 1 ? lo[r] : 0.f;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ia = 0; ia < C::APW; ++ia) {
+      Frag bf[NB][2];
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) bf[bb][kk] = Ops<OP>::from_acc(ST[ia * NB + bb], kk);
+      // both row blocks at once: two independent accumulation chains
+      f32x16 R[2] = {};
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int ib = 0; ib < 2; ++ib)
+            Ops<OP>::mma(R[ib], Ops<OP>::template load_rows<RB>(sQ, 32 * ib, 32 * bb + 16 * kk), bf[bb][kk]);
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+        const float* qa = sQt + (a0 + ia) * TS + 32 * ib + 4 * hh;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 qv = *reinterpret_cast<const f32x4*>(qa + 8 * g);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) Y[ib][4 * g + u] += qv[u] * R[ib][4 * g + u];
+        }
       }
+    }
+    // sum the waves' tiles and store the partial (the next writes to red
+    // come after the next chunk's staging barrier; the low-degree state is
+    // updated only after this barrier)
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[((w * 2 + ib) * 16 + r) * 64 + l] = Y[ib][r];
+    __syncthreads();
+    for (int x = t; x < 2048; x += C::NT) {
+      float s = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < C::NW; ++ww) s += red[ww * 2048 + x];
+      const int ib = x >> 10, r = (x >> 6) & 15, ll = x & 63;
+      const int row = 32 * ib + acc_row(r, ll >> 5);
+      if (row < valid) part[(64LL * c + row) * D + 32 * E + (ll & 31)] = s;
     }
   };
 
   if constexpr (CAUSAL) {
     for (int c = 0; c < a.nchunks; ++c) {
       stage(c);
-      readout(c, true);
+      readout(c, true);  // the state of the chunks before this one
       update(c);
       __syncthreads();
     }
@@ -373,36 +378,50 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
       __syncthreads();
     }
   }
-  if (a.S_out && ib == 0) {
+  if (a.S_out) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rr = acc_row(r, hh);
+    for (int tt = 0; tt < 4; ++tt) {
+      const int av = a0 + tt / NB, bb = tt % NB;
 #pragma unroll
-      for (int bb = 0; bb < C::NBB; ++bb) {
-        if (numw)
-          a.S_out[(SD + 1 + 32 * bb + rr) * D + 32 * E + li] = T[bb][r];
-        else
-          a.z_out[SD + 1 + D + (32 * bb + rr) * D + 32 * E + li] = T[bb][r];
-      }
-      if (numw) {
-        if (r == 0 && hh == 0) a.S_out[SD * D + 32 * E + li] = X[0];
-      } else if (li == 0) {
-        a.z_out[SD + 1 + 32 * E + rr] = X[r];
+      for (int r = 0; r < 16; ++r)
+        a.S_out[(SD + 1 + D + av * D + 32 * bb + acc_row(r, hh)) * D + 32 * E + li] = ST[tt][r];
+    }
+    if ((lnum || lden) && w <= NB) {
+      const f32x16 x = ld_tile(w);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rr = acc_row(r, hh);
+        if (lnum) {
+          if (w < NB)
+            a.S_out[(SD + 1 + 32 * w + rr) * D + 32 * E + li] = x[r];
+          else if (r == 0 && hh == 0)
+            a.S_out[SD * D + 32 * E + li] = x[0];
+        } else {
+          if (w < NB)
+            a.z_out[SD + 1 + D + (32 * w + rr) * D + 32 * E + li] = x[r];
+          else if (li == 0)
+            a.z_out[SD + 1 + 32 * E + rr] = x[r];
+        }
       }
     }
-    if (!numw && E == 0 && l == 0) a.z_out[SD] = n_prev;
+    if (lden && E == 0 && t == 0) a.z_out[SD] = n_prev;
   }
 }
 
 // y = (sum of the partial numerators) / max(den, eps), four outputs per thread
 template <typename IN>
-__global__ __launch_bounds__(256) void poly_finalize_kernel(PolyArgs a, int D, int nslots) {
+__global__ __launch_bounds__(256) void poly_finalize_kernel(PolyArgs a, int D, int nslots, int nden) {
   const long long total = (long long)a.BH * a.N * D;
   const long long e0 = 4 * ((long long)blockIdx.x * 256 + threadIdx.x);
   if (e0 >= total) return;
   f32x4 s = *reinterpret_cast<const f32x4*>(a.part + e0);
   for (int sl = 1; sl < nslots; ++sl) s += *reinterpret_cast<const f32x4*>(a.part + sl * total + e0);
-  if (a.normalize) s *= 1.f / fmaxf(a.den[e0 / D], kEps);
+  if (a.normalize) {
+    const long long row = e0 / D, rows = (long long)a.BH * a.N;
+    float den = a.den[row];
+    for (int sl = 1; sl < nden; ++sl) den += a.den[sl * rows + row];
+    s *= 1.f / fmaxf(den, kEps);
+  }
   IN* out = static_cast<IN*>(a.out) + e0;
   if constexpr (sizeof(IN) == 2) {
     *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
@@ -501,7 +520,7 @@ __global__ __launch_bounds__(256) void poly_fmap_kernel(FmapArgs a, int D) {
 template <int D, typename OP, typename IN>
 hipError_t launch_poly(const PolyArgs& a, bool causal, hipStream_t st) {
   using C = PolyCfg<D>;
-  const dim3 grid(a.BH, C::NE * C::NA + 1), block(C::NT);
+  const dim3 grid(a.BH, C::NE * C::NA), block(C::NT);
   if (causal)
     hipLaunchKernelGGL((poly_chunk_kernel<D, OP, IN, true>), grid, block, 0, st, a);
   else
@@ -510,13 +529,14 @@ hipError_t launch_poly(const PolyArgs& a, bool causal, hipStream_t st) {
   if (e != hipSuccess) return e;
   const long long n4 = (long long)a.BH * a.N * D / 4;
   hipLaunchKernelGGL((poly_finalize_kernel<IN>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, a, D,
-                     C::NA + 1);
+                     C::NA, 1 + C::NE);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int poly_partials(int D) { return D == 32 ? PolyCfg<32>::NA + 1 : PolyCfg<64>::NA + 1; }
+int poly_partials(int D) { return D == 32 ? PolyCfg<32>::NA : PolyCfg<64>::NA; }
+int poly_den_slots(int D) { return D == 32 ? 1 + PolyCfg<32>::NE : 1 + PolyCfg<64>::NE; }
 
 hipError_t poly_forward_dispatch(const PolyArgs& a, int D, int dtype, bool causal, hipStream_t st) {
   const bool bf = dtype == 1;
