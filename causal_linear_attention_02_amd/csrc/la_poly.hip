@@ -40,6 +40,12 @@ struct PolyCfg {
   static constexpr int APB = NW * APW;  // a values per workgroup
   static constexpr int NA = D / APB;    // workgroups per value block
   static constexpr int DP = 1 + D + D * D;
+  // in-chunk part: its own workgroup (hb = 2) with one score tile per wave
+  // when there are more than two workgroups per value block; else it shares
+  // workgroup 0 and one wave takes both tiles of the second row block, whose
+  // row sums then need no extra denominator slot
+  static constexpr bool SPLIT = NA > 2;
+  static constexpr int NDEN = 1 + NE + (SPLIT ? 1 : 0);
   static_assert(NA * APB == D && 4 * NE == NW, "tiling of the state");
 };
 
@@ -236,14 +242,15 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
 
   auto readout = [&](int c, bool intra) {
     const int valid = min(64, a.N - 64 * c);
-    // Low-degree read-outs first (waves 0..3 of workgroup hb = 0, waves 0..1
-    // of hb = 1), while the output tiles are not yet live: the numerator part
-    // lands in lo (row block lo_ib) and seeds this wave's output tile.
+    // Low-degree read-outs first (waves 0..1 of workgroups hb = 0 and 1, and
+    // the in-chunk waves), while the output tiles are not yet live: the
+    // numerator part lands in lo (row block lo_ib) and seeds this wave's
+    // output tile.
     f32x16 lo = {};
     int lo_ib = -1;
-    if (lnum && w < 4) {
-      const int ib = w & 1;
-      if (w < 2) {
+    {
+      const int ib = w;
+      if (lnum && w < 2) {
         // S0[E] + q_i . S1[:, E]
         f32x16 acc = ld_tile(NB);
 #pragma unroll
@@ -256,13 +263,30 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
         }
         lo = acc;
         lo_ib = ib;
+      }
+    }
+    // In-chunk part A V[:, E], A_ij = 1 + s_ij + s_ij^2 on keys j <= i, score
+    // tiles (ib, jb) of this wave; the row sums (plus the carried count, on
+    // the tiles jb = 0) form denominator slot 0, or slot 1 + NE for tile (1, 1)
+    // when it has a wave of its own.
+    {
+      int ib = -1, jb0 = 0, njb = 1;
+      if constexpr (C::SPLIT) {
+        if (hb == 2 && w < 3) {
+          ib = w == 0 ? 0 : 1;
+          jb0 = w == 2 ? 1 : 0;
+        }
       } else {
-        // in-chunk part A V[:, E] with A_ij = 1 + s + s^2 on keys j <= i; its
-        // row sums and the carried count form denominator slot 0
+        if (hb == 0 && (w == 2 || w == 3)) {
+          ib = w - 2;
+          njb = ib + 1;
+        }
+      }
+      if (ib >= 0) {
         float dsum = 0.f;
         f32x16 acc = {};
         if (intra) {
-          for (int jb = 0; jb <= ib; ++jb) {
+          for (int jb = jb0; jb < jb0 + njb; ++jb) {
             f32x16 Sc = {};
 #pragma unroll
             for (int kb = 0; kb < D / 16; ++kb)
@@ -272,8 +296,8 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const bool keep = jb < ib || acc_row(r, hh) <= li;
-              const float s = Sc[r];
-              const float A = keep ? 1.f + s + s * s : 0.f;
+              const float sv = Sc[r];
+              const float A = keep ? 1.f + sv + sv * sv : 0.f;
               Sc[r] = A;
               dsum += A;
             }
@@ -285,8 +309,13 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
           lo_ib = ib;
         }
         dsum += xor32(dsum);
-        const int i = 32 * ib + li;
-        if (E == 0 && a.normalize && hh == 0 && i < valid) a.den[base + 64LL * c + i] = n_prev + dsum;
+        if (E == 0 && a.normalize && hh == 0) {  // the other value blocks repeat these tiles
+          const bool own = C::SPLIT && jb0 == 1;  // tile (1, 1) alone: slot 1 + NE
+          const long long slot = own ? (1 + C::NE) * BHN : 0;
+          const int i = 32 * ib + li;
+          if (i < valid) a.den[slot + base + 64LL * c + i] = (own ? 0.f : n_prev) + dsum;
+          if (own && li < valid) a.den[slot + base + 64LL * c + li] = 0.f;  // rows 0..31 of that slot
+        }
       }
     }
     if (lden && w < 2 && a.normalize) {
@@ -529,14 +558,14 @@ hipError_t launch_poly(const PolyArgs& a, bool causal, hipStream_t st) {
   if (e != hipSuccess) return e;
   const long long n4 = (long long)a.BH * a.N * D / 4;
   hipLaunchKernelGGL((poly_finalize_kernel<IN>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, a, D,
-                     C::NA, 1 + C::NE);
+                     C::NA, C::NDEN);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int poly_partials(int D) { return D == 32 ? PolyCfg<32>::NA : PolyCfg<64>::NA; }
-int poly_den_slots(int D) { return D == 32 ? 1 + PolyCfg<32>::NE : 1 + PolyCfg<64>::NE; }
+int poly_den_slots(int D) { return D == 32 ? PolyCfg<32>::NDEN : PolyCfg<64>::NDEN; }
 
 hipError_t poly_forward_dispatch(const PolyArgs& a, int D, int dtype, bool causal, hipStream_t st) {
   const bool bf = dtype == 1;

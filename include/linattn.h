@@ -88,7 +88,7 @@ const char* la_status_string(int status);
  * It holds the fp32 states of the sequence segments and, for random features,
  * phi(q) and phi(k) ([B][H][N][m] each, sized for fp32). With LA_POLY2 it
  * holds fp32 partial numerators (2 per token at d = 32, 4 at d = 64, [N][d]
- * each per (batch, head)) and partial denominators (2 or 3 per token).
+ * each per (batch, head)) and partial denominators (2 or 4 per token).
  */
 size_t la_forward_workspace_size(int B, int H, int N, int d, const la_feature_map* feature_map, int causal);
 
