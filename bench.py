@@ -45,6 +45,10 @@ def parse():
     p.add_argument("--no-variants", action="store_true")
     p.add_argument("--poly-steps", type=int, default=50)
     p.add_argument("--no-poly", action="store_true")
+    p.add_argument("--mid-steps", type=int, default=200)
+    p.add_argument("--no-mid", action="store_true")
+    p.add_argument("--performer-steps", type=int, default=50)
+    p.add_argument("--no-performer", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="time budget of the oracle's prefill sample (whole heads; the decode sample gets half)")
@@ -267,6 +271,91 @@ def main():
     del tq, tk, tv, out, ws
     torch.cuda.empty_cache()
 
+    def time_calls(fn, warm, steps):
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    # ---------------- elu+1 prefill at B=4 H=8 N=2048 d=64 ----------------
+    # 33.6 MB per input set fits in the 256 MB last-level cache, so the calls
+    # rotate over 8 input sets (268 MB) and every call reads from HBM
+    mid = None
+    if not args.no_mid:
+        Wm = la_inputs.WORKLOADS["prefill_b4h8n2048d64"]
+        Bm, Hm, Nm, dm = Wm["B"], Wm["H"], Wm["N"], Wm["d"]
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(Wm["seed"])
+        shp = (Bm, Hm, Nm, dm)
+        sets = [[(torch.randn(shp, generator=gen, device=dev) * Wm["scale"]).to(torch.bfloat16) for _ in range(3)]
+                + [torch.empty(shp, dtype=torch.bfloat16, device=dev)] for _ in range(8)]
+        mws = torch.empty(max(la.la_forward_workspace_size(Bm, Hm, Nm, dm), 256), dtype=torch.uint8, device=dev)
+
+        def mfwd(i):
+            sq_, sk_, sv_, so_ = sets[i % 8]
+            la.la_forward(sq_, sk_, sv_, causal=True, normalize=True, out=so_, workspace=mws)
+
+        mwall = time_calls(mfwd, 80, args.mid_steps)
+        m_ht = Bm * Hm * Nm
+        m_bytes = m_ht * 4 * dm * 2
+        m_flops = m_ht * (4 * dm * dm + (C + 1) * 2 * dm)
+        t_roof = max(m_bytes / (HBM_PEAK_GBS * 1e9), m_flops / (BF16_MFMA_PEAK_TFLOPS * 1e12))
+        mid = {
+            "metric": "causal linear-attn prefill tokens/s", "value": Bm * Nm / mwall, "unit": "tokens/s",
+            "us_per_call": round(mwall * 1e6, 2), "steps": args.mid_steps,
+            "config": {"workload": "prefill_b4h8n2048d64", "batch": Bm, "heads": Hm, "seq_len": Nm, "d": dm,
+                       "feature_map": "elu1", "causal": True, "normalize": True, "input_sets": 8},
+            "whole_op": {"bytes": m_bytes, "achieved_gbs": round(m_bytes / mwall / 1e9, 1),
+                         "useful_tflops": round(m_flops / mwall / 1e12, 2), "roof_us": round(t_roof * 1e6, 2),
+                         "bound": "hbm", "frac_roof": round(t_roof / mwall, 4)},
+        }
+        log(f"prefill b4h8n2048d64: {mwall*1e6:.1f} us/call ({t_roof / mwall:.1%} of the roof)")
+        del sets, mws
+        torch.cuda.empty_cache()
+
+    # ---------------- random features, B=2 H=8 N=16384 d=64 m=256 ----------------
+    perf = None
+    if not args.no_performer:
+        Wf = la_inputs.WORKLOADS["performer_b2h8n16384d64m256"]
+        Bf, Hf, Nf, df, mf = Wf["B"], Wf["H"], Wf["N"], Wf["d"], Wf["m"]
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(Wf["seed"])
+        shp = (Bf, Hf, Nf, df)
+        fq, fk, fv = (torch.randn(shp, generator=gen, device=dev).to(torch.bfloat16) for _ in range(3))
+        fW = torch.from_numpy(la_inputs.performer_W(mf, df, Wf["w_seed"])).to(dev)
+        fout = torch.empty_like(fq)
+        fws = torch.empty(max(la.la_forward_workspace_size(Bf, Hf, Nf, df, feature_map="performer", W=fW), 256),
+                          dtype=torch.uint8, device=dev)
+
+        def ffwd(i):
+            la.la_forward(fq, fk, fv, feature_map="performer", W=fW, causal=True, normalize=True, out=fout,
+                          workspace=fws)
+
+        fwall = time_calls(ffwd, 40, args.performer_steps)
+        f_ht = Bf * Hf * Nf
+        f_bytes = f_ht * 4 * df * 2
+        # projections of q and k (2 m d each), read-out and state update
+        # (2 m d each), in-chunk scores and products ((C + 1)(m + d))
+        f_flops = f_ht * (4 * mf * df + 4 * mf * df + (C + 1) * (mf + df))
+        t_roof = max(f_bytes / (HBM_PEAK_GBS * 1e9), f_flops / (BF16_MFMA_PEAK_TFLOPS * 1e12))
+        perf = {
+            "metric": "causal random-feature linear-attn prefill tokens/s", "value": Bf * Nf / fwall,
+            "unit": "tokens/s", "us_per_call": round(fwall * 1e6, 2), "steps": args.performer_steps,
+            "config": {"workload": "performer_b2h8n16384d64m256", "batch": Bf, "heads": Hf, "seq_len": Nf,
+                       "d": df, "features": mf, "feature_map": "performer", "causal": True, "normalize": True},
+            "whole_op": {"bytes": f_bytes, "flops": f_flops, "achieved_gbs": round(f_bytes / fwall / 1e9, 1),
+                         "useful_tflops": round(f_flops / fwall / 1e12, 2),
+                         "frac_bf16_mfma": round(f_flops / fwall / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                         "roof_us": round(t_roof * 1e6, 2), "frac_roof": round(t_roof / fwall, 4)},
+        }
+        log(f"performer: {fwall*1e6:.1f} us/call ({t_roof / fwall:.1%} of the roof)")
+        del fq, fk, fv, fW, fout, fws
+        torch.cuda.empty_cache()
+
     # ---------------- degree-2 polynomial map (d' = 1 + d + d^2) ----------------
     poly = None
     if not args.no_poly:
@@ -462,6 +551,8 @@ def main():
         "gated": gated,
         "variants": variants,
         "poly2": poly,
+        "prefill_b4h8n2048d64": mid,
+        "performer": perf,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result))

@@ -11,8 +11,13 @@ namespace {
 
 constexpr int kChunk = 64;
 // Output/state passes aim for this many workgroups so that every compute unit
-// has work even when batch * heads is small (long single sequences).
-constexpr long long kTargetBlocks = 512;
+// has work even when batch * heads is small (long single sequences). One
+// workgroup per compute unit: on the long-context and random-feature
+// workloads 256 ran 5-10% faster than 512 or 384, and 128 far slower.
+constexpr long long kTargetBlocks = 256;
+// The gated forward and the gradient passes keep twice as many: the gated
+// forward on the long-context workload took 916 us at 256 against 811 us at 512.
+constexpr long long kTargetBlocksWide = 512;
 // A segment never gets fewer chunks than this (its carried state costs about
 // as much traffic as 64 tokens of q, k, v and out at d' = d).
 constexpr int kMinChunksPerSegment = 4;
@@ -62,8 +67,8 @@ struct Plan {
   size_t ws_bytes = 0;       // total: two feature buffers, then the segment states
 };
 
-void split(int nchunks, long long BH, int& P, int& cps) {
-  long long want = (kTargetBlocks + BH - 1) / BH;
+void split(int nchunks, long long BH, int& P, int& cps, long long target = kTargetBlocks) {
+  long long want = (target + BH - 1) / BH;
   long long cap = nchunks / kMinChunksPerSegment;
   if (cap < 1) cap = 1;
   if (want > cap) want = cap;
@@ -72,13 +77,14 @@ void split(int nchunks, long long BH, int& P, int& cps) {
   P = (nchunks + cps - 1) / cps;
 }
 
-Plan make_plan(long long BH, int N, int d, int dfeat, bool causal, bool mapped_inputs) {
+Plan make_plan(long long BH, int N, int d, int dfeat, bool causal, bool mapped_inputs,
+               long long target = kTargetBlocks) {
   Plan p;
   if (mapped_inputs && N > 0) p.phi_bytes = align256((size_t)BH * N * dfeat * sizeof(float));
   p.nchunks = (N + kChunk - 1) / kChunk;
   const size_t state_bytes = (size_t)(dfeat * d + dfeat) * sizeof(float);
   if (N == 0 || BH == 0) return p;
-  split(p.nchunks, BH, p.P, p.cps);
+  split(p.nchunks, BH, p.P, p.cps, target);
   if (causal) {
     if (p.P > 1) {
       p.Ps = p.P - 1;  // the last segment's local sums are never carried
@@ -88,7 +94,7 @@ Plan make_plan(long long BH, int N, int d, int dfeat, bool causal, bool mapped_i
       p.scan = true;
     }
   } else {
-    split(p.nchunks, BH, p.Ps, p.cpss);
+    split(p.nchunks, BH, p.Ps, p.cpss, target);
     p.ws_slots = p.Ps + 1;
     p.state_pass = true;
     p.scan = true;
@@ -226,7 +232,10 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
         overlaps(z_out, z_bytes, feature_map->W, wb))
       return LA_ERR_INVALID_ARG;
   }
-  const Plan p = make_plan(BH, N, d, dfeat, causal != 0, mapped);
+  // random features at d = 64 in bf16: the projection runs inside the chunked
+  // passes and the workspace holds segment states only
+  const bool fused = mapped && la::perf_fused_supported(d, dfeat, dtype, causal != 0, gamma != nullptr);
+  const Plan p = make_plan(BH, N, d, dfeat, causal != 0, mapped && !fused);
   if (p.ws_bytes > 0) {
     if (!workspace || workspace_bytes < p.ws_bytes) return LA_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LA_ERR_INVALID_ARG;
@@ -246,7 +255,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   char* wsb = static_cast<char*>(workspace);
   const void* qm = q;
   const void* km = k;
-  if (mapped) {
+  if (mapped && !fused) {
     // random features: phi(q), phi(k) into the workspace, in the operand
     // precision of the chunked passes; those passes then use them as given
     void* fq = wsb;
@@ -317,6 +326,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
     s.S_out = S_out;
     s.z_out = z_out;
   }
+  if (fused) return status_from_hip(la::perf_fused_dispatch(a, s, dfeat, stream, events));
   const int kfm = feature_map->kind == LA_ELU1 ? la::kElu1 : la::kIdentity;  // mapped features: identity inside
   return status_from_hip(la::prefill_dispatch(a, s, d, dfeat, kfm, dtype, causal != 0, gamma != nullptr, stream,
                                               events));
@@ -455,7 +465,7 @@ BwdPlan make_bwd_plan(long long BH, int N, int d) {
   BwdPlan p;
   if (N == 0 || BH == 0) return p;
   p.nchunks = (N + kChunk - 1) / kChunk;
-  split(p.nchunks, BH, p.P, p.cps);
+  split(p.nchunks, BH, p.P, p.cps, kTargetBlocksWide);
   const size_t state_bytes = (size_t)(d * d + d) * sizeof(float);
   p.fwd_bytes = p.P > 1 ? align256((size_t)BH * p.P * state_bytes) : 0;
   p.rev_bytes = align256((size_t)BH * (p.P + 1) * state_bytes);
@@ -667,7 +677,7 @@ struct GatedPlan {
 
 GatedPlan make_gated_plan(long long BH, int N, int d) {
   GatedPlan g;
-  g.p = make_plan(BH, N, d, d, true, false);  // the causal split; its workspace holds the segment states
+  g.p = make_plan(BH, N, d, d, true, false, kTargetBlocksWide);  // the causal split; its workspace holds the segment states
   if (N == 0 || BH == 0) return g;
   g.state_bytes = align256(g.p.ws_bytes);
   g.lfac_bytes = g.p.P > 1 ? align256((size_t)BH * g.p.P * d * sizeof(float)) : 0;

@@ -19,6 +19,8 @@
 
 namespace la {
 
+constexpr int kCUs = 256;  // compute units of one MI355X
+
 template <typename OUT> __device__ __forceinline__ void store8_out(void* p, long long off, const float (&x)[8]);
 template <> __device__ __forceinline__ void store8_out<__bf16>(void* p, long long off, const float (&x)[8]) {
   u32x4 v = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
@@ -81,69 +83,88 @@ __device__ __forceinline__ f32x16 project_tile(const uint8_t* sW, const uint8_t*
   return acc;
 }
 
+// Each block stages W once and then walks 64-row tiles blockIdx.x,
+// blockIdx.x + gridDim.x, ...; the rows of the next tile are loaded into
+// registers while the current tile is projected.
 template <int D, int DF, typename IN, typename OUT, typename OP>
 __global__ __launch_bounds__(256) void fmap_perf_kernel(FmapArgs a) {
   using P = PerfTile<D, DF, OP>;
   constexpr int RBO = DF * (int)sizeof(OUT);
+  constexpr int RL = D / 8;           // threads per X row
+  constexpr int XP = 64 * RL / 256;   // X pieces per thread
+  static_assert(XP >= 1 && 64 * RL == 256 * XP, "X tile geometry");
   __shared__ __attribute__((aligned(16))) uint8_t sX[P::XB];
   __shared__ __attribute__((aligned(16))) uint8_t sW[P::WB];
   __shared__ __attribute__((aligned(16))) uint8_t sO[64 * RBO];
   __shared__ float sB[64];
-  const long long r0 = (long long)blockIdx.x * 64;
-  const int valid = (int)min(64LL, a.rows - r0);
-  const IN* x = static_cast<const IN*>(a.x) + r0 * D;
+  const long long ntiles = (a.rows + 63) / 64;
   const float s2 = 1.0f / sqrtf((float)D);                 // (d^(-1/4))^2
   const float A = sqrtf(sqrtf(1.0f / (float)D)) * 1.4426950408889634f;
   const float Bm = 0.5f * __log2f((float)DF);
+  const IN* xg = static_cast<const IN*>(a.x);
 
+  // rows of tile t held by this thread (rows past the end read as zero)
+  typename In8<IN>::raw xr[XP];
+  auto load_x = [&](long long t) {
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const int p = threadIdx.x + 256 * i;
+      const long long row = 64 * t + p / RL;
+      xr[i] = row < a.rows ? In8<IN>::load(xg + row * D + 8 * (p % RL)) : In8<IN>::zero();
+    }
+  };
+  if ((long long)blockIdx.x < ntiles) load_x(blockIdx.x);
   stage_W<D, DF, OP>(a.W, sW);
-  // X tile and |x|^2 of each row (rows past the end are zero)
-  constexpr int RL = D / 8;
-  for (int p = threadIdx.x; p < 64 * RL; p += 256) {
-    const int row = p / RL, col = 8 * (p % RL);
-    float v[8];
-    if (row < valid) In8<IN>::to_f32(In8<IN>::load(x + (long long)row * D + col), v);
-    else
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
-#pragma unroll
-    for (int m = 1; m < RL; m <<= 1) ss += __shfl_xor(ss, m, 64);
-    if ((p % RL) == 0) sB[row] = 1.4426950408889634f * 0.5f * s2 * ss + Bm;
-    Ops<OP>::template store8<P::RBX>(sX, row, col, v);
-  }
-  __syncthreads();
 
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, li = l & 31;
-  for (int t = w; t < (DF / 32) * 2; t += 4) {
-    const int fb = t >> 1, rb = t & 1;
-    const f32x16 u = project_tile<D, DF, OP>(sW, sX, fb, rb);
-    const int row = 32 * rb + li;
-    const float b = sB[row];
+  for (long long t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    // X tile and |x|^2 of each row
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int f = 32 * fb + 8 * g + 4 * h;
-      float y[4];
+    for (int i = 0; i < XP; ++i) {
+      const int p = threadIdx.x + 256 * i;
+      const int row = p / RL, col = 8 * (p % RL);
+      float v[8];
+      In8<IN>::to_f32(xr[i], v);
+      float ss = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) y[j] = __builtin_amdgcn_exp2f(A * u[4 * g + j] - b);
-      if constexpr (sizeof(OUT) == 2) {
-        *reinterpret_cast<u32x2*>(sO + tile_off<RBO>(row, f * 2)) =
-            u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-      } else {
-        *reinterpret_cast<f32x4*>(sO + tile_off<RBO>(row, f * 4)) = f32x4{y[0], y[1], y[2], y[3]};
+      for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+#pragma unroll
+      for (int m = 1; m < RL; m <<= 1) ss += __shfl_xor(ss, m, 64);
+      if ((p % RL) == 0) sB[row] = 1.4426950408889634f * 0.5f * s2 * ss + Bm;
+      Ops<OP>::template store8<P::RBX>(sX, row, col, v);
+    }
+    __syncthreads();
+    if (t + gridDim.x < ntiles) load_x(t + gridDim.x);
+
+    for (int u = w; u < (DF / 32) * 2; u += 4) {
+      const int fb = u >> 1, rb = u & 1;
+      const f32x16 acc = project_tile<D, DF, OP>(sW, sX, fb, rb);
+      const int row = 32 * rb + li;
+      const float b = sB[row];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int f = 32 * fb + 8 * g + 4 * h;
+        float y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[j] = __builtin_amdgcn_exp2f(A * acc[4 * g + j] - b);
+        if constexpr (sizeof(OUT) == 2) {
+          *reinterpret_cast<u32x2*>(sO + tile_off<RBO>(row, f * 2)) =
+              u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        } else {
+          *reinterpret_cast<f32x4*>(sO + tile_off<RBO>(row, f * 4)) = f32x4{y[0], y[1], y[2], y[3]};
+        }
       }
     }
-  }
-  __syncthreads();
-  OUT* o = static_cast<OUT*>(a.phi) + r0 * DF;
-  constexpr int OPR = RBO / 16;  // 16-byte pieces per output row
-  for (int p = threadIdx.x; p < 64 * OPR; p += 256) {
-    const int row = p / OPR, cb = 16 * (p % OPR);
-    if (row < valid)
-      *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(o + (long long)row * DF) + cb) =
-          *reinterpret_cast<const u32x4*>(sO + tile_off<RBO>(row, cb));
+    __syncthreads();
+    const int valid = (int)min(64LL, a.rows - 64 * t);
+    uint8_t* o = reinterpret_cast<uint8_t*>(static_cast<OUT*>(a.phi) + 64 * t * DF);
+    constexpr int OPR = RBO / 16;  // 16-byte pieces per output row
+    for (int p = threadIdx.x; p < 64 * OPR; p += 256) {
+      const int row = p / OPR, cb = 16 * (p % OPR);
+      if (row < valid)
+        *reinterpret_cast<u32x4*>(o + (long long)row * RBO + cb) =
+            *reinterpret_cast<const u32x4*>(sO + tile_off<RBO>(row, cb));
+    }
   }
 }
 
@@ -168,9 +189,13 @@ static hipError_t fmap_elementwise_dispatch(const FmapArgs& a, int D, int in_dty
 template <int D, int DF, typename IN, typename OUT>
 static hipError_t launch_fmap_perf(const FmapArgs& a, hipStream_t st) {
   if (a.rows == 0) return hipSuccess;
-  const long long blocks = (a.rows + 63) / 64;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   using OP = typename std::conditional<sizeof(IN) == 2, __bf16, float>::type;
+  using P = PerfTile<D, DF, OP>;
+  // blocks that fit on the chip at once (LDS-limited), each walking several tiles
+  constexpr int kLds = P::XB + P::WB + 64 * DF * (int)sizeof(OUT) + 256;
+  constexpr int kPerCU = (160 * 1024) / kLds < 1 ? 1 : ((160 * 1024) / kLds > 4 ? 4 : (160 * 1024) / kLds);
+  long long blocks = (a.rows + 63) / 64;
+  if (blocks > (long long)kCUs * kPerCU) blocks = (long long)kCUs * kPerCU;
   hipLaunchKernelGGL((fmap_perf_kernel<D, DF, IN, OUT, OP>), dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }

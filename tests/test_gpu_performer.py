@@ -89,7 +89,7 @@ def test_performer_forward_small(d, m, dt):
             _check_forward(2, 2, N, d, m, dt, causal, True, seed=500 + N + d + m)
 
 
-@pytest.mark.parametrize("d,m", [(64, 256), (32, 128), (128, 64)])
+@pytest.mark.parametrize("d,m", [(64, 256), (64, 128), (64, 64), (32, 128), (128, 64)])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_performer_forward_multisegment(d, m, dt):
     N = 64 * 40 - 17
