@@ -39,15 +39,7 @@ struct PfL {
   static constexpr int NT = DF / 64;       // S tiles per wave (m/2 features)
   static constexpr int NFB = DF / 32;      // 32-feature blocks
   static constexpr int NG = DF / 4;        // column-sum groups of 4 features
-  static constexpr int NSL = 256 / NG;     // row slices of the column sums
-  static constexpr int SLR = 64 / NSL;     // rows per slice
-  // state pass: W, phi(K), v and the column-sum partials only
-  static constexpr int SK_OFF = DF * RBV;
-  static constexpr int SV_OFF = SK_OFF + 64 * RBF;
-  static constexpr int SZP_OFF = SV_OFF + 64 * RBV;
-  static constexpr int SBYTES = SZP_OFF + NSL * DF * 4;
-  static_assert(NT >= 1 && NG * NSL == 256 && NSL * SLR == 64, "geometry");
-  static_assert(SBYTES <= 80 * 1024, "two state-pass blocks per compute unit");
+  static_assert(NT >= 1 && NG <= 256, "geometry");
 };
 
 // W (fp32 [DF][64], bf16-representable values) -> LDS rows in bf16
@@ -159,35 +151,34 @@ __device__ __forceinline__ void pf_colsum(const uint8_t* tile, float (&cs)[4]) {
   }
 }
 
-// accumulator tiles of S held by wave (fh, cb): element r of tile t is
-// S[fh m/2 + 32 t + 8 (r / 4) + 4 (l / 32) + r % 4][32 cb + l % 32]
-template <int DF>
-__device__ __forceinline__ void pf_load_S(f32x16 (&st)[PfL<DF>::NT], const float* Sp, int fh, int cb) {
+// NT accumulator tiles of S held by one wave: element r of tile t is
+// S[f0 + 32 t + 8 (r / 4) + 4 (l / 32) + r % 4][32 cb + l % 32]
+template <int NT>
+__device__ __forceinline__ void pf_load_S(f32x16 (&st)[NT], const float* Sp, int f0, int cb) {
   const int l = threadIdx.x & 63, h = l >> 5, li = l & 31;
 #pragma unroll
-  for (int t = 0; t < PfL<DF>::NT; ++t)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int f = fh * (DF / 2) + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+      const int f = f0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
       st[t][r] = Sp ? Sp[(long long)f * kPD + 32 * cb + li] : 0.f;
     }
 }
-template <int DF>
-__device__ __forceinline__ void pf_store_S(const f32x16 (&st)[PfL<DF>::NT], float* Sp, int fh, int cb) {
+template <int NT>
+__device__ __forceinline__ void pf_store_S(const f32x16 (&st)[NT], float* Sp, int f0, int cb) {
   const int l = threadIdx.x & 63, h = l >> 5, li = l & 31;
 #pragma unroll
-  for (int t = 0; t < PfL<DF>::NT; ++t)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int f = fh * (DF / 2) + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+      const int f = f0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
       Sp[(long long)f * kPD + 32 * cb + li] = st[t][r];
     }
 }
 
-// S (fh, cb) += phi(K)^T V over the chunk's 64 rows
-template <int DF>
-__device__ __forceinline__ void pf_update_S(f32x16 (&st)[PfL<DF>::NT], const uint8_t* sK, const uint8_t* sV, int fh,
-                                            int cb) {
+// S[f0 .., 32 cb ..] += phi(K)^T V over the chunk's 64 rows
+template <int DF, int NT>
+__device__ __forceinline__ void pf_update_S(f32x16 (&st)[NT], const uint8_t* sK, const uint8_t* sV, int f0, int cb) {
   using L = PfL<DF>;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -196,25 +187,42 @@ __device__ __forceinline__ void pf_update_S(f32x16 (&st)[PfL<DF>::NT], const uin
     __builtin_amdgcn_sched_barrier(0);
     const bf16x8 vf = B16::template load_cols<L::RBV>(sV, 16 * kb, 32 * cb);
 #pragma unroll
-    for (int t = 0; t < L::NT; ++t)
-      B16::mma(st[t], B16::template load_cols<L::RBF>(sK, 16 * kb, fh * (DF / 2) + 32 * t), vf);
+    for (int t = 0; t < NT; ++t)
+      B16::mma(st[t], B16::template load_cols<L::RBF>(sK, 16 * kb, f0 + 32 * t), vf);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // ---------------------------------------------------------------------------
-// State pass: grid (BH, segments - 1), 256 threads.
+// State pass: grid (BH, segments - 1), NW waves (8 for m >= 128, else 4).
+// Wave w maps rows [32 (w & 1), +32) of the chunk's k for feature slice
+// w >> 1 (m / (NW / 2) features) and holds S[slice features][32 (w & 1), +32).
 // ---------------------------------------------------------------------------
-// Two blocks per compute unit (76 KB of LDS each at m = 256), so that one
-// block's projections and exponentials overlap the other's MFMA updates.
-template <int DF>
-__global__ __launch_bounds__(256, 2) void pf_state_kernel(FwdArgs a) {
+template <int DF, int NW>
+struct PsL {
   using L = PfL<DF>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[L::SBYTES];
+  static constexpr int NTH = 64 * NW;
+  static constexpr int FS = DF / (NW / 2);   // features per slice
+  static constexpr int NTS = FS / 32;        // S tiles (and projected blocks) per wave
+  static constexpr int NSL = NTH / L::NG;    // column-sum row slices
+  static constexpr int K_OFF = DF * L::RBV;
+  static constexpr int V_OFF = K_OFF + 64 * L::RBF;
+  static constexpr int ZP_OFF = V_OFF + 64 * L::RBV;
+  static constexpr int BYTES = ZP_OFF + NSL * DF * 4;
+  static_assert(NTS >= 1 && FS % 32 == 0, "feature slices of whole 32-feature blocks");
+  static_assert(BYTES <= 80 * 1024, "two blocks per compute unit");
+};
+
+template <int DF, int NW>
+__global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
+  using L = PfL<DF>;
+  using Q = PsL<DF, NW>;
+  constexpr int NTH = Q::NTH;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Q::BYTES];
   uint8_t* sW = smem;
-  uint8_t* sK = smem + L::SK_OFF;
-  uint8_t* sV = smem + L::SV_OFF;
-  float* zp = reinterpret_cast<float*>(smem + L::SZP_OFF);
+  uint8_t* sK = smem + Q::K_OFF;
+  uint8_t* sV = smem + Q::V_OFF;
+  float* zp = reinterpret_cast<float*>(smem + Q::ZP_OFF);
   const int bh = blockIdx.x, seg = blockIdx.y;
   const int c0 = seg * a.chunks_per_seg_state;
   const int n = max(0, min(c0 + a.chunks_per_seg_state, a.nchunks) - c0);
@@ -222,22 +230,22 @@ __global__ __launch_bounds__(256, 2) void pf_state_kernel(FwdArgs a) {
   const __bf16* k = static_cast<const __bf16*>(a.k);
   const __bf16* v = static_cast<const __bf16*>(a.v);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, li = l & 31;
-  const int rb = w & 1, ph = w >> 1;  // projection: rows [32 rb, +32), features [ph m/2, +m/2)
-  const int fh = w >> 1, cb = w & 1;  // state tiles
+  const int rb = w & 1, sl = w >> 1;  // rows [32 rb, +32); feature slice [sl FS, +FS)
+  const int cb = w & 1;               // S columns [32 cb, +32)
   const float bm = 0.5f * __log2f((float)DF);
 
-  u32x4 xr[4], vr[2];
+  u32x4 xr[4], vr[512 / NTH];
   auto rsrc = [&](const __bf16* p, int c) {
     return make_rsrc(p + (base + 64LL * c) * kPD, (unsigned)(min(64, a.N - 64 * c) * kPD * 2));
   };
   if (n > 0) {
     pf_load_x(xr, rsrc(k, c0), 32 * rb);
-    pf_load_v<256>(vr, rsrc(v, c0));
+    pf_load_v<NTH>(vr, rsrc(v, c0));
   }
-  pf_stage_W<DF, 256>(a.W, sW);
-  f32x16 st[L::NT];
+  pf_stage_W<DF, NTH>(a.W, sW);
+  f32x16 st[Q::NTS];
 #pragma unroll
-  for (int t = 0; t < L::NT; ++t) st[t] = f32x16{};
+  for (int t = 0; t < Q::NTS; ++t) st[t] = f32x16{};
   float cs[4] = {0.f, 0.f, 0.f, 0.f};
   __syncthreads();
 
@@ -247,32 +255,32 @@ __global__ __launch_bounds__(256, 2) void pf_state_kernel(FwdArgs a) {
     const float b = pf_row_bias(xr, bm);
     const bool past = 32 * rb + li >= valid;
 #pragma unroll
-    for (int j = 0; j < L::NFB / 2; ++j) {
-      const int fb = ph * (L::NFB / 2) + j;
+    for (int j = 0; j < Q::NTS; ++j) {
+      const int fb = sl * Q::NTS + j;
       pf_phi_store<DF, false>(pf_project<DF>(sW, xr, fb), b, past, sK, 32 * rb + li, fb, nullptr);
     }
-    pf_store_v<256>(vr, sV);
+    pf_store_v<NTH>(vr, sV);
     if (it + 1 < n) {
       pf_load_x(xr, rsrc(k, c + 1), 32 * rb);
-      pf_load_v<256>(vr, rsrc(v, c + 1));
+      pf_load_v<NTH>(vr, rsrc(v, c + 1));
     }
     __syncthreads();
-    pf_update_S<DF>(st, sK, sV, fh, cb);
-    pf_colsum<DF, 256>(sK, cs);
+    pf_update_S<DF, Q::NTS>(st, sK, sV, sl * Q::FS, cb);
+    pf_colsum<DF, NTH>(sK, cs);
     __syncthreads();
   }
 
   float* out = a.ws + ((long long)bh * a.ws_slots + seg) * a.state_elems;
-  pf_store_S<DF>(st, out, fh, cb);
+  pf_store_S<Q::NTS>(st, out, sl * Q::FS, cb);
   {
-    const int grp = threadIdx.x % L::NG, sl = threadIdx.x / L::NG;
-    *reinterpret_cast<f32x4*>(zp + sl * DF + 4 * grp) = f32x4{cs[0], cs[1], cs[2], cs[3]};
+    const int grp = threadIdx.x % L::NG, zs = threadIdx.x / L::NG;
+    *reinterpret_cast<f32x4*>(zp + zs * DF + 4 * grp) = f32x4{cs[0], cs[1], cs[2], cs[3]};
   }
   __syncthreads();
   if (threadIdx.x < DF) {
     float s = 0.f;
 #pragma unroll
-    for (int sl = 0; sl < L::NSL; ++sl) s += zp[sl * DF + threadIdx.x];
+    for (int zs = 0; zs < Q::NSL; ++zs) s += zp[zs * DF + threadIdx.x];
     out[DF * kPD + threadIdx.x] = s;
   }
 }
@@ -424,7 +432,7 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
   // so that the state tiles take registers in the state waves only.
   if (swave) {
     f32x16 st[L::NT];
-    pf_load_S<DF>(st, Sinit, fh, cb);
+    pf_load_S<L::NT>(st, Sinit, fh * (DF / 2), cb);
     __syncthreads();
     for (int it = 0; it < n; ++it) {
       const int c = c0 + it;
@@ -448,7 +456,7 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
         pf_put16(sR, w, fh ? R0 : R1);
         num = fh ? R1 : R0;
       }
-      pf_update_S<DF>(st, sK, sV, fh, cb);
+      pf_update_S<DF, L::NT>(st, sK, sV, fh * (DF / 2), cb);
       colsum();
       __syncthreads();
       // ---- 3. finish rows [32 fh, +32) x columns [32 cb, +32); move z on ----
@@ -475,7 +483,7 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
       __syncthreads();
     }
     if (a.S_out && seg == a.nseg - 1) {
-      pf_store_S<DF>(st, a.S_out + (long long)bh * DF * kPD, fh, cb);
+      pf_store_S<L::NT>(st, a.S_out + (long long)bh * DF * kPD, fh * (DF / 2), cb);
       if (threadIdx.x < DF) a.z_out[(long long)bh * DF + threadIdx.x] = sZ[(n & 1) * DF + threadIdx.x];
     }
   } else {
@@ -527,7 +535,9 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
 
 template <int DF>
 hipError_t launch_pf(const FwdArgs& a, const ScanArgs& s, hipStream_t st, hipEvent_t* ev) {
-  if (a.run_state_pass) hipLaunchKernelGGL(pf_state_kernel<DF>, dim3(a.BH, a.nseg_state), dim3(256), 0, st, a);
+  constexpr int NW = DF >= 128 ? 8 : 4;
+  if (a.run_state_pass)
+    hipLaunchKernelGGL((pf_state_kernel<DF, NW>), dim3(a.BH, a.nseg_state), dim3(64 * NW), 0, st, a);
   if (ev) (void)hipEventRecord(ev[1], st);
   if (a.run_scan) {
     const hipError_t e = scan_dispatch(s, st);
