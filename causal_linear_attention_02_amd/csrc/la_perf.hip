@@ -313,7 +313,8 @@ struct PoL {
   static constexpr int Z_OFF = ZP_OFF + NSL * DF * 4;     // running z [2][DF]
   static constexpr int DEN_OFF = Z_OFF + 2 * DF * 4;      // phi(q_i) . z per feature half [2][64]
   static constexpr int DP_OFF = DEN_OFF + 2 * 64 * 4;     // in-chunk denominators [64]
-  static constexpr int BYTES = DP_OFF + 64 * 4;
+  static constexpr int Y_OFF = DP_OFF + 64 * 4;           // output tile [64][64] bf16
+  static constexpr int BYTES = Y_OFF + 64 * L::RBV;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -350,6 +351,7 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
   float* sZ = reinterpret_cast<float*>(smem + O::Z_OFF);
   float* sDen = reinterpret_cast<float*>(smem + O::DEN_OFF);
   float* sDp = reinterpret_cast<float*>(smem + O::DP_OFF);
+  uint8_t* sY = smem + O::Y_OFF;
 
   const int bh = blockIdx.x, seg = blockIdx.y;
   const int c0 = seg * a.chunks_per_seg;
@@ -420,6 +422,15 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
       pf_load_v<512>(vr, rsrc(v, c + 1));
     }
   };
+  // the output tile of chunk it (staged in sY) as whole rows, one 16-byte
+  // piece per thread; rows past the end are dropped by the range check
+  auto flush_y = [&](int it) {
+    const int c = c0 + it;
+    const auto ro = make_rsrc(out + (base + 64LL * c) * kPD, (unsigned)(min(64, a.N - 64 * c) * kPD * 2));
+    const int p = threadIdx.x;
+    buf_store16_nt(ro, (p >> 3) * kPD * 2 + 16 * (p & 7),
+                   *reinterpret_cast<const u32x4*>(sY + tile_off<kPD * 2>(p >> 3, 16 * (p & 7))));
+  };
   // column sums of the chunk's phi(K), partials over row slices
   auto colsum = [&]() {
     float cs[4] = {0.f, 0.f, 0.f, 0.f};
@@ -435,8 +446,7 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
     pf_load_S<L::NT>(st, Sinit, fh * (DF / 2), cb);
     __syncthreads();
     for (int it = 0; it < n; ++it) {
-      const int c = c0 + it;
-      const int valid = min(64, a.N - 64 * c);
+      if (it > 0) flush_y(it - 1);
       map_chunk(it);
       __syncthreads();
       // ---- 2. read-out over the wave's feature half, then the S update ----
@@ -465,14 +475,11 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
       const int i = 32 * fh + li;
       float inv = 1.f;
       if (a.normalize) inv = 1.f / fmaxf(sDp[i] + sDen[i] + sDen[64 + i], kEps);
-      if (i < valid) {
-        __bf16* yo = out + (base + 64LL * c + i) * kPD + 32 * cb + 4 * h;
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *reinterpret_cast<u32x2*>(yo + 8 * g) =
-              u32x2{pack_bf16x2(num[4 * g] * inv, num[4 * g + 1] * inv),
-                    pack_bf16x2(num[4 * g + 2] * inv, num[4 * g + 3] * inv)};
-      }
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<u32x2*>(sY + tile_off<kPD * 2>(i, (32 * cb + 8 * g + 4 * h) * 2)) =
+            u32x2{pack_bf16x2(num[4 * g] * inv, num[4 * g + 1] * inv),
+                  pack_bf16x2(num[4 * g + 2] * inv, num[4 * g + 3] * inv)};
       if (threadIdx.x < DF) {  // state waves hold threads 0..255 >= DF - 1
         const float* zc = sZ + (it & 1) * DF;
         float s = zc[threadIdx.x];
@@ -482,6 +489,7 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
       }
       __syncthreads();
     }
+    if (n > 0) flush_y(n - 1);
     if (a.S_out && seg == a.nseg - 1) {
       pf_store_S<L::NT>(st, a.S_out + (long long)bh * DF * kPD, fh * (DF / 2), cb);
       if (threadIdx.x < DF) a.z_out[(long long)bh * DF + threadIdx.x] = sZ[(n & 1) * DF + threadIdx.x];
@@ -490,6 +498,7 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
     __syncthreads();
     const int r = fh;  // query row block of this score wave
     for (int it = 0; it < n; ++it) {
+      if (it > 0) flush_y(it - 1);
       map_chunk(it);
       __syncthreads();
       // ---- 2. A[j][i] for keys j of block 0 (and block 1 when r = 1) and
@@ -530,6 +539,7 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
       __syncthreads();
       __syncthreads();
     }
+    if (n > 0) flush_y(n - 1);
   }
 }
 

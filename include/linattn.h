@@ -86,7 +86,10 @@ const char* la_status_string(int status);
  * Bytes of device workspace that la_forward needs for these sizes (0 when
  * none is needed; any element type). Returns 0 also for invalid arguments.
  * It holds the fp32 states of the sequence segments and, for random features,
- * phi(q) and phi(k) ([B][H][N][m] each, sized for fp32). With LA_POLY2 it
+ * phi(q) and phi(k) ([B][H][N][m] each, sized for fp32). Random features with
+ * d = 64, bf16 input and causal = 1 project q and k inside the chunked passes
+ * and la_forward then needs the segment states only; the size returned here
+ * (which cannot know the element type) still covers phi(q) and phi(k). With LA_POLY2 it
  * holds fp32 partial numerators (2 per token at d = 32, 4 at d = 64, [N][d]
  * each per (batch, head)) and partial denominators (2 or 4 per token).
  */
@@ -105,9 +108,10 @@ size_t la_forward_workspace_size(int B, int H, int N, int d, const la_feature_ma
  *   S_out,z_out optional (both or neither): state after the last token,
  *             S_in + sum_j phi(k_j) v_j^T and z_in + sum_j phi(k_j) (the
  *             hand-off to la_decode_step).
- *   workspace device scratch of at least la_forward_workspace_size() bytes,
- *             256-byte aligned (may be NULL when that size is 0). Its contents
- *             are overwritten.
+ *   workspace device scratch of at least la_forward_workspace_size() bytes
+ *             (random features at d = 64, bf16, causal: the segment states
+ *             suffice), 256-byte aligned (may be NULL when the size needed is
+ *             0). Its contents are overwritten.
  * N = 0 writes only S_out/z_out (= S_in/z_in, or zeros).
  */
 int la_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
