@@ -12,15 +12,16 @@
 //
 // d = 64, bf16 inputs, causal.
 //   state pass : local (S, z) of every segment but the last -> workspace
-//                (4 waves, two blocks per compute unit)
+//                (8 waves for m >= 128, else 4; each holds one feature slice
+//                of S for 32 value columns)
 //   carry scan : the exclusive prefix over segments (la_prefill.hip)
 //   output pass: each segment walks its chunks from its carried prefix
 //                (8 waves, two per SIMD)
-// In both passes wave w < 4 holds S[fh*m/2 .. fh*m/2 + m/2)[32 cb .. 32 cb + 32)
-// in MFMA accumulators (fh = w >> 1, cb = w & 1). In the output pass it also
-// finishes query rows [32 fh, 32 fh + 32) x value columns [32 cb, 32 cb + 32)
-// of every chunk; the read-out over the other feature half comes from wave
-// w ^ 2 and the in-chunk term from a score wave, both through LDS.
+// In the output pass wave w < 4 holds S[fh*m/2 .. fh*m/2 + m/2)[32 cb .. 32 cb + 32)
+// in MFMA accumulators (fh = w >> 1, cb = w & 1) and finishes query rows
+// [32 fh, 32 fh + 32) x value columns [32 cb, 32 cb + 32) of every chunk; the
+// read-out over the other feature half comes from wave w ^ 2 and the in-chunk
+// term from a score wave, both through LDS.
 // Layouts as in the other passes: q, k, v, out [BH][N][64]; S [BH][m][64];
 // z [BH][m].
 #include "la_device.h"
@@ -296,8 +297,10 @@ __global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
 //      score waves 4-7 (r, cb): masked scores of row block r, their product
 //      with v[:, 32 cb, +32) and the in-chunk denominator; all threads: column
 //      sums of phi(K)
-//   3. state wave (fh, cb) adds the hand-overs, normalizes and stores rows
-//      [32 fh, +32) x columns [32 cb, +32); z moves on
+//   3. state wave (fh, cb) adds the hand-overs, normalizes and writes rows
+//      [32 fh, +32) x columns [32 cb, +32) into the LDS output tile; z moves
+//      on. At the start of the next chunk all threads store that tile as
+//      whole rows.
 // ---------------------------------------------------------------------------
 template <int DF>
 struct PoL {
