@@ -21,6 +21,12 @@ constexpr long long kTargetBlocksWide = 512;
 // A segment never gets fewer chunks than this (its carried state costs about
 // as much traffic as 64 tokens of q, k, v and out at d' = d).
 constexpr int kMinChunksPerSegment = 4;
+// Causal forwards whose segment states take at most this many bytes per
+// sequence skip the carry scan: each output-pass workgroup adds the local
+// sums of the segments before it while loading its initial state. On
+// B=4 H=8 N=2048 d=64 (8 segments of 16.6 KB) that saves the scan's launch
+// (~8 us of 27); long sequences (16 states of 66 KB) keep the scan.
+constexpr size_t kFoldBytes = 256 * 1024;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -302,6 +308,11 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   a.W = feature_map->W;
   a.gamma = gamma;
   a.H = H;
+  if (causal && !gamma && p.P > 1 && (size_t)p.P * a.state_elems * sizeof(float) <= kFoldBytes) {
+    a.init_from_ws = 0;
+    a.init_sum_ws = 1;
+    a.run_scan = 0;
+  }
 
   la::ScanArgs s{};
   s.ws = a.ws;

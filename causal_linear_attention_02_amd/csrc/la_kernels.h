@@ -32,6 +32,8 @@ struct FwdArgs {
   int ws_total_slot;       // non-causal: slot holding the full-sequence state
   int state_elems;         // DF * D + DF
   int init_from_ws;        // output pass starts from the workspace slot (else S_in/z_in or zero)
+  int init_sum_ws;         // causal, no decay: segment s starts from S_in/z_in (or zero) plus the
+                           // local sums in slots 0..s-1, added by the output pass itself (no carry scan)
   const float* S_in;       // [BH][DF][D] or null
   const float* z_in;       // [BH][DF] or null
   float* S_out;            // [BH][DF][D] or null (causal: written by the last segment)

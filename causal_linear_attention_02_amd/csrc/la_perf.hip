@@ -166,6 +166,17 @@ __device__ __forceinline__ void pf_load_S(f32x16 (&st)[NT], const float* Sp, int
     }
 }
 template <int NT>
+__device__ __forceinline__ void pf_add_S(f32x16 (&st)[NT], const float* Sp, int f0, int cb) {
+  const int l = threadIdx.x & 63, h = l >> 5, li = l & 31;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int f = f0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+      st[t][r] += Sp[(long long)f * kPD + 32 * cb + li];
+    }
+}
+template <int NT>
 __device__ __forceinline__ void pf_store_S(const f32x16 (&st)[NT], float* Sp, int f0, int cb) {
   const int l = threadIdx.x & 63, h = l >> 5, li = l & 31;
 #pragma unroll
@@ -393,7 +404,12 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
     pf_load_v<512>(vr, rsrc(v, c0));
   }
   pf_stage_W<DF, 512>(a.W, sW);
-  if (threadIdx.x < DF) sZ[threadIdx.x] = zinit ? zinit[threadIdx.x] : 0.f;
+  if (threadIdx.x < DF) {
+    float z0 = zinit ? zinit[threadIdx.x] : 0.f;
+    if (a.init_sum_ws)  // local sums of the segments before this one
+      for (int j = 0; j < seg; ++j) z0 += a.ws[((long long)bh * a.ws_slots + j) * a.state_elems + DF * kPD + threadIdx.x];
+    sZ[threadIdx.x] = z0;
+  }
 
   // 1. feature map of chunk it (all waves), then the loads of chunk it + 1
   auto map_chunk = [&](int it) {
@@ -447,6 +463,9 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
   if (swave) {
     f32x16 st[L::NT];
     pf_load_S<L::NT>(st, Sinit, fh * (DF / 2), cb);
+    if (a.init_sum_ws)
+      for (int j = 0; j < seg; ++j)
+        pf_add_S<L::NT>(st, a.ws + ((long long)bh * a.ws_slots + j) * a.state_elems, fh * (DF / 2), cb);
     __syncthreads();
     for (int it = 0; it < n; ++it) {
       if (it > 0) flush_y(it - 1);

@@ -335,6 +335,18 @@ __device__ __forceinline__ void load_state_tiles(f32x16 (&S)[DF / 32], const flo
 }
 
 template <int D, int DF>
+__device__ __forceinline__ void add_state_tiles(f32x16 (&S)[DF / 32], const float* Sp, int w) {
+  const int l = threadIdx.x & 63, h = l >> 5, li = l & 31;
+#pragma unroll
+  for (int cb = 0; cb < DF / 32; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int c = 32 * cb + 8 * (r >> 2) + 4 * h + (r & 3);
+      S[cb][r] += Sp[(long long)c * D + 32 * w + li];
+    }
+}
+
+template <int D, int DF>
 __device__ __forceinline__ void store_state_tiles(const f32x16 (&S)[DF / 32], float* Sp, int w) {
   const int l = threadIdx.x & 63, h = l >> 5, li = l & 31;
 #pragma unroll
@@ -692,6 +704,15 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
     const Voff<D, DF, IN> vo(p);
 #pragma unroll
     for (int e = 0; e < 8; ++e) zrun[e] = zinit ? fin * zinit[cr + e] : 0.f;
+    if constexpr (CAUSAL && !DECAY) {
+      if (a.init_sum_ws) {  // the carried normalizer: local sums of the segments before this one
+        for (int j = 0; j < seg; ++j) {
+          const float* zj = a.ws + ((long long)bh * a.ws_slots + j) * a.state_elems + DF * D + cr;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) zrun[e] += zj[e];
+        }
+      }
+    }
     // Drain that load now: otherwise the wait-count analysis carries it
     // around the loop and waits for every outstanding prefetch each step.
     wait_vmem_all();
@@ -844,6 +865,12 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
     // ------------------------------------------------------------------
     f32x16 S[DF / 32];
     load_state_tiles<D, DF>(S, Sinit, cw);
+    if constexpr (CAUSAL && !DECAY) {
+      if (a.init_sum_ws) {  // the carried state: local sums of the segments before this one
+        for (int j = 0; j < seg; ++j)
+          add_state_tiles<D, DF>(S, a.ws + ((long long)bh * a.ws_slots + j) * a.state_elems, cw);
+      }
+    }
     if constexpr (DECAY) {  // entering the first chunk: moved on by gamma^64 in the scaled frame
 #pragma unroll
       for (int cb = 0; cb < DF / 32; ++cb) S[cb] = ((S[cb] * fin) * gH) * gH;
