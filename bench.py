@@ -248,10 +248,15 @@ def main():
     if not args.no_variants:
         variants = {}
         gam = torch.linspace(0.9, 0.999, H, device=dev, dtype=torch.float32)  # one decay per head
+        ws_nc = torch.empty(max(la.la_forward_workspace_size(B, H, N, d, causal=False), 256), dtype=torch.uint8,
+                            device=dev)
         runs = {
             "decay": lambda: la.la_forward_decay(tq, tk, tv, gam, normalize=True, out=out, workspace=ws),
             "identity_map": lambda: la.la_forward(tq, tk, tv, feature_map="identity", normalize=False, out=out,
                                                   workspace=ws),
+            # non-causal form: one state pass over every segment, the total by
+            # the scan, then phi(Q) S / phi(Q) z; the same bytes as the causal form
+            "non_causal": lambda: la.la_forward(tq, tk, tv, causal=False, normalize=True, out=out, workspace=ws_nc),
         }
         for name, fn in runs.items():
             for _ in range(20):
@@ -266,7 +271,8 @@ def main():
                               "whole_op_frac_hbm": round(alg_bytes / vw / 1e9 / HBM_PEAK_GBS, 4)}
             log(f"{name}: {vw*1e6:.1f} us/call")
         variants["note"] = ("same workload and bytes as the headline prefill; decay: gamma per head "
-                            "0.9..0.999; identity map: numerator only")
+                            "0.9..0.999; identity map: numerator only; non_causal: sums over all tokens")
+        del ws_nc
 
     del tq, tk, tv, out, ws
     torch.cuda.empty_cache()
