@@ -298,20 +298,22 @@ __global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Output pass: grid (BH, segments), 512 threads (two waves per SIMD).
+// Output pass: grid (BH, segments), 512 threads (two waves per SIMD). Per
+// chunk, two barriers:
 //   1. all waves map the chunk: waves 0-3 q, waves 4-7 k; wave w takes rows
-//      [32 (w & 1), +32) and features [((w >> 1) & 1) m/2, +m/2); q waves
-//      also form phi(q_i) . z over their features; every thread stages one
-//      piece of v
+//      [32 (w & 1), +32) and features [((w >> 1) & 1) m/2, +m/2); every
+//      thread stages one piece of v. After the barrier all threads store the
+//      previous chunk's output tile as whole rows.
 //   2. state waves 0-3 (fh, cb): read-out of both row blocks over their
 //      feature half (the other row block handed to wave w ^ 2), S update;
 //      score waves 4-7 (r, cb): masked scores of row block r, their product
-//      with v[:, 32 cb, +32) and the in-chunk denominator; all threads: column
-//      sums of phi(K)
-//   3. state wave (fh, cb) adds the hand-overs, normalizes and writes rows
-//      [32 fh, +32) x columns [32 cb, +32) into the LDS output tile; z moves
-//      on. At the start of the next chunk all threads store that tile as
-//      whole rows.
+//      with v[:, 32 cb, +32), the in-chunk denominator and phi(q_i) . z over
+//      half of the features; all threads: column sums of phi(K)
+//   3. after the second barrier, state wave (fh, cb) adds the hand-overs,
+//      normalizes and writes rows [32 fh, +32) x columns [32 cb, +32) into the
+//      LDS output tile, and z moves on; then it maps the next chunk, while the
+//      score waves may already be mapping theirs (nothing of steps 1-2 is read
+//      in step 3).
 // ---------------------------------------------------------------------------
 template <int DF>
 struct PoL {
@@ -415,18 +417,14 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
   auto map_chunk = [&](int it) {
     const int c = c0 + it;
     const int valid = min(64, a.N - 64 * c);
-    const float* zc = sZ + (it & 1) * DF;
     const float b = pf_row_bias(xr, bm);
     const int row = 32 * rb + li;
     if (qwave) {
-      float dot = 0.f;
 #pragma unroll 1
       for (int j = 0; j < L::NFB / 2; ++j) {
         const int fb = ph * (L::NFB / 2) + j;
-        dot += pf_phi_store<DF, true>(pf_project<DF>(sW, xr, fb), b, false, sQ, row, fb, zc);
+        pf_phi_store<DF, false>(pf_project<DF>(sW, xr, fb), b, false, sQ, row, fb, nullptr);
       }
-      dot += xor32(dot);
-      if (h == 0) sDen[ph * 64 + row] = dot;
     } else {
       const bool past = row >= valid;
 #pragma unroll 1
@@ -468,9 +466,9 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
         pf_add_S<L::NT>(st, a.ws + ((long long)bh * a.ws_slots + j) * a.state_elems, fh * (DF / 2), cb);
     __syncthreads();
     for (int it = 0; it < n; ++it) {
-      if (it > 0) flush_y(it - 1);
       map_chunk(it);
       __syncthreads();
+      if (it > 0) flush_y(it - 1);
       // ---- 2. read-out over the wave's feature half, then the S update ----
       f32x16 num;
       {
@@ -509,8 +507,8 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
         for (int sl = 0; sl < O::NSL; ++sl) s += zp[sl * DF + threadIdx.x];
         sZ[((it + 1) & 1) * DF + threadIdx.x] = s;
       }
-      __syncthreads();
     }
+    __syncthreads();  // the last output tile is complete
     if (n > 0) flush_y(n - 1);
     if (a.S_out && seg == a.nseg - 1) {
       pf_store_S<L::NT>(st, a.S_out + (long long)bh * DF * kPD, fh * (DF / 2), cb);
@@ -520,9 +518,9 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
     __syncthreads();
     const int r = fh;  // query row block of this score wave
     for (int it = 0; it < n; ++it) {
-      if (it > 0) flush_y(it - 1);
       map_chunk(it);
       __syncthreads();
+      if (it > 0) flush_y(it - 1);
       // ---- 2. A[j][i] for keys j of block 0 (and block 1 when r = 1) and
       // queries i of block r; lane holds query i = 32 r + li ----
       f32x16 Aa = {}, Ab = {};
@@ -547,6 +545,26 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
       }
       dpart += xor32(dpart);
       if (cb == 0 && h == 0) sDp[32 * r + li] = dpart;
+      {
+        // phi(q_i) . z for the rows of block r over features
+        // [cb m/2 + h m/4, +m/4) (bf16 phi(q) from LDS), halves added across
+        // lanes l and l ^ 32; z after the previous chunk
+        const float* zc = sZ + (it & 1) * DF;
+        const int i = 32 * r + li, f0 = cb * (DF / 2) + h * (DF / 4);
+        float dot = 0.f;
+#pragma unroll
+        for (int u = 0; u < DF / 32; ++u) {
+          const u32x4 qv = *reinterpret_cast<const u32x4*>(sQ + tile_off<L::RBF>(i, (f0 + 8 * u) * 2));
+          const f32x4 z0 = *reinterpret_cast<const f32x4*>(zc + f0 + 8 * u);
+          const f32x4 z1 = *reinterpret_cast<const f32x4*>(zc + f0 + 8 * u + 4);
+          dot += __uint_as_float(qv[0] << 16) * z0[0] + __uint_as_float(qv[0] & 0xffff0000u) * z0[1] +
+                 __uint_as_float(qv[1] << 16) * z0[2] + __uint_as_float(qv[1] & 0xffff0000u) * z0[3] +
+                 __uint_as_float(qv[2] << 16) * z1[0] + __uint_as_float(qv[2] & 0xffff0000u) * z1[1] +
+                 __uint_as_float(qv[3] << 16) * z1[2] + __uint_as_float(qv[3] & 0xffff0000u) * z1[3];
+        }
+        dot += xor32(dot);
+        if (h == 0) sDen[cb * 64 + i] = dot;
+      }
       f32x16 av = {};
 #pragma unroll
       for (int kbj = 0; kbj < 2; ++kbj)
@@ -559,8 +577,8 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
       pf_put16(sA, w - 4, av);
       colsum();
       __syncthreads();
-      __syncthreads();
     }
+    __syncthreads();  // the last output tile is complete
     if (n > 0) flush_y(n - 1);
   }
 }
