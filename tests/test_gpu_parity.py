@@ -97,6 +97,19 @@ def test_forward_parity_multisegment(d, dt):
             _check_forward(1, 2, N, d, dt, causal, normalize, seed=7 + d, scale=1.0)
 
 
+@pytest.mark.parametrize("nchunks", [60, 64])
+def test_forward_parity_fold_threshold(nchunks):
+    """One sequence at d = 64 cut into 15 segments (segment states 249.6 KB: the
+    output pass adds the local sums of the segments before it, no carry scan)
+    or 16 (266 KB: carry scan); carried-in state, final state, ragged tail."""
+    d, N = 64, 64 * nchunks - 5
+    rng = np.random.default_rng(nchunks)
+    kk = la_inputs.gaussian(rng, (1, 1, 200, d), bf16=False)
+    vv = la_inputs.gaussian(rng, (1, 1, 200, d), bf16=False)
+    S0, z0 = O.final_state(kk, vv, "elu1")
+    _check_forward(1, 1, N, d, "bf16", True, True, seed=900 + nchunks, scale=1 / 8, S0=S0, z0=z0, state=True)
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_forward_state_in_and_out(dt):
     d, N = 64, 64 * 9 + 5
