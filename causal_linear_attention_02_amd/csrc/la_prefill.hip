@@ -706,6 +706,7 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
     for (int e = 0; e < 8; ++e) zrun[e] = zinit ? fin * zinit[cr + e] : 0.f;
     if constexpr (CAUSAL && !DECAY) {
       if (a.init_sum_ws) {  // the carried normalizer: local sums of the segments before this one
+#pragma unroll 4
         for (int j = 0; j < seg; ++j) {
           const float* zj = a.ws + ((long long)bh * a.ws_slots + j) * a.state_elems + DF * D + cr;
 #pragma unroll
@@ -867,6 +868,7 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
     load_state_tiles<D, DF>(S, Sinit, cw);
     if constexpr (CAUSAL && !DECAY) {
       if (a.init_sum_ws) {  // the carried state: local sums of the segments before this one
+#pragma unroll 4
         for (int j = 0; j < seg; ++j)
           add_state_tiles<D, DF>(S, a.ws + ((long long)bh * a.ws_slots + j) * a.state_elems, cw);
       }
