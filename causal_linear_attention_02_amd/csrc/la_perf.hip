@@ -112,27 +112,20 @@ __device__ __forceinline__ f32x16 pf_project(const uint8_t* sW, const u32x4 (&xr
 
 constexpr float kPfA = 1.4426950408889634f * 0.35355339059327373f;  // log2(e) * 64^(-1/4)
 
-// phi of one projected block -> LDS tile row `row`; returns sum_f phi * z[f]
-// over the lane's features when Z is given
-template <int DF, bool DOT>
-__device__ __forceinline__ float pf_phi_store(const f32x16& u, float b, bool zero, uint8_t* tile, int row, int fb,
-                                              const float* z) {
+// phi of one projected block -> LDS tile row `row` (bf16); zero: the row is
+// past the end of the sequence and gets phi = 0
+template <int DF>
+__device__ __forceinline__ void pf_phi_store(const f32x16& u, float b, bool zero, uint8_t* tile, int row, int fb) {
   const int h = (threadIdx.x >> 5) & 1;
-  float dot = 0.f;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int f = 32 * fb + 8 * g + 4 * h;
     float y[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) y[j] = zero ? 0.f : __builtin_amdgcn_exp2f(kPfA * u[4 * g + j] - b);
-    if constexpr (DOT) {
-      const f32x4 zz = *reinterpret_cast<const f32x4*>(z + f);
-      dot += y[0] * zz[0] + y[1] * zz[1] + y[2] * zz[2] + y[3] * zz[3];
-    }
     *reinterpret_cast<u32x2*>(tile + tile_off<PfL<DF>::RBF>(row, f * 2)) =
         u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
   }
-  return dot;
 }
 
 // column sums of rows [sl * SLR, sl * SLR + SLR) of a phi tile for features
@@ -269,7 +262,7 @@ __global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < Q::NTS; ++j) {
       const int fb = sl * Q::NTS + j;
-      pf_phi_store<DF, false>(pf_project<DF>(sW, xr, fb), b, past, sK, 32 * rb + li, fb, nullptr);
+      pf_phi_store<DF>(pf_project<DF>(sW, xr, fb), b, past, sK, 32 * rb + li, fb);
     }
     pf_store_v<NTH>(vr, sV);
     if (it + 1 < n) {
@@ -423,14 +416,14 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
 #pragma unroll 1
       for (int j = 0; j < L::NFB / 2; ++j) {
         const int fb = ph * (L::NFB / 2) + j;
-        pf_phi_store<DF, false>(pf_project<DF>(sW, xr, fb), b, false, sQ, row, fb, nullptr);
+        pf_phi_store<DF>(pf_project<DF>(sW, xr, fb), b, false, sQ, row, fb);
       }
     } else {
       const bool past = row >= valid;
 #pragma unroll 1
       for (int j = 0; j < L::NFB / 2; ++j) {
         const int fb = ph * (L::NFB / 2) + j;
-        pf_phi_store<DF, false>(pf_project<DF>(sW, xr, fb), b, past, sK, row, fb, nullptr);
+        pf_phi_store<DF>(pf_project<DF>(sW, xr, fb), b, past, sK, row, fb);
       }
     }
     pf_store_v<512>(vr, sV);
