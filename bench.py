@@ -45,9 +45,9 @@ def parse():
     p.add_argument("--no-variants", action="store_true")
     p.add_argument("--poly-steps", type=int, default=50)
     p.add_argument("--no-poly", action="store_true")
-    p.add_argument("--mid-steps", type=int, default=200)
+    p.add_argument("--mid-steps", type=int, default=1000)
     p.add_argument("--no-mid", action="store_true")
-    p.add_argument("--performer-steps", type=int, default=50)
+    p.add_argument("--performer-steps", type=int, default=100)
     p.add_argument("--no-performer", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -92,6 +92,17 @@ def read_traffic(summary, sources, bytes_per_launch):
         return None, "summary without traffic"
     return t, f"{summary}: read {kv.get('read_bytes_per_launch')} + write {kv.get('write_bytes_per_launch')} B " \
               f"(calibrated FETCH_SIZE/WRITE_SIZE), {t / bytes_per_launch:.3f} x algorithmic"
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
 
 
 def blas_threads():
@@ -508,6 +519,7 @@ def main():
             tc += time.perf_counter() - t0
             nh += 1
         cpu = {"value": (nh * N / H) / tc, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+               "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
                "sample": f"oracle.chunked (fp64, numpy) on {nh} of {H} heads x {N} tokens, d={d}; "
                          f"tokens/s = B*N*(heads timed/H)/time", "seconds": round(tc, 2)}
         if decode is not None:
