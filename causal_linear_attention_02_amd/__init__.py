@@ -24,11 +24,13 @@ __all__ = [
     "la_version", "la_status_string", "la_forward_workspace_size", "la_forward", "la_forward_ex",
     "la_decode_step", "la_feature_map_apply", "feature_dim", "la_forward_decay", "la_decode_step_decay",
     "la_backward_workspace_size", "la_backward", "la_backward_decay", "la_forward_gated_workspace_size", "la_forward_gated",
-    "la_decode_step_gated",
+    "la_decode_step_gated", "la_device_status",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "liblinattn.so")
+# LINATTN_LIBRARY names another build of this same library (for example a
+# host-side sanitizer build of the ABI layer used by the CPU tests)
+library_path = os.environ.get("LINATTN_LIBRARY") or os.path.join(_HERE, "liblinattn.so")
 header_path = os.path.join(os.path.dirname(_HERE), "include", "linattn.h")
 
 LA_OK = 0
@@ -58,6 +60,7 @@ def _load():
     fmp = ctypes.POINTER(la_feature_map)
     L.la_version.argtypes, L.la_version.restype = [], i
     L.la_status_string.argtypes, L.la_status_string.restype = [i], ctypes.c_char_p
+    L.la_device_status.argtypes, L.la_device_status.restype = [vp], i
     L.la_forward_workspace_size.argtypes = [i, i, i, i, fmp, i]
     L.la_forward_workspace_size.restype = sz
     fwd = [vp, vp, vp, vp, i, i, i, i, fmp, i, i, i, vp, vp, vp, vp, vp, sz, vp]
@@ -164,6 +167,15 @@ def la_version() -> int:
 
 def la_status_string(status: int) -> str:
     return lib.la_status_string(status).decode()
+
+
+def la_device_status(stream=None) -> int:
+    """Synchronize the stream, then read and clear the device flag raised by
+    decay factors or gates outside [1/4, 1]: LA_OK or LA_ERR_INVALID_ARG."""
+    st = lib.la_device_status(_stream(stream))
+    if st not in (LA_OK, LA_ERR_INVALID_ARG):
+        raise LinAttnError(st, "la_device_status")
+    return st
 
 
 def la_forward_workspace_size(B, H, N, d, feature_map="elu1", W=None, causal=True) -> int:

@@ -1,13 +1,40 @@
 // Host side of the C ABI declared in include/linattn.h: argument validation,
 // work planning (sequence segments, workspace carving) and kernel dispatch.
-// Nothing here allocates device memory or keeps state between calls.
+// Nothing here allocates device memory. The only state kept between calls is
+// the address, per device, of the library's device status flag.
 #include "linattn.h"
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "la_kernels.h"
 
+// Raised (set to nonzero) by the chunked decay and gated kernels when a decay
+// factor or gate lies outside the range they support; read and cleared by
+// la_device_status. One per device: every GPU the library runs on holds its
+// own copy, at its own address.
+__device__ int la_status_flag;
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+int* g_flag_addr[kMaxDevices];
+
+// Device address of la_status_flag on the current device (looked up once per
+// device with that device current), or null when the runtime refuses.
+int* status_flag_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  if (!g_flag_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(la_status_flag)) != hipSuccess) return nullptr;
+    g_flag_addr[dev] = static_cast<int*>(p);
+  }
+  return g_flag_addr[dev];
+}
 
 constexpr int kChunk = 64;
 // Output/state passes aim for this many workgroups so that every compute unit
@@ -125,7 +152,19 @@ size_t poly_ws_bytes(long long BH, int N, int d) {
 
 extern "C" {
 
-int la_version(void) { return (0 << 16) | 1; }
+int la_version(void) { return (0 << 16) | 2; }
+
+int la_device_status(hipStream_t stream) {
+  int* flag = status_flag_ptr();
+  if (!flag) return LA_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return LA_ERR_HIP;
+  int v = 0;
+  if (hipMemcpy(&v, flag, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return LA_ERR_HIP;
+  if (v == 0) return LA_OK;
+  const int zero = 0;
+  if (hipMemcpy(flag, &zero, sizeof(int), hipMemcpyHostToDevice) != hipSuccess) return LA_ERR_HIP;
+  return LA_ERR_INVALID_ARG;
+}
 
 const char* la_status_string(int status) {
   switch (status) {
@@ -197,6 +236,10 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
                 overlaps(z_out, z_bytes, q, tok_bytes) || overlaps(z_out, z_bytes, k, tok_bytes) ||
                 overlaps(z_out, z_bytes, v, tok_bytes) || overlaps(z_out, z_bytes, out, tok_bytes)))
     return LA_ERR_INVALID_ARG;
+  // the decay factors are read by every pass: no output may overlap them
+  if (gamma && (overlaps(out, tok_bytes, gamma, 4LL * H) || overlaps(S_out, s_bytes, gamma, 4LL * H) ||
+                overlaps(z_out, z_bytes, gamma, 4LL * H)))
+    return LA_ERR_INVALID_ARG;
 
   if (feature_map->kind == LA_POLY2) {
     if (gamma) return LA_ERR_UNSUPPORTED;
@@ -251,11 +294,16 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
         overlaps(workspace, (long long)p.ws_bytes, k, tok_bytes) ||
         overlaps(workspace, (long long)p.ws_bytes, v, tok_bytes) ||
         overlaps(workspace, (long long)p.ws_bytes, S_out, s_bytes) ||
+        overlaps(workspace, (long long)p.ws_bytes, z_out, z_bytes) ||
         overlaps(workspace, (long long)p.ws_bytes, S_in, s_bytes) ||
+        overlaps(workspace, (long long)p.ws_bytes, z_in, z_bytes) ||
+        overlaps(workspace, (long long)p.ws_bytes, gamma, 4LL * H) ||
         (mapped && overlaps(workspace, (long long)p.ws_bytes, feature_map->W, (long long)dfeat * d * 4)))
       return LA_ERR_INVALID_ARG;
   }
 
+  int* flag = nullptr;  // looked up after validation: a rejected call makes no HIP call
+  if (gamma && !(flag = status_flag_ptr())) return LA_ERR_HIP;
   if (events) {
     if (hipEventRecord(events[0], stream) != hipSuccess) return LA_ERR_HIP;
   }
@@ -309,6 +357,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   a.W = feature_map->W;
   a.gamma = gamma;
   a.H = H;
+  a.status_flag = flag;
   if (causal && !gamma && p.P > 1 && (size_t)p.P * a.state_elems * sizeof(float) <= kFoldBytes) {
     a.init_from_ws = 0;
     a.init_sum_ws = 1;
@@ -326,6 +375,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   s.z_in = z_in;
   s.gamma = gamma;
   s.H = H;
+  s.status_flag = flag;
   s.seg_len = 64 * p.cps;  // every combined (non-last) segment is whole
   if (causal) {
     s.P = p.P - 1;
@@ -405,6 +455,9 @@ int decode_impl(float* S, float* z, const void* q, const void* k, const void* v,
         overlaps(z, zb, feature_map->W, wb))
       return LA_ERR_INVALID_ARG;
   }
+  if (gamma && (overlaps(out, tb, gamma, 4LL * H) || overlaps(S, sb, gamma, 4LL * H) ||
+                overlaps(z, zb, gamma, 4LL * H)))
+    return LA_ERR_INVALID_ARG;
   la::DecodeArgs a{};
   a.S = S;
   a.z = z;
@@ -562,6 +615,8 @@ int backward_impl(const void* q, const void* k, const void* v, const void* dout,
       if (overlaps(workspace, (long long)p.ws_bytes, all[j], allb[j])) return LA_ERR_INVALID_ARG;
     if (gamma && overlaps(workspace, (long long)p.ws_bytes, gamma, 4LL * H)) return LA_ERR_INVALID_ARG;
   }
+  int* flag = nullptr;
+  if (gamma && !(flag = status_flag_ptr())) return LA_ERR_HIP;
   char* wsb = static_cast<char*>(workspace);
   float* ws_fwd = reinterpret_cast<float*>(wsb);
   float* ws_rev = reinterpret_cast<float*>(wsb + p.fwd_bytes);
@@ -590,6 +645,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* dout,
   fa.normalize = normalize;
   fa.H = H;
   fa.gamma = gamma;
+  fa.status_flag = flag;
   la::ScanArgs fsa{};
   fsa.ws = ws_fwd;
   fsa.ws_slots = p.P;
@@ -605,6 +661,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* dout,
   fsa.H = H;
   fsa.seg_len = 64 * p.cps;
   fsa.gamma = gamma;
+  fsa.status_flag = flag;
 
   la::BwdArgs b{};
   b.q = q;
@@ -632,6 +689,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* dout,
   b.H = H;
   b.dS_out = dS_out;
   b.dz_out = dz_out;
+  b.status_flag = flag;
 
   // suffix sums of the segments' gradient states, seeded with dS_out / dz_out
   la::ScanArgs rs{};
@@ -653,6 +711,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* dout,
   rs.H = H;
   rs.seg_len = 64 * p.cps;
   rs.gamma = gamma;
+  rs.status_flag = flag;
   const int kfm = feature_map->kind == LA_ELU1 ? la::kElu1 : la::kIdentity;
   return status_from_hip(la::backward_dispatch(fa, fsa, b, rs, d, kfm, dtype, gamma != nullptr, stream));
 }
@@ -758,6 +817,8 @@ int la_forward_gated(const void* q, const void* k, const void* v, const float* l
     }
   }
   const Plan& p = g.p;
+  int* flag = status_flag_ptr();
+  if (!flag) return LA_ERR_HIP;
   char* wsb = static_cast<char*>(workspace);
   la::GatedArgs ga{};
   la::FwdArgs& a = ga.f;
@@ -784,6 +845,7 @@ int la_forward_gated(const void* q, const void* k, const void* v, const float* l
   a.z_out = z_out;
   a.normalize = normalize;
   a.H = H;
+  a.status_flag = flag;
   ga.log_gates = log_gates;
   ga.lfac = g.lfac_bytes ? reinterpret_cast<float*>(wsb + g.state_bytes) : nullptr;
 
@@ -803,6 +865,7 @@ int la_forward_gated(const void* q, const void* k, const void* v, const float* l
   s.seg_len = 64 * p.cps;
   s.lfac = ga.lfac;
   s.lfac_stride = p.P;
+  s.status_flag = flag;
   const int kfm = feature_map->kind == LA_ELU1 ? la::kElu1 : la::kIdentity;
   return status_from_hip(la::gated_dispatch(ga, s, d, kfm, dtype, stream));
 }

@@ -228,7 +228,7 @@ struct Decay {
 template <bool DECAY>
 __device__ __forceinline__ Decay decay_of(const BwdArgs& a, int bh) {
   Decay d;
-  if constexpr (DECAY) d.lg = __log2f(a.gamma[bh % a.H]);
+  if constexpr (DECAY) d.lg = decay_log2(a.gamma[bh % a.H], a.status_flag);
   return d;
 }
 

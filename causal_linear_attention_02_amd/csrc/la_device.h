@@ -255,6 +255,35 @@ template <> struct Ops<float> {
 // s_waitcnt vmcnt(0): wait for every outstanding vector memory operation.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// ---------------------------------------------------------------------------
+// Range guard of the chunked decay and gated kernels. They scale the rows of
+// a 64-token chunk by up to gamma^-32 (or alpha^-32 per feature), which stays
+// within 2^64 only for gamma, alpha in [1/4, 1]. A value outside that range
+// (NaN included) becomes NaN, so every output that depends on it is NaN, and
+// raises the device status flag that the host reports (la_device_status).
+// The flag is set by a vector atomic from one lane.
+// ---------------------------------------------------------------------------
+constexpr float kMinFactor = 0.25f;
+constexpr float kMinLogFactor = -1.3862944f;   // log(1/4), rounded toward -inf in fp32
+
+__device__ __forceinline__ void raise_status(int* flag) {
+  if (flag) atomicOr(flag, 1);
+}
+
+// log2(gamma) for gamma in [1/4, 1]; NaN (and the flag, from thread 0) otherwise.
+__device__ __forceinline__ float decay_log2(float g, int* flag) {
+  if (g >= kMinFactor && g <= 1.f) return __log2f(g);
+  if (threadIdx.x == 0) raise_status(flag);
+  return __builtin_nanf("");
+}
+
+// A log-gate in [log(1/4), 0] as given; NaN (and the flag) otherwise.
+__device__ __forceinline__ float checked_log_gate(float x, int* flag) {
+  if (x >= kMinLogFactor && x <= 0.f) return x;
+  raise_status(flag);
+  return __builtin_nanf("");
+}
+
 // Exchange with the lane 32 positions away (l ^ 32).
 __device__ __forceinline__ float xor32(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

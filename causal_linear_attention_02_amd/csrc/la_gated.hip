@@ -66,8 +66,11 @@ __device__ __forceinline__ float colsum_lanes(float x) {
 // 64*D/NT consecutive rows, and add the totals of the rows before theirs.
 // Rows past the end of the sequence load as 0 (buffer range check), so lam
 // stays at its last value there. tot: NT/D x D scratch. Three barriers.
+// A log-gate outside [log(1/4), 0] becomes NaN (checked_log_gate), so the
+// prefix of its channel is NaN from its row on, and raises the status flag.
 template <int D, int NT>
-__device__ __forceinline__ void gate_prefix(const float* lg, long long row0, int valid, float* lam, float* tot) {
+__device__ __forceinline__ void gate_prefix(const float* lg, long long row0, int valid, float* lam, float* tot,
+                                            int* flag) {
   constexpr int NQ = NT / D, RPQ = 64 / NQ, NPC = 16 * D / NT;  // pieces of 4 per thread
   const int t = threadIdx.x, col = t % D, qt = t / D;
   const auto R = make_rsrc(lg + row0 * D, (unsigned)(valid * D * 4));
@@ -75,7 +78,11 @@ __device__ __forceinline__ void gate_prefix(const float* lg, long long row0, int
 #pragma unroll
   for (int i = 0; i < NPC; ++i) p[i] = __builtin_bit_cast(f32x4, buf_load16(R, (t + NT * i) * 16));
 #pragma unroll
-  for (int i = 0; i < NPC; ++i) *reinterpret_cast<f32x4*>(lam + 4 * (t + NT * i)) = p[i];
+  for (int i = 0; i < NPC; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[i][e] = checked_log_gate(p[i][e], flag);
+    *reinterpret_cast<f32x4*>(lam + 4 * (t + NT * i)) = p[i];
+  }
   __syncthreads();
   float run = 0.f;
   for (int r = 0; r < RPQ; ++r) {
@@ -141,7 +148,7 @@ __global__ __launch_bounds__(D * 2) void gla_state_kernel(GatedArgs g) {
       rk[i] = In8<IN>::bload(Rk, o);
       rv[i] = In8<IN>::bload(Rv, o);
     }
-    gate_prefix<D, NT>(g.log_gates, row0, valid, lam, tot);
+    gate_prefix<D, NT>(g.log_gates, row0, valid, lam, tot, g.f.status_flag);
     float l63[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -266,7 +273,7 @@ __global__ __launch_bounds__(D * 4) void gla_output_kernel(GatedArgs g) {
       rk[i] = In8<IN>::bload(Rk, o);
       rv[i] = In8<IN>::bload(Rv, o);
     }
-    gate_prefix<D, NT>(g.log_gates, row0, valid, lam, tot);
+    gate_prefix<D, NT>(g.log_gates, row0, valid, lam, tot, g.f.status_flag);
     // stage Qh, Kh (rows past the end: 0), V; column sums of Kh
     float lc[8], cs[8];
 #pragma unroll

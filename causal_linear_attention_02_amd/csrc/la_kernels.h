@@ -44,6 +44,7 @@ struct FwdArgs {
   int H;                   // heads (gamma index = bh % H)
   int skip_output;         // run the state pass and scan only (segment prefixes for the gradient passes)
   int hilo_keys;           // state pass with phi(K) as hi + lo bf16 (bf16, no decay, d' = d; gradient passes)
+  int* status_flag;        // device flag raised when a decay factor or gate is outside the supported range
 };
 
 struct ScanArgs {
@@ -64,6 +65,7 @@ struct ScanArgs {
   int seg_len;         // tokens per combined segment (all full)
   const float* lfac;   // gated: per-segment, per-channel log factors [BH][lfac_stride][DF] or null:
   int lfac_stride;     //   P_{s+1} = diag(exp(lfac_s)) P_s + L_s
+  int* status_flag;    // as FwdArgs::status_flag
 };
 
 struct DecodeArgs {
@@ -108,6 +110,7 @@ struct BwdArgs {
   int H;
   const float* dS_out;     // decay: cotangents of the final state, added by the passes themselves
   const float* dz_out;
+  int* status_flag;        // as FwdArgs::status_flag
 };
 
 // Gated linear attention (per-token, per-channel log-gates on the feature

@@ -399,7 +399,7 @@ __global__ __launch_bounds__(D * 2, DECAY ? 2 : 1) void state_pass_kernel(FwdArg
 #pragma unroll
   for (int e = 0; e < 8; ++e) zr[e] = 0.f;
   const Voff<D, DF, IN> vo(p);
-  const float lg = DECAY ? __log2f(a.gamma[bh % a.H]) : 0.f;
+  const float lg = DECAY ? decay_log2(a.gamma[bh % a.H], a.status_flag) : 0.f;
   const float gH = DECAY ? gpow(lg, kChunk / 2) : 1.f;  // gamma^32; a chunk moves states on by gH twice
 
   // every load is issued (with zero size past the segment) so that all
@@ -572,7 +572,7 @@ __global__ __launch_bounds__(256) void carry_scan_kernel(ScanArgs a) {
   float* col = a.ws + (long long)bh * a.ws_slots * a.state_elems + e;
   const long long st = a.state_elems;
   // decay: each combined segment of seg_len tokens multiplies what precedes it by gamma^seg_len
-  const float g = a.gamma ? gpow(__log2f(a.gamma[bh % a.H]), (float)a.seg_len) : 1.f;
+  const float g = a.gamma ? gpow(decay_log2(a.gamma[bh % a.H], a.status_flag), (float)a.seg_len) : 1.f;
   constexpr int kScanBatch = 32;
   for (int p0 = 0; p0 < a.P; p0 += kScanBatch) {
     const int cnt = min(kScanBatch, a.P - p0);
@@ -674,7 +674,7 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
   // decay: per-head gamma, the per-chunk factor and the factor of the final
   // state (scaled frame back to the true one, and a partial last chunk of
   // vl rows moved on by gamma^vl instead of gamma^64)
-  const float lg = DECAY ? __log2f(a.gamma[bh % a.H]) : 0.f;
+  const float lg = DECAY ? decay_log2(a.gamma[bh % a.H], a.status_flag) : 0.f;
   const float gH = DECAY ? gpow(lg, kChunk / 2) : 1.f;  // gamma^32; a chunk moves states on by gH twice
   const int vl = a.N - kChunk * (a.nchunks - 1);
   const float fout = DECAY ? gpow(lg, kDecayFrame + vl - kChunk) : 1.f;

@@ -83,6 +83,21 @@ int la_version(void);
 const char* la_status_string(int status);
 
 /*
+ * Status of the device work of earlier calls on the current device.
+ * The chunked decay and gated kernels (la_forward_decay, la_backward_decay,
+ * la_forward_gated) support decay factors and gates in [1/4, 1] only ("Linear
+ * Attention", "Variantes y extensiones": decay and gates enter as powers of
+ * up to 32 within a 64-token chunk). A value outside that range, NaN
+ * included, cannot be seen on the host (it lives in device memory); the
+ * kernels turn it into NaN, so every output that depends on it is NaN, and
+ * raise a device flag. This call synchronizes `stream`, then reads and
+ * clears that flag: LA_ERR_INVALID_ARG if any such value was met since the
+ * last call, LA_OK if none, LA_ERR_HIP if the runtime fails. Work still
+ * running on other streams may raise the flag after the read.
+ */
+int la_device_status(hipStream_t stream);
+
+/*
  * Bytes of device workspace that la_forward needs for these sizes (0 when
  * none is needed; any element type). Returns 0 also for invalid arguments.
  * It holds the fp32 states of the sequence segments and, for random features,
@@ -154,7 +169,8 @@ int la_decode_step(float* S, float* z, const void* q, const void* k, const void*
  *   gamma  in: DEVICE pointer to H fp32 values, one per head (head h of every
  *          batch uses gamma[h]); each must lie in [1/4, 1] (1 = no decay;
  *          the kernels scale rows of a 64-token chunk by up to gamma^(-32)).
- *          Values are not checked on the host.
+ *          A head whose gamma is outside that range gets NaN outputs (and
+ *          NaN S_out/z_out) and raises the flag that la_device_status reports.
  * Everything else as la_forward with causal = 1 (same workspace size).
  */
 int la_forward_decay(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
@@ -220,7 +236,8 @@ int la_backward(const void* q, const void* k, const void* v, const void* dout, v
  * L = <dout, out> + <dS_out, S_out> + <dz_out, z_out>:
  * dS_in/dz_in then hold dL/dS_in, dL/dz_in, in which every token's term
  * carries its decay factor. gamma: DEVICE pointer to H fp32 values in
- * [1/4, 1], as for la_forward_decay (values are not checked on the host).
+ * [1/4, 1], as for la_forward_decay (outside it: NaN gradients for that head
+ * and the la_device_status flag).
  * Workspace: la_backward_workspace_size() bytes. Everything else as
  * la_backward.
  */
@@ -245,7 +262,9 @@ size_t la_forward_gated_workspace_size(int B, int H, int N, int d, const la_feat
  * evaluated blockwise ("Entrenamiento: forma paralela").
  *   log_gates in: DEVICE pointer, [B][H][N][d] fp32, log(alpha) in [-log 4, 0]
  *             (alpha in [1/4, 1]; the kernels scale rows of a 64-token chunk by
- *             up to alpha^-32 per feature). Values are not checked on the host.
+ *             up to alpha^-32 per feature). A log-gate outside that range
+ *             (NaN included) becomes NaN, so the outputs that depend on it
+ *             are NaN, and raises the flag that la_device_status reports.
  *   S_in, z_in enter output t through feature f with the product of the gates
  *             of tokens 0..t; S_out, z_out are the gated state after the last token.
  * elu+1 and the identity map; random features return LA_ERR_UNSUPPORTED.

@@ -279,3 +279,37 @@ def test_poly2_map_planning_and_limits():
                                   FAKE2 * 8, FAKE + 0x500000, 1, 1, 64, ctypes.byref(poly), 1, la.LA_BF16, None)
     assert st == la.LA_ERR_UNSUPPORTED
     assert la.feature_dim(64, "poly2") == 4161
+
+
+def test_forward_rejects_state_and_decay_overlaps():
+    """The segment workspace must overlap no state buffer (z_in, z_out
+    included), and decay factors must overlap no output or the workspace;
+    all of it is checked before any HIP call."""
+    need = lib.la_forward_workspace_size(1, 1, 65536, 128, ctypes.byref(ELU), 1)
+    ws = FAKE2 * 4
+    base = dict(N=65536, d=128, ws=ws, ws_bytes=need)
+    S_ok, z_ok = FAKE2 * 8, FAKE2 * 8 + 0x100000
+    assert _fwd(S_out=S_ok, z_out=ws + 256, **base) == la.LA_ERR_INVALID_ARG      # z_out inside the workspace
+    assert _fwd(S_in=S_ok, z_in=ws + 512, **base) == la.LA_ERR_INVALID_ARG        # z_in inside the workspace
+    assert _fwd(S_out=ws + 1024, z_out=z_ok, **base) == la.LA_ERR_INVALID_ARG     # S_out inside the workspace
+
+    def dec_fwd(gamma, out=FAKE2, S_out=None, z_out=None, ws_=ws):
+        return lib.la_forward_decay(FAKE, FAKE + 0x10000000, FAKE + 0x20000000, out, 1, 1, 65536, 128,
+                                    ctypes.byref(ELU), gamma, 1, la.LA_BF16, None, None, S_out, z_out, ws_, need,
+                                    None)
+    assert dec_fwd(FAKE2 + 64) == la.LA_ERR_INVALID_ARG                              # gamma inside out
+    assert dec_fwd(ws + 4096) == la.LA_ERR_INVALID_ARG                               # gamma inside the workspace
+    assert dec_fwd(z_ok + 8, S_out=S_ok, z_out=z_ok) == la.LA_ERR_INVALID_ARG        # gamma inside z_out
+    assert dec_fwd(FAKE2 + 2) == la.LA_ERR_INVALID_ARG                               # misaligned gamma
+    assert dec_fwd(None) == la.LA_ERR_INVALID_ARG
+
+
+def test_decode_decay_rejects_gamma_overlaps():
+    def dec(gamma):
+        return lib.la_decode_step_decay(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000,
+                                        FAKE + 0x4000000, FAKE + 0x5000000, 2, 2, 64, ctypes.byref(ELU), gamma, 1,
+                                        la.LA_BF16, None)
+    assert dec(FAKE + 0x5000000) == la.LA_ERR_INVALID_ARG    # gamma inside out
+    assert dec(FAKE + 256) == la.LA_ERR_INVALID_ARG          # gamma inside S
+    assert dec(FAKE + 0x1000000) == la.LA_ERR_INVALID_ARG    # gamma inside z
+    assert dec(None) == la.LA_ERR_INVALID_ARG
