@@ -14,3 +14,14 @@ if _ORACLE_UNDER_TEST:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: long-running CPU check")
+
+
+def pytest_terminal_summary(terminalreporter):
+    helpers = sys.modules.get("gpu_helpers")
+    if helpers is not None and helpers.WORST_ROW["where"]:
+        w = helpers.WORST_ROW
+        terminalreporter.write_line(f"worst per-row relative error in the GPU parity checks: {w['err']:.3e} "
+                                    f"({w['where']})")
+        terminalreporter.write_line("worst per-row relative error by check site:")
+        for site, (err, detail) in sorted(helpers.WORST_BY_SITE.items(), key=lambda kv: -kv[1][0]):
+            terminalreporter.write_line(f"  {err:.3e}  {site}  {detail}")

@@ -112,3 +112,32 @@ def test_decay_rejected_for_bad_gamma_argument():
     x = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):
         la.la_forward_decay(x, x.clone(), x.clone(), torch.ones(3, device="cuda"))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_decay_out_of_range_gamma_is_flagged(dt):
+    """gamma outside [1/4, 1] (0.05, 1.5, NaN): that head's outputs and final
+    state are NaN, the other heads still match the oracle, and
+    la_device_status reports the violation once (then it is cleared)."""
+    B, H, N, d = 1, 4, 64 * 9 + 5, 64
+    log(f"case decay out-of-range gamma {dt}")
+    assert la.la_device_status() in (la.LA_OK, la.LA_ERR_INVALID_ARG)   # start from a clear flag
+    q, k, v = qkv(B, H, N, d, 91, dt, 1 / 8)
+    g = np.array([0.05, 0.9, 1.5, np.nan], dtype=np.float32)
+    y, S, z = la.la_forward_decay(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), torch.from_numpy(g).cuda(),
+                                  return_state=True)
+    torch.cuda.synchronize()
+    assert la.la_device_status() == la.LA_ERR_INVALID_ARG
+    assert la.la_device_status() == la.LA_OK
+    yh, Sh, zh = to_host(y), to_host(S), to_host(z)
+    for h in (0, 2, 3):
+        assert np.isnan(yh[:, h]).all() and np.isnan(Sh[:, h]).all() and np.isnan(zh[:, h]).all(), h
+    ref = O.attention(q[:, 1:2], k[:, 1:2], v[:, 1:2], "elu1", decay=0.9)
+    e = rel_err(yh[:, 1:2], ref)
+    log(f"  valid head rel err {e:.3e}")
+    assert e <= TOL[dt]
+    # gamma at the ends of the range raises nothing
+    y2 = la.la_forward_decay(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt),
+                             torch.tensor([0.25, 1.0, 0.5, 0.75], device="cuda"))
+    torch.cuda.synchronize()
+    assert la.la_device_status() == la.LA_OK and not torch.isnan(y2).any()

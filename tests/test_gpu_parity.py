@@ -201,3 +201,90 @@ def test_decode_unnormalized_and_prefill_handoff():
     _, Sr, zr = O.decode_step(Sx, zx, q[:, :, -1], k[:, :, -1], v[:, :, -1], "elu1")
     yr = np.einsum("bhc,bhce->bhe", O.phi_elu1(q[:, :, -1]), Sr)
     assert rel_err(to_host(y)[..., None, :], yr[..., None, :]) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# the denominator clamp: y = num / max(den, 1e-6)
+# ---------------------------------------------------------------------------
+# Rows whose phi(q) vanishes (q = -1e30: elu+1 gives phi = 0 exactly, so
+# num = den = 0 and y = 0) or nearly vanishes (q = -30: phi = e^-30, den of
+# order 1e-9, below the clamp, so y = num / 1e-6 instead of num / den, a value
+# some 10^3 - 10^5 times smaller than the weighted mean of v). The clamped rows
+# are compared as a group of their own, so that their small scale is not
+# hidden under the per-row floor of the other rows.
+def _clamp_rows(N):
+    i = np.arange(N)
+    return np.nonzero(i % 7 == 3)[0], np.nonzero(i % 7 == 5)[0]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_denominator_clamp_prefill(dt, causal):
+    B, H, N, d = 1, 2, 64 * 5 + 11, 64
+    log(f"case denominator clamp prefill B{B} H{H} N{N} d{d} {dt} causal={causal}")
+    q, k, v = qkv(B, H, N, d, 501, dt, 1 / 8)
+    zero_rows, tiny_rows = _clamp_rows(N)
+    fill = (lambda x: la_inputs.bf16_round(np.float32(x))) if dt == "bf16" else np.float32
+    q[:, :, zero_rows] = fill(-1e30)
+    q[:, :, tiny_rows] = fill(-30.0)
+    y = to_host(la.la_forward(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), causal=causal))
+    ref = O.attention(q, k, v, "elu1", causal=causal)
+    # the oracle's clamped rows really are clamped: far below the weighted means
+    unclamped = O.attention(q, k, v, "elu1", causal=causal, normalize=False)
+    den = np.einsum("bhnc,bhnc->bhn", O.phi_elu1(q.astype(np.float64)), np.cumsum(O.phi_elu1(k.astype(np.float64)),
+                    axis=2) if causal else np.broadcast_to(O.phi_elu1(k.astype(np.float64)).sum(axis=2, keepdims=True),
+                                                           k.shape))
+    assert np.all(den[:, :, tiny_rows] < 1e-7) and np.all(den[:, :, zero_rows] == 0.0)
+    np.testing.assert_allclose(ref[:, :, tiny_rows], unclamped[:, :, tiny_rows] / 1e-6, rtol=1e-12)
+    assert not np.isnan(y).any()
+    assert np.all(y[:, :, zero_rows] == 0.0)
+    e_all = rel_err(y, ref)
+    e_tiny = rel_err(y[:, :, tiny_rows], ref[:, :, tiny_rows])
+    log(f"  rel err all rows {e_all:.3e}, clamped rows {e_tiny:.3e}")
+    assert e_all <= TOL[dt] and e_tiny <= TOL[dt]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_denominator_clamp_decode(dt):
+    B, H, d, N0 = 2, 3, 64, 300
+    log(f"case denominator clamp decode B{B} H{H} d{d} {dt}")
+    q, k, v = qkv(B, H, N0 + 1, d, 502, dt, 1 / 8)
+    S0, z0 = O.final_state(k[:, :, :N0], v[:, :, :N0], "elu1")
+    S = torch.from_numpy(S0.astype(np.float32)).cuda()
+    z = torch.from_numpy(z0.astype(np.float32)).cuda()
+    qt = q[:, :, N0].copy()
+    fill = (lambda x: la_inputs.bf16_round(np.float32(x))) if dt == "bf16" else np.float32
+    qt[0, 1] = fill(-30.0)      # den = e^-30 * sum(z) ~ 1e-9: clamped
+    qt[1, 2] = fill(-1e30)      # phi(q) = 0: y = 0
+    y = to_host(la.la_decode_step(S, z, to_dev(qt, dt), to_dev(k[:, :, N0], dt), to_dev(v[:, :, N0], dt)))
+    torch.cuda.synchronize()
+    yr, _, zr = O.decode_step(S0, z0, qt, k[:, :, N0], v[:, :, N0], "elu1")
+    assert float(O.phi_elu1(np.float64(qt[0, 1, 0])) * zr[0, 1].sum()) < 1e-7
+    assert not np.isnan(y).any() and np.all(y[1, 2] == 0.0)
+    e = rel_err(y[..., None, :], yr[..., None, :])
+    e_tiny = rel_err(y[0, 1][None], yr[0, 1][None])
+    log(f"  rel err {e:.3e}, clamped head {e_tiny:.3e}")
+    assert e <= TOL[dt] and e_tiny <= TOL[dt]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_denominator_clamp_negative_identity(causal):
+    """Identity map, normalized: positive keys, and every fifth query row
+    negated, so those rows have a clearly negative denominator (clamped to
+    1e-6: y = num * 1e6) while the others stay clearly positive."""
+    B, H, N, d = 1, 2, 64 * 3 + 7, 32
+    log(f"case denominator clamp, negative identity-map denominators causal={causal}")
+    q, k, v = qkv(B, H, N, d, 503, "f32", 1.0)
+    q, k = np.abs(q) + 0.1, np.abs(k) + 0.1
+    neg = np.nonzero(np.arange(N) % 5 == 1)[0]
+    q[:, :, neg] = -q[:, :, neg]
+    y = to_host(la.la_forward(to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32"), feature_map="identity",
+                              causal=causal))
+    ref = O.attention(q, k, v, "identity", causal=causal)
+    num = O.attention(q, k, v, "identity", causal=causal, normalize=False)
+    np.testing.assert_allclose(ref[:, :, neg], num[:, :, neg] * 1e6, rtol=1e-12)
+    pos = np.setdiff1d(np.arange(N), neg)
+    e_neg = rel_err(y[:, :, neg], ref[:, :, neg])
+    e_pos = rel_err(y[:, :, pos], ref[:, :, pos])
+    log(f"  rel err clamped rows {e_neg:.3e}, other rows {e_pos:.3e}")
+    assert e_neg <= TOL["f32"] and e_pos <= TOL["f32"]
