@@ -24,7 +24,7 @@ __all__ = [
     "la_version", "la_status_string", "la_forward_workspace_size", "la_forward", "la_forward_ex",
     "la_decode_step", "la_feature_map_apply", "feature_dim", "la_forward_decay", "la_decode_step_decay",
     "la_backward_workspace_size", "la_backward", "la_backward_decay", "la_forward_gated_workspace_size", "la_forward_gated",
-    "la_decode_step_gated", "la_device_status",
+    "la_decode_step_gated", "la_device_status", "la_forward_static", "LA_STATIC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,6 +44,7 @@ LA_ELU1 = 0
 LA_PERFORMER = 1
 LA_IDENTITY = 2
 LA_POLY2 = 3
+LA_STATIC_SCRATCH_BYTES = 32 << 20   # the fixed device workspace of la_forward_static, per GPU
 
 
 class la_feature_map(ctypes.Structure):
@@ -66,6 +67,7 @@ def _load():
     fwd = [vp, vp, vp, vp, i, i, i, i, fmp, i, i, i, vp, vp, vp, vp, vp, sz, vp]
     L.la_forward.argtypes, L.la_forward.restype = fwd, i
     L.la_forward_ex.argtypes, L.la_forward_ex.restype = fwd + [vp], i
+    L.la_forward_static.argtypes, L.la_forward_static.restype = fwd[:16] + [vp], i
     L.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, fmp, i, i, vp]
     L.la_decode_step.restype = i
     L.la_forward_decay.argtypes = [vp, vp, vp, vp, i, i, i, i, fmp, vp, i, i, vp, vp, vp, vp, vp, sz, vp]
@@ -224,6 +226,32 @@ def la_forward(q, k, v, **kw):
     """Same as la_forward_ex without timing events."""
     kw.pop("events", None)
     return la_forward_ex(q, k, v, **kw)
+
+
+def la_forward_static(q, k, v, *, feature_map="elu1", W=None, causal=True, normalize=True, S_in=None, z_in=None,
+                      return_state=False, out=None, stream=None):
+    """la_forward with the library's fixed device workspace (no workspace
+    argument; the C call allocates nothing). Pass `out` (and call with
+    return_state=False) to allocate nothing here either."""
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    fm = _fmap(feature_map, W)
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    S_out = z_out = None
+    if return_state:
+        df = feature_dim(d, feature_map, W)
+        S_out = torch.empty((B, H, df, d), device=q.device, dtype=torch.float32)
+        z_out = torch.empty((B, H, df), device=q.device, dtype=torch.float32)
+    st = lib.la_forward_static(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d, ctypes.byref(fm), int(causal),
+                               int(normalize), dt, _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out),
+                               _stream(stream))
+    _check(st, "la_forward_static")
+    return (out, S_out, z_out) if return_state else out
 
 
 def la_decode_step(S, z, q, k, v, *, feature_map="elu1", W=None, normalize=True, out=None, stream=None):

@@ -16,11 +16,35 @@
 // own copy, at its own address.
 __device__ int la_status_flag;
 
+// Workspace of la_forward_static (callers that cannot allocate): the segment
+// states and every other scratch need of la_forward, up to
+// LA_STATIC_SCRATCH_BYTES. Each GPU the library runs on holds its own copy
+// from the first la_forward_static call on it until the process ends. In host
+// code this name is only a stand-in: kernels get the device address that
+// static_scratch_ptr() looked up.
+static __device__ __align__(256) unsigned char scratch[LA_STATIC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int kMaxDevices = 64;
 std::mutex g_dev_mu;
 int* g_flag_addr[kMaxDevices];
+void* g_scratch_addr[kMaxDevices];
+
+// Device address of `scratch` on the current device: looked up with
+// hipGetSymbolAddress on the first call on each device (that device
+// current), kept per device; null when the runtime refuses.
+void* static_scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_addr[dev] = p;
+  }
+  return g_scratch_addr[dev];
+}
 
 // Device address of la_status_flag on the current device (looked up once per
 // device with that device current), or null when the runtime refuses.
@@ -190,10 +214,12 @@ size_t la_forward_workspace_size(int B, int H, int N, int d, const la_feature_ma
 namespace {
 
 // The whole forward; gamma (device, [H]) is the per-head decay or null.
+// static_ws: the workspace is the library's `scratch` array (la_forward_static);
+// workspace / workspace_bytes are then ignored.
 int forward_impl(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
                  const la_feature_map* feature_map, int causal, int normalize, int dtype, const float* S_in,
                  const float* z_in, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
-                 hipStream_t stream, hipEvent_t* events, const float* gamma) {
+                 hipStream_t stream, hipEvent_t* events, const float* gamma, bool static_ws = false) {
   if (B < 0 || H < 0 || N < 0) return LA_ERR_INVALID_ARG;
   if (gamma && (causal != 1 || (reinterpret_cast<uintptr_t>(gamma) & 3u) != 0)) return LA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return LA_ERR_INVALID_ARG;
@@ -244,14 +270,19 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   if (feature_map->kind == LA_POLY2) {
     if (gamma) return LA_ERR_UNSUPPORTED;
     const size_t need = poly_ws_bytes(BH, N, d);
-    if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LA_ERR_INVALID_ARG;
-    const long long wsz = (long long)need;
-    if (overlaps(workspace, wsz, out, tok_bytes) || overlaps(workspace, wsz, q, tok_bytes) ||
-        overlaps(workspace, wsz, k, tok_bytes) || overlaps(workspace, wsz, v, tok_bytes) ||
-        overlaps(workspace, wsz, S_out, s_bytes) || overlaps(workspace, wsz, z_out, z_bytes) ||
-        overlaps(workspace, wsz, S_in, s_bytes) || overlaps(workspace, wsz, z_in, z_bytes))
-      return LA_ERR_INVALID_ARG;
+    if (static_ws) {
+      if (need > LA_STATIC_SCRATCH_BYTES) return LA_ERR_WORKSPACE;
+      if (!(workspace = static_scratch_ptr())) return LA_ERR_HIP;
+    } else {
+      if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
+      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LA_ERR_INVALID_ARG;
+      const long long wsz = (long long)need;
+      if (overlaps(workspace, wsz, out, tok_bytes) || overlaps(workspace, wsz, q, tok_bytes) ||
+          overlaps(workspace, wsz, k, tok_bytes) || overlaps(workspace, wsz, v, tok_bytes) ||
+          overlaps(workspace, wsz, S_out, s_bytes) || overlaps(workspace, wsz, z_out, z_bytes) ||
+          overlaps(workspace, wsz, S_in, s_bytes) || overlaps(workspace, wsz, z_in, z_bytes))
+        return LA_ERR_INVALID_ARG;
+    }
     if (events && hipEventRecord(events[0], stream) != hipSuccess) return LA_ERR_HIP;
     la::PolyArgs pa{};
     pa.q = q;
@@ -286,7 +317,9 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   // passes and the workspace holds segment states only
   const bool fused = mapped && la::perf_fused_supported(d, dfeat, dtype, causal != 0, gamma != nullptr);
   const Plan p = make_plan(BH, N, d, dfeat, causal != 0, mapped && !fused);
-  if (p.ws_bytes > 0) {
+  if (static_ws) {
+    if (p.ws_bytes > LA_STATIC_SCRATCH_BYTES) return LA_ERR_WORKSPACE;
+  } else if (p.ws_bytes > 0) {
     if (!workspace || workspace_bytes < p.ws_bytes) return LA_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LA_ERR_INVALID_ARG;
     if (overlaps(workspace, (long long)p.ws_bytes, out, tok_bytes) ||
@@ -304,6 +337,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
 
   int* flag = nullptr;  // looked up after validation: a rejected call makes no HIP call
   if (gamma && !(flag = status_flag_ptr())) return LA_ERR_HIP;
+  if (static_ws && p.ws_bytes > 0 && !(workspace = static_scratch_ptr())) return LA_ERR_HIP;
   if (events) {
     if (hipEventRecord(events[0], stream) != hipSuccess) return LA_ERR_HIP;
   }
@@ -421,6 +455,13 @@ int la_forward(const void* q, const void* k, const void* v, void* out, int B, in
                hipStream_t stream) {
   return la_forward_ex(q, k, v, out, B, H, N, d, feature_map, causal, normalize, dtype, S_in, z_in, S_out, z_out,
                        workspace, workspace_bytes, stream, nullptr);
+}
+
+int la_forward_static(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+                      const la_feature_map* feature_map, int causal, int normalize, int dtype, const float* S_in,
+                      const float* z_in, float* S_out, float* z_out, hipStream_t stream) {
+  return forward_impl(q, k, v, out, B, H, N, d, feature_map, causal, normalize, dtype, S_in, z_in, S_out, z_out,
+                      nullptr, 0, stream, nullptr, nullptr, true);
 }
 
 }  // extern "C"

@@ -135,6 +135,28 @@ int la_forward(const void* q, const void* k, const void* v, void* out, int B, in
                hipStream_t stream);
 
 /*
+ * la_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and kernels, with no workspace argument. Its workspace is
+ * a fixed device array of the library, LA_STATIC_SCRATCH_BYTES per GPU,
+ * reserved on each GPU by the first call there and held until the process
+ * ends. The call itself allocates nothing.
+ *   Arguments and results as la_forward.
+ *   Returns LA_ERR_WORKSPACE when la_forward_workspace_size() for the request
+ *   (for random features with bf16 input, d = 64 and causal = 1: the segment
+ *   states alone) exceeds LA_STATIC_SCRATCH_BYTES, LA_ERR_HIP when the array's
+ *   address cannot be looked up.
+ *   Every call on one GPU uses the same array and leaves its contents behind:
+ *   calls that overlap in time on one GPU (concurrent streams, threads) race
+ *   on it and must be serialized by the caller. Nothing in the array needs to
+ *   start at zero.
+ */
+#define LA_STATIC_SCRATCH_BYTES (32u << 20)
+int la_forward_static(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+                      const la_feature_map* feature_map, int causal, int normalize, int dtype, const float* S_in,
+                      const float* z_in, float* S_out, float* z_out, hipStream_t stream);
+
+/*
  * la_forward, plus timing markers: when `events` is not NULL it points to 4
  * caller-created HIP events that are recorded on `stream` before the first
  * kernel (the random-feature map, when used, else the state pass), before the

@@ -313,3 +313,21 @@ def test_decode_decay_rejects_gamma_overlaps():
     assert dec(FAKE + 256) == la.LA_ERR_INVALID_ARG          # gamma inside S
     assert dec(FAKE + 0x1000000) == la.LA_ERR_INVALID_ARG    # gamma inside z
     assert dec(None) == la.LA_ERR_INVALID_ARG
+
+
+def test_forward_static_validates_and_rejects_beyond_its_array():
+    """la_forward_static validates like la_forward (before any HIP call) and
+    refuses a request whose workspace would exceed its fixed array."""
+    def st(q=FAKE, out=FAKE2, B=1, H=16, N=65536, d=64, fm=ELU, causal=1, dtype=la.LA_BF16):
+        return lib.la_forward_static(q, FAKE + 0x10000000, FAKE + 0x20000000, out, B, H, N, d, ctypes.byref(fm),
+                                     causal, 1, dtype, None, None, None, None, None)
+    assert st(B=-1) == la.LA_ERR_INVALID_ARG
+    assert st(out=FAKE + 64) == la.LA_ERR_INVALID_ARG      # out overlaps q
+    assert st(d=96) == la.LA_ERR_UNSUPPORTED
+    # random features through the two-stage path: phi(q), phi(k) would take 2 x 16 x 65536 x 256 x 4 bytes
+    W = FAKE2 * 8
+    perf = la_feature_map(la.LA_PERFORMER, 256, W)
+    assert lib.la_forward_workspace_size(1, 16, 65536, 64, ctypes.byref(perf), 1) > la.LA_STATIC_SCRATCH_BYTES
+    assert st(fm=perf, dtype=la.LA_F32) == la.LA_ERR_WORKSPACE
+    # the long-context workload fits (16 heads x 16 segments x 66 KB)
+    assert lib.la_forward_workspace_size(1, 16, 65536, 128, ctypes.byref(ELU), 1) <= la.LA_STATIC_SCRATCH_BYTES
