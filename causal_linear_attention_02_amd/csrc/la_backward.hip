@@ -744,11 +744,16 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
         const bool live = row < valid;
         u32x4* pq = reinterpret_cast<u32x4*>(sQ + o);
         u32x4* pk = reinterpret_cast<u32x4*>(sK + o);
-        const u32x4 fq = phi_bf16x8<FM, true>(*pq, live, DECAY ? dc.pw(row - 32) : 1.f);
-        *pq = fq;
-        *pk = phi_bf16x8<FM, true>(*pk, live, DECAY ? dc.pw(32 - row) : 1.f);
+        // phi(q) in fp32 once: the tile gets it rounded to bf16, Qs = phi(q) / D_i
+        // is rounded once from the fp32 value (not from the rounded phi)
         float x[8];
-        In8<__bf16>::to_f32(fq, x);
+        In8<__bf16>::to_f32(*pq, x);
+        const float sq = DECAY ? dc.pw(row - 32) : 1.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = live ? bphi<FM>(x[e]) * sq : 0.f;
+        *pq = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                    pack_bf16x2(x[6], x[7])};
+        *pk = phi_bf16x8<FM, true>(*pk, live, DECAY ? dc.pw(32 - row) : 1.f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] *= rs[i][0];
         *reinterpret_cast<u32x4*>(sQs + o) = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
@@ -874,18 +879,46 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
             Bt[4 * g + e] = keep ? Bt[4 * g + e] * iq[e] + hq[e] : 0.f;
           }
         }
+        // B enters as hi + lo fragments with bf16 operands: sum_i phi(q_i) B[i][j]
+        // is a sum of terms of both signs that can cancel far below its terms
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-          Ops<OP>::mma(kbk ? K1 : K0, Ops<OP>::template load_cols<RB>(sQ, 32 * qb + 16 * kk, 32 * w),
-                       Ops<OP>::from_acc(Bt, kk));
+        for (int kk = 0; kk < 2; ++kk) {
+          const Frag qf = Ops<OP>::template load_cols<RB>(sQ, 32 * qb + 16 * kk, 32 * w);
+          if constexpr (sizeof(OP) == 2) {
+            bf16x8 bh, bl;
+            frag_hilo(Bt, kk, bh, bl);
+            Ops<OP>::mma(kbk ? K1 : K0, qf, bh);
+            Ops<OP>::mma(kbk ? K1 : K0, qf, bl);
+          } else {
+            Ops<OP>::mma(kbk ? K1 : K0, qf, Ops<OP>::from_acc(Bt, kk));
+          }
+        }
       }
+      // R^T v_j: with bf16 operands R enters as hi + lo fragments. The
+      // product is a dot product over value dims of both signs and can be far
+      // smaller than its terms. With R and B rounded to bf16, rows of dk on the
+      // long-context workload were off by up to ~3%; a CPU emulation of the
+      // pass's rounding puts the worst row at ~0.8% of its 64-token block's
+      // RMS row norm with both as hi + lo (Qs stays bf16: no room in LDS for
+      // a lo tile at d = 128).
 #pragma unroll
       for (int eb = 0; eb < NW; ++eb)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const Frag rf = Ops<OP>::from_acc(RS[eb], kk);
-          Ops<OP>::mma(K0, rf, Ops<OP>::template load_rows<RB>(sV, 0, 32 * eb + 16 * kk));
-          Ops<OP>::mma(K1, rf, Ops<OP>::template load_rows<RB>(sV, 32, 32 * eb + 16 * kk));
+          const Frag v0 = Ops<OP>::template load_rows<RB>(sV, 0, 32 * eb + 16 * kk);
+          const Frag v1 = Ops<OP>::template load_rows<RB>(sV, 32, 32 * eb + 16 * kk);
+          if constexpr (sizeof(OP) == 2) {
+            bf16x8 rh, rl;
+            frag_hilo(RS[eb], kk, rh, rl);
+            Ops<OP>::mma(K0, rh, v0);
+            Ops<OP>::mma(K0, rl, v0);
+            Ops<OP>::mma(K1, rh, v1);
+            Ops<OP>::mma(K1, rl, v1);
+          } else {
+            const Frag rf = Ops<OP>::from_acc(RS[eb], kk);
+            Ops<OP>::mma(K0, rf, v0);
+            Ops<OP>::mma(K1, rf, v1);
+          }
         }
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {

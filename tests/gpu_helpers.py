@@ -72,6 +72,22 @@ def err_parts(y, ref, floor=ROW_FLOOR):
     return float(np.max(frob)), float(np.max(row)), (int(w[0]), int(w[1]), ratio)
 
 
+def err_parts_local(y, ref, block=64, frac=0.5):
+    """Per-row error with a local floor: row i is measured against
+    max(||ref_i||, frac * RMS row norm of its block of `block` rows). Returns
+    (per_row, (slab, row, row norm / block RMS))."""
+    Y, R = _slabs(y, ref)
+    rn = np.linalg.norm(R, axis=2)
+    n = rn.shape[1]
+    pad = (-n) % block
+    rp = np.concatenate([rn, np.full((rn.shape[0], pad), np.nan)], axis=1).reshape(rn.shape[0], -1, block)
+    brms = np.sqrt(np.nanmean(rp * rp, axis=2))
+    floor = np.repeat(brms, block, axis=1)[:, :n]
+    row = np.linalg.norm(Y - R, axis=2) / np.maximum(np.maximum(rn, frac * floor), 1e-30)
+    w = np.unravel_index(int(np.nanargmax(row)) if np.isfinite(row).any() else 0, row.shape)
+    return float(np.max(row)), (int(w[0]), int(w[1]), float(rn[w] / floor[w]) if floor[w] > 0 else 0.0)
+
+
 def note_row(row, at, where):
     """Record a per-row error for the end-of-session report."""
     detail = f"slab {at[0]} row {at[1]} (row norm {at[2]:.2g} x RMS)"
@@ -91,6 +107,27 @@ def rel_err(y, ref, floor=ROW_FLOOR, where=""):
     frob, row, at = err_parts(y, ref, floor)
     note_row(row, at, where or caller(1))
     return float(np.max([frob, row]))
+
+
+def rel_err_terms(y, ref, terms, frac=0.25, where=""):
+    """Larger of the per-slab Frobenius error and a componentwise per-row
+    error: row i is measured against max(||ref_i||, frac * ||terms_i||),
+    where terms holds the same sums taken over the absolute values of their
+    terms. For signed sums whose rows can cancel far below their terms (the
+    identity map without normalization), this is the scale the rounding
+    errors follow; a row that cancels by less than 1/frac is measured against
+    itself."""
+    Y, R = _slabs(y, ref)
+    T = np.asarray(terms, dtype=np.float64).reshape(Y.shape)
+    frob = np.max(np.linalg.norm((Y - R).reshape(Y.shape[0], -1), axis=1) /
+                  np.maximum(np.linalg.norm(R.reshape(R.shape[0], -1), axis=1), 1e-30))
+    rn = np.linalg.norm(R, axis=2)
+    row = np.linalg.norm(Y - R, axis=2) / np.maximum(np.maximum(rn, frac * np.linalg.norm(T, axis=2)), 1e-30)
+    w = np.unravel_index(int(np.nanargmax(row)) if np.isfinite(row).any() else 0, row.shape)
+    rms = np.sqrt(np.mean(rn[w[0]] ** 2))
+    note_row(float(np.max(row)), (int(w[0]), int(w[1]), float(rn[w] / rms) if rms > 0 else 0.0),
+             where or caller(1))
+    return float(np.max([frob, np.max(row)]))
 
 
 def caller(depth=1):

@@ -9,18 +9,19 @@ precisions). Where the exact gradient vanishes (dq and dk of a one-token
 normalized sequence: the output is v_0 whatever q and k are) the error is
 measured against 1e-3 of the output cotangent's norm instead.
 
-Beside that norm, every row is checked on its own (gpu_helpers.err_parts:
-its error over its reference norm), so that one wrong row cannot hide in the
-norm of a long sequence. Gradient rows are sums of terms of both signs
-(dk_j = phi'(k_j) sum_{i>=j} phi(q_i) g_i.(v_j - y_i), and alike), so a row
-can cancel to far below its terms while its rounding error follows the
-terms: measured on the long-context workload, the worst dk row had 7e-2
-relative error with the row norm floored at 1e-3 of the RMS row norm, against
-3.5e-3 for the head as a whole. Rows are therefore measured against at least
-half the slab's RMS row norm (gpu_helpers.SIGNED_ROW_FLOOR). Rows whose exact
-gradient vanishes are left to the norm check: in the normalized form the
-first output is v_0 whatever q_0 is, so row 0 of dq is exactly zero and the
-GPU returns rounding noise there.
+Beside that norm, every row is checked on its own (its error over its
+reference norm), so that one wrong row cannot hide in the norm of a long
+sequence. Gradient rows are sums of terms of both signs (dk_j = phi'(k_j)
+sum_{i>=j} phi(q_i) g_i.(v_j - y_i), and alike), so a row can cancel far below
+its terms while its rounding error follows the terms, and the size of the
+terms falls by orders of magnitude along a sequence (g_i = dy_i / D_i with D_i
+growing with i): on the long-context workload a dk row with 6 times the
+head's RMS row norm sat among neighbours of 40-70 times it. Each row is
+therefore measured against at least half the RMS row norm of its 64-token
+block (gpu_helpers.err_parts_local). Rows whose exact gradient vanishes are
+left to the norm check: in the normalized form the first output is v_0
+whatever q_0 is, so row 0 of dq is exactly zero and the GPU returns rounding
+noise there.
 """
 
 import numpy as np
@@ -36,8 +37,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU containers
     pytest.skip("no GPU", allow_module_level=True)
 
 import causal_linear_attention_02_amd as la  # noqa: E402
-from gpu_helpers import (SIGNED_ROW_FLOOR, TOL, caller, err_parts, log, note_row, qkv, to_dev,  # noqa: E402
-                         to_host)
+from gpu_helpers import TOL, caller, err_parts_local, log, note_row, qkv, to_dev, to_host  # noqa: E402
 
 
 def _dout(B, H, N, d, seed, dt):
@@ -48,8 +48,8 @@ def _dout(B, H, N, d, seed, dt):
 def _err(g, r, dy, vanishing=False, skip_row0=False):
     """Larger of: max over (batch, head) of ||g - r||_F / ||r||_F (or
     / (1e-3 ||dy||_F) for a gradient that vanishes exactly), and the per-row
-    error of err_parts (not taken for a vanishing gradient; without row 0
-    when skip_row0)."""
+    error of err_parts_local (not taken for a vanishing gradient; without
+    row 0 when skip_row0)."""
     G = g.reshape(-1, g.shape[-2] * g.shape[-1])
     R = r.reshape(G.shape)
     Y = dy.reshape(G.shape[0], -1)
@@ -63,9 +63,11 @@ def _err(g, r, dy, vanishing=False, skip_row0=False):
     if skip_row0:
         if g3.shape[1] == 1:
             return frob
-        g3, r3 = g3[:, 1:], r3[:, 1:]
-    _, row, at = err_parts(g3, r3, SIGNED_ROW_FLOOR)
-    note_row(row, (at[0], at[1] + (1 if skip_row0 else 0), at[2]), caller(1))
+        # row 0 keeps its place in its block's scale but is not checked
+        # itself: the GPU's value there is replaced by the reference
+        g3 = np.concatenate([r3[:, :1], g3[:, 1:]], axis=1)
+    row, at = err_parts_local(g3, r3)
+    note_row(row, at, caller(1))
     return float(np.max([frob, row]))
 
 
@@ -211,9 +213,16 @@ def test_backward_decay_one_equals_no_decay():
     a = la.la_backward(*args)
     b = la.la_backward_decay(*args, torch.ones(2, device="cuda"))
     torch.cuda.synchronize()
+    # the same arithmetic up to the order of the fp32 accumulations (the
+    # decay passes scale and walk their states differently), which the
+    # gradients see in full where they carry fp32 states as hi + lo operands:
+    # 1e-4 on the norm of each head, 5e-3 on every row
     for i, (x, y) in enumerate(zip(a, b)):
-        err = _err(to_host(y), to_host(x), dy, skip_row0=(i == 0))
-        assert err <= 1e-5, err
+        gx, gy = to_host(x), to_host(y)
+        frob = float(np.max(np.linalg.norm((gy - gx).reshape(2, -1), axis=1) /
+                            np.linalg.norm(gx.reshape(2, -1), axis=1)))
+        err = _err(gy, gx, dy, skip_row0=(i == 0))
+        assert frob <= 1e-4 and err <= 5e-3, (i, frob, err)
 
 
 def test_backward_decay_empty_sequence_passes_state_gradient():

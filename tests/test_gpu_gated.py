@@ -20,7 +20,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU containers
     pytest.skip("no GPU", allow_module_level=True)
 
 import causal_linear_attention_02_amd as la  # noqa: E402
-from gpu_helpers import ROW_FLOOR, SIGNED_ROW_FLOOR, TOL, log, qkv, rel_err, to_dev, to_host  # noqa: E402
+from gpu_helpers import TOL, log, qkv, rel_err, rel_err_terms, to_dev, to_host  # noqa: E402
 
 
 def _g(shape, seed, lo):
@@ -45,9 +45,18 @@ def _check(B, H, N, d, dt, seed, lo=0.25, fmap="elu1", normalize=True, state=Fal
     torch.cuda.synchronize()
     y = res[0] if state else res
     yr, Sr, zr = O.gated_chunked(q, k, v, lg, fmap, normalize=normalize, chunk=64, **okw)
-    # the identity map without normalization sums terms of both signs (rows may cancel)
-    floor = SIGNED_ROW_FLOOR if (fmap == "identity" and not normalize) else ROW_FLOOR
-    err = rel_err(to_host(y), yr, floor)
+    if fmap == "identity" and not normalize:
+        # signed sums over few tokens (the gates decay fast): a row can cancel
+        # far below its terms, so rows are measured componentwise, against the
+        # same sums over absolute values (a CPU emulation of the kernel's bf16
+        # rounding reproduces its worst row, 2.6e-2 against the row norm,
+        # 1.8e-3 against those sums)
+        aS0 = None if not state else np.abs(okw["S0"])
+        terms = O.gated_chunked(np.abs(q), np.abs(k), np.abs(v), lg, "identity", normalize=False, chunk=64,
+                                S0=aS0, z0=None if not state else okw["z0"])[0]
+        err = rel_err_terms(to_host(y), yr, terms)
+    else:
+        err = rel_err(to_host(y), yr)
     log(f"  rel err {err:.3e}")
     assert err <= TOL[dt], err
     if state:
