@@ -234,45 +234,60 @@ __global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
   const long long base = (long long)bh * a.N;
   const __bf16* k = static_cast<const __bf16*>(a.k);
   const __bf16* v = static_cast<const __bf16*>(a.v);
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, li = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63, li = l & 31;
   const int rb = w & 1, sl = w >> 1;  // rows [32 rb, +32); feature slice [sl FS, +FS)
   const int cb = w & 1;               // S columns [32 cb, +32)
   const float bm = 0.5f * __log2f((float)DF);
 
-  u32x4 xr[4], vr[512 / NTH];
-  auto rsrc = [&](const __bf16* p, int c) {
-    return make_rsrc(p + (base + 64LL * c) * kPD, (unsigned)(min(64, a.N - 64 * c) * kPD * 2));
+  // chunk m of the segment (zero-size descriptors past it)
+  auto rsrc = [&](const __bf16* p, int m) {
+    const int c = c0 + m;
+    const int valid = m < n ? min(64, a.N - 64 * c) : 0;
+    return make_rsrc(p + (base + 64LL * min(c, a.nchunks - 1)) * kPD, (unsigned)(valid * kPD * 2));
   };
-  if (n > 0) {
-    pf_load_x(xr, rsrc(k, c0), 32 * rb);
-    pf_load_v<NTH>(vr, rsrc(v, c0));
-  }
+  struct KSet {
+    u32x4 x[4], v[512 / NTH];
+  };
+  auto load = [&](int m, KSet& s_) {
+    pf_load_x(s_.x, rsrc(k, m), 32 * rb);
+    pf_load_v<NTH>(s_.v, rsrc(v, m));
+  };
   pf_stage_W<DF, NTH>(a.W, sW);
   f32x16 st[Q::NTS];
 #pragma unroll
   for (int t = 0; t < Q::NTS; ++t) st[t] = f32x16{};
   float cs[4] = {0.f, 0.f, 0.f, 0.f};
-  __syncthreads();
-
-  for (int it = 0; it < n; ++it) {
-    const int c = c0 + it;
-    const int valid = min(64, a.N - 64 * c);
-    const float b = pf_row_bias(xr, bm);
-    const bool past = 32 * rb + li >= valid;
+  // Iteration m maps chunk m (registers of cur) into LDS with the loads of
+  // chunk m + 1 already in flight in nxt, then adds it into S. Every
+  // iteration issues the same loads (zero size past the segment), and the
+  // iteration count is even, so that both register sets rotate whole.
+  auto iter = [&](int m, KSet& cur, KSet& nxt) {
+    load(m + 1, nxt);
+    if (m < n) {
+      const int valid = min(64, a.N - 64 * (c0 + m));
+      const float b = pf_row_bias(cur.x, bm);
+      const bool past = 32 * rb + li >= valid;
 #pragma unroll
-    for (int j = 0; j < Q::NTS; ++j) {
-      const int fb = sl * Q::NTS + j;
-      pf_phi_store<DF>(pf_project<DF>(sW, xr, fb), b, past, sK, 32 * rb + li, fb);
-    }
-    pf_store_v<NTH>(vr, sV);
-    if (it + 1 < n) {
-      pf_load_x(xr, rsrc(k, c + 1), 32 * rb);
-      pf_load_v<NTH>(vr, rsrc(v, c + 1));
+      for (int j = 0; j < Q::NTS; ++j) {
+        const int fb = sl * Q::NTS + j;
+        pf_phi_store<DF>(pf_project<DF>(sW, cur.x, fb), b, past, sK, 32 * rb + li, fb);
+      }
+      pf_store_v<NTH>(cur.v, sV);
     }
     __syncthreads();
-    pf_update_S<DF, Q::NTS>(st, sK, sV, sl * Q::FS, cb);
-    pf_colsum<DF, NTH>(sK, cs);
+    if (m < n) {
+      pf_update_S<DF, Q::NTS>(st, sK, sV, sl * Q::FS, cb);
+      pf_colsum<DF, NTH>(sK, cs);
+    }
     __syncthreads();
+  };
+  KSet sa, sb;
+  load(0, sa);
+  __syncthreads();  // W staged
+  for (int m = 0; m < n; m += 2) {
+    iter(m, sa, sb);
+    iter(m + 1, sb, sa);
   }
 
   float* out = a.ws + ((long long)bh * a.ws_slots + seg) * a.state_elems;
@@ -291,288 +306,327 @@ __global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Output pass: grid (BH, segments), 512 threads (two waves per SIMD). Per
-// chunk, two barriers:
-//   1. all waves map the chunk: waves 0-3 q, waves 4-7 k; wave w takes rows
-//      [32 (w & 1), +32) and features [((w >> 1) & 1) m/2, +m/2); every
-//      thread stages one piece of v. After the barrier all threads store the
-//      previous chunk's output tile as whole rows.
-//   2. state waves 0-3 (fh, cb): read-out of both row blocks over their
-//      feature half (the other row block handed to wave w ^ 2), S update;
-//      score waves 4-7 (r, cb): masked scores of row block r, their product
-//      with v[:, 32 cb, +32), the in-chunk denominator and phi(q_i) . z over
-//      half of the features; all threads: column sums of phi(K)
-//   3. after the second barrier, state wave (fh, cb) adds the hand-overs,
-//      normalizes and writes rows [32 fh, +32) x columns [32 cb, +32) into the
-//      LDS output tile, and z moves on; then it maps the next chunk, while the
-//      score waves may already be mapping theirs (nothing of steps 1-2 is read
-//      in step 3).
+// Output pass: grid (BH, segments), 512 threads, two waves per SIMD with
+// different roles, on 32-row sub-chunks of the segment; one barrier per step.
+// In step t:
+//   map waves (4..7) store the output tile of sub-chunk t - 3, map sub-chunk t
+//     (phi(Q), phi(K), v) into LDS buffer t & 1 with W held in registers, and
+//     load the raw rows of sub-chunk t + 2;
+//   contraction waves (0..3) finish sub-chunk t - 2 and start sub-chunk t - 1.
+//     Each owns a range of features: the S tiles (and the z column) of those
+//     features and their share of every product over features, so that the
+//     read-out phi(Q) S, the scores phi(Q) phi(K)^T, their product with v and
+//     the denominators come out as partial sums over the feature ranges,
+//     left in LDS (double-buffered). One step later the waves of value-column
+//     block cb add the partials, normalize and write the output tile. z rides
+//     along as a column of ones in the S update.
 // ---------------------------------------------------------------------------
 template <int DF>
-struct PoL {
-  using L = PfL<DF>;
-  static constexpr int NSL = 512 / L::NG;                 // column-sum row slices
-  static constexpr int W_OFF = 0;
-  static constexpr int Q_OFF = W_OFF + DF * L::RBV;
-  static constexpr int K_OFF = Q_OFF + 64 * L::RBF;
-  static constexpr int V_OFF = K_OFF + 64 * L::RBF;
-  static constexpr int R_OFF = V_OFF + 64 * L::RBV;       // read-out hand-over [4 waves][4][64 lanes] f32x4
-  static constexpr int A_OFF = R_OFF + 4 * 64 * 16 * 4;   // score-wave products with v, same layout
-  static constexpr int ZP_OFF = A_OFF + 4 * 64 * 16 * 4;  // column-sum partials [NSL][DF]
-  static constexpr int Z_OFF = ZP_OFF + NSL * DF * 4;     // running z [2][DF]
-  static constexpr int DEN_OFF = Z_OFF + 2 * DF * 4;      // phi(q_i) . z per feature half [2][64]
-  static constexpr int DP_OFF = DEN_OFF + 2 * 64 * 4;     // in-chunk denominators [64]
-  static constexpr int Y_OFF = DP_OFF + 64 * 4;           // output tile [64][64] bf16
-  static constexpr int BYTES = Y_OFF + 64 * L::RBV;
+struct Po2 {
+  static constexpr int NFB = DF / 32;                    // 32-feature blocks
+  static constexpr int FBJ = NFB >= 4 ? NFB / 4 : 1;     // feature blocks mapped per map wave
+  static constexpr int NMAP = NFB / FBJ;                 // map waves with feature blocks (2 or 4)
+  static constexpr int NFBW = NFB >= 4 ? NFB / 4 : 1;    // feature blocks per contraction wave
+  static constexpr int NCB = NFB >= 4 ? 2 : 1;           // value-column blocks per contraction wave
+  static constexpr int RBF = DF * 2;                     // phi tile rows (bf16)
+  static constexpr int RBV = kPD * 2;                    // v and output rows (bf16)
+  static constexpr int PHI = 32 * RBF;
+  static constexpr int VT = 32 * RBV;
+  static constexpr int Q_OFF = 0;                        // phi(Q) [2]
+  static constexpr int K_OFF = Q_OFF + 2 * PHI;          // phi(K) [2]
+  static constexpr int V_OFF = K_OFF + 2 * PHI;          // v [2]
+  static constexpr int Y_OFF = V_OFF + 2 * VT;           // output tiles [2]
+  static constexpr int PB = 4 * NCB * 16 * 64 * 4;       // partial numerators [4][NCB][16 regs][64 lanes] fp32
+  static constexpr int P_OFF = Y_OFF + 2 * VT;           // [2] buffers
+  static constexpr int DBUF = 4 * 32 * 4;                // partial denominators [4][32]
+  static constexpr int D_OFF = P_OFF + 2 * PB;           // [2]
+  static constexpr int BYTES = D_OFF + 2 * DBUF;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-__device__ __forceinline__ void pf_put16(float* base, int slot, const f32x16& x) {
-  const int l = threadIdx.x & 63;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    *reinterpret_cast<f32x4*>(base + ((slot * 4 + j) * 64 + l) * 4) = f32x4{x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]};
-}
-__device__ __forceinline__ void pf_add16(const float* base, int slot, f32x16& x) {
-  const int l = threadIdx.x & 63;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const f32x4 o = *reinterpret_cast<const f32x4*>(base + ((slot * 4 + j) * 64 + l) * 4);
-    x[4 * j] += o[0];
-    x[4 * j + 1] += o[1];
-    x[4 * j + 2] += o[2];
-    x[4 * j + 3] += o[3];
+// contraction wave c: feature blocks [fb0, fb0 + NFBW), value blocks [cb0, cb0 + NCB);
+// den owner: the wave adds its in-chunk and carried denominators (once per feature range)
+template <int DF>
+struct Cown {
+  int fb0, cb0;
+  bool den;
+  __device__ explicit Cown(int c) {
+    using P = Po2<DF>;
+    if constexpr (P::NFB >= 4) {
+      fb0 = c * P::NFBW;
+      cb0 = 0;
+      den = true;
+    } else {  // m = 64: two feature blocks, two value blocks, one tile per wave
+      fb0 = c & 1;
+      cb0 = c >> 1;
+      den = cb0 == 0;
+    }
   }
-}
+};
 
 template <int DF>
 __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
-  using L = PfL<DF>;
-  using O = PoL<DF>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[O::BYTES];
-  uint8_t* sW = smem + O::W_OFF;
-  uint8_t* sQ = smem + O::Q_OFF;
-  uint8_t* sK = smem + O::K_OFF;
-  uint8_t* sV = smem + O::V_OFF;
-  float* sR = reinterpret_cast<float*>(smem + O::R_OFF);
-  float* sA = reinterpret_cast<float*>(smem + O::A_OFF);
-  float* zp = reinterpret_cast<float*>(smem + O::ZP_OFF);
-  float* sZ = reinterpret_cast<float*>(smem + O::Z_OFF);
-  float* sDen = reinterpret_cast<float*>(smem + O::DEN_OFF);
-  float* sDp = reinterpret_cast<float*>(smem + O::DP_OFF);
-  uint8_t* sY = smem + O::Y_OFF;
+  using P = Po2<DF>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[P::BYTES];
 
   const int bh = blockIdx.x, seg = blockIdx.y;
   const int c0 = seg * a.chunks_per_seg;
-  const int n = max(0, min(c0 + a.chunks_per_seg, a.nchunks) - c0);
-  const long long base = (long long)bh * a.N;
+  const int n64 = max(0, min(c0 + a.chunks_per_seg, a.nchunks) - c0);
+  const int r0 = 64 * c0;                                         // first token of the segment
+  const int nrows = max(0, min(64 * (c0 + n64), a.N) - r0);       // its tokens
+  const int ns = (nrows + 31) / 32;                               // 32-row sub-chunks
+  const long long base = (long long)bh * a.N + r0;
   const __bf16* q = static_cast<const __bf16*>(a.q);
   const __bf16* k = static_cast<const __bf16*>(a.k);
   const __bf16* v = static_cast<const __bf16*>(a.v);
   __bf16* out = static_cast<__bf16*>(a.out);
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, li = l & 31;
-  // mapping roles
-  const bool qwave = w < 4;
-  const int rb = w & 1, ph = (w >> 1) & 1;
-  // chunk roles: state waves (fh, cb), score waves (r, cb)
-  const bool swave = w < 4;
-  const int fh = (w >> 1) & 1, cb = w & 1;
-  const float bm = 0.5f * __log2f((float)DF);
+  // the wave index in a scalar register: role branches and the buffer
+  // descriptors built under them stay uniform (no per-lane loops around loads)
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63, h = l >> 5, li = l & 31;
 
   const float* Sinit;
   const float* zinit;
   if (a.init_from_ws) {
-    const float* s = a.ws + ((long long)bh * a.ws_slots + seg) * a.state_elems;
-    Sinit = s;
-    zinit = s + DF * kPD;
+    const float* st = a.ws + ((long long)bh * a.ws_slots + seg) * a.state_elems;
+    Sinit = st;
+    zinit = st + DF * kPD;
   } else {
     Sinit = a.S_in ? a.S_in + (long long)bh * DF * kPD : nullptr;
     zinit = a.z_in ? a.z_in + (long long)bh * DF : nullptr;
   }
-
-  u32x4 xr[4], vr[1];
-  auto rsrc = [&](const __bf16* p, int c) {
-    return make_rsrc(p + (base + 64LL * c) * kPD, (unsigned)(min(64, a.N - 64 * c) * kPD * 2));
+  // rows [32 t, 32 t + 32) of the segment: descriptor over the valid ones
+  // (none for t < 0 or past the end)
+  auto rsrc = [&](const __bf16* p, int t) {
+    const int valid = t < 0 ? 0 : max(0, min(32, nrows - 32 * t));
+    return make_rsrc(p + (base + 32LL * max(t, 0)) * kPD, (unsigned)(valid * kPD * 2));
   };
-  if (n > 0) {
-    pf_load_x(xr, rsrc(qwave ? q : k, c0), 32 * rb);
-    pf_load_v<512>(vr, rsrc(v, c0));
-  }
-  pf_stage_W<DF, 512>(a.W, sW);
-  if (threadIdx.x < DF) {
-    float z0 = zinit ? zinit[threadIdx.x] : 0.f;
-    if (a.init_sum_ws)  // local sums of the segments before this one
-      for (int j = 0; j < seg; ++j) z0 += a.ws[((long long)bh * a.ws_slots + j) * a.state_elems + DF * kPD + threadIdx.x];
-    sZ[threadIdx.x] = z0;
-  }
+  // steps -2 .. tend - 1: a whole number of three-step rotations covering
+  // steps 0 .. ns + 2 (the output tile of the last sub-chunk is stored in step ns + 2)
+  const int tend = -2 + (ns + 5 + 2) / 3 * 3;
 
-  // 1. feature map of chunk it (all waves), then the loads of chunk it + 1
-  auto map_chunk = [&](int it) {
-    const int c = c0 + it;
-    const int valid = min(64, a.N - 64 * c);
-    const float b = pf_row_bias(xr, bm);
-    const int row = 32 * rb + li;
-    if (qwave) {
-#pragma unroll 1
-      for (int j = 0; j < L::NFB / 2; ++j) {
-        const int fb = ph * (L::NFB / 2) + j;
-        pf_phi_store<DF>(pf_project<DF>(sW, xr, fb), b, false, sQ, row, fb);
+  if (w >= 4) {
+    // ------------------------------------------------------------ map waves
+    const int j = w - 4, p = threadIdx.x - 256;
+    const bool act = P::NMAP == 4 || j < P::NMAP;
+    const int fbm = (act ? j : 0) * P::FBJ;
+    const float bm = 0.5f * __log2f((float)DF);
+    // W rows of the wave's feature blocks as MFMA A operands, bf16
+    bf16x8 Wf[P::FBJ][4];
+#pragma unroll
+    for (int f = 0; f < P::FBJ; ++f)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const float* src = a.W + (32 * (fbm + f) + li) * kPD + 16 * kb + 8 * h;
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+        const u32x4 pk = {pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]), pack_bf16x2(x1[0], x1[1]),
+                          pack_bf16x2(x1[2], x1[3])};
+        Wf[f][kb] = __builtin_bit_cast(bf16x8, pk);
       }
-    } else {
-      const bool past = row >= valid;
-#pragma unroll 1
-      for (int j = 0; j < L::NFB / 2; ++j) {
-        const int fb = ph * (L::NFB / 2) + j;
-        pf_phi_store<DF>(pf_project<DF>(sW, xr, fb), b, past, sK, row, fb);
+    struct XSet {
+      u32x4 q[4], k[4], v;
+    };
+    auto load = [&](int t, XSet& x) {
+      if (act) {
+        pf_load_x(x.q, rsrc(q, t), 0);
+        pf_load_x(x.k, rsrc(k, t), 0);
       }
-    }
-    pf_store_v<512>(vr, sV);
-    if (it + 1 < n) {
-      pf_load_x(xr, rsrc(qwave ? q : k, c + 1), 32 * rb);
-      pf_load_v<512>(vr, rsrc(v, c + 1));
-    }
-  };
-  // the output tile of chunk it (staged in sY) as whole rows, one 16-byte
-  // piece per thread; rows past the end are dropped by the range check
-  auto flush_y = [&](int it) {
-    const int c = c0 + it;
-    const auto ro = make_rsrc(out + (base + 64LL * c) * kPD, (unsigned)(min(64, a.N - 64 * c) * kPD * 2));
-    const int p = threadIdx.x;
-    buf_store16_nt(ro, (p >> 3) * kPD * 2 + 16 * (p & 7),
-                   *reinterpret_cast<const u32x4*>(sY + tile_off<kPD * 2>(p >> 3, 16 * (p & 7))));
-  };
-  // column sums of the chunk's phi(K), partials over row slices
-  auto colsum = [&]() {
-    float cs[4] = {0.f, 0.f, 0.f, 0.f};
-    pf_colsum<DF, 512>(sK, cs);
-    const int grp = threadIdx.x % L::NG, sl = threadIdx.x / L::NG;
-    *reinterpret_cast<f32x4*>(zp + sl * DF + 4 * grp) = f32x4{cs[0], cs[1], cs[2], cs[3]};
-  };
-
-  // The two roles run separate loops with the same three barriers per chunk,
-  // so that the state tiles take registers in the state waves only.
-  if (swave) {
-    f32x16 st[L::NT];
-    pf_load_S<L::NT>(st, Sinit, fh * (DF / 2), cb);
-    if (a.init_sum_ws)
-      for (int j = 0; j < seg; ++j)
-        pf_add_S<L::NT>(st, a.ws + ((long long)bh * a.ws_slots + j) * a.state_elems, fh * (DF / 2), cb);
-    __syncthreads();
-    for (int it = 0; it < n; ++it) {
-      map_chunk(it);
+      x.v = buf_load16_nt(rsrc(v, t), (p >> 3) * kPD * 2 + 16 * (p & 7));
+    };
+    // q and k rows of the sub-chunk together: independent MFMA and exp chains
+    auto map2 = [&](const u32x4 (&xq)[4], const u32x4 (&xk)[4], uint8_t* tq, uint8_t* tk, bool kzero) {
+      const float bq = pf_row_bias(xq, bm), bk = pf_row_bias(xk, bm);
+#pragma unroll
+      for (int f = 0; f < P::FBJ; ++f) {
+        f32x16 uq = {}, uk = {};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          B16::mma(uq, Wf[f][kb], __builtin_bit_cast(bf16x8, xq[kb]));
+          B16::mma(uk, Wf[f][kb], __builtin_bit_cast(bf16x8, xk[kb]));
+        }
+        pf_phi_store<DF>(uq, bq, false, tq, li, fbm + f);
+        pf_phi_store<DF>(uk, bk, kzero, tk, li, fbm + f);
+      }
+    };
+    // Step t: the output tile of sub-chunk t - 3, then sub-chunk t (held in
+    // cur) mapped, and the rows of sub-chunk t + 2 loaded into nxt (the set
+    // sub-chunk t - 1 used). Every step issues the same loads and stores
+    // (zero size past the end) and maps whatever it holds (buffers past the
+    // end are never read), so the wait counts of the loop are the same on
+    // every path and prefetches stay in flight.
+    auto step = [&](int t, XSet& cur, XSet& nxt) {
+      const int set = t & 1;
+      const int valid = max(0, min(32, nrows - 32 * t));
+      const uint8_t* sY = smem + P::Y_OFF + (set ^ 1) * P::VT;
+      buf_store16_nt(rsrc(out, t - 3), (p >> 3) * kPD * 2 + 16 * (p & 7),
+                     *reinterpret_cast<const u32x4*>(sY + tile_off<P::RBV>(p >> 3, 16 * (p & 7))));
+      if (act) map2(cur.q, cur.k, smem + P::Q_OFF + set * P::PHI, smem + P::K_OFF + set * P::PHI, li >= valid);
+      *reinterpret_cast<u32x4*>(smem + P::V_OFF + set * P::VT + tile_off<P::RBV>(p >> 3, 16 * (p & 7))) = cur.v;
+      load(t + 2, nxt);
       __syncthreads();
-      if (it > 0) flush_y(it - 1);
-      // ---- 2. read-out over the wave's feature half, then the S update ----
-      f32x16 num;
-      {
-        f32x16 R0 = {}, R1 = {};
-#pragma unroll
-        for (int t = 0; t < L::NT; ++t)
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2) {
-            const bf16x8 sf = B16::from_acc(st[t], kb2);
-            const int f0 = fh * (DF / 2) + 32 * t + 16 * kb2;
-            B16::mma(R0, sf, B16::template load_rows<L::RBF>(sQ, 0, f0));
-            B16::mma(R1, sf, B16::template load_rows<L::RBF>(sQ, 32, f0));
-          }
-        // row block 1 - fh goes to state wave w ^ 2, which finishes it
-        pf_put16(sR, w, fh ? R0 : R1);
-        num = fh ? R1 : R0;
-      }
-      pf_update_S<DF, L::NT>(st, sK, sV, fh * (DF / 2), cb);
-      colsum();
-      __syncthreads();
-      // ---- 3. finish rows [32 fh, +32) x columns [32 cb, +32); move z on ----
-      pf_add16(sR, w ^ 2, num);
-      pf_add16(sA, 2 * fh + cb, num);
-      const int i = 32 * fh + li;
-      float inv = 1.f;
-      if (a.normalize) inv = 1.f / fmaxf(sDp[i] + sDen[i] + sDen[64 + i], kEps);
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<u32x2*>(sY + tile_off<kPD * 2>(i, (32 * cb + 8 * g + 4 * h) * 2)) =
-            u32x2{pack_bf16x2(num[4 * g] * inv, num[4 * g + 1] * inv),
-                  pack_bf16x2(num[4 * g + 2] * inv, num[4 * g + 3] * inv)};
-      if (threadIdx.x < DF) {  // state waves hold threads 0..255 >= DF - 1
-        const float* zc = sZ + (it & 1) * DF;
-        float s = zc[threadIdx.x];
-#pragma unroll
-        for (int sl = 0; sl < O::NSL; ++sl) s += zp[sl * DF + threadIdx.x];
-        sZ[((it + 1) & 1) * DF + threadIdx.x] = s;
-      }
-    }
-    __syncthreads();  // the last output tile is complete
-    if (n > 0) flush_y(n - 1);
-    if (a.S_out && seg == a.nseg - 1) {
-      pf_store_S<L::NT>(st, a.S_out + (long long)bh * DF * kPD, fh * (DF / 2), cb);
-      if (threadIdx.x < DF) a.z_out[(long long)bh * DF + threadIdx.x] = sZ[(n & 1) * DF + threadIdx.x];
+    };
+    // The rotation of the three register sets starts two steps early (steps
+    // -2 and -1 only load sub-chunks 0 and 1; what they map is never read)
+    // and runs whole rotations, so that the loop is entered with no loads in
+    // flight and every iteration has the same memory instruction stream.
+    XSet xa = {}, xb = {}, xc = {};
+    __syncthreads();  // the contraction waves have their initial state
+    for (int t = -2; t < tend; t += 3) {
+      step(t, xb, xa);
+      step(t + 1, xc, xb);
+      step(t + 2, xa, xc);
     }
   } else {
+    // ---------------------------------------------------- contraction waves
+    const Cown<DF> o(w);
+    f32x16 S[P::NFBW][P::NCB], Z[P::NFBW];
+#pragma unroll
+    for (int f = 0; f < P::NFBW; ++f) {
+#pragma unroll
+      for (int cb = 0; cb < P::NCB; ++cb) {
+        pf_load_S<1>(*reinterpret_cast<f32x16(*)[1]>(&S[f][cb]), Sinit, 32 * (o.fb0 + f), o.cb0 + cb);
+        if (a.init_sum_ws)
+          for (int s2 = 0; s2 < seg; ++s2)
+            pf_add_S<1>(*reinterpret_cast<f32x16(*)[1]>(&S[f][cb]),
+                        a.ws + ((long long)bh * a.ws_slots + s2) * a.state_elems, 32 * (o.fb0 + f), o.cb0 + cb);
+      }
+      // z of the block's features in every column of Z[f]
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int fe = 32 * (o.fb0 + f) + 8 * (r >> 2) + 4 * h + (r & 3);
+        float zv = zinit ? zinit[fe] : 0.f;
+        if (a.init_sum_ws)
+          for (int s2 = 0; s2 < seg; ++s2) zv += a.ws[((long long)bh * a.ws_slots + s2) * a.state_elems + DF * kPD + fe];
+        Z[f][r] = zv;
+      }
+    }
+    bf16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
     __syncthreads();
-    const int r = fh;  // query row block of this score wave
-    for (int it = 0; it < n; ++it) {
-      map_chunk(it);
-      __syncthreads();
-      if (it > 0) flush_y(it - 1);
-      // ---- 2. A[j][i] for keys j of block 0 (and block 1 when r = 1) and
-      // queries i of block r; lane holds query i = 32 r + li ----
-      f32x16 Aa = {}, Ab = {};
-#pragma unroll 4
-      for (int kb = 0; kb < DF / 16; ++kb) {
-        const bf16x8 bq = B16::template load_rows<L::RBF>(sQ, 32 * r, 16 * kb);
-        B16::mma(Aa, B16::template load_rows<L::RBF>(sK, 0, 16 * kb), bq);
-        if (r) B16::mma(Ab, B16::template load_rows<L::RBF>(sK, 32, 16 * kb), bq);
-      }
-      float dpart = 0.f;
+    for (int t = -2; t < tend; ++t) {
+      // finish sub-chunk t - 2: value block cb = w adds the partials of every
+      // wave that holds it, normalizes and writes the output tile
+      const int sf = t - 2;
+      if (sf >= 0 && sf < ns && w < 2) {
+        const float* sP = reinterpret_cast<const float*>(smem + P::P_OFF + (sf & 1) * P::PB);
+        const float* sD = reinterpret_cast<const float*>(smem + P::D_OFF + (sf & 1) * P::DBUF);
+        const int cb = w;
+        f32x16 y = {};
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int jt = 8 * (e >> 2) + 4 * h + (e & 3);
-        const bool keep = jt <= li;
-        if (r) {
-          Ab[e] = keep ? Ab[e] : 0.f;
-          dpart += Aa[e] + Ab[e];
-        } else {
-          Aa[e] = keep ? Aa[e] : 0.f;
-          dpart += Aa[e];
+        for (int c = 0; c < 4; ++c) {
+          const Cown<DF> oc(c);
+          if (cb < oc.cb0 || cb >= oc.cb0 + P::NCB) continue;
+          const int slot = c * P::NCB + (cb - oc.cb0);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(sP + ((slot * 4 + g) * 64 + l) * 4);
+            y[4 * g] += x[0];
+            y[4 * g + 1] += x[1];
+            y[4 * g + 2] += x[2];
+            y[4 * g + 3] += x[3];
+          }
+        }
+        float inv = 1.f;
+        if (a.normalize) {
+          float den = 0.f;
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (Cown<DF>(c).den) den += sD[c * 32 + li];
+          inv = 1.f / fmaxf(den, kEps);
+        }
+        uint8_t* sY = smem + P::Y_OFF + (sf & 1) * P::VT;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<u32x2*>(sY + tile_off<P::RBV>(li, (32 * cb + 8 * g + 4 * h) * 2)) =
+              u32x2{pack_bf16x2(y[4 * g] * inv, y[4 * g + 1] * inv), pack_bf16x2(y[4 * g + 2] * inv, y[4 * g + 3] * inv)};
+      }
+      // partials of sub-chunk t - 1
+      const int sc = t - 1;
+      if (sc >= 0 && sc < ns) {
+        const int set = sc & 1;
+        float* sP = reinterpret_cast<float*>(smem + P::P_OFF + set * P::PB);
+        float* sD = reinterpret_cast<float*>(smem + P::D_OFF + set * P::DBUF);
+        const uint8_t* sQ = smem + P::Q_OFF + set * P::PHI;
+        const uint8_t* sK = smem + P::K_OFF + set * P::PHI;
+        const uint8_t* sV = smem + P::V_OFF + set * P::VT;
+        f32x16 num[P::NCB], A = {};
+#pragma unroll
+        for (int cb = 0; cb < P::NCB; ++cb) num[cb] = f32x16{};
+        // scores over the wave's features and the read-out of S (the state
+        // before this sub-chunk)
+#pragma unroll
+        for (int f = 0; f < P::NFBW; ++f)
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2) {
+            const int f0 = 32 * (o.fb0 + f) + 16 * kb2;
+            const bf16x8 qf = B16::template load_rows<P::RBF>(sQ, 0, f0);
+            B16::mma(A, B16::template load_rows<P::RBF>(sK, 0, f0), qf);
+#pragma unroll
+            for (int cb = 0; cb < P::NCB; ++cb) B16::mma(num[cb], B16::from_acc(S[f][cb], kb2), qf);
+          }
+        // causal mask (key j <= query i; lane = query), the in-chunk denominator
+        float dp = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool keep = 8 * (r >> 2) + 4 * h + (r & 3) <= li;
+          A[r] = keep ? A[r] : 0.f;
+          dp += A[r];
+        }
+        dp += xor32(dp);
+#pragma unroll
+        for (int cb = 0; cb < P::NCB; ++cb)
+#pragma unroll
+          for (int kbj = 0; kbj < 2; ++kbj)
+            B16::mma(num[cb], B16::template load_cols<P::RBV>(sV, 16 * kbj, 32 * (o.cb0 + cb)), B16::from_acc(A, kbj));
+        // numerator partials to LDS, per value block
+#pragma unroll
+        for (int cb = 0; cb < P::NCB; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<f32x4*>(sP + (((w * P::NCB + cb) * 4 + g) * 64 + l) * 4) =
+                f32x4{num[cb][4 * g], num[cb][4 * g + 1], num[cb][4 * g + 2], num[cb][4 * g + 3]};
+        // denominator partial per query: in-chunk part and the read-out of z
+        // (every column of Z holds z, so every row of Dn holds phi(q_j).z)
+        if (o.den) {
+          f32x16 Dn = {};
+#pragma unroll
+          for (int f = 0; f < P::NFBW; ++f)
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+              B16::mma(Dn, B16::from_acc(Z[f], kb2), B16::template load_rows<P::RBF>(sQ, 0, 32 * (o.fb0 + f) + 16 * kb2));
+          if (h == 0) sD[w * 32 + li] = dp + Dn[0];
+        }
+        // S and z move on
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int f = 0; f < P::NFBW; ++f) {
+            const bf16x8 kf = B16::template load_cols<P::RBF>(sK, 16 * kb, 32 * (o.fb0 + f));
+#pragma unroll
+            for (int cb = 0; cb < P::NCB; ++cb)
+              B16::mma(S[f][cb], kf, B16::template load_cols<P::RBV>(sV, 16 * kb, 32 * (o.cb0 + cb)));
+            if (o.den) B16::mma(Z[f], kf, ones);
+          }
         }
       }
-      dpart += xor32(dpart);
-      if (cb == 0 && h == 0) sDp[32 * r + li] = dpart;
-      {
-        // phi(q_i) . z for the rows of block r over features
-        // [cb m/2 + h m/4, +m/4) (bf16 phi(q) from LDS), halves added across
-        // lanes l and l ^ 32; z after the previous chunk
-        const float* zc = sZ + (it & 1) * DF;
-        const int i = 32 * r + li, f0 = cb * (DF / 2) + h * (DF / 4);
-        float dot = 0.f;
-#pragma unroll
-        for (int u = 0; u < DF / 32; ++u) {
-          const u32x4 qv = *reinterpret_cast<const u32x4*>(sQ + tile_off<L::RBF>(i, (f0 + 8 * u) * 2));
-          const f32x4 z0 = *reinterpret_cast<const f32x4*>(zc + f0 + 8 * u);
-          const f32x4 z1 = *reinterpret_cast<const f32x4*>(zc + f0 + 8 * u + 4);
-          dot += __uint_as_float(qv[0] << 16) * z0[0] + __uint_as_float(qv[0] & 0xffff0000u) * z0[1] +
-                 __uint_as_float(qv[1] << 16) * z0[2] + __uint_as_float(qv[1] & 0xffff0000u) * z0[3] +
-                 __uint_as_float(qv[2] << 16) * z1[0] + __uint_as_float(qv[2] & 0xffff0000u) * z1[1] +
-                 __uint_as_float(qv[3] << 16) * z1[2] + __uint_as_float(qv[3] & 0xffff0000u) * z1[3];
-        }
-        dot += xor32(dot);
-        if (h == 0) sDen[cb * 64 + i] = dot;
-      }
-      f32x16 av = {};
-#pragma unroll
-      for (int kbj = 0; kbj < 2; ++kbj)
-        B16::mma(av, B16::template load_cols<L::RBV>(sV, 16 * kbj, 32 * cb), B16::from_acc(Aa, kbj));
-      if (r) {
-#pragma unroll
-        for (int kbj = 0; kbj < 2; ++kbj)
-          B16::mma(av, B16::template load_cols<L::RBV>(sV, 32 + 16 * kbj, 32 * cb), B16::from_acc(Ab, kbj));
-      }
-      pf_put16(sA, w - 4, av);
-      colsum();
       __syncthreads();
     }
-    __syncthreads();  // the last output tile is complete
-    if (n > 0) flush_y(n - 1);
+    if (a.S_out && seg == a.nseg - 1) {
+#pragma unroll
+      for (int f = 0; f < P::NFBW; ++f) {
+#pragma unroll
+        for (int cb = 0; cb < P::NCB; ++cb)
+          pf_store_S<1>(*reinterpret_cast<const f32x16(*)[1]>(&S[f][cb]), a.S_out + (long long)bh * DF * kPD,
+                        32 * (o.fb0 + f), o.cb0 + cb);
+        if (o.den && li == 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            a.z_out[(long long)bh * DF + 32 * (o.fb0 + f) + 8 * (r >> 2) + 4 * h + (r & 3)] = Z[f][r];
+        }
+      }
+    }
   }
 }
 
