@@ -64,6 +64,8 @@ def _load():
     L.la_device_status.argtypes, L.la_device_status.restype = [vp], i
     L.la_forward_workspace_size.argtypes = [i, i, i, i, fmp, i]
     L.la_forward_workspace_size.restype = sz
+    L.la_forward_workspace_size_dt.argtypes = [i, i, i, i, fmp, i, i]
+    L.la_forward_workspace_size_dt.restype = sz
     fwd = [vp, vp, vp, vp, i, i, i, i, fmp, i, i, i, vp, vp, vp, vp, vp, sz, vp]
     L.la_forward.argtypes, L.la_forward.restype = fwd, i
     L.la_forward_ex.argtypes, L.la_forward_ex.restype = fwd + [vp], i
@@ -119,11 +121,15 @@ def declared_functions():
 
 
 def _dtype_code(t: torch.Tensor) -> int:
-    if t.dtype == torch.bfloat16:
+    return _dtype_code_of(t.dtype)
+
+
+def _dtype_code_of(dtype) -> int:
+    if dtype == torch.bfloat16:
         return LA_BF16
-    if t.dtype == torch.float32:
+    if dtype == torch.float32:
         return LA_F32
-    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+    raise TypeError(f"unsupported dtype {dtype}; use bfloat16 or float32")
 
 
 def _ptr(t):
@@ -180,9 +186,13 @@ def la_device_status(stream=None) -> int:
     return st
 
 
-def la_forward_workspace_size(B, H, N, d, feature_map="elu1", W=None, causal=True) -> int:
+def la_forward_workspace_size(B, H, N, d, feature_map="elu1", W=None, causal=True, dtype=None) -> int:
+    """Workspace bytes of la_forward; exact for `dtype` (torch.float32 or
+    torch.bfloat16) when given, else enough for either."""
     fm = _fmap(feature_map, W)
-    return int(lib.la_forward_workspace_size(B, H, N, d, ctypes.byref(fm), int(causal)))
+    if dtype is None:
+        return int(lib.la_forward_workspace_size(B, H, N, d, ctypes.byref(fm), int(causal)))
+    return int(lib.la_forward_workspace_size_dt(B, H, N, d, ctypes.byref(fm), int(causal), _dtype_code_of(dtype)))
 
 
 def la_forward_ex(q, k, v, *, feature_map="elu1", W=None, causal=True, normalize=True, S_in=None, z_in=None,
@@ -202,7 +212,7 @@ def la_forward_ex(q, k, v, *, feature_map="elu1", W=None, causal=True, normalize
         df = feature_dim(d, feature_map, W)
         S_out = torch.empty((B, H, df, d), device=q.device, dtype=torch.float32)
         z_out = torch.empty((B, H, df), device=q.device, dtype=torch.float32)
-    need = int(lib.la_forward_workspace_size(B, H, N, d, ctypes.byref(fm), int(causal)))
+    need = int(lib.la_forward_workspace_size_dt(B, H, N, d, ctypes.byref(fm), int(causal), dt))
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -201,12 +201,22 @@ const char* la_status_string(int status) {
   }
 }
 
-size_t la_forward_workspace_size(int B, int H, int N, int d, const la_feature_map* feature_map, int causal) {
+size_t la_forward_workspace_size_dt(int B, int H, int N, int d, const la_feature_map* feature_map, int causal,
+                                    int dtype) {
   if (B < 0 || H < 0 || N < 0 || !d_supported(d)) return 0;
+  if (dtype != LA_F32 && dtype != LA_BF16) return 0;
   const int dfeat = feature_dim(feature_map, d);
   if (dfeat <= 0) return 0;
   if (feature_map->kind == LA_POLY2) return poly_ws_bytes((long long)B * H, N, d);
-  return make_plan((long long)B * H, N, d, dfeat, causal != 0, feature_map->kind == LA_PERFORMER).ws_bytes;
+  const bool mapped = feature_map->kind == LA_PERFORMER;
+  const bool fused = mapped && la::perf_fused_supported(d, dfeat, dtype, false);
+  return make_plan((long long)B * H, N, d, dfeat, causal != 0, mapped && !fused).ws_bytes;
+}
+
+size_t la_forward_workspace_size(int B, int H, int N, int d, const la_feature_map* feature_map, int causal) {
+  const size_t a = la_forward_workspace_size_dt(B, H, N, d, feature_map, causal, LA_F32);
+  const size_t b = la_forward_workspace_size_dt(B, H, N, d, feature_map, causal, LA_BF16);
+  return a > b ? a : b;
 }
 
 }  // extern "C"
@@ -313,9 +323,9 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
         overlaps(z_out, z_bytes, feature_map->W, wb))
       return LA_ERR_INVALID_ARG;
   }
-  // random features at d = 64 in bf16: the projection runs inside the chunked
-  // passes and the workspace holds segment states only
-  const bool fused = mapped && la::perf_fused_supported(d, dfeat, dtype, causal != 0, gamma != nullptr);
+  // random features at d = 64 in bf16, causal or not: the projection runs
+  // inside the chunked passes and the workspace holds segment states only
+  const bool fused = mapped && la::perf_fused_supported(d, dfeat, dtype, gamma != nullptr);
   const Plan p = make_plan(BH, N, d, dfeat, causal != 0, mapped && !fused);
   if (static_ws) {
     if (p.ws_bytes > LA_STATIC_SCRATCH_BYTES) return LA_ERR_WORKSPACE;
@@ -422,7 +432,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
     s.S_out = S_out;
     s.z_out = z_out;
   }
-  if (fused) return status_from_hip(la::perf_fused_dispatch(a, s, dfeat, stream, events));
+  if (fused) return status_from_hip(la::perf_fused_dispatch(a, s, dfeat, causal != 0, stream, events));
   const int kfm = feature_map->kind == LA_ELU1 ? la::kElu1 : la::kIdentity;  // mapped features: identity inside
   return status_from_hip(la::prefill_dispatch(a, s, d, dfeat, kfm, dtype, causal != 0, gamma != nullptr, stream,
                                               events));

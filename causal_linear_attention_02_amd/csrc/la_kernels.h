@@ -151,9 +151,11 @@ hipError_t prefill_dispatch(const FwdArgs& a, const ScanArgs& s, int D, int DF, 
                             bool decay, hipStream_t st, hipEvent_t* ev);
 hipError_t scan_dispatch(const ScanArgs& s, hipStream_t st);
 // random features with the projection fused into the chunked passes
-// (d = 64, bf16, causal, m in {64, 128, 256}): state pass, carry scan, output pass
-bool perf_fused_supported(int D, int DF, int dtype, bool causal, bool decay);
-hipError_t perf_fused_dispatch(const FwdArgs& a, const ScanArgs& s, int DF, hipStream_t st, hipEvent_t* ev);
+// (d = 64, bf16, m in {64, 128, 256}, causal or not): state pass, carry scan,
+// output pass (causal) or read-out against the total (non-causal)
+bool perf_fused_supported(int D, int DF, int dtype, bool decay);
+hipError_t perf_fused_dispatch(const FwdArgs& a, const ScanArgs& s, int DF, bool causal, hipStream_t st,
+                               hipEvent_t* ev);
 hipError_t backward_dispatch(const FwdArgs& fa, const ScanArgs& fs, const BwdArgs& b, const ScanArgs& rs, int D,
                              int fmap, int dtype, bool decay, hipStream_t st);
 hipError_t gated_dispatch(const GatedArgs& g, const ScanArgs& s, int D, int fmap, int dtype, hipStream_t st);

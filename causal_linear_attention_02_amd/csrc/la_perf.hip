@@ -10,13 +10,15 @@
 // log2(m) / 2 goes straight into LDS as bf16, so the m-wide features never
 // reach HBM.
 //
-// d = 64, bf16 inputs, causal.
-//   state pass : local (S, z) of every segment but the last -> workspace
-//                (8 waves for m >= 128, else 4; each holds one feature slice
-//                of S for 32 value columns)
-//   carry scan : the exclusive prefix over segments (la_prefill.hip)
-//   output pass: each segment walks its chunks from its carried prefix
-//                (8 waves, two per SIMD)
+// d = 64, bf16 inputs, causal or not.
+//   state pass : local (S, z) of every segment (causal: all but the last)
+//                -> workspace (8 waves for m >= 128, else 4; each holds one
+//                feature slice of S for 32 value columns)
+//   carry scan : causal: the exclusive prefix over segments; otherwise the
+//                head's total (la_prefill.hip)
+//   output pass: causal: each segment walks its chunks from its carried
+//                prefix (8 waves, two per SIMD); otherwise every wave reads
+//                out 32-row blocks against the total (pf_readout_kernel)
 // In the output pass wave w < 4 holds S[fh*m/2 .. fh*m/2 + m/2)[32 cb .. 32 cb + 32)
 // in MFMA accumulators (fh = w >> 1, cb = w & 1) and finishes query rows
 // [32 fh, 32 fh + 32) x value columns [32 cb, 32 cb + 32) of every chunk; the
@@ -630,8 +632,158 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Non-causal read-out: y_i = phi(q_i)^T S / phi(q_i)^T z with the head's total
+// (S, z) ("Linear Attention", marovi.ai, "Reformulación con núcleos").
+// grid (BH, segments), 8 waves. S^T and z (bf16) and W sit in LDS; after one
+// barrier every wave maps and reads out 32-row blocks of its own (blocks
+// w, w + 8, ...). For each 32-feature block the projection U^T = W X^T comes
+// out of the MFMA with the lane's query row and 16 of the features in its
+// registers; 2^(A u - B_row) of those registers, packed to bf16, is directly
+// the B operand of num^T = S^T phi^T and of den = z^T phi^T, because the LDS
+// copies of S^T and z store each 16-feature block in the order the
+// accumulator registers hold it (ro_pos). phi(Q) never leaves registers.
+// ---------------------------------------------------------------------------
 template <int DF>
-hipError_t launch_pf(const FwdArgs& a, const ScanArgs& s, hipStream_t st, hipEvent_t* ev) {
+struct RoL {
+  static constexpr int NFB = DF / 32;
+  static constexpr int RBF = DF * 2;   // S^T rows and the z row (bf16)
+  static constexpr int RBV = kPD * 2;  // W rows (bf16)
+  static constexpr int S_OFF = DF * RBV;
+  static constexpr int Z_OFF = S_OFF + kPD * RBF;
+  static constexpr int Y_OFF = Z_OFF + RBF;       // per-wave output tiles, 32 rows x 128 bytes
+  static constexpr int YT = 32 * RBV;
+  static constexpr int BYTES = Y_OFF + 8 * YT;
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+constexpr int kRoWaves = 8;
+
+// LDS position of feature f within S^T and z rows: bits 2 and 3 swapped. Lane
+// half h of a U^T accumulator holds, in registers 8 kb2 .. 8 kb2 + 7, the
+// features 16 kb2 + {4h .. 4h + 3, 8 + 4h .. 8 + 4h + 3} of its 32-feature
+// block, which this order puts at positions 16 kb2 + 8h .. 16 kb2 + 8h + 7.
+// The map is its own inverse.
+__device__ __forceinline__ int ro_pos(int f) { return (f & ~12) | ((f & 4) << 1) | ((f & 8) >> 1); }
+
+template <int DF>
+__global__ __launch_bounds__(64 * kRoWaves) void pf_readout_kernel(FwdArgs a) {
+  using R = RoL<DF>;
+  constexpr int NTH = 64 * kRoWaves;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[R::BYTES];
+  uint8_t* sW = smem;
+  uint8_t* sS = smem + R::S_OFF;
+  const uint8_t* sZ = smem + R::Z_OFF;
+  const int bh = blockIdx.x, seg = blockIdx.y;
+  uint8_t* sY = smem + R::Y_OFF + (threadIdx.x >> 6) * R::YT;
+  const int c0 = seg * a.chunks_per_seg;
+  const int r0 = 64 * c0;
+  const int nrows = max(0, min(64 * (c0 + a.chunks_per_seg), a.N) - r0);
+  const int nb = (nrows + 31) / 32;
+  const long long base = (long long)bh * a.N + r0;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63, h = l >> 5, li = l & 31;
+  const float bm = 0.5f * __log2f((float)DF);
+  const auto rq = make_rsrc(static_cast<const __bf16*>(a.q) + base * kPD, (unsigned)(nrows * kPD * 2));
+  const auto ro = make_rsrc(static_cast<__bf16*>(a.out) + base * kPD, (unsigned)(nrows * kPD * 2));
+  // blocks w, w + 8, ...: cnt of them; the loop runs a whole number of
+  // two-set rotations and loads one block ahead (zero size past the end)
+  const int cnt = nb > w ? (nb - w + kRoWaves - 1) / kRoWaves : 0;
+  struct XSet {
+    u32x4 x[4];
+  };
+  auto load = [&](int it, XSet& s_) { pf_load_x(s_.x, rq, 32 * (w + kRoWaves * it)); };
+  XSet xa, xb;
+  load(0, xa);
+
+  // stage W, S^T and z (the total: slot ws_total_slot of the head)
+  pf_stage_W<DF, NTH>(a.W, sW);
+  const float* st = a.ws + ((long long)bh * a.ws_slots + a.ws_total_slot) * a.state_elems;
+  for (int p = threadIdx.x; p < kPD * DF / 8; p += NTH) {
+    const int c = p & 63, j = p >> 6;  // S^T row c, positions 8 j .. 8 j + 7
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = st[ro_pos(8 * j + e) * kPD + c];
+    B16::template store8<R::RBF>(sS, c, 8 * j, x);
+  }
+  if (threadIdx.x < DF / 8) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = st[DF * kPD + ro_pos(8 * threadIdx.x + e)];
+    B16::template store8<R::RBF>(smem + R::Z_OFF, 0, 8 * threadIdx.x, x);
+  }
+  __syncthreads();
+
+  auto compute = [&](int blk, const XSet& s_) {
+    const float b = pf_row_bias(s_.x, bm);
+    f32x16 num0 = {}, num1 = {}, dn = {};
+    // the projection of block fb + 1 is issued before the exponentials of
+    // block fb; one block at a time keeps the live accumulators bounded
+    f32x16 u = pf_project<DF>(sW, s_.x, 0);
+#pragma unroll
+    for (int fb = 0; fb < R::NFB; ++fb) {
+      __builtin_amdgcn_sched_barrier(0);
+      const f32x16 un = fb + 1 < R::NFB ? pf_project<DF>(sW, s_.x, fb + 1) : u;
+      uint32_t pk[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        pk[j] = pack_bf16x2(__builtin_amdgcn_exp2f(kPfA * u[2 * j] - b), __builtin_amdgcn_exp2f(kPfA * u[2 * j + 1] - b));
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pk[4 * kb2], pk[4 * kb2 + 1], pk[4 * kb2 + 2], pk[4 * kb2 + 3]});
+        const int k0 = 32 * fb + 16 * kb2;
+        B16::mma(num0, B16::template load_rows<R::RBF>(sS, 0, k0), pf);
+        B16::mma(num1, B16::template load_rows<R::RBF>(sS, 32, k0), pf);
+        B16::mma(dn, *reinterpret_cast<const bf16x8*>(sZ + (k0 + 8 * h) * 2), pf);
+      }
+      u = un;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // every row of dn holds phi(q).z for the lane's query
+    const float inv = a.normalize ? 1.f / fmaxf(dn[0], kEps) : 1.f;
+    // lane: query li of the block, value columns 32 cb + 8 g + 4 h + 0..3 in
+    // registers 4 g ..; one swap with the other half gives each lane 8
+    // consecutive columns (16 p2 + 8 h ..), written to the wave's LDS tile and
+    // read back by rows, so that every store covers whole 128-byte rows
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const f32x16& nm = cb ? num1 : num0;
+#pragma unroll
+      for (int p2 = 0; p2 < 2; ++p2) {
+        const int r = 8 * p2;
+        const uint32_t x0 = pack_bf16x2(nm[r] * inv, nm[r + 1] * inv), x1 = pack_bf16x2(nm[r + 2] * inv, nm[r + 3] * inv);
+        const uint32_t y0 = pack_bf16x2(nm[r + 4] * inv, nm[r + 5] * inv), y1 = pack_bf16x2(nm[r + 6] * inv, nm[r + 7] * inv);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+        *reinterpret_cast<u32x4*>(sY + tile_off<R::RBV>(li, (32 * cb + 16 * p2 + 8 * h) * 2)) =
+            u32x4{s0[0], s1[0], s0[1], s1[1]};
+      }
+    }
+    // the tile is the wave's own: its LDS operations complete in order, so
+    // the fences only keep the compiler from moving the reads above the writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 8 * i + (l >> 3), u = l & 7;
+      buf_store16_nt(ro, (32 * blk + rr) * kPD * 2 + 16 * u,
+                     *reinterpret_cast<const u32x4*>(sY + tile_off<R::RBV>(rr, 16 * u)));
+    }
+    // the next block's tile writes must not pass these reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  for (int it = 0; it < cnt; it += 2) {
+    load(it + 1, xb);
+    compute(w + kRoWaves * it, xa);
+    load(it + 2, xa);
+    if (it + 1 < cnt) compute(w + kRoWaves * (it + 1), xb);
+  }
+}
+
+template <int DF>
+hipError_t launch_pf(const FwdArgs& a, const ScanArgs& s, bool causal, hipStream_t st, hipEvent_t* ev) {
   constexpr int NW = DF >= 128 ? 8 : 4;
   if (a.run_state_pass)
     hipLaunchKernelGGL((pf_state_kernel<DF, NW>), dim3(a.BH, a.nseg_state), dim3(64 * NW), 0, st, a);
@@ -641,22 +793,26 @@ hipError_t launch_pf(const FwdArgs& a, const ScanArgs& s, hipStream_t st, hipEve
     if (e != hipSuccess) return e;
   }
   if (ev) (void)hipEventRecord(ev[2], st);
-  hipLaunchKernelGGL(pf_output_kernel<DF>, dim3(a.BH, a.nseg), dim3(512), 0, st, a);
+  if (causal)
+    hipLaunchKernelGGL(pf_output_kernel<DF>, dim3(a.BH, a.nseg), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL(pf_readout_kernel<DF>, dim3(a.BH, a.nseg), dim3(64 * kRoWaves), 0, st, a);
   if (ev) (void)hipEventRecord(ev[3], st);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool perf_fused_supported(int D, int DF, int dtype, bool causal, bool decay) {
-  return D == kPD && (DF == 64 || DF == 128 || DF == 256) && dtype == 1 && causal && !decay;
+bool perf_fused_supported(int D, int DF, int dtype, bool decay) {
+  return D == kPD && (DF == 64 || DF == 128 || DF == 256) && dtype == 1 && !decay;
 }
 
-hipError_t perf_fused_dispatch(const FwdArgs& a, const ScanArgs& s, int DF, hipStream_t st, hipEvent_t* ev) {
+hipError_t perf_fused_dispatch(const FwdArgs& a, const ScanArgs& s, int DF, bool causal, hipStream_t st,
+                               hipEvent_t* ev) {
   switch (DF) {
-    case 64: return launch_pf<64>(a, s, st, ev);
-    case 128: return launch_pf<128>(a, s, st, ev);
-    case 256: return launch_pf<256>(a, s, st, ev);
+    case 64: return launch_pf<64>(a, s, causal, st, ev);
+    case 128: return launch_pf<128>(a, s, causal, st, ev);
+    case 256: return launch_pf<256>(a, s, causal, st, ev);
   }
   return hipErrorInvalidValue;
 }

@@ -99,16 +99,28 @@ int la_device_status(hipStream_t stream);
 
 /*
  * Bytes of device workspace that la_forward needs for these sizes (0 when
- * none is needed; any element type). Returns 0 also for invalid arguments.
- * It holds the fp32 states of the sequence segments and, for random features,
- * phi(q) and phi(k) ([B][H][N][m] each, sized for fp32). Random features with
- * d = 64, bf16 input and causal = 1 project q and k inside the chunked passes
- * and la_forward then needs the segment states only; the size returned here
- * (which cannot know the element type) still covers phi(q) and phi(k). With LA_POLY2 it
- * holds fp32 partial numerators (2 per token at d = 32, 4 at d = 64, [N][d]
- * each per (batch, head)) and partial denominators (2 or 4 per token).
+ * none is needed; enough for either element type). Returns 0 also for
+ * invalid arguments. It holds the fp32 states of the sequence segments and,
+ * for random features outside the fused shapes, phi(q) and phi(k)
+ * ([B][H][N][m] each, sized for fp32). Random features with d = 64 and bf16
+ * input (causal or not) project q and k inside the chunked passes and need
+ * the segment states only; this size, which does not know the element type,
+ * still covers phi(q) and phi(k) for them (la_forward_workspace_size_dt
+ * gives the exact figure). With LA_POLY2 it holds fp32 partial numerators
+ * (2 per token at d = 32, 4 at d = 64, [N][d] each per (batch, head)) and
+ * partial denominators (2 or 4 per token).
  */
 size_t la_forward_workspace_size(int B, int H, int N, int d, const la_feature_map* feature_map, int causal);
+
+/*
+ * The workspace la_forward needs for inputs of element type `dtype` (LA_F32
+ * or LA_BF16): the same as la_forward_workspace_size, except that it leaves
+ * out phi(q) and phi(k) where the random-feature map is fused into the
+ * chunked passes (d = 64, bf16). Returns 0 for invalid arguments, an unknown
+ * dtype included.
+ */
+size_t la_forward_workspace_size_dt(int B, int H, int N, int d, const la_feature_map* feature_map, int causal,
+                                    int dtype);
 
 /*
  * Linear attention over whole sequences ("Reformulación con núcleos"; causal:
@@ -123,10 +135,10 @@ size_t la_forward_workspace_size(int B, int H, int N, int d, const la_feature_ma
  *   S_out,z_out optional (both or neither): state after the last token,
  *             S_in + sum_j phi(k_j) v_j^T and z_in + sum_j phi(k_j) (the
  *             hand-off to la_decode_step).
- *   workspace device scratch of at least la_forward_workspace_size() bytes
- *             (random features at d = 64, bf16, causal: the segment states
- *             suffice), 256-byte aligned (may be NULL when the size needed is
- *             0). Its contents are overwritten.
+ *   workspace device scratch of at least la_forward_workspace_size_dt()
+ *             bytes for `dtype` (la_forward_workspace_size() covers both
+ *             element types), 256-byte aligned (may be NULL when the size
+ *             needed is 0). Its contents are overwritten.
  * N = 0 writes only S_out/z_out (= S_in/z_in, or zeros).
  */
 int la_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
@@ -142,9 +154,8 @@ int la_forward(const void* q, const void* k, const void* v, void* out, int B, in
  * reserved on each GPU by the first call there and held until the process
  * ends. The call itself allocates nothing.
  *   Arguments and results as la_forward.
- *   Returns LA_ERR_WORKSPACE when la_forward_workspace_size() for the request
- *   (for random features with bf16 input, d = 64 and causal = 1: the segment
- *   states alone) exceeds LA_STATIC_SCRATCH_BYTES, LA_ERR_HIP when the array's
+ *   Returns LA_ERR_WORKSPACE when la_forward_workspace_size_dt() for the
+ *   request exceeds LA_STATIC_SCRATCH_BYTES, LA_ERR_HIP when the array's
  *   address cannot be looked up.
  *   Every call on one GPU uses the same array and leaves its contents behind:
  *   calls that overlap in time on one GPU (concurrent streams, threads) race

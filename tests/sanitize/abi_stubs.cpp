@@ -12,10 +12,12 @@ hipError_t prefill_dispatch(const FwdArgs&, const ScanArgs&, int, int, int, int,
   return hipSuccess;
 }
 hipError_t scan_dispatch(const ScanArgs&, hipStream_t) { return hipSuccess; }
-bool perf_fused_supported(int D, int DF, int dtype, bool causal, bool decay) {
-  return D == 64 && dtype == 1 && causal && !decay && (DF == 64 || DF == 128 || DF == 256);
+bool perf_fused_supported(int D, int DF, int dtype, bool decay) {
+  return D == 64 && dtype == 1 && !decay && (DF == 64 || DF == 128 || DF == 256);
 }
-hipError_t perf_fused_dispatch(const FwdArgs&, const ScanArgs&, int, hipStream_t, hipEvent_t*) { return hipSuccess; }
+hipError_t perf_fused_dispatch(const FwdArgs&, const ScanArgs&, int, bool, hipStream_t, hipEvent_t*) {
+  return hipSuccess;
+}
 hipError_t backward_dispatch(const FwdArgs&, const ScanArgs&, const BwdArgs&, const ScanArgs&, int, int, int, bool,
                              hipStream_t) {
   return hipSuccess;

@@ -100,6 +100,30 @@ def test_workspace_size_plan():
     assert b // st(128) == a // st(64)
 
 
+def test_workspace_size_by_dtype():
+    """Random features at d = 64 in bf16 (causal or not) project inside the
+    chunked passes: their exact workspace is the segment states alone; fp32,
+    and the other head dimensions, also hold phi(q) and phi(k) ([B][H][N][m]
+    fp32 each). The dtype-free size covers both element types."""
+    B, H, N = 1, 2, 64 * 40 - 17
+    for d, m in ((64, 256), (64, 64), (32, 128), (128, 64)):
+        fm = la_feature_map(la.LA_PERFORMER, m, FAKE)
+        for c in (1, 0):
+            f32 = lib.la_forward_workspace_size_dt(B, H, N, d, ctypes.byref(fm), c, la.LA_F32)
+            bf = lib.la_forward_workspace_size_dt(B, H, N, d, ctypes.byref(fm), c, la.LA_BF16)
+            anyt = lib.la_forward_workspace_size(B, H, N, d, ctypes.byref(fm), c)
+            phi = 2 * ((B * H * N * m * 4 + 255) // 256 * 256)
+            assert anyt == max(f32, bf)
+            if d == 64:
+                assert f32 - bf == phi, (d, m, c)
+                assert bf % ((m * d + m) * 4) == 0     # segment states only
+            else:
+                assert f32 == bf and f32 > phi
+    elu = lib.la_forward_workspace_size_dt(1, 16, 65536, 128, ctypes.byref(ELU), 1, la.LA_BF16)
+    assert elu == lib.la_forward_workspace_size(1, 16, 65536, 128, ctypes.byref(ELU), 1) > 0
+    assert lib.la_forward_workspace_size_dt(1, 16, 65536, 128, ctypes.byref(ELU), 1, 7) == 0
+
+
 def test_decode_rejects_bad_arguments():
     dec = lambda **kw: lib.la_decode_step(kw.get("S", FAKE), kw.get("z", FAKE + 0x1000000),
                                           kw.get("q", FAKE + 0x2000000), kw.get("k", FAKE + 0x3000000),

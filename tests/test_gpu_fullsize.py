@@ -183,20 +183,21 @@ def test_full_noncausal_b1h16n65536d128_sampled():
         assert e <= TOL["bf16"]
 
 
-def test_full_performer_b2h8n16384d64m256_sampled():
+@pytest.mark.parametrize("causal", [True, False])
+def test_full_performer_b2h8n16384d64m256_sampled(causal):
     Wl = la_inputs.WORKLOADS["performer_b2h8n16384d64m256"]
     B, H, N, d, m = Wl["B"], Wl["H"], Wl["N"], Wl["d"], Wl["m"]
-    log(f"case full random-feature prefill B{B} H{H} N{N} d{d} m{m} bf16 causal (sampled rows)")
+    log(f"case full random-feature prefill B{B} H{H} N{N} d{d} m{m} bf16 causal={causal} (sampled rows)")
     q, k, v = la_inputs.gaussian_qkv(B, H, N, d, seed=Wl["seed"], scale=Wl["scale"], bf16=True)
     Wm = la_inputs.performer_W(m, d, Wl["w_seed"], bf16=True)
     y, S, z = la.la_forward(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), feature_map="performer",
-                            W=torch.from_numpy(Wm).cuda(), causal=True, return_state=True)
+                            W=torch.from_numpy(Wm).cuda(), causal=causal, return_state=True)
     torch.cuda.synchronize()
     rows = _rows(N, _segment_tokens(B * H, N), seed=5)
     yh = to_host(y[:, :, rows])
     Wr = Wm.astype(np.float64)
     for b, h in ((0, 0), (0, 5), (1, 7)):
-        ref = O.attention(q[b, h], k[b, h], v[b, h], "performer", W=Wr, causal=True, rows=rows)
+        ref = O.attention(q[b, h], k[b, h], v[b, h], "performer", W=Wr, causal=causal, rows=rows)
         e = rel_err(yh[b, h], ref)
         Sr, zr = O.final_state(k[b, h], v[b, h], "performer", W=Wr)
         eS = rel_err(to_host(S[b, h]), Sr)

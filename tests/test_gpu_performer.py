@@ -159,23 +159,29 @@ def test_performer_unsupported_pair_rejected():
         la.la_forward(x, x.clone(), x.clone(), feature_map="performer", W=tW)
 
 
-def test_performer_fused_needs_states_only():
-    """d = 64, bf16, causal: the projection runs inside the chunked passes, so a
-    workspace far below la_forward_workspace_size() (which also covers the
-    two-stage path's phi(q), phi(k)) is enough; fp32 still needs all of it."""
-    log("case performer fused path, small workspace")
+@pytest.mark.parametrize("causal", [True, False])
+def test_performer_fused_needs_states_only(causal):
+    """d = 64, bf16, causal or not: the projection runs inside the chunked
+    passes, so the exact bf16 workspace (la_forward_workspace_size with
+    dtype) holds the segment states only, far below the fp32 figure, which
+    also holds phi(q) and phi(k); fp32 inputs are rejected with it."""
+    log(f"case performer fused path, states-only workspace, causal={causal}")
     d, m, N = 64, 256, 64 * 40 - 17
     q, k, v = qkv(1, 2, N, d, 123, "bf16", 1.0)
     tW, Wref = _W(m, d, 124, "bf16")
-    full = la.la_forward_workspace_size(1, 2, N, d, feature_map="performer", W=tW)
-    ws = torch.empty(full // 4, dtype=torch.uint8, device="cuda")
+    need = la.la_forward_workspace_size(1, 2, N, d, feature_map="performer", W=tW, causal=causal,
+                                        dtype=torch.bfloat16)
+    full = la.la_forward_workspace_size(1, 2, N, d, feature_map="performer", W=tW, causal=causal,
+                                        dtype=torch.float32)
+    assert 0 < need and need * 4 < full
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     y = la.la_forward(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), feature_map="performer", W=tW,
-                      workspace=ws)
+                      workspace=ws, causal=causal)
     torch.cuda.synchronize()
-    ref = O.attention(q, k, v, "performer", W=Wref, causal=True)
+    ref = O.attention(q, k, v, "performer", W=Wref, causal=causal)
     err = rel_err(to_host(y), ref)
     log(f"  rel err {err:.3e}")
     assert err <= TOL["bf16"], err
     with pytest.raises(ValueError):  # LA_ERR_WORKSPACE
         la.la_forward(to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32"), feature_map="performer", W=tW,
-                      workspace=ws)
+                      workspace=ws, causal=causal)
