@@ -41,8 +41,7 @@ struct PfL {
   static constexpr int RBV = kPD * 2;      // v and W rows, bf16
   static constexpr int NT = DF / 64;       // S tiles per wave (m/2 features)
   static constexpr int NFB = DF / 32;      // 32-feature blocks
-  static constexpr int NG = DF / 4;        // column-sum groups of 4 features
-  static_assert(NT >= 1 && NG <= 256, "geometry");
+  static_assert(NT >= 1, "geometry");
 };
 
 // W (fp32 [DF][64], bf16-representable values) -> LDS rows in bf16
@@ -67,24 +66,6 @@ __device__ __forceinline__ void pf_load_x(u32x4 (&xr)[4], __amdgpu_buffer_rsrc_t
   const int off = (row0 + (l & 31)) * kPD * 2 + 16 * (l >> 5);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) xr[kb] = buf_load16(r, off + 32 * kb);
-}
-
-// v of one chunk: 512 / NTH 16-byte pieces per thread (rows p / 8, bytes 16 (p % 8))
-template <int NTH>
-__device__ __forceinline__ void pf_load_v(u32x4 (&vr)[512 / NTH], __amdgpu_buffer_rsrc_t r) {
-#pragma unroll
-  for (int i = 0; i < 512 / NTH; ++i) {
-    const int p = threadIdx.x + NTH * i;
-    vr[i] = buf_load16_nt(r, (p >> 3) * kPD * 2 + 16 * (p & 7));
-  }
-}
-template <int NTH>
-__device__ __forceinline__ void pf_store_v(const u32x4 (&vr)[512 / NTH], uint8_t* sV) {
-#pragma unroll
-  for (int i = 0; i < 512 / NTH; ++i) {
-    const int p = threadIdx.x + NTH * i;
-    *reinterpret_cast<u32x4*>(sV + tile_off<kPD * 2>(p >> 3, 16 * (p & 7))) = vr[i];
-  }
 }
 
 // B_row of the lane's row: log2(e) d^(-1/2) |x|^2 / 2 + log2(m) / 2
@@ -130,23 +111,6 @@ __device__ __forceinline__ void pf_phi_store(const f32x16& u, float b, bool zero
   }
 }
 
-// column sums of rows [sl * SLR, sl * SLR + SLR) of a phi tile for features
-// [4 grp, 4 grp + 4), added into cs; NTH threads, NTH / (DF / 4) row slices
-template <int DF, int NTH>
-__device__ __forceinline__ void pf_colsum(const uint8_t* tile, float (&cs)[4]) {
-  using L = PfL<DF>;
-  constexpr int SLR = 64 / (NTH / L::NG);
-  const int grp = threadIdx.x % L::NG, sl = threadIdx.x / L::NG;
-#pragma unroll
-  for (int r = 0; r < SLR; ++r) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(tile + tile_off<L::RBF>(sl * SLR + r, grp * 8));
-    cs[0] += __uint_as_float(v[0] << 16);
-    cs[1] += __uint_as_float(v[0] & 0xffff0000u);
-    cs[2] += __uint_as_float(v[1] << 16);
-    cs[3] += __uint_as_float(v[1] & 0xffff0000u);
-  }
-}
-
 // NT accumulator tiles of S held by one wave: element r of tile t is
 // S[f0 + 32 t + 8 (r / 4) + 4 (l / 32) + r % 4][32 cb + l % 32]
 template <int NT>
@@ -183,53 +147,45 @@ __device__ __forceinline__ void pf_store_S(const f32x16 (&st)[NT], float* Sp, in
     }
 }
 
-// S[f0 .., 32 cb ..] += phi(K)^T V over the chunk's 64 rows
-template <int DF, int NT>
-__device__ __forceinline__ void pf_update_S(f32x16 (&st)[NT], const uint8_t* sK, const uint8_t* sV, int f0, int cb) {
-  using L = PfL<DF>;
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    // one k-block at a time: keeps the operand fragments in flight (and the
-    // registers they take) bounded
-    __builtin_amdgcn_sched_barrier(0);
-    const bf16x8 vf = B16::template load_cols<L::RBV>(sV, 16 * kb, 32 * cb);
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      B16::mma(st[t], B16::template load_cols<L::RBF>(sK, 16 * kb, f0 + 32 * t), vf);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // ---------------------------------------------------------------------------
-// State pass: grid (BH, segments - 1), NW waves (8 for m >= 128, else 4).
-// Wave w maps rows [32 (w & 1), +32) of the chunk's k for feature slice
-// w >> 1 (m / (NW / 2) features) and holds S[slice features][32 (w & 1), +32).
+// State pass: grid (BH, segments to sum), NW waves (8 for m >= 128, else 4).
+// Wave w takes rows [32 (w & 1), +32) of every chunk and the feature slice
+// w >> 1 (FS = m / (NW / 2) features), with the slice's W rows in registers.
+// It projects U = X W^T: the accumulator holds the slice's features on lanes
+// and the wave's 32 rows on registers, so phi = 2^(A u - B_row) is directly
+// the A operand of S[slice][:] += phi^T V; v is staged in LDS with its rows
+// in the order the accumulator registers hold them (ro_pos on the row
+// index), and z is the sum of the registers. The two waves of a slice (row
+// halves) add their sums through LDS at the end. One barrier per chunk: the
+// v tile is double-buffered.
 // ---------------------------------------------------------------------------
 template <int DF, int NW>
 struct PsL {
-  using L = PfL<DF>;
   static constexpr int NTH = 64 * NW;
   static constexpr int FS = DF / (NW / 2);   // features per slice
-  static constexpr int NTS = FS / 32;        // S tiles (and projected blocks) per wave
-  static constexpr int NSL = NTH / L::NG;    // column-sum row slices
-  static constexpr int K_OFF = DF * L::RBV;
-  static constexpr int V_OFF = K_OFF + 64 * L::RBF;
-  static constexpr int ZP_OFF = V_OFF + 64 * L::RBV;
-  static constexpr int BYTES = ZP_OFF + NSL * DF * 4;
+  static constexpr int NTS = FS / 32;        // 32-feature tiles per wave
+  static constexpr int NV = 512 / NTH;       // 16-byte pieces of a v tile per thread
+  static constexpr int VT = 64 * kPD * 2;    // v tile bytes (bf16)
+  static constexpr int B_OFF = 2 * VT;       // row biases, [NW][32] fp32
+  static constexpr int PW = NTS * 2 * 16 * 64 + NTS * 64;  // one wave's partial S and z (fp32)
+  static constexpr int P_OFF = B_OFF + NW * 32 * 4;
+  static constexpr int BYTES = P_OFF + (NW / 2) * PW * 4;
   static_assert(NTS >= 1 && FS % 32 == 0, "feature slices of whole 32-feature blocks");
-  static_assert(BYTES <= 80 * 1024, "two blocks per compute unit");
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
+
+// LDS row (or position) of row (or feature) f in tiles whose 16-row blocks
+// follow the register order of an MFMA accumulator: bits 2 and 3 swapped.
+// Lane half h of a 32x32 accumulator holds, in registers 8 kb2 .. 8 kb2 + 7,
+// the rows 16 kb2 + {4h .. 4h + 3, 8 + 4h .. 8 + 4h + 3}, which this order
+// puts at 16 kb2 + 8h .. 16 kb2 + 8h + 7. The map is its own inverse.
+__device__ __forceinline__ int ro_pos(int f) { return (f & ~12) | ((f & 4) << 1) | ((f & 8) >> 1); }
 
 template <int DF, int NW>
 __global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
-  using L = PfL<DF>;
   using Q = PsL<DF, NW>;
   constexpr int NTH = Q::NTH;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Q::BYTES];
-  uint8_t* sW = smem;
-  uint8_t* sK = smem + Q::K_OFF;
-  uint8_t* sV = smem + Q::V_OFF;
-  float* zp = reinterpret_cast<float*>(smem + Q::ZP_OFF);
   const int bh = blockIdx.x, seg = blockIdx.y;
   const int c0 = seg * a.chunks_per_seg_state;
   const int n = max(0, min(c0 + a.chunks_per_seg_state, a.nchunks) - c0);
@@ -237,10 +193,11 @@ __global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
   const __bf16* k = static_cast<const __bf16*>(a.k);
   const __bf16* v = static_cast<const __bf16*>(a.v);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int l = threadIdx.x & 63, li = l & 31;
-  const int rb = w & 1, sl = w >> 1;  // rows [32 rb, +32); feature slice [sl FS, +FS)
-  const int cb = w & 1;               // S columns [32 cb, +32)
+  const int l = threadIdx.x & 63, h = l >> 5, li = l & 31;
+  const int rb = w & 1, sl = w >> 1;  // rows [32 rb, +32); features [f0, f0 + FS)
+  const int f0 = sl * Q::FS;
   const float bm = 0.5f * __log2f((float)DF);
+  float* sb = reinterpret_cast<float*>(smem + Q::B_OFF) + 32 * w;
 
   // chunk m of the segment (zero-size descriptors past it)
   auto rsrc = [&](const __bf16* p, int m) {
@@ -248,62 +205,144 @@ __global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
     const int valid = m < n ? min(64, a.N - 64 * c) : 0;
     return make_rsrc(p + (base + 64LL * min(c, a.nchunks - 1)) * kPD, (unsigned)(valid * kPD * 2));
   };
+  // the slice's W rows as MFMA B operands: lane = feature f0 + 32 t + li,
+  // dimensions 16 kb + 8 h .. + 7, bf16
+  bf16x8 Wf[Q::NTS][4];
+#pragma unroll
+  for (int t = 0; t < Q::NTS; ++t)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const float* src = a.W + (f0 + 32 * t + li) * kPD + 16 * kb + 8 * h;
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+      const u32x4 pk = {pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]), pack_bf16x2(x1[0], x1[1]),
+                        pack_bf16x2(x1[2], x1[3])};
+      Wf[t][kb] = __builtin_bit_cast(bf16x8, pk);
+    }
+  // x rows of chunk m and the v tile of chunk m + 1
   struct KSet {
-    u32x4 x[4], v[512 / NTH];
+    u32x4 x[4], v[Q::NV];
+  };
+  auto load_v = [&](u32x4 (&vr)[Q::NV], int m) {
+#pragma unroll
+    for (int i = 0; i < Q::NV; ++i) {
+      const int p = threadIdx.x + NTH * i;
+      vr[i] = buf_load16_nt(rsrc(v, m), (p >> 3) * kPD * 2 + 16 * (p & 7));
+    }
+  };
+  auto store_v = [&](const u32x4 (&vr)[Q::NV], int buf) {
+#pragma unroll
+    for (int i = 0; i < Q::NV; ++i) {
+      const int p = threadIdx.x + NTH * i;
+      *reinterpret_cast<u32x4*>(smem + buf * Q::VT + tile_off<kPD * 2>(ro_pos(p >> 3), 16 * (p & 7))) = vr[i];
+    }
   };
   auto load = [&](int m, KSet& s_) {
     pf_load_x(s_.x, rsrc(k, m), 32 * rb);
-    pf_load_v<NTH>(s_.v, rsrc(v, m));
+    load_v(s_.v, m + 1);
   };
-  pf_stage_W<DF, NTH>(a.W, sW);
-  f32x16 st[Q::NTS];
+  f32x16 st[Q::NTS][2];
+  float zs[Q::NTS];
 #pragma unroll
-  for (int t = 0; t < Q::NTS; ++t) st[t] = f32x16{};
-  float cs[4] = {0.f, 0.f, 0.f, 0.f};
-  // Iteration m maps chunk m (registers of cur) into LDS with the loads of
-  // chunk m + 1 already in flight in nxt, then adds it into S. Every
-  // iteration issues the same loads (zero size past the segment), and the
-  // iteration count is even, so that both register sets rotate whole.
+  for (int t = 0; t < Q::NTS; ++t) {
+    st[t][0] = f32x16{};
+    st[t][1] = f32x16{};
+    zs[t] = 0.f;
+  }
+  {
+    u32x4 v0[Q::NV];
+    load_v(v0, 0);
+    store_v(v0, 0);
+  }
+  KSet sa, sb2;
+  load(0, sa);
+  __syncthreads();  // v of chunk 0 staged
+
+  // Iteration m: loads x of chunk m + 1 and v of chunk m + 2 into nxt,
+  // stages v of chunk m + 1 (held in cur) into the other buffer, and adds
+  // chunk m into S and z. Every iteration issues the same loads (zero size
+  // past the segment) and the count is even, so both register sets rotate
+  // whole. (Keeping three chunks in flight with four sets measured no faster.)
   auto iter = [&](int m, KSet& cur, KSet& nxt) {
     load(m + 1, nxt);
+    store_v(cur.v, (m + 1) & 1);
     if (m < n) {
       const int valid = min(64, a.N - 64 * (c0 + m));
+      // B_row of the lane's row, then of the 16 rows its registers hold
+      // (rows past the sequence get +inf, so their phi is 0)
       const float b = pf_row_bias(cur.x, bm);
-      const bool past = 32 * rb + li >= valid;
+      if (h == 0) sb[li] = 32 * rb + li < valid ? b : __builtin_inff();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      f32x4 bq[4];
 #pragma unroll
-      for (int j = 0; j < Q::NTS; ++j) {
-        const int fb = sl * Q::NTS + j;
-        pf_phi_store<DF>(pf_project<DF>(sW, cur.x, fb), b, past, sK, 32 * rb + li, fb);
+      for (int g = 0; g < 4; ++g) bq[g] = *reinterpret_cast<const f32x4*>(sb + 8 * g + 4 * h);
+      const uint8_t* sV = smem + (m & 1) * Q::VT;
+#pragma unroll
+      for (int t = 0; t < Q::NTS; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 u = {};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) B16::mma(u, __builtin_bit_cast(bf16x8, cur.x[kb]), Wf[t][kb]);
+        float zp = 0.f;
+        bf16x8 pf[2];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * kb2 + e;
+            y[e] = __builtin_amdgcn_exp2f(kPfA * u[r] - bq[r >> 2][r & 3]);
+            zp += y[e];
+          }
+          pf[kb2] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                                                     pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])});
+        }
+        zs[t] += zp;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+            B16::mma(st[t][cb], pf[kb2], B16::template load_cols<kPD * 2>(sV, 32 * rb + 16 * kb2, 32 * cb));
       }
-      pf_store_v<NTH>(cur.v, sV);
-    }
-    __syncthreads();
-    if (m < n) {
-      pf_update_S<DF, Q::NTS>(st, sK, sV, sl * Q::FS, cb);
-      pf_colsum<DF, NTH>(sK, cs);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
   };
-  KSet sa, sb;
-  load(0, sa);
-  __syncthreads();  // W staged
   for (int m = 0; m < n; m += 2) {
-    iter(m, sa, sb);
-    iter(m + 1, sb, sa);
+    iter(m, sa, sb2);
+    iter(m + 1, sb2, sa);
   }
 
-  float* out = a.ws + ((long long)bh * a.ws_slots + seg) * a.state_elems;
-  pf_store_S<Q::NTS>(st, out, sl * Q::FS, cb);
-  {
-    const int grp = threadIdx.x % L::NG, zs = threadIdx.x / L::NG;
-    *reinterpret_cast<f32x4*>(zp + zs * DF + 4 * grp) = f32x4{cs[0], cs[1], cs[2], cs[3]};
+  // the upper row half hands its sums to the lower one
+#pragma unroll
+  for (int t = 0; t < Q::NTS; ++t) zs[t] += xor32(zs[t]);
+  float* P = reinterpret_cast<float*>(smem + Q::P_OFF) + sl * Q::PW;
+  if (rb == 1) {
+#pragma unroll
+    for (int t = 0; t < Q::NTS; ++t) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) P[((t * 2 + cb) * 16 + r) * 64 + l] = st[t][cb][r];
+      P[Q::NTS * 2 * 16 * 64 + t * 64 + l] = zs[t];
+    }
   }
   __syncthreads();
-  if (threadIdx.x < DF) {
-    float s = 0.f;
+  if (rb == 0) {
+    float* out = a.ws + ((long long)bh * a.ws_slots + seg) * a.state_elems;
 #pragma unroll
-    for (int zs = 0; zs < Q::NSL; ++zs) s += zp[zs * DF + threadIdx.x];
-    out[DF * kPD + threadIdx.x] = s;
+    for (int t = 0; t < Q::NTS; ++t) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[t][cb][r] += P[((t * 2 + cb) * 16 + r) * 64 + l];
+        pf_store_S<1>(*reinterpret_cast<const f32x16(*)[1]>(&st[t][cb]), out, f0 + 32 * t, cb);
+      }
+      const float z = zs[t] + P[Q::NTS * 2 * 16 * 64 + t * 64 + l];
+      if (h == 0) out[DF * kPD + f0 + 32 * t + li] = z;
+    }
   }
 }
 
@@ -658,13 +697,6 @@ struct RoL {
 };
 constexpr int kRoWaves = 8;
 
-// LDS position of feature f within S^T and z rows: bits 2 and 3 swapped. Lane
-// half h of a U^T accumulator holds, in registers 8 kb2 .. 8 kb2 + 7, the
-// features 16 kb2 + {4h .. 4h + 3, 8 + 4h .. 8 + 4h + 3} of its 32-feature
-// block, which this order puts at positions 16 kb2 + 8h .. 16 kb2 + 8h + 7.
-// The map is its own inverse.
-__device__ __forceinline__ int ro_pos(int f) { return (f & ~12) | ((f & 4) << 1) | ((f & 8) >> 1); }
-
 template <int DF>
 __global__ __launch_bounds__(64 * kRoWaves) void pf_readout_kernel(FwdArgs a) {
   using R = RoL<DF>;
@@ -774,11 +806,13 @@ __global__ __launch_bounds__(64 * kRoWaves) void pf_readout_kernel(FwdArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
+  auto step = [&](int it, const XSet& cur, XSet& nxt) {
+    load(it + 1, nxt);
+    if (it < cnt) compute(w + kRoWaves * it, cur);
+  };
   for (int it = 0; it < cnt; it += 2) {
-    load(it + 1, xb);
-    compute(w + kRoWaves * it, xa);
-    load(it + 2, xa);
-    if (it + 1 < cnt) compute(w + kRoWaves * (it + 1), xb);
+    step(it, xa, xb);
+    step(it + 1, xb, xa);
   }
 }
 
