@@ -385,7 +385,28 @@ def main():
                          "roof_us": round(t_roof * 1e6, 2), "frac_roof": round(t_roof / fwall, 4)},
         }
         log(f"performer: {fwall*1e6:.1f} us/call ({t_roof / fwall:.1%} of the roof)")
-        del fq, fk, fv, fW, fout, fws
+        # the non-causal form on the same inputs: the state pass over every
+        # segment, the total by the scan, then the read-out phi(q).S / phi(q).z
+        fws_nc = torch.empty(max(la.la_forward_workspace_size(Bf, Hf, Nf, df, feature_map="performer", W=fW,
+                                                              causal=False, dtype=torch.bfloat16), 256),
+                             dtype=torch.uint8, device=dev)
+
+        def ffwd_nc(i):
+            la.la_forward(fq, fk, fv, feature_map="performer", W=fW, causal=False, normalize=True, out=fout,
+                          workspace=fws_nc)
+
+        fwall_nc = time_calls(ffwd_nc, 40, args.performer_steps)
+        # k, v read for the sums, q read and out written for the read-out;
+        # projections of k and q, state update and read-out (2 m d FLOP each)
+        nc_flops = f_ht * 8 * mf * df
+        nc_roof = max(f_bytes / (HBM_PEAK_GBS * 1e9), nc_flops / (BF16_MFMA_PEAK_TFLOPS * 1e12))
+        perf["non_causal"] = {
+            "us_per_call": round(fwall_nc * 1e6, 2), "value": Bf * Nf / fwall_nc, "unit": "tokens/s",
+            "workspace_bytes": int(fws_nc.numel()),
+            "whole_op": {"bytes": f_bytes, "flops": nc_flops, "achieved_gbs": round(f_bytes / fwall_nc / 1e9, 1),
+                         "roof_us": round(nc_roof * 1e6, 2), "frac_roof": round(nc_roof / fwall_nc, 4)}}
+        log(f"performer, non-causal: {fwall_nc*1e6:.1f} us/call ({nc_roof / fwall_nc:.1%} of the roof)")
+        del fq, fk, fv, fW, fout, fws, fws_nc
         torch.cuda.empty_cache()
 
     # ---------------- degree-2 polynomial map (d' = 1 + d + d^2) ----------------
