@@ -136,7 +136,12 @@ template <int RB>
 __device__ __forceinline__ int swz(int row) {
   if constexpr (RB <= 64) return (row >> 2) & 3;
   else if constexpr (RB == 128) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-  else return ((row & 3) << 2) | ((row >> 2) & 3);
+  else if constexpr (RB == 256) return ((row & 3) << 2) | ((row >> 2) & 3);
+  // rows of 32 or more units: row bit 4 also picks the upper half of 32
+  // units, so that the 32 rows of one MFMA tile read at one column land in
+  // 32 different units (the transposed reads, 4 rows within a 16-row block,
+  // see the same permutation as above)
+  else return ((row & 3) << 2) | ((row >> 2) & 3) | (row & 16);
 }
 
 template <int RB>
