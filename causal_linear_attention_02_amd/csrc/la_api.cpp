@@ -209,7 +209,7 @@ size_t la_forward_workspace_size_dt(int B, int H, int N, int d, const la_feature
   if (dfeat <= 0) return 0;
   if (feature_map->kind == LA_POLY2) return poly_ws_bytes((long long)B * H, N, d);
   const bool mapped = feature_map->kind == LA_PERFORMER;
-  const bool fused = mapped && la::perf_fused_supported(d, dfeat, dtype, false);
+  const bool fused = mapped && la::perf_fused_supported(d, dfeat, dtype, causal != 0, false);
   return make_plan((long long)B * H, N, d, dfeat, causal != 0, mapped && !fused).ws_bytes;
 }
 
@@ -323,9 +323,10 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
         overlaps(z_out, z_bytes, feature_map->W, wb))
       return LA_ERR_INVALID_ARG;
   }
-  // random features at d = 64 in bf16, causal or not: the projection runs
-  // inside the chunked passes and the workspace holds segment states only
-  const bool fused = mapped && la::perf_fused_supported(d, dfeat, dtype, gamma != nullptr);
+  // random features in bf16 (non-causal, or causal at d = 64): the
+  // projection runs inside the chunked passes and the workspace holds
+  // segment states only
+  const bool fused = mapped && la::perf_fused_supported(d, dfeat, dtype, causal != 0, gamma != nullptr);
   const Plan p = make_plan(BH, N, d, dfeat, causal != 0, mapped && !fused);
   if (static_ws) {
     if (p.ws_bytes > LA_STATIC_SCRATCH_BYTES) return LA_ERR_WORKSPACE;
@@ -432,7 +433,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
     s.S_out = S_out;
     s.z_out = z_out;
   }
-  if (fused) return status_from_hip(la::perf_fused_dispatch(a, s, dfeat, causal != 0, stream, events));
+  if (fused) return status_from_hip(la::perf_fused_dispatch(a, s, d, dfeat, causal != 0, stream, events));
   const int kfm = feature_map->kind == LA_ELU1 ? la::kElu1 : la::kIdentity;  // mapped features: identity inside
   return status_from_hip(la::prefill_dispatch(a, s, d, dfeat, kfm, dtype, causal != 0, gamma != nullptr, stream,
                                               events));

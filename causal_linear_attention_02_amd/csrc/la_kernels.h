@@ -150,11 +150,12 @@ struct FmapArgs {
 hipError_t prefill_dispatch(const FwdArgs& a, const ScanArgs& s, int D, int DF, int fmap, int dtype, bool causal,
                             bool decay, hipStream_t st, hipEvent_t* ev);
 hipError_t scan_dispatch(const ScanArgs& s, hipStream_t st);
-// random features with the projection fused into the chunked passes
-// (d = 64, bf16, m in {64, 128, 256}, causal or not): state pass, carry scan,
-// output pass (causal) or read-out against the total (non-causal)
-bool perf_fused_supported(int D, int DF, int dtype, bool decay);
-hipError_t perf_fused_dispatch(const FwdArgs& a, const ScanArgs& s, int DF, bool causal, hipStream_t st,
+// random features with the projection fused into the chunked passes (bf16):
+// state pass, carry scan, then the output pass (causal, d = 64, m in
+// {64, 128, 256}) or the read-out against the total (non-causal, every
+// supported (d, m) pair)
+bool perf_fused_supported(int D, int DF, int dtype, bool causal, bool decay);
+hipError_t perf_fused_dispatch(const FwdArgs& a, const ScanArgs& s, int D, int DF, bool causal, hipStream_t st,
                                hipEvent_t* ev);
 hipError_t backward_dispatch(const FwdArgs& fa, const ScanArgs& fs, const BwdArgs& b, const ScanArgs& rs, int D,
                              int fmap, int dtype, bool decay, hipStream_t st);

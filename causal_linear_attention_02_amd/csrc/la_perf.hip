@@ -111,6 +111,74 @@ __device__ __forceinline__ void pf_phi_store(const f32x16& u, float b, bool zero
   }
 }
 
+// ---------------------------------------------------------------------------
+// Head dimension D of the state pass and the non-causal read-out (32, 64 or
+// 128): a row of D bf16 values is D / 16 MFMA k-blocks, the map's scale is
+// A = log2(e) D^(-1/4) and B_row = log2(e) D^(-1/2) |x|^2 / 2 + log2(m) / 2.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Pd {
+  static_assert(D == 32 || D == 64 || D == 128, "head dimension");
+  static constexpr int NKB = D / 16;   // k-blocks of a raw row
+  static constexpr int RBV = D * 2;    // W, v and output rows (bf16 bytes)
+  static constexpr int NCB = D / 32;   // 32-column value blocks
+  static constexpr int UR = D / 8;     // 16-byte units of a row
+  static constexpr float A = 1.4426950408889634f * (D == 32 ? 0.42044820762685725f
+                                                   : D == 64 ? 0.35355339059327373f
+                                                             : 0.29730177875068026f);  // log2(e) D^(-1/4)
+  static constexpr float BS = 1.4426950408889634f * (D == 32 ? 0.088388347648318440f
+                                                    : D == 64 ? 0.0625f
+                                                              : 0.044194173824159220f);  // log2(e) D^(-1/2) / 2
+};
+
+// W (fp32 [DF][D]) -> LDS rows in bf16
+template <int DF, int D, int NTH>
+__device__ __forceinline__ void pf_stage_W_d(const float* W, uint8_t* sW) {
+  for (int p = threadIdx.x; p < DF * D / 8; p += NTH) {
+    const int row = p / Pd<D>::UR, col = 8 * (p % Pd<D>::UR);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(W + row * D + col);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(W + row * D + col + 4);
+    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    B16::template store8<Pd<D>::RBV>(sW, row, col, x);
+  }
+}
+
+// Raw rows [row0, row0 + 32) as MFMA operands: lane l gets
+// x[row0 + l % 32][16 kb + 8 (l / 32) + 0..7] for kb = 0..D/16 - 1 (rows
+// past the descriptor's range read as zero)
+template <int D>
+__device__ __forceinline__ void pf_load_x_d(u32x4 (&xr)[Pd<D>::NKB], __amdgpu_buffer_rsrc_t r, int row0) {
+  const int l = threadIdx.x & 63;
+  const int off = (row0 + (l & 31)) * D * 2 + 16 * (l >> 5);
+#pragma unroll
+  for (int kb = 0; kb < Pd<D>::NKB; ++kb) xr[kb] = buf_load16(r, off + 32 * kb);
+}
+
+// B_row of the lane's row
+template <int D>
+__device__ __forceinline__ float pf_row_bias_d(const u32x4 (&xr)[Pd<D>::NKB], float bm) {
+  float ss = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < Pd<D>::NKB; ++kb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = __uint_as_float(xr[kb][j] << 16), hi = __uint_as_float(xr[kb][j] & 0xffff0000u);
+      ss += lo * lo + hi * hi;
+    }
+  ss += xor32(ss);
+  return Pd<D>::BS * ss + bm;
+}
+
+// U^T block for features [32 fb, 32 fb + 32), W rows from LDS
+template <int D>
+__device__ __forceinline__ f32x16 pf_project_d(const uint8_t* sW, const u32x4 (&xr)[Pd<D>::NKB], int fb) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int kb = 0; kb < Pd<D>::NKB; ++kb)
+    B16::mma(acc, B16::template load_rows<Pd<D>::RBV>(sW, 32 * fb, 16 * kb), __builtin_bit_cast(bf16x8, xr[kb]));
+  return acc;
+}
+
 // NT accumulator tiles of S held by one wave: element r of tile t is
 // S[f0 + 32 t + 8 (r / 4) + 4 (l / 32) + r % 4][32 cb + l % 32]
 template <int NT>
@@ -135,7 +203,7 @@ __device__ __forceinline__ void pf_add_S(f32x16 (&st)[NT], const float* Sp, int 
       st[t][r] += Sp[(long long)f * kPD + 32 * cb + li];
     }
 }
-template <int NT>
+template <int NT, int D = kPD>
 __device__ __forceinline__ void pf_store_S(const f32x16 (&st)[NT], float* Sp, int f0, int cb) {
   const int l = threadIdx.x & 63, h = l >> 5, li = l & 31;
 #pragma unroll
@@ -143,7 +211,7 @@ __device__ __forceinline__ void pf_store_S(const f32x16 (&st)[NT], float* Sp, in
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int f = f0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-      Sp[(long long)f * kPD + 32 * cb + li] = st[t][r];
+      Sp[(long long)f * D + 32 * cb + li] = st[t][r];
     }
 }
 
@@ -159,15 +227,17 @@ __device__ __forceinline__ void pf_store_S(const f32x16 (&st)[NT], float* Sp, in
 // halves) add their sums through LDS at the end. One barrier per chunk: the
 // v tile is double-buffered.
 // ---------------------------------------------------------------------------
-template <int DF, int NW>
+template <int DF, int NW, int D>
 struct PsL {
   static constexpr int NTH = 64 * NW;
   static constexpr int FS = DF / (NW / 2);   // features per slice
   static constexpr int NTS = FS / 32;        // 32-feature tiles per wave
-  static constexpr int NV = 512 / NTH;       // 16-byte pieces of a v tile per thread
-  static constexpr int VT = 64 * kPD * 2;    // v tile bytes (bf16)
+  static constexpr int NCB = Pd<D>::NCB;     // 32-column value blocks
+  static constexpr int VP = 8 * D;           // 16-byte pieces of a v tile
+  static constexpr int NV = (VP + NTH - 1) / NTH;  // per thread
+  static constexpr int VT = 64 * D * 2;      // v tile bytes (bf16)
   static constexpr int B_OFF = 2 * VT;       // row biases, [NW][32] fp32
-  static constexpr int PW = NTS * 2 * 16 * 64 + NTS * 64;  // one wave's partial S and z (fp32)
+  static constexpr int PW = NTS * NCB * 16 * 64 + NTS * 64;  // one wave's partial S and z (fp32)
   static constexpr int P_OFF = B_OFF + NW * 32 * 4;
   static constexpr int BYTES = P_OFF + (NW / 2) * PW * 4;
   static_assert(NTS >= 1 && FS % 32 == 0, "feature slices of whole 32-feature blocks");
@@ -181,10 +251,11 @@ struct PsL {
 // puts at 16 kb2 + 8h .. 16 kb2 + 8h + 7. The map is its own inverse.
 __device__ __forceinline__ int ro_pos(int f) { return (f & ~12) | ((f & 4) << 1) | ((f & 8) >> 1); }
 
-template <int DF, int NW>
+template <int DF, int NW, int D>
 __global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
-  using Q = PsL<DF, NW>;
+  using Q = PsL<DF, NW, D>;
   constexpr int NTH = Q::NTH;
+  constexpr int NKB = Pd<D>::NKB, NCB = Q::NCB;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Q::BYTES];
   const int bh = blockIdx.x, seg = blockIdx.y;
   const int c0 = seg * a.chunks_per_seg_state;
@@ -203,50 +274,53 @@ __global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
   auto rsrc = [&](const __bf16* p, int m) {
     const int c = c0 + m;
     const int valid = m < n ? min(64, a.N - 64 * c) : 0;
-    return make_rsrc(p + (base + 64LL * min(c, a.nchunks - 1)) * kPD, (unsigned)(valid * kPD * 2));
+    return make_rsrc(p + (base + 64LL * min(c, a.nchunks - 1)) * D, (unsigned)(valid * D * 2));
   };
   // the slice's W rows as MFMA B operands: lane = feature f0 + 32 t + li,
   // dimensions 16 kb + 8 h .. + 7, bf16
-  bf16x8 Wf[Q::NTS][4];
+  bf16x8 Wf[Q::NTS][NKB];
 #pragma unroll
   for (int t = 0; t < Q::NTS; ++t)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const float* src = a.W + (f0 + 32 * t + li) * kPD + 16 * kb + 8 * h;
+    for (int kb = 0; kb < NKB; ++kb) {
+      const float* src = a.W + (f0 + 32 * t + li) * D + 16 * kb + 8 * h;
       const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
       const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
       const u32x4 pk = {pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]), pack_bf16x2(x1[0], x1[1]),
                         pack_bf16x2(x1[2], x1[3])};
       Wf[t][kb] = __builtin_bit_cast(bf16x8, pk);
     }
-  // x rows of chunk m and the v tile of chunk m + 1
+  // x rows of chunk m and the v tile of chunk m + 1; a v piece p covers row
+  // p / (D / 8), bytes 16 (p % (D / 8)); threads past the tile's pieces
+  // repeat one (the same value to the same place)
   struct KSet {
-    u32x4 x[4], v[Q::NV];
+    u32x4 x[NKB], v[Q::NV];
   };
   auto load_v = [&](u32x4 (&vr)[Q::NV], int m) {
 #pragma unroll
     for (int i = 0; i < Q::NV; ++i) {
-      const int p = threadIdx.x + NTH * i;
-      vr[i] = buf_load16_nt(rsrc(v, m), (p >> 3) * kPD * 2 + 16 * (p & 7));
+      const int p = (threadIdx.x + NTH * i) % Q::VP;
+      vr[i] = buf_load16_nt(rsrc(v, m), (p / Pd<D>::UR) * D * 2 + 16 * (p % Pd<D>::UR));
     }
   };
   auto store_v = [&](const u32x4 (&vr)[Q::NV], int buf) {
 #pragma unroll
     for (int i = 0; i < Q::NV; ++i) {
-      const int p = threadIdx.x + NTH * i;
-      *reinterpret_cast<u32x4*>(smem + buf * Q::VT + tile_off<kPD * 2>(ro_pos(p >> 3), 16 * (p & 7))) = vr[i];
+      const int p = (threadIdx.x + NTH * i) % Q::VP;
+      *reinterpret_cast<u32x4*>(smem + buf * Q::VT +
+                                tile_off<Pd<D>::RBV>(ro_pos(p / Pd<D>::UR), 16 * (p % Pd<D>::UR))) = vr[i];
     }
   };
   auto load = [&](int m, KSet& s_) {
-    pf_load_x(s_.x, rsrc(k, m), 32 * rb);
+    pf_load_x_d<D>(s_.x, rsrc(k, m), 32 * rb);
     load_v(s_.v, m + 1);
   };
-  f32x16 st[Q::NTS][2];
+  f32x16 st[Q::NTS][NCB];
   float zs[Q::NTS];
 #pragma unroll
   for (int t = 0; t < Q::NTS; ++t) {
-    st[t][0] = f32x16{};
-    st[t][1] = f32x16{};
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) st[t][cb] = f32x16{};
     zs[t] = 0.f;
   }
   {
@@ -270,7 +344,7 @@ __global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
       const int valid = min(64, a.N - 64 * (c0 + m));
       // B_row of the lane's row, then of the 16 rows its registers hold
       // (rows past the sequence get +inf, so their phi is 0)
-      const float b = pf_row_bias(cur.x, bm);
+      const float b = pf_row_bias_d<D>(cur.x, bm);
       if (h == 0) sb[li] = 32 * rb + li < valid ? b : __builtin_inff();
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -284,7 +358,7 @@ __global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         f32x16 u = {};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) B16::mma(u, __builtin_bit_cast(bf16x8, cur.x[kb]), Wf[t][kb]);
+        for (int kb = 0; kb < NKB; ++kb) B16::mma(u, __builtin_bit_cast(bf16x8, cur.x[kb]), Wf[t][kb]);
         float zp = 0.f;
         bf16x8 pf[2];
 #pragma unroll
@@ -293,7 +367,7 @@ __global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int r = 8 * kb2 + e;
-            y[e] = __builtin_amdgcn_exp2f(kPfA * u[r] - bq[r >> 2][r & 3]);
+            y[e] = __builtin_amdgcn_exp2f(Pd<D>::A * u[r] - bq[r >> 2][r & 3]);
             zp += y[e];
           }
           pf[kb2] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
@@ -303,8 +377,8 @@ __global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb)
-            B16::mma(st[t][cb], pf[kb2], B16::template load_cols<kPD * 2>(sV, 32 * rb + 16 * kb2, 32 * cb));
+          for (int cb = 0; cb < NCB; ++cb)
+            B16::mma(st[t][cb], pf[kb2], B16::template load_cols<Pd<D>::RBV>(sV, 32 * rb + 16 * kb2, 32 * cb));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -323,10 +397,10 @@ __global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
 #pragma unroll
     for (int t = 0; t < Q::NTS; ++t) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) P[((t * 2 + cb) * 16 + r) * 64 + l] = st[t][cb][r];
-      P[Q::NTS * 2 * 16 * 64 + t * 64 + l] = zs[t];
+        for (int r = 0; r < 16; ++r) P[((t * NCB + cb) * 16 + r) * 64 + l] = st[t][cb][r];
+      P[Q::NTS * NCB * 16 * 64 + t * 64 + l] = zs[t];
     }
   }
   __syncthreads();
@@ -335,13 +409,13 @@ __global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
 #pragma unroll
     for (int t = 0; t < Q::NTS; ++t) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
+      for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st[t][cb][r] += P[((t * 2 + cb) * 16 + r) * 64 + l];
-        pf_store_S<1>(*reinterpret_cast<const f32x16(*)[1]>(&st[t][cb]), out, f0 + 32 * t, cb);
+        for (int r = 0; r < 16; ++r) st[t][cb][r] += P[((t * NCB + cb) * 16 + r) * 64 + l];
+        pf_store_S<1, D>(*reinterpret_cast<const f32x16(*)[1]>(&st[t][cb]), out, f0 + 32 * t, cb);
       }
-      const float z = zs[t] + P[Q::NTS * 2 * 16 * 64 + t * 64 + l];
-      if (h == 0) out[DF * kPD + f0 + 32 * t + li] = z;
+      const float z = zs[t] + P[Q::NTS * NCB * 16 * 64 + t * 64 + l];
+      if (h == 0) out[DF * D + f0 + 32 * t + li] = z;
     }
   }
 }
@@ -683,24 +757,25 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
 // copies of S^T and z store each 16-feature block in the order the
 // accumulator registers hold it (ro_pos). phi(Q) never leaves registers.
 // ---------------------------------------------------------------------------
-template <int DF>
+template <int DF, int D>
 struct RoL {
   static constexpr int NFB = DF / 32;
-  static constexpr int RBF = DF * 2;   // S^T rows and the z row (bf16)
-  static constexpr int RBV = kPD * 2;  // W rows (bf16)
+  static constexpr int RBF = DF * 2;       // S^T rows and the z row (bf16)
+  static constexpr int RBV = Pd<D>::RBV;   // W and output rows (bf16)
   static constexpr int S_OFF = DF * RBV;
-  static constexpr int Z_OFF = S_OFF + kPD * RBF;
-  static constexpr int Y_OFF = Z_OFF + RBF;       // per-wave output tiles, 32 rows x 128 bytes
+  static constexpr int Z_OFF = S_OFF + D * RBF;
+  static constexpr int Y_OFF = Z_OFF + RBF;  // per-wave output tiles, 32 rows
   static constexpr int YT = 32 * RBV;
   static constexpr int BYTES = Y_OFF + 8 * YT;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 constexpr int kRoWaves = 8;
 
-template <int DF>
+template <int DF, int D>
 __global__ __launch_bounds__(64 * kRoWaves) void pf_readout_kernel(FwdArgs a) {
-  using R = RoL<DF>;
+  using R = RoL<DF, D>;
   constexpr int NTH = 64 * kRoWaves;
+  constexpr int NCB = Pd<D>::NCB, UR = Pd<D>::UR;
   __shared__ __attribute__((aligned(16))) uint8_t smem[R::BYTES];
   uint8_t* sW = smem;
   uint8_t* sS = smem + R::S_OFF;
@@ -715,56 +790,59 @@ __global__ __launch_bounds__(64 * kRoWaves) void pf_readout_kernel(FwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63, h = l >> 5, li = l & 31;
   const float bm = 0.5f * __log2f((float)DF);
-  const auto rq = make_rsrc(static_cast<const __bf16*>(a.q) + base * kPD, (unsigned)(nrows * kPD * 2));
-  const auto ro = make_rsrc(static_cast<__bf16*>(a.out) + base * kPD, (unsigned)(nrows * kPD * 2));
+  const auto rq = make_rsrc(static_cast<const __bf16*>(a.q) + base * D, (unsigned)(nrows * D * 2));
+  const auto ro = make_rsrc(static_cast<__bf16*>(a.out) + base * D, (unsigned)(nrows * D * 2));
   // blocks w, w + 8, ...: cnt of them; the loop runs a whole number of
   // two-set rotations and loads one block ahead (zero size past the end)
   const int cnt = nb > w ? (nb - w + kRoWaves - 1) / kRoWaves : 0;
   struct XSet {
-    u32x4 x[4];
+    u32x4 x[Pd<D>::NKB];
   };
-  auto load = [&](int it, XSet& s_) { pf_load_x(s_.x, rq, 32 * (w + kRoWaves * it)); };
+  auto load = [&](int it, XSet& s_) { pf_load_x_d<D>(s_.x, rq, 32 * (w + kRoWaves * it)); };
   XSet xa, xb;
   load(0, xa);
 
   // stage W, S^T and z (the total: slot ws_total_slot of the head)
-  pf_stage_W<DF, NTH>(a.W, sW);
+  pf_stage_W_d<DF, D, NTH>(a.W, sW);
   const float* st = a.ws + ((long long)bh * a.ws_slots + a.ws_total_slot) * a.state_elems;
-  for (int p = threadIdx.x; p < kPD * DF / 8; p += NTH) {
-    const int c = p & 63, j = p >> 6;  // S^T row c, positions 8 j .. 8 j + 7
+  for (int p = threadIdx.x; p < D * DF / 8; p += NTH) {
+    const int c = p % D, j = p / D;  // S^T row c, positions 8 j .. 8 j + 7
     float x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = st[ro_pos(8 * j + e) * kPD + c];
+    for (int e = 0; e < 8; ++e) x[e] = st[ro_pos(8 * j + e) * D + c];
     B16::template store8<R::RBF>(sS, c, 8 * j, x);
   }
   if (threadIdx.x < DF / 8) {
     float x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = st[DF * kPD + ro_pos(8 * threadIdx.x + e)];
+    for (int e = 0; e < 8; ++e) x[e] = st[DF * D + ro_pos(8 * threadIdx.x + e)];
     B16::template store8<R::RBF>(smem + R::Z_OFF, 0, 8 * threadIdx.x, x);
   }
   __syncthreads();
 
   auto compute = [&](int blk, const XSet& s_) {
-    const float b = pf_row_bias(s_.x, bm);
-    f32x16 num0 = {}, num1 = {}, dn = {};
+    const float b = pf_row_bias_d<D>(s_.x, bm);
+    f32x16 num[NCB], dn = {};
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) num[cb] = f32x16{};
     // the projection of block fb + 1 is issued before the exponentials of
     // block fb; one block at a time keeps the live accumulators bounded
-    f32x16 u = pf_project<DF>(sW, s_.x, 0);
+    f32x16 u = pf_project_d<D>(sW, s_.x, 0);
 #pragma unroll
     for (int fb = 0; fb < R::NFB; ++fb) {
       __builtin_amdgcn_sched_barrier(0);
-      const f32x16 un = fb + 1 < R::NFB ? pf_project<DF>(sW, s_.x, fb + 1) : u;
+      const f32x16 un = fb + 1 < R::NFB ? pf_project_d<D>(sW, s_.x, fb + 1) : u;
       uint32_t pk[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        pk[j] = pack_bf16x2(__builtin_amdgcn_exp2f(kPfA * u[2 * j] - b), __builtin_amdgcn_exp2f(kPfA * u[2 * j + 1] - b));
+        pk[j] = pack_bf16x2(__builtin_amdgcn_exp2f(Pd<D>::A * u[2 * j] - b),
+                            __builtin_amdgcn_exp2f(Pd<D>::A * u[2 * j + 1] - b));
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pk[4 * kb2], pk[4 * kb2 + 1], pk[4 * kb2 + 2], pk[4 * kb2 + 3]});
         const int k0 = 32 * fb + 16 * kb2;
-        B16::mma(num0, B16::template load_rows<R::RBF>(sS, 0, k0), pf);
-        B16::mma(num1, B16::template load_rows<R::RBF>(sS, 32, k0), pf);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) B16::mma(num[cb], B16::template load_rows<R::RBF>(sS, 32 * cb, k0), pf);
         B16::mma(dn, *reinterpret_cast<const bf16x8*>(sZ + (k0 + 8 * h) * 2), pf);
       }
       u = un;
@@ -775,10 +853,10 @@ __global__ __launch_bounds__(64 * kRoWaves) void pf_readout_kernel(FwdArgs a) {
     // lane: query li of the block, value columns 32 cb + 8 g + 4 h + 0..3 in
     // registers 4 g ..; one swap with the other half gives each lane 8
     // consecutive columns (16 p2 + 8 h ..), written to the wave's LDS tile and
-    // read back by rows, so that every store covers whole 128-byte rows
+    // read back by rows, so that every store covers whole rows
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const f32x16& nm = cb ? num1 : num0;
+    for (int cb = 0; cb < NCB; ++cb) {
+      const f32x16& nm = num[cb];
 #pragma unroll
       for (int p2 = 0; p2 < 2; ++p2) {
         const int r = 8 * p2;
@@ -795,10 +873,11 @@ __global__ __launch_bounds__(64 * kRoWaves) void pf_readout_kernel(FwdArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    constexpr int RPP = 64 / UR;  // rows per pass of the wave's 64 lanes
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = 8 * i + (l >> 3), u = l & 7;
-      buf_store16_nt(ro, (32 * blk + rr) * kPD * 2 + 16 * u,
+    for (int i = 0; i < 32 / RPP; ++i) {
+      const int rr = RPP * i + l / UR, u = l % UR;
+      buf_store16_nt(ro, (32 * blk + rr) * D * 2 + 16 * u,
                      *reinterpret_cast<const u32x4*>(sY + tile_off<R::RBV>(rr, 16 * u)));
     }
     // the next block's tile writes must not pass these reads
@@ -816,38 +895,48 @@ __global__ __launch_bounds__(64 * kRoWaves) void pf_readout_kernel(FwdArgs a) {
   }
 }
 
-template <int DF>
+template <int DF, int D>
 hipError_t launch_pf(const FwdArgs& a, const ScanArgs& s, bool causal, hipStream_t st, hipEvent_t* ev) {
   constexpr int NW = DF >= 128 ? 8 : 4;
   if (a.run_state_pass)
-    hipLaunchKernelGGL((pf_state_kernel<DF, NW>), dim3(a.BH, a.nseg_state), dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((pf_state_kernel<DF, NW, D>), dim3(a.BH, a.nseg_state), dim3(64 * NW), 0, st, a);
   if (ev) (void)hipEventRecord(ev[1], st);
   if (a.run_scan) {
     const hipError_t e = scan_dispatch(s, st);
     if (e != hipSuccess) return e;
   }
   if (ev) (void)hipEventRecord(ev[2], st);
-  if (causal)
-    hipLaunchKernelGGL(pf_output_kernel<DF>, dim3(a.BH, a.nseg), dim3(512), 0, st, a);
-  else
-    hipLaunchKernelGGL(pf_readout_kernel<DF>, dim3(a.BH, a.nseg), dim3(64 * kRoWaves), 0, st, a);
+  if (causal) {
+    if constexpr (D == kPD) hipLaunchKernelGGL(pf_output_kernel<DF>, dim3(a.BH, a.nseg), dim3(512), 0, st, a);
+    else return hipErrorInvalidValue;
+  } else {
+    hipLaunchKernelGGL((pf_readout_kernel<DF, D>), dim3(a.BH, a.nseg), dim3(64 * kRoWaves), 0, st, a);
+  }
   if (ev) (void)hipEventRecord(ev[3], st);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool perf_fused_supported(int D, int DF, int dtype, bool decay) {
-  return D == kPD && (DF == 64 || DF == 128 || DF == 256) && dtype == 1 && !decay;
+bool perf_fused_supported(int D, int DF, int dtype, bool causal, bool decay) {
+  if (dtype != 1 || decay) return false;
+  if (causal) return D == kPD && (DF == 64 || DF == 128 || DF == 256);
+  switch (D) {
+    case 32: return DF == 64 || DF == 128;
+    case 64: return DF == 64 || DF == 128 || DF == 256;
+    case 128: return DF == 64 || DF == 128;
+  }
+  return false;
 }
 
-hipError_t perf_fused_dispatch(const FwdArgs& a, const ScanArgs& s, int DF, bool causal, hipStream_t st,
+hipError_t perf_fused_dispatch(const FwdArgs& a, const ScanArgs& s, int D, int DF, bool causal, hipStream_t st,
                                hipEvent_t* ev) {
-  switch (DF) {
-    case 64: return launch_pf<64>(a, s, causal, st, ev);
-    case 128: return launch_pf<128>(a, s, causal, st, ev);
-    case 256: return launch_pf<256>(a, s, causal, st, ev);
-  }
+#define LA_PF_CASE(d, m) \
+  if (D == d && DF == m) return launch_pf<m, d>(a, s, causal, st, ev);
+  LA_PF_CASE(32, 64) LA_PF_CASE(32, 128)
+  LA_PF_CASE(64, 64) LA_PF_CASE(64, 128) LA_PF_CASE(64, 256)
+  LA_PF_CASE(128, 64) LA_PF_CASE(128, 128)
+#undef LA_PF_CASE
   return hipErrorInvalidValue;
 }
 

@@ -12,10 +12,13 @@ hipError_t prefill_dispatch(const FwdArgs&, const ScanArgs&, int, int, int, int,
   return hipSuccess;
 }
 hipError_t scan_dispatch(const ScanArgs&, hipStream_t) { return hipSuccess; }
-bool perf_fused_supported(int D, int DF, int dtype, bool decay) {
-  return D == 64 && dtype == 1 && !decay && (DF == 64 || DF == 128 || DF == 256);
+bool perf_fused_supported(int D, int DF, int dtype, bool causal, bool decay) {
+  if (dtype != 1 || decay) return false;
+  if (causal) return D == 64 && (DF == 64 || DF == 128 || DF == 256);
+  return (D == 32 && (DF == 64 || DF == 128)) || (D == 64 && (DF == 64 || DF == 128 || DF == 256)) ||
+         (D == 128 && (DF == 64 || DF == 128));
 }
-hipError_t perf_fused_dispatch(const FwdArgs&, const ScanArgs&, int, bool, hipStream_t, hipEvent_t*) {
+hipError_t perf_fused_dispatch(const FwdArgs&, const ScanArgs&, int, int, bool, hipStream_t, hipEvent_t*) {
   return hipSuccess;
 }
 hipError_t backward_dispatch(const FwdArgs&, const ScanArgs&, const BwdArgs&, const ScanArgs&, int, int, int, bool,

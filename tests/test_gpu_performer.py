@@ -159,14 +159,15 @@ def test_performer_unsupported_pair_rejected():
         la.la_forward(x, x.clone(), x.clone(), feature_map="performer", W=tW)
 
 
-@pytest.mark.parametrize("causal", [True, False])
-def test_performer_fused_needs_states_only(causal):
-    """d = 64, bf16, causal or not: the projection runs inside the chunked
-    passes, so the exact bf16 workspace (la_forward_workspace_size with
-    dtype) holds the segment states only, far below the fp32 figure, which
-    also holds phi(q) and phi(k); fp32 inputs are rejected with it."""
-    log(f"case performer fused path, states-only workspace, causal={causal}")
-    d, m, N = 64, 256, 64 * 40 - 17
+@pytest.mark.parametrize("d,m,causal", [(64, 256, True), (64, 256, False), (128, 128, False), (32, 64, False)])
+def test_performer_fused_needs_states_only(d, m, causal):
+    """bf16, non-causal at every head dimension and causal at d = 64: the
+    projection runs inside the chunked passes, so the exact bf16 workspace
+    (la_forward_workspace_size with dtype) holds the segment states only,
+    far below the fp32 figure, which also holds phi(q) and phi(k); fp32
+    inputs are rejected with it."""
+    log(f"case performer fused path, states-only workspace, d={d} m={m} causal={causal}")
+    N = 64 * 40 - 17
     q, k, v = qkv(1, 2, N, d, 123, "bf16", 1.0)
     tW, Wref = _W(m, d, 124, "bf16")
     need = la.la_forward_workspace_size(1, 2, N, d, feature_map="performer", W=tW, causal=causal,
