@@ -35,86 +35,10 @@ namespace {
 constexpr int kPD = 64;  // head dimension of the fused kernels
 using B16 = Ops<__bf16>;
 
-template <int DF>
-struct PfL {
-  static constexpr int RBF = DF * 2;       // phi tile rows, bf16
-  static constexpr int RBV = kPD * 2;      // v and W rows, bf16
-  static constexpr int NT = DF / 64;       // S tiles per wave (m/2 features)
-  static constexpr int NFB = DF / 32;      // 32-feature blocks
-  static_assert(NT >= 1, "geometry");
-};
-
-// W (fp32 [DF][64], bf16-representable values) -> LDS rows in bf16
-template <int DF, int NTH>
-__device__ __forceinline__ void pf_stage_W(const float* W, uint8_t* sW) {
-  for (int p = threadIdx.x; p < DF * kPD / 8; p += NTH) {
-    const int row = p >> 3, col = 8 * (p & 7);
-    const f32x4 a = *reinterpret_cast<const f32x4*>(W + row * kPD + col);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(W + row * kPD + col + 4);
-    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    B16::template store8<PfL<DF>::RBV>(sW, row, col, x);
-  }
-}
-
-// Raw rows [row0, row0 + 32) of a chunk as the B operand of U^T = W X^T:
-// lane l gets x[row0 + l % 32][16 kb + 8 (l / 32) + 0..7] for kb = 0..3.
-// Rows past the descriptor's range read as zero. Each 128-byte row is read
-// by four instructions (and by two waves), so these loads keep the default
-// cache policy: with the non-temporal hint the output pass took 13% longer.
-__device__ __forceinline__ void pf_load_x(u32x4 (&xr)[4], __amdgpu_buffer_rsrc_t r, int row0) {
-  const int l = threadIdx.x & 63;
-  const int off = (row0 + (l & 31)) * kPD * 2 + 16 * (l >> 5);
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) xr[kb] = buf_load16(r, off + 32 * kb);
-}
-
-// B_row of the lane's row: log2(e) d^(-1/2) |x|^2 / 2 + log2(m) / 2
-__device__ __forceinline__ float pf_row_bias(const u32x4 (&xr)[4], float bm) {
-  float ss = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float lo = __uint_as_float(xr[kb][j] << 16), hi = __uint_as_float(xr[kb][j] & 0xffff0000u);
-      ss += lo * lo + hi * hi;
-    }
-  ss += xor32(ss);
-  return 1.4426950408889634f * 0.0625f * ss + bm;  // d^(-1/2) / 2 = 1/16 at d = 64
-}
-
-// U^T block for features [32 fb, 32 fb + 32): lane holds the lane's row and
-// features 32 fb + 8 g + 4 (l / 32) + i in element 4 g + i
-template <int DF>
-__device__ __forceinline__ f32x16 pf_project(const uint8_t* sW, const u32x4 (&xr)[4], int fb) {
-  f32x16 acc = {};
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-    B16::mma(acc, B16::template load_rows<PfL<DF>::RBV>(sW, 32 * fb, 16 * kb), __builtin_bit_cast(bf16x8, xr[kb]));
-  return acc;
-}
-
-constexpr float kPfA = 1.4426950408889634f * 0.35355339059327373f;  // log2(e) * 64^(-1/4)
-
-// phi of one projected block -> LDS tile row `row` (bf16); zero: the row is
-// past the end of the sequence and gets phi = 0
-template <int DF>
-__device__ __forceinline__ void pf_phi_store(const f32x16& u, float b, bool zero, uint8_t* tile, int row, int fb) {
-  const int h = (threadIdx.x >> 5) & 1;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int f = 32 * fb + 8 * g + 4 * h;
-    float y[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) y[j] = zero ? 0.f : __builtin_amdgcn_exp2f(kPfA * u[4 * g + j] - b);
-    *reinterpret_cast<u32x2*>(tile + tile_off<PfL<DF>::RBF>(row, f * 2)) =
-        u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Head dimension D of the state pass and the non-causal read-out (32, 64 or
-// 128): a row of D bf16 values is D / 16 MFMA k-blocks, the map's scale is
-// A = log2(e) D^(-1/4) and B_row = log2(e) D^(-1/2) |x|^2 / 2 + log2(m) / 2.
+// Head dimension D of the fused passes (32, 64 or 128): a row of D bf16
+// values is D / 16 MFMA k-blocks, the map's scale is A = log2(e) D^(-1/4)
+// and B_row = log2(e) D^(-1/2) |x|^2 / 2 + log2(m) / 2.
 // ---------------------------------------------------------------------------
 template <int D>
 struct Pd {
@@ -130,6 +54,22 @@ struct Pd {
                                                     : D == 64 ? 0.0625f
                                                               : 0.044194173824159220f);  // log2(e) D^(-1/2) / 2
 };
+
+// phi of one projected block -> LDS tile row `row` (bf16); zero: the row is
+// past the end of the sequence and gets phi = 0
+template <int DF, int D = kPD>
+__device__ __forceinline__ void pf_phi_store(const f32x16& u, float b, bool zero, uint8_t* tile, int row, int fb) {
+  const int h = (threadIdx.x >> 5) & 1;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int f = 32 * fb + 8 * g + 4 * h;
+    float y[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = zero ? 0.f : __builtin_amdgcn_exp2f(Pd<D>::A * u[4 * g + j] - b);
+    *reinterpret_cast<u32x2*>(tile + tile_off<DF * 2>(row, f * 2)) =
+        u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+  }
+}
 
 // W (fp32 [DF][D]) -> LDS rows in bf16
 template <int DF, int D, int NTH>
@@ -181,7 +121,7 @@ __device__ __forceinline__ f32x16 pf_project_d(const uint8_t* sW, const u32x4 (&
 
 // NT accumulator tiles of S held by one wave: element r of tile t is
 // S[f0 + 32 t + 8 (r / 4) + 4 (l / 32) + r % 4][32 cb + l % 32]
-template <int NT>
+template <int NT, int D = kPD>
 __device__ __forceinline__ void pf_load_S(f32x16 (&st)[NT], const float* Sp, int f0, int cb) {
   const int l = threadIdx.x & 63, h = l >> 5, li = l & 31;
 #pragma unroll
@@ -189,10 +129,10 @@ __device__ __forceinline__ void pf_load_S(f32x16 (&st)[NT], const float* Sp, int
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int f = f0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-      st[t][r] = Sp ? Sp[(long long)f * kPD + 32 * cb + li] : 0.f;
+      st[t][r] = Sp ? Sp[(long long)f * D + 32 * cb + li] : 0.f;
     }
 }
-template <int NT>
+template <int NT, int D = kPD>
 __device__ __forceinline__ void pf_add_S(f32x16 (&st)[NT], const float* Sp, int f0, int cb) {
   const int l = threadIdx.x & 63, h = l >> 5, li = l & 31;
 #pragma unroll
@@ -200,7 +140,7 @@ __device__ __forceinline__ void pf_add_S(f32x16 (&st)[NT], const float* Sp, int 
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int f = f0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-      st[t][r] += Sp[(long long)f * kPD + 32 * cb + li];
+      st[t][r] += Sp[(long long)f * D + 32 * cb + li];
     }
 }
 template <int NT, int D = kPD>
@@ -423,28 +363,40 @@ __global__ __launch_bounds__(64 * NW) void pf_state_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // Output pass: grid (BH, segments), 512 threads, two waves per SIMD with
 // different roles, on 32-row sub-chunks of the segment; one barrier per step.
-// In step t:
+// Head dimension D (32, 64 or 128). In step t:
 //   map waves (4..7) store the output tile of sub-chunk t - 3, map sub-chunk t
 //     (phi(Q), phi(K), v) into LDS buffer t & 1 with W held in registers, and
-//     load the raw rows of sub-chunk t + 2;
+//     load the raw rows of sub-chunk t + NSET - 1 (NSET register sets: 3, or
+//     2 at D = 128, whose rows would not fit three times);
 //   contraction waves (0..3) finish sub-chunk t - 2 and start sub-chunk t - 1.
-//     Each owns a range of features: the S tiles (and the z column) of those
-//     features and their share of every product over features, so that the
+//     Each owns a range of features and of value columns: the S tiles (and
+//     the z column) there and its share of every product over features, so that the
 //     read-out phi(Q) S, the scores phi(Q) phi(K)^T, their product with v and
 //     the denominators come out as partial sums over the feature ranges,
 //     left in LDS (double-buffered). One step later the waves of value-column
 //     block cb add the partials, normalize and write the output tile. z rides
 //     along as a column of ones in the S update.
 // ---------------------------------------------------------------------------
-template <int DF>
+template <int DF, int D>
 struct Po2 {
   static constexpr int NFB = DF / 32;                    // 32-feature blocks
   static constexpr int FBJ = NFB >= 4 ? NFB / 4 : 1;     // feature blocks mapped per map wave
   static constexpr int NMAP = NFB / FBJ;                 // map waves with feature blocks (2 or 4)
-  static constexpr int NFBW = NFB >= 4 ? NFB / 4 : 1;    // feature blocks per contraction wave
-  static constexpr int NCB = NFB >= 4 ? 2 : 1;           // value-column blocks per contraction wave
+  static constexpr int NCBT = D / 32;                    // 32-column value blocks
+  // the contraction waves split the features FS ways and the value blocks
+  // VS ways (FS * VS waves take part: 4, or 2 when there are only two
+  // (feature, value) block pairs)
+  static constexpr int FS = (NFB >= 4 && NCBT <= 2) ? 4 : 2;
+  static constexpr int VS = (NFB >= 4 && NCBT <= 2) || NCBT == 1 ? 1 : 2;
+  static constexpr int NFBW = NFB / FS;                  // feature blocks per contraction wave
+  static constexpr int NCB = NCBT / VS;                  // value-column blocks per contraction wave
+  static constexpr int NSET = D == 128 ? 2 : 3;          // register sets of the map waves' loads
+  static constexpr int NKB = Pd<D>::NKB;
+  static constexpr int UR = Pd<D>::UR;
+  static constexpr int VP = 32 * UR;                     // 16-byte pieces of a 32-row v or output tile
+  static constexpr int NVP = (VP + 255) / 256;           // per map-wave thread
   static constexpr int RBF = DF * 2;                     // phi tile rows (bf16)
-  static constexpr int RBV = kPD * 2;                    // v and output rows (bf16)
+  static constexpr int RBV = D * 2;                      // v and output rows (bf16)
   static constexpr int PHI = 32 * RBF;
   static constexpr int VT = 32 * RBV;
   static constexpr int Q_OFF = 0;                        // phi(Q) [2]
@@ -460,28 +412,24 @@ struct Po2 {
 };
 
 // contraction wave c: feature blocks [fb0, fb0 + NFBW), value blocks [cb0, cb0 + NCB);
-// den owner: the wave adds its in-chunk and carried denominators (once per feature range)
-template <int DF>
+// den owner: the wave adds its in-chunk and carried denominators (once per feature range);
+// act: the wave takes part (all four, unless there are only two block pairs)
+template <int DF, int D>
 struct Cown {
   int fb0, cb0;
-  bool den;
+  bool den, act;
   __device__ explicit Cown(int c) {
-    using P = Po2<DF>;
-    if constexpr (P::NFB >= 4) {
-      fb0 = c * P::NFBW;
-      cb0 = 0;
-      den = true;
-    } else {  // m = 64: two feature blocks, two value blocks, one tile per wave
-      fb0 = c & 1;
-      cb0 = c >> 1;
-      den = cb0 == 0;
-    }
+    using P = Po2<DF, D>;
+    act = c < P::FS * P::VS;
+    fb0 = (c % P::FS) * P::NFBW;
+    cb0 = act ? (c / P::FS) * P::NCB : 0;
+    den = act && c / P::FS == 0;
   }
 };
 
-template <int DF>
+template <int DF, int D>
 __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
-  using P = Po2<DF>;
+  using P = Po2<DF, D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[P::BYTES];
 
   const int bh = blockIdx.x, seg = blockIdx.y;
@@ -505,20 +453,25 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
   if (a.init_from_ws) {
     const float* st = a.ws + ((long long)bh * a.ws_slots + seg) * a.state_elems;
     Sinit = st;
-    zinit = st + DF * kPD;
+    zinit = st + DF * D;
   } else {
-    Sinit = a.S_in ? a.S_in + (long long)bh * DF * kPD : nullptr;
+    Sinit = a.S_in ? a.S_in + (long long)bh * DF * D : nullptr;
     zinit = a.z_in ? a.z_in + (long long)bh * DF : nullptr;
   }
   // rows [32 t, 32 t + 32) of the segment: descriptor over the valid ones
   // (none for t < 0 or past the end)
   auto rsrc = [&](const __bf16* p, int t) {
     const int valid = t < 0 ? 0 : max(0, min(32, nrows - 32 * t));
-    return make_rsrc(p + (base + 32LL * max(t, 0)) * kPD, (unsigned)(valid * kPD * 2));
+    return make_rsrc(p + (base + 32LL * max(t, 0)) * D, (unsigned)(valid * D * 2));
   };
-  // steps -2 .. tend - 1: a whole number of three-step rotations covering
-  // steps 0 .. ns + 2 (the output tile of the last sub-chunk is stored in step ns + 2)
-  const int tend = -2 + (ns + 5 + 2) / 3 * 3;
+  // steps t0 .. tend - 1 (t0 = 1 - NSET): a whole number of NSET-step
+  // rotations covering steps 0 .. ns + 2 (the output tile of the last
+  // sub-chunk is stored in step ns + 2)
+  constexpr int t0 = 1 - P::NSET;
+  const int tend = t0 + (ns + 3 - t0 + P::NSET - 1) / P::NSET * P::NSET;
+  // piece i of a thread of the map waves in a 32-row v or output tile: row
+  // pp / UR, bytes 16 (pp % UR) (threads past the tile's pieces repeat one)
+  auto vpiece = [&](int p, int i) { return (p + 256 * i) % P::VP; };
 
   if (w >= 4) {
     // ------------------------------------------------------------ map waves
@@ -527,12 +480,12 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
     const int fbm = (act ? j : 0) * P::FBJ;
     const float bm = 0.5f * __log2f((float)DF);
     // W rows of the wave's feature blocks as MFMA A operands, bf16
-    bf16x8 Wf[P::FBJ][4];
+    bf16x8 Wf[P::FBJ][P::NKB];
 #pragma unroll
     for (int f = 0; f < P::FBJ; ++f)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const float* src = a.W + (32 * (fbm + f) + li) * kPD + 16 * kb + 8 * h;
+      for (int kb = 0; kb < P::NKB; ++kb) {
+        const float* src = a.W + (32 * (fbm + f) + li) * D + 16 * kb + 8 * h;
         const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
         const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
         const u32x4 pk = {pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]), pack_bf16x2(x1[0], x1[1]),
@@ -540,33 +493,37 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
         Wf[f][kb] = __builtin_bit_cast(bf16x8, pk);
       }
     struct XSet {
-      u32x4 q[4], k[4], v;
+      u32x4 q[P::NKB], k[P::NKB], v[P::NVP];
     };
     auto load = [&](int t, XSet& x) {
       if (act) {
-        pf_load_x(x.q, rsrc(q, t), 0);
-        pf_load_x(x.k, rsrc(k, t), 0);
+        pf_load_x_d<D>(x.q, rsrc(q, t), 0);
+        pf_load_x_d<D>(x.k, rsrc(k, t), 0);
       }
-      x.v = buf_load16_nt(rsrc(v, t), (p >> 3) * kPD * 2 + 16 * (p & 7));
+#pragma unroll
+      for (int i = 0; i < P::NVP; ++i) {
+        const int pp = vpiece(p, i);
+        x.v[i] = buf_load16_nt(rsrc(v, t), (pp / P::UR) * D * 2 + 16 * (pp % P::UR));
+      }
     };
     // q and k rows of the sub-chunk together: independent MFMA and exp chains
-    auto map2 = [&](const u32x4 (&xq)[4], const u32x4 (&xk)[4], uint8_t* tq, uint8_t* tk, bool kzero) {
-      const float bq = pf_row_bias(xq, bm), bk = pf_row_bias(xk, bm);
+    auto map2 = [&](const u32x4 (&xq)[P::NKB], const u32x4 (&xk)[P::NKB], uint8_t* tq, uint8_t* tk, bool kzero) {
+      const float bq = pf_row_bias_d<D>(xq, bm), bk = pf_row_bias_d<D>(xk, bm);
 #pragma unroll
       for (int f = 0; f < P::FBJ; ++f) {
         f32x16 uq = {}, uk = {};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < P::NKB; ++kb) {
           B16::mma(uq, Wf[f][kb], __builtin_bit_cast(bf16x8, xq[kb]));
           B16::mma(uk, Wf[f][kb], __builtin_bit_cast(bf16x8, xk[kb]));
         }
-        pf_phi_store<DF>(uq, bq, false, tq, li, fbm + f);
-        pf_phi_store<DF>(uk, bk, kzero, tk, li, fbm + f);
+        pf_phi_store<DF, D>(uq, bq, false, tq, li, fbm + f);
+        pf_phi_store<DF, D>(uk, bk, kzero, tk, li, fbm + f);
       }
     };
     // Step t: the output tile of sub-chunk t - 3, then sub-chunk t (held in
-    // cur) mapped, and the rows of sub-chunk t + 2 loaded into nxt (the set
-    // sub-chunk t - 1 used). Every step issues the same loads and stores
+    // cur) mapped, and the rows of sub-chunk t + NSET - 1 loaded into nxt
+    // (the set sub-chunk t - 1 used). Every step issues the same loads and stores
     // (zero size past the end) and maps whatever it holds (buffers past the
     // end are never read), so the wait counts of the loop are the same on
     // every path and prefetches stay in flight.
@@ -574,36 +531,53 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
       const int set = t & 1;
       const int valid = max(0, min(32, nrows - 32 * t));
       const uint8_t* sY = smem + P::Y_OFF + (set ^ 1) * P::VT;
-      buf_store16_nt(rsrc(out, t - 3), (p >> 3) * kPD * 2 + 16 * (p & 7),
-                     *reinterpret_cast<const u32x4*>(sY + tile_off<P::RBV>(p >> 3, 16 * (p & 7))));
+#pragma unroll
+      for (int i = 0; i < P::NVP; ++i) {
+        const int pp = vpiece(p, i);
+        buf_store16_nt(rsrc(out, t - 3), (pp / P::UR) * D * 2 + 16 * (pp % P::UR),
+                       *reinterpret_cast<const u32x4*>(sY + tile_off<P::RBV>(pp / P::UR, 16 * (pp % P::UR))));
+      }
       if (act) map2(cur.q, cur.k, smem + P::Q_OFF + set * P::PHI, smem + P::K_OFF + set * P::PHI, li >= valid);
-      *reinterpret_cast<u32x4*>(smem + P::V_OFF + set * P::VT + tile_off<P::RBV>(p >> 3, 16 * (p & 7))) = cur.v;
-      load(t + 2, nxt);
+#pragma unroll
+      for (int i = 0; i < P::NVP; ++i) {
+        const int pp = vpiece(p, i);
+        *reinterpret_cast<u32x4*>(smem + P::V_OFF + set * P::VT + tile_off<P::RBV>(pp / P::UR, 16 * (pp % P::UR))) =
+            cur.v[i];
+      }
+      load(t + P::NSET - 1, nxt);
       __syncthreads();
     };
-    // The rotation of the three register sets starts two steps early (steps
-    // -2 and -1 only load sub-chunks 0 and 1; what they map is never read)
+    // The rotation of the register sets starts NSET - 1 steps early (those
+    // steps only load sub-chunks 0 .. NSET - 2; what they map is never read)
     // and runs whole rotations, so that the loop is entered with no loads in
     // flight and every iteration has the same memory instruction stream.
-    XSet xa = {}, xb = {}, xc = {};
     __syncthreads();  // the contraction waves have their initial state
-    for (int t = -2; t < tend; t += 3) {
-      step(t, xb, xa);
-      step(t + 1, xc, xb);
-      step(t + 2, xa, xc);
+    if constexpr (P::NSET == 3) {
+      XSet xa = {}, xb = {}, xc = {};
+      for (int t = t0; t < tend; t += 3) {
+        step(t, xb, xa);
+        step(t + 1, xc, xb);
+        step(t + 2, xa, xc);
+      }
+    } else {
+      XSet xa = {}, xb = {};
+      for (int t = t0; t < tend; t += 2) {
+        step(t, xb, xa);
+        step(t + 1, xa, xb);
+      }
     }
   } else {
     // ---------------------------------------------------- contraction waves
-    const Cown<DF> o(w);
+    const Cown<DF, D> o(w);
     f32x16 S[P::NFBW][P::NCB], Z[P::NFBW];
 #pragma unroll
     for (int f = 0; f < P::NFBW; ++f) {
 #pragma unroll
       for (int cb = 0; cb < P::NCB; ++cb) {
-        pf_load_S<1>(*reinterpret_cast<f32x16(*)[1]>(&S[f][cb]), Sinit, 32 * (o.fb0 + f), o.cb0 + cb);
+        pf_load_S<1, D>(*reinterpret_cast<f32x16(*)[1]>(&S[f][cb]), Sinit, 32 * (o.fb0 + f), o.cb0 + cb);
         if (a.init_sum_ws)
           for (int s2 = 0; s2 < seg; ++s2)
-            pf_add_S<1>(*reinterpret_cast<f32x16(*)[1]>(&S[f][cb]),
+            pf_add_S<1, D>(*reinterpret_cast<f32x16(*)[1]>(&S[f][cb]),
                         a.ws + ((long long)bh * a.ws_slots + s2) * a.state_elems, 32 * (o.fb0 + f), o.cb0 + cb);
       }
       // z of the block's features in every column of Z[f]
@@ -612,7 +586,7 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
         const int fe = 32 * (o.fb0 + f) + 8 * (r >> 2) + 4 * h + (r & 3);
         float zv = zinit ? zinit[fe] : 0.f;
         if (a.init_sum_ws)
-          for (int s2 = 0; s2 < seg; ++s2) zv += a.ws[((long long)bh * a.ws_slots + s2) * a.state_elems + DF * kPD + fe];
+          for (int s2 = 0; s2 < seg; ++s2) zv += a.ws[((long long)bh * a.ws_slots + s2) * a.state_elems + DF * D + fe];
         Z[f][r] = zv;
       }
     }
@@ -620,19 +594,19 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
     __syncthreads();
-    for (int t = -2; t < tend; ++t) {
+    for (int t = t0; t < tend; ++t) {
       // finish sub-chunk t - 2: value block cb = w adds the partials of every
       // wave that holds it, normalizes and writes the output tile
       const int sf = t - 2;
-      if (sf >= 0 && sf < ns && w < 2) {
+      if (sf >= 0 && sf < ns && w < P::NCBT) {
         const float* sP = reinterpret_cast<const float*>(smem + P::P_OFF + (sf & 1) * P::PB);
         const float* sD = reinterpret_cast<const float*>(smem + P::D_OFF + (sf & 1) * P::DBUF);
         const int cb = w;
         f32x16 y = {};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const Cown<DF> oc(c);
-          if (cb < oc.cb0 || cb >= oc.cb0 + P::NCB) continue;
+          const Cown<DF, D> oc(c);
+          if (!oc.act || cb < oc.cb0 || cb >= oc.cb0 + P::NCB) continue;
           const int slot = c * P::NCB + (cb - oc.cb0);
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
@@ -648,7 +622,7 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
           float den = 0.f;
 #pragma unroll
           for (int c = 0; c < 4; ++c)
-            if (Cown<DF>(c).den) den += sD[c * 32 + li];
+            if (Cown<DF, D>(c).den) den += sD[c * 32 + li];
           inv = 1.f / fmaxf(den, kEps);
         }
         uint8_t* sY = smem + P::Y_OFF + (sf & 1) * P::VT;
@@ -659,7 +633,7 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
       }
       // partials of sub-chunk t - 1
       const int sc = t - 1;
-      if (sc >= 0 && sc < ns) {
+      if (sc >= 0 && sc < ns && o.act) {
         const int set = sc & 1;
         float* sP = reinterpret_cast<float*>(smem + P::P_OFF + set * P::PB);
         float* sD = reinterpret_cast<float*>(smem + P::D_OFF + set * P::DBUF);
@@ -728,13 +702,13 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
       }
       __syncthreads();
     }
-    if (a.S_out && seg == a.nseg - 1) {
+    if (a.S_out && seg == a.nseg - 1 && o.act) {
 #pragma unroll
       for (int f = 0; f < P::NFBW; ++f) {
 #pragma unroll
         for (int cb = 0; cb < P::NCB; ++cb)
-          pf_store_S<1>(*reinterpret_cast<const f32x16(*)[1]>(&S[f][cb]), a.S_out + (long long)bh * DF * kPD,
-                        32 * (o.fb0 + f), o.cb0 + cb);
+          pf_store_S<1, D>(*reinterpret_cast<const f32x16(*)[1]>(&S[f][cb]), a.S_out + (long long)bh * DF * D,
+                           32 * (o.fb0 + f), o.cb0 + cb);
         if (o.den && li == 0) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
@@ -907,8 +881,7 @@ hipError_t launch_pf(const FwdArgs& a, const ScanArgs& s, bool causal, hipStream
   }
   if (ev) (void)hipEventRecord(ev[2], st);
   if (causal) {
-    if constexpr (D == kPD) hipLaunchKernelGGL(pf_output_kernel<DF>, dim3(a.BH, a.nseg), dim3(512), 0, st, a);
-    else return hipErrorInvalidValue;
+    hipLaunchKernelGGL((pf_output_kernel<DF, D>), dim3(a.BH, a.nseg), dim3(512), 0, st, a);
   } else {
     hipLaunchKernelGGL((pf_readout_kernel<DF, D>), dim3(a.BH, a.nseg), dim3(64 * kRoWaves), 0, st, a);
   }
@@ -920,7 +893,7 @@ hipError_t launch_pf(const FwdArgs& a, const ScanArgs& s, bool causal, hipStream
 
 bool perf_fused_supported(int D, int DF, int dtype, bool causal, bool decay) {
   if (dtype != 1 || decay) return false;
-  if (causal) return D == kPD && (DF == 64 || DF == 128 || DF == 256);
+  (void)causal;  // both forms are fused for every supported pair
   switch (D) {
     case 32: return DF == 64 || DF == 128;
     case 64: return DF == 64 || DF == 128 || DF == 256;

@@ -89,7 +89,7 @@ def test_performer_forward_small(d, m, dt):
             _check_forward(2, 2, N, d, m, dt, causal, True, seed=500 + N + d + m)
 
 
-@pytest.mark.parametrize("d,m", [(64, 256), (64, 128), (64, 64), (32, 128), (128, 64)])
+@pytest.mark.parametrize("d,m", PAIRS)
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_performer_forward_multisegment(d, m, dt):
     N = 64 * 40 - 17
@@ -159,10 +159,11 @@ def test_performer_unsupported_pair_rejected():
         la.la_forward(x, x.clone(), x.clone(), feature_map="performer", W=tW)
 
 
-@pytest.mark.parametrize("d,m,causal", [(64, 256, True), (64, 256, False), (128, 128, False), (32, 64, False)])
+@pytest.mark.parametrize("d,m,causal", [(64, 256, True), (64, 256, False), (128, 128, True), (128, 128, False),
+                                        (32, 64, True), (32, 64, False)])
 def test_performer_fused_needs_states_only(d, m, causal):
-    """bf16, non-causal at every head dimension and causal at d = 64: the
-    projection runs inside the chunked passes, so the exact bf16 workspace
+    """bf16, causal or not, at every head dimension: the projection runs
+    inside the chunked passes, so the exact bf16 workspace
     (la_forward_workspace_size with dtype) holds the segment states only,
     far below the fp32 figure, which also holds phi(q) and phi(k); fp32
     inputs are rejected with it."""
