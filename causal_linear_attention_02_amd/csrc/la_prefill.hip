@@ -43,13 +43,14 @@ struct Stage {
   static constexpr int RLF = DF / 8, RSF = NP / RLF, NQ = 64 / RSF;
   static constexpr int RLV = D / 8;
   static_assert(NP % RLF == 0 && 64 % RSF == 0 && NQ <= 16, "staging geometry");
-  // register sets for the loads in flight (prefetch distance NSET - 1)
-  static constexpr int NSET = NQ <= 4 ? 3 : 2;
-  // the decay variants keep one set fewer: their scaling needs registers
-  // (with a third set the decay state pass ran at half the occupancy and
-  // the decay output pass spilled more)
+  // register sets for the loads in flight. Two, for every head dimension:
+  // against three, the long-context prefill ran 1% faster at d = 128, 3-4%
+  // at d = 32 and 64, and 16% with many 4096-token sequences (B32 H32) at
+  // d = 32 and 64 (the decay variants, whose scaling needs registers, had
+  // kept two all along)
+  static constexpr int NSET = 2;
   template <bool DECAY>
-  static constexpr int nset() { return DECAY ? 2 : NSET; }
+  static constexpr int nset() { return NSET; }
 };
 
 template <int D, int DF, typename IN>
@@ -501,21 +502,9 @@ __global__ __launch_bounds__(D * 2, DECAY ? 2 : 1) void state_pass_kernel(FwdArg
     else retire<D, DF, IN, false, true>(st);
     __syncthreads();
   };
+  static_assert(NS == 2, "two register sets rotate");
   const int nround = (nch + NS - 1) / NS * NS;
-  if constexpr (NS == 3) {
-    Pref<D, DF, IN> pA, pB, pC;
-    load(pA, 0);
-    load(pB, 1);
-    load(pC, 2);
-    if (nch > 0) stage(pA, 0);
-    else retire<D, DF, IN, false, true>(pA);
-    __syncthreads();
-    for (int m = 0; m < nround; m += 3) {
-      iter(m, pA, pB);
-      iter(m + 1, pB, pC);
-      iter(m + 2, pC, pA);
-    }
-  } else {
+  {
     Pref<D, DF, IN> pA, pB;
     load(pA, 0);
     load(pB, 1);
@@ -839,14 +828,8 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
     // whole rotations of the register sets; the steps past n + LAST only
     // retire their empty loads (the consumers run as many barriers)
     // chunk c is held in the set that step c - NSET + 1 loads and step c stages
-    if constexpr (NS == 3) {
-      Pref<D, DF, IN> pA, pB, pC;
-      for (int it = IT0; it < itend; it += 3) {
-        pstep(it, pA, pC);
-        pstep(it + 1, pB, pA);
-        pstep(it + 2, pC, pB);
-      }
-    } else {
+    static_assert(NS == 2, "two register sets rotate");
+    {
       Pref<D, DF, IN> pA, pB;
       for (int it = IT0; it < itend; it += 2) {
         pstep(it, pA, pB);
