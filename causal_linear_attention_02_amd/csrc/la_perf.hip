@@ -460,8 +460,11 @@ __global__ __launch_bounds__(512) void pf_output_kernel(FwdArgs a) {
   }
   // rows [32 t, 32 t + 32) of the segment: descriptor over the valid ones
   // (none for t < 0 or past the end)
+  // (the row count goes through readfirstlane: computed as a vector med3 it
+  // would leave the descriptor in vector registers, and every load and store
+  // under it in a loop over lanes)
   auto rsrc = [&](const __bf16* p, int t) {
-    const int valid = t < 0 ? 0 : max(0, min(32, nrows - 32 * t));
+    const int valid = __builtin_amdgcn_readfirstlane(t < 0 ? 0 : max(0, min(32, nrows - 32 * t)));
     return make_rsrc(p + (base + 32LL * max(t, 0)) * D, (unsigned)(valid * D * 2));
   };
   // steps t0 .. tend - 1 (t0 = 1 - NSET): a whole number of NSET-step
