@@ -37,12 +37,16 @@ namespace la {
 // rows (D values) by RLV = D/8 threads, pieces i = 0..3 at row p/RLV + 16 i.
 // Threads with equal p % RLF share feature columns.
 // ---------------------------------------------------------------------------
-template <int D, int DF>
+// Staging geometry of NPT threads over a 64-row chunk: a q/k row is RLF
+// 16-byte pieces and the threads cover RSF rows per pass (NQ passes); a v
+// row is RLV pieces, RSV rows per pass (NV passes).
+template <int D, int DF, int NPT = 2 * D>
 struct Stage {
-  static constexpr int NP = 2 * D;
+  static constexpr int NP = NPT;
   static constexpr int RLF = DF / 8, RSF = NP / RLF, NQ = 64 / RSF;
-  static constexpr int RLV = D / 8;
-  static_assert(NP % RLF == 0 && 64 % RSF == 0 && NQ <= 16, "staging geometry");
+  static constexpr int RLV = D / 8, RSV = NP / RLV, NV = 64 / RSV;
+  static_assert(NP % RLF == 0 && 64 % RSF == 0 && NQ >= 1 && NQ <= 16, "staging geometry");
+  static_assert(NP % RLV == 0 && 64 % RSV == 0 && NV >= 1 && NV <= 16, "staging geometry");
   // register sets for the loads in flight. Two, for every head dimension:
   // against three, the long-context prefill ran 1% faster at d = 128, 3-4%
   // at d = 32 and 64, and 16% with many 4096-token sequences (B32 H32) at
@@ -53,24 +57,25 @@ struct Stage {
   static constexpr int nset() { return NSET; }
 };
 
-template <int D, int DF, typename IN>
+template <int D, int DF, typename IN, int NPT = 2 * D>
 struct Pref {
-  typename In8<IN>::raw q[Stage<D, DF>::NQ], k[Stage<D, DF>::NQ], v[4];
+  typename In8<IN>::raw q[Stage<D, DF, NPT>::NQ], k[Stage<D, DF, NPT>::NQ], v[Stage<D, DF, NPT>::NV];
 };
 
-template <int D, int DF, typename IN>
+template <int D, int DF, typename IN, int NPT = 2 * D>
 struct Voff {
   static constexpr bool kSame = DF == D;  // then feature and value pieces coincide
-  int f[Stage<D, DF>::NQ];  // byte offsets of the feature-side pieces
-  int v_[kSame ? 1 : 4];    // byte offsets of the value pieces
+  int f[Stage<D, DF, NPT>::NQ];                    // byte offsets of the feature-side pieces
+  int v_[kSame ? 1 : Stage<D, DF, NPT>::NV];       // byte offsets of the value pieces
   __device__ __forceinline__ explicit Voff(int p) {
-    using G = Stage<D, DF>;
+    using G = Stage<D, DF, NPT>;
 #pragma unroll
     for (int i = 0; i < G::NQ; ++i)
       f[i] = ((p / G::RLF + G::RSF * i) * DF + 8 * (p % G::RLF)) * (int)sizeof(IN);
     if constexpr (!kSame) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v_[i] = ((p / G::RLV + 16 * i) * D + 8 * (p % G::RLV)) * (int)sizeof(IN);
+      for (int i = 0; i < G::NV; ++i)
+        v_[i] = ((p / G::RLV + G::RSV * i) * D + 8 * (p % G::RLV)) * (int)sizeof(IN);
     }
   }
   __device__ __forceinline__ int v(int i) const {
@@ -82,10 +87,10 @@ struct Voff {
 // Loads of one chunk (rows [row_base, row_base + valid)); rows past the end
 // read as zero through the descriptor's range check. q and k rows have DF
 // elements, v rows D.
-template <int D, int DF, typename IN, bool LQ, bool LKV>
-__device__ __forceinline__ void prod_load(Pref<D, DF, IN>& pf, const Voff<D, DF, IN>& vo, const IN* q, const IN* k,
-                                          const IN* v, long long row_base, int valid) {
-  using G = Stage<D, DF>;
+template <int D, int DF, typename IN, bool LQ, bool LKV, int NPT>
+__device__ __forceinline__ void prod_load(Pref<D, DF, IN, NPT>& pf, const Voff<D, DF, IN, NPT>& vo, const IN* q,
+                                          const IN* k, const IN* v, long long row_base, int valid) {
+  using G = Stage<D, DF, NPT>;
   const unsigned fbytes = (unsigned)(valid * DF * (int)sizeof(IN));
   const unsigned vbytes = (unsigned)(valid * D * (int)sizeof(IN));
 #pragma unroll
@@ -95,7 +100,7 @@ __device__ __forceinline__ void prod_load(Pref<D, DF, IN>& pf, const Voff<D, DF,
   }
   if constexpr (LKV) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pf.v[i] = In8<IN>::bload_nt(make_rsrc(v + row_base * D, vbytes), vo.v(i));
+    for (int i = 0; i < G::NV; ++i) pf.v[i] = In8<IN>::bload_nt(make_rsrc(v + row_base * D, vbytes), vo.v(i));
   }
 }
 
@@ -111,25 +116,25 @@ template <typename R> __device__ __forceinline__ void touch(const R& r) {
     asm volatile("" ::"v"(r.b));
   }
 }
-template <int D, int DF, typename IN, bool LQ, bool LKV>
-__device__ __forceinline__ void retire(const Pref<D, DF, IN>& pf) {
+template <int D, int DF, typename IN, bool LQ, bool LKV, int NPT>
+__device__ __forceinline__ void retire(const Pref<D, DF, IN, NPT>& pf) {
 #pragma unroll
-  for (int i = 0; i < Stage<D, DF>::NQ; ++i) {
+  for (int i = 0; i < Stage<D, DF, NPT>::NQ; ++i) {
     if constexpr (LQ) touch(pf.q[i]);
     if constexpr (LKV) touch(pf.k[i]);
   }
   if constexpr (LKV) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) touch(pf.v[i]);
+    for (int i = 0; i < Stage<D, DF, NPT>::NV; ++i) touch(pf.v[i]);
   }
 }
 
 // Key rows past the end of the sequence become -inf (elu+1: phi = 0 there)
 // or 0 (pre-mapped features), so they add nothing to the scores, S or z.
 // Branch-free, so every step has the same instruction stream.
-template <int D, int DF, typename IN, int FM>
-__device__ __forceinline__ void mask_tail_keys(Pref<D, DF, IN>& pf, int p, int valid) {
-  using G = Stage<D, DF>;
+template <int D, int DF, typename IN, int FM, int NPT>
+__device__ __forceinline__ void mask_tail_keys(Pref<D, DF, IN, NPT>& pf, int p, int valid) {
+  using G = Stage<D, DF, NPT>;
   const auto fill = FM == kElu1 ? In8<IN>::neg_inf() : In8<IN>::zero();
 #pragma unroll
   for (int i = 0; i < G::NQ; ++i) {
@@ -167,10 +172,11 @@ __device__ __forceinline__ float fmap_in_stage(float x) {
 // Feature map + LDS writes for one chunk.
 // Accumulates, per piece i, dp[i] = sum_e phi(q)[i][e] * z[e] (if LQ) and the
 // column sums of phi(k) over the thread's rows in cs (if LKV).
-template <int D, int DF, typename IN, typename OP, int FM, bool LQ, bool LKV>
-__device__ __forceinline__ void prod_stage(const Pref<D, DF, IN>& pf, int p, uint8_t* sQ, uint8_t* sK, uint8_t* sV,
-                                           const float (&z)[8], float (&dp)[Stage<D, DF>::NQ], float (&cs)[8]) {
-  using G = Stage<D, DF>;
+template <int D, int DF, typename IN, typename OP, int FM, bool LQ, bool LKV, int NPT>
+__device__ __forceinline__ void prod_stage(const Pref<D, DF, IN, NPT>& pf, int p, uint8_t* sQ, uint8_t* sK,
+                                           uint8_t* sV, const float (&z)[8], float (&dp)[Stage<D, DF, NPT>::NQ],
+                                           float (&cs)[8]) {
+  using G = Stage<D, DF, NPT>;
   constexpr int RBF = DF * Ops<OP>::kBytes, RBV = D * Ops<OP>::kBytes;
   const int fcol = 8 * (p % G::RLF);
 #pragma unroll
@@ -205,7 +211,7 @@ __device__ __forceinline__ void prod_stage(const Pref<D, DF, IN>& pf, int p, uin
   }
   if constexpr (LKV && DF != D) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) store_raw<IN, OP, RBV>(sV, p / G::RLV + 16 * i, 8 * (p % G::RLV), pf.v[i]);
+    for (int i = 0; i < G::NV; ++i) store_raw<IN, OP, RBV>(sV, p / G::RLV + G::RSV * i, 8 * (p % G::RLV), pf.v[i]);
   }
 }
 
@@ -246,10 +252,10 @@ __device__ __forceinline__ float stage_q_piece(const typename In8<IN>::raw& r, i
 
 // phi(k) piece i (rows past `valid` masked to phi = 0; times the row scale sc
 // when SC): LDS tile row, column sums into cs
-template <int D, int DF, typename IN, typename OP, int FM, bool SC>
+template <int D, int DF, typename IN, typename OP, int FM, bool SC, int NPT = 2 * D>
 __device__ __forceinline__ void stage_k_piece(typename In8<IN>::raw r, int p, int i, int valid, uint8_t* sK,
                                               float (&cs)[8], float sc) {
-  using G = Stage<D, DF>;
+  using G = Stage<D, DF, NPT>;
   const int row = p / G::RLF + G::RSF * i;
   const auto fill = FM == kElu1 ? In8<IN>::neg_inf() : In8<IN>::zero();
   const bool past = row >= valid;
@@ -360,30 +366,45 @@ __device__ __forceinline__ void store_state_tiles(const f32x16 (&S)[DF / 32], fl
 }
 
 // ---------------------------------------------------------------------------
-// State pass: local (S, z) of every segment. All 2*D threads stage; wave w
-// owns value columns [32w, 32w+32) of S.
+// State pass: local (S, z) of every segment. NW = D/32 value blocks times KS
+// key splits: wave w = nw + NW ks owns value columns [32 nw, 32 nw + 32) of
+// S and, of every 64-row chunk, the 16-key blocks kb = ks, ks + KS, ..; all
+// threads stage. The KS partial states are added through LDS at the end.
+// Splitting the keys gives every SIMD two waves at d = 64 and 128 (one wave
+// per SIMD runs its VALU staging at about half the SIMD's rate).
 // HILO (bf16 operands, for the gradient passes): phi(K) enters S as hi + lo
 // bf16 tiles, so S carries phi(k) to about 2^-16 instead of 2^-9 (the
 // gradient with respect to q magnifies that rounding where phi(k) varies
 // little over the keys).
-// grid = (BH, P), block = 2*D threads.
+// grid = (BH, P), block = StateGeo<D>::NT threads.
 // ---------------------------------------------------------------------------
+template <int D>
+struct StateGeo {
+  static constexpr int NW = D / 32;              // value blocks
+  static constexpr int KS = D == 128 ? 2 : 4;    // key splits (4 key blocks per chunk)
+  static constexpr int NT = 64 * NW * KS;        // 512 threads at d = 64 and 128, 256 at d = 32
+  static constexpr int KPW = 4 / KS;             // key blocks per wave and chunk
+};
+
 template <int D, int DF, typename OP, typename IN, int FM, bool DECAY, bool HILO = false>
-__global__ __launch_bounds__(D * 2, DECAY ? 2 : 1) void state_pass_kernel(FwdArgs a) {
+__global__ __launch_bounds__(StateGeo<D>::NT, 1) void state_pass_kernel(FwdArgs a) {
   using Frag = typename Ops<OP>::frag;
-  using G = Stage<D, DF>;
+  using SG = StateGeo<D>;
+  constexpr int NT = SG::NT, NW = SG::NW, KS = SG::KS, NWT = NW * KS;
+  using G = Stage<D, DF, NT>;
   static_assert(!HILO || (sizeof(OP) == 2 && DF == D), "hi + lo keys: bf16 operands, d' = d");
   constexpr int RBF = DF * Ops<OP>::kBytes;
   constexpr int RBV = D * Ops<OP>::kBytes;
   constexpr int KB = 64 * RBF, VB = 64 * RBV, BUF = KB + VB + (HILO ? KB : 0);
-  constexpr int NW = D / 32;
   constexpr int NS = G::template nset<DECAY>();  // register sets in the load rotation
   // two staged chunks when they fit; otherwise one, with an extra barrier.
-  // The hi + lo-keys variant stages one: two of its larger buffers would
-  // leave room for one workgroup per CU, one buffer for two.
-  constexpr int NB = (!HILO && 2 * BUF + NW * DF * 4 <= 160 * 1024) ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NB * BUF];
-  __shared__ float zsum[NW][DF];
+  // The hi + lo-keys variant stages one.
+  constexpr int NB = (!HILO && 2 * BUF + NWT * DF * 4 <= 160 * 1024) ? 2 : 1;
+  // the end of the pass reuses the buffers for one key split's partial states
+  constexpr int RED = NW * DF * 128;
+  constexpr int SMEM = NB * BUF > RED ? NB * BUF : RED;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  __shared__ float zsum[NWT][DF];
 
   const int bh = blockIdx.x, seg = blockIdx.y;
   const int c0 = seg * a.chunks_per_seg_state;
@@ -391,7 +412,9 @@ __global__ __launch_bounds__(D * 2, DECAY ? 2 : 1) void state_pass_kernel(FwdArg
   const long long base = (long long)bh * a.N;
   const IN* k = static_cast<const IN*>(a.k);
   const IN* v = static_cast<const IN*>(a.v);
-  const int p = threadIdx.x, w = p >> 6, l = p & 63;
+  const int p = threadIdx.x, l = p & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(p >> 6);
+  const int w = wv % NW, ks = wv / NW;  // value block, key split
 
   f32x16 S[DF / 32];
 #pragma unroll
@@ -399,19 +422,19 @@ __global__ __launch_bounds__(D * 2, DECAY ? 2 : 1) void state_pass_kernel(FwdArg
   float zr[8], cs[8], dp[G::NQ];
 #pragma unroll
   for (int e = 0; e < 8; ++e) zr[e] = 0.f;
-  const Voff<D, DF, IN> vo(p);
+  const Voff<D, DF, IN, NT> vo(p);
   const float lg = DECAY ? decay_log2(a.gamma[bh % a.H], a.status_flag) : 0.f;
   const float gH = DECAY ? gpow(lg, kChunk / 2) : 1.f;  // gamma^32; a chunk moves states on by gH twice
 
   // every load is issued (with zero size past the segment) so that all
   // iterations have the same memory instruction stream
   const int nch = c1 - c0;
-  auto load = [&](Pref<D, DF, IN>& pf, int m) {
+  auto load = [&](Pref<D, DF, IN, NT>& pf, int m) {
     const int c = c0 + m;
     const int valid = m < nch ? min(64, a.N - 64 * c) : 0;
     prod_load<D, DF, IN, false, true>(pf, vo, nullptr, k, v, base + 64LL * min(c, a.nchunks - 1), valid);
   };
-  auto stage = [&](Pref<D, DF, IN>& pf, int m) {
+  auto stage = [&](Pref<D, DF, IN, NT>& pf, int m) {
     const int c = c0 + m;
     mask_tail_keys<D, DF, IN, FM>(pf, p, min(64, a.N - 64 * c));
     uint8_t* sK = smem + (NB == 2 ? (m & 1) : 0) * BUF;
@@ -439,11 +462,12 @@ __global__ __launch_bounds__(D * 2, DECAY ? 2 : 1) void state_pass_kernel(FwdArg
       } else {
 #pragma unroll
         for (int i = 0; i < G::NQ; ++i)
-          stage_k_piece<D, DF, IN, OP, FM, true>(pf.k[i], p, i, 64, sK, cs,
-                                                 gpow(lg, kDecayCenter - (p / G::RLF + G::RSF * i)));
+          stage_k_piece<D, DF, IN, OP, FM, true, NT>(pf.k[i], p, i, 64, sK, cs,
+                                                     gpow(lg, kDecayCenter - (p / G::RLF + G::RSF * i)));
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) store_raw<IN, OP, RBV>(sK + KB, p / G::RLV + 16 * i, 8 * (p % G::RLV), pf.v[i]);
+      for (int i = 0; i < G::NV; ++i)
+        store_raw<IN, OP, RBV>(sK + KB, p / G::RLV + G::RSV * i, 8 * (p % G::RLV), pf.v[i]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) zr[e] = gH * (gH * zr[e]) + cs[e];
     } else if constexpr (HILO) {
@@ -469,8 +493,8 @@ __global__ __launch_bounds__(D * 2, DECAY ? 2 : 1) void state_pass_kernel(FwdArg
       for (int e = 0; e < 8; ++e) zr[e] += cs[e];
     }
   };
-  // iteration m: multiply chunk m (in LDS), stage chunk m+1, and keep the
-  // loads of the following chunk(s) in flight
+  // iteration m: multiply the wave's key blocks of chunk m (in LDS), stage
+  // chunk m+1, and keep the loads of the following chunk(s) in flight
   auto mult = [&](int m) {
     const uint8_t* sK = smem + (NB == 2 ? (m & 1) : 0) * BUF;
     const uint8_t* sV = sK + KB;
@@ -478,15 +502,16 @@ __global__ __launch_bounds__(D * 2, DECAY ? 2 : 1) void state_pass_kernel(FwdArg
 #pragma unroll
       for (int cb = 0; cb < DF / 32; ++cb) S[cb] = (S[cb] * gH) * gH;
     }
-    Frag Vf[4];
+    Frag Vf[SG::KPW];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) Vf[kb] = Ops<OP>::template load_cols<RBV>(sV, 16 * kb, 32 * w);
+    for (int j = 0; j < SG::KPW; ++j) Vf[j] = Ops<OP>::template load_cols<RBV>(sV, 16 * (ks + KS * j), 32 * w);
 #pragma unroll
     for (int cb = 0; cb < DF / 32; ++cb)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        Ops<OP>::mma(S[cb], Ops<OP>::template load_cols<RBF>(sK, 16 * kb, 32 * cb), Vf[kb]);
-        if constexpr (HILO) Ops<OP>::mma(S[cb], Ops<OP>::template load_cols<RBF>(sV + VB, 16 * kb, 32 * cb), Vf[kb]);
+      for (int j = 0; j < SG::KPW; ++j) {
+        const int kb = ks + KS * j;
+        Ops<OP>::mma(S[cb], Ops<OP>::template load_cols<RBF>(sK, 16 * kb, 32 * cb), Vf[j]);
+        if constexpr (HILO) Ops<OP>::mma(S[cb], Ops<OP>::template load_cols<RBF>(sV + VB, 16 * kb, 32 * cb), Vf[j]);
       }
   };
   // iteration m multiplies chunk m (LDS), stages chunk m+1 (registers) and
@@ -494,7 +519,7 @@ __global__ __launch_bounds__(D * 2, DECAY ? 2 : 1) void state_pass_kernel(FwdArg
   // The rotation of register sets runs whole (iteration count rounded up to
   // a multiple of NSET); iterations past the segment multiply nothing and
   // only retire their (empty) loads.
-  auto iter = [&](int m, Pref<D, DF, IN>& ld, Pref<D, DF, IN>& st) {
+  auto iter = [&](int m, Pref<D, DF, IN, NT>& ld, Pref<D, DF, IN, NT>& st) {
     load(ld, m + NS);
     if (m < nch) mult(m);
     if constexpr (NB == 1) __syncthreads();
@@ -505,7 +530,7 @@ __global__ __launch_bounds__(D * 2, DECAY ? 2 : 1) void state_pass_kernel(FwdArg
   static_assert(NS == 2, "two register sets rotate");
   const int nround = (nch + NS - 1) / NS * NS;
   {
-    Pref<D, DF, IN> pA, pB;
+    Pref<D, DF, IN, NT> pA, pB;
     load(pA, 0);
     load(pB, 1);
     if (nch > 0) stage(pA, 0);
@@ -521,20 +546,47 @@ __global__ __launch_bounds__(D * 2, DECAY ? 2 : 1) void state_pass_kernel(FwdArg
   for (int e = 0; e < 8; ++e) zr[e] = col_reduce<G::RLF>(zr[e]);
   if (l < G::RLF) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) zsum[w][8 * l + e] = zr[e];
+    for (int e = 0; e < 8; ++e) zsum[wv][8 * l + e] = zr[e];
+  }
+  // S: the key splits ks = 1 .. KS-1 hand their partial tiles to ks = 0, one
+  // split at a time, through the (now idle) staging buffers
+  f32x4* red = reinterpret_cast<f32x4*>(smem);
+#pragma unroll
+  for (int r = 1; r < KS; ++r) {
+    __syncthreads();
+    if (ks == r) {
+#pragma unroll
+      for (int cb = 0; cb < DF / 32; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          red[((w * (DF / 32) + cb) * 4 + g) * 64 + l] = f32x4{S[cb][4 * g], S[cb][4 * g + 1], S[cb][4 * g + 2], S[cb][4 * g + 3]};
+    }
+    __syncthreads();
+    if (ks == 0) {
+#pragma unroll
+      for (int cb = 0; cb < DF / 32; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 x = red[((w * (DF / 32) + cb) * 4 + g) * 64 + l];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[cb][4 * g + e] += x[e];
+        }
+    }
   }
   __syncthreads();
   float* st = a.ws + ((long long)bh * a.ws_slots + seg) * a.state_elems;
   const float fr = DECAY ? gpow(lg, kDecayFrame) : 1.f;  // back from the scaled frame
-  if constexpr (DECAY) {
+  if (ks == 0) {
+    if constexpr (DECAY) {
 #pragma unroll
-    for (int cb = 0; cb < DF / 32; ++cb) S[cb] *= fr;
+      for (int cb = 0; cb < DF / 32; ++cb) S[cb] *= fr;
+    }
+    store_state_tiles<D, DF>(S, st, w);
   }
-  store_state_tiles<D, DF>(S, st, w);
-  for (int c = p; c < DF; c += 2 * D) {
+  for (int c = p; c < DF; c += NT) {
     float s = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) s += zsum[ww][c];
+    for (int ww = 0; ww < NWT; ++ww) s += zsum[ww][c];
     st[DF * D + c] = fr * s;
   }
 }
@@ -1000,10 +1052,10 @@ static hipError_t launch_prefill_t(const FwdArgs& a, const ScanArgs& s, bool cau
     constexpr bool kHiloOk = sizeof(OP) == 2 && DF == D;
     if (kHiloOk && a.hilo_keys)
       hipLaunchKernelGGL((state_pass_kernel<D, DF, OP, IN, FM, DECAY, kHiloOk>), dim3(a.BH, a.nseg_state),
-                         dim3(D * 2), 0, st, a);
+                         dim3(StateGeo<D>::NT), 0, st, a);
     else
-      hipLaunchKernelGGL((state_pass_kernel<D, DF, OP, IN, FM, DECAY>), dim3(a.BH, a.nseg_state), dim3(D * 2), 0,
-                         st, a);
+      hipLaunchKernelGGL((state_pass_kernel<D, DF, OP, IN, FM, DECAY>), dim3(a.BH, a.nseg_state),
+                         dim3(StateGeo<D>::NT), 0, st, a);
   }
   if (ev) (void)hipEventRecord(ev[1], st);
   if (a.run_scan) {
