@@ -376,20 +376,23 @@ __device__ __forceinline__ void store_state_tiles(const f32x16 (&S)[DF / 32], fl
 // bf16 tiles, so S carries phi(k) to about 2^-16 instead of 2^-9 (the
 // gradient with respect to q magnifies that rounding where phi(k) varies
 // little over the keys).
-// grid = (BH, P), block = StateGeo<D>::NT threads.
+// grid = (BH, P), block = StateGeo<D, HILO>::NT threads.
 // ---------------------------------------------------------------------------
-template <int D>
+// The hi + lo-keys variant keeps one key split: the gradient passes launch
+// twice as many segments, which already puts two of its workgroups on every
+// compute unit (with eight waves per block only one would fit).
+template <int D, bool HILO = false>
 struct StateGeo {
-  static constexpr int NW = D / 32;              // value blocks
-  static constexpr int KS = D == 128 ? 2 : 4;    // key splits (4 key blocks per chunk)
-  static constexpr int NT = 64 * NW * KS;        // 512 threads at d = 64 and 128, 256 at d = 32
-  static constexpr int KPW = 4 / KS;             // key blocks per wave and chunk
+  static constexpr int NW = D / 32;                           // value blocks
+  static constexpr int KS = HILO ? 1 : D == 128 ? 2 : 4;      // key splits (4 key blocks per chunk)
+  static constexpr int NT = 64 * NW * KS;                     // 512 threads at d = 64 and 128, 256 at d = 32
+  static constexpr int KPW = 4 / KS;                          // key blocks per wave and chunk
 };
 
 template <int D, int DF, typename OP, typename IN, int FM, bool DECAY, bool HILO = false>
-__global__ __launch_bounds__(StateGeo<D>::NT, 1) void state_pass_kernel(FwdArgs a) {
+__global__ __launch_bounds__((StateGeo<D, HILO>::NT), (HILO ? 2 : 1)) void state_pass_kernel(FwdArgs a) {
   using Frag = typename Ops<OP>::frag;
-  using SG = StateGeo<D>;
+  using SG = StateGeo<D, HILO>;
   constexpr int NT = SG::NT, NW = SG::NW, KS = SG::KS, NWT = NW * KS;
   using G = Stage<D, DF, NT>;
   static_assert(!HILO || (sizeof(OP) == 2 && DF == D), "hi + lo keys: bf16 operands, d' = d");
@@ -1052,7 +1055,7 @@ static hipError_t launch_prefill_t(const FwdArgs& a, const ScanArgs& s, bool cau
     constexpr bool kHiloOk = sizeof(OP) == 2 && DF == D;
     if (kHiloOk && a.hilo_keys)
       hipLaunchKernelGGL((state_pass_kernel<D, DF, OP, IN, FM, DECAY, kHiloOk>), dim3(a.BH, a.nseg_state),
-                         dim3(StateGeo<D>::NT), 0, st, a);
+                         dim3(StateGeo<D, kHiloOk>::NT), 0, st, a);
     else
       hipLaunchKernelGGL((state_pass_kernel<D, DF, OP, IN, FM, DECAY>), dim3(a.BH, a.nseg_state),
                          dim3(StateGeo<D>::NT), 0, st, a);
