@@ -10,21 +10,21 @@
 // log2(m) / 2 goes straight into LDS as bf16, so the m-wide features never
 // reach HBM.
 //
-// d = 64, bf16 inputs, causal or not.
+// bf16 inputs, d in {32, 64, 128} with m in {64, 128} (and 256 at d = 64),
+// causal or not.
 //   state pass : local (S, z) of every segment (causal: all but the last)
-//                -> workspace (8 waves for m >= 128, else 4; each holds one
-//                feature slice of S for 32 value columns)
+//                -> workspace (8 waves for m >= 128, else 4; each projects one
+//                feature slice for half of every chunk's rows)
 //   carry scan : causal: the exclusive prefix over segments; otherwise the
 //                head's total (la_prefill.hip)
-//   output pass: causal: each segment walks its chunks from its carried
-//                prefix (8 waves, two per SIMD); otherwise every wave reads
-//                out 32-row blocks against the total (pf_readout_kernel)
-// In the output pass wave w < 4 holds S[fh*m/2 .. fh*m/2 + m/2)[32 cb .. 32 cb + 32)
-// in MFMA accumulators (fh = w >> 1, cb = w & 1) and finishes query rows
-// [32 fh, 32 fh + 32) x value columns [32 cb, 32 cb + 32) of every chunk; the
-// read-out over the other feature half comes from wave w ^ 2 and the in-chunk
-// term from a score wave, both through LDS.
-// Layouts as in the other passes: q, k, v, out [BH][N][64]; S [BH][m][64];
+//   output pass: causal: each segment walks its chunks in 32-row steps from
+//                its carried prefix, 8 waves: four map waves stage phi(Q),
+//                phi(K) and v, four contraction waves hold S in accumulators
+//                and add their feature ranges' partial numerators through
+//                LDS (pf_output_kernel); non-causal: every wave maps and
+//                reads out 32-row blocks against the total in registers
+//                (pf_readout_kernel)
+// Layouts as in the other passes: q, k, v, out [BH][N][d]; S [BH][m][d];
 // z [BH][m].
 #include "la_device.h"
 #include "la_kernels.h"

@@ -10,6 +10,7 @@
 // Sequence parallelism on one GPU: each (batch, head) sequence is split into
 // P segments of whole chunks.
 //   state pass : every segment's local sums (S_loc, z_loc)         -> workspace
+//                (the chunk's keys split across waves, partials added at the end)
 //   carry scan : exclusive prefix over segments (+ initial state)  -> workspace
 //   output pass: every segment starts from its prefix and walks its chunks
 // The non-causal form reuses the state pass, a total-sum scan and the output
@@ -31,15 +32,13 @@
 namespace la {
 
 // ---------------------------------------------------------------------------
-// Staging geometry. NP = 2*D staging threads. Feature-side rows (phi(Q),
+// Staging geometry of NPT threads over a 64-row chunk (NPT = 2*D producers in
+// the output pass; the state pass's whole block). Feature-side rows (phi(Q),
 // phi(K); DF values) are covered by RLF = DF/8 threads each, so thread p
 // holds pieces i = 0..NQ-1 at row p/RLF + RSF*i, columns 8*(p % RLF); value
-// rows (D values) by RLV = D/8 threads, pieces i = 0..3 at row p/RLV + 16 i.
-// Threads with equal p % RLF share feature columns.
+// rows (D values) by RLV = D/8 threads, pieces i = 0..NV-1 at row
+// p/RLV + RSV*i. Threads with equal p % RLF share feature columns.
 // ---------------------------------------------------------------------------
-// Staging geometry of NPT threads over a 64-row chunk: a q/k row is RLF
-// 16-byte pieces and the threads cover RSF rows per pass (NQ passes); a v
-// row is RLV pieces, RSV rows per pass (NV passes).
 template <int D, int DF, int NPT = 2 * D>
 struct Stage {
   static constexpr int NP = NPT;
