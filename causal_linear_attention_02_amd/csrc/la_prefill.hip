@@ -400,7 +400,8 @@ __global__ __launch_bounds__((StateGeo<D, HILO>::NT), (HILO ? 2 : 1)) void state
   constexpr int KB = 64 * RBF, VB = 64 * RBV, BUF = KB + VB + (HILO ? KB : 0);
   constexpr int NS = G::template nset<DECAY>();  // register sets in the load rotation
   // two staged chunks when they fit; otherwise one, with an extra barrier.
-  // The hi + lo-keys variant stages one.
+  // The hi + lo-keys variant stages one: two of its larger buffers would
+  // leave room for one workgroup per CU, one buffer for two.
   constexpr int NB = (!HILO && 2 * BUF + NWT * DF * 4 <= 160 * 1024) ? 2 : 1;
   // the end of the pass reuses the buffers for one key split's partial states
   constexpr int RED = NW * DF * 128;
