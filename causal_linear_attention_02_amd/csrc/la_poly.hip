@@ -84,8 +84,8 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
   float* sQt = reinterpret_cast<float*>(smem + 2 * TB);  // [feature][row]
   float* sKt = sQt + D * TS;
   float* sVt = sKt + D * TS;
-  float* red = sVt + D * TS;                              // [wave][2][16 registers][64 lanes]
-  float* lowst = red + C::NW * 2048;                     // [tile][16 registers][64 lanes]
+  f32x4* red = reinterpret_cast<f32x4*>(sVt + D * TS);   // [wave][2][4 register groups][64 lanes] of f32x4
+  f32x4* lowst = red + C::NW * 512;                       // [tile][4 register groups][64 lanes] of f32x4
 
   const int bh = blockIdx.x, blk = blockIdx.y;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, hh = l >> 5, li = l & 31;
@@ -164,12 +164,16 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
   auto ld_tile = [&](int ti) {
     f32x16 x;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = lowst[(ti * 16 + r) * 64 + l];
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 y = lowst[(ti * 4 + g) * 64 + l];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[4 * g + u] = y[u];
+    }
     return x;
   };
   auto st_tile = [&](int ti, const f32x16& x) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) lowst[(ti * 16 + r) * 64 + l] = x[r];
+    for (int g = 0; g < 4; ++g) lowst[(ti * 4 + g) * 64 + l] = f32x4{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
   };
 
   // quadratic state: tile (ia, bb) at ia * NB + bb, rows b = 32 bb + ..,
@@ -330,9 +334,27 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
           Ops<OP>::mma(acc, Ops<OP>::from_acc(z2, kk), Ops<OP>::template load_rows<RB>(sQ, 32 * ib, 32 * bb + 16 * kk));
       }
       const int i = 32 * ib + li;
+      // q_ic for c = 32 E + acc_row(r, hh): four groups of four consecutive
+      // features of row i of the operand tile (the same values as Q^T)
       float p = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p += sQt[(32 * E + acc_row(r, hh)) * TS + i] * acc[r];
+      for (int g = 0; g < 4; ++g) {
+        const int byte = (32 * E + 8 * g + 4 * hh) * Ops<OP>::kBytes;  // inside one 16-byte unit
+        float qc[4];
+        if constexpr (sizeof(OP) == 2) {
+          const u32x2 r = *reinterpret_cast<const u32x2*>(sQ + tile_off<RB>(i, byte));
+          qc[0] = __uint_as_float(r[0] << 16);
+          qc[1] = __uint_as_float(r[0] & 0xffff0000u);
+          qc[2] = __uint_as_float(r[1] << 16);
+          qc[3] = __uint_as_float(r[1] & 0xffff0000u);
+        } else {
+          const f32x4 r = *reinterpret_cast<const f32x4*>(sQ + tile_off<RB>(i, byte));
+#pragma unroll
+          for (int u = 0; u < 4; ++u) qc[u] = r[u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) p += qc[u] * acc[4 * g + u];
+      }
       p += xor32(p);
       if (hh == 0 && i < valid) a.den[(1 + E) * BHN + base + 64LL * c + i] = p;
     }
@@ -376,15 +398,19 @@ __global__ __launch_bounds__(PolyCfg<D>::NT) void poly_chunk_kernel(PolyArgs a) 
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) red[((w * 2 + ib) * 16 + r) * 64 + l] = Y[ib][r];
+      for (int g = 0; g < 4; ++g)
+        red[((w * 2 + ib) * 4 + g) * 64 + l] = f32x4{Y[ib][4 * g], Y[ib][4 * g + 1], Y[ib][4 * g + 2], Y[ib][4 * g + 3]};
     __syncthreads();
-    for (int x = t; x < 2048; x += C::NT) {
-      float s = 0.f;
+    // slot x = (ib, g, lane): four rows 32 ib + 8 g + 4 (lane / 32) + 0..3 of column lane % 32
+    for (int x = t; x < 512; x += C::NT) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ww = 0; ww < C::NW; ++ww) s += red[ww * 2048 + x];
-      const int ib = x >> 10, r = (x >> 6) & 15, ll = x & 63;
-      const int row = 32 * ib + acc_row(r, ll >> 5);
-      if (row < valid) part[(64LL * c + row) * D + 32 * E + (ll & 31)] = s;
+      for (int ww = 0; ww < C::NW; ++ww) s += red[ww * 512 + x];
+      const int ib = x >> 8, g = (x >> 6) & 3, ll = x & 63;
+      const int row0 = 32 * ib + 8 * g + 4 * (ll >> 5);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (row0 + u < valid) part[(64LL * c + row0 + u) * D + 32 * E + (ll & 31)] = s[u];
     }
   };
 
