@@ -41,63 +41,128 @@ __device__ __forceinline__ float gphi(float x) {
 }
 __device__ __forceinline__ float exp_nat(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
-template <typename IN, typename OP, int RB>
-__device__ __forceinline__ void put_raw_g(uint8_t* tile, int row, int col, const typename In8<IN>::raw& r) {
-  static_assert(sizeof(IN) == sizeof(OP), "raw staging needs matching element types");
-  if constexpr (sizeof(IN) == 2) {
-    *reinterpret_cast<u32x4*>(tile + tile_off<RB>(row, col * 2)) = r;
+// 4 consecutive input elements: raw form (one buffer load) and fp32
+template <typename IN> struct In4;
+template <> struct In4<__bf16> {
+  using raw = u32x2;  // 8 bytes
+  __device__ static raw bload(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
+  }
+  __device__ static void to_f32(const raw& r, float (&x)[4]) {
+    x[0] = __uint_as_float(r[0] << 16);
+    x[1] = __uint_as_float(r[0] & 0xffff0000u);
+    x[2] = __uint_as_float(r[1] << 16);
+    x[3] = __uint_as_float(r[1] & 0xffff0000u);
+  }
+};
+template <> struct In4<float> {
+  using raw = f32x4;  // 16 bytes
+  __device__ static raw bload(__amdgpu_buffer_rsrc_t r, int voff) { return __builtin_bit_cast(f32x4, buf_load16(r, voff)); }
+  __device__ static void to_f32(const raw& r, float (&x)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = r[i];
+  }
+};
+
+// 4 fp32 values of a row (columns col .. col+3) into a swizzled operand tile
+template <typename OP, int RB>
+__device__ __forceinline__ void store4(uint8_t* tile, int row, int col, const float (&x)[4]) {
+  if constexpr (sizeof(OP) == 2) {
+    *reinterpret_cast<u32x2*>(tile + tile_off<RB>(row, col * 2)) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
   } else {
-    *reinterpret_cast<f32x4*>(tile + tile_off<RB>(row, col * 4)) = r.a;
-    *reinterpret_cast<f32x4*>(tile + tile_off<RB>(row, col * 4 + 16)) = r.b;
+    *reinterpret_cast<f32x4*>(tile + tile_off<RB>(row, col * 4)) = f32x4{x[0], x[1], x[2], x[3]};
   }
 }
-
-// sum over the lanes of a wave that share lane % RL
-template <int RL>
-__device__ __forceinline__ float colsum_lanes(float x) {
-#pragma unroll
-  for (int s = RL; s < 64; s <<= 1) x += __shfl_xor(x, s, 64);
-  return x;
+template <typename IN, typename OP, int RB>
+__device__ __forceinline__ void store4_raw(uint8_t* tile, int row, int col, const typename In4<IN>::raw& r) {
+  static_assert(sizeof(IN) == sizeof(OP), "raw staging needs matching element types");
+  *reinterpret_cast<typename In4<IN>::raw*>(tile + tile_off<RB>(row, col * (int)sizeof(IN))) = r;
 }
 
-// In-chunk prefix of the log-gates: lam[r][f] = lg_0f + ... + lg_rf for the
-// 64 rows of the chunk (fp32). The gate tile is loaded in 16-byte row pieces
-// into lam; then NT/D threads per channel scan it in place, each over
-// 64*D/NT consecutive rows, and add the totals of the rows before theirs.
-// Rows past the end of the sequence load as 0 (buffer range check), so lam
-// stays at its last value there. tot: NT/D x D scratch. Three barriers.
-// A log-gate outside [log(1/4), 0] becomes NaN (checked_log_gate), so the
-// prefix of its channel is NaN from its row on, and raises the status flag.
+// Thread layout of the gated passes' loads and staging: NT threads over a
+// 64 x D chunk. Thread t holds channels [4 g, 4 g + 4) of the R consecutive
+// rows [R j, R j + R), with g = t / J and j = t % J. The J threads of a
+// channel group are consecutive lanes of one wave, so the in-chunk prefix of
+// the log-gates is a sum in registers over R rows and a scan across J lanes,
+// and per-channel values of one row are a lane broadcast away.
 template <int D, int NT>
-__device__ __forceinline__ void gate_prefix(const float* lg, long long row0, int valid, float* lam, float* tot,
-                                            int* flag) {
-  constexpr int NQ = NT / D, RPQ = 64 / NQ, NPC = 16 * D / NT;  // pieces of 4 per thread
-  const int t = threadIdx.x, col = t % D, qt = t / D;
-  const auto R = make_rsrc(lg + row0 * D, (unsigned)(valid * D * 4));
-  f32x4 p[NPC];
+struct GMap {
+  static constexpr int CG = D / 4, J = NT / CG, R = 64 / J;
+  static_assert(NT % CG == 0 && 64 % J == 0 && R >= 1, "gate layout");
+};
+
+// Registers of one chunk: log-gates, and k, v (and q) in the layout above.
+template <int D, int NT, typename IN, bool Q>
+struct GSet {
+  static constexpr int R = GMap<D, NT>::R;
+  f32x4 lg[R];
+  typename In4<IN>::raw q[Q ? R : 1], k[R], v[R];
+};
+
+// Loads of the chunk at rows [row0, row0 + valid); rows past `valid` read as
+// zero through the descriptors' range check (log-gate 0: the prefix stays at
+// its last value there). `valid` must be wave-uniform.
+template <int D, int NT, typename IN, bool Q>
+__device__ __forceinline__ void gload(GSet<D, NT, IN, Q>& s, const float* lg, const IN* q, const IN* k, const IN* v,
+                                      long long row0, int valid, int t) {
+  using M = GMap<D, NT>;
+  const int gi = t / M::J, j = t % M::J;
+  const unsigned eb = (unsigned)(valid * D * (int)sizeof(IN));
+  const auto Rg = make_rsrc(lg + row0 * D, (unsigned)(valid * D * 4));
+  const auto Rk = make_rsrc(k + row0 * D, eb);
+  const auto Rv = make_rsrc(v + row0 * D, eb);
 #pragma unroll
-  for (int i = 0; i < NPC; ++i) p[i] = __builtin_bit_cast(f32x4, buf_load16(R, (t + NT * i) * 16));
+  for (int e = 0; e < M::R; ++e) {
+    const int el = (M::R * j + e) * D + 4 * gi;
+    s.lg[e] = __builtin_bit_cast(f32x4, buf_load16(Rg, el * 4));
+    if constexpr (Q) s.q[e] = In4<IN>::bload(make_rsrc(q + row0 * D, eb), el * (int)sizeof(IN));
+    s.k[e] = In4<IN>::bload(Rk, el * (int)sizeof(IN));
+    s.v[e] = In4<IN>::bload(Rv, el * (int)sizeof(IN));
+  }
+}
+
+// In-chunk prefix of the log-gates, in place: p[e][c] becomes
+// lam = lg_0 + ... + lg_r at row r = R j + e, channel 4 g + c (fp32). A
+// log-gate outside [log(1/4), 0] becomes NaN (checked_log_gate), so the
+// prefix of its channel is NaN from its row on, and raises the status flag.
+template <int D, int NT, int NR>
+__device__ __forceinline__ void gate_scan(f32x4 (&p)[NR], int* flag, int t) {
+  using M = GMap<D, NT>;
+  static_assert(NR == M::R, "rows per thread");
 #pragma unroll
-  for (int i = 0; i < NPC; ++i) {
+  for (int e = 0; e < M::R; ++e)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) p[i][e] = checked_log_gate(p[i][e], flag);
-    *reinterpret_cast<f32x4*>(lam + 4 * (t + NT * i)) = p[i];
+    for (int c = 0; c < 4; ++c) p[e][c] = checked_log_gate(p[e][c], flag);
+#pragma unroll
+  for (int e = 1; e < M::R; ++e) p[e] += p[e - 1];
+  // inclusive scan of the row-block totals across the group's lanes, then
+  // shifted by one lane: the sum of the row blocks before this one
+  const int j = t % M::J;
+  f32x4 inc = p[M::R - 1];
+#pragma unroll
+  for (int s = 1; s < M::J; s <<= 1) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float y = __shfl_up(inc[c], s, M::J);
+      if (j >= s) inc[c] += y;
+    }
   }
-  __syncthreads();
-  float run = 0.f;
-  for (int r = 0; r < RPQ; ++r) {
-    float* x = lam + (qt * RPQ + r) * D + col;
-    run += *x;
-    *x = run;
+  f32x4 off;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float y = __shfl_up(inc[c], 1, M::J);
+    off[c] = j >= 1 ? y : 0.f;
   }
-  tot[qt * D + col] = run;
-  __syncthreads();
-  float off = 0.f;
-  for (int q2 = 0; q2 < qt; ++q2) off += tot[q2 * D + col];
-  if (qt > 0) {
-    for (int r = 0; r < RPQ; ++r) lam[(qt * RPQ + r) * D + col] += off;
-  }
-  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < M::R; ++e) p[e] += off;
+}
+
+// sum over the J lanes of a channel group
+template <int J>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int s = 1; s < J; s <<= 1) x += __shfl_xor(x, s, J);
+  return x;
 }
 
 // ---------------------------------------------------------------------------
@@ -106,139 +171,157 @@ __device__ __forceinline__ void gate_prefix(const float* lg, long long row0, int
 // alike), and the segment's total log-gate per channel (lfac[bh][seg][f]).
 // Per chunk S <- diag(exp(lam_63)) S + Kt^T V with Kt[r] = phi(k_r) exp(lam_63 - lam_r) <= phi(k_r).
 // grid = (BH, P - 1), block = 2*D threads; wave w owns S[:, 32w:32w+32].
+// The next chunk's rows are loaded once this one is staged, during its
+// products; two LDS buffers leave one barrier per chunk.
 // ---------------------------------------------------------------------------
 template <int D, typename OP, typename IN, int FM>
-__global__ __launch_bounds__(D * 2) void gla_state_kernel(GatedArgs g) {
-  using Frag = typename Ops<OP>::frag;
-  constexpr int NW = D / 32, NT = 2 * D, RL = D / 8;
+__global__ __launch_bounds__(D * 2, 2) void gla_state_kernel(GatedArgs g) {
+  constexpr int NW = D / 32, NT = 2 * D;
+  using M = GMap<D, NT>;
+  constexpr int R = M::R, J = M::J;
   constexpr int RB = D * Ops<OP>::kBytes, TB = 64 * RB;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TB];
-  __shared__ __attribute__((aligned(16))) float lam[64 * D];
-  __shared__ float tot[(NT / D) * D];
-  __shared__ float zsum[NW][D];
-  __shared__ float f63[D];  // per channel exp(lam_63)
-  uint8_t* sK = smem;
-  uint8_t* sV = smem + TB;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][2 * TB];
+  __shared__ __attribute__((aligned(16))) float f63[2][D];  // per channel exp(lam_63)
   const FwdArgs& a = g.f;
   const int bh = blockIdx.x, seg = blockIdx.y;
   const int c0 = seg * a.chunks_per_seg_state;
   const int n = max(0, min(c0 + a.chunks_per_seg_state, a.nchunks) - c0);
   const int t = threadIdx.x, w = t >> 6, l = t & 63, h = l >> 5, li = l & 31;
+  const int gi = t / J, j = t % J;
   const long long base = (long long)bh * a.N;
   const IN* k = static_cast<const IN*>(a.k);
   const IN* v = static_cast<const IN*>(a.v);
-  const int col = 8 * (t % RL);
 
   f32x16 S[NW];
 #pragma unroll
   for (int fb = 0; fb < NW; ++fb) S[fb] = f32x16{};
-  float zr[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float ltot = 0.f;  // thread t < D: the segment's total log-gate of channel t
-  for (int m = 0; m < n; ++m) {
-    const int c = c0 + m;
-    const int valid = min(64, a.N - 64 * c);
-    const long long row0 = base + 64LL * c;
-    const unsigned bytes = (unsigned)(valid * D * (int)sizeof(IN));
-    const auto Rk = make_rsrc(k + row0 * D, bytes);
-    const auto Rv = make_rsrc(v + row0 * D, bytes);
-    typename In8<IN>::raw rk[4], rv[4];
+  float zr[4] = {0.f, 0.f, 0.f, 0.f};    // this lane's rows' part of z, channels 4 gi + c
+  float ltot[4] = {0.f, 0.f, 0.f, 0.f};  // the segment's total log-gate, channels 4 gi + c
+
+  auto load = [&](int m, GSet<D, NT, IN, false>& s) {
+    const int c = min(c0 + m, a.nchunks - 1);
+    const int valid = __builtin_amdgcn_readfirstlane(m < n ? min(64, a.N - 64 * c) : 0);
+    gload<D, NT, IN, false>(s, g.log_gates, nullptr, k, v, base + 64LL * c, valid, t);
+  };
+  GSet<D, NT, IN, false> cur;
+  auto step = [&](int m) {
+    const int valid = __builtin_amdgcn_readfirstlane(min(64, a.N - 64 * (c0 + m)));
+    uint8_t* sK = smem[m & 1];
+    uint8_t* sV = sK + TB;
+    float* fb63 = f63[m & 1];
+    gate_scan<D, NT>(cur.lg, a.status_flag, t);
+    float l63[4];
+    f32x4 e63;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int o = ((t / RL + 16 * i) * D + col) * (int)sizeof(IN);
-      rk[i] = In8<IN>::bload(Rk, o);
-      rv[i] = In8<IN>::bload(Rv, o);
-    }
-    gate_prefix<D, NT>(g.log_gates, row0, valid, lam, tot, g.f.status_flag);
-    float l63[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      l63[e] = lam[63 * D + col + e];
-      zr[e] *= exp_nat(l63[e]);
-    }
-    if (t < D) {
-      ltot += lam[63 * D + t];
-      f63[t] = exp_nat(lam[63 * D + t]);
+    for (int c = 0; c < 4; ++c) {
+      l63[c] = __shfl(cur.lg[R - 1][c], J - 1, J);
+      ltot[c] += l63[c];
+      e63[c] = exp_nat(l63[c]);
+      zr[c] *= e63[c];
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = t / RL + 16 * i;
-      float x[8];
-      In8<IN>::to_f32(rk[i], x);
+    for (int e = 0; e < R; ++e) {
+      const int row = R * j + e;
+      float x[4];
+      In4<IN>::to_f32(cur.k[e], x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] = row < valid ? gphi<FM>(x[e]) * exp_nat(l63[e] - lam[row * D + col + e]) : 0.f;
-        zr[e] += x[e];
+      for (int c = 0; c < 4; ++c) {
+        x[c] = row < valid ? gphi<FM>(x[c]) * exp_nat(l63[c] - cur.lg[e][c]) : 0.f;
+        zr[c] += x[c];
       }
-      Ops<OP>::template store8<RB>(sK, row, col, x);
-      put_raw_g<IN, OP, RB>(sV, row, col, rv[i]);
+      store4<OP, RB>(sK, row, 4 * gi, x);
+      store4_raw<IN, OP, RB>(sV, row, 4 * gi, cur.v[e]);
     }
+    if (j == 0) *reinterpret_cast<f32x4*>(fb63 + 4 * gi) = e63;
+    load(m + 1, cur);  // in flight during the products below and the next staging's wait
     __syncthreads();
     // S <- diag(exp(lam_63)) S + Kt^T V
 #pragma unroll
     for (int fb = 0; fb < NW; ++fb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S[fb][r] *= f63[32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)];
+      for (int r = 0; r < 16; ++r) S[fb][r] *= fb63[32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const Frag vf = Ops<OP>::template load_cols<RB>(sV, 16 * kb, 32 * w);
+      const auto vf = Ops<OP>::template load_cols<RB>(sV, 16 * kb, 32 * w);
 #pragma unroll
       for (int fb = 0; fb < NW; ++fb) Ops<OP>::mma(S[fb], Ops<OP>::template load_cols<RB>(sK, 16 * kb, 32 * fb), vf);
     }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) zr[e] = colsum_lanes<RL>(zr[e]);
-  if (l < RL) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) zsum[w][col + e] = zr[e];
-  }
-  __syncthreads();
+  };
+  load(0, cur);
+  for (int m = 0; m < n; ++m) step(m);
   float* st = a.ws + ((long long)bh * a.ws_slots + seg) * a.state_elems;
 #pragma unroll
   for (int fb = 0; fb < NW; ++fb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) st[(long long)(32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)) * D + 32 * w + li] = S[fb][r];
-  for (int f = t; f < D; f += NT) {
-    float s = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) s += zsum[ww][f];
-    st[D * D + f] = s;
+  for (int c = 0; c < 4; ++c) zr[c] = group_sum<J>(zr[c]);
+  if (j == 0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      st[D * D + 4 * gi + c] = zr[c];
+      g.lfac[((long long)bh * a.nseg + seg) * D + 4 * gi + c] = ltot[c];
+    }
   }
-  if (t < D) g.lfac[((long long)bh * a.nseg + seg) * D + t] = ltot;
 }
 
 // ---------------------------------------------------------------------------
-// Output pass. grid = (BH, P), block = 4*D threads: wave (ib, w) handles
-// query rows [32 ib, 32 ib + 32) of the chunk and value columns [32 w,
-// 32 w + 32), keeping S[:, 32w:32w+32] (rows = features) in accumulators;
-// threads t < D keep z_t.
+// Output pass. grid = (BH, P), block = 64 (NW + NWP) threads in two roles:
+//   producers (NWP waves): load chunk m + 1 while they stage chunk m: the
+//     in-chunk gate prefix, Qh and Kh, V, the column sums of Kh (the lanes of
+//     channel group g keep z of channels [4 g, 4 g + 4)), the factors
+//     exp(lam_c) and exp(lam_63 - lam_c), and each producer wave's part of
+//     the carried denominator Qh_i . exp(lam_c) z of every row;
+//   consumers (D/32 waves): wave w keeps S[:, 32w:32w+32] (rows = features)
+//     in accumulators and, for both 32-row blocks of chunk m - 1, forms the
+//     scores, both numerator terms and the denominator, writes the output
+//     rows and moves S on.
+// Step it: the producers stage chunk it while the consumers compute chunk
+// it - 1 from the other LDS buffer; one barrier per step hands them over
+// (two where one buffer is all that fits).
 // ---------------------------------------------------------------------------
+// Producer waves of the output pass: two per consumer wave where the
+// registers allow it (d <= 64: the producers' vector work is the longer
+// chain), one at d = 128 (three waves per SIMD would leave the consumers too
+// few registers; measured 900 against 746 us on B1 H16 N65536).
+template <int D>
+constexpr int gla_producer_waves() { return (D == 128 ? 1 : 2) * D / 32; }
+template <int D>
+constexpr int gla_output_threads() { return 64 * (D / 32 + gla_producer_waves<D>()); }
+
 template <int D, typename OP, typename IN, int FM>
-__global__ __launch_bounds__(D * 4) void gla_output_kernel(GatedArgs g) {
-  using Frag = typename Ops<OP>::frag;
-  constexpr int NW = D / 32, NT = 4 * D, RL = D / 8, NWAVE = NT / 64;
+__global__ __launch_bounds__(gla_output_threads<D>()) void gla_output_kernel(GatedArgs g) {
+  constexpr int NW = D / 32;       // consumer waves = value blocks = feature blocks
+  constexpr int NWP = gla_producer_waves<D>();
+  // consumer loops unrolled where the registers allow it (one producer wave
+  // per consumer wave)
+  constexpr int UNR = NWP == NW ? 2 : 1;
+  constexpr int NTP = 64 * NWP;    // producer threads
+  using M = GMap<D, NTP>;
+  constexpr int R = M::R, J = M::J;
   constexpr int RB = D * Ops<OP>::kBytes, TB = 64 * RB;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * TB];
-  __shared__ __attribute__((aligned(16))) float lam[64 * D];
-  __shared__ float tot[(NT / D) * D];
-  __shared__ float zpart[NWAVE][D];
-  __shared__ __attribute__((aligned(16))) float zc[D];  // exp(lam_c) z of the state entering the chunk
-  __shared__ float fc[D], fe[D];                         // per channel: exp(lam_c), exp(lam_63 - lam_c)
-  uint8_t* sQ = smem;
-  uint8_t* sK = smem + TB;
-  uint8_t* sV = smem + 2 * TB;
+  constexpr int NBUF = 2 * (3 * TB + 2 * D * 4 + NWP * 64 * 4) <= 160 * 1024 ? 2 : 1;
+  // Two register sets of prefetched rows where they fit (bf16): the next
+  // chunk's loads go out before this one is staged. With one set they go out
+  // after it, during the consumers' products.
+  constexpr int PSETS = sizeof(IN) == 2 && D <= 64 ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF][3 * TB];
+  // per buffer and channel: exp(lam_c) and exp(lam_63 - lam_c)
+  __shared__ __attribute__((aligned(16))) float fac[NBUF][2][D];
+  // per buffer: each producer wave's part of the carried denominator of every row
+  __shared__ float dpart[NBUF][NWP][64];
   const FwdArgs& a = g.f;
   const int bh = blockIdx.x, seg = blockIdx.y;
   const int c0 = seg * a.chunks_per_seg;
   const int n = max(0, min(c0 + a.chunks_per_seg, a.nchunks) - c0);
-  const int t = threadIdx.x, wave = t >> 6, l = t & 63, h = l >> 5, li = l & 31;
-  const int ib = wave / NW, w = wave % NW;
+  const int t = threadIdx.x, l = t & 63, h = l >> 5, li = l & 31;
+  // the wave index in a scalar register: the role branches stay uniform
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const long long base = (long long)bh * a.N;
   const IN* q = static_cast<const IN*>(a.q);
   const IN* k = static_cast<const IN*>(a.k);
   const IN* v = static_cast<const IN*>(a.v);
   IN* out = static_cast<IN*>(a.out);
-  const int col = 8 * (t % RL);
 
   const float* Sinit;
   const float* zinit;
@@ -249,162 +332,204 @@ __global__ __launch_bounds__(D * 4) void gla_output_kernel(GatedArgs g) {
     Sinit = a.S_in ? a.S_in + (long long)bh * D * D : nullptr;
     zinit = a.z_in ? a.z_in + (long long)bh * D : nullptr;
   }
-  f32x16 S[NW];
-#pragma unroll
-  for (int fb = 0; fb < NW; ++fb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      S[fb][r] = Sinit ? Sinit[(long long)(32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)) * D + 32 * w + li] : 0.f;
-  float zreg = (t < D && zinit) ? zinit[t] : 0.f;
 
-  for (int m = 0; m < n; ++m) {
-    const int c = c0 + m;
-    const int valid = min(64, a.N - 64 * c);
-    const long long row0 = base + 64LL * c;
-    const unsigned bytes = (unsigned)(valid * D * (int)sizeof(IN));
-    const auto Rq = make_rsrc(q + row0 * D, bytes);
-    const auto Rk = make_rsrc(k + row0 * D, bytes);
-    const auto Rv = make_rsrc(v + row0 * D, bytes);
-    typename In8<IN>::raw rq[2], rk[2], rv[2];
+  if (wave >= NW) {
+    // ------------------------------------------------------------ producers
+    const int p = t - 64 * NW, pw = wave - NW;
+    const int gi = p / J, j = p % J;
+    float zreg[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int o = ((t / RL + 32 * i) * D + col) * (int)sizeof(IN);
-      rq[i] = In8<IN>::bload(Rq, o);
-      rk[i] = In8<IN>::bload(Rk, o);
-      rv[i] = In8<IN>::bload(Rv, o);
-    }
-    gate_prefix<D, NT>(g.log_gates, row0, valid, lam, tot, g.f.status_flag);
-    // stage Qh, Kh (rows past the end: 0), V; column sums of Kh
-    float lc[8], cs[8];
+    for (int c = 0; c < 4; ++c) zreg[c] = zinit ? zinit[4 * gi + c] : 0.f;
+    auto load = [&](int m, GSet<D, NTP, IN, true>& s) {
+      const int c = min(c0 + m, a.nchunks - 1);
+      const int valid = __builtin_amdgcn_readfirstlane(m < n ? min(64, a.N - 64 * c) : 0);
+      gload<D, NTP, IN, true>(s, g.log_gates, q, k, v, base + 64LL * c, valid, p);
+    };
+    auto stage = [&](int m, GSet<D, NTP, IN, true>& cur) {
+      const int valid = __builtin_amdgcn_readfirstlane(min(64, a.N - 64 * (c0 + m)));
+      uint8_t* sQ = smem[m % NBUF];
+      uint8_t* sK = sQ + TB;
+      uint8_t* sV = sK + TB;
+      gate_scan<D, NTP>(cur.lg, a.status_flag, p);
+      float lc[4], l63[4], cs[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      lc[e] = lam[kCenter * D + col + e];
-      cs[e] = 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = t / RL + 32 * i;
-      float xq[8], xk[8];
-      In8<IN>::to_f32(rq[i], xq);
-      In8<IN>::to_f32(rk[i], xk);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float f = exp_nat(lam[row * D + col + e] - lc[e]);
-        xq[e] = gphi<FM>(xq[e]) * f;
-        xk[e] = row < valid ? gphi<FM>(xk[e]) * __builtin_amdgcn_rcpf(f) : 0.f;
-        cs[e] += xk[e];
+      for (int c = 0; c < 4; ++c) {
+        lc[c] = __shfl(cur.lg[kCenter % R][c], kCenter / R, J);
+        l63[c] = __shfl(cur.lg[R - 1][c], J - 1, J);
+        cs[c] = 0.f;
       }
-      Ops<OP>::template store8<RB>(sQ, row, col, xq);
-      Ops<OP>::template store8<RB>(sK, row, col, xk);
-      put_raw_g<IN, OP, RB>(sV, row, col, rv[i]);
-    }
+      // the carried part exp(lam_c) z for this chunk's readout (its dot
+      // products with the staged Qh rows form the carried denominator)
+      f32x4 ec, ee, zcar;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) cs[e] = colsum_lanes<RL>(cs[e]);
-    if (l < RL) {
+      for (int c = 0; c < 4; ++c) {
+        ec[c] = exp_nat(lc[c]);
+        zcar[c] = ec[c] * zreg[c];
+      }
+      float dq[R];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) zpart[wave][col + e] = cs[e];
-    }
-    __syncthreads();
-    // z: the carried part exp(lam_c) z for this chunk's readout, then the
-    // state leaving it, exp(lam_63 - lam_c) (exp(lam_c) z + colsum Kh)
-    if (t < D) {
-      float s = 0.f;
+      for (int e = 0; e < R; ++e) {
+        const int row = R * j + e;
+        float xq[4], xk[4];
+        In4<IN>::to_f32(cur.q[e], xq);
+        In4<IN>::to_f32(cur.k[e], xk);
 #pragma unroll
-      for (int ww = 0; ww < NWAVE; ++ww) s += zpart[ww][t];
-      const float lct = lam[kCenter * D + t];
-      const float ec = exp_nat(lct), ee = exp_nat(lam[63 * D + t] - lct);
-      fc[t] = ec;
-      fe[t] = ee;
-      const float zcar = ec * zreg;
-      zc[t] = zcar;
-      zreg = ee * (zcar + s);
+        for (int c = 0; c < 4; ++c) {
+          const float f = exp_nat(cur.lg[e][c] - lc[c]);
+          xq[c] = gphi<FM>(xq[c]) * f;
+          xk[c] = row < valid ? gphi<FM>(xk[c]) * __builtin_amdgcn_rcpf(f) : 0.f;
+          cs[c] += xk[c];
+        }
+        store4<OP, RB>(sQ, row, 4 * gi, xq);
+        store4<OP, RB>(sK, row, 4 * gi, xk);
+        store4_raw<IN, OP, RB>(sV, row, 4 * gi, cur.v[e]);
+        // with Qh as the operand holds it (bf16: rounded)
+        if constexpr (sizeof(OP) == 2) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) xq[c] = round_bf16(xq[c]);
+        }
+        dq[e] = xq[0] * zcar[0] + xq[1] * zcar[1] + xq[2] * zcar[2] + xq[3] * zcar[3];
+      }
+      // the wave's channel groups: lanes J, 2J, ... apart hold the same rows
+#pragma unroll
+      for (int e = 0; e < R; ++e) {
+#pragma unroll
+        for (int sh = J; sh < 64; sh <<= 1) dq[e] += __shfl_xor(dq[e], sh, 64);
+      }
+      if (l < J) {
+#pragma unroll
+        for (int e = 0; e < R; ++e) dpart[m % NBUF][pw][R * j + e] = dq[e];
+      }
+      // the state leaving the chunk, exp(lam_63 - lam_c) (exp(lam_c) z + colsum Kh)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        cs[c] = group_sum<J>(cs[c]);
+        ee[c] = exp_nat(l63[c] - lc[c]);
+        zreg[c] = ee[c] * (zcar[c] + cs[c]);
+      }
+      if (j == 0) {
+        *reinterpret_cast<f32x4*>(&fac[m % NBUF][0][4 * gi]) = ec;
+        *reinterpret_cast<f32x4*>(&fac[m % NBUF][1][4 * gi]) = ee;
+      }
+    };
+    // step it: stage chunk it (if any) and load chunk it + 1; one barrier
+    // (two with one buffer: the consumers first finish chunk it - 1)
+    auto pstep = [&](int it, GSet<D, NTP, IN, true>& cur, GSet<D, NTP, IN, true>& nxt) {
+      if constexpr (PSETS == 2) load(it + 1, nxt);
+      if constexpr (NBUF == 1) __syncthreads();
+      if (it < n) stage(it, cur);
+      if constexpr (PSETS == 1) load(it + 1, nxt);
+      __syncthreads();
+    };
+    if constexpr (PSETS == 2) {
+      GSet<D, NTP, IN, true> A, B;
+      load(0, A);
+      for (int it = 0; it <= n; it += 2) {
+        pstep(it, A, B);
+        if (it + 1 <= n) pstep(it + 1, B, A);
+      }
+    } else {
+      GSet<D, NTP, IN, true> A;
+      load(0, A);
+      for (int it = 0; it <= n; ++it) pstep(it, A, A);
     }
-    __syncthreads();
-    // S' = diag(exp(lam_c)) S
+    if (a.S_out && seg == a.nseg - 1 && j == 0) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) a.z_out[(long long)bh * D + 4 * gi + c] = zreg[c];
+    }
+  } else {
+    // ------------------------------------------------------------ consumers
+    const int w = wave;
+    f32x16 S[NW];
 #pragma unroll
     for (int fb = 0; fb < NW; ++fb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S[fb][r] *= fc[32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)];
-
-    // scores A[j][i] for the wave's query rows (key blocks 0..ib), numerator
-    f32x16 num = {};
-    float den = 0.f;
+      for (int r = 0; r < 16; ++r)
+        S[fb][r] = Sinit ? Sinit[(long long)(32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)) * D + 32 * w + li] : 0.f;
+    auto compute = [&](int m) {
+      const int valid = __builtin_amdgcn_readfirstlane(min(64, a.N - 64 * (c0 + m)));
+      const long long row0 = base + 64LL * (c0 + m);
+      const uint8_t* sQ = smem[m % NBUF];
+      const uint8_t* sK = sQ + TB;
+      const uint8_t* sV = sK + TB;
+      const float* fc = fac[m % NBUF][0];
+      const float* fe = fac[m % NBUF][1];
+      // S' = diag(exp(lam_c)) S
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      if (jb > ib) break;
-      f32x16 A = {};
-      // partial unroll: full unrolling hoists every fragment load and spills
+      for (int fb = 0; fb < NW; ++fb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[fb][r] *= fc[32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)];
+#pragma unroll UNR
+      for (int rb = 0; rb < 2; ++rb) {
+        // scores A[j][i] of query block rb (key blocks 0..rb), numerator
+        f32x16 num = {};
+        float den = 0.f;
+#pragma unroll UNR
+        for (int jb = 0; jb <= rb; ++jb) {
+          f32x16 A = {};
+          // partial unroll: full unrolling hoists every fragment load
 #pragma unroll 2
-      for (int kb = 0; kb < D / 16; ++kb)
-        Ops<OP>::mma(A, Ops<OP>::template load_rows<RB>(sK, 32 * jb, 16 * kb),
-                     Ops<OP>::template load_rows<RB>(sQ, 32 * ib, 16 * kb));
-      if (jb == ib) {
+          for (int kb = 0; kb < D / 16; ++kb)
+            Ops<OP>::mma(A, Ops<OP>::template load_rows<RB>(sK, 32 * jb, 16 * kb),
+                         Ops<OP>::template load_rows<RB>(sQ, 32 * rb, 16 * kb));
+          if (jb == rb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) A[r] = 8 * (r >> 2) + 4 * h + (r & 3) <= li ? A[r] : 0.f;
-      }
+            for (int r = 0; r < 16; ++r) A[r] = 8 * (r >> 2) + 4 * h + (r & 3) <= li ? A[r] : 0.f;
+          }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) den += A[r];
+          for (int r = 0; r < 16; ++r) den += A[r];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        Ops<OP>::mma(num, Ops<OP>::template load_cols<RB>(sV, 32 * jb + 16 * kk, 32 * w), Ops<OP>::from_acc(A, kk));
-    }
+          for (int kk = 0; kk < 2; ++kk)
+            Ops<OP>::mma(num, Ops<OP>::template load_cols<RB>(sV, 32 * jb + 16 * kk, 32 * w), Ops<OP>::from_acc(A, kk));
+        }
 #pragma unroll
-    for (int fb = 0; fb < NW; ++fb)
+        for (int fb = 0; fb < NW; ++fb)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        Ops<OP>::mma(num, Ops<OP>::from_acc(S[fb], kk), Ops<OP>::template load_rows<RB>(sQ, 32 * ib, 32 * fb + 16 * kk));
-    // carried denominator Qh_i . zc over this lane half's features
-    const int irow = 32 * ib + li;
+          for (int kk = 0; kk < 2; ++kk)
+            Ops<OP>::mma(num, Ops<OP>::from_acc(S[fb], kk),
+                         Ops<OP>::template load_rows<RB>(sQ, 32 * rb, 32 * fb + 16 * kk));
+        // carried denominator: the producer waves' parts (added by one lane half)
+        const int irow = 32 * rb + li;
+        if (h == 0) {
 #pragma unroll
-    for (int u = 0; u < D / 8; ++u) {  // D/2 features per lane half, 4 at a time
-      const int f0 = (D / 2) * h + 4 * u;
-      float x[4];
-      if constexpr (sizeof(OP) == 2) {
-        const u32x2 p = *reinterpret_cast<const u32x2*>(sQ + tile_off<RB>(irow, f0 * 2));
-        x[0] = __uint_as_float(p[0] << 16);
-        x[1] = __uint_as_float(p[0] & 0xffff0000u);
-        x[2] = __uint_as_float(p[1] << 16);
-        x[3] = __uint_as_float(p[1] & 0xffff0000u);
-      } else {
-        const f32x4 p = *reinterpret_cast<const f32x4*>(sQ + tile_off<RB>(irow, f0 * 4));
-        x[0] = p[0];
-        x[1] = p[1];
-        x[2] = p[2];
-        x[3] = p[3];
-      }
-      const f32x4 zz = *reinterpret_cast<const f32x4*>(zc + f0);
-      den += x[0] * zz[0] + x[1] * zz[1] + x[2] * zz[2] + x[3] * zz[3];
-    }
-    den += xor32(den);
-    const float inv = a.normalize ? 1.f / fmaxf(den, kEps) : 1.f;
-    if (irow < valid) {
-      IN* o = out + (row0 + irow) * D + 32 * w + 4 * h;
+          for (int ww = 0; ww < NWP; ++ww) den += dpart[m % NBUF][ww][irow];
+        }
+        den += xor32(den);
+        const float inv = a.normalize ? 1.f / fmaxf(den, kEps) : 1.f;
+        if (irow < valid) {
+          IN* o = out + (row0 + irow) * D + 32 * w + 4 * h;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const float y0 = num[4 * gq] * inv, y1 = num[4 * gq + 1] * inv;
-        const float y2 = num[4 * gq + 2] * inv, y3 = num[4 * gq + 3] * inv;
-        if constexpr (sizeof(IN) == 2) {
-          *reinterpret_cast<u32x2*>(o + 8 * gq) = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
-        } else {
-          *reinterpret_cast<f32x4*>(o + 8 * gq) = f32x4{y0, y1, y2, y3};
+          for (int gq = 0; gq < 4; ++gq) {
+            const float y0 = num[4 * gq] * inv, y1 = num[4 * gq + 1] * inv;
+            const float y2 = num[4 * gq + 2] * inv, y3 = num[4 * gq + 3] * inv;
+            if constexpr (sizeof(IN) == 2) {
+              *reinterpret_cast<u32x2*>(o + 8 * gq) = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+            } else {
+              *reinterpret_cast<f32x4*>(o + 8 * gq) = f32x4{y0, y1, y2, y3};
+            }
+          }
         }
       }
+      // S <- diag(exp(lam_63 - lam_c)) (S' + Kh^T V)
+#pragma unroll(UNR == 2 ? 4 : 1)
+      for (int kb = 0; kb < 4; ++kb) {
+        const auto vf = Ops<OP>::template load_cols<RB>(sV, 16 * kb, 32 * w);
+#pragma unroll
+        for (int fb = 0; fb < NW; ++fb)
+          Ops<OP>::mma(S[fb], Ops<OP>::template load_cols<RB>(sK, 16 * kb, 32 * fb), vf);
+      }
+#pragma unroll
+      for (int fb = 0; fb < NW; ++fb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[fb][r] *= fe[32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)];
+    };
+    // step it: chunk it - 1 (if any); the producers' barriers, one or two a step
+    for (int it = 0; it <= n; ++it) {
+      if (it >= 1) compute(it - 1);
+      if constexpr (NBUF == 1) __syncthreads();
+      __syncthreads();
     }
-    // S <- diag(exp(lam_63 - lam_c)) (S' + Kh^T V)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const Frag vf = Ops<OP>::template load_cols<RB>(sV, 16 * kb, 32 * w);
-#pragma unroll
-      for (int fb = 0; fb < NW; ++fb) Ops<OP>::mma(S[fb], Ops<OP>::template load_cols<RB>(sK, 16 * kb, 32 * fb), vf);
-    }
-#pragma unroll
-    for (int fb = 0; fb < NW; ++fb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[fb][r] *= fe[32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)];
-    __syncthreads();
-  }
-  if (a.S_out && seg == a.nseg - 1) {
-    if (ib == 0) {
+    if (a.S_out && seg == a.nseg - 1) {
 #pragma unroll
       for (int fb = 0; fb < NW; ++fb)
 #pragma unroll
@@ -412,7 +537,6 @@ __global__ __launch_bounds__(D * 4) void gla_output_kernel(GatedArgs g) {
           a.S_out[(long long)bh * D * D + (long long)(32 * fb + 8 * (r >> 2) + 4 * h + (r & 3)) * D + 32 * w + li] =
               S[fb][r];
     }
-    if (t < D) a.z_out[(long long)bh * D + t] = zreg;
   }
 }
 
@@ -424,7 +548,8 @@ hipError_t launch_gated(const GatedArgs& g, const ScanArgs& s, hipStream_t st) {
     const hipError_t e = scan_dispatch(s, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((gla_output_kernel<D, T, T, FM>), dim3(g.f.BH, g.f.nseg), dim3(4 * D), 0, st, g);
+  hipLaunchKernelGGL((gla_output_kernel<D, T, T, FM>), dim3(g.f.BH, g.f.nseg), dim3(gla_output_threads<D>()), 0, st,
+                     g);
   return hipGetLastError();
 }
 
