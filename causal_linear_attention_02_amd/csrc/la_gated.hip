@@ -102,23 +102,33 @@ struct GSet {
 // Loads of the chunk at rows [row0, row0 + valid); rows past `valid` read as
 // zero through the descriptors' range check (log-gate 0: the prefix stays at
 // its last value there). `valid` must be wave-uniform.
+struct GRsrc {
+  __amdgpu_buffer_rsrc_t g, q, k, v;
+};
+template <int D, typename IN>
+__device__ __forceinline__ GRsrc grsrc(const float* lg, const IN* q, const IN* k, const IN* v, long long row0,
+                                       int valid) {
+  const unsigned eb = (unsigned)(valid * D * (int)sizeof(IN));
+  return GRsrc{make_rsrc(lg + row0 * D, (unsigned)(valid * D * 4)), make_rsrc(q ? q + row0 * D : q, eb),
+               make_rsrc(k + row0 * D, eb), make_rsrc(v + row0 * D, eb)};
+}
+// row e of the thread's rows
+template <int D, int NT, typename IN, bool Q>
+__device__ __forceinline__ void gload_row(GSet<D, NT, IN, Q>& s, const GRsrc& r, int e, int t) {
+  using M = GMap<D, NT>;
+  const int gi = t / M::J, j = t % M::J;
+  const int el = (M::R * j + e) * D + 4 * gi;
+  s.lg[e] = __builtin_bit_cast(f32x4, buf_load16(r.g, el * 4));
+  if constexpr (Q) s.q[e] = In4<IN>::bload(r.q, el * (int)sizeof(IN));
+  s.k[e] = In4<IN>::bload(r.k, el * (int)sizeof(IN));
+  s.v[e] = In4<IN>::bload(r.v, el * (int)sizeof(IN));
+}
 template <int D, int NT, typename IN, bool Q>
 __device__ __forceinline__ void gload(GSet<D, NT, IN, Q>& s, const float* lg, const IN* q, const IN* k, const IN* v,
                                       long long row0, int valid, int t) {
-  using M = GMap<D, NT>;
-  const int gi = t / M::J, j = t % M::J;
-  const unsigned eb = (unsigned)(valid * D * (int)sizeof(IN));
-  const auto Rg = make_rsrc(lg + row0 * D, (unsigned)(valid * D * 4));
-  const auto Rk = make_rsrc(k + row0 * D, eb);
-  const auto Rv = make_rsrc(v + row0 * D, eb);
+  const GRsrc r = grsrc<D, IN>(lg, q, k, v, row0, valid);
 #pragma unroll
-  for (int e = 0; e < M::R; ++e) {
-    const int el = (M::R * j + e) * D + 4 * gi;
-    s.lg[e] = __builtin_bit_cast(f32x4, buf_load16(Rg, el * 4));
-    if constexpr (Q) s.q[e] = In4<IN>::bload(make_rsrc(q + row0 * D, eb), el * (int)sizeof(IN));
-    s.k[e] = In4<IN>::bload(Rk, el * (int)sizeof(IN));
-    s.v[e] = In4<IN>::bload(Rv, el * (int)sizeof(IN));
-  }
+  for (int e = 0; e < GMap<D, NT>::R; ++e) gload_row<D, NT, IN, Q>(s, r, e, t);
 }
 
 // In-chunk prefix of the log-gates, in place: p[e][c] becomes
@@ -171,8 +181,9 @@ __device__ __forceinline__ float group_sum(float x) {
 // alike), and the segment's total log-gate per channel (lfac[bh][seg][f]).
 // Per chunk S <- diag(exp(lam_63)) S + Kt^T V with Kt[r] = phi(k_r) exp(lam_63 - lam_r) <= phi(k_r).
 // grid = (BH, P - 1), block = 2*D threads; wave w owns S[:, 32w:32w+32].
-// The next chunk's rows are loaded once this one is staged, during its
-// products; two LDS buffers leave one barrier per chunk.
+// The next chunk's rows are loaded while this one is staged (row by row, in
+// the registers just freed) and multiplied; two LDS buffers leave one
+// barrier per chunk.
 // ---------------------------------------------------------------------------
 template <int D, typename OP, typename IN, int FM>
 __global__ __launch_bounds__(D * 2, 2) void gla_state_kernel(GatedArgs g) {
@@ -206,6 +217,11 @@ __global__ __launch_bounds__(D * 2, 2) void gla_state_kernel(GatedArgs g) {
   GSet<D, NT, IN, false> cur;
   auto step = [&](int m) {
     const int valid = __builtin_amdgcn_readfirstlane(min(64, a.N - 64 * (c0 + m)));
+    // chunk m + 1 (none past the segment): each row's registers take its
+    // row as soon as they are staged, so its loads go out during the staging
+    const int cn = min(c0 + m + 1, a.nchunks - 1);
+    const int vn = __builtin_amdgcn_readfirstlane(m + 1 < n ? min(64, a.N - 64 * cn) : 0);
+    const GRsrc nr = grsrc<D, IN>(g.log_gates, static_cast<const IN*>(nullptr), k, v, base + 64LL * cn, vn);
     uint8_t* sK = smem[m & 1];
     uint8_t* sV = sK + TB;
     float* fb63 = f63[m & 1];
@@ -231,9 +247,9 @@ __global__ __launch_bounds__(D * 2, 2) void gla_state_kernel(GatedArgs g) {
       }
       store4<OP, RB>(sK, row, 4 * gi, x);
       store4_raw<IN, OP, RB>(sV, row, 4 * gi, cur.v[e]);
+      gload_row<D, NT, IN, false>(cur, nr, e, t);
     }
     if (j == 0) *reinterpret_cast<f32x4*>(fb63 + 4 * gi) = e63;
-    load(m + 1, cur);  // in flight during the products below and the next staging's wait
     __syncthreads();
     // S <- diag(exp(lam_63)) S + Kt^T V
 #pragma unroll
@@ -295,7 +311,7 @@ __global__ __launch_bounds__(gla_output_threads<D>()) void gla_output_kernel(Gat
   constexpr int NWP = gla_producer_waves<D>();
   // consumer loops unrolled where the registers allow it (one producer wave
   // per consumer wave)
-  constexpr int UNR = NWP == NW ? 2 : 1;
+  constexpr int UNR = NWP == NW ? 2 : 1, UNR4 = NWP == NW ? 4 : 1;
   constexpr int NTP = 64 * NWP;    // producer threads
   using M = GMap<D, NTP>;
   constexpr int R = M::R, J = M::J;
@@ -340,12 +356,21 @@ __global__ __launch_bounds__(gla_output_threads<D>()) void gla_output_kernel(Gat
     float zreg[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) zreg[c] = zinit ? zinit[4 * gi + c] : 0.f;
-    auto load = [&](int m, GSet<D, NTP, IN, true>& s) {
+    auto rsrc_of = [&](int m) {
       const int c = min(c0 + m, a.nchunks - 1);
       const int valid = __builtin_amdgcn_readfirstlane(m < n ? min(64, a.N - 64 * c) : 0);
-      gload<D, NTP, IN, true>(s, g.log_gates, q, k, v, base + 64LL * c, valid, p);
+      return grsrc<D, IN>(g.log_gates, q, k, v, base + 64LL * c, valid);
     };
+    auto load = [&](int m, GSet<D, NTP, IN, true>& s) {
+      const GRsrc r = rsrc_of(m);
+#pragma unroll
+      for (int e = 0; e < R; ++e) gload_row<D, NTP, IN, true>(s, r, e, p);
+    };
+    // With one register set (PSETS == 1) each row's registers take the same
+    // row of chunk m + 1 as soon as it is staged: the next chunk's loads go
+    // out during the staging rather than after it.
     auto stage = [&](int m, GSet<D, NTP, IN, true>& cur) {
+      const GRsrc nr = rsrc_of(m + 1);
       const int valid = __builtin_amdgcn_readfirstlane(min(64, a.N - 64 * (c0 + m)));
       uint8_t* sQ = smem[m % NBUF];
       uint8_t* sK = sQ + TB;
@@ -389,6 +414,7 @@ __global__ __launch_bounds__(gla_output_threads<D>()) void gla_output_kernel(Gat
           for (int c = 0; c < 4; ++c) xq[c] = round_bf16(xq[c]);
         }
         dq[e] = xq[0] * zcar[0] + xq[1] * zcar[1] + xq[2] * zcar[2] + xq[3] * zcar[3];
+        if constexpr (PSETS == 1) gload_row<D, NTP, IN, true>(cur, nr, e, p);
       }
       // the wave's channel groups: lanes J, 2J, ... apart hold the same rows
 #pragma unroll
@@ -418,7 +444,6 @@ __global__ __launch_bounds__(gla_output_threads<D>()) void gla_output_kernel(Gat
       if constexpr (PSETS == 2) load(it + 1, nxt);
       if constexpr (NBUF == 1) __syncthreads();
       if (it < n) stage(it, cur);
-      if constexpr (PSETS == 1) load(it + 1, nxt);
       __syncthreads();
     };
     if constexpr (PSETS == 2) {
@@ -511,7 +536,7 @@ __global__ __launch_bounds__(gla_output_threads<D>()) void gla_output_kernel(Gat
         }
       }
       // S <- diag(exp(lam_63 - lam_c)) (S' + Kh^T V)
-#pragma unroll(UNR == 2 ? 4 : 1)
+#pragma unroll UNR4
       for (int kb = 0; kb < 4; ++kb) {
         const auto vf = Ops<OP>::template load_cols<RB>(sV, 16 * kb, 32 * w);
 #pragma unroll
