@@ -38,6 +38,10 @@ def parse():
     # back to back for this long; the phase is reported in the JSON
     # ("settle") and lies outside the timed steps.
     p.add_argument("--settle-ms", type=float, default=300.0)
+    # each further workload (gradients, gated, variants, short sequences,
+    # random features, polynomial map) runs back to back this long before
+    # its own warm-up and timed calls, reported as its "settle_ms"
+    p.add_argument("--settle-ms-each", type=float, default=100.0)
     p.add_argument("--decode-steps", type=int, default=1000)
     p.add_argument("--decode-warmup", type=int, default=20)
     p.add_argument("--no-decode", action="store_true")
@@ -156,6 +160,16 @@ def main():
     def fwd(events=None):
         la.la_forward_ex(tq, tk, tv, causal=True, normalize=True, out=out, workspace=ws, events=events)
 
+    def settle_phase(fn, ms):
+        # fn back to back for `ms` milliseconds, outside any timed region
+        torch.cuda.synchronize()
+        t_s = time.perf_counter()
+        while time.perf_counter() - t_s < ms * 1e-3:
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+        return round((time.perf_counter() - t_s) * 1e3, 1)
+
     log(f"prefill: settling the clocks for {args.settle_ms:.0f} ms")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -212,6 +226,7 @@ def main():
         def bwd():
             la.la_backward(tq, tk, tv, tdy, normalize=True, dq=gq, dk=gk, dv=gv, workspace=bws)
 
+        b_settle = settle_phase(bwd, args.settle_ms_each)
         for _ in range(10):
             bwd()
         torch.cuda.synchronize()
@@ -226,7 +241,7 @@ def main():
         backward = {
             "metric": "causal linear-attn gradients (dq, dk, dv) head-tokens/s",
             "value": head_tokens / bwall, "unit": "head-tokens/s", "us_per_call": round(bwall * 1e6, 1),
-            "steps": args.backward_steps, "forward_us_per_call": round(ms_step * 1e3, 1),
+            "steps": args.backward_steps, "settle_ms": b_settle, "forward_us_per_call": round(ms_step * 1e3, 1),
             "config": {"workload": "prefill_b1h16n65536d128", "batch": B, "heads": H, "seq_len": N, "d": d,
                        "feature_map": "elu1", "normalize": True, "dout": "N(0,1) bf16, seeded"},
             "min_traffic": {"bytes": min_bytes, "achieved_gbs": round(min_bytes / bwall / 1e9, 1),
@@ -247,6 +262,7 @@ def main():
         def gfwd():
             la.la_forward_gated(tq, tk, tv, tlg, normalize=True, out=out, workspace=gws)
 
+        g_settle = settle_phase(gfwd, args.settle_ms_each)
         for _ in range(10):
             gfwd()
         torch.cuda.synchronize()
@@ -260,7 +276,7 @@ def main():
         gated = {
             "metric": "causal gated linear-attn prefill tokens/s (per-channel gates)",
             "value": tokens / gwall, "unit": "tokens/s", "us_per_call": round(gwall * 1e6, 1),
-            "steps": args.gated_steps,
+            "steps": args.gated_steps, "settle_ms": g_settle,
             "config": {"workload": "prefill_b1h16n65536d128", "batch": B, "heads": H, "seq_len": N, "d": d,
                        "feature_map": "elu1", "normalize": True, "gates": "log U(1/4, 1), fp32, per token and channel"},
             "whole_op": {"bytes": g_bytes, "achieved_gbs": round(g_bytes / gwall / 1e9, 1),
@@ -285,6 +301,7 @@ def main():
             "non_causal": lambda: la.la_forward(tq, tk, tv, causal=False, normalize=True, out=out, workspace=ws_nc),
         }
         for name, fn in runs.items():
+            v_settle = settle_phase(fn, args.settle_ms_each)
             for _ in range(20):
                 fn()
             torch.cuda.synchronize()
@@ -294,6 +311,7 @@ def main():
             torch.cuda.synchronize()
             vw = (time.perf_counter() - t0) / 20
             variants[name] = {"us_per_call": round(vw * 1e6, 1), "tokens_per_s": tokens / vw,
+                              "settle_ms": v_settle,
                               "whole_op_frac_hbm": round(alg_bytes / vw / 1e9 / HBM_PEAK_GBS, 4)}
             log(f"{name}: {vw*1e6:.1f} us/call")
         variants["note"] = ("same workload and bytes as the headline prefill; decay: gamma per head "
@@ -304,6 +322,8 @@ def main():
     torch.cuda.empty_cache()
 
     def time_calls(fn, warm, steps):
+        # (seconds per call, settle phase in ms)
+        st_ms = settle_phase(lambda: fn(0), args.settle_ms_each)
         for i in range(warm):
             fn(i)
         torch.cuda.synchronize()
@@ -311,7 +331,7 @@ def main():
         for i in range(steps):
             fn(i)
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps
+        return (time.perf_counter() - t0) / steps, st_ms
 
     # ---------------- elu+1 prefill at B=4 H=8 N=2048 d=64 ----------------
     # 33.6 MB per input set fits in the 256 MB last-level cache, so the calls
@@ -331,14 +351,14 @@ def main():
             sq_, sk_, sv_, so_ = sets[i % 8]
             la.la_forward(sq_, sk_, sv_, causal=True, normalize=True, out=so_, workspace=mws)
 
-        mwall = time_calls(mfwd, 80, args.mid_steps)
+        mwall, m_settle = time_calls(mfwd, 80, args.mid_steps)
         m_ht = Bm * Hm * Nm
         m_bytes = m_ht * 4 * dm * 2
         m_flops = m_ht * (4 * dm * dm + (C + 1) * 2 * dm)
         t_roof = max(m_bytes / (HBM_PEAK_GBS * 1e9), m_flops / (BF16_MFMA_PEAK_TFLOPS * 1e12))
         mid = {
             "metric": "causal linear-attn prefill tokens/s", "value": Bm * Nm / mwall, "unit": "tokens/s",
-            "us_per_call": round(mwall * 1e6, 2), "steps": args.mid_steps,
+            "us_per_call": round(mwall * 1e6, 2), "steps": args.mid_steps, "settle_ms": m_settle,
             "config": {"workload": "prefill_b4h8n2048d64", "batch": Bm, "heads": Hm, "seq_len": Nm, "d": dm,
                        "feature_map": "elu1", "causal": True, "normalize": True, "input_sets": 8},
             "whole_op": {"bytes": m_bytes, "achieved_gbs": round(m_bytes / mwall / 1e9, 1),
@@ -367,7 +387,7 @@ def main():
             la.la_forward(fq, fk, fv, feature_map="performer", W=fW, causal=True, normalize=True, out=fout,
                           workspace=fws)
 
-        fwall = time_calls(ffwd, 40, args.performer_steps)
+        fwall, f_settle = time_calls(ffwd, 40, args.performer_steps)
         f_ht = Bf * Hf * Nf
         f_bytes = f_ht * 4 * df * 2
         # projections of q and k (2 m d each), read-out and state update
@@ -377,6 +397,7 @@ def main():
         perf = {
             "metric": "causal random-feature linear-attn prefill tokens/s", "value": Bf * Nf / fwall,
             "unit": "tokens/s", "us_per_call": round(fwall * 1e6, 2), "steps": args.performer_steps,
+            "settle_ms": f_settle,
             "config": {"workload": "performer_b2h8n16384d64m256", "batch": Bf, "heads": Hf, "seq_len": Nf,
                        "d": df, "features": mf, "feature_map": "performer", "causal": True, "normalize": True},
             "whole_op": {"bytes": f_bytes, "flops": f_flops, "achieved_gbs": round(f_bytes / fwall / 1e9, 1),
@@ -395,7 +416,7 @@ def main():
             la.la_forward(fq, fk, fv, feature_map="performer", W=fW, causal=False, normalize=True, out=fout,
                           workspace=fws_nc)
 
-        fwall_nc = time_calls(ffwd_nc, 40, args.performer_steps)
+        fwall_nc, _ = time_calls(ffwd_nc, 40, args.performer_steps)
         # k, v read for the sums, q read and out written for the read-out;
         # projections of k and q, state update and read-out (2 m d FLOP each)
         nc_flops = f_ht * 8 * mf * df
@@ -426,6 +447,7 @@ def main():
         def pfwd():
             la.la_forward(pq, pk, pv, feature_map="poly2", normalize=True, out=pout, workspace=pws)
 
+        p_settle = settle_phase(pfwd, args.settle_ms_each)
         for _ in range(20):
             pfwd()
         torch.cuda.synchronize()
@@ -443,7 +465,7 @@ def main():
         poly = {
             "metric": "causal prefill tokens/s, degree-2 polynomial map (d' = 1 + d + d^2)",
             "value": Bp * Np / pwall, "unit": "tokens/s", "us_per_call": round(pwall * 1e6, 1),
-            "steps": args.poly_steps,
+            "steps": args.poly_steps, "settle_ms": p_settle,
             "config": {"workload": "prefill_b4h8n2048d64", "batch": Bp, "heads": Hp, "seq_len": Np, "d": dp,
                        "feature_dim": 1 + dp + dp * dp, "feature_map": "poly2", "normalize": True},
             "mfma": {"useful_tflops": round(p_tf, 2), "frac_bf16_mfma": round(p_tf / BF16_MFMA_PEAK_TFLOPS, 4),
