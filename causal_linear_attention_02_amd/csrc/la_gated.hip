@@ -73,6 +73,20 @@ __device__ __forceinline__ void store4(uint8_t* tile, int row, int col, const fl
     *reinterpret_cast<f32x4*>(tile + tile_off<RB>(row, col * 4)) = f32x4{x[0], x[1], x[2], x[3]};
   }
 }
+// The same, and x becomes the values as the tile holds them (bf16: rounded)
+template <typename OP, int RB>
+__device__ __forceinline__ void store4_held(uint8_t* tile, int row, int col, float (&x)[4]) {
+  if constexpr (sizeof(OP) == 2) {
+    const u32x2 pk = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+    *reinterpret_cast<u32x2*>(tile + tile_off<RB>(row, col * 2)) = pk;
+    x[0] = __uint_as_float(pk[0] << 16);
+    x[1] = __uint_as_float(pk[0] & 0xffff0000u);
+    x[2] = __uint_as_float(pk[1] << 16);
+    x[3] = __uint_as_float(pk[1] & 0xffff0000u);
+  } else {
+    *reinterpret_cast<f32x4*>(tile + tile_off<RB>(row, col * 4)) = f32x4{x[0], x[1], x[2], x[3]};
+  }
+}
 template <typename IN, typename OP, int RB>
 __device__ __forceinline__ void store4_raw(uint8_t* tile, int row, int col, const typename In4<IN>::raw& r) {
   static_assert(sizeof(IN) == sizeof(OP), "raw staging needs matching element types");
@@ -135,14 +149,26 @@ __device__ __forceinline__ void gload(GSet<D, NT, IN, Q>& s, const float* lg, co
 // lam = lg_0 + ... + lg_r at row r = R j + e, channel 4 g + c (fp32). A
 // log-gate outside [log(1/4), 0] becomes NaN (checked_log_gate), so the
 // prefix of its channel is NaN from its row on, and raises the status flag.
+// The thread's values are checked at once through their NaN-propagating
+// minimum and maximum; only a thread holding a bad one checks them one by one.
 template <int D, int NT, int NR>
 __device__ __forceinline__ void gate_scan(f32x4 (&p)[NR], int* flag, int t) {
   using M = GMap<D, NT>;
   static_assert(NR == M::R, "rows per thread");
+  float mn = p[0][0], mx = p[0][0];
 #pragma unroll
   for (int e = 0; e < M::R; ++e)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) p[e][c] = checked_log_gate(p[e][c], flag);
+    for (int c = 0; c < 4; ++c) {
+      mn = __builtin_elementwise_minimum(mn, p[e][c]);
+      mx = __builtin_elementwise_maximum(mx, p[e][c]);
+    }
+  if (!(mn >= kMinLogFactor && mx <= 0.f)) {
+#pragma unroll
+    for (int e = 0; e < M::R; ++e)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) p[e][c] = checked_log_gate(p[e][c], flag);
+  }
 #pragma unroll
   for (int e = 1; e < M::R; ++e) p[e] += p[e - 1];
   // inclusive scan of the row-block totals across the group's lanes, then
@@ -185,8 +211,9 @@ __device__ __forceinline__ float group_sum(float x) {
 // the registers just freed) and multiplied; two LDS buffers leave one
 // barrier per chunk.
 // ---------------------------------------------------------------------------
+// two workgroups per CU where the LDS holds two (bf16 tiles)
 template <int D, typename OP, typename IN, int FM>
-__global__ __launch_bounds__(D * 2, 2) void gla_state_kernel(GatedArgs g) {
+__global__ __launch_bounds__(D * 2, (sizeof(IN) == 2 ? 2 : 1)) void gla_state_kernel(GatedArgs g) {
   constexpr int NW = D / 32, NT = 2 * D;
   using M = GMap<D, NT>;
   constexpr int R = M::R, J = M::J;
@@ -405,14 +432,9 @@ __global__ __launch_bounds__(gla_output_threads<D>()) void gla_output_kernel(Gat
           xk[c] = row < valid ? gphi<FM>(xk[c]) * __builtin_amdgcn_rcpf(f) : 0.f;
           cs[c] += xk[c];
         }
-        store4<OP, RB>(sQ, row, 4 * gi, xq);
+        store4_held<OP, RB>(sQ, row, 4 * gi, xq);  // xq: Qh as the operand holds it
         store4<OP, RB>(sK, row, 4 * gi, xk);
         store4_raw<IN, OP, RB>(sV, row, 4 * gi, cur.v[e]);
-        // with Qh as the operand holds it (bf16: rounded)
-        if constexpr (sizeof(OP) == 2) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) xq[c] = round_bf16(xq[c]);
-        }
         dq[e] = xq[0] * zcar[0] + xq[1] * zcar[1] + xq[2] * zcar[2] + xq[3] * zcar[3];
         if constexpr (PSETS == 1) gload_row<D, NTP, IN, true>(cur, nr, e, p);
       }
