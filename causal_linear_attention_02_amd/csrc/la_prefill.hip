@@ -287,8 +287,10 @@ __device__ __forceinline__ void stage_k_piece(typename In8<IN>::raw r, int p, in
 // kept as gamma^-31 times the true ones; then one chunk moves them on as
 // S' <- gamma^64 S' + K^T V with the scaled keys, and the carried term of row
 // r_i, gamma^(r_i+1) phi(q_i) S, is (scaled q_i) . (gamma^64 S'). With
-// gamma >= 1/4 no scale exceeds 2^64; gamma^64 itself can fall below the
-// normal fp32 range, so it is applied as gamma^32 twice.
+// gamma >= 1/4 no scale exceeds 2^64. gamma^64 is formed as gamma^32
+// squared: below gamma = 0.2552 it is a denormal (2^-128 at gamma = 1/4),
+// and the state it moves on is then 2^-126 or less of the chunk's own
+// terms. The running normalizers take gamma^32 twice.
 // ---------------------------------------------------------------------------
 constexpr int kDecayCenter = 32;
 constexpr int kDecayFrame = kChunk - 1 - kDecayCenter;  // 31
@@ -427,7 +429,7 @@ __global__ __launch_bounds__((StateGeo<D, HILO>::NT), (HILO ? 2 : 1)) void state
   for (int e = 0; e < 8; ++e) zr[e] = 0.f;
   const Voff<D, DF, IN, NT> vo(p);
   const float lg = DECAY ? decay_log2(a.gamma[bh % a.H], a.status_flag) : 0.f;
-  const float gH = DECAY ? gpow(lg, kChunk / 2) : 1.f;  // gamma^32; a chunk moves states on by gH twice
+  const float gH = DECAY ? gpow(lg, kChunk / 2) : 1.f;  // gamma^32; a chunk moves states on by gH^2
 
   // every load is issued (with zero size past the segment) so that all
   // iterations have the same memory instruction stream
@@ -503,7 +505,7 @@ __global__ __launch_bounds__((StateGeo<D, HILO>::NT), (HILO ? 2 : 1)) void state
     const uint8_t* sV = sK + KB;
     if constexpr (DECAY) {
 #pragma unroll
-      for (int cb = 0; cb < DF / 32; ++cb) S[cb] = (S[cb] * gH) * gH;
+      for (int cb = 0; cb < DF / 32; ++cb) S[cb] *= gH * gH;
     }
     Frag Vf[SG::KPW];
 #pragma unroll
@@ -719,7 +721,7 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
   // state (scaled frame back to the true one, and a partial last chunk of
   // vl rows moved on by gamma^vl instead of gamma^64)
   const float lg = DECAY ? decay_log2(a.gamma[bh % a.H], a.status_flag) : 0.f;
-  const float gH = DECAY ? gpow(lg, kChunk / 2) : 1.f;  // gamma^32; a chunk moves states on by gH twice
+  const float gH = DECAY ? gpow(lg, kChunk / 2) : 1.f;  // gamma^32; a chunk moves states on by gH^2
   const int vl = a.N - kChunk * (a.nchunks - 1);
   const float fout = DECAY ? gpow(lg, kDecayFrame + vl - kChunk) : 1.f;
   const float fin = DECAY ? gpow(lg, -kDecayFrame) : 1.f;
@@ -1026,7 +1028,7 @@ __global__ __launch_bounds__(D * 4) void output_pass_kernel(FwdArgs a) {
         if constexpr (DECAY) {  // the state as the next chunk's rows see it: moved on by gamma^64
           if (it < n) {
 #pragma unroll
-            for (int cb = 0; cb < DF / 32; ++cb) S[cb] = (S[cb] * gH) * gH;
+            for (int cb = 0; cb < DF / 32; ++cb) S[cb] *= gH * gH;
           }
         }
       }
