@@ -278,7 +278,7 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
   const float* Sp;
   const float* zp;
   if (a.init_from_ws) {
-    Sp = a.ws_fwd + ((long long)bh * a.fwd_slots + seg) * a.state_elems;
+    Sp = a.ws_fwd + ((long long)bh * a.fwd_slots + seg * a.seg_stride) * a.state_elems;
     zp = Sp + D * D;
   } else {
     Sp = a.S_in ? a.S_in + (long long)bh * D * D : nullptr;
@@ -544,9 +544,9 @@ __global__ __launch_bounds__(D * 2) void bwd_rstate_kernel(BwdArgs a) {
   uint8_t* sQ = smem;
   uint8_t* sG = smem + TB;
 
-  const int bh = blockIdx.x, seg = blockIdx.y;
-  const int c0 = seg * a.chunks_per_seg;
-  const int n = max(0, min(c0 + a.chunks_per_seg, a.nchunks) - c0);
+  const int bh = blockIdx.x, seg = blockIdx.y;  // a state-pass segment
+  const int c0 = seg * a.chunks_per_seg_state;
+  const int n = max(0, min(c0 + a.chunks_per_seg_state, a.nchunks) - c0);
   const int t = threadIdx.x, w = t >> 6, l = t & 63, h = l >> 5, li = l & 31;
   const long long base = (long long)bh * a.N;
   const IN* q = static_cast<const IN*>(a.q);
@@ -616,10 +616,10 @@ __global__ __launch_bounds__(D * 2) void bwd_rstate_kernel(BwdArgs a) {
     for (int e = 0; e < 8; ++e) rsum[w][col + e] = cs[e];
   }
   __syncthreads();
-  float* st = a.ws_rev + ((long long)bh * (a.nseg + 1) + (a.nseg - 1 - seg)) * a.state_elems;
+  float* st = a.ws_rev + ((long long)bh * (a.nseg_state + 1) + (a.nseg_state - 1 - seg)) * a.state_elems;
   // decay: the last segment also carries the final-state cotangents, which
   // reach the row before the segment with gamma^(N - s0)
-  const bool seed = DECAY && a.dS_out && seg == a.nseg - 1;
+  const bool seed = DECAY && a.dS_out && seg == a.nseg_state - 1;
   const float fs = seed ? dc.pw((float)(a.N - 64 * c0)) : 0.f;
   const float* sS = seed ? a.dS_out + (long long)bh * D * D : nullptr;
   const float* sz = seed ? a.dz_out + (long long)bh * D : nullptr;
@@ -690,7 +690,8 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
   const float* sS = seed ? a.dS_out + (long long)bh * D * D : nullptr;
   const float* sz = seed ? a.dz_out + (long long)bh * D : nullptr;
 
-  const float* Rp = a.ws_rev + ((long long)bh * (a.nseg + 1) + (a.nseg - 1 - seg)) * a.state_elems;
+  const int last = min(seg * a.seg_stride + a.seg_stride - 1, a.nseg_state - 1);  // its last state-pass segment
+  const float* Rp = a.ws_rev + ((long long)bh * (a.nseg_state + 1) + (a.nseg_state - 1 - last)) * a.state_elems;
   f32x16 RS[NW], rK;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -973,7 +974,7 @@ hipError_t launch_backward(const FwdArgs& fa, const ScanArgs& fs, const BwdArgs&
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((bwd_dq_kernel<D, T, T, FM, DECAY>), dim3(b.BH, b.nseg), dim3(4 * D), 0, st, b);
-  hipLaunchKernelGGL((bwd_rstate_kernel<D, T, T, FM, DECAY>), dim3(b.BH, b.nseg), dim3(2 * D), 0, st, b);
+  hipLaunchKernelGGL((bwd_rstate_kernel<D, T, T, FM, DECAY>), dim3(b.BH, b.nseg_state), dim3(2 * D), 0, st, b);
   const hipError_t e = scan_dispatch(rs, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkv_kernel<D, T, T, FM, DECAY>), dim3(b.BH, b.nseg), dim3(4 * D), 0, st, b);

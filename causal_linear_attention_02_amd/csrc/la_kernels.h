@@ -95,15 +95,19 @@ struct BwdArgs {
   void* dk;
   void* dv;
   int BH, N, nchunks;
-  int nseg, chunks_per_seg;
+  int nseg, chunks_per_seg;  // segments of the dq and dk/dv passes
+  // The state passes (forward states, r-state pass, both scans) split each
+  // of those segments into seg_stride (1 or 2) segments of chunks_per_seg_state
+  // chunks, nseg_state in all; the state slots below count those.
+  int nseg_state, chunks_per_seg_state, seg_stride;
   int normalize;
-  const float* ws_fwd;     // [BH][fwd_slots][state_elems]: state entering segment s (slot s)
+  const float* ws_fwd;     // [BH][fwd_slots][state_elems]: state entering state-pass segment s (slot s)
   int fwd_slots;
   int init_from_ws;        // else S_in / z_in (or zero) enter the single segment
   const float* S_in;
   const float* z_in;
-  float* ws_rev;           // [BH][nseg + 1][state_elems]: slot nseg-1-s holds segment s's sums, then
-                           // (after the scan) the cotangent of the state leaving segment s
+  float* ws_rev;           // [BH][nseg_state + 1][state_elems]: slot nseg_state-1-s holds state-pass
+                           // segment s's sums, then (after the scan) the cotangent of the state leaving it
   int state_elems;         // D * D + D
   float* rowstats;         // [BH][N][2]: 1 / max(den, eps), d loss / d den
   const float* gamma;      // decay per head [H] or null
