@@ -889,8 +889,12 @@ int la_forward_gated(const void* q, const void* k, const void* v, const float* l
   a.BH = (int)BH;
   a.N = N;
   a.nchunks = p.nchunks;
-  a.nseg = p.P;
-  a.chunks_per_seg = p.cps;
+  // The output pass (one workgroup per CU) runs whole segments of two
+  // state-pass segments when the state pass's split needs two rounds of
+  // workgroups; the state pass (two workgroups per CU) keeps the finer split.
+  const int stride = (p.P >= 2 && BH * p.P >= 2 * kTargetBlocks) ? 2 : 1;
+  a.nseg = (p.P + stride - 1) / stride;
+  a.chunks_per_seg = p.cps * stride;
   a.nseg_state = p.Ps;
   a.chunks_per_seg_state = p.cpss;
   a.run_state_pass = p.state_pass;
@@ -908,6 +912,8 @@ int la_forward_gated(const void* q, const void* k, const void* v, const float* l
   a.status_flag = flag;
   ga.log_gates = log_gates;
   ga.lfac = g.lfac_bytes ? reinterpret_cast<float*>(wsb + g.state_bytes) : nullptr;
+  ga.lfac_stride = p.P;
+  ga.seg_stride = stride;
 
   la::ScanArgs s{};
   s.ws = a.ws;

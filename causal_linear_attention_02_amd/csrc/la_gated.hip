@@ -303,7 +303,7 @@ __global__ __launch_bounds__(D * 2, (sizeof(IN) == 2 ? 2 : 1)) void gla_state_ke
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       st[D * D + 4 * gi + c] = zr[c];
-      g.lfac[((long long)bh * a.nseg + seg) * D + 4 * gi + c] = ltot[c];
+      g.lfac[((long long)bh * g.lfac_stride + seg) * D + 4 * gi + c] = ltot[c];
     }
   }
 }
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(gla_output_threads<D>()) void gla_output_kernel(Gat
   const float* Sinit;
   const float* zinit;
   if (a.init_from_ws) {
-    Sinit = a.ws + ((long long)bh * a.ws_slots + seg) * a.state_elems;
+    Sinit = a.ws + ((long long)bh * a.ws_slots + seg * g.seg_stride) * a.state_elems;
     zinit = Sinit + D * D;
   } else {
     Sinit = a.S_in ? a.S_in + (long long)bh * D * D : nullptr;

@@ -123,7 +123,12 @@ struct BwdArgs {
 struct GatedArgs {
   FwdArgs f;
   const float* log_gates;  // [BH][N][D] fp32, natural log of the gates, in [-log 4, 0]
-  float* lfac;             // [BH][f.nseg][D] fp32 (workspace)
+  float* lfac;             // [BH][lfac_stride][D] fp32 (workspace): total log-gate of each state-pass segment
+  int lfac_stride;
+  // output-pass segment s starts where state-pass segment s * seg_stride does
+  // (its state in ws slot s * seg_stride); f.nseg, f.chunks_per_seg describe
+  // the output pass, f.nseg_state, f.chunks_per_seg_state the state pass
+  int seg_stride;
 };
 
 // Degree-2 polynomial map (d' = 1 + d + d^2), chunked forward. Workspace:
