@@ -174,6 +174,40 @@ def test_backward_full_b1h16n65536d128_sampled_heads():
         assert ez <= TOL["bf16"], (h, "dz_in", ez)
 
 
+@pytest.mark.parametrize("decay", [False, True])
+def test_backward_odd_segment_count(decay):
+    """B1 H3 with 684 chunks (a ragged tail of 47 tokens): the state passes
+    split each sequence into 171 segments, and the dq and dk/dv passes, which
+    take two of those per segment, end on a segment of one. Every gradient of
+    every head, with final-state cotangents, against the recurrent form of the
+    oracle's gradients."""
+    B, H, N, d = 1, 3, 64 * 684 - 17, 64
+    log(f"case backward B{B} H{H} N{N} d{d} bf16 decay={decay} (171 state-pass segments)")
+    q, k, v = qkv(B, H, N, d, 77, "bf16", 1.0)
+    dy = _dout(B, H, N, d, 77, "bf16")
+    rng = np.random.default_rng(78)
+    dS = (rng.standard_normal((B, H, d, d)) * 0.1).astype(np.float32)
+    dz = (rng.standard_normal((B, H, d)) * 0.1).astype(np.float32)
+    args = (to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(dy, "bf16"))
+    kw = dict(dS_out=torch.from_numpy(dS).cuda(), dz_out=torch.from_numpy(dz).cuda(), return_state_grad=True)
+    g = _gammas(H)
+    if decay:
+        res = la.la_backward_decay(*args, torch.from_numpy(g).cuda(), **kw)
+    else:
+        res = la.la_backward(*args, **kw)
+    torch.cuda.synchronize()
+    for h in range(H):
+        ref = O.recurrent_backward(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], dy[:, h:h + 1], "elu1",
+                                   dS_N=dS[:, h:h + 1], dz_N=dz[:, h:h + 1],
+                                   decay=g[h:h + 1].astype(np.float64) if decay else None)
+        for name, got, r in zip(("dq", "dk", "dv", "dS_in"), res[:4], ref[:4]):
+            err = _err(to_host(got[:, h:h + 1]), r, dy[:, h:h + 1], skip_row0=(name == "dq"))
+            log(f"  head {h} {name} rel err {err:.3e}")
+            assert err <= TOL["bf16"], (h, name, err)
+        ez = _err(to_host(res[4][:, h:h + 1])[..., None, :], ref[4][..., None, :], dy[:, h:h + 1])
+        assert ez <= TOL["bf16"], (h, "dz_in", ez)
+
+
 # --- decay (per-head gamma): gradients of la_forward_decay ---------------------------------------------------
 
 

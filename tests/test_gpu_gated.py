@@ -173,6 +173,30 @@ def test_gated_full_b1h16n65536d128_sampled_heads():
         assert e <= TOL["bf16"] and eS <= TOL["bf16"]
 
 
+def test_gated_odd_segment_count():
+    """B1 H3 with 684 chunks (a ragged tail of 47 tokens): the state pass splits
+    each sequence into 171 segments, and the output pass, which takes two of
+    those per segment, ends on a segment of one. Every head, with a state in
+    and out, against the oracle's blockwise form."""
+    B, H, N, d = 1, 3, 64 * 684 - 17, 64
+    log(f"case gated forward B{B} H{H} N{N} d{d} bf16 (171 state-pass segments)")
+    q, k, v = qkv(B, H, N, d, 19, "bf16", 1.0)
+    lg = _g((B, H, N, d), 19, 0.25)
+    rng = np.random.default_rng(20)
+    S0 = (rng.standard_normal((B, H, d, d)) * 0.5).astype(np.float32)
+    z0 = rng.uniform(0.5, 2.0, (B, H, d)).astype(np.float32)
+    y, S, z = la.la_forward_gated(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                                  torch.from_numpy(lg).cuda(), S_in=torch.from_numpy(S0).cuda(),
+                                  z_in=torch.from_numpy(z0).cuda(), return_state=True)
+    torch.cuda.synchronize()
+    yr, Sr, zr = O.gated_chunked(q, k, v, lg, S0=S0, z0=z0)
+    e = rel_err(to_host(y), yr)
+    eS = rel_err(to_host(S), Sr)
+    ez = rel_err(to_host(z)[..., None], zr[..., None])
+    log(f"  rel err y {e:.3e} S {eS:.3e} z {ez:.3e}")
+    assert e <= TOL["bf16"] and eS <= TOL["bf16"] and ez <= TOL["bf16"]
+
+
 def test_gated_out_of_range_gate_is_flagged():
     """One gate below 1/4 in one head (token 200, channel 5): that head's
     outputs from the chunk of that token on are NaN, earlier rows and the
