@@ -19,12 +19,16 @@
 // Qh_i . diag(exp(lam_c)) S) and by exp(lam_63 - lam_c) after adding Kh^T V.
 // With alpha >= 1/4 no factor exceeds exp(32 log 4) = 2^64.
 //
-// Passes (the forward's segment split, P segments of whole chunks):
+// Passes (each sequence split into P segments of whole chunks; d' = d):
 //   gla_state_kernel : local (S, z) of every segment but the last, relative to
 //                      the segment's end, and the segment's total log-gate
 //   carry scan       : P_{s+1} = diag(exp(total_s)) P_s + local_s (la_prefill.hip)
-//   gla_output_kernel: every segment from its carried state
-// All waves load and stage (no producer/consumer split); d' = d.
+//   gla_output_kernel: every segment from its carried state; producer waves
+//                      stage the gated q, k tiles while consumer waves run
+//                      the previous chunk's products. Where the split needs
+//                      two rounds of workgroups it takes two of the state
+//                      pass's segments at a time (GatedArgs::seg_stride).
+// Both passes load the next chunk while they stage the current one.
 #include "la_device.h"
 #include "la_kernels.h"
 
