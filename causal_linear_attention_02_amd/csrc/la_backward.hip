@@ -14,8 +14,9 @@
 // r_j = dz_N + sum_{i>=j} phi(q_i) h_i, and dq, dk through phi'
 // (elu+1: phi' = 1 for x > 0, exp(x) otherwise, i.e. min(phi(x), 1)).
 //
-// Passes (each (batch, head) sequence split into P segments of whole chunks,
-// as in the forward):
+// Passes (each (batch, head) sequence split into P segments of whole chunks
+// for the state passes and scans; the dq and dk/dv passes take seg_stride
+// (1 or 2) of those at a time):
 //   forward state pass + carry scan : state (S, z) entering every segment
 //   dq pass      : per chunk, in order: scores, value products, numerator and
 //                  denominator terms -> D_i, h_i (kept per token), dq
