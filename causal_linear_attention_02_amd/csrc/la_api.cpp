@@ -573,6 +573,11 @@ int la_feature_map_apply(const void* x, void* phi, long long rows, int d, const 
 
 namespace {
 
+// Segments of a pass with one workgroup per CU, in state-pass segments: two
+// where P state-pass segments per sequence need two rounds of workgroups
+// (B*H*P >= 512), else one.
+int paired_segments(long long BH, int P) { return (P >= 2 && BH * P >= 2 * kTargetBlocks) ? 2 : 1; }
+
 struct BwdPlan {
   int nchunks = 0, P = 1, cps = 0;
   size_t fwd_bytes = 0, rev_bytes = 0, row_bytes = 0, ws_bytes = 0;
@@ -730,7 +735,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* dout,
   // state-pass segments when the state passes' split needs two rounds of
   // workgroups; the state passes (two workgroups per CU) stay faster at the
   // finer split. Gradients on B1 H16 N65536 d128: 1307-1319 -> 1277-1302 us.
-  const int stride = (p.P >= 2 && BH * p.P >= 2 * kTargetBlocks) ? 2 : 1;
+  const int stride = paired_segments(BH, p.P);
   b.nseg = (p.P + stride - 1) / stride;
   b.chunks_per_seg = p.cps * stride;
   b.nseg_state = p.P;
@@ -892,7 +897,7 @@ int la_forward_gated(const void* q, const void* k, const void* v, const float* l
   // The output pass (one workgroup per CU) runs whole segments of two
   // state-pass segments when the state pass's split needs two rounds of
   // workgroups; the state pass (two workgroups per CU) keeps the finer split.
-  const int stride = (p.P >= 2 && BH * p.P >= 2 * kTargetBlocks) ? 2 : 1;
+  const int stride = paired_segments(BH, p.P);
   a.nseg = (p.P + stride - 1) / stride;
   a.chunks_per_seg = p.cps * stride;
   a.nseg_state = p.Ps;
