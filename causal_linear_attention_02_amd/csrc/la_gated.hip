@@ -12,7 +12,7 @@
 // row i through channel f with weight exp(lam_if - lam_jf) (j <= i), the
 // state carried into the chunk with exp(lam_if), and the chunk moves it on
 // as S <- diag(exp(lam_63)) S + sum_j diag(exp(lam_63 - lam_j)) phi(k_j) v_j^T.
-// With c = 32 the output pass stages
+// With c = 31 (lam_c is the first half's total) the output pass stages
 //   Qh[r][f] = phi(q_r)_f exp(lam_rf - lam_cf),  Kh[r][f] = phi(k_r)_f exp(lam_cf - lam_rf),
 // so Qh Kh^T carries exactly those weights, and it scales the carried state
 // by exp(lam_c) before the readout (the carried term of row i is
@@ -36,7 +36,6 @@ namespace la {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kCenter = 32;
 
 template <int FM>
 __device__ __forceinline__ float gphi(float x) {
@@ -45,6 +44,26 @@ __device__ __forceinline__ float gphi(float x) {
 }
 __device__ __forceinline__ float exp_nat(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
+// Cross-lane moves of the gate layout below: DPP inside a 16-lane row and
+// the gfx950 row swaps between rows run on the vector ALU, where a shuffle
+// through ds_bpermute costs an LDS round trip and its address arithmetic.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kRowShr = 0x110;  // + s: the value of lane l - s of the same row (0 before the row's start)
+constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;
+constexpr int kMirror = 0x140;
+constexpr int kRor4 = 0x124;
+constexpr int kRor8 = 0x128;
+// the value of lane l ^ 16
+__device__ __forceinline__ float xor16(float x) {
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // even rows receive the odd row above in s[1]; odd rows the even row below in s[0]
+  return __uint_as_float((threadIdx.x & 16) ? s[0] : s[1]);
+}
 // 4 consecutive input elements: raw form (one buffer load) and fp32
 template <typename IN> struct In4;
 template <> struct In4<__bf16> {
@@ -91,30 +110,43 @@ __device__ __forceinline__ void store4_held(uint8_t* tile, int row, int col, flo
     *reinterpret_cast<f32x4*>(tile + tile_off<RB>(row, col * 4)) = f32x4{x[0], x[1], x[2], x[3]};
   }
 }
-template <typename IN, typename OP, int RB>
-__device__ __forceinline__ void store4_raw(uint8_t* tile, int row, int col, const typename In4<IN>::raw& r) {
-  static_assert(sizeof(IN) == sizeof(OP), "raw staging needs matching element types");
-  *reinterpret_cast<typename In4<IN>::raw*>(tile + tile_off<RB>(row, col * (int)sizeof(IN))) = r;
-}
 
 // Thread layout of the gated passes' loads and staging: NT threads over a
 // 64 x D chunk. Thread t holds channels [4 g, 4 g + 4) of the R consecutive
-// rows [R j, R j + R), with g = t / J and j = t % J. The J threads of a
-// channel group are consecutive lanes of one wave, so the in-chunk prefix of
-// the log-gates is a sum in registers over R rows and a scan across J lanes,
-// and per-channel values of one row are a lane broadcast away.
+// rows [R j, R j + R) (row block j of channel group g). A wave holds GW = R
+// channel groups of all J row blocks, lane l = g % GW + GW j: the 16 lanes of
+// a DPP row then hold 16 / GW row blocks of 4 GW consecutive channels, so a
+// load of those lanes covers 2 (or 4) row pieces of 64 (or 32) bytes rather
+// than 8 (or 16) pieces of 16. The in-chunk prefix of the log-gates is a sum
+// in registers over R rows and a scan over the J lanes of the group, GW apart.
 template <int D, int NT>
 struct GMap {
-  static constexpr int CG = D / 4, J = NT / CG, R = 64 / J;
-  static_assert(NT % CG == 0 && 64 % J == 0 && R >= 1, "gate layout");
+  static constexpr int CG = D / 4, J = NT / CG, R = 64 / J, GW = R;
+  static constexpr int PR = 16 / GW;  // row blocks of a group in one DPP row
+  static_assert(NT % 64 == 0 && CG == NT / 64 * GW && (J == 8 || J == 16), "gate layout");
+  __device__ static int group(int t) { return (t >> 6) * GW + (t & 63) % GW; }
+  __device__ static int block(int t) { return (t & 63) / GW; }
 };
 
-// Registers of one chunk: log-gates, and k, v (and q) in the layout above.
+// The value rows need no gate, so they take a layout of their own: thread t
+// holds the 16-byte units i NT + t (i < NU) of the chunk's rows, so that a
+// wave's load covers whole rows. Unit i goes out with row i EVERY of the gate
+// layout.
+template <int D, int NT, typename IN>
+struct VMap {
+  static constexpr int UPR = D * (int)sizeof(IN) / 16;  // 16-byte units per row
+  static constexpr int NU = 64 * UPR / NT;              // units per thread
+  static constexpr int EVERY = GMap<D, NT>::R / NU;
+  static_assert(NU >= 1 && NU * NT == 64 * UPR && GMap<D, NT>::R % NU == 0, "value layout");
+};
+
+// Registers of one chunk: log-gates, k (and q) in the gate layout, v in its own.
 template <int D, int NT, typename IN, bool Q>
 struct GSet {
   static constexpr int R = GMap<D, NT>::R;
   f32x4 lg[R];
-  typename In4<IN>::raw q[Q ? R : 1], k[R], v[R];
+  typename In4<IN>::raw q[Q ? R : 1], k[R];
+  u32x4 v[VMap<D, NT, IN>::NU];
 };
 
 // Loads of the chunk at rows [row0, row0 + valid); rows past `valid` read as
@@ -134,12 +166,23 @@ __device__ __forceinline__ GRsrc grsrc(const float* lg, const IN* q, const IN* k
 template <int D, int NT, typename IN, bool Q>
 __device__ __forceinline__ void gload_row(GSet<D, NT, IN, Q>& s, const GRsrc& r, int e, int t) {
   using M = GMap<D, NT>;
-  const int gi = t / M::J, j = t % M::J;
+  const int gi = M::group(t), j = M::block(t);
   const int el = (M::R * j + e) * D + 4 * gi;
   s.lg[e] = __builtin_bit_cast(f32x4, buf_load16(r.g, el * 4));
   if constexpr (Q) s.q[e] = In4<IN>::bload(r.q, el * (int)sizeof(IN));
   s.k[e] = In4<IN>::bload(r.k, el * (int)sizeof(IN));
-  s.v[e] = In4<IN>::bload(r.v, el * (int)sizeof(IN));
+  using V = VMap<D, NT, IN>;
+  if (e % V::EVERY == 0) s.v[e / V::EVERY] = buf_load16(r.v, 16 * ((e / V::EVERY) * NT + t));
+}
+// Row e's share of the value units into the swizzled value tile
+template <int D, int NT, typename IN, int RB, bool Q>
+__device__ __forceinline__ void stage_v(uint8_t* sV, const GSet<D, NT, IN, Q>& s, int e, int t) {
+  using V = VMap<D, NT, IN>;
+  static_assert(RB == 16 * V::UPR, "value tile rows hold the input rows");
+  if (e % V::EVERY == 0) {
+    const int u = (e / V::EVERY) * NT + t;
+    *reinterpret_cast<u32x4*>(sV + tile_off<RB>(u / V::UPR, 16 * (u % V::UPR))) = s.v[e / V::EVERY];
+  }
 }
 template <int D, int NT, typename IN, bool Q>
 __device__ __forceinline__ void gload(GSet<D, NT, IN, Q>& s, const float* lg, const IN* q, const IN* k, const IN* v,
@@ -150,13 +193,14 @@ __device__ __forceinline__ void gload(GSet<D, NT, IN, Q>& s, const float* lg, co
 }
 
 // In-chunk prefix of the log-gates, in place: p[e][c] becomes
-// lam = lg_0 + ... + lg_r at row r = R j + e, channel 4 g + c (fp32). A
+// lam = lg_0 + ... + lg_r at row r = R j + e, channel 4 g + c (fp32); every
+// lane of the group also gets lam at rows 31 and 63 (half and whole). A
 // log-gate outside [log(1/4), 0] becomes NaN (checked_log_gate), so the
 // prefix of its channel is NaN from its row on, and raises the status flag.
 // The thread's values are checked at once through their NaN-propagating
 // minimum and maximum; only a thread holding a bad one checks them one by one.
 template <int D, int NT, int NR>
-__device__ __forceinline__ void gate_scan(f32x4 (&p)[NR], int* flag, int t) {
+__device__ __forceinline__ void gate_scan(f32x4 (&p)[NR], int* flag, int t, f32x4& half, f32x4& whole) {
   using M = GMap<D, NT>;
   static_assert(NR == M::R, "rows per thread");
   float mn = p[0][0], mx = p[0][0];
@@ -175,33 +219,56 @@ __device__ __forceinline__ void gate_scan(f32x4 (&p)[NR], int* flag, int t) {
   }
 #pragma unroll
   for (int e = 1; e < M::R; ++e) p[e] += p[e - 1];
-  // inclusive scan of the row-block totals across the group's lanes, then
-  // shifted by one lane: the sum of the row blocks before this one
-  const int j = t % M::J;
-  f32x4 inc = p[M::R - 1];
-#pragma unroll
-  for (int s = 1; s < M::J; s <<= 1) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float y = __shfl_up(inc[c], s, M::J);
-      if (j >= s) inc[c] += y;
-    }
-  }
+  // the sum of the group's row blocks before this one: first over the
+  // blocks in this lane's DPP row (GW lanes apart), then over the rows before
+  // it (the row totals through the row swaps). A row shift gives 0 where its
+  // source lies before the row's start, which masks the first blocks; no
+  // shift sits under a lane condition (a DPP read from a lane that the
+  // condition switched off would read nothing).
+  const int row = (t >> 4) & 3;
   f32x4 off;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const float y = __shfl_up(inc[c], 1, M::J);
-    off[c] = j >= 1 ? y : 0.f;
+    const float x = p[M::R - 1][c];
+    float ex, tot;
+    if constexpr (M::PR == 2) {
+      ex = dpp<kRowShr + 8>(x);
+      tot = x + dpp<kRor8>(x);
+    } else {
+      float inc = x + dpp<kRowShr + 4>(x);
+      inc += dpp<kRowShr + 8>(inc);
+      ex = dpp<kRowShr + 4>(inc);
+      tot = x + dpp<kRor4>(x);
+      tot += dpp<kRor8>(tot);
+    }
+    const float below = xor16(tot);         // rows 1, 3: the total of rows 0, 2
+    const float pair = tot + below;         // rows 0+1 or 2+3
+    const float other = xor32(pair);        // rows 2, 3: the total of rows 0+1
+    off[c] = ex + ((row & 1) ? below : 0.f) + ((row & 2) ? other : 0.f);
+    half[c] = (row & 2) ? other : pair;     // rows 0+1: row blocks 0 .. J/2 - 1
+    whole[c] = pair + other;
   }
 #pragma unroll
   for (int e = 0; e < M::R; ++e) p[e] += off;
 }
 
-// sum over the J lanes of a channel group
+// sum over the J row blocks of a channel group (lanes GW apart)
 template <int J>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int s = 1; s < J; s <<= 1) x += __shfl_xor(x, s, J);
+  static_assert(J == 8 || J == 16, "gate layout");
+  if constexpr (J == 16) x += dpp<kRor4>(x);
+  x += dpp<kRor8>(x);
+  x += xor16(x);
+  return x + xor32(x);
+}
+// sum over the channel groups of a wave that hold the same rows (GW = 64 / J
+// consecutive lanes)
+template <int J>
+__device__ __forceinline__ float across_groups(float x) {
+  static_assert(J == 8 || J == 16, "gate layout");
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  if constexpr (J == 8) x += dpp<kHalfMirror>(x);
   return x;
 }
 
@@ -229,7 +296,7 @@ __global__ __launch_bounds__(D * 2, (sizeof(IN) == 2 ? 2 : 1)) void gla_state_ke
   const int c0 = seg * a.chunks_per_seg_state;
   const int n = max(0, min(c0 + a.chunks_per_seg_state, a.nchunks) - c0);
   const int t = threadIdx.x, w = t >> 6, l = t & 63, h = l >> 5, li = l & 31;
-  const int gi = t / J, j = t % J;
+  const int gi = M::group(t), j = M::block(t);
   const long long base = (long long)bh * a.N;
   const IN* k = static_cast<const IN*>(a.k);
   const IN* v = static_cast<const IN*>(a.v);
@@ -256,12 +323,11 @@ __global__ __launch_bounds__(D * 2, (sizeof(IN) == 2 ? 2 : 1)) void gla_state_ke
     uint8_t* sK = smem[m & 1];
     uint8_t* sV = sK + TB;
     float* fb63 = f63[m & 1];
-    gate_scan<D, NT>(cur.lg, a.status_flag, t);
-    float l63[4];
+    f32x4 l31, l63;
+    gate_scan<D, NT>(cur.lg, a.status_flag, t, l31, l63);
     f32x4 e63;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      l63[c] = __shfl(cur.lg[R - 1][c], J - 1, J);
       ltot[c] += l63[c];
       e63[c] = exp_nat(l63[c]);
       zr[c] *= e63[c];
@@ -269,15 +335,18 @@ __global__ __launch_bounds__(D * 2, (sizeof(IN) == 2 ? 2 : 1)) void gla_state_ke
 #pragma unroll
     for (int e = 0; e < R; ++e) {
       const int row = R * j + e;
+      // rows past the end (zero k and log-gates: finite products) times 0,
+      // without a branch around the exponentials
+      const float keep = row < valid ? 1.f : 0.f;
       float x[4];
       In4<IN>::to_f32(cur.k[e], x);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        x[c] = row < valid ? gphi<FM>(x[c]) * exp_nat(l63[c] - cur.lg[e][c]) : 0.f;
+        x[c] = gphi<FM>(x[c]) * exp_nat(l63[c] - cur.lg[e][c]) * keep;
         zr[c] += x[c];
       }
       store4<OP, RB>(sK, row, 4 * gi, x);
-      store4_raw<IN, OP, RB>(sV, row, 4 * gi, cur.v[e]);
+      stage_v<D, NT, IN, RB>(sV, cur, e, t);
       gload_row<D, NT, IN, false>(cur, nr, e, t);
     }
     if (j == 0) *reinterpret_cast<f32x4*>(fb63 + 4 * gi) = e63;
@@ -347,7 +416,10 @@ __global__ __launch_bounds__(gla_output_threads<D>()) void gla_output_kernel(Gat
   using M = GMap<D, NTP>;
   constexpr int R = M::R, J = M::J;
   constexpr int RB = D * Ops<OP>::kBytes, TB = 64 * RB;
-  constexpr int NBUF = 2 * (3 * TB + 2 * D * 4 + NWP * 64 * 4) <= 160 * 1024 ? 2 : 1;
+  // output staging: each consumer wave's 32 x 32 block of a row block, rows
+  // padded by 16 bytes (the lanes of one write then fall in distinct banks)
+  constexpr int YRS = 32 * (int)sizeof(IN) + 16, YST = NW * 32 * YRS;
+  constexpr int NBUF = 2 * (3 * TB + 2 * D * 4 + NWP * 64 * 4) + YST <= 160 * 1024 ? 2 : 1;
   // Two register sets of prefetched rows where they fit (bf16): the next
   // chunk's loads go out before this one is staged. With one set they go out
   // after it, during the consumers' products.
@@ -357,6 +429,7 @@ __global__ __launch_bounds__(gla_output_threads<D>()) void gla_output_kernel(Gat
   __shared__ __attribute__((aligned(16))) float fac[NBUF][2][D];
   // per buffer: each producer wave's part of the carried denominator of every row
   __shared__ float dpart[NBUF][NWP][64];
+  __shared__ __attribute__((aligned(16))) uint8_t ystage[YST];
   const FwdArgs& a = g.f;
   const int bh = blockIdx.x, seg = blockIdx.y;
   const int c0 = seg * a.chunks_per_seg;
@@ -383,7 +456,7 @@ __global__ __launch_bounds__(gla_output_threads<D>()) void gla_output_kernel(Gat
   if (wave >= NW) {
     // ------------------------------------------------------------ producers
     const int p = t - 64 * NW, pw = wave - NW;
-    const int gi = p / J, j = p % J;
+    const int gi = M::group(p), j = M::block(p);
     float zreg[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) zreg[c] = zinit ? zinit[4 * gi + c] : 0.f;
@@ -406,14 +479,10 @@ __global__ __launch_bounds__(gla_output_threads<D>()) void gla_output_kernel(Gat
       uint8_t* sQ = smem[m % NBUF];
       uint8_t* sK = sQ + TB;
       uint8_t* sV = sK + TB;
-      gate_scan<D, NTP>(cur.lg, a.status_flag, p);
-      float lc[4], l63[4], cs[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        lc[c] = __shfl(cur.lg[kCenter % R][c], kCenter / R, J);
-        l63[c] = __shfl(cur.lg[R - 1][c], J - 1, J);
-        cs[c] = 0.f;
-      }
+      // lam_c = lam_31 (the first half's total), lam_63 (the chunk's)
+      f32x4 lc, l63;
+      gate_scan<D, NTP>(cur.lg, a.status_flag, p, lc, l63);
+      float cs[4] = {0.f, 0.f, 0.f, 0.f};
       // the carried part exp(lam_c) z for this chunk's readout (its dot
       // products with the staged Qh rows form the carried denominator)
       f32x4 ec, ee, zcar;
@@ -426,6 +495,7 @@ __global__ __launch_bounds__(gla_output_threads<D>()) void gla_output_kernel(Gat
 #pragma unroll
       for (int e = 0; e < R; ++e) {
         const int row = R * j + e;
+        const float keep = row < valid ? 1.f : 0.f;  // key rows past the end, without a branch
         float xq[4], xk[4];
         In4<IN>::to_f32(cur.q[e], xq);
         In4<IN>::to_f32(cur.k[e], xk);
@@ -433,22 +503,19 @@ __global__ __launch_bounds__(gla_output_threads<D>()) void gla_output_kernel(Gat
         for (int c = 0; c < 4; ++c) {
           const float f = exp_nat(cur.lg[e][c] - lc[c]);
           xq[c] = gphi<FM>(xq[c]) * f;
-          xk[c] = row < valid ? gphi<FM>(xk[c]) * __builtin_amdgcn_rcpf(f) : 0.f;
+          xk[c] = gphi<FM>(xk[c]) * __builtin_amdgcn_rcpf(f) * keep;
           cs[c] += xk[c];
         }
         store4_held<OP, RB>(sQ, row, 4 * gi, xq);  // xq: Qh as the operand holds it
         store4<OP, RB>(sK, row, 4 * gi, xk);
-        store4_raw<IN, OP, RB>(sV, row, 4 * gi, cur.v[e]);
+        stage_v<D, NTP, IN, RB>(sV, cur, e, p);
         dq[e] = xq[0] * zcar[0] + xq[1] * zcar[1] + xq[2] * zcar[2] + xq[3] * zcar[3];
         if constexpr (PSETS == 1) gload_row<D, NTP, IN, true>(cur, nr, e, p);
       }
-      // the wave's channel groups: lanes J, 2J, ... apart hold the same rows
+      // the wave's GW channel groups (consecutive lanes) hold the same rows
 #pragma unroll
-      for (int e = 0; e < R; ++e) {
-#pragma unroll
-        for (int sh = J; sh < 64; sh <<= 1) dq[e] += __shfl_xor(dq[e], sh, 64);
-      }
-      if (l < J) {
+      for (int e = 0; e < R; ++e) dq[e] = across_groups<J>(dq[e]);
+      if (l % M::GW == 0) {
 #pragma unroll
         for (int e = 0; e < R; ++e) dpart[m % NBUF][pw][R * j + e] = dq[e];
       }
@@ -547,19 +614,42 @@ __global__ __launch_bounds__(gla_output_threads<D>()) void gla_output_kernel(Gat
         }
         den += xor32(den);
         const float inv = a.normalize ? 1.f / fmaxf(den, kEps) : 1.f;
-        if (irow < valid) {
-          IN* o = out + (row0 + irow) * D + 32 * w + 4 * h;
+        // lane (li, h) holds row li, columns 8 gq + 4 h + 0..3 of the wave's
+        // 32: written to the wave's LDS block and read back by rows, so that
+        // every store covers whole 32-column row pieces (rows past the end
+        // fall outside the descriptor's range)
+        uint8_t* ys = ystage + w * 32 * YRS;
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const float y0 = num[4 * gq] * inv, y1 = num[4 * gq + 1] * inv;
-            const float y2 = num[4 * gq + 2] * inv, y3 = num[4 * gq + 3] * inv;
-            if constexpr (sizeof(IN) == 2) {
-              *reinterpret_cast<u32x2*>(o + 8 * gq) = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
-            } else {
-              *reinterpret_cast<f32x4*>(o + 8 * gq) = f32x4{y0, y1, y2, y3};
-            }
+        for (int gq = 0; gq < 4; ++gq) {
+          const float y0 = num[4 * gq] * inv, y1 = num[4 * gq + 1] * inv;
+          const float y2 = num[4 * gq + 2] * inv, y3 = num[4 * gq + 3] * inv;
+          uint8_t* yp = ys + li * YRS + (8 * gq + 4 * h) * (int)sizeof(IN);
+          if constexpr (sizeof(IN) == 2)
+            *reinterpret_cast<u32x2*>(yp) = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+          else
+            *reinterpret_cast<f32x4*>(yp) = f32x4{y0, y1, y2, y3};
+        }
+        // the block is the wave's own: its LDS operations complete in order,
+        // so the fences only keep the compiler from moving the reads above
+        // the writes (and, after the stores, the next block's writes above
+        // these reads)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        {
+          constexpr int UPR = 2 * (int)sizeof(IN);  // 16-byte units per row piece
+          constexpr int RPP = 64 / UPR;             // rows per pass of the wave
+          const auto ro = make_rsrc(out + row0 * D, (unsigned)(valid * D * (int)sizeof(IN)));
+#pragma unroll
+          for (int i = 0; i < 32 / RPP; ++i) {
+            const int rr = RPP * i + l / UPR, u = l % UPR;
+            buf_store16_nt(ro, ((32 * rb + rr) * D + 32 * w) * (int)sizeof(IN) + 16 * u,
+                           *reinterpret_cast<const u32x4*>(ys + rr * YRS + 16 * u));
           }
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
       // S <- diag(exp(lam_63 - lam_c)) (S' + Kh^T V)
 #pragma unroll UNR4
