@@ -74,12 +74,32 @@ __device__ __forceinline__ void lds_read4(const uint8_t* tile, int row, int col,
   }
 }
 
-template <typename IN>
-__device__ __forceinline__ void store4(IN* p, float a, float b, float c, float d) {
+// Lane (li, h) holds y[4 g + c] = row `row`, column col0 + 8 g + 4 h + c of
+// a wave's 32-column block (the accumulator layout) of a chunk whose rows
+// start at `chunk`. bf16: one swap with the other lane half gives each lane
+// 8 consecutive columns (16 p + 8 h ..), so each of its two stores covers 32
+// bytes of every row rather than 16. Rows at or past `valid` fall outside
+// the descriptor's range. Every lane calls it (the swap pairs lanes l and
+// l ^ 32, which hold the same row).
+template <typename IN, int D>
+__device__ __forceinline__ void store_block_rows(IN* chunk, int valid, int row, int col0, const float (&y)[16]) {
+  const auto r = make_rsrc(chunk, (unsigned)(valid * D * (int)sizeof(IN)));
+  const int h = (threadIdx.x >> 5) & 1;
   if constexpr (sizeof(IN) == 2) {
-    *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int b = 8 * p;
+      const uint32_t x0 = pack_bf16x2(y[b], y[b + 1]), x1 = pack_bf16x2(y[b + 2], y[b + 3]);
+      const uint32_t z0 = pack_bf16x2(y[b + 4], y[b + 5]), z1 = pack_bf16x2(y[b + 6], y[b + 7]);
+      const auto s0 = __builtin_amdgcn_permlane32_swap(x0, z0, false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(x1, z1, false, false);
+      buf_store16(r, (row * D + col0 + 16 * p + 8 * h) * 2, u32x4{s0[0], s1[0], s0[1], s1[1]});
+    }
   } else {
-    *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      buf_store16(r, (row * D + col0 + 8 * g + 4 * h) * 4,
+                  __builtin_bit_cast(u32x4, f32x4{y[4 * g], y[4 * g + 1], y[4 * g + 2], y[4 * g + 3]}));
   }
 }
 
@@ -483,17 +503,14 @@ __global__ __launch_bounds__(D * 4) void bwd_dq_kernel(BwdArgs a) {
     };
     intra(Pd, 32 * ib);
     if (ib) intra(Po, 0);
-    if (irow < valid) {
-      IN* o = dq + (base + 64LL * c + irow) * D + 32 * w + 4 * h;
+    {
       // decay: the row's factor gamma^(r-32), and phi(q) back from the staged row
       const float fr = DECAY ? dc.pw(irow - 32) : 1.f, fb = DECAY ? dc.pw(32 - irow) : 1.f;
+      float y[16];
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        store4<IN>(o + 8 * g, fr * T[4 * g] * bdphi<FM>(fb * fq[4 * g]),
-                   fr * T[4 * g + 1] * bdphi<FM>(fb * fq[4 * g + 1]),
-                   fr * T[4 * g + 2] * bdphi<FM>(fb * fq[4 * g + 2]),
-                   fr * T[4 * g + 3] * bdphi<FM>(fb * fq[4 * g + 3]));
-      if (w == 0 && h == 0)
+      for (int r = 0; r < 16; ++r) y[r] = fr * T[r] * bdphi<FM>(fb * fq[r]);
+      store_block_rows<IN, D>(dq + (base + 64LL * c) * D, valid, irow, 32 * w, y);
+      if (irow < valid && w == 0 && h == 0)
         *reinterpret_cast<f32x2*>(a.rowstats + 2 * (base + 64LL * c + irow)) = f32x2{inv, hh};
     }
     if constexpr (DECAY) {
@@ -843,12 +860,10 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
         const f32x16& Vt = jb ? V1 : V0;
-        const int j = 32 * jb + li;
-        if (j < valid) {
-          IN* o = dv + (base + 64LL * c + j) * D + 32 * w + 4 * h;
+        float y[16];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) store4<IN>(o + 8 * g, Vt[4 * g], Vt[4 * g + 1], Vt[4 * g + 2], Vt[4 * g + 3]);
-        }
+        for (int r = 0; r < 16; ++r) y[r] = Vt[r];
+        store_block_rows<IN, D>(dv + (base + 64LL * c) * D, valid, 32 * jb + li, 32 * w, y);
       }
       // R += phi(Q)^T G = Qs^T Y over the chunk
 #pragma unroll
@@ -926,18 +941,17 @@ __global__ __launch_bounds__(D * 4) void bwd_dkv_kernel(BwdArgs a) {
       for (int jb = 0; jb < 2; ++jb) {
         const f32x16& Kt = jb ? K1 : K0;
         const int j = 32 * jb + li;
-        if (j < valid) {
-          IN* o = dk + (base + 64LL * c + j) * D + 32 * w + 4 * h;
-          // decay: the row's factor gamma^(32-r), and phi(k) back from the staged row
-          const float fr = DECAY ? dc.pw(32 - j) : 1.f, fb = DECAY ? dc.pw(j - 32) : 1.f;
+        // decay: the row's factor gamma^(32-r), and phi(k) back from the staged row
+        const float fr = DECAY ? dc.pw(32 - j) : 1.f, fb = DECAY ? dc.pw(j - 32) : 1.f;
+        float y[16];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float fk[4];
-            lds_read4<OP, RB>(sK, j, 32 * w + 8 * g + 4 * h, fk);
-            store4<IN>(o + 8 * g, fr * Kt[4 * g] * bdphi<FM>(fb * fk[0]), fr * Kt[4 * g + 1] * bdphi<FM>(fb * fk[1]),
-                       fr * Kt[4 * g + 2] * bdphi<FM>(fb * fk[2]), fr * Kt[4 * g + 3] * bdphi<FM>(fb * fk[3]));
-          }
+        for (int g = 0; g < 4; ++g) {
+          float fk[4];
+          lds_read4<OP, RB>(sK, j, 32 * w + 8 * g + 4 * h, fk);
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) y[4 * g + cc] = fr * Kt[4 * g + cc] * bdphi<FM>(fb * fk[cc]);
         }
+        store_block_rows<IN, D>(dk + (base + 64LL * c) * D, valid, j, 32 * w, y);
       }
       // R^T += G^T phi(Q), r += phi(Q)^T h over the chunk
 #pragma unroll
