@@ -22,14 +22,9 @@
 
 namespace la {
 
-// TPH = DF * D / 32 threads per head (8 rows of a 4-column group each, at
-// least one wave, at most one block): with 16 rows per thread (64 registers
-// of state) only about five blocks fit per CU, and the 2048 blocks of an
-// 8192-head step at d = 64 ran in 1.6 rounds (58.7 against 53.5 us a step
-// with a live state larger than the last-level cache).
 template <int D, int DF>
 struct DecodeShape {
-  static constexpr int TPH = (DF * D / 32 > 256) ? 256 : (DF * D / 32 > 64) ? DF * D / 32 : 64;  // threads per head
+  static constexpr int TPH = (DF * D / 64 > 64) ? DF * D / 64 : 64;  // threads per head
   static constexpr int HPB = 256 / TPH;                               // heads per block
   static constexpr int CG = D / 4;                                    // 16-byte column groups
   static constexpr int R = TPH / CG;                                  // row groups
